@@ -1,0 +1,20 @@
+"""CPU oracle for the q4_K x q8_1 quantized matrix multiply (MMQ).
+
+TEST INFRASTRUCTURE ONLY. Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything here. The HIP
+path (``q4_q8_int8_amd``) never imports this package and this package never
+imports it; the two share no code, headers, tables or constants.
+
+Every function is a plain, slow, readable restatement of what the pages define
+(see the docstrings for the page and section each step follows). Floating-point
+results are computed in float64 except where the pages fix the precision (the
+q8_1 scale and quantization steps are float32, the stored scale is float16).
+"""
+from .mmq_oracle import (  # noqa: F401
+    QK8, QK_K, Q4K_BLOCK_BYTES,
+    Q8, Q4K,
+    f16_encode, f16_decode, round_half_away,
+    quantize_q8_1, q8_1_image,
+    decode_q4_K, q4_K_scales, dequantize_q4_K,
+    mmq, block_dots, mmq_terms,
+)
