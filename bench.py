@@ -1,0 +1,191 @@
+"""Benchmark of the q4_K x q8_1 MMQ hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rotate R] [--no-cpu-baseline]
+
+Workload: the LLaMA-7B q-proj prefill product, M=2048 tokens, K=4096, N=4096, with
+synthetic seeded inputs (synth.py: activations N(0,1) with 0.1% outliers x20, q4_K fit of
+N(0, 0.02) weights). The weights are repacked once before timing (an offline, per-weight
+step); one timed step is the whole per-batch path: quantize_q8_1 of the f32 activations
+followed by the GEMM, with every input already resident in device memory. R copies of the
+activations, weights and outputs are rotated so that consecutive steps do not hit in the
+256 MB last-level cache.
+
+Prints one JSON line. value = M*N*K / (time per step) in TMAC/s (1 MAC = one int8
+multiply-accumulate); the GEMM kernel's own time, measured with HIP events on the stream it
+runs on, gives the roofline entry against the dense int8 MFMA peak.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, tera-ops/s (1 MAC = 2 ops)
+HBM_PEAK_GBS = 8000.0
+PAGES_QPROJ_TMACS = 15.19        # the pages' best q-proj MMQ kernel: 34.36 GMAC in 2.262 ms
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmq_qproj_traffic.json")
+KERNEL_SOURCES = ["q4_q8_int8_amd/csrc/mmq_gemm.hip", "q4_q8_int8_amd/csrc/mmq_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(W: dict) -> dict:
+    """The CPU oracle (as it stands) on the same workload: quantize, decode, f64 product."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    M, N, K = W["M"], W["N"], W["K"]
+    rows = M // 4  # a bounded sample: the first quarter of the token rows
+    t0 = time.perf_counter()
+    q = oracle.quantize_q8_1(W["x"][:rows])
+    wf = oracle.decode_q4_K(W["w"])
+    C = oracle.mmq(q, wf)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(C).all()
+    return {"value": rows * N * K / dt / 1e12, "unit": "TMAC/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {rows} of {M} token rows, all {N} outputs, K={K}: quantize + "
+                      f"q4_K decode + float64 product, {dt:.2f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              "(how it would shard is described in DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth
+    import q4_q8_int8_amd as mmq
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W = synth.workload("qproj")
+    M, N, K = W["M"], W["N"], W["K"]
+    R = max(1, args.rotate)
+    stream = torch.cuda.current_stream()
+
+    xs = [torch.from_numpy(W["x"]).to(dev) for _ in range(R)]
+    w_dev = torch.from_numpy(W["w"]).to(dev)
+    reps = [torch.empty(mmq.mmq_q4K_repacked_bytes(N, K), dtype=torch.uint8, device=dev)
+            for _ in range(R)]
+    q8s = [torch.empty(mmq.mmq_q8_1_bytes(M, K), dtype=torch.uint8, device=dev) for _ in range(R)]
+    Cs = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(R)]
+
+    ev_r0, ev_r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev_r0.record(stream)
+    for r in range(R):
+        mmq.repack_q4_K(w_dev, N, K, reps[r])
+    ev_r1.record(stream)
+    torch.cuda.synchronize()
+    repack_us = ev_r0.elapsed_time(ev_r1) * 1e3 / R
+
+    def step(i, evs=None):
+        r = i % R
+        if evs:
+            evs[0].record(stream)
+        mmq.quantize_q8_1(xs[r], M, K, q8s[r])
+        if evs:
+            evs[1].record(stream)
+        mmq.mmq_q4K_q8_1(M, N, K, q8s[r], reps[r], Cs[r])
+        if evs:
+            evs[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    plan = mmq.mmq_last_kernel()
+
+    # timed region: exactly K steps between synchronizations; HIP events on the launch
+    # stream bracket each kernel for the per-kernel durations
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    q_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    g_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+
+    macs = M * N * K
+    ms_per_step = wall * 1e3 / args.steps
+    gemm_s = float(g_ms.mean()) * 1e-3
+    achieved_tops = 2.0 * macs / gemm_s / 1e12
+    value = macs / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": "q4_K x q8_1 MMQ TMAC/s (and us/GMAC) at M=2048,K=4096,N=4096",
+        "value": round(value, 2),
+        "unit": "TMAC/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGES_QPROJ_TMACS, 2),
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "q4_K x q8_1 q-proj prefill GEMM, quantize + GEMM per step",
+                   "M": M, "N": N, "K": K, "rotate": R,
+                   "tile": plan["tile"], "block_m": plan["block_m"], "block_n": plan["block_n"],
+                   "grid": plan["grid"], "lds_bytes": plan["lds_bytes"]},
+        "roofline": {"bound": "mfma", "achieved": round(achieved_tops, 1),
+                     "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved_tops / INT8_PEAK_TOPS, 4),
+                     "traffic": measured_traffic()},
+        "us_per_gmac": round(ms_per_step * 1e3 / (macs / 1e9), 4),
+        "gemm": {"us": round(gemm_s * 1e6, 2), "us_min": round(float(g_ms.min()) * 1e3, 2),
+                 "tmacs": round(macs / gemm_s / 1e12, 2),
+                 "us_per_gmac": round(gemm_s * 1e6 / (macs / 1e9), 4)},
+        "quantize": {"us": round(float(q_ms.mean()) * 1e3, 2),
+                     "hbm_frac": round((M * K * (4 + 1.125)) / (float(q_ms.mean()) * 1e-3)
+                                       / (HBM_PEAK_GBS * 1e9), 4)},
+        "repack_us_once": round(repack_us, 2),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(W)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

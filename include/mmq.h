@@ -1,0 +1,191 @@
+/*
+ * mmq.h -- C ABI of the q4_K x q8_1 quantized matrix multiply (MMQ) for LLM prefill
+ * on AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ *   C[M][N] = sum_k (da_i,b(k) * q_ik) * (dsv_j,b(k) * v_jk + dmv_j,b(k))
+ *           = sum_b ( da_ib * dsv_jb * S_ijb  +  dmv_jb * (da_ib * sa_ib) )
+ *
+ * Activations are quantized to q8_1 blocks of 32 (int8 values q, an f16 scale da and the
+ * integer block sum sa); weights are q4_K super-blocks of 256 (f16 d and dmin, 6-bit
+ * sub-block scale sc and min m, unsigned nibbles v). S_ijb is the integer dot product of
+ * one 32-block, dsv = d*sc, dmv = -dmin*m. Definitions: the r15 page ("f32-accumulate mma
+ * probe + rank-1 term2 rescale", section 2.1, the two-term rescale), its section 3.2 (the
+ * packed da/sa word) and the r16 page ("Narrow kernel gets the rank-1 fold", section 2.1,
+ * the rank-1 term2 fold).
+ *
+ * Conventions for every entry point below:
+ *   - Pointers named x, q8, w, w_rep, C, S are DEVICE pointers owned by the caller; the
+ *     library never frees, keeps or allocates device memory.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Kernels are enqueued on it and the
+ *     call returns without synchronizing.
+ *   - All arguments are validated on the host before anything is launched; on any error
+ *     nothing is launched and nothing is written. Return value: an mmq_status code.
+ *   - Buffers may not overlap. Device pointers must be 16-byte aligned.
+ *   - Thread-safe: the per-device property cache is initialized once under a lock;
+ *     mmq_last_kernel and mmq_last_error report the calling thread's last call.
+ */
+#ifndef MMQ_H
+#define MMQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum mmq_status {
+  MMQ_OK = 0,
+  MMQ_E_ARG = 1,     /* null or misaligned pointer, non-positive size, bad option value */
+  MMQ_E_SHAPE = 2,   /* K not a multiple of the block length, size overflow, bad window */
+  MMQ_E_LDS = 3,     /* no tile fits the LDS budget: refused, nothing launched */
+  MMQ_E_DEVICE = 4,  /* current device is not gfx950, or no device */
+  MMQ_E_HIP = 5      /* a HIP runtime call or the kernel launch failed (see mmq_last_error) */
+};
+
+#define MMQ_QK8 32               /* q8_1 block length */
+#define MMQ_QK_K 256             /* q4_K super-block length */
+#define MMQ_Q4K_BLOCK_BYTES 144  /* bytes of one q4_K super-block */
+#define MMQ_REP_TILE_ROWS 32     /* weight rows per repacked tile */
+#define MMQ_REP_TILE_BYTES 6144  /* bytes per (repacked tile, super-block) */
+
+/* Tile variants of the GEMM kernel (one template, two instantiations). */
+enum mmq_tile {
+  MMQ_TILE_AUTO = 0,   /* let the guard choose */
+  MMQ_TILE_LARGE = 1,  /* 128 tokens x 128 output features per workgroup, 4 wavefronts */
+  MMQ_TILE_SMALL = 2   /* 32 tokens x 64 output features per workgroup, 2 wavefronts */
+};
+
+/* Why the guard chose what it chose. */
+enum mmq_reason {
+  MMQ_REASON_NONE = 0,
+  MMQ_REASON_LARGE = 1,         /* large tile fits the LDS budget and M is large enough */
+  MMQ_REASON_SMALL_M = 2,       /* M <= 64: the small tile wastes fewer token rows */
+  MMQ_REASON_LDS_FALLBACK = 3,  /* the large tile does not fit the LDS budget: small tile */
+  MMQ_REASON_FORCED = 4,        /* the caller's options asked for this tile */
+  MMQ_REASON_NO_FIT = 5         /* nothing fits the budget: refused with MMQ_E_LDS */
+};
+
+/* Optional knobs for the _ex entry points (NULL = defaults). */
+typedef struct mmq_options {
+  int32_t force_tile;   /* enum mmq_tile. A forced tile that does not fit is refused (MMQ_E_LDS) */
+  int32_t reserved;
+  int64_t lds_budget;   /* > 0: check tiles against this many bytes of LDS instead of the
+                           device's per-workgroup limit (lets a caller force the fallback) */
+} mmq_options;
+
+/* What the guard decided for a product (filled by mmq_plan and by every GEMM call). */
+typedef struct mmq_kernel_info {
+  int32_t tile;         /* enum mmq_tile actually chosen; MMQ_TILE_AUTO (0) when none */
+  int32_t reason;       /* enum mmq_reason */
+  int32_t block_m;      /* tokens per workgroup */
+  int32_t block_n;      /* output features per workgroup */
+  int32_t threads;      /* threads per workgroup */
+  int32_t fallback;     /* 1 when the large tile was rejected by the LDS budget */
+  int64_t lds_bytes;    /* LDS the chosen kernel uses (0 when none) */
+  int64_t lds_budget;   /* budget the guard checked against */
+  int64_t grid;         /* workgroups launched (1-D grid) */
+} mmq_kernel_info;
+
+/* ---------------------------------------------------------------- sizes (host only) */
+
+/* Bytes of a q8_1 buffer for M x K activations: M*K int8 values followed by M*(K/32)
+ * 32-bit scale words. K must be a positive multiple of 32. */
+int mmq_q8_1_bytes(int64_t M, int64_t K, size_t* bytes);
+
+/* Bytes of q4_K weights N x K in the GGUF layout: N*(K/256)*144. K % 256 == 0. */
+int mmq_q4K_bytes(int64_t N, int64_t K, size_t* bytes);
+
+/* Bytes of repacked q4_K weights: ceil(N/32)*(K/256)*6144. K % 256 == 0. */
+int mmq_q4K_repacked_bytes(int64_t N, int64_t K, size_t* bytes);
+
+/* ---------------------------------------------------------------- the hot path */
+
+/*
+ * quantize_q8_1: f32 activations x[M][K] (row-major, leading dimension K) -> q8_1.
+ * Defined on the r15 page, section 2.1 (blocks of 32 with scale da and integer in-block sum
+ * sa, computed by the quantize prepass). Per block of 32 values, in float32:
+ *   amax = max|x|, d = amax/127 (IEEE division), id = d > 0 ? 1/d : 0,
+ *   q = roundf(x*id) clamped to [-127, 127] (a NaN product, which only a block whose 1/d
+ *   overflows can produce from x = 0, gives 0), sa = sum of q, da = f16(d) (nearest even).
+ * Output layout of q8 (mmq_q8_1_bytes(M, K) bytes):
+ *   bytes [0, M*K):          int8 q, row-major [M][K]
+ *   bytes [M*K, M*K*9/8):    uint32 words [M][K/32]: bits 0..15 = f16 bits of da,
+ *                            bits 16..31 = sa as a signed 16-bit integer (|sa| <= 4064).
+ * Preconditions: finite x with |x| <= 8.3e6 (so that amax/127 fits f16). K % 32 == 0.
+ * Errors: MMQ_E_ARG (null pointer, M or K <= 0), MMQ_E_SHAPE (K % 32, size overflow),
+ *         MMQ_E_DEVICE, MMQ_E_HIP.
+ */
+int quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, void* stream);
+
+/*
+ * repack_q4_K: q4_K weights (GGUF layout, [N][K/256] super-blocks of 144 bytes, the fields of
+ * the r15 page, section 2.1) -> the GEMM's layout. Run once per weight matrix.
+ * Output (mmq_q4K_repacked_bytes(N, K) bytes): one 6144-byte record per (tile t of 32 weight
+ * rows, super-block s), records ordered [t][s]; rows N..32*ceil(N/32)-1 are zero. Record:
+ *   bytes [0, 4096):   nibbles, [g 0..3][h 0..1][j 0..31][16 bytes] = bytes 32g+16h .. +15 of
+ *                      the 128 nibble bytes of row 32t+j (low nibble: sub-block 2g, element
+ *                      16h+e; high nibble: sub-block 2g+1, element 16h+e)
+ *   bytes [4096, 5120): float dsv[b 0..7][j 0..31] = d*sc of sub-block b of row 32t+j
+ *   bytes [5120, 6144): float dmv[b 0..7][j 0..31] = -(dmin*m)
+ * Both scale products are exact in float32.
+ * Errors: MMQ_E_ARG, MMQ_E_SHAPE (K % 256), MMQ_E_DEVICE, MMQ_E_HIP.
+ */
+int repack_q4_K(const void* w_q4K, int64_t N, int64_t K, void* w_rep, void* stream);
+
+/*
+ * mmq_q4K_q8_1: C[M][N] (float32, row-major, leading dimension N; overwritten) =
+ *   sum over 32-blocks b of  da_ib*dsv_jb*S_ijb  +  dmv_jb*(da_ib*sa_ib)
+ * (the two-term rescale of the r15 page, section 2.1, with the row factor da*sa folded once
+ * per token row as on the r16 page, section 2.1). q8 comes from quantize_q8_1 (M x K), w_rep
+ * from repack_q4_K (N x K). S_ijb is computed exactly with int8 MFMA; each block's terms are
+ * added to a float32 accumulator in increasing b, so the result is deterministic.
+ * M, N >= 1 (any value; ragged tiles are masked), K % 256 == 0.
+ * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_LDS (no tile fits), MMQ_E_DEVICE, MMQ_E_HIP.
+ */
+int mmq_q4K_q8_1(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+                 float* C, void* stream);
+
+/* As mmq_q4K_q8_1, with options (tile choice, LDS budget); opt may be NULL. */
+int mmq_q4K_q8_1_ex(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+                    float* C, void* stream, const mmq_options* opt);
+
+/*
+ * mmq_q4K_q8_1_blockdots: the per-block integer dot products S_ijb = sum_{k in block b}
+ * q_ik * v_jk (the r15 page, section 2.1) for a window of tokens [i0, i1) and output
+ * features [j0, j1), through the same GEMM kernel template with a store-S epilogue.
+ * S (int32, device) has layout [K/32][i1-i0][j1-j0]. For testing bit-exactness.
+ * Errors: as mmq_q4K_q8_1; MMQ_E_SHAPE for an empty or out-of-range window.
+ */
+int mmq_q4K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+                           int64_t i0, int64_t i1, int64_t j0, int64_t j1, int32_t* S,
+                           void* stream, const mmq_options* opt);
+
+/* ---------------------------------------------------------------- the guard (host only) */
+
+/*
+ * mmq_plan: the LDS-budget guard as a pure host function (no device access). Chooses the
+ * tile for an M x N x K product given `lds_budget` bytes per workgroup (opt->lds_budget,
+ * when set, takes precedence): the large tile when it fits and M > 64, else the small tile,
+ * else MMQ_E_LDS. A kernel that does not fit the budget is never launched: on the r16 page
+ * (section 1) an over-budget launch failed silently and produced wrong numbers, so here
+ * the fallback is explicit and reported (fallback, reason), and a refusal is an error.
+ */
+int mmq_plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t lds_budget,
+             mmq_kernel_info* out);
+
+/* The guard decision of the calling thread's last GEMM or blockdots call. */
+int mmq_last_kernel(mmq_kernel_info* out);
+
+/* Static text for a status code. */
+const char* mmq_status_str(int status);
+
+/* Detail of the calling thread's last error (empty string when the last call succeeded). */
+const char* mmq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MMQ_H */

@@ -213,7 +213,9 @@ def mmq_terms(q: Q8, w: Q4K, rows: Sequence[int] | None = None):
     term1 scales the integer block dot product S, term2 is the rank-1 correction from the
     block sums sa (the row factor da*sa times the column factor dmv). Each term is exact in
     f64. S is formed one block at a time as an f64 matrix product of integer matrices
-    (exact: every partial sum is an integer below 2^16). Returns (C_terms, T), [R, N].
+    (exact: every partial sum is an integer below 2^16). Summed over b, term2 is the
+    product of the [R, K/32] row factors and the [N, K/32] column factors, taken as one f64
+    matrix product (and likewise for its absolute values in T). Returns (C_terms, T), [R, N].
     """
     if rows is None:
         rows = np.arange(q.qs.shape[0])
@@ -225,14 +227,15 @@ def mmq_terms(q: Q8, w: Q4K, rows: Sequence[int] | None = None):
     sa = q.sa[rows].astype(np.float64)                  # [R, nb]
     dsv, dmv = q4_K_scales(w)                           # [N, nb]
     v = w.v.astype(np.float64)
-    N = v.shape[0]
-    C = np.zeros((R, N))
-    T = np.zeros((R, N))
+    dma = da * sa                                       # row factor of term2, exact
+    C = dma @ dmv.T                                     # sum_b term2
+    T = np.abs(dma) @ np.abs(dmv).T                     # sum_b |term2|
     for b in range(nb):
         ks = slice(b * QK8, (b + 1) * QK8)
-        S = qs[:, ks] @ v[:, ks].T                      # [R, N], exact integers
-        t1 = (da[:, b:b + 1] * dsv[None, :, b]) * S
-        t2 = dmv[None, :, b] * (da[:, b] * sa[:, b])[:, None]
-        C += t1 + t2
-        T += np.abs(t1) + np.abs(t2)
+        t1 = qs[:, ks] @ v[:, ks].T                     # S, [R, N], exact integers
+        t1 *= da[:, b:b + 1]
+        t1 *= dsv[None, :, b]                           # term1 = da * dsv * S
+        C += t1
+        np.abs(t1, out=t1)
+        T += t1
     return C, T

@@ -1,0 +1,190 @@
+"""q4_K x q8_1 quantized matrix multiply (MMQ) on MI355X (gfx950).
+
+A thin ctypes binding over libmmq.so, whose C ABI is declared in include/mmq.h. The
+functions here have the same names and arguments as the C entry points and only marshal
+arguments: tensors are passed as device pointers, the stream defaults to torch's current
+stream, and a nonzero status raises MMQError. Every step of the computation runs in the
+library's HIP kernels; there is no fallback path. Importing this package fails loudly when
+libmmq.so has not been built (python -m q4_q8_int8_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmmq.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "mmq.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m q4_q8_int8_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+MMQ_OK, MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_LDS, MMQ_E_DEVICE, MMQ_E_HIP = range(6)
+MMQ_TILE_AUTO, MMQ_TILE_LARGE, MMQ_TILE_SMALL = 0, 1, 2
+(MMQ_REASON_NONE, MMQ_REASON_LARGE, MMQ_REASON_SMALL_M, MMQ_REASON_LDS_FALLBACK,
+ MMQ_REASON_FORCED, MMQ_REASON_NO_FIT) = range(6)
+QK8, QK_K, Q4K_BLOCK_BYTES, REP_TILE_ROWS, REP_TILE_BYTES = 32, 256, 144, 32, 6144
+
+
+class mmq_options(ctypes.Structure):
+    _fields_ = [("force_tile", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("lds_budget", ctypes.c_int64)]
+
+
+class mmq_kernel_info(ctypes.Structure):
+    _fields_ = [("tile", ctypes.c_int32), ("reason", ctypes.c_int32),
+                ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
+                ("threads", ctypes.c_int32), ("fallback", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int64), ("lds_budget", ctypes.c_int64),
+                ("grid", ctypes.c_int64)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class MMQError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        detail = _lib.mmq_last_error().decode()
+        super().__init__(f"{fn}: {_lib.mmq_status_str(status).decode()}"
+                         + (f" ({detail})" if detail else ""))
+
+
+_i64, _vp, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+_SIGS = {
+    "mmq_q8_1_bytes": [_i64, _i64, ctypes.POINTER(_sz)],
+    "mmq_q4K_bytes": [_i64, _i64, ctypes.POINTER(_sz)],
+    "mmq_q4K_repacked_bytes": [_i64, _i64, ctypes.POINTER(_sz)],
+    "quantize_q8_1": [_vp, _i64, _i64, _vp, _vp],
+    "repack_q4_K": [_vp, _i64, _i64, _vp, _vp],
+    "mmq_q4K_q8_1": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
+    "mmq_q4K_q8_1_ex": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.POINTER(mmq_options)],
+    "mmq_q4K_q8_1_blockdots": [_i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp,
+                               ctypes.POINTER(mmq_options)],
+    "mmq_plan": [_i64, _i64, _i64, ctypes.POINTER(mmq_options), _i64,
+                 ctypes.POINTER(mmq_kernel_info)],
+    "mmq_last_kernel": [ctypes.POINTER(mmq_kernel_info)],
+    "mmq_status_str": [ctypes.c_int],
+    "mmq_last_error": [],
+}
+for _name, _args in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = ctypes.c_char_p if _name in ("mmq_status_str", "mmq_last_error") else ctypes.c_int
+
+
+def exported_symbols() -> list[str]:
+    """Function names declared in include/mmq.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MMQ_OK:
+        raise MMQError(fn, status)
+
+
+def _ptr(t) -> int | None:
+    """Device pointer of a tensor (or an int address, or None)."""
+    if t is None or isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _opts(force_tile: int = MMQ_TILE_AUTO, lds_budget: int = 0):
+    if force_tile == MMQ_TILE_AUTO and lds_budget == 0:
+        return None
+    return ctypes.byref(mmq_options(force_tile, 0, lds_budget))
+
+
+# ---------------------------------------------------------------- sizes
+def mmq_q8_1_bytes(M: int, K: int) -> int:
+    n = _sz()
+    _check("mmq_q8_1_bytes", _lib.mmq_q8_1_bytes(M, K, ctypes.byref(n)))
+    return n.value
+
+
+def mmq_q4K_bytes(N: int, K: int) -> int:
+    n = _sz()
+    _check("mmq_q4K_bytes", _lib.mmq_q4K_bytes(N, K, ctypes.byref(n)))
+    return n.value
+
+
+def mmq_q4K_repacked_bytes(N: int, K: int) -> int:
+    n = _sz()
+    _check("mmq_q4K_repacked_bytes", _lib.mmq_q4K_repacked_bytes(N, K, ctypes.byref(n)))
+    return n.value
+
+
+# ---------------------------------------------------------------- the hot path
+def quantize_q8_1(x, M: int, K: int, q8, stream=None) -> None:
+    """x: f32 [M, K] device tensor; q8: device buffer of mmq_q8_1_bytes(M, K) bytes."""
+    _check("quantize_q8_1", _lib.quantize_q8_1(_ptr(x), M, K, _ptr(q8), _stream(stream)))
+
+
+def repack_q4_K(w_q4K, N: int, K: int, w_rep, stream=None) -> None:
+    """w_q4K: q4_K blocks (mmq_q4K_bytes); w_rep: mmq_q4K_repacked_bytes(N, K) bytes."""
+    _check("repack_q4_K", _lib.repack_q4_K(_ptr(w_q4K), N, K, _ptr(w_rep), _stream(stream)))
+
+
+def mmq_q4K_q8_1(M: int, N: int, K: int, q8, w_rep, C, stream=None) -> None:
+    """C[M, N] (f32 device tensor) = q8 (M x K) times repacked q4_K weights (N x K)^T."""
+    _check("mmq_q4K_q8_1",
+           _lib.mmq_q4K_q8_1(M, N, K, _ptr(q8), _ptr(w_rep), _ptr(C), _stream(stream)))
+
+
+def mmq_q4K_q8_1_ex(M: int, N: int, K: int, q8, w_rep, C, stream=None,
+                    force_tile: int = MMQ_TILE_AUTO, lds_budget: int = 0) -> None:
+    _check("mmq_q4K_q8_1_ex",
+           _lib.mmq_q4K_q8_1_ex(M, N, K, _ptr(q8), _ptr(w_rep), _ptr(C), _stream(stream),
+                                _opts(force_tile, lds_budget)))
+
+
+def mmq_q4K_q8_1_blockdots(M: int, N: int, K: int, q8, w_rep, i0: int, i1: int, j0: int,
+                           j1: int, S, stream=None, force_tile: int = MMQ_TILE_AUTO,
+                           lds_budget: int = 0) -> None:
+    """S: int32 device tensor [K/32, i1-i0, j1-j0] of per-block integer dot products."""
+    _check("mmq_q4K_q8_1_blockdots",
+           _lib.mmq_q4K_q8_1_blockdots(M, N, K, _ptr(q8), _ptr(w_rep), i0, i1, j0, j1, _ptr(S),
+                                       _stream(stream), _opts(force_tile, lds_budget)))
+
+
+# ---------------------------------------------------------------- the guard
+def mmq_plan(M: int, N: int, K: int, lds_budget: int, force_tile: int = MMQ_TILE_AUTO,
+             opt_lds_budget: int = 0) -> dict:
+    info = mmq_kernel_info()
+    _check("mmq_plan", _lib.mmq_plan(M, N, K, _opts(force_tile, opt_lds_budget), lds_budget,
+                                     ctypes.byref(info)))
+    return info.as_dict()
+
+
+def mmq_last_kernel() -> dict:
+    info = mmq_kernel_info()
+    _check("mmq_last_kernel", _lib.mmq_last_kernel(ctypes.byref(info)))
+    return info.as_dict()
+
+
+def mmq_status_str(status: int) -> str:
+    return _lib.mmq_status_str(status).decode()
+
+
+def mmq_last_error() -> str:
+    return _lib.mmq_last_error().decode()
+
+
+def raw_call(name: str, *args) -> int:
+    """Call a C entry point by name with raw ctypes-compatible arguments; returns the status."""
+    return getattr(_lib, name)(*args)

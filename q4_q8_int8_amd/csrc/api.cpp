@@ -1,0 +1,293 @@
+// Host side of the C ABI declared in include/mmq.h: argument validation, the LDS-budget
+// guard, the per-device property cache and the launches. Nothing here touches the device
+// before every argument has been validated, so the validation and the guard can be
+// exercised on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "mmq.h"
+#include "mmq_internal.h"
+
+namespace {
+
+thread_local mmq_kernel_info g_last = {};
+thread_local char g_err[512] = {0};
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return MMQ_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every in-kernel 32-bit index in range
+
+struct DeviceInfo {
+  std::once_flag once;
+  int status = MMQ_OK;
+  int64_t lds_budget = 0;
+  char msg[256] = {0};
+};
+constexpr int kMaxDevices = 64;
+DeviceInfo g_dev[kMaxDevices];
+
+// Checks the current device once: it must be gfx950; records its per-workgroup LDS limit.
+int current_device(DeviceInfo** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return fail(MMQ_E_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+  if (dev >= kMaxDevices) return fail(MMQ_E_DEVICE, "device index %d out of range", dev);
+  DeviceInfo& di = g_dev[dev];
+  std::call_once(di.once, [&di, dev]() {
+    hipDeviceProp_t prop;
+    hipError_t pe = hipGetDeviceProperties(&prop, dev);
+    if (pe != hipSuccess) {
+      di.status = MMQ_E_DEVICE;
+      snprintf(di.msg, sizeof(di.msg), "hipGetDeviceProperties: %s", hipGetErrorString(pe));
+      return;
+    }
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      di.status = MMQ_E_DEVICE;
+      snprintf(di.msg, sizeof(di.msg), "device %d is %s, this library is built for gfx950", dev,
+               prop.gcnArchName);
+      return;
+    }
+    int lds = 0;
+    pe = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (pe != hipSuccess || lds <= 0) {
+      di.status = MMQ_E_DEVICE;
+      snprintf(di.msg, sizeof(di.msg), "cannot read the LDS limit: %s", hipGetErrorString(pe));
+      return;
+    }
+    di.lds_budget = lds;
+  });
+  if (di.status != MMQ_OK) return fail(di.status, "%s", di.msg);
+  *out = &di;
+  return MMQ_OK;
+}
+
+int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return fail(MMQ_E_ARG, "M, N, K must be positive (%lld, %lld, %lld)",
+                                              (long long)M, (long long)N, (long long)K);
+  if (K % MMQ_QK_K) return fail(MMQ_E_SHAPE, "K = %lld is not a multiple of 256", (long long)K);
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(MMQ_E_SHAPE, "dimension above 2^30");
+  if ((__int128)M * K > ((__int128)1 << 40) || (__int128)M * N > ((__int128)1 << 40))
+    return fail(MMQ_E_SHAPE, "operand larger than 2^40 elements");
+  return MMQ_OK;
+}
+
+int check_options(const mmq_options* opt) {
+  if (!opt) return MMQ_OK;
+  if (opt->force_tile < MMQ_TILE_AUTO || opt->force_tile > MMQ_TILE_SMALL)
+    return fail(MMQ_E_ARG, "force_tile %d is not an mmq_tile", opt->force_tile);
+  if (opt->lds_budget < 0) return fail(MMQ_E_ARG, "negative lds_budget");
+  return MMQ_OK;
+}
+
+int plan(int64_t M, int64_t N, const mmq_options* opt, int64_t budget, mmq_kernel_info* info) {
+  memset(info, 0, sizeof(*info));
+  if (opt && opt->lds_budget > 0) budget = opt->lds_budget;
+  info->lds_budget = budget;
+  const int64_t need_large = mmq::kLarge.lds_bytes();
+  const int64_t need_small = mmq::kSmall.lds_bytes();
+  const int forced = opt ? opt->force_tile : MMQ_TILE_AUTO;
+
+  int tile = 0, reason = MMQ_REASON_NONE, fallback = 0;
+  if (forced == MMQ_TILE_LARGE) {
+    if (need_large <= budget) { tile = MMQ_TILE_LARGE; reason = MMQ_REASON_FORCED; }
+  } else if (forced == MMQ_TILE_SMALL) {
+    if (need_small <= budget) { tile = MMQ_TILE_SMALL; reason = MMQ_REASON_FORCED; }
+  } else if (need_large <= budget) {
+    if (M > 64) { tile = MMQ_TILE_LARGE; reason = MMQ_REASON_LARGE; }
+    else { tile = MMQ_TILE_SMALL; reason = MMQ_REASON_SMALL_M; }
+  } else if (need_small <= budget) {
+    tile = MMQ_TILE_SMALL; reason = MMQ_REASON_LDS_FALLBACK; fallback = 1;
+  }
+  if (!tile) {
+    info->reason = MMQ_REASON_NO_FIT;
+    return fail(MMQ_E_LDS, "no GEMM tile fits %lld bytes of LDS (large needs %lld, small %lld)",
+                (long long)budget, (long long)need_large, (long long)need_small);
+  }
+  const mmq::TileShape ts = tile == MMQ_TILE_LARGE ? mmq::kLarge : mmq::kSmall;
+  const int64_t gm = (M + ts.block_m() - 1) / ts.block_m();
+  const int64_t ntiles = (N + 31) / 32;
+  const int64_t gn = (ntiles + ts.nw - 1) / ts.nw;
+  info->tile = tile;
+  info->reason = reason;
+  info->fallback = fallback;
+  info->block_m = ts.block_m();
+  info->block_n = ts.block_n();
+  info->threads = ts.threads();
+  info->lds_bytes = ts.lds_bytes();
+  info->grid = gm * gn;
+  return MMQ_OK;
+}
+
+int hip_fail(const char* what, hipError_t e) {
+  return fail(MMQ_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mmq_q8_1_bytes(int64_t M, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(MMQ_E_ARG, "bytes is NULL");
+  if (M <= 0 || K <= 0) return fail(MMQ_E_ARG, "M and K must be positive");
+  if (K % MMQ_QK8) return fail(MMQ_E_SHAPE, "K = %lld is not a multiple of 32", (long long)K);
+  if (M > kMaxDim || K > kMaxDim || (__int128)M * K > ((__int128)1 << 40))
+    return fail(MMQ_E_SHAPE, "activation matrix too large");
+  *bytes = (size_t)M * (size_t)K + (size_t)4 * (size_t)M * (size_t)(K / MMQ_QK8);
+  return ok();
+}
+
+int mmq_q4K_bytes(int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(MMQ_E_ARG, "bytes is NULL");
+  if (N <= 0 || K <= 0) return fail(MMQ_E_ARG, "N and K must be positive");
+  if (K % MMQ_QK_K) return fail(MMQ_E_SHAPE, "K = %lld is not a multiple of 256", (long long)K);
+  if (N > kMaxDim || K > kMaxDim) return fail(MMQ_E_SHAPE, "weight matrix too large");
+  *bytes = (size_t)N * (size_t)(K / MMQ_QK_K) * MMQ_Q4K_BLOCK_BYTES;
+  return ok();
+}
+
+int mmq_q4K_repacked_bytes(int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(MMQ_E_ARG, "bytes is NULL");
+  if (N <= 0 || K <= 0) return fail(MMQ_E_ARG, "N and K must be positive");
+  if (K % MMQ_QK_K) return fail(MMQ_E_SHAPE, "K = %lld is not a multiple of 256", (long long)K);
+  if (N > kMaxDim || K > kMaxDim) return fail(MMQ_E_SHAPE, "weight matrix too large");
+  *bytes = (size_t)((N + 31) / 32) * (size_t)(K / MMQ_QK_K) * MMQ_REP_TILE_BYTES;
+  return ok();
+}
+
+int quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, void* stream) {
+  size_t nb;
+  int st = mmq_q8_1_bytes(M, K, &nb);
+  if (st) return st;
+  if (!x || !q8) return fail(MMQ_E_ARG, "null device pointer");
+  if (!aligned16(x) || !aligned16(q8)) return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
+  DeviceInfo* di;
+  if ((st = current_device(&di))) return st;
+  hipError_t e = mmq::launch_quantize_q8_1(x, M, K, q8, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("quantize_q8_1 launch", e);
+  return ok();
+}
+
+int repack_q4_K(const void* w_q4K, int64_t N, int64_t K, void* w_rep, void* stream) {
+  size_t nb;
+  int st = mmq_q4K_repacked_bytes(N, K, &nb);
+  if (st) return st;
+  if (!w_q4K || !w_rep) return fail(MMQ_E_ARG, "null device pointer");
+  if (!aligned16(w_q4K) || !aligned16(w_rep)) return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
+  DeviceInfo* di;
+  if ((st = current_device(&di))) return st;
+  hipError_t e = mmq::launch_repack_q4_K(w_q4K, N, K, w_rep, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("repack_q4_K launch", e);
+  return ok();
+}
+
+int mmq_plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t lds_budget,
+             mmq_kernel_info* out) {
+  if (!out) return fail(MMQ_E_ARG, "out is NULL");
+  int st = check_gemm_shape(M, N, K);
+  if (st) return st;
+  if ((st = check_options(opt))) return st;
+  if (lds_budget <= 0 && !(opt && opt->lds_budget > 0)) return fail(MMQ_E_ARG, "lds_budget must be positive");
+  if ((st = plan(M, N, opt, lds_budget, out))) return st;
+  return ok();
+}
+
+int mmq_q4K_q8_1_ex(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+                    float* C, void* stream, const mmq_options* opt) {
+  int st = check_gemm_shape(M, N, K);
+  if (st) return st;
+  if ((st = check_options(opt))) return st;
+  if (!q8 || !w_rep || !C) return fail(MMQ_E_ARG, "null device pointer");
+  if (!aligned16(q8) || !aligned16(w_rep) || !aligned16(C))
+    return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
+  DeviceInfo* di;
+  if ((st = current_device(&di))) return st;
+  mmq_kernel_info info;
+  st = plan(M, N, opt, di->lds_budget, &info);
+  g_last = info;
+  if (st) return st;
+  const mmq::TileShape ts = info.tile == MMQ_TILE_LARGE ? mmq::kLarge : mmq::kSmall;
+  const int64_t gm = (M + ts.block_m() - 1) / ts.block_m();
+  const int64_t gn = info.grid / gm;
+  hipError_t e = mmq::launch_mmq(info.tile, q8, w_rep, C, M, N, K, gm, gn, 0, 0, false, 0, 0,
+                                 0, 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("mmq_q4K_q8_1 launch", e);
+  return ok();
+}
+
+int mmq_q4K_q8_1(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep, float* C,
+                 void* stream) {
+  return mmq_q4K_q8_1_ex(M, N, K, q8, w_rep, C, stream, nullptr);
+}
+
+int mmq_q4K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+                           int64_t i0, int64_t i1, int64_t j0, int64_t j1, int32_t* S,
+                           void* stream, const mmq_options* opt) {
+  int st = check_gemm_shape(M, N, K);
+  if (st) return st;
+  if ((st = check_options(opt))) return st;
+  if (!q8 || !w_rep || !S) return fail(MMQ_E_ARG, "null device pointer");
+  if (!aligned16(q8) || !aligned16(w_rep) || !aligned16(S))
+    return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
+  if (!(0 <= i0 && i0 < i1 && i1 <= M && 0 <= j0 && j0 < j1 && j1 <= N))
+    return fail(MMQ_E_SHAPE, "window [%lld,%lld) x [%lld,%lld) is empty or outside %lld x %lld",
+                (long long)i0, (long long)i1, (long long)j0, (long long)j1, (long long)M,
+                (long long)N);
+  DeviceInfo* di;
+  if ((st = current_device(&di))) return st;
+  mmq_kernel_info info;
+  st = plan(M, N, opt, di->lds_budget, &info);
+  g_last = info;
+  if (st) return st;
+  const mmq::TileShape ts = info.tile == MMQ_TILE_LARGE ? mmq::kLarge : mmq::kSmall;
+  const int64_t tm0 = i0 / ts.block_m();
+  const int64_t tm1 = (i1 + ts.block_m() - 1) / ts.block_m();
+  const int64_t tn0 = j0 / ts.block_n();
+  const int64_t tn1 = (j1 + ts.block_n() - 1) / ts.block_n();
+  const int64_t gm = tm1 - tm0, gn = tn1 - tn0;
+  g_last.grid = gm * gn;
+  hipError_t e = mmq::launch_mmq(info.tile, q8, w_rep, S, M, N, K, gm, gn, tm0, tn0, true, i0,
+                                 i1, j0, j1, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("mmq_q4K_q8_1_blockdots launch", e);
+  return ok();
+}
+
+int mmq_last_kernel(mmq_kernel_info* out) {
+  if (!out) return fail(MMQ_E_ARG, "out is NULL");
+  *out = g_last;
+  return MMQ_OK;
+}
+
+const char* mmq_status_str(int status) {
+  switch (status) {
+    case MMQ_OK: return "MMQ_OK";
+    case MMQ_E_ARG: return "MMQ_E_ARG: invalid argument";
+    case MMQ_E_SHAPE: return "MMQ_E_SHAPE: unsupported shape";
+    case MMQ_E_LDS: return "MMQ_E_LDS: no tile fits the LDS budget";
+    case MMQ_E_DEVICE: return "MMQ_E_DEVICE: no gfx950 device";
+    case MMQ_E_HIP: return "MMQ_E_HIP: HIP runtime error";
+    default: return "unknown mmq status";
+  }
+}
+
+const char* mmq_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// q8_1 quantize prepass: f32 activations -> int8 blocks of 32 with an f16 scale and the
+// integer block sum, the format of the r15 page ("f32-accumulate mma probe + rank-1 term2
+// rescale", section 2.1). HBM-bound: 4 bytes read and 1.125 bytes written per element.
+//
+// Mapping: 8 lanes own one 32-element block (one float4 each), so a wavefront covers 8
+// consecutive blocks = 1 KiB of contiguous input; the max and the sum are reduced with
+// xor-shuffles inside the 8-lane group.
+#include "mmq_internal.h"
+
+namespace mmq {
+namespace {
+
+__device__ __forceinline__ int quant1(float x, float id) {
+  const float p = x * id;
+  if (p != p) return 0;  // 0 * inf, only when 1/d overflowed for a block of tiny values
+  return (int)fminf(fmaxf(roundf(p), -127.0f), 127.0f);
+}
+
+__global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float4* __restrict__ x,
+                                                            uint32_t* __restrict__ qs,
+                                                            uint32_t* __restrict__ ds,
+                                                            int64_t nblocks) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t blk = t >> 3;      // all 8 lanes of a group share blk
+  const bool ok = blk < nblocks;
+  const float4 v = ok ? x[t] : make_float4(0.f, 0.f, 0.f, 0.f);
+
+  float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
+  amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+
+  const float d = amax / 127.0f;                 // IEEE division
+  const float id = d > 0.0f ? 1.0f / d : 0.0f;   // IEEE reciprocal (division)
+  const int q0 = quant1(v.x, id), q1 = quant1(v.y, id);
+  const int q2 = quant1(v.z, id), q3 = quant1(v.w, id);
+
+  int sum = q0 + q1 + q2 + q3;
+  sum += __shfl_xor(sum, 1, 8);
+  sum += __shfl_xor(sum, 2, 8);
+  sum += __shfl_xor(sum, 4, 8);
+
+  if (ok) {
+    qs[t] = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) |
+            ((uint32_t)(q2 & 0xFF) << 16) | ((uint32_t)(q3 & 0xFF) << 24);
+    if ((threadIdx.x & 7) == 0) {
+      const uint32_t hbits = __builtin_bit_cast(uint16_t, (_Float16)d);  // RNE
+      ds[blk] = hbits | ((uint32_t)(sum & 0xFFFF) << 16);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, hipStream_t s) {
+  const int64_t nblocks = M * (K / 32);
+  const int64_t threads = nblocks * 8;
+  const int64_t grid = (threads + 255) / 256;
+  uint8_t* base = static_cast<uint8_t*>(q8);
+  hipLaunchKernelGGL(quantize_q8_1_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                     reinterpret_cast<const float4*>(x), reinterpret_cast<uint32_t*>(base),
+                     reinterpret_cast<uint32_t*>(base + M * K), nblocks);
+  return hipGetLastError();
+}
+
+}  // namespace mmq

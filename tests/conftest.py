@@ -18,3 +18,14 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return GOLDEN
+
+
+def _ensure_built():
+    """Build libmmq.so in-tree when it is missing (hipcc cross-compiles without a GPU)."""
+    lib = os.path.join(ROOT, "q4_q8_int8_amd", "libmmq.so")
+    if not os.path.exists(lib):
+        from q4_q8_int8_amd.build import build
+        build()
+
+
+_ensure_built()

@@ -1,0 +1,151 @@
+"""The C-ABI library on the host (CPU only, no GPU needed).
+
+Loads libmmq.so, checks that it exports every function include/mmq.h declares, and
+exercises the size queries, the LDS-budget guard (mmq_plan) and the argument validation
+of every entry point. Validation happens before any device access, so each bad call must
+return its error code here; a well-formed call reaches the device check.
+"""
+import ctypes
+import subprocess
+
+import pytest
+
+mmq = pytest.importorskip("q4_q8_int8_amd")
+
+
+def test_exports_every_declared_symbol():
+    names = mmq.exported_symbols()
+    assert set(names) >= {"quantize_q8_1", "repack_q4_K", "mmq_q4K_q8_1", "mmq_plan"}
+    out = subprocess.run(["nm", "-D", "--defined-only", mmq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in names:
+        assert name in exported, name
+        assert hasattr(mmq._lib, name)
+
+
+def test_sizes():
+    assert mmq.mmq_q8_1_bytes(2048, 4096) == 2048 * 4096 * 9 // 8
+    assert mmq.mmq_q8_1_bytes(1, 32) == 36
+    assert mmq.mmq_q4K_bytes(4096, 4096) == 4096 * 16 * 144
+    assert mmq.mmq_q4K_repacked_bytes(4096, 4096) == 128 * 16 * 6144
+    assert mmq.mmq_q4K_repacked_bytes(33, 256) == 2 * 6144
+    assert mmq.mmq_q4K_repacked_bytes(11008, 4096) == 344 * 16 * 6144
+
+
+@pytest.mark.parametrize("fn,args,status", [
+    ("mmq_q8_1_bytes", (0, 32), mmq.MMQ_E_ARG),
+    ("mmq_q8_1_bytes", (4, 33), mmq.MMQ_E_SHAPE),
+    ("mmq_q4K_bytes", (4, 128), mmq.MMQ_E_SHAPE),
+    ("mmq_q4K_bytes", (-1, 256), mmq.MMQ_E_ARG),
+    ("mmq_q4K_repacked_bytes", (4, 300), mmq.MMQ_E_SHAPE),
+    ("mmq_q8_1_bytes", (1 << 31, 32), mmq.MMQ_E_SHAPE),
+])
+def test_size_errors(fn, args, status):
+    n = ctypes.c_size_t()
+    assert mmq.raw_call(fn, *args, ctypes.byref(n)) == status
+    assert mmq.mmq_last_error()
+
+
+def test_size_null_out():
+    assert mmq.raw_call("mmq_q8_1_bytes", 1, 32, None) == mmq.MMQ_E_ARG
+
+
+LARGE_LDS = 128 * 256 + 8 * 128 * 16 + 4 * 2048
+SMALL_LDS = 32 * 256 + 8 * 32 * 16 + 2 * 2048
+
+
+def test_plan_large_when_it_fits():
+    p = mmq.mmq_plan(2048, 4096, 4096, 160 * 1024)
+    assert p["tile"] == mmq.MMQ_TILE_LARGE and p["reason"] == mmq.MMQ_REASON_LARGE
+    assert p["fallback"] == 0 and p["lds_bytes"] == LARGE_LDS
+    assert p["block_m"] == 128 and p["block_n"] == 128 and p["threads"] == 256
+    assert p["grid"] == 16 * 32
+
+
+def test_plan_lds_fallback_and_refusal():
+    p = mmq.mmq_plan(2048, 4096, 4096, LARGE_LDS - 1)
+    assert p["tile"] == mmq.MMQ_TILE_SMALL and p["fallback"] == 1
+    assert p["reason"] == mmq.MMQ_REASON_LDS_FALLBACK and p["lds_bytes"] == SMALL_LDS
+    assert p["grid"] == 64 * 64
+    p = mmq.mmq_plan(2048, 4096, 4096, LARGE_LDS)
+    assert p["tile"] == mmq.MMQ_TILE_LARGE
+    with pytest.raises(mmq.MMQError) as e:
+        mmq.mmq_plan(2048, 4096, 4096, SMALL_LDS - 1)
+    assert e.value.status == mmq.MMQ_E_LDS
+
+
+def test_plan_small_m_and_forced_tiles():
+    p = mmq.mmq_plan(16, 4096, 4096, 160 * 1024)
+    assert p["tile"] == mmq.MMQ_TILE_SMALL and p["reason"] == mmq.MMQ_REASON_SMALL_M
+    assert p["fallback"] == 0
+    p = mmq.mmq_plan(16, 4096, 4096, 160 * 1024, force_tile=mmq.MMQ_TILE_LARGE)
+    assert p["tile"] == mmq.MMQ_TILE_LARGE and p["reason"] == mmq.MMQ_REASON_FORCED
+    p = mmq.mmq_plan(2048, 4096, 4096, 160 * 1024, force_tile=mmq.MMQ_TILE_SMALL)
+    assert p["tile"] == mmq.MMQ_TILE_SMALL and p["reason"] == mmq.MMQ_REASON_FORCED
+    with pytest.raises(mmq.MMQError) as e:   # a forced tile over budget is refused, not swapped
+        mmq.mmq_plan(2048, 4096, 4096, 160 * 1024, force_tile=mmq.MMQ_TILE_LARGE,
+                     opt_lds_budget=LARGE_LDS - 1)
+    assert e.value.status == mmq.MMQ_E_LDS
+    # the option's budget overrides the argument
+    p = mmq.mmq_plan(2048, 4096, 4096, 160 * 1024, opt_lds_budget=SMALL_LDS)
+    assert p["tile"] == mmq.MMQ_TILE_SMALL and p["lds_budget"] == SMALL_LDS
+
+
+def test_plan_ragged_grid():
+    p = mmq.mmq_plan(2047, 11008, 4096, 160 * 1024)
+    assert p["grid"] == 16 * 86
+    p = mmq.mmq_plan(1, 33, 256, 160 * 1024)
+    assert p["grid"] == 1 and p["tile"] == mmq.MMQ_TILE_SMALL
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 4096, 4096), mmq.MMQ_E_ARG),
+    ((16, 4096, 4000), mmq.MMQ_E_SHAPE),
+    ((16, -5, 4096), mmq.MMQ_E_ARG),
+])
+def test_plan_shape_errors(args, status):
+    info = mmq.mmq_kernel_info()
+    assert mmq.raw_call("mmq_plan", *args, None, 65536, ctypes.byref(info)) == status
+
+
+# well-formed-looking device addresses (never dereferenced: validation fails first)
+A = 0x10000000
+B = 0x20000000
+Cp = 0x30000000
+
+
+@pytest.mark.parametrize("call,status", [
+    (("quantize_q8_1", None, 4, 64, B, None), mmq.MMQ_E_ARG),
+    (("quantize_q8_1", A, 4, 64, None, None), mmq.MMQ_E_ARG),
+    (("quantize_q8_1", A + 4, 4, 64, B, None), mmq.MMQ_E_ARG),
+    (("quantize_q8_1", A, 4, 48, B, None), mmq.MMQ_E_SHAPE),
+    (("quantize_q8_1", A, 0, 64, B, None), mmq.MMQ_E_ARG),
+    (("repack_q4_K", A, 4, 200, B, None), mmq.MMQ_E_SHAPE),
+    (("repack_q4_K", None, 4, 256, B, None), mmq.MMQ_E_ARG),
+    (("repack_q4_K", A, 4, 256, B + 8, None), mmq.MMQ_E_ARG),
+    (("mmq_q4K_q8_1", 4, 8, 100, A, B, Cp, None), mmq.MMQ_E_SHAPE),
+    (("mmq_q4K_q8_1", 4, 8, 256, None, B, Cp, None), mmq.MMQ_E_ARG),
+    (("mmq_q4K_q8_1", 4, 8, 256, A, B, Cp + 4, None), mmq.MMQ_E_ARG),
+    (("mmq_q4K_q8_1", 0, 8, 256, A, B, Cp, None), mmq.MMQ_E_ARG),
+    (("mmq_q4K_q8_1_blockdots", 4, 8, 256, A, B, 0, 5, 0, 8, Cp, None, None), mmq.MMQ_E_SHAPE),
+    (("mmq_q4K_q8_1_blockdots", 4, 8, 256, A, B, 2, 2, 0, 8, Cp, None, None), mmq.MMQ_E_SHAPE),
+    (("mmq_q4K_q8_1_blockdots", 4, 8, 256, A, B, 0, 4, -1, 8, Cp, None, None), mmq.MMQ_E_SHAPE),
+    (("mmq_q4K_q8_1_blockdots", 4, 8, 256, A, B, 0, 4, 0, 8, None, None, None), mmq.MMQ_E_ARG),
+])
+def test_hot_path_validation(call, status):
+    assert mmq.raw_call(*call) == status
+    assert mmq.mmq_last_error() != ""
+
+
+def test_bad_options_rejected():
+    bad = mmq.mmq_options(7, 0, 0)
+    assert mmq.raw_call("mmq_q4K_q8_1_ex", 4, 8, 256, A, B, Cp, None, ctypes.byref(bad)) == mmq.MMQ_E_ARG
+    neg = mmq.mmq_options(0, 0, -1)
+    assert mmq.raw_call("mmq_q4K_q8_1_ex", 4, 8, 256, A, B, Cp, None, ctypes.byref(neg)) == mmq.MMQ_E_ARG
+
+
+def test_status_strings():
+    for s in range(6):
+        assert mmq.mmq_status_str(s).startswith("MMQ_")
+    assert "unknown" in mmq.mmq_status_str(99)
