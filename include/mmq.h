@@ -141,7 +141,7 @@ int repack_q4_K(const void* w_q4K, int64_t N, int64_t K, void* w_rep, void* stre
  * per token row as on the r16 page, section 2.1). q8 comes from quantize_q8_1 (M x K), w_rep
  * from repack_q4_K (N x K). S_ijb is computed exactly with int8 MFMA; each block's terms are
  * added to a float32 accumulator in increasing b, so the result is deterministic.
- * M, N >= 1 (any value; ragged tiles are masked), K % 256 == 0.
+ * M, N >= 1 (any value; ragged tiles are masked), K % 256 == 0, K <= 2^24, M*K < 2^31.
  * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_LDS (no tile fits), MMQ_E_DEVICE, MMQ_E_HIP.
  */
 int mmq_q4K_q8_1(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,

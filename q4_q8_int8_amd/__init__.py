@@ -14,11 +14,18 @@ import os
 import re
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmmq.so")
+# MMQ_LIBRARY may name another build of the same library (e.g. a tile-shape variant)
+LIB_PATH = os.environ.get("MMQ_LIBRARY") or os.path.join(_PKG, "libmmq.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "mmq.h")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m q4_q8_int8_amd.build`")
+# torch ships its own HIP runtime. Loading torch first makes libmmq.so's libamdhip64
+# dependency resolve to that already-loaded runtime, so the process has a single HIP runtime
+# and torch's device pointers and streams are valid in the library's calls. (Loaded the other
+# way round, the process would hold two runtimes and the second sees no device.)
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 MMQ_OK, MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_LDS, MMQ_E_DEVICE, MMQ_E_HIP = range(6)

@@ -25,6 +25,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     # keep the compiler from forming packed FP32 instructions (v_pk_fma_f32 and friends)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the epilogue reads every S on the vector ALU, and an MFMA that
+    # writes accumulation registers would cost one v_accvgpr_read per element
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
 
@@ -41,8 +44,11 @@ def _run(cmd: list[str]) -> None:
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP/C++ source and link libmmq.so; returns its path."""
+def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
+    """Compile every HIP/C++ source and link libmmq.so (or `out`); returns its path.
+
+    `defines` are extra -D options (e.g. tile-shape variants built for comparison).
+    """
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     tmp = tempfile.mkdtemp(prefix="mmq_build_")
@@ -53,17 +59,18 @@ def build(verbose: bool = False) -> str:
             obj = os.path.join(tmp, src + ".o")
             objs.append(obj)
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmds.append([HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+            cmds.append([HIPCC, *FLAGS, *[f"-D{d}" for d in defines], *lang, "-c",
+                         os.path.join(CSRC, src), "-o", obj])
         with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
             for cmd, _ in zip(cmds, ex.map(_run, cmds)):
                 if verbose:
                     print(" ".join(cmd))
-        out_tmp = LIB + ".tmp"
+        out_tmp = out + ".tmp"
         _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out_tmp])
-        os.replace(out_tmp, LIB)
+        os.replace(out_tmp, out)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":

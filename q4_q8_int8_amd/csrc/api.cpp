@@ -34,6 +34,7 @@ int ok() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every in-kernel 32-bit index in range
+constexpr int64_t kMaxK = (int64_t)1 << 24;
 
 struct DeviceInfo {
   std::once_flag once;
@@ -83,10 +84,11 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return fail(MMQ_E_ARG, "M, N, K must be positive (%lld, %lld, %lld)",
                                               (long long)M, (long long)N, (long long)K);
   if (K % MMQ_QK_K) return fail(MMQ_E_SHAPE, "K = %lld is not a multiple of 256", (long long)K);
-  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
-    return fail(MMQ_E_SHAPE, "dimension above 2^30");
-  if ((__int128)M * K > ((__int128)1 << 40) || (__int128)M * N > ((__int128)1 << 40))
-    return fail(MMQ_E_SHAPE, "operand larger than 2^40 elements");
+  if (M > kMaxDim || N > kMaxDim || K > kMaxK)
+    return fail(MMQ_E_SHAPE, "M or N above 2^30, or K above 2^24");
+  // the GEMM addresses its operands with 32-bit buffer offsets
+  if ((__int128)M * K >= ((__int128)1 << 31) || (__int128)M * N > ((__int128)1 << 40))
+    return fail(MMQ_E_SHAPE, "activations of M*K >= 2^31 bytes, or an output above 2^40 elements");
   return MMQ_OK;
 }
 

@@ -23,14 +23,20 @@ struct TileShape {
   constexpr int block_m() const { return 32 * tt; }
   constexpr int block_n() const { return 32 * nw; }
   constexpr int threads() const { return 64 * nw; }
-  // LDS: swizzled int8 token tile [BM][256], token scales float4 [8][BM], weight scales
-  // float [NW][2][8][32]
+  // LDS: int8 token tile [BM][272] (256 bytes + 16 padding per row), token scales {da, nb}
+  // float2 [8][BM] and dma float [8][BM], weight scales float [NW][2][8][32]
   constexpr int64_t lds_bytes() const {
-    return (int64_t)block_m() * 256 + (int64_t)8 * block_m() * 16 + (int64_t)nw * 2048;
+    return (int64_t)block_m() * 272 + (int64_t)8 * block_m() * 12 + (int64_t)nw * 2048;
   }
 };
 constexpr TileShape kLarge{4, 4};
 constexpr TileShape kSmall{1, 2};
+// global prefetch of the next super-block (one wavefront per SIMD) or two wavefronts per SIMD
+#ifndef MMQ_LARGE_PF
+#define MMQ_LARGE_PF 0
+#endif
+constexpr bool kLargePF = MMQ_LARGE_PF;
+constexpr bool kSmallPF = false;
 
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, hipStream_t s);
 hipError_t launch_repack_q4_K(const void* w, int64_t N, int64_t K, void* w_rep, hipStream_t s);

@@ -51,8 +51,8 @@ def test_size_null_out():
     assert mmq.raw_call("mmq_q8_1_bytes", 1, 32, None) == mmq.MMQ_E_ARG
 
 
-LARGE_LDS = 128 * 256 + 8 * 128 * 16 + 4 * 2048
-SMALL_LDS = 32 * 256 + 8 * 32 * 16 + 2 * 2048
+LARGE_LDS = 128 * 272 + 8 * 128 * 12 + 4 * 2048
+SMALL_LDS = 32 * 272 + 8 * 32 * 12 + 2 * 2048
 
 
 def test_plan_large_when_it_fits():
@@ -103,6 +103,8 @@ def test_plan_ragged_grid():
     ((0, 4096, 4096), mmq.MMQ_E_ARG),
     ((16, 4096, 4000), mmq.MMQ_E_SHAPE),
     ((16, -5, 4096), mmq.MMQ_E_ARG),
+    ((1 << 20, 64, 4096), mmq.MMQ_E_SHAPE),
+    ((4, 64, 1 << 25), mmq.MMQ_E_SHAPE),
 ])
 def test_plan_shape_errors(args, status):
     info = mmq.mmq_kernel_info()
