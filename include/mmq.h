@@ -53,7 +53,7 @@ enum mmq_status {
 /* Tile variants of the GEMM kernel (one template, two instantiations). */
 enum mmq_tile {
   MMQ_TILE_AUTO = 0,   /* let the guard choose */
-  MMQ_TILE_LARGE = 1,  /* 128 tokens x 128 output features per workgroup, 4 wavefronts */
+  MMQ_TILE_LARGE = 1,  /* 128 tokens x 256 output features per workgroup, 8 wavefronts */
   MMQ_TILE_SMALL = 2   /* 32 tokens x 64 output features per workgroup, 2 wavefronts */
 };
 
@@ -90,8 +90,9 @@ typedef struct mmq_kernel_info {
 
 /* ---------------------------------------------------------------- sizes (host only) */
 
-/* Bytes of a q8_1 buffer for M x K activations: M*K int8 values followed by M*(K/32)
- * 32-bit scale words. K must be a positive multiple of 32. */
+/* Bytes of a q8_1 buffer for M x K activations (layout at quantize_q8_1): M*K int8 values,
+ * M*(K/32) 32-bit scale words, padding to 256 bytes, M*(K/32) float pairs.
+ * K must be a positive multiple of 32. */
 int mmq_q8_1_bytes(int64_t M, int64_t K, size_t* bytes);
 
 /* Bytes of q4_K weights N x K in the GGUF layout: N*(K/256)*144. K % 256 == 0. */
@@ -112,7 +113,11 @@ int mmq_q4K_repacked_bytes(int64_t N, int64_t K, size_t* bytes);
  * Output layout of q8 (mmq_q8_1_bytes(M, K) bytes):
  *   bytes [0, M*K):          int8 q, row-major [M][K]
  *   bytes [M*K, M*K*9/8):    uint32 words [M][K/32]: bits 0..15 = f16 bits of da,
- *                            bits 16..31 = sa as a signed 16-bit integer (|sa| <= 4064).
+ *                            bits 16..31 = sa as a signed 16-bit integer (|sa| <= 4064)
+ *                            (the packed da/sa word of the r15 page, section 3.2)
+ *   up to P = the next multiple of 256: padding (not written)
+ *   bytes [P, P + 8*M*K/32): float pairs {da, da*sa} [K/32][M] (block-major): the rescale's
+ *                            row factors, exact in float32, in the order the GEMM stages them.
  * Preconditions: finite x with |x| <= 8.3e6 (so that amax/127 fits f16). K % 32 == 0.
  * Errors: MMQ_E_ARG (null pointer, M or K <= 0), MMQ_E_SHAPE (K % 32, size overflow),
  *         MMQ_E_DEVICE, MMQ_E_HIP.

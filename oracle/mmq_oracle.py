@@ -96,16 +96,26 @@ def quantize_q8_1(x) -> Q8:
 def q8_1_image(q: Q8) -> np.ndarray:
     """Byte image of quantized activations as the library stores them.
 
-    qs int8 [M][K] row-major, followed by one 32-bit word per (row, 32-block),
-    [M][K/32]: low 16 bits = f16 bits of da, high 16 bits = sa as a signed 16-bit
-    integer. The packed scale word is the token-pair staging word of the r15 page
-    (§3.2, the wide kernel's uint2-packed da/sa).
+    1. qs int8 [M][K] row-major;
+    2. one 32-bit word per (row, 32-block), [M][K/32]: low 16 bits = f16 bits of da, high
+       16 bits = sa as a signed 16-bit integer (the token-pair staging word of the r15 page,
+       §3.2, the wide kernel's uint2-packed da/sa);
+    3. zero padding up to a multiple of 256 bytes;
+    4. the row factors of the rescale as float32 pairs {da, da*sa}, block-major [K/32][M]
+       (da*sa is the folded row factor of term2, r16 page §2.1; both values are exact in f32).
     """
     M, K = q.qs.shape
+    nb = K // QK8
     words = (q.da_bits.astype(np.uint32)
              | ((q.sa.astype(np.int32) & 0xFFFF).astype(np.uint32) << np.uint32(16)))
-    return np.concatenate([q.qs.reshape(-1).view(np.uint8),
+    head = np.concatenate([q.qs.reshape(-1).view(np.uint8),
                            words.astype("<u4").reshape(-1).view(np.uint8)])
+    pad = (-head.size) % 256
+    da = f16_decode(q.da_bits)                                  # exact f64
+    dma = da * q.sa.astype(np.float64)                          # exact: <= 23 significant bits
+    planes = np.stack([da.T, dma.T], axis=-1).astype("<f4")    # [K/32][M][2]
+    assert np.array_equal(planes.astype(np.float64), np.stack([da.T, dma.T], axis=-1))
+    return np.concatenate([head, np.zeros(pad, np.uint8), planes.reshape(-1).view(np.uint8)])
 
 
 # ----------------------------------------------------------------------------- q4_K

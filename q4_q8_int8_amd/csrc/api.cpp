@@ -66,14 +66,20 @@ int current_device(DeviceInfo** out) {
                prop.gcnArchName);
       return;
     }
-    int lds = 0;
+    // the per-workgroup LDS limit: the default one, or the larger one a kernel may opt in to
+    // (the GEMM launch opts in with hipFuncSetAttribute when it needs more than 64 KiB)
+    int lds = 0, lds_optin = 0;
     pe = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
     if (pe != hipSuccess || lds <= 0) {
       di.status = MMQ_E_DEVICE;
       snprintf(di.msg, sizeof(di.msg), "cannot read the LDS limit: %s", hipGetErrorString(pe));
       return;
     }
-    di.lds_budget = lds;
+    if (hipDeviceGetAttribute(&lds_optin, hipDeviceAttributeSharedMemPerBlockOptin, dev) !=
+        hipSuccess)
+      lds_optin = 0;
+    (void)hipGetLastError();  // an unsupported attribute query leaves no sticky error
+    di.lds_budget = lds_optin > lds ? lds_optin : lds;
   });
   if (di.status != MMQ_OK) return fail(di.status, "%s", di.msg);
   *out = &di;
@@ -153,7 +159,7 @@ int mmq_q8_1_bytes(int64_t M, int64_t K, size_t* bytes) {
   if (K % MMQ_QK8) return fail(MMQ_E_SHAPE, "K = %lld is not a multiple of 32", (long long)K);
   if (M > kMaxDim || K > kMaxDim || (__int128)M * K > ((__int128)1 << 40))
     return fail(MMQ_E_SHAPE, "activation matrix too large");
-  *bytes = (size_t)M * (size_t)K + (size_t)4 * (size_t)M * (size_t)(K / MMQ_QK8);
+  *bytes = (size_t)mmq::q8_total_bytes(M, K);
   return ok();
 }
 

@@ -16,6 +16,8 @@ constexpr int kRepTileRows = 32;
 constexpr int kRepTileBytes = 6144;
 constexpr int kRepNibBytes = 4096;
 
+constexpr int kRowStride = 272;  // LDS bytes per staged token row (256 + 16 padding)
+
 // GEMM tile shapes: TT token tiles of 32 per wavefront, NW wavefronts (one 32-row weight
 // tile each) per workgroup.
 struct TileShape {
@@ -23,20 +25,23 @@ struct TileShape {
   constexpr int block_m() const { return 32 * tt; }
   constexpr int block_n() const { return 32 * nw; }
   constexpr int threads() const { return 64 * nw; }
-  // LDS: int8 token tile [BM][272] (256 bytes + 16 padding per row), token scales {da, nb}
-  // float2 [8][BM] and dma float [8][BM], weight scales float [NW][2][8][32]
+  // LDS: two stages, each: int8 token tile [BM][272], {da, dma} float2 [8][BM], and per
+  // wavefront its dsv/dmv float [2][8][32]
   constexpr int64_t lds_bytes() const {
-    return (int64_t)block_m() * 272 + (int64_t)8 * block_m() * 12 + (int64_t)nw * 2048;
+    return 2 * ((int64_t)block_m() * kRowStride + (int64_t)block_m() * 64 + (int64_t)nw * 2048);
   }
 };
-constexpr TileShape kLarge{4, 4};
+constexpr TileShape kLarge{4, 8};
 constexpr TileShape kSmall{1, 2};
-// global prefetch of the next super-block (one wavefront per SIMD) or two wavefronts per SIMD
-#ifndef MMQ_LARGE_PF
-#define MMQ_LARGE_PF 0
-#endif
-constexpr bool kLargePF = MMQ_LARGE_PF;
-constexpr bool kSmallPF = false;
+
+// q8 buffer: int8 q [M][K], u32 scale words [M][K/32], then (at a 256-byte boundary) the
+// GEMM's scale plane float2 {da, da*sa} [K/32][M].
+__host__ __device__ constexpr int64_t q8_planes_offset(int64_t M, int64_t K) {
+  return ((M * K + 4 * M * (K / 32)) + 255) / 256 * 256;
+}
+__host__ __device__ constexpr int64_t q8_total_bytes(int64_t M, int64_t K) {
+  return q8_planes_offset(M, K) + 8 * M * (K / 32);
+}
 
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, hipStream_t s);
 hipError_t launch_repack_q4_K(const void* w, int64_t N, int64_t K, void* w_rep, hipStream_t s);

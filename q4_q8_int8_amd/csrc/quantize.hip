@@ -1,6 +1,9 @@
 // q8_1 quantize prepass: f32 activations -> int8 blocks of 32 with an f16 scale and the
 // integer block sum, the format of the r15 page ("f32-accumulate mma probe + rank-1 term2
-// rescale", section 2.1). HBM-bound: 4 bytes read and 1.125 bytes written per element.
+// rescale", section 2.1), computed "for free" by the prepass as on that page (section 2.1).
+// It also writes the GEMM's scale plane {da, da*sa} as f32 in block-major order, so that the
+// GEMM stages it with direct-to-LDS loads and never converts. HBM-bound: 4 bytes read and
+// 1.375 bytes written per element.
 //
 // Mapping: 8 lanes own one 32-element block (one float4 each), so a wavefront covers 8
 // consecutive blocks = 1 KiB of contiguous input; the max and the sum are reduced with
@@ -19,7 +22,8 @@ __device__ __forceinline__ int quant1(float x, float id) {
 __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float4* __restrict__ x,
                                                             uint32_t* __restrict__ qs,
                                                             uint32_t* __restrict__ ds,
-                                                            int64_t nblocks) {
+                                                            float2* __restrict__ planes,
+                                                            int64_t nblocks, int M, int kb) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t blk = t >> 3;      // all 8 lanes of a group share blk
   const bool ok = blk < nblocks;
@@ -44,8 +48,13 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float4* __rest
     qs[t] = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) |
             ((uint32_t)(q2 & 0xFF) << 16) | ((uint32_t)(q3 & 0xFF) << 24);
     if ((threadIdx.x & 7) == 0) {
-      const uint32_t hbits = __builtin_bit_cast(uint16_t, (_Float16)d);  // RNE
+      const _Float16 dh = (_Float16)d;  // RNE
+      const uint32_t hbits = __builtin_bit_cast(uint16_t, dh);
       ds[blk] = hbits | ((uint32_t)(sum & 0xFFFF) << 16);
+      // the GEMM's scale plane, block-major: {da, da * sa}, both exact in f32
+      const int64_t row = blk / kb, b = blk - row * kb;
+      const float da = (float)dh;
+      planes[b * M + row] = make_float2(da, da * (float)sum);
     }
   }
 }
@@ -59,7 +68,9 @@ hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, 
   uint8_t* base = static_cast<uint8_t*>(q8);
   hipLaunchKernelGGL(quantize_q8_1_kernel, dim3((unsigned)grid), dim3(256), 0, s,
                      reinterpret_cast<const float4*>(x), reinterpret_cast<uint32_t*>(base),
-                     reinterpret_cast<uint32_t*>(base + M * K), nblocks);
+                     reinterpret_cast<uint32_t*>(base + M * K),
+                     reinterpret_cast<float2*>(base + q8_planes_offset(M, K)), nblocks, (int)M,
+                     (int)(K / 32));
   return hipGetLastError();
 }
 

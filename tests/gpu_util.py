@@ -24,7 +24,7 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
 
 def gpu_quantize(x: np.ndarray) -> torch.Tensor:
     M, K = x.shape
-    q8 = torch.empty(mmq.mmq_q8_1_bytes(M, K), dtype=torch.uint8, device="cuda")
+    q8 = torch.zeros(mmq.mmq_q8_1_bytes(M, K), dtype=torch.uint8, device="cuda")  # padding = 0
     mmq.quantize_q8_1(to_dev(x), M, K, q8)
     torch.cuda.synchronize()
     return q8

@@ -25,8 +25,9 @@ def test_exports_every_declared_symbol():
 
 
 def test_sizes():
-    assert mmq.mmq_q8_1_bytes(2048, 4096) == 2048 * 4096 * 9 // 8
-    assert mmq.mmq_q8_1_bytes(1, 32) == 36
+    assert mmq.mmq_q8_1_bytes(2048, 4096) == 2048 * 4096 * 9 // 8 + 8 * 2048 * 128
+    assert mmq.mmq_q8_1_bytes(1, 32) == 256 + 8
+    assert mmq.mmq_q8_1_bytes(3, 96) == 512 + 8 * 3 * 3
     assert mmq.mmq_q4K_bytes(4096, 4096) == 4096 * 16 * 144
     assert mmq.mmq_q4K_repacked_bytes(4096, 4096) == 128 * 16 * 6144
     assert mmq.mmq_q4K_repacked_bytes(33, 256) == 2 * 6144
@@ -51,16 +52,16 @@ def test_size_null_out():
     assert mmq.raw_call("mmq_q8_1_bytes", 1, 32, None) == mmq.MMQ_E_ARG
 
 
-LARGE_LDS = 128 * 272 + 8 * 128 * 12 + 4 * 2048
-SMALL_LDS = 32 * 272 + 8 * 32 * 12 + 2 * 2048
+LARGE_LDS = 2 * (128 * 272 + 128 * 64 + 8 * 2048)
+SMALL_LDS = 2 * (32 * 272 + 32 * 64 + 2 * 2048)
 
 
 def test_plan_large_when_it_fits():
     p = mmq.mmq_plan(2048, 4096, 4096, 160 * 1024)
     assert p["tile"] == mmq.MMQ_TILE_LARGE and p["reason"] == mmq.MMQ_REASON_LARGE
     assert p["fallback"] == 0 and p["lds_bytes"] == LARGE_LDS
-    assert p["block_m"] == 128 and p["block_n"] == 128 and p["threads"] == 256
-    assert p["grid"] == 16 * 32
+    assert p["block_m"] == 128 and p["block_n"] == 256 and p["threads"] == 512
+    assert p["grid"] == 16 * 16
 
 
 def test_plan_lds_fallback_and_refusal():
@@ -94,7 +95,7 @@ def test_plan_small_m_and_forced_tiles():
 
 def test_plan_ragged_grid():
     p = mmq.mmq_plan(2047, 11008, 4096, 160 * 1024)
-    assert p["grid"] == 16 * 86
+    assert p["grid"] == 16 * 43
     p = mmq.mmq_plan(1, 33, 256, 160 * 1024)
     assert p["grid"] == 1 and p["tile"] == mmq.MMQ_TILE_SMALL
 

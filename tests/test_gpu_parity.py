@@ -183,7 +183,7 @@ def test_mmq_lds_fallback_reported():
     w, f = synth.q4k_weights("random_fields", 64, 512, 2)
     q8 = gpu_quantize(x)
     rep = gpu_repack(w, 64, 512)
-    large_lds = 128 * 272 + 8 * 128 * 12 + 4 * 2048
+    large_lds = 2 * (128 * 272 + 128 * 64 + 8 * 2048)
     say("mmq lds fallback")
     C = gpu_mmq(96, 64, 512, q8, rep, lds_budget=large_lds - 1)
     info = mmq.mmq_last_kernel()

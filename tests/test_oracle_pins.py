@@ -144,15 +144,21 @@ def test_q8_1_image_layout():
     x = synth.activations("normal", 3, 64, 5)
     q = oracle.quantize_q8_1(x)
     img = oracle.q8_1_image(q)
-    assert img.dtype == np.uint8 and img.size == 3 * 64 + 4 * 3 * 2
+    assert img.dtype == np.uint8 and img.size == 256 + 3 * 2 * 8
     assert np.array_equal(img[:192].view(np.int8).reshape(3, 64), q.qs)
-    words = img[192:].view("<u4").reshape(3, 2)
+    words = img[192:216].view("<u4").reshape(3, 2)
+    assert np.all(img[216:256] == 0)
+    planes = img[256:].view("<f4").reshape(2, 3, 2)            # [block][row][da, da*sa]
     for i in range(3):
         for b in range(2):
             w = int(words[i, b])
             assert w & 0xFFFF == int(q.da_bits[i, b])
             hi = w >> 16
-            assert (hi - 65536 if hi >= 32768 else hi) == int(q.sa[i, b])
+            sa = hi - 65536 if hi >= 32768 else hi
+            assert sa == int(q.sa[i, b])
+            da = Fraction(float(np.uint16(w & 0xFFFF).view(np.float16)))
+            assert Fraction(float(planes[b, i, 0])) == da
+            assert Fraction(float(planes[b, i, 1])) == da * sa
 
 
 # ----------------------------------------------------------------------------- q4_K
