@@ -48,7 +48,7 @@ enum mmq_status {
 #define MMQ_QK_K 256             /* q4_K super-block length */
 #define MMQ_Q4K_BLOCK_BYTES 144  /* bytes of one q4_K super-block */
 #define MMQ_REP_TILE_ROWS 32     /* weight rows per repacked tile */
-#define MMQ_REP_TILE_BYTES 6144  /* bytes per (repacked tile, super-block) */
+#define MMQ_REP_TILE_BYTES 6656  /* bytes per (repacked tile, super-block) */
 
 /* Tile variants of the GEMM kernel (one template, two instantiations). */
 enum mmq_tile {
@@ -91,14 +91,14 @@ typedef struct mmq_kernel_info {
 /* ---------------------------------------------------------------- sizes (host only) */
 
 /* Bytes of a q8_1 buffer for M x K activations (layout at quantize_q8_1): M*K int8 values,
- * M*(K/32) 32-bit scale words, padding to 256 bytes, M*(K/32) float pairs.
- * K must be a positive multiple of 32. */
+ * M*(K/32) 32-bit scale words, padding to 256 bytes, M*(K/32) floats, padding to 256 bytes,
+ * 48*M*ceil(K/256) bytes of bf16 pieces. K must be a positive multiple of 32. */
 int mmq_q8_1_bytes(int64_t M, int64_t K, size_t* bytes);
 
 /* Bytes of q4_K weights N x K in the GGUF layout: N*(K/256)*144. K % 256 == 0. */
 int mmq_q4K_bytes(int64_t N, int64_t K, size_t* bytes);
 
-/* Bytes of repacked q4_K weights: ceil(N/32)*(K/256)*6144. K % 256 == 0. */
+/* Bytes of repacked q4_K weights: ceil(N/32)*(K/256)*6656. K % 256 == 0. */
 int mmq_q4K_repacked_bytes(int64_t N, int64_t K, size_t* bytes);
 
 /* ---------------------------------------------------------------- the hot path */
@@ -116,8 +116,15 @@ int mmq_q4K_repacked_bytes(int64_t N, int64_t K, size_t* bytes);
  *                            bits 16..31 = sa as a signed 16-bit integer (|sa| <= 4064)
  *                            (the packed da/sa word of the r15 page, section 3.2)
  *   up to P = the next multiple of 256: padding (not written)
- *   bytes [P, P + 8*M*K/32): float pairs {da, da*sa} [K/32][M] (block-major): the rescale's
- *                            row factors, exact in float32, in the order the GEMM stages them.
+ *   bytes [P, P + 4*M*K/32): float da [K/32][M] (block-major), the token factor of term1
+ *   up to Q = the next multiple of 256: padding (not written)
+ *   bytes [Q, Q + 48*M*ceil(K/256)): uint16 bf16 pieces [K/256 rounded up][3][M][8]: piece
+ *                            i of da*sa of row r, block 8s+e at [s][i][r][e]. da*sa is the
+ *                            folded row factor of term2 (r16 page, section 2.1), exact in
+ *                            float32; the pieces are p0 = bf16_rne(v), p1 = bf16_rne(v - p0),
+ *                            p2 = v - p0 - p1, which sum to v exactly (a non-finite v is
+ *                            stored as {top 16 bits of v, 0, 0}). Slots of blocks past K/32
+ *                            are not written.
  * Preconditions: finite x with |x| <= 8.3e6 (so that amax/127 fits f16). K % 32 == 0.
  * Errors: MMQ_E_ARG (null pointer, M or K <= 0), MMQ_E_SHAPE (K % 32, size overflow),
  *         MMQ_E_DEVICE, MMQ_E_HIP.
@@ -127,13 +134,14 @@ int quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, void* stream);
 /*
  * repack_q4_K: q4_K weights (GGUF layout, [N][K/256] super-blocks of 144 bytes, the fields of
  * the r15 page, section 2.1) -> the GEMM's layout. Run once per weight matrix.
- * Output (mmq_q4K_repacked_bytes(N, K) bytes): one 6144-byte record per (tile t of 32 weight
+ * Output (mmq_q4K_repacked_bytes(N, K) bytes): one 6656-byte record per (tile t of 32 weight
  * rows, super-block s), records ordered [t][s]; rows N..32*ceil(N/32)-1 are zero. Record:
  *   bytes [0, 4096):   nibbles, [g 0..3][h 0..1][j 0..31][16 bytes] = bytes 32g+16h .. +15 of
  *                      the 128 nibble bytes of row 32t+j (low nibble: sub-block 2g, element
  *                      16h+e; high nibble: sub-block 2g+1, element 16h+e)
  *   bytes [4096, 5120): float dsv[b 0..7][j 0..31] = d*sc of sub-block b of row 32t+j
- *   bytes [5120, 6144): float dmv[b 0..7][j 0..31] = -(dmin*m)
+ *   bytes [5120, 6656): uint16 bf16 pieces [i 0..2][j 0..31][b 0..7] of dmv = -(dmin*m),
+ *                       split as the pieces of da*sa at quantize_q8_1 (they sum to dmv)
  * Both scale products are exact in float32.
  * Errors: MMQ_E_ARG, MMQ_E_SHAPE (K % 256), MMQ_E_DEVICE, MMQ_E_HIP.
  */
@@ -144,8 +152,12 @@ int repack_q4_K(const void* w_q4K, int64_t N, int64_t K, void* w_rep, void* stre
  *   sum over 32-blocks b of  da_ib*dsv_jb*S_ijb  +  dmv_jb*(da_ib*sa_ib)
  * (the two-term rescale of the r15 page, section 2.1, with the row factor da*sa folded once
  * per token row as on the r16 page, section 2.1). q8 comes from quantize_q8_1 (M x K), w_rep
- * from repack_q4_K (N x K). S_ijb is computed exactly with int8 MFMA; each block's terms are
- * added to a float32 accumulator in increasing b, so the result is deterministic.
+ * from repack_q4_K (N x K). S_ijb is computed exactly with int8 MFMA and term1 of each block
+ * is added to a float32 accumulator in increasing b. term2 of each super-block is added as
+ * three bf16 matrix products of the pieces of dmv and da*sa (six of the nine piece pairs:
+ * every product is exact, the three dropped pairs are below 2^-17 of |dmv*da*sa| per
+ * block), after the term1 of its blocks 1, 3 and 5. The order is fixed, so the result is
+ * deterministic and the same for every tile variant.
  * M, N >= 1 (any value; ragged tiles are masked), K % 256 == 0, K <= 2^24, M*K < 2^31.
  * Errors: MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_LDS (no tile fits), MMQ_E_DEVICE, MMQ_E_HIP.
  */

@@ -93,6 +93,35 @@ def quantize_q8_1(x) -> Q8:
     return Q8(qs=q.reshape(M, K), da_bits=f16_encode(d), sa=sa)
 
 
+def bf16_pieces(v) -> np.ndarray:
+    """Three bfloat16 values summing exactly to each float32 v, as uint16 bits [..., 3].
+
+    A storage form (not part of the method): the library keeps the two rank-1 factors of
+    term2 in this form so that a bf16 matrix instruction can multiply them. For finite v:
+        p0 = bf16_rne(v), p1 = bf16_rne(v - p0), p2 = v - p0 - p1,
+    where bf16_rne rounds a float32 to its top 16 bits, to nearest with ties to even.
+    Both differences are exact (each operand pair is within a factor of two), and p2 has
+    few enough significant bits to be a bfloat16 whenever v has at most 23, which covers
+    every da*sa and every dmin*m. A non-finite v is stored as {top 16 bits of v, 0, 0}.
+    """
+    v = np.ascontiguousarray(v, dtype=np.float32)
+
+    def rne_bits(x):
+        b = x.view(np.uint32).astype(np.uint64)
+        return ((b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+
+    with np.errstate(invalid="ignore", over="ignore"):   # non-finite v: replaced below
+        a = rne_bits(v)
+        r = (v - a.view(np.float32)).astype(np.float32)
+        b = rne_bits(r)
+        c = (r - b.view(np.float32)).astype(np.float32)
+    out = np.stack([a >> 16, b >> 16, c.view(np.uint32) >> 16], axis=-1).astype(np.uint16)
+    bad = ~np.isfinite(v)
+    out[bad] = 0
+    out[bad, 0] = (v[bad].view(np.uint32) >> 16).astype(np.uint16)
+    return out
+
+
 def q8_1_image(q: Q8) -> np.ndarray:
     """Byte image of quantized activations as the library stores them.
 
@@ -101,24 +130,34 @@ def q8_1_image(q: Q8) -> np.ndarray:
        16 bits = sa as a signed 16-bit integer (the token-pair staging word of the r15 page,
        §3.2, the wide kernel's uint2-packed da/sa);
     3. zero padding up to a multiple of 256 bytes;
-    4. the row factors of the rescale as float32 pairs {da, da*sa}, block-major [K/32][M]
-       (da*sa is the folded row factor of term2, r16 page §2.1; both values are exact in f32).
+    4. da as float32, block-major [K/32][M] (the token factor of term1);
+    5. zero padding up to a multiple of 256 bytes;
+    6. the folded row factor of term2, da*sa (r16 page §2.1, exact in float32), as the three
+       bf16 pieces of bf16_pieces, [ceil(K/256)][3][M][8]: piece i of row r, block 8s+e at
+       [s][i][r][e]; slots of blocks past K/32 are zero.
     """
     M, K = q.qs.shape
     nb = K // QK8
+    nsb = -(-nb // 8)
     words = (q.da_bits.astype(np.uint32)
              | ((q.sa.astype(np.int32) & 0xFFFF).astype(np.uint32) << np.uint32(16)))
     head = np.concatenate([q.qs.reshape(-1).view(np.uint8),
                            words.astype("<u4").reshape(-1).view(np.uint8)])
-    pad = (-head.size) % 256
     da = f16_decode(q.da_bits)                                  # exact f64
     dma = da * q.sa.astype(np.float64)                          # exact: <= 23 significant bits
-    planes = np.stack([da.T, dma.T], axis=-1).astype("<f4")    # [K/32][M][2]
-    assert np.array_equal(planes.astype(np.float64), np.stack([da.T, dma.T], axis=-1))
-    return np.concatenate([head, np.zeros(pad, np.uint8), planes.reshape(-1).view(np.uint8)])
+    assert np.array_equal(dma.astype(np.float32).astype(np.float64), dma)
+    plane = np.ascontiguousarray(da.T).astype("<f4").reshape(-1).view(np.uint8)
+    pieces = np.zeros((nsb, 3, M, 8), "<u2")
+    pc = bf16_pieces(dma.astype(np.float32))                    # [M][K/32][3]
+    for b in range(nb):
+        pieces[b // 8, :, :, b % 8] = pc[:, b, :].T
+
+    def pad256(a):
+        return np.concatenate([a, np.zeros((-a.size) % 256, np.uint8)])
+
+    return np.concatenate([pad256(head), pad256(plane), pieces.reshape(-1).view(np.uint8)])
 
 
-# ----------------------------------------------------------------------------- q4_K
 def decode_q4_K(blocks) -> Q4K:
     """Decode q4_K super-blocks u8 [N, K/256, 144] into their fields [r15 §2.1].
 

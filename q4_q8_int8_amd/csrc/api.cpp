@@ -177,6 +177,7 @@ int mmq_q4K_repacked_bytes(int64_t N, int64_t K, size_t* bytes) {
   if (N <= 0 || K <= 0) return fail(MMQ_E_ARG, "N and K must be positive");
   if (K % MMQ_QK_K) return fail(MMQ_E_SHAPE, "K = %lld is not a multiple of 256", (long long)K);
   if (N > kMaxDim || K > kMaxDim) return fail(MMQ_E_SHAPE, "weight matrix too large");
+  static_assert(MMQ_REP_TILE_BYTES == mmq::kRepTileBytes, "repacked record size");
   *bytes = (size_t)((N + 31) / 32) * (size_t)(K / MMQ_QK_K) * MMQ_REP_TILE_BYTES;
   return ok();
 }

@@ -49,6 +49,7 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Raw buffer descriptor over [p, p + bytes): reads at offsets >= bytes return zero.
@@ -59,25 +60,56 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+// The same descriptor as four SGPRs, for the direct-to-LDS load below.
+__device__ __forceinline__ v4i make_rsrc_sgpr(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
 // 16 bytes per lane from the buffer at `off` into LDS at lds_base + 16 * lane (lds_base is
-// wave-uniform); completion is tracked by the vector-memory counter.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds_base, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_base, 16, (int)off, 0, 0, 0);
+// wave-uniform); completion is tracked by the vector-memory counter and waited for
+// explicitly before the barrier that ends a stage. The instruction is issued from inline
+// assembly on purpose: the compiler cannot tell which LDS bytes such a load writes, so for
+// the intrinsic it waits for every outstanding one before the next LDS read, which would
+// stall each wavefront on its own prefetch at the start of every stage.
+__device__ __forceinline__ void dma16(v4i r, uint8_t* lds_base, uint32_t off) {
+  const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)lds_base);
+  int saved;  // m0 is reserved by the compiler: restore it after use
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(off), "s"(r)
+      : "memory");
 }
 
 template <int TT, int NW, bool STORE_S>
 __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
-    const int8_t* __restrict__ qs, const float2* __restrict__ planes,
+    const int8_t* __restrict__ qs, const float* __restrict__ da_plane,
+    const uint16_t* __restrict__ tpieces,
     const uint8_t* __restrict__ wrep, void* __restrict__ out, int M, int N, int K, int gm,
     int tm0, int tn0, int i0, int i1, int j0, int j1) {
   constexpr int BM = 32 * TT;
   constexpr int NS = 8 * TT;                      // (block, token tile) steps per super-block
   constexpr int A_BYTES = BM * kRowStride;        // token tile
-  constexpr int P_BYTES = BM * 64;                // {da, dma} [8][BM]
-  constexpr int STAGE = A_BYTES + P_BYTES + NW * 2048;
+  constexpr int DA_BYTES = BM * 32;               // da [8][BM]
+  constexpr int TP_BYTES = BM * 48;               // token pieces of da*sa [3][BM][8]
+  constexpr int W_BYTES = kRepDsvBytes + kRepPieceBytes;  // per wavefront: dsv, dmv pieces
+  constexpr int STAGE = A_BYTES + DA_BYTES + TP_BYTES + NW * W_BYTES;
+  static_assert(STAGE == TileShape{TT, NW}.stage_bytes(), "LDS stage layout");
   constexpr int A_SLOTS = BM * (kRowStride / 16);  // 16-byte slots of the token tile
   constexpr int A_DMA = (A_SLOTS + 63) / 64;       // wavefront-wide DMA instructions
   constexpr int A_PER_WAVE = (A_DMA + NW - 1) / NW;
+  constexpr int TP_SLOTS = 3 * BM;                 // 16-byte slots of the token pieces
+  constexpr int TP_DMA = (TP_SLOTS + 63) / 64;
+  constexpr int TP_PER_WAVE = (TP_DMA + NW - 1) / NW;
 
   extern __shared__ __align__(16) uint8_t smem[];
 
@@ -96,10 +128,12 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   const int wt = wt_ok ? wt_raw : ntiles - 1;  // idle wavefronts still stage and sync
   const int nsb = K >> 8;
   const int kb = K >> 5;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qs, (uint32_t)M * (uint32_t)K);
-  const __amdgpu_buffer_rsrc_t rp = make_rsrc(planes, (uint32_t)M * (uint32_t)kb * 8u);
-  const __amdgpu_buffer_rsrc_t rw =
-      make_rsrc(wrep + (size_t)wt * nsb * kRepTileBytes, (uint32_t)nsb * kRepTileBytes);
+  const v4i rq = make_rsrc_sgpr(qs, (uint32_t)M * (uint32_t)K);
+  const v4i rda = make_rsrc_sgpr(da_plane, (uint32_t)M * (uint32_t)kb * 4u);
+  const v4i rtp = make_rsrc_sgpr(tpieces, (uint32_t)M * (uint32_t)nsb * 48u);
+  const uint8_t* wtile = wrep + (size_t)wt * nsb * kRepTileBytes;
+  const v4i rwd = make_rsrc_sgpr(wtile, (uint32_t)nsb * kRepTileBytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wtile, (uint32_t)nsb * kRepTileBytes);
 
   // Token-tile DMA slots of this lane: slot q = 64*k + lane holds chunk q % 17 of row q / 17;
   // chunk 16 is the row's padding and reads past the end (zero), as do rows past M.
@@ -113,6 +147,18 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
     a_act[j] = k < A_DMA && q < A_SLOTS;
     a_off[j] = c < 16 ? (uint32_t)(m0 + row) * (uint32_t)K + c * 16 : (uint32_t)M * (uint32_t)K;
   }
+  // Token-piece DMA slots: slot q = 64*k + lane holds piece q / BM of token m0 + q % BM; the
+  // pieces of super-block s sit at [s][piece][M][8] in memory and [piece][BM][8] in LDS.
+  uint32_t tp_off[TP_PER_WAVE];
+  bool tp_act[TP_PER_WAVE];
+#pragma unroll
+  for (int j = 0; j < TP_PER_WAVE; ++j) {
+    const int k = wave + j * NW;
+    const int q = k * 64 + lane;
+    const int pc = q / BM, r = q - pc * BM;
+    tp_act[j] = k < TP_DMA && q < TP_SLOTS;
+    tp_off[j] = ((uint32_t)pc * (uint32_t)M + (uint32_t)(m0 + r)) * 16u;
+  }
   auto issue_stage = [&](int s, int p) {
     uint8_t* st = smem + p * STAGE;
 #pragma unroll
@@ -120,16 +166,26 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
       const int k = wave + j * NW;
       if (k < A_DMA && a_act[j]) dma16(rq, st + k * 1024, a_off[j] + (uint32_t)s * 256);
     }
-    // {da, dma} of blocks 8s..8s+7 for rows m0..m0+BM-1: BM/2 lanes per block
+    // da of blocks 8s..8s+7 for rows m0..m0+BM-1: BM/4 lanes per block
 #pragma unroll
     for (int b = wave; b < 8; b += NW)
-      if (lane < BM / 2)
-        dma16(rp, st + A_BYTES + b * BM * 8,
-              (((uint32_t)s * 8 + b) * (uint32_t)M + m0) * 8u + lane * 16);
-    // this wavefront's dsv [8][32] and dmv [8][32]
-    uint8_t* sw = st + A_BYTES + P_BYTES + wave * 2048;
-    dma16(rw, sw, (uint32_t)s * kRepTileBytes + kRepNibBytes + lane * 16);
-    dma16(rw, sw + 1024, (uint32_t)s * kRepTileBytes + kRepNibBytes + 1024 + lane * 16);
+      if (lane < BM / 4)
+        dma16(rda, st + A_BYTES + b * BM * 4,
+              (((uint32_t)s * 8 + b) * (uint32_t)M + m0) * 4u + lane * 16);
+    // the token pieces of da*sa for super-block s
+#pragma unroll
+    for (int j = 0; j < TP_PER_WAVE; ++j) {
+      const int k = wave + j * NW;
+      if (k < TP_DMA && tp_act[j])
+        dma16(rtp, st + A_BYTES + DA_BYTES + k * 1024,
+              tp_off[j] + (uint32_t)s * 3u * (uint32_t)M * 16u);
+    }
+    // this wavefront's dsv [8][32] and dmv pieces [3][32][8]: 2560 contiguous bytes
+    uint8_t* sw = st + A_BYTES + DA_BYTES + TP_BYTES + wave * W_BYTES;
+    const uint32_t wo = (uint32_t)s * kRepTileBytes + kRepNibBytes + lane * 16;
+    dma16(rwd, sw, wo);
+    dma16(rwd, sw + 1024, wo + 1024);
+    if (lane < 32) dma16(rwd, sw + 2048, wo + 2048);
   };
   auto load_nibbles = [&](int s, v4i (&raw)[4]) {
 #pragma unroll
@@ -164,8 +220,10 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
 
     const uint8_t* st = smem + p * STAGE;
     const uint8_t* sArow = st + l32 * kRowStride + h * 16;
-    const float2* sP = reinterpret_cast<const float2*>(st + A_BYTES);
-    const float* sWw = reinterpret_cast<const float*>(st + A_BYTES + P_BYTES + wave * 2048);
+    const float* sDa = reinterpret_cast<const float*>(st + A_BYTES);
+    const uint8_t* sTp = st + A_BYTES + DA_BYTES;
+    const uint8_t* sW = st + A_BYTES + DA_BYTES + TP_BYTES + wave * W_BYTES;
+    const float* sWw = reinterpret_cast<const float*>(sW);
     auto wop_of = [&](int b) -> v4i {
       const v4i rr = raw[b >> 1];
       return (b & 1) ? ((rr >> 4) & 0x0F0F0F0F) : (rr & 0x0F0F0F0F);
@@ -174,7 +232,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
       const int b = n / TT, t = n % TT;
       return *reinterpret_cast<const v4i*>(sArow + t * 32 * kRowStride + b * 32);
     };
-    auto da_of = [&](int n) -> float { return sP[(n / TT) * BM + (n % TT) * 32 + l32].x; };
+    auto da_of = [&](int n) -> float { return sDa[(n / TT) * BM + (n % TT) * 32 + l32]; };
     auto dsv_of = [&](int b, float (&d)[16]) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -227,12 +285,16 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
           const float y = __builtin_fmaf(__int_as_float(D[r]), dac, nb);
           acc[t][r] = __builtin_fmaf(y, dsv[b & 1][r], acc[t][r]);
         }
-        if (b & 1) {
-          // term2 of blocks b-1 and b: lane l supplies dmv of weight row l%32 and dma of
-          // token l%32 for block b-1+l/32, a K=2 outer product added on the matrix unit
-          const float dmv = sWw[256 + (b - 1 + h) * 32 + l32];
-          const float dma = sP[(b - 1 + h) * BM + t * 32 + l32].y;
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x2f32(dmv, dma, acc[t], 0, 0, 0);
+        if (b == 1 || b == 3 || b == 5) {
+          // one third of term2 of the super-block: products of bf16 pieces (dmv piece ia,
+          // da*sa piece jb) over its 8 blocks, lane half h supplying one pair; the three
+          // instructions cover the pairs (0,0) (0,1) | (1,0) (0,2) | (1,1) (2,0)
+          const int u = b >> 1;
+          const int ia = u == 0 ? 0 : (u == 1 ? 1 - h : 1 + h);
+          const int jb = u == 0 ? h : (u == 1 ? 2 * h : 1 - h);
+          const v8bf wa = *reinterpret_cast<const v8bf*>(sW + kRepDsvBytes + (ia * 32 + l32) * 16);
+          const v8bf tb = *reinterpret_cast<const v8bf*>(sTp + (jb * BM + t * 32 + l32) * 16);
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, tb, acc[t], 0, 0, 0);
         }
       }
     }
@@ -242,24 +304,39 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   }
 
   if constexpr (!STORE_S) {
-    if (!wt_ok) return;
+    // Output tile by tile through LDS (the stage buffers are free now): lane (l32, h) holds
+    // 16 columns of one token row, which would make every store instruction touch 64
+    // rows; after the transpose 8 consecutive lanes write one token row's 128 contiguous
+    // bytes. Each wavefront uses its own 32 x 36 float region, double-buffered over t.
+    constexpr int TS = 36;  // row stride in floats: rows 36 dwords apart hit distinct banks
     float* C = static_cast<float*>(out);
-    const bool vec = (N & 3) == 0;
+    const int j0c = wt * 32;
+    const int rr = lane >> 3, c4 = lane & 7;  // read-back: rows rr + 8k, columns 4*c4..+3
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
-      const int i = m0 + t * 32 + l32;
-      if (i >= M) continue;
+      float* tile = reinterpret_cast<float*>(smem) + ((t & 1) * NW + wave) * (32 * TS);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j = wt * 32 + 8 * g + 4 * h;
-        float* p = C + (size_t)i * N + j;
-        if (vec && j + 3 < N) {
-          *reinterpret_cast<float4*>(p) =
-              make_float4(acc[t][4 * g], acc[t][4 * g + 1], acc[t][4 * g + 2], acc[t][4 * g + 3]);
-        } else {
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(tile + l32 * TS + 8 * g + 4 * h) =
+            make_float4(acc[t][4 * g], acc[t][4 * g + 1], acc[t][4 * g + 2], acc[t][4 * g + 3]);
+      __syncthreads();
+      if (wt_ok) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (j + e < N) p[e] = acc[t][4 * g + e];
+        for (int k = 0; k < 4; ++k) {
+          const int row = rr + 8 * k;
+          const int i = m0 + t * 32 + row;
+          const int j = j0c + 4 * c4;
+          if (i >= M) continue;
+          const float4 v = *reinterpret_cast<const float4*>(tile + row * TS + 4 * c4);
+          float* p = C + (size_t)i * N + j;
+          if ((N & 3) == 0 && j + 3 < N) {
+            *reinterpret_cast<float4*>(p) = v;
+          } else {
+            if (j + 0 < N) p[0] = v.x;
+            if (j + 1 < N) p[1] = v.y;
+            if (j + 2 < N) p[2] = v.z;
+            if (j + 3 < N) p[3] = v.w;
+          }
         }
       }
     }
@@ -273,7 +350,8 @@ hipError_t launch_t(const void* q8, const void* w_rep, void* out, int64_t M, int
   constexpr TileShape ts{TT, NW};
   const uint8_t* base = static_cast<const uint8_t*>(q8);
   const int8_t* qs = reinterpret_cast<const int8_t*>(base);
-  const float2* planes = reinterpret_cast<const float2*>(base + q8_planes_offset(M, K));
+  const float* da_plane = reinterpret_cast<const float*>(base + q8_planes_offset(M, K));
+  const uint16_t* tpieces = reinterpret_cast<const uint16_t*>(base + q8_pieces_offset(M, K));
   auto kern = mmq_kernel<TT, NW, STORE_S>;
   if (ts.lds_bytes() > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -282,7 +360,7 @@ hipError_t launch_t(const void* q8, const void* w_rep, void* out, int64_t M, int
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)(gm * gn)), dim3(ts.threads()), (size_t)ts.lds_bytes(),
-                     s, qs, planes, static_cast<const uint8_t*>(w_rep), out, (int)M, (int)N,
+                     s, qs, da_plane, tpieces, static_cast<const uint8_t*>(w_rep), out, (int)M, (int)N,
                      (int)K, (int)gm, (int)tm0, (int)tn0, (int)i0, (int)i1, (int)j0, (int)j1);
   return hipGetLastError();
 }

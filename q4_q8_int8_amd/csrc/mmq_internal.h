@@ -13,8 +13,12 @@ constexpr int32_t kBiasBits = 0x4B400000;
 constexpr float kBiasF = 12582912.0f;
 
 constexpr int kRepTileRows = 32;
-constexpr int kRepTileBytes = 6144;
+// Repacked weight record per (32-row tile, super-block): nibbles [4][2][32][16] (4096 B),
+// dsv f32 [8][32] (1024 B), then dmv as three bf16 pieces [3][32][8] (1536 B).
 constexpr int kRepNibBytes = 4096;
+constexpr int kRepDsvBytes = 1024;
+constexpr int kRepPieceBytes = 1536;
+constexpr int kRepTileBytes = kRepNibBytes + kRepDsvBytes + kRepPieceBytes;  // 6656
 
 constexpr int kRowStride = 272;  // LDS bytes per staged token row (256 + 16 padding)
 
@@ -25,22 +29,54 @@ struct TileShape {
   constexpr int block_m() const { return 32 * tt; }
   constexpr int block_n() const { return 32 * nw; }
   constexpr int threads() const { return 64 * nw; }
-  // LDS: two stages, each: int8 token tile [BM][272], {da, dma} float2 [8][BM], and per
-  // wavefront its dsv/dmv float [2][8][32]
-  constexpr int64_t lds_bytes() const {
-    return 2 * ((int64_t)block_m() * kRowStride + (int64_t)block_m() * 64 + (int64_t)nw * 2048);
+  // LDS: two stages, each: the int8 token tile [BM][272], da f32 [8][BM], the token
+  // pieces bf16 [3][BM][8], and per wavefront its dsv and dmv pieces (2560 bytes)
+  constexpr int64_t stage_bytes() const {
+    return (int64_t)block_m() * (kRowStride + 32 + 48) + (int64_t)nw * (kRepDsvBytes + kRepPieceBytes);
   }
+  constexpr int64_t lds_bytes() const { return 2 * stage_bytes(); }
 };
 constexpr TileShape kLarge{4, 8};
 constexpr TileShape kSmall{1, 2};
 
-// q8 buffer: int8 q [M][K], u32 scale words [M][K/32], then (at a 256-byte boundary) the
-// GEMM's scale plane float2 {da, da*sa} [K/32][M].
+// q8 buffer: int8 q [M][K], u32 scale words [M][K/32], then (each at a 256-byte boundary)
+// the GEMM's planes: da f32 [K/32][M] and dma = da*sa as three bf16 pieces per value,
+// [ceil(K/256)][3][M][8].
+__host__ __device__ constexpr int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
 __host__ __device__ constexpr int64_t q8_planes_offset(int64_t M, int64_t K) {
-  return ((M * K + 4 * M * (K / 32)) + 255) / 256 * 256;
+  return round256(M * K + 4 * M * (K / 32));
+}
+__host__ __device__ constexpr int64_t q8_pieces_offset(int64_t M, int64_t K) {
+  return round256(q8_planes_offset(M, K) + 4 * M * (K / 32));
 }
 __host__ __device__ constexpr int64_t q8_total_bytes(int64_t M, int64_t K) {
-  return q8_planes_offset(M, K) + 8 * M * (K / 32);
+  return q8_pieces_offset(M, K) + 48 * M * ((K / 32 + 7) / 8);
+}
+
+// Split of a finite float into three bfloat16 values with p1 + p2 + p3 == v exactly (each
+// piece is the top 16 bits of a float): p1 = RNE_bf16(v), p2 = RNE_bf16(v - p1),
+// p3 = v - p1 - p2. Both subtractions are exact (Sterbenz), and p3 is exact in bf16 for
+// every value of at most 23 significant bits, which covers every da*sa (an f16 times an
+// integer below 2^12) and every dmin*m (an f16 times an integer below 2^6). A non-finite
+// v gives {top 16 bits of v, 0, 0}.
+__host__ __device__ inline uint32_t bf16_rne_bits(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) & 0xFFFF0000u;
+}
+__host__ __device__ inline void bf16_split3(float v, uint16_t& p1, uint16_t& p2, uint16_t& p3) {
+  const uint32_t vb = __builtin_bit_cast(uint32_t, v);
+  if ((vb & 0x7F800000u) == 0x7F800000u) {
+    p1 = (uint16_t)(vb >> 16);
+    p2 = p3 = 0;
+    return;
+  }
+  const uint32_t a = bf16_rne_bits(v);
+  const float r = v - __builtin_bit_cast(float, a);
+  const uint32_t b = bf16_rne_bits(r);
+  const float c = r - __builtin_bit_cast(float, b);
+  p1 = (uint16_t)(a >> 16);
+  p2 = (uint16_t)(b >> 16);
+  p3 = (uint16_t)(__builtin_bit_cast(uint32_t, c) >> 16);
 }
 
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, hipStream_t s);

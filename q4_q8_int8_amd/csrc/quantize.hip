@@ -1,9 +1,11 @@
 // q8_1 quantize prepass: f32 activations -> int8 blocks of 32 with an f16 scale and the
 // integer block sum, the format of the r15 page ("f32-accumulate mma probe + rank-1 term2
 // rescale", section 2.1), computed "for free" by the prepass as on that page (section 2.1).
-// It also writes the GEMM's scale plane {da, da*sa} as f32 in block-major order, so that the
-// GEMM stages it with direct-to-LDS loads and never converts. HBM-bound: 4 bytes read and
-// 1.375 bytes written per element.
+// It also writes the GEMM's planes, so that the GEMM stages them with direct-to-LDS loads
+// and never converts: da as f32 in block-major order, and the folded row factor da*sa of
+// term2 (r16 page, "Narrow kernel gets the rank-1 fold", section 2.1) as three bf16 pieces
+// that sum to it exactly, grouped per super-block of 8 blocks for the GEMM's bf16 matrix
+// instruction. HBM-bound: 4 bytes read and about 1.44 bytes written per element.
 //
 // Mapping: 8 lanes own one 32-element block (one float4 each), so a wavefront covers 8
 // consecutive blocks = 1 KiB of contiguous input; the max and the sum are reduced with
@@ -22,7 +24,8 @@ __device__ __forceinline__ int quant1(float x, float id) {
 __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float4* __restrict__ x,
                                                             uint32_t* __restrict__ qs,
                                                             uint32_t* __restrict__ ds,
-                                                            float2* __restrict__ planes,
+                                                            float* __restrict__ da_plane,
+                                                            uint16_t* __restrict__ pieces,
                                                             int64_t nblocks, int M, int kb) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t blk = t >> 3;      // all 8 lanes of a group share blk
@@ -51,10 +54,15 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float4* __rest
       const _Float16 dh = (_Float16)d;  // RNE
       const uint32_t hbits = __builtin_bit_cast(uint16_t, dh);
       ds[blk] = hbits | ((uint32_t)(sum & 0xFFFF) << 16);
-      // the GEMM's scale plane, block-major: {da, da * sa}, both exact in f32
+      // the GEMM's planes: da block-major, and da * sa (exact in f32) as bf16 pieces
       const int64_t row = blk / kb, b = blk - row * kb;
       const float da = (float)dh;
-      planes[b * M + row] = make_float2(da, da * (float)sum);
+      da_plane[b * M + row] = da;
+      uint16_t p[3];
+      bf16_split3(da * (float)sum, p[0], p[1], p[2]);
+      uint16_t* dst = pieces + ((b >> 3) * 3 * (int64_t)M + row) * 8 + (b & 7);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) dst[j * (int64_t)M * 8] = p[j];
     }
   }
 }
@@ -69,8 +77,9 @@ hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, 
   hipLaunchKernelGGL(quantize_q8_1_kernel, dim3((unsigned)grid), dim3(256), 0, s,
                      reinterpret_cast<const float4*>(x), reinterpret_cast<uint32_t*>(base),
                      reinterpret_cast<uint32_t*>(base + M * K),
-                     reinterpret_cast<float2*>(base + q8_planes_offset(M, K)), nblocks, (int)M,
-                     (int)(K / 32));
+                     reinterpret_cast<float*>(base + q8_planes_offset(M, K)),
+                     reinterpret_cast<uint16_t*>(base + q8_pieces_offset(M, K)), nblocks,
+                     (int)M, (int)(K / 32));
   return hipGetLastError();
 }
 

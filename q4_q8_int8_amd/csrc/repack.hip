@@ -1,8 +1,9 @@
-// Offline q4_K repack: GGUF-layout super-blocks -> one 6144-byte record per (32-row weight
+// Offline q4_K repack: GGUF-layout super-blocks -> one 6656-byte record per (32-row weight
 // tile, super-block) laid out for the GEMM's operand loads (layout in include/mmq.h).
 // The q4_K fields are those of the r15 page ("f32-accumulate mma probe + rank-1 term2
 // rescale", section 2.1); the scale expansion dsv = d*sc, dmv = -(dmin*m) is the B-staging
-// step quoted there, moved to load time.
+// step quoted there, moved to load time. dmv is stored as three bf16 pieces that sum to it
+// exactly, the operand form of the GEMM's bf16 matrix instruction for term2.
 #include "mmq_internal.h"
 
 namespace mmq {
@@ -55,7 +56,11 @@ __global__ __launch_bounds__(256) void repack_q4_K_kernel(const uint8_t* __restr
       dmv = -(dmin * (float)m);
     }
     reinterpret_cast<float*>(rec + kRepNibBytes)[b * 32 + j] = dsv;
-    reinterpret_cast<float*>(rec + kRepNibBytes + 1024)[b * 32 + j] = dmv;
+    uint16_t p[3];
+    bf16_split3(dmv, p[0], p[1], p[2]);
+    uint16_t* pc = reinterpret_cast<uint16_t*>(rec + kRepNibBytes + kRepDsvBytes);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) pc[(i * 32 + j) * 8 + b] = p[i];
   }
 }
 

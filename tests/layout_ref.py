@@ -6,8 +6,10 @@ produce, and a reader of such records used to check the layout spec round-trips.
 """
 import numpy as np
 
+import oracle
+
 TILE_ROWS = 32
-TILE_BYTES = 6144
+TILE_BYTES = 6656
 
 
 def repack_reference(w_blocks: np.ndarray, fields: dict) -> np.ndarray:
@@ -27,9 +29,11 @@ def repack_reference(w_blocks: np.ndarray, fields: dict) -> np.ndarray:
     dmv = np.zeros((nt * TILE_ROWS, nsb, 8), np.float32)
     dsv[:N] = d[..., None] * sc
     dmv[:N] = -(dmin[..., None] * m)
-    for name, arr, off in (("dsv", dsv, 4096), ("dmv", dmv, 5120)):
-        a = arr.reshape(nt, TILE_ROWS, nsb, 8).transpose(0, 2, 3, 1)    # [t, s, b, j]
-        out[..., off:off + 1024] = np.ascontiguousarray(a).view(np.uint8).reshape(nt, nsb, 1024)
+    a = dsv.reshape(nt, TILE_ROWS, nsb, 8).transpose(0, 2, 3, 1)        # [t, s, b, j]
+    out[..., 4096:5120] = np.ascontiguousarray(a).view(np.uint8).reshape(nt, nsb, 1024)
+    pc = oracle.bf16_pieces(dmv).reshape(nt, TILE_ROWS, nsb, 8, 3)      # [t, j, s, b, i]
+    pc = np.ascontiguousarray(pc.transpose(0, 2, 4, 1, 3)).astype("<u2")  # [t, s, i, j, b]
+    out[..., 5120:6656] = pc.view(np.uint8).reshape(nt, nsb, 1536)
     return out.reshape(-1)
 
 
@@ -44,7 +48,8 @@ def read_repacked(rep: np.ndarray, N: int, K: int) -> dict:
     v = np.stack([lo, hi], axis=3)                                     # [t, s, g, lohi, h, j, 16]
     v = v.transpose(0, 5, 1, 2, 3, 4, 6).reshape(nt * TILE_ROWS, K)    # [t, j, s, g, lohi, h, e]
     dsv = r[..., 4096:5120].copy().view(np.float32).reshape(nt, nsb, 8, TILE_ROWS)
-    dmv = r[..., 5120:6144].copy().view(np.float32).reshape(nt, nsb, 8, TILE_ROWS)
     dsv = dsv.transpose(0, 3, 1, 2).reshape(nt * TILE_ROWS, K // 32)
-    dmv = dmv.transpose(0, 3, 1, 2).reshape(nt * TILE_ROWS, K // 32)
+    pc = r[..., 5120:6656].copy().view("<u2").reshape(nt, nsb, 3, TILE_ROWS, 8)
+    vals = (pc.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    dmv = vals.sum(axis=2).transpose(0, 2, 1, 3).reshape(nt * TILE_ROWS, K // 32)
     return {"v": v[:N], "dsv": dsv[:N], "dmv": dmv[:N]}

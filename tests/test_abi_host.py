@@ -25,13 +25,16 @@ def test_exports_every_declared_symbol():
 
 
 def test_sizes():
-    assert mmq.mmq_q8_1_bytes(2048, 4096) == 2048 * 4096 * 9 // 8 + 8 * 2048 * 128
-    assert mmq.mmq_q8_1_bytes(1, 32) == 256 + 8
-    assert mmq.mmq_q8_1_bytes(3, 96) == 512 + 8 * 3 * 3
+    # q, words, pad to 256, da plane, pad to 256, 48 bytes of pieces per (row, super-block)
+    assert mmq.mmq_q8_1_bytes(2048, 4096) == (2048 * 4096 * 9 // 8 + 4 * 2048 * 128
+                                              + 48 * 2048 * 16)
+    assert mmq.mmq_q8_1_bytes(1, 32) == 256 + 256 + 48
+    assert mmq.mmq_q8_1_bytes(3, 96) == 512 + 256 + 48 * 3
+    assert mmq.mmq_q8_1_bytes(2, 288) == 768 + 256 + 48 * 2 * 2
     assert mmq.mmq_q4K_bytes(4096, 4096) == 4096 * 16 * 144
-    assert mmq.mmq_q4K_repacked_bytes(4096, 4096) == 128 * 16 * 6144
-    assert mmq.mmq_q4K_repacked_bytes(33, 256) == 2 * 6144
-    assert mmq.mmq_q4K_repacked_bytes(11008, 4096) == 344 * 16 * 6144
+    assert mmq.mmq_q4K_repacked_bytes(4096, 4096) == 128 * 16 * 6656
+    assert mmq.mmq_q4K_repacked_bytes(33, 256) == 2 * 6656
+    assert mmq.mmq_q4K_repacked_bytes(11008, 4096) == 344 * 16 * 6656
 
 
 @pytest.mark.parametrize("fn,args,status", [
@@ -52,8 +55,10 @@ def test_size_null_out():
     assert mmq.raw_call("mmq_q8_1_bytes", 1, 32, None) == mmq.MMQ_E_ARG
 
 
-LARGE_LDS = 2 * (128 * 272 + 128 * 64 + 8 * 2048)
-SMALL_LDS = 2 * (32 * 272 + 32 * 64 + 2 * 2048)
+# two stages of: token tile [BM][272], da [8][BM] f32, token pieces [3][BM][8] bf16, and per
+# wavefront dsv [8][32] f32 + dmv pieces [3][32][8] bf16
+LARGE_LDS = 2 * (128 * 272 + 128 * 32 + 128 * 48 + 8 * 2560)
+SMALL_LDS = 2 * (32 * 272 + 32 * 32 + 32 * 48 + 2 * 2560)
 
 
 def test_plan_large_when_it_fits():

@@ -10,7 +10,7 @@ from tests.layout_ref import read_repacked, repack_reference
 def test_repack_reference_roundtrip(N, K):
     f = synth.q4k_random_fields(N, K, N * 7 + K)
     rep = repack_reference(synth.q4k_pack(f), f)
-    assert rep.size == -(-N // 32) * (K // 256) * 6144
+    assert rep.size == -(-N // 32) * (K // 256) * 6656
     got = read_repacked(rep, N, K)
     assert np.array_equal(got["v"], f["v"])
     d = np.repeat(f["d_bits"].view(np.float16).astype(np.float64), 8, axis=1)
@@ -19,7 +19,7 @@ def test_repack_reference_roundtrip(N, K):
     assert np.array_equal(got["dmv"].astype(np.float64), -(dmin * f["m"]))
     # padding rows of the last tile are zero
     nt = -(-N // 32)
-    last = rep.reshape(nt, K // 256, 6144)[-1]
+    last = rep.reshape(nt, K // 256, 6656)[-1]
     rows_used = N - (nt - 1) * 32
     nib = last[:, :4096].reshape(K // 256, 4, 2, 32, 16)
     assert np.all(nib[:, :, :, rows_used:, :] == 0)
