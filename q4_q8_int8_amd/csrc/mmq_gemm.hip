@@ -75,7 +75,10 @@ __device__ __forceinline__ v4i make_rsrc_sgpr(const void* p, uint32_t bytes) {
 // explicitly before the barrier that ends a stage. The instruction is issued from inline
 // assembly on purpose: the compiler cannot tell which LDS bytes such a load writes, so for
 // the intrinsic it waits for every outstanding one before the next LDS read, which would
-// stall each wavefront on its own prefetch at the start of every stage.
+// stall each wavefront on its own prefetch at the start of every stage. The asm declares no
+// memory effects on purpose too: it only writes the stage buffer that nothing reads until
+// after the explicit wait and the barrier (both ordered with the asm), and so the compiler
+// stays free to schedule the current stage's LDS reads around it.
 __device__ __forceinline__ void dma16(v4i r, uint8_t* lds_base, uint32_t off) {
   const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)lds_base);
   int saved;  // m0 is reserved by the compiler: restore it after use
@@ -86,8 +89,7 @@ __device__ __forceinline__ void dma16(v4i r, uint8_t* lds_base, uint32_t off) {
       "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(off), "s"(r)
-      : "memory");
+      : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(off), "s"(r));
 }
 
 template <int TT, int NW, bool STORE_S>
@@ -159,38 +161,52 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
     tp_act[j] = k < TP_DMA && q < TP_SLOTS;
     tp_off[j] = ((uint32_t)pc * (uint32_t)M + (uint32_t)(m0 + r)) * 16u;
   }
-  auto issue_stage = [&](int s, int p) {
+  // What stage s of the pipeline loads into LDS, as NOPS single DMA instructions of this
+  // wavefront (its token-tile DMAs, its da DMAs, its token-piece DMA, its 2560 bytes of dsv
+  // and dmv pieces), followed by op NOPS: nibble group 3 into registers. Op v is a
+  // compile-time constant wherever it is issued, so each call folds to one instruction.
+  // Nibble groups 0..2 are loaded separately, in place (load_nib).
+  constexpr int DA_PER_WAVE = (8 + NW - 1) / NW;
+  // The next stage's ops are issued three at a time at the first step of every other
+  // sub-block (the last ones at the last step at the latest), so that the wavefronts of a
+  // workgroup do not queue all their memory instructions at once. Finer spreading costs
+  // registers: each issue point constrains how far ahead the compiler schedules LDS reads.
+  auto op_step = [](int v) { return ((v / 3) * 2 * TT < NS - 1) ? (v / 3) * 2 * TT : NS - 1; };
+  constexpr int NOPS = A_PER_WAVE + DA_PER_WAVE + TP_PER_WAVE + 3 + 1;
+  auto load_nib = [&](int s, int g) -> v4i {
+    return buf_load16(rw, (uint32_t)s * kRepTileBytes + g * 1024 + lane * 16);
+  };
+  auto issue_op = [&](int v, int s, int p, v4i& nib3) {
     uint8_t* st = smem + p * STAGE;
-#pragma unroll
-    for (int j = 0; j < A_PER_WAVE; ++j) {
-      const int k = wave + j * NW;
-      if (k < A_DMA && a_act[j]) dma16(rq, st + k * 1024, a_off[j] + (uint32_t)s * 256);
+    if (v < A_PER_WAVE) {
+      const int k = wave + v * NW;
+      if (k < A_DMA && a_act[v]) dma16(rq, st + k * 1024, a_off[v] + (uint32_t)s * 256);
+      return;
     }
-    // da of blocks 8s..8s+7 for rows m0..m0+BM-1: BM/4 lanes per block
-#pragma unroll
-    for (int b = wave; b < 8; b += NW)
-      if (lane < BM / 4)
+    v -= A_PER_WAVE;
+    if (v < DA_PER_WAVE) {  // da of block b for rows m0..m0+BM-1: BM/4 lanes
+      const int b = wave + v * NW;
+      if (b < 8 && lane < BM / 4)
         dma16(rda, st + A_BYTES + b * BM * 4,
               (((uint32_t)s * 8 + b) * (uint32_t)M + m0) * 4u + lane * 16);
-    // the token pieces of da*sa for super-block s
-#pragma unroll
-    for (int j = 0; j < TP_PER_WAVE; ++j) {
-      const int k = wave + j * NW;
-      if (k < TP_DMA && tp_act[j])
-        dma16(rtp, st + A_BYTES + DA_BYTES + k * 1024,
-              tp_off[j] + (uint32_t)s * 3u * (uint32_t)M * 16u);
+      return;
     }
-    // this wavefront's dsv [8][32] and dmv pieces [3][32][8]: 2560 contiguous bytes
-    uint8_t* sw = st + A_BYTES + DA_BYTES + TP_BYTES + wave * W_BYTES;
-    const uint32_t wo = (uint32_t)s * kRepTileBytes + kRepNibBytes + lane * 16;
-    dma16(rwd, sw, wo);
-    dma16(rwd, sw + 1024, wo + 1024);
-    if (lane < 32) dma16(rwd, sw + 2048, wo + 2048);
-  };
-  auto load_nibbles = [&](int s, v4i (&raw)[4]) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      raw[g] = buf_load16(rw, (uint32_t)s * kRepTileBytes + g * 1024 + lane * 16);
+    v -= DA_PER_WAVE;
+    if (v < TP_PER_WAVE) {
+      const int k = wave + v * NW;
+      if (k < TP_DMA && tp_act[v])
+        dma16(rtp, st + A_BYTES + DA_BYTES + k * 1024,
+              tp_off[v] + (uint32_t)s * 3u * (uint32_t)M * 16u);
+      return;
+    }
+    v -= TP_PER_WAVE;
+    if (v < 3) {  // dsv [8][32] and dmv pieces [3][32][8]: 2560 contiguous bytes
+      uint8_t* sw = st + A_BYTES + DA_BYTES + TP_BYTES + wave * W_BYTES;
+      const uint32_t wo = (uint32_t)s * kRepTileBytes + kRepNibBytes + lane * 16;
+      if (v < 2 || lane < 32) dma16(rwd, sw + v * 1024, wo + v * 1024);
+      return;
+    }
+    nib3 = load_nib(s, 3);
   };
 
   v16i bias;
@@ -202,21 +218,21 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 
-  v4i rawn[4];
-  issue_stage(0, 0);
-  load_nibbles(0, rawn);
+  // raw[g]: the nibbles of sub-blocks 2g and 2g+1 of the current stage. Groups 0..2 of the
+  // next stage are loaded into raw[g] as soon as the last MFMA that reads them has been
+  // issued; group 3 is still in use at the end of the stage, so it goes through nib3.
+  v4i raw[4], nib3;
+#pragma unroll
+  for (int v = 0; v < NOPS; ++v) issue_op(v, 0, 0, nib3);
+#pragma unroll
+  for (int g = 0; g < 3; ++g) raw[g] = load_nib(0, g);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int s = 0; s < nsb; ++s) {
     const int p = s & 1;
-    v4i raw[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) raw[g] = rawn[g];
-    if (s + 1 < nsb) {
-      issue_stage(s + 1, p ^ 1);
-      load_nibbles(s + 1, rawn);
-    }
+    raw[3] = nib3;
+    const bool more = s + 1 < nsb;
 
     const uint8_t* st = smem + p * STAGE;
     const uint8_t* sArow = st + l32 * kRowStride + h * 16;
@@ -243,6 +259,13 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
 
     if constexpr (STORE_S) {
       // test path: every S of the window, straight from the MFMA
+      v4i nxt[3] = {raw[0], raw[1], raw[2]};
+      if (more) {
+#pragma unroll
+        for (int v = 0; v < NOPS; ++v) issue_op(v, s + 1, p ^ 1, nib3);
+#pragma unroll
+        for (int g = 0; g < 3; ++g) nxt[g] = load_nib(s + 1, g);
+      }
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
         const int b = n / TT, t = n % TT;
@@ -260,6 +283,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
           }
         }
       }
+#pragma unroll
+      for (int g = 0; g < 3; ++g) raw[g] = nxt[g];
     } else {
       // Step n = b*TT + t. Entering step n: D(n) has been issued, the token operand of step
       // n+1 and da of step n are in registers; dsv[b & 1] holds block b's weight scales.
@@ -271,6 +296,15 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
         const int b = n / TT, t = n % TT;
+        if (more) {
+#pragma unroll
+          for (int v = 0; v < NOPS; ++v)
+            if (op_step(v) == n) issue_op(v, s + 1, p ^ 1, nib3);
+          // the MFMAs of sub-blocks 2g, 2g+1 were issued by step (2g+2)*TT - 2
+#pragma unroll
+          for (int g = 0; g < 3; ++g)
+            if (n == (2 * g + 2) * TT) raw[g] = load_nib(s + 1, g);
+        }
         const v16i D = Dn;
         const float dac = da;
         if (n + 1 < NS) {
