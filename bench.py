@@ -7,12 +7,16 @@ synthetic seeded inputs (synth.py: activations N(0,1) with 0.1% outliers x20, q4
 N(0, 0.02) weights). The weights are repacked once before timing (an offline, per-weight
 step); one timed step is the whole per-batch path: quantize_q8_1 of the f32 activations
 followed by the GEMM, with every input already resident in device memory. R copies of the
-activations, weights and outputs are rotated so that consecutive steps do not hit in the
-256 MB last-level cache.
+activations, weights and outputs are rotated (R = 8: about 740 MB for the steps, 470 MB for
+the GEMM alone) so that no launch finds another launch's data in the 256 MB last-level
+cache, as in a prefill where every product has its own weights.
 
 Prints one JSON line. value = M*N*K / (time per step) in TMAC/s (1 MAC = one int8
-multiply-accumulate); the GEMM kernel's own time, measured with HIP events on the stream it
-runs on, gives the roofline entry against the dense int8 MFMA peak.
+multiply-accumulate), the time per step being the host wall clock over the K timed steps
+between synchronizations. The GEMM kernel's own average duration, from HIP events around K
+back-to-back launches on the stream it runs on, gives the roofline entry against the dense
+int8 MFMA peak; its HBM traffic comes from the committed rocprofv3 counter summary of the
+same kernel source (null once the kernel has changed since the counters were taken).
 """
 from __future__ import annotations
 
@@ -51,6 +55,12 @@ def measured_traffic():
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def quant_bytes(M: int, K: int) -> int:
+    """Algorithmic HBM bytes of one quantize launch: f32 activations in, the q8 buffer out."""
+    import q4_q8_int8_amd as mmq
+    return 4 * M * K + mmq.mmq_q8_1_bytes(M, K)
 
 
 def cpu_baseline(W: dict, window_s: float = 10.0) -> dict:
@@ -99,7 +109,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rotate", type=int, default=4)
+    ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
@@ -140,37 +150,57 @@ def main() -> int:
     torch.cuda.synchronize()
     repack_us = ev_r0.elapsed_time(ev_r1) * 1e3 / R
 
-    def step(i, evs=None):
+    def step(i):
         r = i % R
-        if evs:
-            evs[0].record(stream)
         mmq.quantize_q8_1(xs[r], M, K, q8s[r])
-        if evs:
-            evs[1].record(stream)
         mmq.mmq_q4K_q8_1(M, N, K, q8s[r], reps[r], Cs[r])
-        if evs:
-            evs[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     plan = mmq.mmq_last_kernel()
 
-    # timed region: exactly K steps between synchronizations; HIP events on the launch
-    # stream bracket each kernel for the per-kernel durations
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    def events():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    # The timed region: exactly K steps of the whole path between synchronizations, with
+    # one pair of HIP events on the launch stream around it (events between the kernels
+    # would add their own packets and gaps to every step).
+    ev0, ev1 = events()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    q_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    g_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    region_gpu_ms = ev0.elapsed_time(ev1)
+
+    # Per-kernel average launch durations: K back-to-back launches of one kernel between
+    # one pair of HIP events, the inputs rotating as in the steps (R copies of a GEMM's
+    # inputs and output exceed the last-level cache, so no launch reuses another's data).
+    def kernel_avg_ms(launch):
+        e0, e1 = events()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            launch(i % R)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    def quant(r):
+        mmq.quantize_q8_1(xs[r], M, K, q8s[r])
+
+    def gemm(r):
+        mmq.mmq_q4K_q8_1(M, N, K, q8s[r], reps[r], Cs[r])
+
+    q_avg, g_avg = kernel_avg_ms(quant), kernel_avg_ms(gemm)
 
     macs = M * N * K
     ms_per_step = wall * 1e3 / args.steps
-    gemm_s = float(g_ms.mean()) * 1e-3
+    gemm_s = g_avg * 1e-3
     achieved_tops = 2.0 * macs / gemm_s / 1e12
     value = macs / (ms_per_step * 1e-3) / 1e12
     out = {
@@ -195,12 +225,13 @@ def main() -> int:
                      "frac": round(achieved_tops / INT8_PEAK_TOPS, 4),
                      "traffic": measured_traffic()},
         "us_per_gmac": round(ms_per_step * 1e3 / (macs / 1e9), 4),
-        "gemm": {"us": round(gemm_s * 1e6, 2), "us_min": round(float(g_ms.min()) * 1e3, 2),
+        "step_gpu_us": round(region_gpu_ms * 1e3 / args.steps, 2),
+        "gemm": {"us": round(gemm_s * 1e6, 2),
                  "tmacs": round(macs / gemm_s / 1e12, 2),
                  "us_per_gmac": round(gemm_s * 1e6 / (macs / 1e9), 4)},
-        "quantize": {"us": round(float(q_ms.mean()) * 1e3, 2),
-                     "hbm_frac": round((M * K * (4 + 1.125)) / (float(q_ms.mean()) * 1e-3)
-                                       / (HBM_PEAK_GBS * 1e9), 4)},
+        "quantize": {"us": round(q_avg * 1e3, 2),
+                     "hbm_frac": round(quant_bytes(M, K) / (q_avg * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                                       4)},
         "repack_us_once": round(repack_us, 2),
     }
     if not args.no_cpu_baseline:

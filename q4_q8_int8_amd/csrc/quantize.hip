@@ -8,8 +8,8 @@
 // instruction. HBM-bound: 4 bytes read and about 1.44 bytes written per element.
 //
 // Mapping: 8 lanes own one 32-element block (one float4 each), so a wavefront covers 8
-// consecutive blocks = 1 KiB of contiguous input; the max and the sum are reduced with
-// xor-shuffles inside the 8-lane group.
+// consecutive blocks = 1 KiB of contiguous input at a time, and 4 such groups in all; the
+// max and the sum are reduced with xor-shuffles inside the 8-lane group.
 #include "mmq_internal.h"
 
 namespace mmq {
@@ -21,49 +21,110 @@ __device__ __forceinline__ int quant1(float x, float id) {
   return (int)fminf(fmaxf(roundf(p), -127.0f), 127.0f);
 }
 
+// Reductions over the 8 lanes of a group with DPP moves: swap neighbours, swap pairs, then
+// mirror within the 8 lanes, after which every lane holds the group's result.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kSwap1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kSwap2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;  // row_half_mirror: lane i <-> 7 - i within 8 lanes
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, __int_as_float(dpp<kSwap1>(__float_as_int(v))));
+  v = fmaxf(v, __int_as_float(dpp<kSwap2>(__float_as_int(v))));
+  return fmaxf(v, __int_as_float(dpp<kHalfMirror>(__float_as_int(v))));
+}
+__device__ __forceinline__ int group_sum(int v) {
+  v += dpp<kSwap1>(v);
+  v += dpp<kSwap2>(v);
+  return v + dpp<kHalfMirror>(v);
+}
+
+// One group of 8 lanes and one block (row, b): quantize, then store q, the scale word, da
+// and the pieces of da*sa. gathered: the wavefront's 8 blocks are blocks 8s..8s+7 of one
+// row, so lanes 0..2 gather the pieces of all 8 and store 16 bytes each.
+__device__ __forceinline__ void quantize_block(const float4 v, const uint32_t blk, const bool ok,
+                                               const uint32_t row, const uint32_t b,
+                                               const bool gathered, const int lane,
+                                               uint32_t* __restrict__ qs,
+                                               uint32_t* __restrict__ ds,
+                                               float* __restrict__ da_plane,
+                                               uint16_t* __restrict__ pieces, uint32_t M) {
+  const float amax =
+      group_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  const float d = amax / 127.0f;                 // IEEE division
+  const float id = d > 0.0f ? 1.0f / d : 0.0f;   // IEEE reciprocal (division)
+  const int q0 = quant1(v.x, id), q1 = quant1(v.y, id);
+  const int q2 = quant1(v.z, id), q3 = quant1(v.w, id);
+  const int sum = group_sum(q0 + q1 + q2 + q3);
+
+  const _Float16 dh = (_Float16)d;  // RNE
+  if (ok) {
+    qs[blk * 8u + (lane & 7)] = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) |
+                                ((uint32_t)(q2 & 0xFF) << 16) | ((uint32_t)(q3 & 0xFF) << 24);
+    if ((lane & 7) == 0) {
+      ds[blk] = (uint32_t)__builtin_bit_cast(uint16_t, dh) | ((uint32_t)(sum & 0xFFFF) << 16);
+      da_plane[b * M + row] = (float)dh;  // the GEMM's da plane, block-major
+    }
+  }
+
+  // da*sa (exact in f32) as three bf16 pieces, [K/256][3][M][8]
+  uint16_t p[3];
+  bf16_split3((float)dh * (float)sum, p[0], p[1], p[2]);
+  if (gathered) {
+    // lane j < 3 gathers piece j of the 8 blocks and stores 16 bytes
+    const int j = lane & 7;
+    const uint32_t offer = j < 3 ? p[j] : 0u;
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = (uint32_t)__shfl((int)offer, 8 * e + j, 64);
+    if (ok && lane < 3)
+      *reinterpret_cast<uint4*>(pieces + (((b >> 3) * 3 + j) * M + row) * 8) =
+          make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16),
+                     w[6] | (w[7] << 16));
+  } else if (ok && (lane & 7) == 0) {
+    uint16_t* dst = pieces + ((b >> 3) * 3 * M + row) * 8 + (b & 7);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) dst[j * M * 8] = p[j];
+  }
+}
+
+// A wavefront quantizes kGroups groups of 8 consecutive blocks (1 KiB of input each); all
+// its loads are issued before the first block is processed. Indices fit in 32 bits
+// (M*K < 2^31).
+constexpr int kGroups = 2;
+
 __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float4* __restrict__ x,
                                                             uint32_t* __restrict__ qs,
                                                             uint32_t* __restrict__ ds,
                                                             float* __restrict__ da_plane,
                                                             uint16_t* __restrict__ pieces,
-                                                            int64_t nblocks, int M, int kb) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t blk = t >> 3;      // all 8 lanes of a group share blk
-  const bool ok = blk < nblocks;
-  const float4 v = ok ? x[t] : make_float4(0.f, 0.f, 0.f, 0.f);
-
-  float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
-  amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
-
-  const float d = amax / 127.0f;                 // IEEE division
-  const float id = d > 0.0f ? 1.0f / d : 0.0f;   // IEEE reciprocal (division)
-  const int q0 = quant1(v.x, id), q1 = quant1(v.y, id);
-  const int q2 = quant1(v.z, id), q3 = quant1(v.w, id);
-
-  int sum = q0 + q1 + q2 + q3;
-  sum += __shfl_xor(sum, 1, 8);
-  sum += __shfl_xor(sum, 2, 8);
-  sum += __shfl_xor(sum, 4, 8);
-
-  if (ok) {
-    qs[t] = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) |
-            ((uint32_t)(q2 & 0xFF) << 16) | ((uint32_t)(q3 & 0xFF) << 24);
-    if ((threadIdx.x & 7) == 0) {
-      const _Float16 dh = (_Float16)d;  // RNE
-      const uint32_t hbits = __builtin_bit_cast(uint16_t, dh);
-      ds[blk] = hbits | ((uint32_t)(sum & 0xFFFF) << 16);
-      // the GEMM's planes: da block-major, and da * sa (exact in f32) as bf16 pieces
-      const int64_t row = blk / kb, b = blk - row * kb;
-      const float da = (float)dh;
-      da_plane[b * M + row] = da;
-      uint16_t p[3];
-      bf16_split3(da * (float)sum, p[0], p[1], p[2]);
-      uint16_t* dst = pieces + ((b >> 3) * 3 * (int64_t)M + row) * 8 + (b & 7);
+                                                            uint32_t nblocks, uint32_t M,
+                                                            uint32_t kb) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t wid = __builtin_amdgcn_readfirstlane((blockIdx.x * 256u + threadIdx.x) >> 6);
+  const bool aligned = (kb & 7) == 0;  // then a group of 8 blocks lies in one row
+  float4 v[kGroups];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) dst[j * (int64_t)M * 8] = p[j];
+  for (int g = 0; g < kGroups; ++g) {
+    const uint32_t blk = (wid * kGroups + g) * 8 + (lane >> 3);
+    v[g] = blk < nblocks ? x[blk * 8u + (lane & 7)] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    const uint32_t blk0 = (wid * kGroups + g) * 8;  // wave-uniform
+    const uint32_t blk = blk0 + (lane >> 3);
+    uint32_t row, b;
+    if (aligned) {
+      row = blk0 / kb;
+      b = blk0 - row * kb + (lane >> 3);
+    } else {
+      row = blk / kb;
+      b = blk - row * kb;
     }
+    quantize_block(v[g], blk, blk < nblocks, row, b, aligned, lane, qs, ds, da_plane, pieces,
+                   M);
   }
 }
 
@@ -71,15 +132,15 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float4* __rest
 
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, hipStream_t s) {
   const int64_t nblocks = M * (K / 32);
-  const int64_t threads = nblocks * 8;
-  const int64_t grid = (threads + 255) / 256;
+  const int64_t waves = (nblocks + 8 * kGroups - 1) / (8 * kGroups);
+  const int64_t grid = (waves + 3) / 4;
   uint8_t* base = static_cast<uint8_t*>(q8);
   hipLaunchKernelGGL(quantize_q8_1_kernel, dim3((unsigned)grid), dim3(256), 0, s,
                      reinterpret_cast<const float4*>(x), reinterpret_cast<uint32_t*>(base),
                      reinterpret_cast<uint32_t*>(base + M * K),
                      reinterpret_cast<float*>(base + q8_planes_offset(M, K)),
-                     reinterpret_cast<uint16_t*>(base + q8_pieces_offset(M, K)), nblocks,
-                     (int)M, (int)(K / 32));
+                     reinterpret_cast<uint16_t*>(base + q8_pieces_offset(M, K)),
+                     (uint32_t)nblocks, (uint32_t)M, (uint32_t)(K / 32));
   return hipGetLastError();
 }
 
