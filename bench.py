@@ -34,7 +34,8 @@ INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, tera-ops/s (1 MAC = 2
 HBM_PEAK_GBS = 8000.0
 PAGES_QPROJ_TMACS = 15.19        # the pages' best q-proj MMQ kernel: 34.36 GMAC in 2.262 ms
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmq_qproj_traffic.json")
-KERNEL_SOURCES = ["q4_q8_int8_amd/csrc/mmq_gemm.hip", "q4_q8_int8_amd/csrc/mmq_internal.h"]
+KERNEL_SOURCES = ["q4_q8_int8_amd/csrc/mmq_gemm.hip", "q4_q8_int8_amd/csrc/mmq_device.h",
+                  "q4_q8_int8_amd/csrc/mmq_internal.h"]
 
 
 def kernel_source_hash() -> str:
@@ -104,35 +105,14 @@ def copy_probe(mib: int) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rotate", type=int, default=8)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
-    args = ap.parse_args()
-    if args.copy_probe:
-        return copy_probe(args.copy_probe)
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
-              "(how it would shard is described in DESIGN.md)", file=sys.stderr)
-        return 2
-
-    import numpy as np
+def measure(W: dict, R: int, steps: int, warmup: int, tile: int = 0) -> dict:
+    """Time the whole path (quantize + GEMM) on one workload; see the module docstring."""
     import torch
 
-    import synth
     import q4_q8_int8_amd as mmq
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    W = synth.workload("qproj")
     M, N, K = W["M"], W["N"], W["K"]
-    R = max(1, args.rotate)
     stream = torch.cuda.current_stream()
 
     xs = [torch.from_numpy(W["x"]).to(dev) for _ in range(R)]
@@ -142,7 +122,10 @@ def main() -> int:
     q8s = [torch.empty(mmq.mmq_q8_1_bytes(M, K), dtype=torch.uint8, device=dev) for _ in range(R)]
     Cs = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(R)]
 
-    ev_r0, ev_r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def events():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    ev_r0, ev_r1 = events()
     ev_r0.record(stream)
     for r in range(R):
         mmq.repack_q4_K(w_dev, N, K, reps[r])
@@ -150,57 +133,157 @@ def main() -> int:
     torch.cuda.synchronize()
     repack_us = ev_r0.elapsed_time(ev_r1) * 1e3 / R
 
-    def step(i):
-        r = i % R
+    def quant(r):
         mmq.quantize_q8_1(xs[r], M, K, q8s[r])
-        mmq.mmq_q4K_q8_1(M, N, K, q8s[r], reps[r], Cs[r])
 
-    for i in range(args.warmup):
+    def gemm(r):
+        mmq.mmq_q4K_q8_1_ex(M, N, K, q8s[r], reps[r], Cs[r], force_tile=tile)
+
+    def step(i):
+        quant(i % R)
+        gemm(i % R)
+
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     plan = mmq.mmq_last_kernel()
 
-    def events():
-        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    # The timed region: exactly K steps of the whole path between synchronizations, with
-    # one pair of HIP events on the launch stream around it (events between the kernels
-    # would add their own packets and gaps to every step).
+    # The timed region: exactly `steps` steps of the whole path between synchronizations,
+    # with one pair of HIP events on the launch stream around it (events between the
+    # kernels would add their own packets and gaps to every step).
     ev0, ev1 = events()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     region_gpu_ms = ev0.elapsed_time(ev1)
 
-    # Per-kernel average launch durations: K back-to-back launches of one kernel between
-    # one pair of HIP events, the inputs rotating as in the steps (R copies of a GEMM's
-    # inputs and output exceed the last-level cache, so no launch reuses another's data).
+    # Per-kernel average launch durations: `steps` back-to-back launches of one kernel
+    # between one pair of HIP events, the inputs rotating as in the steps (R copies of a
+    # GEMM's inputs and output exceed the last-level cache, so no launch reuses another's
+    # data).
     def kernel_avg_ms(launch):
         e0, e1 = events()
         torch.cuda.synchronize()
         e0.record(stream)
-        for i in range(args.steps):
+        for i in range(steps):
             launch(i % R)
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
+        return e0.elapsed_time(e1) / steps
 
-    def quant(r):
-        mmq.quantize_q8_1(xs[r], M, K, q8s[r])
+    q_ms, g_ms = kernel_avg_ms(quant), kernel_avg_ms(gemm)
+    del xs, reps, q8s, Cs
+    torch.cuda.empty_cache()
+    return {"ms_per_step": wall * 1e3 / steps, "step_gpu_us": region_gpu_ms * 1e3 / steps,
+            "gemm_us": g_ms * 1e3, "quant_us": q_ms * 1e3, "repack_us": repack_us, "plan": plan}
 
-    def gemm(r):
-        mmq.mmq_q4K_q8_1(M, N, K, q8s[r], reps[r], Cs[r])
 
-    q_avg, g_avg = kernel_avg_ms(quant), kernel_avg_ms(gemm)
+def gemm_bytes(M: int, N: int, K: int) -> int:
+    """Algorithmic HBM bytes of one GEMM launch: the q8 buffer and the repacked weights in,
+    C out."""
+    import q4_q8_int8_amd as mmq
+    return mmq.mmq_q8_1_bytes(M, K) + mmq.mmq_q4K_repacked_bytes(N, K) + 4 * M * N
 
+
+def config_line(name: str, W: dict, t: dict) -> dict:
+    """One JSON line of the per-config table: throughput, peak and HBM fractions."""
+    M, N, K = W["M"], W["N"], W["K"]
     macs = M * N * K
-    ms_per_step = wall * 1e3 / args.steps
-    gemm_s = g_avg * 1e-3
+    g = t["gemm_us"] * 1e-6
+    return {"config": name, "M": M, "N": N, "K": K, "tile": t["plan"]["tile"],
+            "grid": t["plan"]["grid"],
+            "gemm_us": round(t["gemm_us"], 2), "gemm_tmacs": round(macs / g / 1e12, 2),
+            "gemm_us_per_gmac": round(t["gemm_us"] / (macs / 1e9), 4),
+            "int8_peak_frac": round(2 * macs / g / 1e12 / INT8_PEAK_TOPS, 4),
+            "gemm_hbm_frac": round(gemm_bytes(M, N, K) / g / (HBM_PEAK_GBS * 1e9), 4),
+            "quant_us": round(t["quant_us"], 2),
+            "quant_hbm_frac": round(quant_bytes(M, K) / (t["quant_us"] * 1e-6)
+                                    / (HBM_PEAK_GBS * 1e9), 4),
+            "step_us": round(t["step_gpu_us"], 2),
+            "path_tmacs": round(macs / (t["step_gpu_us"] * 1e-6) / 1e12, 2)}
+
+
+def sweep(args) -> int:
+    """Every configuration (and each tile the guard allows), then the 7-projection prefill:
+    one JSON line each. Not the driver's benchmark line; see the profiles."""
+    import synth
+    import q4_q8_int8_amd as mmq
+    names = ["tiny", "qproj", "gateup", "down"] + [f"sweep_m{m}" for m in synth.SWEEP_M]
+    times = {}
+    for name in names:
+        W = synth.workload(name)
+        tiles = [mmq.MMQ_TILE_LARGE, mmq.MMQ_TILE_SMALL]
+        if W["M"] <= 512:
+            tiles.append(mmq.MMQ_TILE_SKINNY)
+        for tile in tiles:
+            t = measure(W, args.rotate, args.steps, args.warmup, tile)
+            times[(name, tile)] = t
+            print(json.dumps(config_line(name, W, t)), flush=True)
+        del W
+    # 7-projection prefill of a 32-layer 7B at 2048 tokens, GEMM-only: per layer q, k, v, o
+    # are q-proj shaped, gate and up gate/up shaped, down down shaped; three K=4096
+    # activations (attention input, attention output, FFN input) and one K=11008 one are
+    # quantized. Each product takes its faster tile.
+    best = {n: min((t for (c, _), t in times.items() if c == n), key=lambda t: t["gemm_us"])
+            for n in ("qproj", "gateup", "down")}
+    layer_gemm = 4 * best["qproj"]["gemm_us"] + 2 * best["gateup"]["gemm_us"] \
+        + best["down"]["gemm_us"]
+    layer_quant = 3 * best["qproj"]["quant_us"] + best["down"]["quant_us"]
+    macs = 32 * (4 * 2048 * 4096 * 4096 + 2 * 2048 * 4096 * 11008 + 2048 * 11008 * 4096)
+    total_us = 32 * (layer_gemm + layer_quant)
+    print(json.dumps({"config": "prefill_7shape_32layer", "tokens": 2048,
+                      "tok_per_s": round(2048 / (total_us * 1e-6), 1),
+                      "ms": round(total_us * 1e-3, 3), "gemm_ms": round(32 * layer_gemm * 1e-3, 3),
+                      "quant_ms": round(32 * layer_quant * 1e-3, 3),
+                      "tmacs": round(macs / (total_us * 1e-6) / 1e12, 2),
+                      "note": "sum of per-kernel averages of the 3 distinct shapes, x32 layers; "
+                              "GEMM-only prefill, not whole-model"}), flush=True)
+    return 0
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="per-config table (one JSON line per config and tile) instead of the "
+                         "benchmark line")
+    args = ap.parse_args()
+    if args.copy_probe:
+        return copy_probe(args.copy_probe)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
+              "(how it would shard is described in DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.sweep:
+        return sweep(args)
+
+    W = synth.workload("qproj")
+    M, N, K = W["M"], W["N"], W["K"]
+    R = max(1, args.rotate)
+    t = measure(W, R, args.steps, args.warmup)
+    plan = t["plan"]
+    macs = M * N * K
+    ms_per_step = t["ms_per_step"]
+    gemm_s = t["gemm_us"] * 1e-6
+    q_us = t["quant_us"]
     achieved_tops = 2.0 * macs / gemm_s / 1e12
     value = macs / (ms_per_step * 1e-3) / 1e12
     out = {
@@ -225,14 +308,14 @@ def main() -> int:
                      "frac": round(achieved_tops / INT8_PEAK_TOPS, 4),
                      "traffic": measured_traffic()},
         "us_per_gmac": round(ms_per_step * 1e3 / (macs / 1e9), 4),
-        "step_gpu_us": round(region_gpu_ms * 1e3 / args.steps, 2),
+        "step_gpu_us": round(t["step_gpu_us"], 2),
         "gemm": {"us": round(gemm_s * 1e6, 2),
                  "tmacs": round(macs / gemm_s / 1e12, 2),
                  "us_per_gmac": round(gemm_s * 1e6 / (macs / 1e9), 4)},
-        "quantize": {"us": round(q_avg * 1e3, 2),
-                     "hbm_frac": round(quant_bytes(M, K) / (q_avg * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "quantize": {"us": round(q_us, 2),
+                     "hbm_frac": round(quant_bytes(M, K) / (q_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
                                        4)},
-        "repack_us_once": round(repack_us, 2),
+        "repack_us_once": round(t["repack_us"], 2),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W)

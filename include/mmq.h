@@ -50,27 +50,33 @@ enum mmq_status {
 #define MMQ_REP_TILE_ROWS 32     /* weight rows per repacked tile */
 #define MMQ_REP_TILE_BYTES 6656  /* bytes per (repacked tile, super-block) */
 
-/* Tile variants of the GEMM kernel (one template, two instantiations). */
+/* Tile variants of the GEMM: one template in two instantiations (large, small), and a
+ * skinny kernel for few tokens that splits K over the wavefronts of a workgroup. */
 enum mmq_tile {
   MMQ_TILE_AUTO = 0,   /* let the guard choose */
   MMQ_TILE_LARGE = 1,  /* 128 tokens x 256 output features per workgroup, 8 wavefronts */
-  MMQ_TILE_SMALL = 2   /* 32 tokens x 64 output features per workgroup, 2 wavefronts */
+  MMQ_TILE_SMALL = 2,  /* 32 tokens x 64 output features per workgroup, 2 wavefronts */
+  MMQ_TILE_SKINNY = 3  /* 32 tokens x 32 output features per workgroup, K split over 8
+                          wavefronts and summed in wavefront order (no block-dot output) */
 };
 
 /* Why the guard chose what it chose. */
 enum mmq_reason {
   MMQ_REASON_NONE = 0,
   MMQ_REASON_LARGE = 1,         /* large tile fits the LDS budget and M is large enough */
-  MMQ_REASON_SMALL_M = 2,       /* M <= 64: the small tile wastes fewer token rows */
+  MMQ_REASON_SMALL_GRID = 2,    /* the large tile's grid would leave compute units idle */
   MMQ_REASON_LDS_FALLBACK = 3,  /* the large tile does not fit the LDS budget: small tile */
   MMQ_REASON_FORCED = 4,        /* the caller's options asked for this tile */
-  MMQ_REASON_NO_FIT = 5         /* nothing fits the budget: refused with MMQ_E_LDS */
+  MMQ_REASON_NO_FIT = 5,        /* nothing fits the budget: refused with MMQ_E_LDS */
+  MMQ_REASON_FEW_TOKENS = 6     /* M <= 128 and the large grid would leave compute units idle:
+                                   the skinny kernel, which splits K over wavefronts */
 };
 
 /* Optional knobs for the _ex entry points (NULL = defaults). */
 typedef struct mmq_options {
   int32_t force_tile;   /* enum mmq_tile. A forced tile that does not fit is refused (MMQ_E_LDS) */
-  int32_t reserved;
+  int32_t min_workgroups; /* > 0: choose the large tile only when its grid has at least this many
+                             workgroups; 0: the device's compute-unit count (256 in mmq_plan) */
   int64_t lds_budget;   /* > 0: check tiles against this many bytes of LDS instead of the
                            device's per-workgroup limit (lets a caller force the fallback) */
 } mmq_options;
@@ -184,8 +190,12 @@ int mmq_q4K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, cons
 /*
  * mmq_plan: the LDS-budget guard as a pure host function (no device access). Chooses the
  * tile for an M x N x K product given `lds_budget` bytes per workgroup (opt->lds_budget,
- * when set, takes precedence): the large tile when it fits and M > 64, else the small tile,
- * else MMQ_E_LDS. A kernel that does not fit the budget is never launched: on the r16 page
+ * when set, takes precedence): the large tile when it fits and its grid has at least
+ * opt->min_workgroups workgroups (default 256, the MI355X compute-unit count; a GEMM call
+ * uses the device's count); else, for M <= 128, the skinny kernel; else the small tile (more,
+ * smaller workgroups: at M = 512, N = 4096 the large tile has 64 workgroups for 256 compute
+ * units); when the large tile does not fit the budget, the small tile; else MMQ_E_LDS. A
+ * kernel that does not fit the budget is never launched: on the r16 page
  * (section 1) an over-budget launch failed silently and produced wrong numbers, so here
  * the fallback is explicit and reported (fallback, reason), and a refusal is an error.
  */

@@ -29,14 +29,14 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 
 MMQ_OK, MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_LDS, MMQ_E_DEVICE, MMQ_E_HIP = range(6)
-MMQ_TILE_AUTO, MMQ_TILE_LARGE, MMQ_TILE_SMALL = 0, 1, 2
-(MMQ_REASON_NONE, MMQ_REASON_LARGE, MMQ_REASON_SMALL_M, MMQ_REASON_LDS_FALLBACK,
- MMQ_REASON_FORCED, MMQ_REASON_NO_FIT) = range(6)
-QK8, QK_K, Q4K_BLOCK_BYTES, REP_TILE_ROWS, REP_TILE_BYTES = 32, 256, 144, 32, 6144
+MMQ_TILE_AUTO, MMQ_TILE_LARGE, MMQ_TILE_SMALL, MMQ_TILE_SKINNY = 0, 1, 2, 3
+(MMQ_REASON_NONE, MMQ_REASON_LARGE, MMQ_REASON_SMALL_GRID, MMQ_REASON_LDS_FALLBACK,
+ MMQ_REASON_FORCED, MMQ_REASON_NO_FIT, MMQ_REASON_FEW_TOKENS) = range(7)
+QK8, QK_K, Q4K_BLOCK_BYTES, REP_TILE_ROWS, REP_TILE_BYTES = 32, 256, 144, 32, 6656
 
 
 class mmq_options(ctypes.Structure):
-    _fields_ = [("force_tile", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    _fields_ = [("force_tile", ctypes.c_int32), ("min_workgroups", ctypes.c_int32),
                 ("lds_budget", ctypes.c_int64)]
 
 
@@ -111,10 +111,10 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream
 
 
-def _opts(force_tile: int = MMQ_TILE_AUTO, lds_budget: int = 0):
-    if force_tile == MMQ_TILE_AUTO and lds_budget == 0:
+def _opts(force_tile: int = MMQ_TILE_AUTO, lds_budget: int = 0, min_workgroups: int = 0):
+    if force_tile == MMQ_TILE_AUTO and lds_budget == 0 and min_workgroups == 0:
         return None
-    return ctypes.byref(mmq_options(force_tile, 0, lds_budget))
+    return ctypes.byref(mmq_options(force_tile, min_workgroups, lds_budget))
 
 
 # ---------------------------------------------------------------- sizes
@@ -154,10 +154,11 @@ def mmq_q4K_q8_1(M: int, N: int, K: int, q8, w_rep, C, stream=None) -> None:
 
 
 def mmq_q4K_q8_1_ex(M: int, N: int, K: int, q8, w_rep, C, stream=None,
-                    force_tile: int = MMQ_TILE_AUTO, lds_budget: int = 0) -> None:
+                    force_tile: int = MMQ_TILE_AUTO, lds_budget: int = 0,
+                    min_workgroups: int = 0) -> None:
     _check("mmq_q4K_q8_1_ex",
            _lib.mmq_q4K_q8_1_ex(M, N, K, _ptr(q8), _ptr(w_rep), _ptr(C), _stream(stream),
-                                _opts(force_tile, lds_budget)))
+                                _opts(force_tile, lds_budget, min_workgroups)))
 
 
 def mmq_q4K_q8_1_blockdots(M: int, N: int, K: int, q8, w_rep, i0: int, i1: int, j0: int,
@@ -171,10 +172,10 @@ def mmq_q4K_q8_1_blockdots(M: int, N: int, K: int, q8, w_rep, i0: int, i1: int, 
 
 # ---------------------------------------------------------------- the guard
 def mmq_plan(M: int, N: int, K: int, lds_budget: int, force_tile: int = MMQ_TILE_AUTO,
-             opt_lds_budget: int = 0) -> dict:
+             opt_lds_budget: int = 0, min_workgroups: int = 0) -> dict:
     info = mmq_kernel_info()
-    _check("mmq_plan", _lib.mmq_plan(M, N, K, _opts(force_tile, opt_lds_budget), lds_budget,
-                                     ctypes.byref(info)))
+    _check("mmq_plan", _lib.mmq_plan(M, N, K, _opts(force_tile, opt_lds_budget, min_workgroups),
+                                     lds_budget, ctypes.byref(info)))
     return info.as_dict()
 
 

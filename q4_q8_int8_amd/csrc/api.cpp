@@ -36,10 +36,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every in-kernel 32-bit index in range
 constexpr int64_t kMaxK = (int64_t)1 << 24;
 
+constexpr int64_t kDefaultComputeUnits = 256;  // MI355X; mmq_plan assumes it
+// Up to this many tokens the skinny kernel (K split over the wavefronts of a workgroup) beats
+// the small tile: at K = N = 4096 it takes 7.7 / 9.8 / 24.6 us for M = 1 / 16 / 128 against
+// 28.8 / 28.8 / 30.6 us, and loses at M = 512 (85 against 42 us).
+constexpr int64_t kSkinnyMaxM = 128;
 struct DeviceInfo {
   std::once_flag once;
   int status = MMQ_OK;
   int64_t lds_budget = 0;
+  int64_t compute_units = kDefaultComputeUnits;
   char msg[256] = {0};
 };
 constexpr int kMaxDevices = 64;
@@ -80,6 +86,12 @@ int current_device(DeviceInfo** out) {
       lds_optin = 0;
     (void)hipGetLastError();  // an unsupported attribute query leaves no sticky error
     di.lds_budget = lds_optin > lds ? lds_optin : lds;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = kDefaultComputeUnits;
+    (void)hipGetLastError();
+    di.compute_units = cus;
   });
   if (di.status != MMQ_OK) return fail(di.status, "%s", di.msg);
   *out = &di;
@@ -100,15 +112,24 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 
 int check_options(const mmq_options* opt) {
   if (!opt) return MMQ_OK;
-  if (opt->force_tile < MMQ_TILE_AUTO || opt->force_tile > MMQ_TILE_SMALL)
+  if (opt->force_tile < MMQ_TILE_AUTO || opt->force_tile > MMQ_TILE_SKINNY)
     return fail(MMQ_E_ARG, "force_tile %d is not an mmq_tile", opt->force_tile);
   if (opt->lds_budget < 0) return fail(MMQ_E_ARG, "negative lds_budget");
+  if (opt->min_workgroups < 0) return fail(MMQ_E_ARG, "negative min_workgroups");
   return MMQ_OK;
 }
 
-int plan(int64_t M, int64_t N, const mmq_options* opt, int64_t budget, mmq_kernel_info* info) {
+// The guard: which tile, given the LDS budget and the compute units the grid should fill.
+int plan(int64_t M, int64_t N, const mmq_options* opt, int64_t budget, int64_t compute_units,
+         mmq_kernel_info* info) {
   memset(info, 0, sizeof(*info));
   if (opt && opt->lds_budget > 0) budget = opt->lds_budget;
+  const int64_t min_wg = opt && opt->min_workgroups > 0 ? opt->min_workgroups : compute_units;
+  auto grid_of = [&](const mmq::TileShape& ts) {
+    const int64_t gm = (M + ts.block_m() - 1) / ts.block_m();
+    const int64_t gn = ((N + 31) / 32 + ts.nw - 1) / ts.nw;
+    return gm * gn;
+  };
   info->lds_budget = budget;
   const int64_t need_large = mmq::kLarge.lds_bytes();
   const int64_t need_small = mmq::kSmall.lds_bytes();
@@ -119,9 +140,16 @@ int plan(int64_t M, int64_t N, const mmq_options* opt, int64_t budget, mmq_kerne
     if (need_large <= budget) { tile = MMQ_TILE_LARGE; reason = MMQ_REASON_FORCED; }
   } else if (forced == MMQ_TILE_SMALL) {
     if (need_small <= budget) { tile = MMQ_TILE_SMALL; reason = MMQ_REASON_FORCED; }
+  } else if (forced == MMQ_TILE_SKINNY) {
+    if (mmq::skinny_lds_bytes() <= budget) { tile = MMQ_TILE_SKINNY; reason = MMQ_REASON_FORCED; }
   } else if (need_large <= budget) {
-    if (M > 64) { tile = MMQ_TILE_LARGE; reason = MMQ_REASON_LARGE; }
-    else { tile = MMQ_TILE_SMALL; reason = MMQ_REASON_SMALL_M; }
+    if (grid_of(mmq::kLarge) >= min_wg) {
+      tile = MMQ_TILE_LARGE; reason = MMQ_REASON_LARGE;
+    } else if (M <= kSkinnyMaxM && mmq::skinny_lds_bytes() <= budget) {
+      tile = MMQ_TILE_SKINNY; reason = MMQ_REASON_FEW_TOKENS;
+    } else {
+      tile = MMQ_TILE_SMALL; reason = MMQ_REASON_SMALL_GRID;
+    }
   } else if (need_small <= budget) {
     tile = MMQ_TILE_SMALL; reason = MMQ_REASON_LDS_FALLBACK; fallback = 1;
   }
@@ -130,13 +158,21 @@ int plan(int64_t M, int64_t N, const mmq_options* opt, int64_t budget, mmq_kerne
     return fail(MMQ_E_LDS, "no GEMM tile fits %lld bytes of LDS (large needs %lld, small %lld)",
                 (long long)budget, (long long)need_large, (long long)need_small);
   }
+  info->tile = tile;
+  info->reason = reason;
+  info->fallback = fallback;
+  if (tile == MMQ_TILE_SKINNY) {
+    info->block_m = 32;
+    info->block_n = 32;
+    info->threads = 64 * mmq::kSkinnyWaves;
+    info->lds_bytes = mmq::skinny_lds_bytes();
+    info->grid = ((M + 31) / 32) * ((N + 31) / 32);
+    return MMQ_OK;
+  }
   const mmq::TileShape ts = tile == MMQ_TILE_LARGE ? mmq::kLarge : mmq::kSmall;
   const int64_t gm = (M + ts.block_m() - 1) / ts.block_m();
   const int64_t ntiles = (N + 31) / 32;
   const int64_t gn = (ntiles + ts.nw - 1) / ts.nw;
-  info->tile = tile;
-  info->reason = reason;
-  info->fallback = fallback;
   info->block_m = ts.block_m();
   info->block_n = ts.block_n();
   info->threads = ts.threads();
@@ -215,7 +251,7 @@ int mmq_plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t ld
   if (st) return st;
   if ((st = check_options(opt))) return st;
   if (lds_budget <= 0 && !(opt && opt->lds_budget > 0)) return fail(MMQ_E_ARG, "lds_budget must be positive");
-  if ((st = plan(M, N, opt, lds_budget, out))) return st;
+  if ((st = plan(M, N, opt, lds_budget, kDefaultComputeUnits, out))) return st;
   return ok();
 }
 
@@ -230,14 +266,19 @@ int mmq_q4K_q8_1_ex(int64_t M, int64_t N, int64_t K, const void* q8, const void*
   DeviceInfo* di;
   if ((st = current_device(&di))) return st;
   mmq_kernel_info info;
-  st = plan(M, N, opt, di->lds_budget, &info);
+  st = plan(M, N, opt, di->lds_budget, di->compute_units, &info);
   g_last = info;
   if (st) return st;
-  const mmq::TileShape ts = info.tile == MMQ_TILE_LARGE ? mmq::kLarge : mmq::kSmall;
-  const int64_t gm = (M + ts.block_m() - 1) / ts.block_m();
-  const int64_t gn = info.grid / gm;
-  hipError_t e = mmq::launch_mmq(info.tile, q8, w_rep, C, M, N, K, gm, gn, 0, 0, false, 0, 0,
-                                 0, 0, static_cast<hipStream_t>(stream));
+  hipError_t e;
+  if (info.tile == MMQ_TILE_SKINNY) {
+    e = mmq::launch_mmq_skinny(q8, w_rep, C, M, N, K, static_cast<hipStream_t>(stream));
+  } else {
+    const mmq::TileShape ts = info.tile == MMQ_TILE_LARGE ? mmq::kLarge : mmq::kSmall;
+    const int64_t gm = (M + ts.block_m() - 1) / ts.block_m();
+    const int64_t gn = info.grid / gm;
+    e = mmq::launch_mmq(info.tile, q8, w_rep, C, M, N, K, gm, gn, 0, 0, false, 0, 0, 0, 0,
+                        static_cast<hipStream_t>(stream));
+  }
   if (e != hipSuccess) return hip_fail("mmq_q4K_q8_1 launch", e);
   return ok();
 }
@@ -260,10 +301,17 @@ int mmq_q4K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, cons
     return fail(MMQ_E_SHAPE, "window [%lld,%lld) x [%lld,%lld) is empty or outside %lld x %lld",
                 (long long)i0, (long long)i1, (long long)j0, (long long)j1, (long long)M,
                 (long long)N);
+  if (opt && opt->force_tile == MMQ_TILE_SKINNY)
+    return fail(MMQ_E_ARG, "the skinny tile has no block-dot output; force large or small");
   DeviceInfo* di;
   if ((st = current_device(&di))) return st;
   mmq_kernel_info info;
-  st = plan(M, N, opt, di->lds_budget, &info);
+  st = plan(M, N, opt, di->lds_budget, di->compute_units, &info);
+  if (!st && info.tile == MMQ_TILE_SKINNY) {  // the block dots come from the small tile
+    mmq_options o = opt ? *opt : mmq_options{};
+    o.force_tile = MMQ_TILE_SMALL;
+    st = plan(M, N, &o, di->lds_budget, di->compute_units, &info);
+  }
   g_last = info;
   if (st) return st;
   const mmq::TileShape ts = info.tile == MMQ_TILE_LARGE ? mmq::kLarge : mmq::kSmall;

@@ -1,0 +1,58 @@
+// Device-side helpers shared by the GEMM kernels of libmmq (not part of the ABI): vector
+// types, raw buffer descriptors, and the direct-to-LDS load.
+#pragma once
+
+#include "mmq_internal.h"
+
+namespace mmq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Raw buffer descriptor over [p, p + bytes): reads at offsets >= bytes return zero.
+// The last descriptor word is the gfx9-family default data format (32-bit, untyped).
+static __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+static __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+static __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+// The same descriptor as four SGPRs, for the direct-to-LDS load below.
+static __device__ __forceinline__ v4i make_rsrc_sgpr(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+// 16 bytes per lane from the buffer at `off` into LDS at lds_base + 16 * lane (lds_base is
+// wave-uniform); completion is tracked by the vector-memory counter and waited for
+// explicitly before the barrier that ends a stage. The instruction is issued from inline
+// assembly on purpose: the compiler cannot tell which LDS bytes such a load writes, so for
+// the intrinsic it waits for every outstanding one before the next LDS read, which would
+// stall each wavefront on its own prefetch at the start of every stage. The asm declares no
+// memory effects on purpose too: it only writes the stage buffer that nothing reads until
+// after the explicit wait and the barrier (both ordered with the asm), and so the compiler
+// stays free to schedule the current stage's LDS reads around it.
+static __device__ __forceinline__ void dma16(v4i r, uint8_t* lds_base, uint32_t off) {
+  const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)lds_base);
+  int saved;  // m0 is reserved by the compiler: restore it after use
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(off), "s"(r));
+}
+
+}  // namespace mmq

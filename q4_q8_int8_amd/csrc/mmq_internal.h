@@ -79,6 +79,13 @@ __host__ __device__ inline void bf16_split3(float v, uint16_t& p1, uint16_t& p2,
   p3 = (uint16_t)(__builtin_bit_cast(uint32_t, c) >> 16);
 }
 
+// Skinny GEMM (few tokens): one 32 x 32 output tile per workgroup, K split over
+// kSkinnyWaves wavefronts and summed through LDS in wavefront order.
+constexpr int kSkinnyWaves = 8;
+int64_t skinny_lds_bytes();
+hipError_t launch_mmq_skinny(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
+                             int64_t K, hipStream_t s);
+
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, hipStream_t s);
 hipError_t launch_repack_q4_K(const void* w, int64_t N, int64_t K, void* w_rep, hipStream_t s);
 

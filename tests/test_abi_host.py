@@ -57,6 +57,7 @@ def test_size_null_out():
 
 # two stages of: token tile [BM][272], da [8][BM] f32, token pieces [3][BM][8] bf16, and per
 # wavefront dsv [8][32] f32 + dmv pieces [3][32][8] bf16
+LARGE, SMALL = mmq.MMQ_TILE_LARGE, mmq.MMQ_TILE_SMALL
 LARGE_LDS = 2 * (128 * 272 + 128 * 32 + 128 * 48 + 8 * 2560)
 SMALL_LDS = 2 * (32 * 272 + 32 * 32 + 32 * 48 + 2 * 2560)
 
@@ -81,10 +82,56 @@ def test_plan_lds_fallback_and_refusal():
     assert e.value.status == mmq.MMQ_E_LDS
 
 
-def test_plan_small_m_and_forced_tiles():
-    p = mmq.mmq_plan(16, 4096, 4096, 160 * 1024)
-    assert p["tile"] == mmq.MMQ_TILE_SMALL and p["reason"] == mmq.MMQ_REASON_SMALL_M
+SKINNY = mmq.MMQ_TILE_SKINNY
+REASON = {LARGE: mmq.MMQ_REASON_LARGE, SMALL: mmq.MMQ_REASON_SMALL_GRID,
+          SKINNY: mmq.MMQ_REASON_FEW_TOKENS}
+
+
+@pytest.mark.parametrize("M,N,tile", [
+    (1, 4096, SKINNY),      # large grid 1 x 16, few tokens
+    (16, 4096, SKINNY),
+    (128, 4096, SKINNY),
+    (129, 4096, SMALL),     # 2 x 16
+    (512, 4096, SMALL),     # 4 x 16 = 64 < 256 compute units
+    (1024, 4096, SMALL),    # 8 x 16 = 128
+    (2048, 4096, LARGE),    # 16 x 16 = 256
+    (1024, 11008, LARGE),   # 8 x 43 = 344
+    (128, 65536, LARGE),    # 1 x 256
+    (8192, 4096, LARGE),
+])
+def test_plan_prefers_a_grid_that_fills_the_gpu(M, N, tile):
+    p = mmq.mmq_plan(M, N, 4096, 160 * 1024)
+    assert p["tile"] == tile and p["reason"] == REASON[tile]
     assert p["fallback"] == 0
+
+
+def test_plan_min_workgroups_option():
+    assert mmq.mmq_plan(512, 4096, 4096, 160 * 1024, min_workgroups=64)["tile"] == LARGE
+    assert mmq.mmq_plan(512, 4096, 4096, 160 * 1024, min_workgroups=65)["tile"] == SMALL
+    assert mmq.mmq_plan(64, 4096, 4096, 160 * 1024, min_workgroups=16)["tile"] == LARGE
+    assert mmq.mmq_plan(2048, 4096, 4096, 160 * 1024, min_workgroups=257)["tile"] == SMALL
+
+
+def test_plan_skinny_tile():
+    p = mmq.mmq_plan(16, 4096, 4096, 160 * 1024, force_tile=mmq.MMQ_TILE_SKINNY)
+    assert p["tile"] == mmq.MMQ_TILE_SKINNY and p["reason"] == mmq.MMQ_REASON_FORCED
+    assert p["block_m"] == 32 and p["block_n"] == 32 and p["threads"] == 512
+    assert p["lds_bytes"] == 8 * 16 * 64 * 4 and p["grid"] == 1 * 128
+    p = mmq.mmq_plan(70, 100, 512, 160 * 1024, force_tile=mmq.MMQ_TILE_SKINNY)
+    assert p["grid"] == 3 * 4
+    with pytest.raises(mmq.MMQError) as e:
+        mmq.mmq_plan(16, 4096, 4096, 160 * 1024, force_tile=mmq.MMQ_TILE_SKINNY,
+                     opt_lds_budget=8 * 16 * 64 * 4 - 1)
+    assert e.value.status == mmq.MMQ_E_LDS
+
+
+def test_blockdots_refuse_the_skinny_tile():
+    opt = mmq.mmq_options(mmq.MMQ_TILE_SKINNY, 0, 0)
+    assert mmq.raw_call("mmq_q4K_q8_1_blockdots", 4, 8, 256, A, B, 0, 4, 0, 8, Cp, None,
+                        ctypes.byref(opt)) == mmq.MMQ_E_ARG
+
+
+def test_plan_forced_tiles():
     p = mmq.mmq_plan(16, 4096, 4096, 160 * 1024, force_tile=mmq.MMQ_TILE_LARGE)
     assert p["tile"] == mmq.MMQ_TILE_LARGE and p["reason"] == mmq.MMQ_REASON_FORCED
     p = mmq.mmq_plan(2048, 4096, 4096, 160 * 1024, force_tile=mmq.MMQ_TILE_SMALL)
@@ -102,7 +149,9 @@ def test_plan_ragged_grid():
     p = mmq.mmq_plan(2047, 11008, 4096, 160 * 1024)
     assert p["grid"] == 16 * 43
     p = mmq.mmq_plan(1, 33, 256, 160 * 1024)
-    assert p["grid"] == 1 and p["tile"] == mmq.MMQ_TILE_SMALL
+    assert p["grid"] == 2 and p["tile"] == mmq.MMQ_TILE_SKINNY
+    p = mmq.mmq_plan(1, 33, 256, 160 * 1024, force_tile=mmq.MMQ_TILE_SMALL)
+    assert p["grid"] == 1
 
 
 @pytest.mark.parametrize("args,status", [
@@ -151,6 +200,9 @@ def test_bad_options_rejected():
     assert mmq.raw_call("mmq_q4K_q8_1_ex", 4, 8, 256, A, B, Cp, None, ctypes.byref(bad)) == mmq.MMQ_E_ARG
     neg = mmq.mmq_options(0, 0, -1)
     assert mmq.raw_call("mmq_q4K_q8_1_ex", 4, 8, 256, A, B, Cp, None, ctypes.byref(neg)) == mmq.MMQ_E_ARG
+    neg_wg = mmq.mmq_options(0, -1, 0)
+    assert mmq.raw_call("mmq_q4K_q8_1_ex", 4, 8, 256, A, B, Cp, None,
+                        ctypes.byref(neg_wg)) == mmq.MMQ_E_ARG
 
 
 def test_status_strings():

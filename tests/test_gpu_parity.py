@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 mmq = pytest.importorskip("q4_q8_int8_amd")
 torch = pytest.importorskip("torch")
 
-LARGE, SMALL = mmq.MMQ_TILE_LARGE, mmq.MMQ_TILE_SMALL
+LARGE, SMALL, SKINNY = mmq.MMQ_TILE_LARGE, mmq.MMQ_TILE_SMALL, mmq.MMQ_TILE_SKINNY
 CONFIGS = ["tiny", "qproj", "gateup", "down"]
 SWEEP = [f"sweep_m{m}" for m in synth.SWEEP_M]
 
@@ -164,6 +164,37 @@ def test_mmq_sampled_rows(name):
     say("max |err|/T", r, "rows", len(rows))
 
 
+@pytest.mark.parametrize("name", ["tiny", "sweep_m1", "sweep_m16", "sweep_m128"])
+def test_mmq_skinny_every_element(name):
+    """The skinny kernel (K split over the wavefronts of a workgroup) on every element."""
+    W = workload(name)
+    M, N, K = W["M"], W["N"], W["K"]
+    q8 = gpu_quantize(W["x"])
+    rep = gpu_repack(W["w"], N, K)
+    say("mmq skinny", name, (M, N, K))
+    C = gpu_mmq(M, N, K, q8, rep, force_tile=SKINNY)
+    assert mmq.mmq_last_kernel()["tile"] == SKINNY
+    C_ref = oracle.mmq(oracle_q8(name), oracle_w(name))
+    _, T = oracle.mmq_terms(oracle_q8(name), oracle_w(name))
+    r = assert_within_tolerance(C, C_ref, T)
+    say("max |err|/T", r)
+
+
+def test_mmq_skinny_deterministic():
+    x = synth.activations("normal_outliers", 40, 2816, 15)
+    w, f = synth.q4k_weights("fit", 70, 2816, 16)
+    q8 = gpu_quantize(x)
+    rep = gpu_repack(w, 70, 2816)
+    say("mmq skinny deterministic")
+    a = gpu_mmq(40, 70, 2816, q8, rep, force_tile=SKINNY)
+    b = gpu_mmq(40, 70, 2816, q8, rep, force_tile=SKINNY)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    q = oracle.quantize_q8_1(x)
+    wo = oracle.decode_q4_K(w)
+    _, T = oracle.mmq_terms(q, wo)
+    assert_within_tolerance(a, oracle.mmq(q, wo), T)
+
+
 def test_mmq_tiles_agree_bitwise_and_deterministic():
     """Both tile instantiations add the same terms in the same order: identical bits."""
     x = synth.activations("normal_outliers", 300, 1024, 5)
@@ -183,7 +214,7 @@ def test_mmq_lds_fallback_reported():
     w, f = synth.q4k_weights("random_fields", 64, 512, 2)
     q8 = gpu_quantize(x)
     rep = gpu_repack(w, 64, 512)
-    large_lds = 2 * (128 * 272 + 128 * 64 + 8 * 2048)
+    large_lds = mmq.mmq_plan(96, 64, 512, 1 << 20, force_tile=LARGE)["lds_bytes"]
     say("mmq lds fallback")
     C = gpu_mmq(96, 64, 512, q8, rep, lds_budget=large_lds - 1)
     info = mmq.mmq_last_kernel()
@@ -209,7 +240,7 @@ def test_mmq_edge_shapes(M, N, K):
     wo = oracle.decode_q4_K(w)
     _, T = oracle.mmq_terms(q, wo)
     C_ref = oracle.mmq(q, wo)
-    for tile in (LARGE, SMALL):
+    for tile in (LARGE, SMALL, SKINNY):
         say("mmq edge", (M, N, K), tile)
         C = gpu_mmq(M, N, K, q8, rep, force_tile=tile)
         assert_within_tolerance(C, C_ref, T)
