@@ -1,4 +1,4 @@
-"""CPU oracle for the q4_K x q8_1 quantized matrix multiply (MMQ).
+"""CPU oracle for the q4_K x q8_1 quantized matrix multiply (MMQ) and its f16 comparator.
 
 TEST INFRASTRUCTURE ONLY. Only the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call anything here. The HIP
@@ -18,3 +18,4 @@ from .mmq_oracle import (  # noqa: F401
     decode_q4_K, q4_K_scales, dequantize_q4_K,
     mmq, block_dots, mmq_terms,
 )
+from .f16_oracle import convert_f32_f16, dequantize_q4_K_f16, gemm_f16  # noqa: F401

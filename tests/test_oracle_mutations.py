@@ -113,3 +113,76 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 def test_unmutated_oracle_passes_all_pins():
     for pin_name, pin in _pins().items():
         pin()
+
+
+# ----------------------------------------------------------------------------- f16 comparator
+import oracle.f16_oracle as fo  # noqa: E402
+import tests.test_oracle_f16_pins as f16pins  # noqa: E402
+
+_F16_ORIG = {"scales": fo.q4_K_scales, "dequant": fo.dequantize_q4_K_f16}
+
+
+def _f16_pins():
+    return {
+        "convert_values": f16pins.test_convert_hand_derived_values,
+        "convert_order": f16pins.test_convert_keeps_shape_and_order,
+        "dequant_golden": f16pins.test_dequant_hand_packed_block,
+        "dequant_int": f16pins.test_dequant_integer_case_exact,
+        "dequant_ulp": f16pins.test_dequant_within_one_ulp_of_the_exact_value,
+        "gemm_int": f16pins.test_gemm_integer_case_exact,
+        "gemm_rational": f16pins.test_gemm_exact_rationals_tiny,
+    }
+
+
+def _dequant_single_rounding(w):
+    # rounds the exact value straight to f16 instead of through float32
+    return oracle.f16_encode(oracle.dequantize_q4_K(w).astype(np.float16).astype(np.float32))
+
+
+def _f16_scales_flipped(w):
+    dsv, dmv = _F16_ORIG["scales"](w)
+    return dsv, -dmv
+
+
+def _convert_truncating(x):
+    x = np.asarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    # drop the 13 low significand bits (rounds toward zero for normal values)
+    t = (bits & ~np.uint64(0x1FFF)).astype(np.uint32).view(np.float32)
+    with np.errstate(over="ignore"):
+        return oracle.f16_encode(t)
+
+
+def _gemm_transposed(a_bits, w_bits):
+    a = oracle.f16_decode(a_bits)
+    w = oracle.f16_decode(w_bits)[:, ::-1]          # a misindexed K axis of the weights
+    return a @ w.T, np.abs(a) @ np.abs(w).T
+
+
+F16_MUTATIONS = {
+    "f16_single_rounding": ("dequantize_q4_K_f16", _dequant_single_rounding),
+    "f16_dmv_sign_flipped": ("q4_K_scales", _f16_scales_flipped),
+    "f16_convert_truncating": ("convert_f32_f16", _convert_truncating),
+    "f16_gemm_operand_transposed": ("gemm_f16", _gemm_transposed),
+}
+
+
+@pytest.mark.parametrize("name", sorted(F16_MUTATIONS))
+def test_planted_f16_mistake_is_caught(name, monkeypatch):
+    attr, bad = F16_MUTATIONS[name]
+    monkeypatch.setattr(fo, attr, bad)
+    if hasattr(oracle, attr) and attr != "q4_K_scales":
+        monkeypatch.setattr(oracle, attr, bad)
+    caught = []
+    for pin_name, pin in _f16_pins().items():
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except AssertionError:
+            caught.append(pin_name)
+    assert caught, f"no pin detects the planted mistake {name!r}"
+
+
+def test_unmutated_f16_oracle_passes_all_pins():
+    for pin_name, pin in _f16_pins().items():
+        pin()
