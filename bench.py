@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, tera-ops/s (1 MAC = 2 ops)
+F16_PEAK_TFLOPS = 2500.0         # MI355X dense f16 MFMA
 HBM_PEAK_GBS = 8000.0
 PAGES_QPROJ_TMACS = 15.19        # the pages' best q-proj MMQ kernel: 34.36 GMAC in 2.262 ms
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmq_qproj_traffic.json")
@@ -125,6 +126,8 @@ def measure(W: dict, R: int, steps: int, warmup: int, tile: int = 0) -> dict:
     def events():
         return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
+    mmq.repack_q4_K(w_dev, N, K, reps[0])   # the library's first launch loads its code object
+    torch.cuda.synchronize()
     ev_r0, ev_r1 = events()
     ev_r0.record(stream)
     for r in range(R):
@@ -183,6 +186,83 @@ def measure(W: dict, R: int, steps: int, warmup: int, tile: int = 0) -> dict:
             "gemm_us": g_ms * 1e3, "quant_us": q_ms * 1e3, "repack_us": repack_us, "plan": plan}
 
 
+def measure_f16(W: dict, R: int, steps: int, warmup: int) -> dict:
+    """Time the f16 comparator path on one workload: f32 -> f16 conversion of the activations,
+    q4_K -> f16 dequantization of the weights, and the f16 GEMM, each as `steps`
+    back-to-back launches between one pair of HIP events (inputs rotating over R copies as in
+    measure()), and the two whole paths: per call (convert + dequantize + GEMM, the weights
+    kept in q4_K) and with the weights resident in f16 (convert + GEMM)."""
+    import torch
+
+    import q4_q8_int8_amd as mmq
+
+    dev = torch.device("cuda:0")
+    M, N, K = W["M"], W["N"], W["K"]
+    stream = torch.cuda.current_stream()
+    xs = [torch.from_numpy(W["x"]).to(dev) for _ in range(R)]
+    ws = [torch.from_numpy(W["w"]).to(dev) for _ in range(R)]
+    x16 = [torch.empty(M * K, dtype=torch.float16, device=dev) for _ in range(R)]
+    w16 = [torch.empty(N * K, dtype=torch.float16, device=dev) for _ in range(R)]
+    Cs = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(R)]
+
+    def conv(r):
+        mmq.convert_f32_f16(xs[r], M, K, x16[r])
+
+    def deq(r):
+        mmq.dequantize_q4_K_f16(ws[r], N, K, w16[r])
+
+    def gemm(r):
+        mmq.gemm_f16(M, N, K, x16[r], w16[r], Cs[r])
+
+    def per_call(r):
+        conv(r)
+        deq(r)
+        gemm(r)
+
+    def resident(r):
+        conv(r)
+        gemm(r)
+
+    def avg_us(launch):
+        for i in range(warmup):
+            launch(i % R)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            launch(i % R)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    out = {"convert_us": avg_us(conv), "dequant_us": avg_us(deq), "gemm_us": avg_us(gemm),
+           "per_call_us": avg_us(per_call), "resident_us": avg_us(resident)}
+    del xs, ws, x16, w16, Cs
+    torch.cuda.empty_cache()
+    return out
+
+
+def f16_summary(M: int, N: int, K: int, f: dict) -> dict:
+    """The comparator's times, throughput and HBM fractions of its two own kernels."""
+    macs = M * N * K
+    conv_bytes = 6 * M * K                       # f32 in, f16 out
+    deq_bytes = N * (K // 256) * 144 + 2 * N * K  # q4_K in, f16 out
+    return {"path": "f32->f16 convert + q4_K->f16 dequantize + f16 MFMA GEMM (f32 out)",
+            "dtype": "f16",
+            "convert_us": round(f["convert_us"], 2),
+            "convert_hbm_frac": round(conv_bytes / (f["convert_us"] * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+            "dequant_us": round(f["dequant_us"], 2),
+            "dequant_hbm_frac": round(deq_bytes / (f["dequant_us"] * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+            "gemm_us": round(f["gemm_us"], 2),
+            "gemm_tmacs": round(macs / (f["gemm_us"] * 1e-6) / 1e12, 2),
+            "gemm_f16_peak_frac": round(2 * macs / (f["gemm_us"] * 1e-6) / 1e12 / F16_PEAK_TFLOPS, 4),
+            "per_call_us": round(f["per_call_us"], 2),
+            "per_call_tmacs": round(macs / (f["per_call_us"] * 1e-6) / 1e12, 2),
+            "weights_resident_us": round(f["resident_us"], 2),
+            "weights_resident_tmacs": round(macs / (f["resident_us"] * 1e-6) / 1e12, 2)}
+
+
 def gemm_bytes(M: int, N: int, K: int) -> int:
     """Algorithmic HBM bytes of one GEMM launch: the q8 buffer and the repacked weights in,
     C out."""
@@ -224,12 +304,19 @@ def sweep(args) -> int:
             t = measure(W, args.rotate, args.steps, args.warmup, tile)
             times[(name, tile)] = t
             print(json.dumps(config_line(name, W, t)), flush=True)
+        if not args.no_f16:
+            f = measure_f16(W, args.rotate, args.steps, args.warmup)
+            times[(name, "f16")] = f
+            print(json.dumps({"config": name, "M": W["M"], "N": W["N"], "K": W["K"],
+                              "comparator_f16": f16_summary(W["M"], W["N"], W["K"], f)}),
+                  flush=True)
         del W
     # 7-projection prefill of a 32-layer 7B at 2048 tokens, GEMM-only: per layer q, k, v, o
     # are q-proj shaped, gate and up gate/up shaped, down down shaped; three K=4096
     # activations (attention input, attention output, FFN input) and one K=11008 one are
     # quantized. Each product takes its faster tile.
-    best = {n: min((t for (c, _), t in times.items() if c == n), key=lambda t: t["gemm_us"])
+    best = {n: min((t for (c, k), t in times.items() if c == n and k != "f16"),
+                   key=lambda t: t["gemm_us"])
             for n in ("qproj", "gateup", "down")}
     layer_gemm = 4 * best["qproj"]["gemm_us"] + 2 * best["gateup"]["gemm_us"] \
         + best["down"]["gemm_us"]
@@ -243,6 +330,25 @@ def sweep(args) -> int:
                       "tmacs": round(macs / (total_us * 1e-6) / 1e12, 2),
                       "note": "sum of per-kernel averages of the 3 distinct shapes, x32 layers; "
                               "GEMM-only prefill, not whole-model"}), flush=True)
+    if not args.no_f16:
+        # the same prefill on the f16 comparator: per call (weights dequantized each product)
+        # and with the weights resident in f16
+        f16 = {n: times[(n, "f16")] for n in ("qproj", "gateup", "down")}
+        layer_gemm = 4 * f16["qproj"]["gemm_us"] + 2 * f16["gateup"]["gemm_us"] \
+            + f16["down"]["gemm_us"]
+        layer_deq = 4 * f16["qproj"]["dequant_us"] + 2 * f16["gateup"]["dequant_us"] \
+            + f16["down"]["dequant_us"]
+        layer_conv = 3 * f16["qproj"]["convert_us"] + f16["down"]["convert_us"]
+        for mode, layer in (("per_call", layer_gemm + layer_deq + layer_conv),
+                            ("weights_resident", layer_gemm + layer_conv)):
+            total = 32 * layer
+            print(json.dumps({"config": "prefill_7shape_32layer_f16", "mode": mode,
+                              "tokens": 2048, "tok_per_s": round(2048 / (total * 1e-6), 1),
+                              "ms": round(total * 1e-3, 3),
+                              "tmacs": round(macs / (total * 1e-6) / 1e12, 2),
+                              "note": "f16 comparator, sum of per-kernel averages x32 layers; "
+                                      "per_call dequantizes every weight matrix"}),
+                  flush=True)
     return 0
 
 
@@ -255,6 +361,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
+    ap.add_argument("--no-f16", action="store_true",
+                    help="skip the f16 comparator path's timing")
     ap.add_argument("--sweep", action="store_true",
                     help="per-config table (one JSON line per config and tile) instead of the "
                          "benchmark line")
@@ -317,6 +425,8 @@ def main() -> int:
                                        4)},
         "repack_us_once": round(t["repack_us"], 2),
     }
+    if not args.no_f16:
+        out["comparator_f16"] = f16_summary(M, N, K, measure_f16(W, R, args.steps, args.warmup))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W)
     print(json.dumps(out), flush=True)

@@ -1,6 +1,7 @@
 """q4_K x q8_1 quantized matrix multiply (MMQ) on MI355X (gfx950).
 
-A thin ctypes binding over libmmq.so, whose C ABI is declared in include/mmq.h. The
+A thin ctypes binding over libmmq.so, whose C ABI is declared in include/mmq.h (the integer
+product) and include/mmq_f16.h (the f16 comparator path). The
 functions here have the same names and arguments as the C entry points and only marshal
 arguments: tensors are passed as device pointers, the stream defaults to torch's current
 stream, and a nonzero status raises MMQError. Every step of the computation runs in the
@@ -16,7 +17,9 @@ import re
 _PKG = os.path.dirname(os.path.abspath(__file__))
 # MMQ_LIBRARY may name another build of the same library (e.g. a tile-shape variant)
 LIB_PATH = os.environ.get("MMQ_LIBRARY") or os.path.join(_PKG, "libmmq.so")
-HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "mmq.h")
+INCLUDE_DIR = os.path.join(os.path.dirname(_PKG), "include")
+HEADER_PATH = os.path.join(INCLUDE_DIR, "mmq.h")
+HEADER_PATHS = (HEADER_PATH, os.path.join(INCLUDE_DIR, "mmq_f16.h"))
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m q4_q8_int8_amd.build`")
@@ -73,6 +76,10 @@ _SIGS = {
     "mmq_plan": [_i64, _i64, _i64, ctypes.POINTER(mmq_options), _i64,
                  ctypes.POINTER(mmq_kernel_info)],
     "mmq_last_kernel": [ctypes.POINTER(mmq_kernel_info)],
+    "mmq_f16_bytes": [_i64, _i64, ctypes.POINTER(_sz)],
+    "convert_f32_f16": [_vp, _i64, _i64, _vp, _vp],
+    "dequantize_q4_K_f16": [_vp, _i64, _i64, _vp, _vp],
+    "gemm_f16": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "mmq_status_str": [ctypes.c_int],
     "mmq_last_error": [],
 }
@@ -83,11 +90,14 @@ for _name, _args in _SIGS.items():
 
 
 def exported_symbols() -> list[str]:
-    """Function names declared in include/mmq.h."""
-    with open(HEADER_PATH) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    """Function names declared in the library's headers (include/mmq.h, include/mmq_f16.h)."""
+    names = []
+    for path in HEADER_PATHS:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return names
 
 
 def _check(fn: str, status: int) -> None:
@@ -177,6 +187,29 @@ def mmq_plan(M: int, N: int, K: int, lds_budget: int, force_tile: int = MMQ_TILE
     _check("mmq_plan", _lib.mmq_plan(M, N, K, _opts(force_tile, opt_lds_budget, min_workgroups),
                                      lds_budget, ctypes.byref(info)))
     return info.as_dict()
+
+
+# ---------------------------------------------------------------- the f16 comparator path
+def mmq_f16_bytes(rows: int, K: int) -> int:
+    n = _sz()
+    _check("mmq_f16_bytes", _lib.mmq_f16_bytes(rows, K, ctypes.byref(n)))
+    return n.value
+
+
+def convert_f32_f16(x, M: int, K: int, x_f16, stream=None) -> None:
+    """x: f32 [M, K] device tensor; x_f16: device buffer of mmq_f16_bytes(M, K) bytes."""
+    _check("convert_f32_f16", _lib.convert_f32_f16(_ptr(x), M, K, _ptr(x_f16), _stream(stream)))
+
+
+def dequantize_q4_K_f16(w_q4K, N: int, K: int, w_f16, stream=None) -> None:
+    """w_q4K: q4_K blocks (mmq_q4K_bytes); w_f16: mmq_f16_bytes(N, K) bytes."""
+    _check("dequantize_q4_K_f16",
+           _lib.dequantize_q4_K_f16(_ptr(w_q4K), N, K, _ptr(w_f16), _stream(stream)))
+
+
+def gemm_f16(M: int, N: int, K: int, x_f16, w_f16, C, stream=None) -> None:
+    """C[M, N] (f32 device tensor) = x_f16 [M, K] times w_f16 [N, K]^T, f32 accumulation."""
+    _check("gemm_f16", _lib.gemm_f16(M, N, K, _ptr(x_f16), _ptr(w_f16), _ptr(C), _stream(stream)))
 
 
 def mmq_last_kernel() -> dict:

@@ -11,6 +11,7 @@
 #include <mutex>
 
 #include "mmq.h"
+#include "mmq_f16.h"
 #include "mmq_internal.h"
 
 namespace {
@@ -324,6 +325,71 @@ int mmq_q4K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, cons
   hipError_t e = mmq::launch_mmq(info.tile, q8, w_rep, S, M, N, K, gm, gn, tm0, tn0, true, i0,
                                  i1, j0, j1, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("mmq_q4K_q8_1_blockdots launch", e);
+  return ok();
+}
+
+// ---------------------------------------------------------------- f16 comparator path
+
+int mmq_f16_bytes(int64_t rows, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(MMQ_E_ARG, "bytes is NULL");
+  if (rows <= 0 || K <= 0) return fail(MMQ_E_ARG, "rows and K must be positive");
+  if (rows > kMaxDim || K > kMaxDim || (__int128)rows * K > ((__int128)1 << 40))
+    return fail(MMQ_E_SHAPE, "f16 matrix too large");
+  *bytes = (size_t)rows * (size_t)K * 2;
+  return ok();
+}
+
+int convert_f32_f16(const float* x, int64_t M, int64_t K, void* x_f16, void* stream) {
+  size_t nb;
+  int st = mmq_f16_bytes(M, K, &nb);
+  if (st) return st;
+  if (!x || !x_f16) return fail(MMQ_E_ARG, "null device pointer");
+  if (!aligned16(x) || !aligned16(x_f16))
+    return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
+  DeviceInfo* di;
+  if ((st = current_device(&di))) return st;
+  hipError_t e = mmq::launch_convert_f32_f16(x, M * K, x_f16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("convert_f32_f16 launch", e);
+  return ok();
+}
+
+int dequantize_q4_K_f16(const void* w_q4K, int64_t N, int64_t K, void* w_f16, void* stream) {
+  size_t nb;
+  int st = mmq_q4K_bytes(N, K, &nb);
+  if (st) return st;
+  if ((st = mmq_f16_bytes(N, K, &nb))) return st;
+  if (!w_q4K || !w_f16) return fail(MMQ_E_ARG, "null device pointer");
+  if (!aligned16(w_q4K) || !aligned16(w_f16))
+    return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
+  DeviceInfo* di;
+  if ((st = current_device(&di))) return st;
+  hipError_t e =
+      mmq::launch_dequantize_q4_K_f16(w_q4K, N, K, w_f16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("dequantize_q4_K_f16 launch", e);
+  return ok();
+}
+
+int gemm_f16(int64_t M, int64_t N, int64_t K, const void* x_f16, const void* w_f16, float* C,
+             void* stream) {
+  if (M <= 0 || N <= 0 || K <= 0)
+    return fail(MMQ_E_ARG, "M, N, K must be positive (%lld, %lld, %lld)", (long long)M,
+                (long long)N, (long long)K);
+  if (K % 8) return fail(MMQ_E_SHAPE, "K = %lld is not a multiple of 8", (long long)K);
+  // the kernel addresses each operand with 32-bit byte offsets below 2^31
+  if (M > kMaxDim || N > kMaxDim || (__int128)M * K >= ((__int128)1 << 30) ||
+      (__int128)N * K >= ((__int128)1 << 30))
+    return fail(MMQ_E_SHAPE, "an f16 operand of 2^30 or more elements");
+  if (!x_f16 || !w_f16 || !C) return fail(MMQ_E_ARG, "null device pointer");
+  if (!aligned16(x_f16) || !aligned16(w_f16) || !aligned16(C))
+    return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
+  DeviceInfo* di;
+  int st;
+  if ((st = current_device(&di))) return st;
+  if (mmq::gemm_f16_lds_bytes() > di->lds_budget)
+    return fail(MMQ_E_LDS, "the f16 GEMM needs %lld bytes of LDS, the device allows %lld",
+                (long long)mmq::gemm_f16_lds_bytes(), (long long)di->lds_budget);
+  hipError_t e = mmq::launch_gemm_f16(x_f16, w_f16, C, M, N, K, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("gemm_f16 launch", e);
   return ok();
 }
 

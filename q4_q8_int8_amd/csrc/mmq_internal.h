@@ -97,4 +97,13 @@ hipError_t launch_mmq(int tile, const void* q8, const void* w_rep, void* out, in
                       bool store_s, int64_t i0, int64_t i1, int64_t j0, int64_t j1,
                       hipStream_t s);
 
+// The f16 comparator path: f32 -> f16 conversion of n values, q4_K -> f16 dequantization,
+// and the f16 GEMM (K % 8 == 0, 2*M*K and 2*N*K below 2^31).
+hipError_t launch_convert_f32_f16(const float* x, int64_t n, void* y, hipStream_t s);
+hipError_t launch_dequantize_q4_K_f16(const void* w, int64_t N, int64_t K, void* out,
+                                      hipStream_t s);
+hipError_t launch_gemm_f16(const void* x, const void* w, float* C, int64_t M, int64_t N,
+                           int64_t K, hipStream_t s);
+int64_t gemm_f16_lds_bytes();
+
 }  // namespace mmq

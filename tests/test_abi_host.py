@@ -209,3 +209,51 @@ def test_status_strings():
     for s in range(6):
         assert mmq.mmq_status_str(s).startswith("MMQ_")
     assert "unknown" in mmq.mmq_status_str(99)
+
+
+# ---------------------------------------------------------------- the f16 comparator path
+def test_f16_sizes():
+    assert mmq.mmq_f16_bytes(2048, 4096) == 2 * 2048 * 4096
+    assert mmq.mmq_f16_bytes(1, 1) == 2
+    assert mmq.mmq_f16_bytes(3, 5) == 30
+    n = ctypes.c_size_t()
+    assert mmq.raw_call("mmq_f16_bytes", 0, 8, ctypes.byref(n)) == mmq.MMQ_E_ARG
+    assert mmq.raw_call("mmq_f16_bytes", 1 << 31, 8, ctypes.byref(n)) == mmq.MMQ_E_SHAPE
+    assert mmq.raw_call("mmq_f16_bytes", 4, 8, None) == mmq.MMQ_E_ARG
+
+
+@pytest.mark.parametrize("call,status", [
+    (("convert_f32_f16", None, 4, 64, B, None), mmq.MMQ_E_ARG),
+    (("convert_f32_f16", A, 4, 64, None, None), mmq.MMQ_E_ARG),
+    (("convert_f32_f16", A + 4, 4, 64, B, None), mmq.MMQ_E_ARG),
+    (("convert_f32_f16", A, 4, 64, B + 2, None), mmq.MMQ_E_ARG),
+    (("convert_f32_f16", A, 0, 64, B, None), mmq.MMQ_E_ARG),
+    (("convert_f32_f16", A, 4, -1, B, None), mmq.MMQ_E_ARG),
+    (("dequantize_q4_K_f16", A, 4, 200, B, None), mmq.MMQ_E_SHAPE),
+    (("dequantize_q4_K_f16", None, 4, 256, B, None), mmq.MMQ_E_ARG),
+    (("dequantize_q4_K_f16", A, 4, 256, B + 8, None), mmq.MMQ_E_ARG),
+    (("dequantize_q4_K_f16", A, 0, 256, B, None), mmq.MMQ_E_ARG),
+    (("gemm_f16", 0, 8, 16, A, B, Cp, None), mmq.MMQ_E_ARG),
+    (("gemm_f16", 4, 8, 12, A, B, Cp, None), mmq.MMQ_E_SHAPE),        # K % 8
+    (("gemm_f16", 1 << 20, 8, 1 << 10, A, B, Cp, None), mmq.MMQ_E_SHAPE),  # M*K = 2^30
+    (("gemm_f16", 4, 1 << 21, 1 << 9, A, B, Cp, None), mmq.MMQ_E_SHAPE),   # N*K = 2^30
+    (("gemm_f16", 4, 8, 16, None, B, Cp, None), mmq.MMQ_E_ARG),
+    (("gemm_f16", 4, 8, 16, A, B + 8, Cp, None), mmq.MMQ_E_ARG),
+    (("gemm_f16", 4, 8, 16, A, B, Cp + 4, None), mmq.MMQ_E_ARG),
+])
+def test_f16_path_validation(call, status):
+    assert mmq.raw_call(*call) == status
+    assert mmq.mmq_last_error() != ""
+
+
+@pytest.mark.parametrize("call", [
+    ("convert_f32_f16", A, 4, 64, B, None),
+    ("dequantize_q4_K_f16", A, 4, 256, B, None),
+    ("gemm_f16", 4, 8, 16, A, B, Cp, None),
+])
+def test_f16_path_reaches_the_device_check(call):
+    # well-formed arguments pass validation; without a GPU the device check refuses them
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: the call would run")
+    assert mmq.raw_call(*call) == mmq.MMQ_E_DEVICE

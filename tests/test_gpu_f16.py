@@ -1,0 +1,198 @@
+"""Parity of the f16 comparator path with its CPU oracle, through the C ABI (needs a GPU).
+
+Bars:
+- convert_f32_f16 and dequantize_q4_K_f16: the f16 bytes are bit-exact.
+- gemm_f16: |C_gpu - C_ref| <= K * 2^-24 * T per element, where C_ref is the exact product
+  of the f16 operands and T = sum over k of |a_ik * w_jk|.
+  Why this bound: every product of two f16 values is exact in float32, and any order of
+  float32 additions of K such terms, each rounded once, stays within (K - 1) * 2^-24 * T
+  (the matrix instruction adds its 16 products per step with no more than that). The
+  measured ratio is far below it (printed).
+The operands of the GEMM come from the oracle's own conversion and dequantization of the
+seeded inputs, so a GEMM case does not depend on the other two kernels.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import oracle_w, sample_rows, say, to_dev, workload
+from tests.test_oracle_f16_pins import _F16_CASES
+
+pytestmark = pytest.mark.gpu
+
+mmq = pytest.importorskip("q4_q8_int8_amd")
+torch = pytest.importorskip("torch")
+
+CONFIGS = ["tiny", "qproj", "gateup", "down"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the gpu tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_convert(x: np.ndarray) -> np.ndarray:
+    M, K = x.shape
+    out = torch.full((M * K,), 0x7E00, dtype=torch.int16, device="cuda")   # NaN-filled
+    mmq.convert_f32_f16(to_dev(x.astype(np.float32)), M, K, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16).reshape(M, K)
+
+
+def gpu_dequant(w: np.ndarray, N: int, K: int) -> np.ndarray:
+    assert w.shape == (N, K // 256, 144)
+    out = torch.full((N * K,), 0x7E00, dtype=torch.int16, device="cuda")
+    mmq.dequantize_q4_K_f16(to_dev(w), N, K, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16).reshape(N, K)
+
+
+def gpu_gemm(a_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    M, K = a_bits.shape
+    N = w_bits.shape[0]
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    mmq.gemm_f16(M, N, K, to_dev(a_bits.view(np.int16)), to_dev(w_bits.view(np.int16)), C)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+def check_gemm(C_gpu, a_bits, w_bits, K):
+    C_ref, T = oracle.gemm_f16(a_bits, w_bits)
+    assert np.all(np.isfinite(C_gpu)), "non-finite output"
+    err = np.abs(C_gpu.astype(np.float64) - C_ref)
+    tol = K * 2.0 ** -24
+    bad = err > tol * T
+    assert not bad.any(), f"{bad.sum()} elements outside K*2^-24*T, first {np.argwhere(bad)[:5]}"
+    pos = T > 0
+    ratio = float((err[pos] / T[pos]).max()) if pos.any() else 0.0
+    print(f"[f16 gemm] max |err|/T = {ratio:.3e} (bound {tol:.3e})")
+    return ratio
+
+
+# ----------------------------------------------------------------------------- conversion
+@pytest.mark.parametrize("name", CONFIGS)
+def test_convert_bitexact(name):
+    x = workload(name)["x"]
+    say("convert_f32_f16", name, x.shape)
+    assert np.array_equal(gpu_convert(x), oracle.convert_f32_f16(x))
+
+
+def test_convert_special_values():
+    vals = np.array([v for v, _ in _F16_CASES], dtype=np.float32)
+    rng = np.random.default_rng(11)
+    # magnitudes over the whole f16 range, subnormals and overflow included, both signs
+    spread = (np.exp2(rng.uniform(-27, 17, 4093)) * rng.choice([-1, 1], 4093)).astype(np.float32)
+    x = np.concatenate([vals, spread])[None, :]
+    say("convert special values", x.shape)
+    assert np.array_equal(gpu_convert(x), oracle.convert_f32_f16(x))
+
+
+@pytest.mark.parametrize("M,K", [(1, 1), (3, 5), (7, 13), (1, 8), (129, 4099)])
+def test_convert_ragged(M, K):
+    x = synth.activations("normal_outliers", M, K, 7 * M + K)
+    say("convert ragged", M, K)
+    assert np.array_equal(gpu_convert(x), oracle.convert_f32_f16(x))
+
+
+# ----------------------------------------------------------------------------- dequantization
+@pytest.mark.parametrize("name", CONFIGS)
+def test_dequant_bitexact(name):
+    W = workload(name)
+    say("dequantize_q4_K_f16", name, W["N"], W["K"])
+    got = gpu_dequant(W["w"], W["N"], W["K"])
+    assert np.array_equal(got, oracle.dequantize_q4_K_f16(oracle_w(name)))
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (33, 512), (95, 768)])
+def test_dequant_ragged_rows(N, K):
+    w = synth.q4k_pack(synth.q4k_random_fields(N, K, 3 * N + K))
+    say("dequant ragged", N, K)
+    assert np.array_equal(gpu_dequant(w, N, K), oracle.dequantize_q4_K_f16(oracle.decode_q4_K(w)))
+
+
+def test_dequant_double_rounding_block(golden_dir):
+    """The hand-derived block whose float32 value lands on an f16 tie, plus fields with a
+    tiny dmin beside a large d, where such ties are common: the GPU takes the two-step
+    rounding, as the oracle does."""
+    with open(os.path.join(golden_dir, "q4_K_f16_dequant.json")) as f:
+        g = json.load(f)
+    blk = np.frombuffer(bytes.fromhex(g["bytes_hex"]), dtype=np.uint8)
+    rng = np.random.default_rng(21)
+    N, K = 64, 1024
+    f = synth.q4k_random_fields(N, K, 21)
+    f["d_bits"] = np.float16(rng.uniform(0.01, 2.0, f["d_bits"].shape)).view(np.uint16)
+    f["dmin_bits"] = rng.integers(1, 64, f["dmin_bits"].shape).astype(np.uint16)  # subnormal
+    w = synth.q4k_pack(f)
+    w[5, 2] = blk
+    want = oracle.dequantize_q4_K_f16(oracle.decode_q4_K(w))
+    single = oracle.f16_encode(oracle.dequantize_q4_K(oracle.decode_q4_K(w))
+                               .astype(np.float16).astype(np.float32))
+    assert np.count_nonzero(want != single) > 10, "the case must hold double-rounding ties"
+    say("dequant double rounding", N, K)
+    got = gpu_dequant(w, N, K)
+    assert np.array_equal(got, want), f"{np.count_nonzero(got != want)} values differ"
+
+
+# ----------------------------------------------------------------------------- the GEMM
+def test_gemm_tiny_every_element():
+    W = workload("tiny")
+    a = oracle.convert_f32_f16(W["x"])
+    w = oracle.dequantize_q4_K_f16(oracle_w("tiny"))
+    say("gemm_f16 tiny", a.shape, w.shape)
+    check_gemm(gpu_gemm(a, w), a, w, W["K"])
+
+
+# one partial stage of 64 k, a tail stage, ragged tiles in M and N, single tokens and features
+@pytest.mark.parametrize("M,N,K", [(1, 1, 8), (3, 5, 8), (17, 33, 104), (1, 4096, 4096),
+                                   (129, 257, 512), (300, 64, 4096), (257, 129, 136),
+                                   (2048, 4100, 256)])
+def test_gemm_ragged_and_degenerate(M, N, K):
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    a = oracle.convert_f32_f16(synth.activations("normal_outliers", M, K, M + N + K))
+    w = oracle.convert_f32_f16((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    say("gemm_f16 ragged", M, N, K)
+    check_gemm(gpu_gemm(a, w), a, w, K)
+
+
+@pytest.mark.parametrize("name", ["qproj", "gateup", "down"])
+def test_gemm_full_size_sampled_rows(name):
+    W = workload(name)
+    a = oracle.convert_f32_f16(W["x"])
+    w = oracle.dequantize_q4_K_f16(oracle_w(name))
+    say("gemm_f16 full size", name, a.shape, w.shape)
+    C = gpu_gemm(a, w)
+    rows = sample_rows(W["M"])
+    check_gemm(C[rows], a[rows], w, W["K"])
+
+
+def test_gemm_deterministic():
+    W = workload("tiny")
+    a = oracle.convert_f32_f16(W["x"])
+    w = oracle.dequantize_q4_K_f16(oracle_w("tiny"))
+    say("gemm_f16 twice", a.shape, w.shape)
+    assert np.array_equal(gpu_gemm(a, w), gpu_gemm(a, w))
+
+
+def test_comparator_end_to_end_qproj():
+    """The whole comparator on the GPU: convert, dequantize, multiply, against the oracle
+    chain, on sampled rows at the q-proj size."""
+    W = workload("qproj")
+    M, N, K = W["M"], W["N"], W["K"]
+    say("comparator end to end", M, N, K)
+    xa = torch.empty(M * K, dtype=torch.int16, device="cuda")
+    wf = torch.empty(N * K, dtype=torch.int16, device="cuda")
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    mmq.convert_f32_f16(to_dev(W["x"]), M, K, xa)
+    mmq.dequantize_q4_K_f16(to_dev(W["w"]), N, K, wf)
+    mmq.gemm_f16(M, N, K, xa, wf, C)
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    a = oracle.convert_f32_f16(W["x"][rows])
+    w = oracle.dequantize_q4_K_f16(oracle_w("qproj"))
+    check_gemm(C.cpu().numpy()[rows], a, w, K)
