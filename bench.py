@@ -17,6 +17,10 @@ between synchronizations. The GEMM kernel's own average duration, from HIP event
 back-to-back launches on the stream it runs on, gives the roofline entry against the dense
 int8 MFMA peak; its HBM traffic comes from the committed rocprofv3 counter summary of the
 same kernel source (null once the kernel has changed since the counters were taken).
+
+The line also carries `comparator_f16`: the same workload through the f16 comparator path
+(convert_f32_f16, dequantize_q4_K_f16, gemm_f16), each kernel timed the same way, and the
+two whole paths: per call, and with the weights resident in f16. `--no-f16` skips it.
 """
 from __future__ import annotations
 

@@ -5,9 +5,11 @@
 //
 // Workgroup tile: 256 tokens x 128 output features, 4 wavefronts in a 2 x 2 arrangement, each
 // owning 128 tokens x 64 features (4 x 2 tiles of 32 x 32, 128 accumulator registers). K is
-// staged 64 at a time through LDS, double-buffered: while a stage is multiplied, the next
-// one is loaded straight from global memory into the other LDS buffer (direct-to-LDS loads,
-// 16 bytes per lane). A tile row of 64 halves is 8 chunks of 16 bytes; chunk c of row r sits
+// staged 64 at a time through a ring of kStages LDS buffers: while a stage is multiplied,
+// the next kStages - 1 are in flight, loaded straight from global memory into LDS
+// (direct-to-LDS loads, 16 bytes per lane). A stage is 0.5 us of matrix work per compute
+// unit, shorter than a load's latency under full load, so one stage in flight (double
+// buffering) leaves the matrix units waiting for memory; two cover it. A tile row of 64 halves is 8 chunks of 16 bytes; chunk c of row r sits
 // in slot c ^ ((r >> 1) & 7) of its 128-byte LDS row, so that the fragment reads (32 rows
 // at one chunk, per half-wavefront) hit 16 distinct 16-byte bank groups per 16 lanes, while
 // each group of 8 lanes of a load still reads one row's 128 contiguous bytes.
@@ -29,17 +31,54 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kBM = 256, kBN = 128, kBK = 64;
 constexpr int kThreads = 256;
-constexpr int kAStage = kBM * kBK * 2;        // 32 KiB
-constexpr int kBStage = kBN * kBK * 2;        // 16 KiB
-constexpr int kStage = kAStage + kBStage;     // 48 KiB
-constexpr int kLds = 2 * kStage;              // 96 KiB
+constexpr uint32_t kAStage = kBM * kBK * 2;   // 32 KiB
+constexpr uint32_t kBStage = kBN * kBK * 2;   // 16 KiB
+constexpr uint32_t kStage = kAStage + kBStage;  // 48 KiB
+constexpr int kStages = 3;                     // LDS ring: 1 stage multiplied, 2 in flight
+constexpr int kLds = kStages * kStage;        // 144 KiB
 constexpr uint32_t kOob = 0x80000000u;        // an offset past every buffer (all < 2^31 bytes)
 constexpr int kGroupM = 4;                    // token tiles per group of the tile order
+// s_waitcnt immediate: vector-memory count <= 12 (one stage of this wavefront's loads), the
+// other counters unconstrained
+constexpr int kWaitOneStage = 0x0F7C;
+static_assert(kStages == 3, "the ring indexing and the waits assume three buffers");
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-// One workgroup per compute unit (96 KiB of LDS), so one wavefront per SIMD: the register
-// budget is the whole file, which the fragment prefetch below uses.
+// One stage's 12 direct-to-LDS loads of this wavefront, issued back to back: 8 of A (LDS
+// blocks of 1 KiB from `ma` on) and 4 of B (from `mb` on). Each lane's byte offset within
+// its operand (`va`, `vb`) is fixed for the whole K loop; the stage's k offset is the
+// instruction's scalar offset `so`. m0 holds the LDS address of each load; it is restored
+// afterwards (the compiler reserves it).
+__device__ __forceinline__ void issue_stage(v4i rx, v4i rw, uint32_t ma, uint32_t mb,
+                                            uint32_t so, const uint32_t (&va)[8],
+                                            const uint32_t (&vb)[4]) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_add_u32 m0, %[ma], 0\n\ts_nop 0\n\tbuffer_load_dwordx4 %[a0], %[rx], %[so] offen lds\n\t"
+      "s_add_u32 m0, %[ma], 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %[a1], %[rx], %[so] offen lds\n\t"
+      "s_add_u32 m0, %[ma], 0x800\n\ts_nop 0\n\tbuffer_load_dwordx4 %[a2], %[rx], %[so] offen lds\n\t"
+      "s_add_u32 m0, %[ma], 0xc00\n\ts_nop 0\n\tbuffer_load_dwordx4 %[a3], %[rx], %[so] offen lds\n\t"
+      "s_add_u32 m0, %[ma], 0x1000\n\ts_nop 0\n\tbuffer_load_dwordx4 %[a4], %[rx], %[so] offen lds\n\t"
+      "s_add_u32 m0, %[ma], 0x1400\n\ts_nop 0\n\tbuffer_load_dwordx4 %[a5], %[rx], %[so] offen lds\n\t"
+      "s_add_u32 m0, %[ma], 0x1800\n\ts_nop 0\n\tbuffer_load_dwordx4 %[a6], %[rx], %[so] offen lds\n\t"
+      "s_add_u32 m0, %[ma], 0x1c00\n\ts_nop 0\n\tbuffer_load_dwordx4 %[a7], %[rx], %[so] offen lds\n\t"
+      "s_add_u32 m0, %[mb], 0\n\ts_nop 0\n\tbuffer_load_dwordx4 %[b0], %[rw], %[so] offen lds\n\t"
+      "s_add_u32 m0, %[mb], 0x400\n\ts_nop 0\n\tbuffer_load_dwordx4 %[b1], %[rw], %[so] offen lds\n\t"
+      "s_add_u32 m0, %[mb], 0x800\n\ts_nop 0\n\tbuffer_load_dwordx4 %[b2], %[rw], %[so] offen lds\n\t"
+      "s_add_u32 m0, %[mb], 0xc00\n\ts_nop 0\n\tbuffer_load_dwordx4 %[b3], %[rw], %[so] offen lds\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [ma] "s"(ma), [mb] "s"(mb), [rx] "s"(rx), [rw] "s"(rw), [so] "s"(so), [a0] "v"(va[0]),
+        [a1] "v"(va[1]), [a2] "v"(va[2]), [a3] "v"(va[3]), [a4] "v"(va[4]), [a5] "v"(va[5]),
+        [a6] "v"(va[6]), [a7] "v"(va[7]), [b0] "v"(vb[0]), [b1] "v"(vb[1]), [b2] "v"(vb[2]),
+        [b3] "v"(vb[3])
+      : "scc");
+}
+
+// One wavefront per SIMD (a 144 KiB workgroup per compute unit): the whole register file is
+// this wavefront's.
 __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_f16_kernel(
     const _Float16* __restrict__ X, const _Float16* __restrict__ W, float* __restrict__ C, int M,
@@ -67,49 +106,62 @@ void gemm_f16_kernel(
 
   const v4i rx = make_rsrc_sgpr(X, (uint32_t)M * (uint32_t)K * 2u);
   const v4i rw = make_rsrc_sgpr(W, (uint32_t)N * (uint32_t)K * 2u);
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)smem);
 
   // Loads of one stage by this wavefront: A rows [64w, 64w + 64) in 8 instructions of 8 rows,
   // B rows [32w, 32w + 32) in 4. Lane l of instruction d writes LDS row 8d + l/8 (of its
   // block), slot l % 8, which holds chunk (l % 8) ^ swz(row).
-  uint32_t offa[8], offb[4];
+  uint32_t va[8], vb[4];
   int chka[8], chkb[4];
 #pragma unroll
   for (int d = 0; d < 8; ++d) {
     const int r = 64 * wave + 8 * d + (lane >> 3);
     chka[d] = (lane & 7) ^ swz(r);
-    offa[d] = (m0 + r < M) ? ((uint32_t)(m0 + r) * (uint32_t)K + 8u * chka[d]) * 2u : kOob;
+    va[d] = (m0 + r < M) ? ((uint32_t)(m0 + r) * (uint32_t)K + 8u * chka[d]) * 2u : kOob;
   }
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const int r = 32 * wave + 8 * d + (lane >> 3);
     chkb[d] = (lane & 7) ^ swz(r);
-    offb[d] = (n0 + r < N) ? ((uint32_t)(n0 + r) * (uint32_t)K + 8u * chkb[d]) * 2u : kOob;
+    vb[d] = (n0 + r < N) ? ((uint32_t)(n0 + r) * (uint32_t)K + 8u * chkb[d]) * 2u : kOob;
   }
-  auto issue = [&](int s) {
-    uint8_t* buf = smem + (s & 1) * kStage;
+  const uint32_t ma0 = lds0 + (uint32_t)(64 * wave) * 128u;
+  const uint32_t mb0 = lds0 + kAStage + (uint32_t)(32 * wave) * 128u;
+  // stage s into ring buffer bi
+  auto issue = [&](int s, int bi) {
     const int k0 = s * kBK;
-    const bool tail = k0 + kBK > K;
+    const uint32_t off = (uint32_t)bi * kStage;
+    if (k0 + kBK <= K) {
+      issue_stage(rx, rw, __builtin_amdgcn_readfirstlane(ma0 + off),
+                  __builtin_amdgcn_readfirstlane(mb0 + off), 2u * (uint32_t)k0, va, vb);
+    } else {  // the last, partial stage: chunks past K read as zero
+      uint32_t ta[8], tb[4];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      uint32_t o = offa[d] == kOob ? kOob : offa[d] + 2u * (uint32_t)k0;
-      if (tail && k0 + 8 * chka[d] >= K) o = kOob;
-      dma16(rx, buf + (64 * wave + 8 * d) * 128, o);
-    }
+      for (int d = 0; d < 8; ++d) ta[d] = (k0 + 8 * chka[d] < K) ? va[d] : kOob;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      uint32_t o = offb[d] == kOob ? kOob : offb[d] + 2u * (uint32_t)k0;
-      if (tail && k0 + 8 * chkb[d] >= K) o = kOob;
-      dma16(rw, buf + kAStage + (32 * wave + 8 * d) * 128, o);
+      for (int d = 0; d < 4; ++d) tb[d] = (k0 + 8 * chkb[d] < K) ? vb[d] : kOob;
+      issue_stage(rx, rw, __builtin_amdgcn_readfirstlane(ma0 + off),
+                  __builtin_amdgcn_readfirstlane(mb0 + off), 2u * (uint32_t)k0, ta, tb);
     }
   };
 
-  // fragment rows of this wavefront: tokens 128 * wm + 32a + l32, features 64 * wn + 32b + l32
+  // Fragment reads. Tile row r = (base) + l32 has swz(r) = (l32 >> 1) & 7 for every fragment
+  // of this wavefront (the bases are multiples of 32), so in step t (16 k: chunk 2t + h) every
+  // fragment's lane offset within its 32-row block is the same, lo[t]; the 32-row blocks are
+  // 4 KiB apart (an immediate offset of the read).
   const int wm = wave & 1, wn = wave >> 1;
-  int rowa[4], rowb[2];
+  uint32_t lo[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) rowa[a] = 128 * wm + 32 * a + l32;
+  for (int t = 0; t < 4; ++t) lo[t] = (uint32_t)l32 * 128u + ((uint32_t)((2 * t + h) ^ ((l32 >> 1) & 7)) << 4);
+  const uint32_t fa0 = (uint32_t)(128 * wm) * 128u;             // this wavefront's A rows
+  const uint32_t fb0 = kAStage + (uint32_t)(64 * wn) * 128u;    // and B rows
+  auto load_frags = [&](uint32_t base_a, uint32_t base_b, v8h (&fa)[4], v8h (&fb)[2]) {
 #pragma unroll
-  for (int bb = 0; bb < 2; ++bb) rowb[bb] = 64 * wn + 32 * bb + l32;
+    for (int a = 0; a < 4; ++a) fa[a] = *reinterpret_cast<const v8h*>(smem + base_a + a * 4096);
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+      fb[bb] = *reinterpret_cast<const v8h*>(smem + base_b + bb * 4096);
+  };
 
   v16f acc[4][2];
 #pragma unroll
@@ -118,41 +170,48 @@ void gemm_f16_kernel(
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][bb][r] = 0.0f;
-
-  const int S = (K + kBK - 1) / kBK;
-  issue(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  // fragments of step t (16 k) of the stage in buffer `buf`: chunk 2t + h of each row
-  auto load_frags = [&](const uint8_t* buf, int t, v8h (&fa)[4], v8h (&fb)[2]) {
-    const int c = 2 * t + h;
+  auto mfmas = [&](const v8h (&fa)[4], const v8h (&fb)[2]) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
-      fa[a] = *reinterpret_cast<const v8h*>(buf + rowa[a] * 128 + ((c ^ swz(rowa[a])) << 4));
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-      fb[bb] = *reinterpret_cast<const v8h*>(buf + kAStage + rowb[bb] * 128 +
-                                             ((c ^ swz(rowb[bb])) << 4));
+      for (int bb = 0; bb < 2; ++bb)
+        acc[a][bb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[a], fb[bb], acc[a][bb], 0, 0, 0);
   };
-  v8h fa[2][4], fb[2][2];
-  load_frags(smem, 0, fa[0], fb[0]);
+
+  const int S = (K + kBK - 1) / kBK;
+  issue(0, 0);
+  if (S > 1) issue(1, 1);
+  // stage 0 has landed when at most stage 1's loads are pending
+  if (S > 1) __builtin_amdgcn_s_waitcnt(kWaitOneStage);
+  else __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  v8h f0a[4], f0b[2], f1a[4], f1b[2];
+  load_frags(fa0 + lo[0], fb0 + lo[0], f0a, f0b);
+  int bi = 0;  // ring buffer of stage s
   for (int s = 0; s < S; ++s) {
-    if (s + 1 < S) issue(s + 1);
-    const uint8_t* buf = smem + (s & 1) * kStage;
-    // steps 0..3 of the stage; the fragments of step t + 1 are read while step t multiplies
-#pragma unroll
-    for (int t = 0; t < kBK / 16; ++t) {
-      if (t + 1 < kBK / 16) load_frags(buf, t + 1, fa[(t + 1) & 1], fb[(t + 1) & 1]);
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-          acc[a][bb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[t & 1][a], fb[t & 1][bb],
-                                                             acc[a][bb], 0, 0, 0);
+    const uint32_t st = (uint32_t)bi * kStage;
+    const int bn = bi == 2 ? 0 : bi + 1;       // buffer of stage s + 1
+    // the buffer of stage s + 2 was last read in iteration s - 1, which every wavefront
+    // finished before that iteration's barrier
+    if (s + 2 < S) issue(s + 2, bn == 2 ? 0 : bn + 1);
+    // steps 0..2; each reads the next step's fragments while it multiplies
+    load_frags(st + fa0 + lo[1], st + fb0 + lo[1], f1a, f1b);
+    mfmas(f0a, f0b);
+    load_frags(st + fa0 + lo[2], st + fb0 + lo[2], f0a, f0b);
+    mfmas(f1a, f1b);
+    load_frags(st + fa0 + lo[3], st + fb0 + lo[3], f1a, f1b);
+    mfmas(f0a, f0b);
+    // stage s + 1 has landed for this wavefront (stage s + 2's 12 loads may be pending) ...
+    if (s + 2 < S) __builtin_amdgcn_s_waitcnt(kWaitOneStage);
+    else __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // ... and for every wavefront, all of whose reads of stage s are done
+    // step 3 multiplies while the first fragments of stage s + 1 are read
+    if (s + 1 < S) {
+      const uint32_t sn = (uint32_t)bn * kStage;
+      load_frags(sn + fa0 + lo[0], sn + fb0 + lo[0], f0a, f0b);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads of stage s + 1 have landed
-    __syncthreads();                // ... and everyone's; stage s is no longer read
-    if (s + 1 < S) load_frags(smem + ((s + 1) & 1) * kStage, 0, fa[0], fb[0]);
+    mfmas(f1a, f1b);
+    bi = bn;
   }
 
   // store: register r of tile (a, b) holds token 8(r/4) + 4h + r%4 of the tile, feature l32
