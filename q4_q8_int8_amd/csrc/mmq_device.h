@@ -33,7 +33,13 @@ static __device__ __forceinline__ v4i make_rsrc_sgpr(const void* p, uint32_t byt
   r[3] = 0x00020000;
   return r;
 }
-// 16 bytes per lane from the buffer at `off` into LDS at lds_base + 16 * lane (lds_base is
+// LDS byte address of a pointer into a __shared__ array. Taken once from the array itself it
+// is a constant; converting a pointer computed at run time instead costs a null check and
+// an aperture lookup at every use.
+static __device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)p);
+}
+// 16 bytes per lane from the buffer at `off` into LDS at byte address lds + 16 * lane (lds is
 // wave-uniform); completion is tracked by the vector-memory counter and waited for
 // explicitly before the barrier that ends a stage. The instruction is issued from inline
 // assembly on purpose: the compiler cannot tell which LDS bytes such a load writes, so for
@@ -42,8 +48,7 @@ static __device__ __forceinline__ v4i make_rsrc_sgpr(const void* p, uint32_t byt
 // memory effects on purpose too: it only writes the stage buffer that nothing reads until
 // after the explicit wait and the barrier (both ordered with the asm), and so the compiler
 // stays free to schedule the current stage's LDS reads around it.
-static __device__ __forceinline__ void dma16(v4i r, uint8_t* lds_base, uint32_t off) {
-  const uint32_t m0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr_t)lds_base);
+static __device__ __forceinline__ void dma16(v4i r, uint32_t lds, uint32_t off) {
   int saved;  // m0 is reserved by the compiler: restore it after use
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -52,7 +57,7 @@ static __device__ __forceinline__ void dma16(v4i r, uint8_t* lds_base, uint32_t 
       "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(off), "s"(r));
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r));
 }
 
 }  // namespace mmq

@@ -130,8 +130,9 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   auto load_nib = [&](int s, int g) -> v4i {
     return buf_load16(rw, (uint32_t)s * kRepTileBytes + g * 1024 + lane * 16);
   };
+  const uint32_t lds0 = lds_addr(smem);
   auto issue_op = [&](int v, int s, int p, v4i& nib3) {
-    uint8_t* st = smem + p * STAGE;
+    const uint32_t st = lds0 + (uint32_t)(p * STAGE);
     if (v < A_PER_WAVE) {
       const int k = wave + v * NW;
       if (k < A_DMA && a_act[v]) dma16(rq, st + k * 1024, a_off[v] + (uint32_t)s * 256);
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
     }
     v -= TP_PER_WAVE;
     if (v < 3) {  // dsv [8][32] and dmv pieces [3][32][8]: 2560 contiguous bytes
-      uint8_t* sw = st + A_BYTES + DA_BYTES + TP_BYTES + wave * W_BYTES;
+      const uint32_t sw = st + A_BYTES + DA_BYTES + TP_BYTES + wave * W_BYTES;
       const uint32_t wo = (uint32_t)s * kRepTileBytes + kRepNibBytes + lane * 16;
       if (v < 2 || lane < 32) dma16(rwd, sw + v * 1024, wo + v * 1024);
       return;

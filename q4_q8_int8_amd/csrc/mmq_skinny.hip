@@ -55,6 +55,7 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
   const v4i rwd = make_rsrc_sgpr(wtile, (uint32_t)nsb * kRepTileBytes);
 
   uint8_t* sW = smem + wave * W_BYTES;
+  const uint32_t sWa = lds_addr(smem) + (uint32_t)(wave * W_BYTES);  // its LDS address
   const float* sWw = reinterpret_cast<const float*>(sW);
   // token row of this lane: every offset inside the row is below K, so rows past M read
   // past the end of the buffer (zero)
@@ -71,9 +72,9 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
     // this wavefront's earlier LDS reads of its region are done before the loads overwrite it
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), the other counters unconstrained
     const uint32_t wo = (uint32_t)s * kRepTileBytes + kRepNibBytes + lane * 16;
-    dma16(rwd, sW, wo);
-    dma16(rwd, sW + 1024, wo + 1024);
-    if (lane < 32) dma16(rwd, sW + 2048, wo + 2048);
+    dma16(rwd, sWa, wo);
+    dma16(rwd, sWa + 1024, wo + 1024);
+    if (lane < 32) dma16(rwd, sWa + 2048, wo + 2048);
     v4i raw[4], tok[8], tp[3];
     float da[8];
 #pragma unroll
