@@ -131,8 +131,9 @@ int mmq_q4K_repacked_bytes(int64_t N, int64_t K, size_t* bytes);
  *                            p2 = v - p0 - p1, which sum to v exactly (a non-finite v is
  *                            stored as {top 16 bits of v, 0, 0}). Slots of blocks past K/32
  *                            are not written.
- * Preconditions: finite x with |x| <= 8.3e6 (so that amax/127 fits f16). K % 32 == 0.
- * Errors: MMQ_E_ARG (null pointer, M or K <= 0), MMQ_E_SHAPE (K % 32, size overflow),
+ * Preconditions: finite x with |x| <= 8.3e6 (so that amax/127 fits f16). K % 32 == 0;
+ * M*K < 2^34 (the GEMM takes M*K < 2^31).
+ * Errors: MMQ_E_ARG (null pointer, M or K <= 0), MMQ_E_SHAPE (K % 32, M*K too large),
  *         MMQ_E_DEVICE, MMQ_E_HIP.
  */
 int quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, void* stream);
@@ -149,7 +150,8 @@ int quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, void* stream);
  *   bytes [5120, 6656): uint16 bf16 pieces [i 0..2][j 0..31][b 0..7] of dmv = -(dmin*m),
  *                       split as the pieces of da*sa at quantize_q8_1 (they sum to dmv)
  * Both scale products are exact in float32.
- * Errors: MMQ_E_ARG, MMQ_E_SHAPE (K % 256), MMQ_E_DEVICE, MMQ_E_HIP.
+ * Errors: MMQ_E_ARG, MMQ_E_SHAPE (K % 256; ceil(N/32)*(K/256) >= 2^31), MMQ_E_DEVICE,
+ *         MMQ_E_HIP.
  */
 int repack_q4_K(const void* w_q4K, int64_t N, int64_t K, void* w_rep, void* stream);
 

@@ -223,6 +223,10 @@ int quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, void* stream) 
   size_t nb;
   int st = mmq_q8_1_bytes(M, K, &nb);
   if (st) return st;
+  // the prepass indexes the input in 16-byte words with 32-bit offsets
+  if ((__int128)M * K >= ((__int128)1 << 34))
+    return fail(MMQ_E_SHAPE, "quantize_q8_1 takes M*K below 2^34 (M=%lld, K=%lld)",
+                (long long)M, (long long)K);
   if (!x || !q8) return fail(MMQ_E_ARG, "null device pointer");
   if (!aligned16(x) || !aligned16(q8)) return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
   DeviceInfo* di;
@@ -236,6 +240,9 @@ int repack_q4_K(const void* w_q4K, int64_t N, int64_t K, void* w_rep, void* stre
   size_t nb;
   int st = mmq_q4K_repacked_bytes(N, K, &nb);
   if (st) return st;
+  // one workgroup per (32-row tile, super-block), on a 1-D grid
+  if ((__int128)((N + 31) / 32) * (K / MMQ_QK_K) >= ((__int128)1 << 31))
+    return fail(MMQ_E_SHAPE, "repack_q4_K takes ceil(N/32)*(K/256) below 2^31");
   if (!w_q4K || !w_rep) return fail(MMQ_E_ARG, "null device pointer");
   if (!aligned16(w_q4K) || !aligned16(w_rep)) return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
   DeviceInfo* di;

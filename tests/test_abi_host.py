@@ -181,6 +181,8 @@ Cp = 0x30000000
     (("repack_q4_K", A, 4, 200, B, None), mmq.MMQ_E_SHAPE),
     (("repack_q4_K", None, 4, 256, B, None), mmq.MMQ_E_ARG),
     (("repack_q4_K", A, 4, 256, B + 8, None), mmq.MMQ_E_ARG),
+    (("quantize_q8_1", A, 1 << 20, 1 << 14, B, None), mmq.MMQ_E_SHAPE),   # M*K = 2^34
+    (("repack_q4_K", A, 1 << 30, 1 << 14, B, None), mmq.MMQ_E_SHAPE),     # 2^25 x 64 workgroups
     (("mmq_q4K_q8_1", 4, 8, 100, A, B, Cp, None), mmq.MMQ_E_SHAPE),
     (("mmq_q4K_q8_1", 4, 8, 256, None, B, Cp, None), mmq.MMQ_E_ARG),
     (("mmq_q4K_q8_1", 4, 8, 256, A, B, Cp + 4, None), mmq.MMQ_E_ARG),

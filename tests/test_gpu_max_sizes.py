@@ -1,0 +1,140 @@
+"""Parity at the largest sizes each entry point accepts (needs a GPU with ~30 GB free).
+
+The kernels address operands with 32-bit offsets, or loop with 64-bit indices, and these
+cases sit at the edge of what each accepts:
+- the integer GEMM at M*K = 2^31 - 4096 (its limit is M*K < 2^31), and at K = 2^24 (its
+  limit);
+- the f16 GEMM at M*K = 2^30 - 4096 (limit M*K < 2^30);
+- the conversion and the dequantization past 2^32 elements (64-bit indices).
+
+The large operands are built on the device by repeating a seeded block from synth.py (row r
+of the operand is row r mod R of the block). The oracle therefore gets the same values for
+any row it checks. Checked rows include the first and the last, where the offsets are
+largest.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import assert_within_tolerance, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+mmq = pytest.importorskip("q4_q8_int8_amd")
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the gpu tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def repeat_rows(block: np.ndarray, rows: int) -> "torch.Tensor":
+    """Device tensor of `rows` rows: row r is block[r % len(block)]."""
+    b = to_dev(block)
+    reps = -(-rows // block.shape[0])
+    return b.repeat((reps,) + (1,) * (block.ndim - 1))[:rows].contiguous()
+
+
+def check_rows(M):
+    return sorted({0, 1, 4095, 4096, M // 2, M - 129, M - 128, M - 33, M - 2, M - 1})
+
+
+@pytest.mark.parametrize("tile", [mmq.MMQ_TILE_AUTO, mmq.MMQ_TILE_SMALL])
+def test_mmq_largest_activations(tile):
+    K, N = 4096, 64
+    M = ((1 << 31) - 1) // K                  # M*K = 2^31 - 4096
+    block = synth.activations("normal_outliers", 4096, K, 5001)
+    w, _ = synth.q4k_weights("fit", N, K, 5002)
+    say("mmq largest activations", M, N, K, "tile", tile)
+    x = repeat_rows(block, M)
+    q8 = torch.zeros(mmq.mmq_q8_1_bytes(M, K), dtype=torch.uint8, device="cuda")
+    mmq.quantize_q8_1(x, M, K, q8)
+    del x
+    rep = torch.empty(mmq.mmq_q4K_repacked_bytes(N, K), dtype=torch.uint8, device="cuda")
+    mmq.repack_q4_K(to_dev(w), N, K, rep)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    mmq.mmq_q4K_q8_1_ex(M, N, K, q8, rep, C, force_tile=tile)
+    torch.cuda.synchronize()
+    rows = check_rows(M)
+    got = C[rows].cpu().numpy()
+    q = oracle.quantize_q8_1(block[[r % 4096 for r in rows]])
+    wo = oracle.decode_q4_K(w)
+    _, T = oracle.mmq_terms(q, wo)
+    r = assert_within_tolerance(got, oracle.mmq(q, wo), T)
+    say("max |err|/T", r, "plan", mmq.mmq_last_kernel()["tile"])
+
+
+def test_mmq_largest_k():
+    M, N, K = 2, 33, 1 << 24                  # K at its limit, 65536 super-blocks
+    x = synth.activations("normal_outliers", M, K, 5003)
+    w, _ = synth.q4k_weights("random_fields", N, K, 5004)
+    q = oracle.quantize_q8_1(x)
+    wo = oracle.decode_q4_K(w)
+    C_ref = oracle.mmq(q, wo)
+    _, T = oracle.mmq_terms(q, wo)
+    q8 = torch.zeros(mmq.mmq_q8_1_bytes(M, K), dtype=torch.uint8, device="cuda")
+    rep = torch.empty(mmq.mmq_q4K_repacked_bytes(N, K), dtype=torch.uint8, device="cuda")
+    say("mmq largest K: quantize, repack", M, N, K)
+    mmq.quantize_q8_1(to_dev(x), M, K, q8)
+    mmq.repack_q4_K(to_dev(w), N, K, rep)
+    for tile in (mmq.MMQ_TILE_SKINNY, mmq.MMQ_TILE_SMALL, mmq.MMQ_TILE_LARGE):
+        say("mmq largest K", tile)
+        C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        mmq.mmq_q4K_q8_1_ex(M, N, K, q8, rep, C, force_tile=tile)
+        torch.cuda.synchronize()
+        r = assert_within_tolerance(C.cpu().numpy(), C_ref, T)
+        say("max |err|/T", r)
+
+
+def test_gemm_f16_largest():
+    K, N = 4096, 64
+    M = ((1 << 30) - 1) // K                  # M*K = 2^30 - 4096
+    a_block = oracle.convert_f32_f16(synth.activations("normal_outliers", 4096, K, 5005))
+    rng = np.random.default_rng(5006)
+    w_bits = oracle.convert_f32_f16((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    say("gemm_f16 largest", M, N, K)
+    a = repeat_rows(a_block.view(np.int16), M)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    mmq.gemm_f16(M, N, K, a, to_dev(w_bits.view(np.int16)), C)
+    torch.cuda.synchronize()
+    rows = check_rows(M)
+    got = C[rows].cpu().numpy().astype(np.float64)
+    C_ref, T = oracle.gemm_f16(a_block[[r % 4096 for r in rows]], w_bits)
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - C_ref) <= K * 2.0 ** -24 * T)
+
+
+def test_convert_past_2_32_elements():
+    K = 4096
+    M = (1 << 20) + 1                         # M*K = 2^32 + 4096 values
+    block = synth.activations("normal_outliers", 4096, K, 5007)
+    say("convert past 2^32 elements", M, K)
+    x = repeat_rows(block, M)
+    out = torch.empty(M * K, dtype=torch.int16, device="cuda")
+    mmq.convert_f32_f16(x, M, K, out)
+    torch.cuda.synchronize()
+    del x
+    rows = sorted({0, 1, (1 << 20) - 1, 1 << 20, M - 1})
+    got = out.view(M, K)[rows].cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, oracle.convert_f32_f16(block[[r % 4096 for r in rows]]))
+
+
+def test_dequantize_past_2_32_weights():
+    K = 4096
+    N = (1 << 20) + 33                        # N*K past 2^32, ragged last tile
+    w_block, _ = synth.q4k_weights("random_fields", 4096, K, 5008)
+    say("dequantize past 2^32 weights", N, K)
+    w = repeat_rows(w_block, N)
+    out = torch.empty(N * K, dtype=torch.int16, device="cuda")
+    mmq.dequantize_q4_K_f16(w, N, K, out)
+    torch.cuda.synchronize()
+    del w
+    rows = sorted({0, 1, (1 << 20) - 1, 1 << 20, N - 1})
+    got = out.view(N, K)[rows].cpu().numpy().view(np.uint16)
+    want = oracle.dequantize_q4_K_f16(oracle.decode_q4_K(w_block[[r % 4096 for r in rows]]))
+    assert np.array_equal(got, want)
