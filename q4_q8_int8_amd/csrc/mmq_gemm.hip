@@ -46,6 +46,14 @@
 namespace mmq {
 namespace {
 
+// s_setprio takes an immediate: one call per value, selected at compile time once unrolled.
+__device__ __forceinline__ void set_priority(int p) {
+  if (p >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (p == 2) __builtin_amdgcn_s_setprio(2);
+  else if (p == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 template <int TT, int NW, bool STORE_S>
 __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
     const int8_t* __restrict__ qs, const float* __restrict__ da_plane,
@@ -251,6 +259,11 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
         const int b = n / TT, t = n % TT;
+        // Issue priority falls by one every two steps within each group of eight, so of the
+        // two wavefronts sharing a SIMD the one that is ahead yields to the other: the pair
+        // keeps step rather than one running ahead and the other finishing the super-block
+        // alone (a lone wavefront issues at well under half the rate of a pair).
+        if (n % 2 == 0) set_priority(3 - (n % 8) / 2);
         if (more) {
 #pragma unroll
           for (int v = 0; v < NOPS; ++v)
@@ -288,6 +301,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
       }
     }
 
+    if constexpr (!STORE_S) __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0);  // this wavefront's stage s+1 loads have landed
     __syncthreads();                // ... and everyone's; stage s is no longer read
   }
