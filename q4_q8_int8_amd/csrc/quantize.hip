@@ -8,8 +8,15 @@
 // instruction. HBM-bound: 4 bytes read and about 1.44 bytes written per element.
 //
 // Mapping: 8 lanes own one 32-element block (one float4 each), so a wavefront covers 8
-// consecutive blocks = 1 KiB of contiguous input at a time, and 4 such groups in all; the
-// max and the sum are reduced with xor-shuffles inside the 8-lane group.
+// consecutive blocks = 1 KiB of contiguous input at a time; the max and the sum are reduced
+// with lane moves inside the 8-lane group. Two kernels:
+// - K % 256 == 0 (whole super-blocks): a workgroup takes a tile of kTileRows rows x one
+//   super-block. The int8 values and scale words of each row go out directly (256 and 32
+//   contiguous bytes); the da plane and the pieces are staged in LDS and written after a
+//   barrier as runs of 4*kTileRows and 16*kTileRows contiguous bytes, not as one 4- or
+//   16-byte store per row scattered M entries apart;
+// - any other K: each wavefront takes 2 groups of 8 consecutive blocks and stores every
+//   block's plane entries where they fall.
 #include "mmq_internal.h"
 
 namespace mmq {
@@ -128,13 +135,106 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float4* __rest
   }
 }
 
+// Whole super-blocks: tile of kTileRows rows x one super-block, kTileWaves wavefronts of
+// kTileRows/kTileWaves rows each, all loads of a wavefront issued first. Indices fit in 32
+// bits: 16-byte words of the input below M*K/4 < 2^32.
+constexpr int kTileRows = 8;
+constexpr int kTileWaves = 4;
+constexpr int kRowsPerWave = kTileRows / kTileWaves;
+static_assert(kTileRows % 4 == 0 && 5 * kTileRows <= 64 * kTileWaves, "store phase mapping");
+
+__global__ __launch_bounds__(64 * kTileWaves) void quantize_q8_1_tiled_kernel(
+    const float4* __restrict__ x, uint32_t* __restrict__ qs, uint32_t* __restrict__ ds,
+    float* __restrict__ da_plane, uint16_t* __restrict__ pieces, uint32_t M, uint32_t K,
+    uint32_t nsb) {
+  __shared__ __align__(16) float sDa[8][kTileRows];  // [block of the super-block][row]
+  __shared__ __align__(16) uint4 sPc[3][kTileRows];  // [piece][row]: 8 bf16, one per block
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const uint32_t s = blockIdx.x % nsb;
+  const uint32_t r0 = (blockIdx.x / nsb) * kTileRows;
+  const uint32_t k4 = K / 4;
+  float4 v[kRowsPerWave];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const uint32_t row = r0 + kRowsPerWave * w + i;
+    v[i] = row < M ? x[row * k4 + 64 * s + lane] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  const int j = lane & 7;
+  const uint32_t b = lane >> 3;  // block of this lane's group within the super-block
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int rl = kRowsPerWave * w + i;
+    const uint32_t row = r0 + rl;
+    const float amax = group_max(fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)),
+                                       fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    const float d = amax / 127.0f;                 // IEEE division
+    const float id = d > 0.0f ? 1.0f / d : 0.0f;   // IEEE reciprocal (division)
+    const int q0 = quant1(v[i].x, id), q1 = quant1(v[i].y, id);
+    const int q2 = quant1(v[i].z, id), q3 = quant1(v[i].w, id);
+    const int sum = group_sum(q0 + q1 + q2 + q3);
+    const _Float16 dh = (_Float16)d;  // RNE
+    if (row < M) {
+      qs[row * k4 + 64 * s + lane] = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) |
+                                     ((uint32_t)(q2 & 0xFF) << 16) |
+                                     ((uint32_t)(q3 & 0xFF) << 24);
+      if (j == 0)
+        ds[row * (K / 32) + 8 * s + b] =
+            (uint32_t)__builtin_bit_cast(uint16_t, dh) | ((uint32_t)(sum & 0xFFFF) << 16);
+    }
+    if (j == 0) sDa[b][rl] = (float)dh;
+    // da*sa (exact in f32) as three bf16 pieces; lane j < 3 gathers piece j of the 8 blocks
+    uint16_t pc[3];
+    bf16_split3((float)dh * (float)sum, pc[0], pc[1], pc[2]);
+    const uint32_t offer = j < 3 ? pc[j] : 0u;
+    uint32_t g[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[e] = (uint32_t)__shfl((int)offer, 8 * e + j, 64);
+    if (lane < 3)
+      sPc[lane][rl] = make_uint4(g[0] | (g[1] << 16), g[2] | (g[3] << 16), g[4] | (g[5] << 16),
+                                 g[6] | (g[7] << 16));
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  constexpr int kDaThreads = 2 * kTileRows;  // 8 blocks x kTileRows/4 float4 each
+  if (t < kDaThreads) {
+    const int bb = t / (kTileRows / 4), c = t % (kTileRows / 4);
+    const uint32_t row = r0 + 4 * c;
+    float* dst = da_plane + (8 * s + bb) * M + row;
+    if ((M & 3) == 0 && row + 3 < M) {  // 16-byte aligned: the plane starts on 256 bytes
+      *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(&sDa[bb][4 * c]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (row + e < M) dst[e] = sDa[bb][4 * c + e];
+    }
+  } else if (t < kDaThreads + 3 * kTileRows) {  // piece pp of row rr of the tile
+    const int pp = (t - kDaThreads) / kTileRows, rr = (t - kDaThreads) % kTileRows;
+    const uint32_t row = r0 + rr;
+    if (row < M)
+      *reinterpret_cast<uint4*>(pieces + ((s * 3 + pp) * M + row) * 8) = sPc[pp][rr];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, hipStream_t s) {
+  uint8_t* base = static_cast<uint8_t*>(q8);
+  if (K % 256 == 0) {
+    // ceil(M/8) * K/256 workgroups of 256 work-items: below 2^31 work-items for M*K < 2^34
+    const int64_t nsb = K / 256;
+    const int64_t grid = (M + kTileRows - 1) / kTileRows * nsb;
+    hipLaunchKernelGGL(quantize_q8_1_tiled_kernel, dim3((unsigned)grid), dim3(64 * kTileWaves),
+                       0, s, reinterpret_cast<const float4*>(x), reinterpret_cast<uint32_t*>(base),
+                       reinterpret_cast<uint32_t*>(base + M * K),
+                       reinterpret_cast<float*>(base + q8_planes_offset(M, K)),
+                       reinterpret_cast<uint16_t*>(base + q8_pieces_offset(M, K)),
+                       (uint32_t)M, (uint32_t)K, (uint32_t)nsb);
+    return hipGetLastError();
+  }
   const int64_t nblocks = M * (K / 32);
   const int64_t waves = (nblocks + 8 * kGroups - 1) / (8 * kGroups);
   const int64_t grid = (waves + 3) / 4;
-  uint8_t* base = static_cast<uint8_t*>(q8);
   hipLaunchKernelGGL(quantize_q8_1_kernel, dim3((unsigned)grid), dim3(256), 0, s,
                      reinterpret_cast<const float4*>(x), reinterpret_cast<uint32_t*>(base),
                      reinterpret_cast<uint32_t*>(base + M * K),

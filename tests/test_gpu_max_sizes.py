@@ -1,11 +1,12 @@
-"""Parity at the largest sizes each entry point accepts (needs a GPU with ~30 GB free).
+"""Parity at the largest sizes each entry point accepts (needs a GPU with ~90 GB free).
 
 The kernels address operands with 32-bit offsets, or loop with 64-bit indices, and these
 cases sit at the edge of what each accepts:
 - the integer GEMM at M*K = 2^31 - 4096 (its limit is M*K < 2^31), and at K = 2^24 (its
   limit);
 - the f16 GEMM at M*K = 2^30 - 4096 (limit M*K < 2^30);
-- the conversion and the dequantization past 2^32 elements (64-bit indices).
+- the conversion and the dequantization past 2^32 elements (64-bit indices);
+- the quantize prepass at M*K = 2^34 - 4096 (its limit is M*K < 2^34).
 
 The large operands are built on the device by repeating a seeded block from synth.py (row r
 of the operand is row r mod R of the block). The oracle therefore gets the same values for
@@ -138,3 +139,48 @@ def test_dequantize_past_2_32_weights():
     got = out.view(N, K)[rows].cpu().numpy().view(np.uint16)
     want = oracle.dequantize_q4_K_f16(oracle.decode_q4_K(w_block[[r % 4096 for r in rows]]))
     assert np.array_equal(got, want)
+
+
+def q8_rows(image, M: int, K: int, rows):
+    """The parts of a q8_1 byte image (uint8, device tensor or numpy) that belong to `rows`:
+    int8 values, scale words, da-plane entries and bf16 pieces, as numpy arrays."""
+    def host(a):
+        return a.cpu().numpy() if hasattr(a, "cpu") else np.asarray(a)
+    nb, nsb = K // 32, -(-K // 256)
+    P = -(-(M * K + 4 * M * nb) // 256) * 256
+    Q = -(-(P + 4 * M * nb) // 256) * 256
+    qs = np.stack([host(image[r * K:(r + 1) * K]) for r in rows])
+    words = np.stack([host(image[M * K + 4 * nb * r:M * K + 4 * nb * (r + 1)]) for r in rows])
+    plane = np.stack([host(image[P + 4 * (b * M + r):P + 4 * (b * M + r) + 4])
+                      for b in range(nb) for r in rows])
+    pieces = np.stack([host(image[Q + 16 * (i * M + r):Q + 16 * (i * M + r) + 16])
+                       for i in range(3 * nsb) for r in rows])
+    return qs, words, plane, pieces
+
+
+@pytest.mark.parametrize("K", [4096, 4128])
+def test_quantize_largest(K):
+    """quantize_q8_1 at M*K just below 2^34, its limit: 64 GiB of f32 input. K = 4096 takes
+    the prepass for whole super-blocks, K = 4128 the one for any multiple of 32."""
+    M = ((1 << 34) - 1) // K
+    R = 1024
+    block = synth.activations("normal_outliers", R, K, 5009 + K)
+    say("quantize largest", M, K)
+    b = to_dev(block)
+    x = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    full = M // R * R
+    x[:full].view(-1, R, K).copy_(b.unsqueeze(0).expand(full // R, R, K))
+    x[full:].copy_(b[:M - full])
+    del b
+    q8 = torch.zeros(mmq.mmq_q8_1_bytes(M, K), dtype=torch.uint8, device="cuda")
+    mmq.quantize_q8_1(x, M, K, q8)
+    torch.cuda.synchronize()
+    del x
+    # 16-byte input words past 2^31 from row 2^31 / (K/4) on
+    edge = (1 << 31) // (K // 4)
+    rows = sorted({0, 1, 31, 32, edge - 1, edge, M // 2, M - 33, M - 32, M - 2, M - 1})
+    got = q8_rows(q8, M, K, rows)
+    want_image = oracle.q8_1_image(oracle.quantize_q8_1(block[[r % R for r in rows]]))
+    want = q8_rows(want_image, len(rows), K, range(len(rows)))
+    for name, g, w in zip(("qs", "words", "da plane", "pieces"), got, want):
+        assert np.array_equal(g, w), f"{name}: {np.count_nonzero(g != w)} bytes differ"
