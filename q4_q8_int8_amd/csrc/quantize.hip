@@ -7,16 +7,17 @@
 // that sum to it exactly, grouped per super-block of 8 blocks for the GEMM's bf16 matrix
 // instruction. HBM-bound: 4 bytes read and about 1.44 bytes written per element.
 //
-// Mapping: 8 lanes own one 32-element block (one float4 each), so a wavefront covers 8
-// consecutive blocks = 1 KiB of contiguous input at a time; the max and the sum are reduced
-// with lane moves inside the 8-lane group. Two kernels:
+// Mapping: every load instruction of a wavefront reads 1 KiB of contiguous input, 8
+// consecutive blocks with 8 lanes per block and one float4 per lane; block maxima and sums
+// are reduced with lane moves inside each group of lanes that owns a block. Two kernels:
 // - K % 256 == 0 (whole super-blocks): a workgroup takes a tile of kTileRows rows x one
-//   super-block. The int8 values and scale words of each row go out directly (256 and 32
+//   super-block, and a lane-exchange gives each lane 8 values of one block (4 lanes per
+//   block). The int8 values and scale words of each row go out directly (256 and 32
 //   contiguous bytes); the da plane and the pieces are staged in LDS and written after a
 //   barrier as runs of 4*kTileRows and 16*kTileRows contiguous bytes, not as one 4- or
 //   16-byte store per row scattered M entries apart;
-// - any other K: each wavefront takes 2 groups of 8 consecutive blocks and stores every
-//   block's plane entries where they fall.
+// - any other K: each wavefront takes 2 groups of 8 consecutive blocks, 8 lanes per block,
+//   and stores every block's plane entries where they fall.
 #include "mmq_internal.h"
 
 namespace mmq {
@@ -136,83 +137,114 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float4* __rest
 }
 
 // Whole super-blocks: tile of kTileRows rows x one super-block, kTileWaves wavefronts of
-// kTileRows/kTileWaves rows each, all loads of a wavefront issued first. Indices fit in 32
-// bits: 16-byte words of the input below M*K/4 < 2^32.
+// kTileRows/kTileWaves rows each; 4 lanes own one block, 8 values each, so the per-block
+// work (the max, two divisions, the sum, the f16 and bf16 conversions) is shared by 8
+// values. Indices fit in 32 bits: 16-byte words of the input below M*K/4 < 2^32.
 constexpr int kTileRows = 8;
 constexpr int kTileWaves = 4;
 constexpr int kRowsPerWave = kTileRows / kTileWaves;
+static_assert(kRowsPerWave == 2, "a wavefront's two halves take one row each");
 static_assert(kTileRows % 4 == 0 && 5 * kTileRows <= 64 * kTileWaves, "store phase mapping");
+
+// roundf (half away from zero) of p, converted and clamped to [-127, 127], in three
+// instructions: for every finite float p, trunc(RN(p + copysign(0.5 - 2^-25, p))) equals
+// roundf(p), and v_cvt_i32_f32 truncates, saturates +-inf to the int range and maps NaN to
+// 0 (the 0 * inf of a block whose reciprocal overflowed). p must be the rounded product
+// x * id: the barrier keeps the compiler from fusing it into the add.
+__device__ __forceinline__ int quant_round(float x, float id) {
+  float p = x * id;
+  asm volatile("" : "+v"(p));
+  const float t = p + __builtin_copysignf(0.49999997f, p);
+  int r;
+  asm("v_cvt_i32_f32 %0, %1" : "=v"(r) : "v"(t));
+  return min(max(r, -127), 127);
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+         ((uint32_t)d << 24);
+}
 
 __global__ __launch_bounds__(64 * kTileWaves) void quantize_q8_1_tiled_kernel(
     const float4* __restrict__ x, uint32_t* __restrict__ qs, uint32_t* __restrict__ ds,
     float* __restrict__ da_plane, uint16_t* __restrict__ pieces, uint32_t M, uint32_t K,
     uint32_t nsb) {
-  __shared__ __align__(16) float sDa[8][kTileRows];  // [block of the super-block][row]
-  __shared__ __align__(16) uint4 sPc[3][kTileRows];  // [piece][row]: 8 bf16, one per block
+  __shared__ __align__(16) float sDa[8][kTileRows];      // [block of the super-block][row]
+  __shared__ __align__(16) uint16_t sPc[3][kTileRows][8];  // [piece][row][block]
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const uint32_t s = blockIdx.x % nsb;
   const uint32_t r0 = (blockIdx.x / nsb) * kTileRows;
-  const uint32_t k4 = K / 4;
-  float4 v[kRowsPerWave];
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const uint32_t row = r0 + kRowsPerWave * w + i;
-    v[i] = row < M ? x[row * k4 + 64 * s + lane] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  const int j = lane & 7;
-  const uint32_t b = lane >> 3;  // block of this lane's group within the super-block
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int rl = kRowsPerWave * w + i;
-    const uint32_t row = r0 + rl;
-    const float amax = group_max(fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)),
-                                       fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
-    const float d = amax / 127.0f;                 // IEEE division
-    const float id = d > 0.0f ? 1.0f / d : 0.0f;   // IEEE reciprocal (division)
-    const int q0 = quant1(v[i].x, id), q1 = quant1(v[i].y, id);
-    const int q2 = quant1(v[i].z, id), q3 = quant1(v[i].w, id);
-    const int sum = group_sum(q0 + q1 + q2 + q3);
-    const _Float16 dh = (_Float16)d;  // RNE
-    if (row < M) {
-      qs[row * k4 + 64 * s + lane] = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) |
-                                     ((uint32_t)(q2 & 0xFF) << 16) |
-                                     ((uint32_t)(q3 & 0xFF) << 24);
-      if (j == 0)
-        ds[row * (K / 32) + 8 * s + b] =
-            (uint32_t)__builtin_bit_cast(uint16_t, dh) | ((uint32_t)(sum & 0xFFFF) << 16);
-    }
-    if (j == 0) sDa[b][rl] = (float)dh;
-    // da*sa (exact in f32) as three bf16 pieces; lane j < 3 gathers piece j of the 8 blocks
-    uint16_t pc[3];
-    bf16_split3((float)dh * (float)sum, pc[0], pc[1], pc[2]);
-    const uint32_t offer = j < 3 ? pc[j] : 0u;
-    uint32_t g[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) g[e] = (uint32_t)__shfl((int)offer, 8 * e + j, 64);
-    if (lane < 3)
-      sPc[lane][rl] = make_uint4(g[0] | (g[1] << 16), g[2] | (g[3] << 16), g[4] | (g[5] << 16),
-                                 g[6] | (g[7] << 16));
-  }
+  // Loads: lane l reads 16-byte chunk l of row A (= row 2w of the tile) and of row B, one
+  // contiguous KiB per instruction; chunk l is chunk c = l % 8 of block l / 8. A half-mirror
+  // swap inside each 8-lane group then gives lanes c < 4 chunks c and 7-c of row A, and
+  // lanes c >= 4 chunks c and 7-c of row B: every lane holds 8 values of one block.
+  const int c = lane & 7;
+  const bool lo = c < 4;
+  const int b = lane >> 3;         // block within the super-block
+  const int rl = kRowsPerWave * w + (lo ? 0 : 1);  // row of this lane's block
+  const uint32_t rowA = r0 + kRowsPerWave * w, rowB = rowA + 1;
+  const uint32_t row = lo ? rowA : rowB;
+  const bool ok = row < M;
+  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+  const uint32_t seg = 64 * s + lane;  // 16-byte word of chunk l within a row
+  const float4 uA = rowA < M ? x[rowA * (K / 4) + seg] : zero;
+  const float4 uB = rowB < M ? x[rowB * (K / 4) + seg] : zero;
+  const float4 snd = lo ? uB : uA;
+  const float4 u = lo ? uA : uB;
+  float4 v;
+  v.x = __int_as_float(dpp<kHalfMirror>(__float_as_int(snd.x)));
+  v.y = __int_as_float(dpp<kHalfMirror>(__float_as_int(snd.y)));
+  v.z = __int_as_float(dpp<kHalfMirror>(__float_as_int(snd.z)));
+  v.w = __int_as_float(dpp<kHalfMirror>(__float_as_int(snd.w)));
+  const float m = fmaxf(fmaxf(fmaxf(fabsf(u.x), fabsf(u.y)), fmaxf(fabsf(u.z), fabsf(u.w))),
+                        fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  float amax = fmaxf(m, __int_as_float(dpp<kSwap1>(__float_as_int(m))));
+  amax = fmaxf(amax, __int_as_float(dpp<kSwap2>(__float_as_int(amax))));
+  const float d = amax / 127.0f;                 // IEEE division
+  const float id = d > 0.0f ? 1.0f / d : 0.0f;   // IEEE reciprocal (division)
+  const int q0 = quant_round(u.x, id), q1 = quant_round(u.y, id);
+  const int q2 = quant_round(u.z, id), q3 = quant_round(u.w, id);
+  const int q4 = quant_round(v.x, id), q5 = quant_round(v.y, id);
+  const int q6 = quant_round(v.z, id), q7 = quant_round(v.w, id);
+  int sum = (q0 + q1) + (q2 + q3) + ((q4 + q5) + (q6 + q7));
+  sum += dpp<kSwap1>(sum);
+  sum += dpp<kSwap2>(sum);
+  const _Float16 dh = (_Float16)d;  // RNE
+  // q words back to chunk order: lane l stores word l of row A and of row B
+  const uint32_t own = pack4(q0, q1, q2, q3), oth = pack4(q4, q5, q6, q7);
+  const uint32_t got = (uint32_t)dpp<kHalfMirror>((int)oth);
+  if (rowA < M) qs[rowA * (K / 4) + seg] = lo ? own : got;
+  if (rowB < M) qs[rowB * (K / 4) + seg] = lo ? got : own;
+  if (ok && (c & 3) == 0)
+    ds[row * (K / 32) + 8 * s + b] =
+        (uint32_t)__builtin_bit_cast(uint16_t, dh) | ((uint32_t)(sum & 0xFFFF) << 16);
+  // da, and da*sa (exact in f32) as three bf16 pieces: lane j < 3 stages piece j
+  uint16_t pc[3];
+  bf16_split3((float)dh * (float)sum, pc[0], pc[1], pc[2]);
+  const int j = c & 3;
+  if (j == 0) sDa[b][rl] = (float)dh;
+  if (j < 3) sPc[j][rl][b] = j == 0 ? pc[0] : (j == 1 ? pc[1] : pc[2]);
   __syncthreads();
   const int t = threadIdx.x;
   constexpr int kDaThreads = 2 * kTileRows;  // 8 blocks x kTileRows/4 float4 each
   if (t < kDaThreads) {
-    const int bb = t / (kTileRows / 4), c = t % (kTileRows / 4);
-    const uint32_t row = r0 + 4 * c;
-    float* dst = da_plane + (8 * s + bb) * M + row;
-    if ((M & 3) == 0 && row + 3 < M) {  // 16-byte aligned: the plane starts on 256 bytes
-      *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(&sDa[bb][4 * c]);
+    const int bb = t / (kTileRows / 4), cc = t % (kTileRows / 4);
+    const uint32_t r = r0 + 4 * cc;
+    float* dst = da_plane + (8 * s + bb) * M + r;
+    if ((M & 3) == 0 && r + 3 < M) {  // 16-byte aligned: the plane starts on 256 bytes
+      *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(&sDa[bb][4 * cc]);
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (row + e < M) dst[e] = sDa[bb][4 * c + e];
+        if (r + e < M) dst[e] = sDa[bb][4 * cc + e];
     }
   } else if (t < kDaThreads + 3 * kTileRows) {  // piece pp of row rr of the tile
     const int pp = (t - kDaThreads) / kTileRows, rr = (t - kDaThreads) % kTileRows;
-    const uint32_t row = r0 + rr;
-    if (row < M)
-      *reinterpret_cast<uint4*>(pieces + ((s * 3 + pp) * M + row) * 8) = sPc[pp][rr];
+    const uint32_t r = r0 + rr;
+    if (r < M)
+      *reinterpret_cast<uint4*>(pieces + ((s * 3 + pp) * M + r) * 8) =
+          *reinterpret_cast<const uint4*>(&sPc[pp][rr][0]);
   }
 }
 
