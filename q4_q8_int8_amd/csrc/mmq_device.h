@@ -49,15 +49,14 @@ static __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // after the explicit wait and the barrier (both ordered with the asm), and so the compiler
 // stays free to schedule the current stage's LDS reads around it.
 static __device__ __forceinline__ void dma16(v4i r, uint32_t lds, uint32_t off) {
-  int saved;  // m0 is reserved by the compiler: restore it after use
+  // m0 is declared clobbered, so the compiler re-initialises it wherever it relies on it
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r));
+      "buffer_load_dwordx4 %1, %2, 0 offen lds"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(r)
+      : "m0");
 }
 
 }  // namespace mmq

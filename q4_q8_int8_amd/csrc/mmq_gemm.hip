@@ -175,6 +175,9 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   v16i bias;
 #pragma unroll
   for (int r = 0; r < 16; ++r) bias[r] = kBiasBits;
+  // Opaque to the compiler from here on, so the tuple stays resident in VGPRs: as a known
+  // constant it was kept in SGPRs and copied back (8 moves) before one MFMA in seven.
+  asm volatile("" : "+v"(bias));
   v16f acc[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t)
