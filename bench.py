@@ -218,6 +218,61 @@ def measure(W: dict, R: int, steps: int, warmup: int, tile: int = 0) -> dict:
             "graph_step_us": graph_step_us}
 
 
+def measure_fused(W: dict, R: int, steps: int, warmup: int) -> dict:
+    """Time mmq_q4K_f32 (few tokens: the GEMM quantizes its own activations) as measure()
+    times the two-kernel step: `steps` back-to-back launches between one pair of HIP events,
+    and the same launches replayed from a HIP graph."""
+    import torch
+
+    import q4_q8_int8_amd as mmq
+
+    dev = torch.device("cuda:0")
+    M, N, K = W["M"], W["N"], W["K"]
+    stream = torch.cuda.current_stream()
+    xs = [torch.from_numpy(W["x"]).to(dev) for _ in range(R)]
+    w_dev = torch.from_numpy(W["w"]).to(dev)
+    reps = [torch.empty(mmq.mmq_q4K_repacked_bytes(N, K), dtype=torch.uint8, device=dev)
+            for _ in range(R)]
+    for r in range(R):
+        mmq.repack_q4_K(w_dev, N, K, reps[r])
+    Cs = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(R)]
+
+    def call(r):
+        mmq.mmq_q4K_f32(M, N, K, xs[r], reps[r], Cs[r])
+
+    for i in range(warmup):
+        call(i % R)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        call(i % R)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(stream)
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            for r in range(R):
+                call(r)
+    stream.wait_stream(cs)
+    reps_g = max(1, steps // R)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps_g):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / (reps_g * R)
+    del g, xs, reps, Cs
+    torch.cuda.empty_cache()
+    return {"us": us, "graph_us": graph_us}
+
+
 def measure_f16(W: dict, R: int, steps: int, warmup: int) -> dict:
     """Time the f16 comparator path on one workload: f32 -> f16 conversion of the activations,
     q4_K -> f16 dequantization of the weights, and the f16 GEMM, each as `steps`
@@ -338,6 +393,14 @@ def sweep(args) -> int:
             t = measure(W, args.rotate, args.steps, args.warmup, tile)
             times[(name, tile)] = t
             print(json.dumps(config_line(name, W, t)), flush=True)
+        if W["M"] <= 128:
+            fu = measure_fused(W, args.rotate, args.steps, args.warmup)
+            macs = W["M"] * W["N"] * W["K"]
+            print(json.dumps({"config": name, "M": W["M"], "N": W["N"], "K": W["K"],
+                              "fused": {"us": round(fu["us"], 2),
+                                        "graph_us": round(fu["graph_us"], 2),
+                                        "tmacs": round(macs / (fu["us"] * 1e-6) / 1e12, 2)}}),
+                  flush=True)
         if not args.no_f16:
             f = measure_f16(W, args.rotate, args.steps, args.warmup)
             times[(name, "f16")] = f

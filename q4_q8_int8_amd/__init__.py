@@ -6,7 +6,7 @@ functions here have the same names and arguments as the C entry points and only 
 arguments: tensors are passed as device pointers, the stream defaults to torch's current
 stream, and a nonzero status raises MMQError. Every step of the computation runs in the
 library's HIP kernels; there is no fallback path. Importing this package fails loudly when
-libmmq.so has not been built (python -m q4_q8_int8_amd.build).
+libmmq.so has not been built (python q4_q8_int8_amd/build.py).
 """
 from __future__ import annotations
 
@@ -22,7 +22,7 @@ HEADER_PATH = os.path.join(INCLUDE_DIR, "mmq.h")
 HEADER_PATHS = (HEADER_PATH, os.path.join(INCLUDE_DIR, "mmq_f16.h"))
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m q4_q8_int8_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python q4_q8_int8_amd/build.py`")
 # torch ships its own HIP runtime. Loading torch first makes libmmq.so's libamdhip64
 # dependency resolve to that already-loaded runtime, so the process has a single HIP runtime
 # and torch's device pointers and streams are valid in the library's calls. (Loaded the other
@@ -34,7 +34,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 MMQ_OK, MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_LDS, MMQ_E_DEVICE, MMQ_E_HIP = range(6)
 MMQ_TILE_AUTO, MMQ_TILE_LARGE, MMQ_TILE_SMALL, MMQ_TILE_SKINNY = 0, 1, 2, 3
 (MMQ_REASON_NONE, MMQ_REASON_LARGE, MMQ_REASON_SMALL_GRID, MMQ_REASON_LDS_FALLBACK,
- MMQ_REASON_FORCED, MMQ_REASON_NO_FIT, MMQ_REASON_FEW_TOKENS) = range(7)
+ MMQ_REASON_FORCED, MMQ_REASON_NO_FIT, MMQ_REASON_FEW_TOKENS, MMQ_REASON_FUSED) = range(8)
 QK8, QK_K, Q4K_BLOCK_BYTES, REP_TILE_ROWS, REP_TILE_BYTES = 32, 256, 144, 32, 6656
 
 
@@ -71,6 +71,7 @@ _SIGS = {
     "repack_q4_K": [_vp, _i64, _i64, _vp, _vp],
     "mmq_q4K_q8_1": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "mmq_q4K_q8_1_ex": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.POINTER(mmq_options)],
+    "mmq_q4K_f32": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "mmq_q4K_q8_1_blockdots": [_i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp,
                                ctypes.POINTER(mmq_options)],
     "mmq_plan": [_i64, _i64, _i64, ctypes.POINTER(mmq_options), _i64,
@@ -169,6 +170,12 @@ def mmq_q4K_q8_1_ex(M: int, N: int, K: int, q8, w_rep, C, stream=None,
     _check("mmq_q4K_q8_1_ex",
            _lib.mmq_q4K_q8_1_ex(M, N, K, _ptr(q8), _ptr(w_rep), _ptr(C), _stream(stream),
                                 _opts(force_tile, lds_budget, min_workgroups)))
+
+
+def mmq_q4K_f32(M: int, N: int, K: int, x, w_rep, C, stream=None) -> None:
+    """Few tokens (M <= 128): C[M, N] from f32 activations x [M, K], quantized in the GEMM."""
+    _check("mmq_q4K_f32",
+           _lib.mmq_q4K_f32(M, N, K, _ptr(x), _ptr(w_rep), _ptr(C), _stream(stream)))
 
 
 def mmq_q4K_q8_1_blockdots(M: int, N: int, K: int, q8, w_rep, i0: int, i1: int, j0: int,

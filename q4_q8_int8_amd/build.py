@@ -1,6 +1,7 @@
 """Build libmmq.so in-tree with hipcc for gfx950.
 
-Usage: python -m q4_q8_int8_amd.build   (or q4_q8_int8_amd.build.build())
+Usage: python q4_q8_int8_amd/build.py (run as a file: importing the package loads the library
+this builds).
 """
 from __future__ import annotations
 

@@ -296,6 +296,40 @@ int mmq_q4K_q8_1(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_
   return mmq_q4K_q8_1_ex(M, N, K, q8, w_rep, C, stream, nullptr);
 }
 
+int mmq_q4K_f32(int64_t M, int64_t N, int64_t K, const float* x, const void* w_rep, float* C,
+                void* stream) {
+  int st = check_gemm_shape(M, N, K);
+  if (st) return st;
+  if (M > kSkinnyMaxM)
+    return fail(MMQ_E_SHAPE, "mmq_q4K_f32 is for few tokens: M = %lld is above %lld",
+                (long long)M, (long long)kSkinnyMaxM);
+  if (!x || !w_rep || !C) return fail(MMQ_E_ARG, "null device pointer");
+  if (!aligned16(x) || !aligned16(w_rep) || !aligned16(C))
+    return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
+  DeviceInfo* di;
+  if ((st = current_device(&di))) return st;
+  mmq_kernel_info info = {};
+  info.tile = MMQ_TILE_SKINNY;
+  info.reason = MMQ_REASON_FUSED;
+  info.block_m = 32;
+  info.block_n = 32;
+  info.threads = 64 * mmq::kSkinnyWaves;
+  info.lds_bytes = mmq::fused_lds_bytes();
+  info.lds_budget = di->lds_budget;
+  info.grid = ((M + 31) / 32) * ((N + 31) / 32);
+  if (info.lds_bytes > di->lds_budget) {
+    info.tile = MMQ_TILE_AUTO;
+    info.reason = MMQ_REASON_NO_FIT;
+    g_last = info;
+    return fail(MMQ_E_LDS, "mmq_q4K_f32 needs %lld bytes of LDS, the device allows %lld",
+                (long long)info.lds_bytes, (long long)di->lds_budget);
+  }
+  g_last = info;
+  hipError_t e = mmq::launch_mmq_fused(x, w_rep, C, M, N, K, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("mmq_q4K_f32 launch", e);
+  return ok();
+}
+
 int mmq_q4K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
                            int64_t i0, int64_t i1, int64_t j0, int64_t j1, int32_t* S,
                            void* stream, const mmq_options* opt) {

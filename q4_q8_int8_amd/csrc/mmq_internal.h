@@ -85,6 +85,10 @@ constexpr int kSkinnyWaves = 8;
 int64_t skinny_lds_bytes();
 hipError_t launch_mmq_skinny(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
                              int64_t K, hipStream_t s);
+// The same kernel quantizing its own f32 activations (few tokens; per-wavefront LDS tile).
+int64_t fused_lds_bytes();
+hipError_t launch_mmq_fused(const float* x, const void* w_rep, float* C, int64_t M, int64_t N,
+                            int64_t K, hipStream_t s);
 
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, hipStream_t s);
 hipError_t launch_repack_q4_K(const void* w, int64_t N, int64_t K, void* w_rep, hipStream_t s);

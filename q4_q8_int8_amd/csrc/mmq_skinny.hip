@@ -22,18 +22,37 @@
 // Summation order per output element: within a wavefront as in the main kernel, then the
 // wavefronts' partial sums in increasing wavefront order. Deterministic, but not the same
 // association as the main kernel's (the results agree within the f32 tolerance).
+//
+// The FUSED instantiation takes the f32 activations instead of the q8 buffer. Each wavefront
+// quantizes the real token rows of its own super-blocks itself (8 lanes per block, one row of
+// 1 KiB per pass, with the prepass's arithmetic from quant_device.h) into its own LDS tile:
+// int8 values in 272-byte rows, da, and the three bf16 pieces of da*sa, all in the layout the
+// token operands are then read in. Rows past M stay zero. So with few tokens the q8 buffer
+// never goes through HBM and the prepass launch disappears, and the result is bit for bit the
+// one of the prepass followed by the unfused kernel: the same bytes, the same arithmetic in
+// the same order.
 #include "mmq_device.h"
+#include "quant_device.h"
 
 namespace mmq {
 namespace {
 
-template <int KW>
+// Per-wavefront LDS region of the fused kernel: the weight scales (as in the unfused one),
+// then the quantized token tile of one super-block.
+constexpr int kFQRow = 272;                        // int8 row: 256 values + 16 bytes padding
+constexpr int kFQBytes = 32 * kFQRow;              // [32 rows][272]
+constexpr int kFDaBytes = 8 * 32 * 4;              // da [8 blocks][32 rows]
+constexpr int kFPcBytes = 3 * 32 * 16;             // pieces [3][32 rows][8 bf16]
+constexpr int kFRegion = kRepDsvBytes + kRepPieceBytes + kFQBytes + kFDaBytes + kFPcBytes;
+
+template <int KW, bool FUSED>
 __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
     const int8_t* __restrict__ qs, const float* __restrict__ da_plane,
-    const uint16_t* __restrict__ tpieces, const uint8_t* __restrict__ wrep,
-    float* __restrict__ C, int M, int N, int K, int gm) {
+    const uint16_t* __restrict__ tpieces, const float4* __restrict__ x,
+    const uint8_t* __restrict__ wrep, float* __restrict__ C, int M, int N, int K, int gm) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int W_BYTES = kRepDsvBytes + kRepPieceBytes;
+  constexpr int REGION = FUSED ? kFRegion : W_BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -54,9 +73,18 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wtile, (uint32_t)nsb * kRepTileBytes);
   const v4i rwd = make_rsrc_sgpr(wtile, (uint32_t)nsb * kRepTileBytes);
 
-  uint8_t* sW = smem + wave * W_BYTES;
-  const uint32_t sWa = lds_addr(smem) + (uint32_t)(wave * W_BYTES);  // its LDS address
+  uint8_t* sW = smem + wave * REGION;
+  const uint32_t sWa = lds_addr(smem) + (uint32_t)(wave * REGION);  // its LDS address
   const float* sWw = reinterpret_cast<const float*>(sW);
+  uint8_t* sQ = sW + W_BYTES;                                      // fused: token tile
+  float* sDa = reinterpret_cast<float*>(sQ + kFQBytes);
+  uint8_t* sPc = sQ + kFQBytes + kFDaBytes;
+  const int mt = M - m0 < 32 ? M - m0 : 32;  // real token rows of this tile
+  if constexpr (FUSED) {
+    // rows past M stay zero: q = 0, da = 0, pieces 0
+    for (int o = lane * 16; o < kFQBytes + kFDaBytes + kFPcBytes; o += 64 * 16)
+      *reinterpret_cast<v4i*>(sQ + o) = v4i{0, 0, 0, 0};
+  }
   // token row of this lane: every offset inside the row is below K, so rows past M read
   // past the end of the buffer (zero)
   const uint32_t tok_row = (uint32_t)(m0 + l32) * (uint32_t)K + h * 16;
@@ -69,8 +97,13 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
   for (int s = s0; s < s1; ++s) {
-    // this wavefront's earlier LDS reads of its region are done before the loads overwrite it
+    // this wavefront's earlier LDS reads of its region are done before the loads (and, fused,
+    // the quantized tile of this super-block) overwrite it
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), the other counters unconstrained
+    if constexpr (FUSED) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
     const uint32_t wo = (uint32_t)s * kRepTileBytes + kRepNibBytes + lane * 16;
     dma16(rwd, sWa, wo);
     dma16(rwd, sWa + 1024, wo + 1024);
@@ -80,14 +113,68 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g)
       raw[g] = buf_load16(rw, (uint32_t)s * kRepTileBytes + g * 1024 + lane * 16);
+    if constexpr (FUSED) {
+      // quantize rows 0..mt-1 of super-block s: lane = 8 * block + chunk, one float4 each.
+      // Rows go in unrolled chunks of 8, 4, 2 or 1 (no early exit inside a chunk), so the
+      // loads of a chunk are in flight together and its rows' dependent chains interleave.
+      const int b = lane >> 3, c = lane & 7;
+      auto rows = [&](const int r0, auto count) {
+        constexpr int R = decltype(count)::value;
+        float4 vr[R];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) tok[b] = buf_load16(rq, tok_row + (uint32_t)s * 256 + b * 32);
+        for (int i = 0; i < R; ++i)
+          vr[i] = x[((uint32_t)(m0 + r0 + i) * (uint32_t)K + (uint32_t)s * 256) / 4 + lane];
 #pragma unroll
-    for (int b = 0; b < 8; ++b)
-      da[b] = buf_load_f32(rda, (((uint32_t)s * 8 + b) * (uint32_t)M + m0 + l32) * 4u);
+        for (int i = 0; i < R; ++i) {
+          const int r = r0 + i;
+          const float4 v = vr[i];
+          const float amax =
+              group_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+          const float d = amax / 127.0f;                 // IEEE division
+          const float id = d > 0.0f ? 1.0f / d : 0.0f;   // IEEE reciprocal (division)
+          const int q0 = quant1(v.x, id), q1 = quant1(v.y, id);
+          const int q2 = quant1(v.z, id), q3 = quant1(v.w, id);
+          const int sum = group_sum(q0 + q1 + q2 + q3);
+          const _Float16 dh = (_Float16)d;  // RNE
+          *reinterpret_cast<uint32_t*>(sQ + r * kFQRow + lane * 4) =
+              (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
+              ((uint32_t)(q3 & 0xFF) << 24);
+          if (c == 0) sDa[b * 32 + r] = (float)dh;
+          // da*sa (exact in f32) as three bf16 pieces: lane c < 3 of the block's group
+          // writes piece c into slot b of the row's 16 bytes for that piece
+          uint16_t pc[3];
+          bf16_split3((float)dh * (float)sum, pc[0], pc[1], pc[2]);
+          if (c < 3)
+            reinterpret_cast<uint16_t*>(sPc)[(c * 32 + r) * 8 + b] =
+                c == 0 ? pc[0] : (c == 1 ? pc[1] : pc[2]);
+        }
+      };
+      int r0 = 0;
+      for (; r0 + 8 <= mt; r0 += 8) rows(r0, std::integral_constant<int, 8>{});
+      if (r0 + 4 <= mt) { rows(r0, std::integral_constant<int, 4>{}); r0 += 4; }
+      if (r0 + 2 <= mt) { rows(r0, std::integral_constant<int, 2>{}); r0 += 2; }
+      if (r0 < mt) rows(r0, std::integral_constant<int, 1>{});
+      // the tile is complete: other lanes' writes are visible to this wavefront's reads
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-      tp[j] = buf_load16(rtp, (((uint32_t)s * 3 + j) * (uint32_t)M + m0 + l32) * 16u);
+      for (int b2 = 0; b2 < 8; ++b2)
+        tok[b2] = *reinterpret_cast<const v4i*>(sQ + l32 * kFQRow + b2 * 32 + h * 16);
+#pragma unroll
+      for (int b2 = 0; b2 < 8; ++b2) da[b2] = sDa[b2 * 32 + l32];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) tp[j] = *reinterpret_cast<const v4i*>(sPc + (j * 32 + l32) * 16);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 8; ++b) tok[b] = buf_load16(rq, tok_row + (uint32_t)s * 256 + b * 32);
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        da[b] = buf_load_f32(rda, (((uint32_t)s * 8 + b) * (uint32_t)M + m0 + l32) * 4u);
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        tp[j] = buf_load16(rtp, (((uint32_t)s * 3 + j) * (uint32_t)M + m0 + l32) * 16u);
+    }
     // everything, the LDS region included, has landed; the fence keeps the compiler from
     // moving the region's reads above the wait
     __builtin_amdgcn_s_waitcnt(0);
@@ -155,6 +242,12 @@ int64_t skinny_lds_bytes() {
   return regions > reduce ? regions : reduce;
 }
 
+int64_t fused_lds_bytes() {
+  const int64_t regions = (int64_t)kSkinnyWaves * kFRegion;
+  const int64_t reduce = (int64_t)kSkinnyWaves * 16 * 64 * 4;
+  return regions > reduce ? regions : reduce;
+}
+
 hipError_t launch_mmq_skinny(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
                              int64_t K, hipStream_t s) {
   const uint8_t* base = static_cast<const uint8_t*>(q8);
@@ -162,10 +255,25 @@ hipError_t launch_mmq_skinny(const void* q8, const void* w_rep, float* C, int64_
   const float* da_plane = reinterpret_cast<const float*>(base + q8_planes_offset(M, K));
   const uint16_t* tpieces = reinterpret_cast<const uint16_t*>(base + q8_pieces_offset(M, K));
   const int64_t gm = (M + 31) / 32, gn = (N + 31) / 32;
-  hipLaunchKernelGGL(mmq_skinny_kernel<kSkinnyWaves>, dim3((unsigned)(gm * gn)),
+  hipLaunchKernelGGL((mmq_skinny_kernel<kSkinnyWaves, false>), dim3((unsigned)(gm * gn)),
                      dim3(kSkinnyWaves * 64), (size_t)skinny_lds_bytes(), s, qs, da_plane,
-                     tpieces, static_cast<const uint8_t*>(w_rep), C, (int)M, (int)N, (int)K,
-                     (int)gm);
+                     tpieces, nullptr, static_cast<const uint8_t*>(w_rep), C, (int)M, (int)N,
+                     (int)K, (int)gm);
+  return hipGetLastError();
+}
+
+hipError_t launch_mmq_fused(const float* x, const void* w_rep, float* C, int64_t M, int64_t N,
+                            int64_t K, hipStream_t s) {
+  auto kern = mmq_skinny_kernel<kSkinnyWaves, true>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)fused_lds_bytes());
+  if (e != hipSuccess) return e;
+  const int64_t gm = (M + 31) / 32, gn = (N + 31) / 32;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(gm * gn)), dim3(kSkinnyWaves * 64),
+                     (size_t)fused_lds_bytes(), s, nullptr, nullptr, nullptr,
+                     reinterpret_cast<const float4*>(x), static_cast<const uint8_t*>(w_rep), C,
+                     (int)M, (int)N, (int)K, (int)gm);
   return hipGetLastError();
 }
 

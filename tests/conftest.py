@@ -24,8 +24,13 @@ def _ensure_built():
     """Build libmmq.so in-tree when it is missing (hipcc cross-compiles without a GPU)."""
     lib = os.path.join(ROOT, "q4_q8_int8_amd", "libmmq.so")
     if not os.path.exists(lib):
-        from q4_q8_int8_amd.build import build
-        build()
+        # by path: importing the package needs the library it builds
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "q4_q8_int8_amd_build", os.path.join(ROOT, "q4_q8_int8_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
 
 
 _ensure_built()

@@ -191,6 +191,11 @@ Cp = 0x30000000
     (("mmq_q4K_q8_1_blockdots", 4, 8, 256, A, B, 2, 2, 0, 8, Cp, None, None), mmq.MMQ_E_SHAPE),
     (("mmq_q4K_q8_1_blockdots", 4, 8, 256, A, B, 0, 4, -1, 8, Cp, None, None), mmq.MMQ_E_SHAPE),
     (("mmq_q4K_q8_1_blockdots", 4, 8, 256, A, B, 0, 4, 0, 8, None, None, None), mmq.MMQ_E_ARG),
+    (("mmq_q4K_f32", 129, 8, 256, A, B, Cp, None), mmq.MMQ_E_SHAPE),     # few tokens only
+    (("mmq_q4K_f32", 4, 8, 100, A, B, Cp, None), mmq.MMQ_E_SHAPE),
+    (("mmq_q4K_f32", 4, 8, 256, None, B, Cp, None), mmq.MMQ_E_ARG),
+    (("mmq_q4K_f32", 4, 8, 256, A + 4, B, Cp, None), mmq.MMQ_E_ARG),
+    (("mmq_q4K_f32", 0, 8, 256, A, B, Cp, None), mmq.MMQ_E_ARG),
 ])
 def test_hot_path_validation(call, status):
     assert mmq.raw_call(*call) == status
@@ -259,3 +264,11 @@ def test_f16_path_reaches_the_device_check(call):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: the call would run")
     assert mmq.raw_call(*call) == mmq.MMQ_E_DEVICE
+
+
+def test_fused_path_reaches_the_device_check():
+    # M = 128 is the largest accepted; without a GPU the device check refuses the call
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: the call would run")
+    assert mmq.raw_call("mmq_q4K_f32", 128, 8, 256, A, B, Cp, None) == mmq.MMQ_E_DEVICE

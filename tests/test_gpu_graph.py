@@ -122,3 +122,30 @@ def test_side_stream_is_honoured():
     mmq.mmq_q4K_q8_1(M, N, K, q8b, rep, C1, stream=s)
     s.synchronize()
     assert np.array_equal(C1.cpu().numpy(), C0.cpu().numpy())
+
+
+def test_fused_few_token_step_in_a_graph():
+    M, N, K = 2, 4096, 4096
+    x = to_dev(synth.activations("normal_outliers", M, K, 7006))
+    w, _ = synth.q4k_weights("fit", N, K, 7007)
+    rep = torch.empty(mmq.mmq_q4K_repacked_bytes(N, K), dtype=torch.uint8, device="cuda")
+    mmq.repack_q4_K(to_dev(w), N, K, rep)
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    say("graph: fused step eager", M, N, K)
+    mmq.mmq_q4K_f32(M, N, K, x, rep, C)
+    torch.cuda.synchronize()
+    want = C.cpu().numpy()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            mmq.mmq_q4K_f32(M, N, K, x, rep, C)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    def disturb():
+        C.fill_(0.0)
+    say("graph: fused replays", M, N, K)
+    _replay_and_check(g, C, want, disturb)
+

@@ -6,6 +6,7 @@ of it. So the helper is only correct while the compiler itself neither reads nor
 in the kernels that call it. This test compiles those sources to gfx950 assembly with the
 library's own flags and checks every instruction outside the inline-assembly blocks.
 """
+import importlib.util
 import os
 import re
 import shutil
@@ -15,7 +16,11 @@ from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
-build = pytest.importorskip("q4_q8_int8_amd.build")
+_spec = importlib.util.spec_from_file_location(
+    "q4_q8_int8_amd_build", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                         "q4_q8_int8_amd", "build.py"))
+build = importlib.util.module_from_spec(_spec)
+_spec.loader.exec_module(build)
 
 USERS = ["mmq_gemm.hip", "mmq_skinny.hip"]   # the sources that call dma16
 M0 = re.compile(r"\bm0\b")
