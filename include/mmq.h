@@ -123,7 +123,10 @@ int mmq_q4K_repacked_bytes(int64_t N, int64_t K, size_t* bytes);
  *                            bits 16..31 = sa as a signed 16-bit integer (|sa| <= 4064)
  *                            (the packed da/sa word of the r15 page, section 3.2)
  *   up to P = the next multiple of 256: padding (not written)
- *   bytes [P, P + 4*M*K/32): float da [K/32][M] (block-major), the token factor of term1
+ *   bytes [P, P + 8*M*K/32): float pairs (da, nda) [K/32][M] (block-major): da, the token
+ *                            factor of term1, and nda = -1.5 * 2^23 * da (exact), the
+ *                            constant of the GEMM's rescale of its integer results, which
+ *                            come offset by 1.5 * 2^23
  *   up to Q = the next multiple of 256: padding (not written)
  *   bytes [Q, Q + 48*M*ceil(K/256)): uint16 bf16 pieces [K/256 rounded up][3][M][8]: piece
  *                            i of da*sa of row r, block 8s+e at [s][i][r][e]. da*sa is the

@@ -130,7 +130,9 @@ def q8_1_image(q: Q8) -> np.ndarray:
        16 bits = sa as a signed 16-bit integer (the token-pair staging word of the r15 page,
        §3.2, the wide kernel's uint2-packed da/sa);
     3. zero padding up to a multiple of 256 bytes;
-    4. da as float32, block-major [K/32][M] (the token factor of term1);
+    4. per (block, row), block-major [K/32][M], the float32 pair (da, -1.5 * 2^23 * da): the
+       token factor of term1, and with it the constant the GEMM adds when it rescales an
+       integer result offset by 1.5 * 2^23 (both exact: da has 11 significant bits);
     5. zero padding up to a multiple of 256 bytes;
     6. the folded row factor of term2, da*sa (r16 page §2.1, exact in float32), as the three
        bf16 pieces of bf16_pieces, [ceil(K/256)][3][M][8]: piece i of row r, block 8s+e at
@@ -146,7 +148,10 @@ def q8_1_image(q: Q8) -> np.ndarray:
     da = f16_decode(q.da_bits)                                  # exact f64
     dma = da * q.sa.astype(np.float64)                          # exact: <= 23 significant bits
     assert np.array_equal(dma.astype(np.float32).astype(np.float64), dma)
-    plane = np.ascontiguousarray(da.T).astype("<f4").reshape(-1).view(np.uint8)
+    nda = -1.5 * 2.0 ** 23 * da                                  # exact in f64
+    assert np.array_equal(nda.astype(np.float32).astype(np.float64), nda)
+    plane = np.ascontiguousarray(np.stack([da.T, nda.T], axis=-1)).astype("<f4")
+    plane = plane.reshape(-1).view(np.uint8)                    # [K/32][M][2]
     pieces = np.zeros((nsb, 3, M, 8), "<u2")
     pc = bf16_pieces(dma.astype(np.float32))                    # [M][K/32][3]
     for b in range(nb):

@@ -23,6 +23,9 @@ static __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, uint3
 static __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
+static __device__ __forceinline__ float2 buf_load_f32x2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
 // The same descriptor as four SGPRs, for the direct-to-LDS load below.
 static __device__ __forceinline__ v4i make_rsrc_sgpr(const void* p, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(p);

@@ -9,7 +9,8 @@
 // so every S is rescaled on the vector ALU:
 //
 //   D   = MFMA_i8(w, q, bias)       bias = 0x4B400000, so float(D) = 12582912 + S exactly
-//   y   = fma(float(D), da, nb)     nb = -12582912 * da (exact), y = RN(S * da)
+//   y   = fma(float(D), da, nb)     nb = -12582912 * da (exact, written by the prepass beside
+//                                   da), y = RN(S * da)
 //   acc = fma(y, dsv, acc)          term1
 //
 // y equals float(S) * da bit for bit, without an int->float conversion instruction.
@@ -21,8 +22,9 @@
 //
 // Operand orientation: MFMA rows (src0) are weight rows, columns (src1, one per lane) are
 // tokens. Lane l holds token l%32 of a tile and, in its 16 accumulator registers r, the
-// weight rows 8*(r/4) + 4*(l/32) + r%4. Per block, the token scale da is one float per lane
-// and the weight scales dsv 16 floats per lane (lane-half broadcast), both read from LDS;
+// weight rows 8*(r/4) + 4*(l/32) + r%4. Per block, the token scale da and its nb are one
+// float pair per lane and the weight scales dsv 16 floats per lane (lane-half broadcast),
+// all read from LDS;
 // dma and dmv for term2 are one float per lane per pair of blocks.
 //
 // Workgroup: NW wavefronts; wavefront w owns weight tile (32 rows) tn*NW + w for all
@@ -31,7 +33,8 @@
 //   - into LDS by direct-to-LDS buffer loads (no registers, no conversion): the int8 token
 //     tile in 272-byte rows (16 bytes of padding, so the 16-byte operand reads of 16
 //     consecutive rows hit distinct banks and every LDS address is a per-lane base plus a
-//     constant), the {da, dma} plane of the token tile, and each wavefront's dsv/dmv;
+//     constant), the (da, nb) pairs and the dma pieces of the token tile, and each
+//     wavefront's dsv/dmv;
 //   - into registers: the wavefront's nibbles, where the 64 lanes of one load read 1 KiB of
 //     contiguous memory.
 // Buffer loads take 32-bit offsets off wave-uniform descriptors; reads past the end of an
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   constexpr int BM = 32 * TT;
   constexpr int NS = 8 * TT;                      // (block, token tile) steps per super-block
   constexpr int A_BYTES = BM * kRowStride;        // token tile
-  constexpr int DA_BYTES = BM * 32;               // da [8][BM]
+  constexpr int DA_BYTES = BM * 64;               // (da, nb) pairs [8][BM][2]
   constexpr int TP_BYTES = BM * 48;               // token pieces of da*sa [3][BM][8]
   constexpr int W_BYTES = kRepDsvBytes + kRepPieceBytes;  // per wavefront: dsv, dmv pieces
   constexpr int STAGE = A_BYTES + DA_BYTES + TP_BYTES + NW * W_BYTES;
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   const int nsb = K >> 8;
   const int kb = K >> 5;
   const v4i rq = make_rsrc_sgpr(qs, (uint32_t)M * (uint32_t)K);
-  const v4i rda = make_rsrc_sgpr(da_plane, (uint32_t)M * (uint32_t)kb * 4u);
+  const v4i rda = make_rsrc_sgpr(da_plane, (uint32_t)M * (uint32_t)kb * 8u);
   const v4i rtp = make_rsrc_sgpr(tpieces, (uint32_t)M * (uint32_t)nsb * 48u);
   const uint8_t* wtile = wrep + (size_t)wt * nsb * kRepTileBytes;
   const v4i rwd = make_rsrc_sgpr(wtile, (uint32_t)nsb * kRepTileBytes);
@@ -147,11 +150,11 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
       return;
     }
     v -= A_PER_WAVE;
-    if (v < DA_PER_WAVE) {  // da of block b for rows m0..m0+BM-1: BM/4 lanes
+    if (v < DA_PER_WAVE) {  // (da, nb) of block b for rows m0..m0+BM-1: BM/2 lanes
       const int b = wave + v * NW;
-      if (b < 8 && lane < BM / 4)
-        dma16(rda, st + A_BYTES + b * BM * 4,
-              (((uint32_t)s * 8 + b) * (uint32_t)M + m0) * 4u + lane * 16);
+      if (b < 8 && lane < BM / 2)
+        dma16(rda, st + A_BYTES + b * BM * 8,
+              (((uint32_t)s * 8 + b) * (uint32_t)M + m0) * 8u + lane * 16);
       return;
     }
     v -= DA_PER_WAVE;
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
 
     const uint8_t* st = smem + p * STAGE;
     const uint8_t* sArow = st + l32 * kRowStride + h * 16;
-    const float* sDa = reinterpret_cast<const float*>(st + A_BYTES);
+    const float2* sDa = reinterpret_cast<const float2*>(st + A_BYTES);
     const uint8_t* sTp = st + A_BYTES + DA_BYTES;
     const uint8_t* sW = st + A_BYTES + DA_BYTES + TP_BYTES + wave * W_BYTES;
     const float* sWw = reinterpret_cast<const float*>(sW);
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
       const int b = n / TT, t = n % TT;
       return *reinterpret_cast<const v4i*>(sArow + t * 32 * kRowStride + b * 32);
     };
-    auto da_of = [&](int n) -> float { return sDa[(n / TT) * BM + (n % TT) * 32 + l32]; };
+    auto da_of = [&](int n) -> float2 { return sDa[(n / TT) * BM + (n % TT) * 32 + l32]; };
     auto dsv_of = [&](int b, float (&d)[16]) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
       float dsv[2][16];
       dsv_of(0, dsv[0]);
       v4i tnext = top_of(1 % NS);
-      float da = da_of(0);
+      float2 da = da_of(0);
       v16i Dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(wop_of(0), top_of(0), bias, 0, 0, 0);
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
@@ -277,17 +280,16 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
             if (n == (2 * g + 2) * TT) raw[g] = load_nib(s + 1, g);
         }
         const v16i D = Dn;
-        const float dac = da;
+        const float2 dac = da;  // (da, nb)
         if (n + 1 < NS) {
           Dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(wop_of((n + 1) / TT), tnext, bias, 0, 0, 0);
           da = da_of(n + 1);
         }
         if (n + 2 < NS) tnext = top_of(n + 2);
         if (t == 0 && b + 1 < 8) dsv_of(b + 1, dsv[(b + 1) & 1]);
-        const float nb = -kBiasF * dac;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float y = __builtin_fmaf(__int_as_float(D[r]), dac, nb);
+          const float y = __builtin_fmaf(__int_as_float(D[r]), dac.x, dac.y);
           acc[t][r] = __builtin_fmaf(y, dsv[b & 1][r], acc[t][r]);
         }
         if (b == 1 || b == 3 || b == 5) {

@@ -29,10 +29,10 @@ struct TileShape {
   constexpr int block_m() const { return 32 * tt; }
   constexpr int block_n() const { return 32 * nw; }
   constexpr int threads() const { return 64 * nw; }
-  // LDS: two stages, each: the int8 token tile [BM][272], da f32 [8][BM], the token
-  // pieces bf16 [3][BM][8], and per wavefront its dsv and dmv pieces (2560 bytes)
+  // LDS: two stages, each: the int8 token tile [BM][272], the (da, nda) pairs f32 [8][BM][2],
+  // the token pieces bf16 [3][BM][8], and per wavefront its dsv and dmv pieces (2560 bytes)
   constexpr int64_t stage_bytes() const {
-    return (int64_t)block_m() * (kRowStride + 32 + 48) + (int64_t)nw * (kRepDsvBytes + kRepPieceBytes);
+    return (int64_t)block_m() * (kRowStride + 64 + 48) + (int64_t)nw * (kRepDsvBytes + kRepPieceBytes);
   }
   constexpr int64_t lds_bytes() const { return 2 * stage_bytes(); }
 };
@@ -40,14 +40,14 @@ constexpr TileShape kLarge{4, 8};
 constexpr TileShape kSmall{1, 2};
 
 // q8 buffer: int8 q [M][K], u32 scale words [M][K/32], then (each at a 256-byte boundary)
-// the GEMM's planes: da f32 [K/32][M] and dma = da*sa as three bf16 pieces per value,
-// [ceil(K/256)][3][M][8].
+// the GEMM's planes: f32 pairs (da, nda = -kBiasF * da) [K/32][M][2], and dma = da*sa as
+// three bf16 pieces per value, [ceil(K/256)][3][M][8].
 __host__ __device__ constexpr int64_t round256(int64_t v) { return (v + 255) / 256 * 256; }
 __host__ __device__ constexpr int64_t q8_planes_offset(int64_t M, int64_t K) {
   return round256(M * K + 4 * M * (K / 32));
 }
 __host__ __device__ constexpr int64_t q8_pieces_offset(int64_t M, int64_t K) {
-  return round256(q8_planes_offset(M, K) + 4 * M * (K / 32));
+  return round256(q8_planes_offset(M, K) + 8 * M * (K / 32));
 }
 __host__ __device__ constexpr int64_t q8_total_bytes(int64_t M, int64_t K) {
   return q8_pieces_offset(M, K) + 48 * M * ((K / 32 + 7) / 8);

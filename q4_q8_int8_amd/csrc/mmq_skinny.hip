@@ -12,10 +12,10 @@
 //
 // Per super-block a wavefront loads everything it needs with single instructions: the
 // token operand of each block straight into registers (16 bytes per lane; token rows past
-// M read past the end of the buffer, which returns zero), da of each block, the three bf16
+// M read past the end of the buffer, which returns zero), (da, nb) of each block, the three bf16
 // pieces of da*sa, its four 16-byte nibble words, and, into its own 2560-byte LDS region,
 // the weight scales dsv and the dmv pieces (which every lane half needs in a different
-// pattern). Per block: D = MFMA_i8(w, q, bias), y = fma(D, da, -12582912*da),
+// pattern). Per block: D = MFMA_i8(w, q, bias), y = fma(D, da, nb) with nb = -12582912*da,
 // acc = fma(y, dsv, acc) exactly as in the main kernel; one third of the super-block's
 // term2 is added by a bf16 MFMA after blocks 1, 3 and 5.
 //
@@ -26,7 +26,7 @@
 // The FUSED instantiation takes the f32 activations instead of the q8 buffer. Each wavefront
 // quantizes the real token rows of its own super-blocks itself (8 lanes per block, one row of
 // 1 KiB per pass, with the prepass's arithmetic from quant_device.h) into its own LDS tile:
-// int8 values in 272-byte rows, da, and the three bf16 pieces of da*sa, all in the layout the
+// int8 values in 272-byte rows, (da, nb), and the three bf16 pieces of da*sa, all in the layout the
 // token operands are then read in. Rows past M stay zero. So with few tokens the q8 buffer
 // never goes through HBM and the prepass launch disappears, and the result is bit for bit the
 // one of the prepass followed by the unfused kernel: the same bytes, the same arithmetic in
@@ -41,7 +41,7 @@ namespace {
 // then the quantized token tile of one super-block.
 constexpr int kFQRow = 272;                        // int8 row: 256 values + 16 bytes padding
 constexpr int kFQBytes = 32 * kFQRow;              // [32 rows][272]
-constexpr int kFDaBytes = 8 * 32 * 4;              // da [8 blocks][32 rows]
+constexpr int kFDaBytes = 8 * 32 * 8;              // (da, nb) [8 blocks][32 rows]
 constexpr int kFPcBytes = 3 * 32 * 16;             // pieces [3][32 rows][8 bf16]
 constexpr int kFRegion = kRepDsvBytes + kRepPieceBytes + kFQBytes + kFDaBytes + kFPcBytes;
 
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
 
   const uint8_t* wtile = wrep + (size_t)tn * nsb * kRepTileBytes;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(qs, (uint32_t)M * (uint32_t)K);
-  const __amdgpu_buffer_rsrc_t rda = make_rsrc(da_plane, (uint32_t)M * (uint32_t)kb * 4u);
+  const __amdgpu_buffer_rsrc_t rda = make_rsrc(da_plane, (uint32_t)M * (uint32_t)kb * 8u);
   const __amdgpu_buffer_rsrc_t rtp = make_rsrc(tpieces, (uint32_t)M * (uint32_t)nsb * 48u);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wtile, (uint32_t)nsb * kRepTileBytes);
   const v4i rwd = make_rsrc_sgpr(wtile, (uint32_t)nsb * kRepTileBytes);
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
   const uint32_t sWa = lds_addr(smem) + (uint32_t)(wave * REGION);  // its LDS address
   const float* sWw = reinterpret_cast<const float*>(sW);
   uint8_t* sQ = sW + W_BYTES;                                      // fused: token tile
-  float* sDa = reinterpret_cast<float*>(sQ + kFQBytes);
+  float2* sDa = reinterpret_cast<float2*>(sQ + kFQBytes);
   uint8_t* sPc = sQ + kFQBytes + kFDaBytes;
   const int mt = M - m0 < 32 ? M - m0 : 32;  // real token rows of this tile
   if constexpr (FUSED) {
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
     dma16(rwd, sWa + 1024, wo + 1024);
     if (lane < 32) dma16(rwd, sWa + 2048, wo + 2048);
     v4i raw[4], tok[8], tp[3];
-    float da[8];
+    float2 da[8];  // (da, nb) per block
 #pragma unroll
     for (int g = 0; g < 4; ++g)
       raw[g] = buf_load16(rw, (uint32_t)s * kRepTileBytes + g * 1024 + lane * 16);
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
           *reinterpret_cast<uint32_t*>(sQ + r * kFQRow + lane * 4) =
               (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
               ((uint32_t)(q3 & 0xFF) << 24);
-          if (c == 0) sDa[b * 32 + r] = (float)dh;
+          if (c == 0) sDa[b * 32 + r] = make_float2((float)dh, -kBiasF * (float)dh);
           // da*sa (exact in f32) as three bf16 pieces: lane c < 3 of the block's group
           // writes piece c into slot b of the row's 16 bytes for that piece
           uint16_t pc[3];
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
       for (int b = 0; b < 8; ++b) tok[b] = buf_load16(rq, tok_row + (uint32_t)s * 256 + b * 32);
 #pragma unroll
       for (int b = 0; b < 8; ++b)
-        da[b] = buf_load_f32(rda, (((uint32_t)s * 8 + b) * (uint32_t)M + m0 + l32) * 4u);
+        da[b] = buf_load_f32x2(rda, (((uint32_t)s * 8 + b) * (uint32_t)M + m0 + l32) * 8u);
 #pragma unroll
       for (int j = 0; j < 3; ++j)
         tp[j] = buf_load16(rtp, (((uint32_t)s * 3 + j) * (uint32_t)M + m0 + l32) * 16u);
@@ -195,10 +195,9 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
         const float4 a = *reinterpret_cast<const float4*>(sWw + b * 32 + 8 * g + 4 * h);
         dsv[4 * g + 0] = a.x; dsv[4 * g + 1] = a.y; dsv[4 * g + 2] = a.z; dsv[4 * g + 3] = a.w;
       }
-      const float nb = -kBiasF * da[b];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float y = __builtin_fmaf(__int_as_float(D[r]), da[b], nb);
+        const float y = __builtin_fmaf(__int_as_float(D[r]), da[b].x, da[b].y);
         acc[r] = __builtin_fmaf(y, dsv[r], acc[r]);
       }
       if (b == 1 || b == 3 || b == 5) {

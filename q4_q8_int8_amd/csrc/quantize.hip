@@ -2,10 +2,12 @@
 // integer block sum, the format of the r15 page ("f32-accumulate mma probe + rank-1 term2
 // rescale", section 2.1), computed "for free" by the prepass as on that page (section 2.1).
 // It also writes the GEMM's planes, so that the GEMM stages them with direct-to-LDS loads
-// and never converts: da as f32 in block-major order, and the folded row factor da*sa of
+// and never converts: da as f32 in block-major order, paired with nda = -1.5*2^23*da (the
+// constant of the GEMM's rescale of an integer result offset by 1.5*2^23, exact), and the
+// folded row factor da*sa of
 // term2 (r16 page, "Narrow kernel gets the rank-1 fold", section 2.1) as three bf16 pieces
 // that sum to it exactly, grouped per super-block of 8 blocks for the GEMM's bf16 matrix
-// instruction. HBM-bound: 4 bytes read and about 1.44 bytes written per element.
+// instruction. HBM-bound: 4 bytes read and about 1.56 bytes written per element.
 //
 // Mapping: every load instruction of a wavefront reads 1 KiB of contiguous input, 8
 // consecutive blocks with 8 lanes per block and one float4 per lane; block maxima and sums
@@ -14,7 +16,7 @@
 //   super-block, and a lane-exchange gives each lane 8 values of one block (4 lanes per
 //   block). The int8 values and scale words of each row go out directly (256 and 32
 //   contiguous bytes); the da plane and the pieces are staged in LDS and written after a
-//   barrier as runs of 4*kTileRows and 16*kTileRows contiguous bytes, not as one 4- or
+//   barrier as runs of 8*kTileRows and 16*kTileRows contiguous bytes, not as one 8- or
 //   16-byte store per row scattered M entries apart;
 // - any other K: each wavefront takes 2 groups of 8 consecutive blocks, 8 lanes per block,
 //   and stores every block's plane entries where they fall.
@@ -47,7 +49,8 @@ __device__ __forceinline__ void quantize_block(const float4 v, const uint32_t bl
                                 ((uint32_t)(q2 & 0xFF) << 16) | ((uint32_t)(q3 & 0xFF) << 24);
     if ((lane & 7) == 0) {
       ds[blk] = (uint32_t)__builtin_bit_cast(uint16_t, dh) | ((uint32_t)(sum & 0xFFFF) << 16);
-      da_plane[b * M + row] = (float)dh;  // the GEMM's da plane, block-major
+      reinterpret_cast<float2*>(da_plane)[b * M + row] =  // the GEMM's plane, block-major
+          make_float2((float)dh, -kBiasF * (float)dh);
     }
   }
 
@@ -118,7 +121,7 @@ constexpr int kTileRows = 8;
 constexpr int kTileWaves = 4;
 constexpr int kRowsPerWave = kTileRows / kTileWaves;
 static_assert(kRowsPerWave == 2, "a wavefront's two halves take one row each");
-static_assert(kTileRows % 4 == 0 && 5 * kTileRows <= 64 * kTileWaves, "store phase mapping");
+static_assert(kTileRows % 2 == 0 && 7 * kTileRows <= 64 * kTileWaves, "store phase mapping");
 
 // roundf (half away from zero) of p, converted and clamped to [-127, 127], in three
 // instructions: for every finite float p, trunc(RN(p + copysign(0.5 - 2^-25, p))) equals
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void quantize_q8_1_tiled_kernel(
     const float4* __restrict__ x, uint32_t* __restrict__ qs, uint32_t* __restrict__ ds,
     float* __restrict__ da_plane, uint16_t* __restrict__ pieces, uint32_t M, uint32_t K,
     uint32_t nsb) {
-  __shared__ __align__(16) float sDa[8][kTileRows];      // [block of the super-block][row]
+  __shared__ __align__(16) float2 sDa[8][kTileRows];     // [block of the super-block][row]
   __shared__ __align__(16) uint16_t sPc[3][kTileRows][8];  // [piece][row][block]
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -197,21 +200,21 @@ __global__ __launch_bounds__(64 * kTileWaves) void quantize_q8_1_tiled_kernel(
   uint16_t pc[3];
   bf16_split3((float)dh * (float)sum, pc[0], pc[1], pc[2]);
   const int j = c & 3;
-  if (j == 0) sDa[b][rl] = (float)dh;
+  if (j == 0) sDa[b][rl] = make_float2((float)dh, -kBiasF * (float)dh);
   if (j < 3) sPc[j][rl][b] = j == 0 ? pc[0] : (j == 1 ? pc[1] : pc[2]);
   __syncthreads();
   const int t = threadIdx.x;
-  constexpr int kDaThreads = 2 * kTileRows;  // 8 blocks x kTileRows/4 float4 each
+  constexpr int kDaThreads = 4 * kTileRows;  // 8 blocks x kTileRows/2 row pairs
   if (t < kDaThreads) {
-    const int bb = t / (kTileRows / 4), cc = t % (kTileRows / 4);
-    const uint32_t r = r0 + 4 * cc;
-    float* dst = da_plane + (8 * s + bb) * M + r;
-    if ((M & 3) == 0 && r + 3 < M) {  // 16-byte aligned: the plane starts on 256 bytes
-      *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(&sDa[bb][4 * cc]);
+    const int bb = t / (kTileRows / 2), cc = t % (kTileRows / 2);
+    const uint32_t r = r0 + 2 * cc;
+    float2* dst = reinterpret_cast<float2*>(da_plane) + (8 * s + bb) * M + r;
+    if ((M & 1) == 0 && r + 1 < M) {  // 16-byte aligned: the plane starts on 256 bytes
+      *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(&sDa[bb][2 * cc]);
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (r + e < M) dst[e] = sDa[bb][4 * cc + e];
+      for (int e = 0; e < 2; ++e)
+        if (r + e < M) dst[e] = sDa[bb][2 * cc + e];
     }
   } else if (t < kDaThreads + 3 * kTileRows) {  // piece pp of row rr of the tile
     const int pp = (t - kDaThreads) / kTileRows, rr = (t - kDaThreads) % kTileRows;

@@ -25,8 +25,9 @@ def test_exports_every_declared_symbol():
 
 
 def test_sizes():
-    # q, words, pad to 256, da plane, pad to 256, 48 bytes of pieces per (row, super-block)
-    assert mmq.mmq_q8_1_bytes(2048, 4096) == (2048 * 4096 * 9 // 8 + 4 * 2048 * 128
+    # q, words, pad to 256, (da, nda) plane, pad to 256, 48 bytes of pieces per (row,
+    # super-block)
+    assert mmq.mmq_q8_1_bytes(2048, 4096) == (2048 * 4096 * 9 // 8 + 8 * 2048 * 128
                                               + 48 * 2048 * 16)
     assert mmq.mmq_q8_1_bytes(1, 32) == 256 + 256 + 48
     assert mmq.mmq_q8_1_bytes(3, 96) == 512 + 256 + 48 * 3
@@ -55,11 +56,11 @@ def test_size_null_out():
     assert mmq.raw_call("mmq_q8_1_bytes", 1, 32, None) == mmq.MMQ_E_ARG
 
 
-# two stages of: token tile [BM][272], da [8][BM] f32, token pieces [3][BM][8] bf16, and per
-# wavefront dsv [8][32] f32 + dmv pieces [3][32][8] bf16
+# two stages of: token tile [BM][272], (da, nda) [8][BM][2] f32, token pieces [3][BM][8]
+# bf16, and per wavefront dsv [8][32] f32 + dmv pieces [3][32][8] bf16
 LARGE, SMALL = mmq.MMQ_TILE_LARGE, mmq.MMQ_TILE_SMALL
-LARGE_LDS = 2 * (128 * 272 + 128 * 32 + 128 * 48 + 8 * 2560)
-SMALL_LDS = 2 * (32 * 272 + 32 * 32 + 32 * 48 + 2 * 2560)
+LARGE_LDS = 2 * (128 * 272 + 128 * 64 + 128 * 48 + 8 * 2560)
+SMALL_LDS = 2 * (32 * 272 + 32 * 64 + 32 * 48 + 2 * 2560)
 
 
 def test_plan_large_when_it_fits():

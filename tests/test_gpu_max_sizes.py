@@ -143,15 +143,16 @@ def test_dequantize_past_2_32_weights():
 
 def q8_rows(image, M: int, K: int, rows):
     """The parts of a q8_1 byte image (uint8, device tensor or numpy) that belong to `rows`:
-    int8 values, scale words, da-plane entries and bf16 pieces, as numpy arrays."""
+    int8 values, scale words, (da, -1.5*2^23*da) plane entries and bf16 pieces, as numpy
+    arrays."""
     def host(a):
         return a.cpu().numpy() if hasattr(a, "cpu") else np.asarray(a)
     nb, nsb = K // 32, -(-K // 256)
     P = -(-(M * K + 4 * M * nb) // 256) * 256
-    Q = -(-(P + 4 * M * nb) // 256) * 256
+    Q = -(-(P + 8 * M * nb) // 256) * 256
     qs = np.stack([host(image[r * K:(r + 1) * K]) for r in rows])
     words = np.stack([host(image[M * K + 4 * nb * r:M * K + 4 * nb * (r + 1)]) for r in rows])
-    plane = np.stack([host(image[P + 4 * (b * M + r):P + 4 * (b * M + r) + 4])
+    plane = np.stack([host(image[P + 8 * (b * M + r):P + 8 * (b * M + r) + 8])
                       for b in range(nb) for r in rows])
     pieces = np.stack([host(image[Q + 16 * (i * M + r):Q + 16 * (i * M + r) + 16])
                        for i in range(3 * nsb) for r in rows])
@@ -182,5 +183,5 @@ def test_quantize_largest(K):
     got = q8_rows(q8, M, K, rows)
     want_image = oracle.q8_1_image(oracle.quantize_q8_1(block[[r % R for r in rows]]))
     want = q8_rows(want_image, len(rows), K, range(len(rows)))
-    for name, g, w in zip(("qs", "words", "da plane", "pieces"), got, want):
+    for name, g, w in zip(("qs", "words", "(da, nda) plane", "pieces"), got, want):
         assert np.array_equal(g, w), f"{name}: {np.count_nonzero(g != w)} bytes differ"

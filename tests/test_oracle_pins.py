@@ -187,8 +187,8 @@ def test_q8_1_image_layout():
     assert np.array_equal(img[:192].view(np.int8).reshape(3, 64), q.qs)
     words = img[192:216].view("<u4").reshape(3, 2)
     assert np.all(img[216:256] == 0)
-    da_plane = img[256:280].view("<f4").reshape(2, 3)          # [block][row]
-    assert np.all(img[280:512] == 0)
+    pairs = img[256:304].view("<f4").reshape(2, 3, 2)          # [block][row][da, -1.5*2^23*da]
+    assert np.all(img[304:512] == 0)
     pieces = _bf16_value(img[512:].view("<u2")).reshape(1, 3, 3, 8)   # [sb][piece][row][e]
     assert np.all(pieces[..., 2:] == 0)                        # blocks past K/32
     for i in range(3):
@@ -199,7 +199,8 @@ def test_q8_1_image_layout():
             sa = hi - 65536 if hi >= 32768 else hi
             assert sa == int(q.sa[i, b])
             da = Fraction(float(np.uint16(w & 0xFFFF).view(np.float16)))
-            assert Fraction(float(da_plane[b, i])) == da
+            assert Fraction(float(pairs[b, i, 0])) == da
+            assert Fraction(float(pairs[b, i, 1])) == -Fraction(3 * 2 ** 22) * da
             assert sum(Fraction(float(pieces[0, k, i, b])) for k in range(3)) == da * sa
 
 
