@@ -41,6 +41,8 @@ sys.path.insert(0, ROOT)
 INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, tera-ops/s (1 MAC = 2 ops)
 F16_PEAK_TFLOPS = 2500.0         # MI355X dense f16 MFMA
 HBM_PEAK_GBS = 8000.0
+FP32_VECTOR_TFLOPS = 157.3       # MI355X FP32 vector rate (no packed FP32: one FMA per lane)
+RESCALE_FMA_PER_EB = 2           # the rescale's FMAs per element-block (32-block of one C value)
 PAGES_QPROJ_TMACS = 15.19        # the pages' best q-proj MMQ kernel: 34.36 GMAC in 2.262 ms
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmq_qproj_traffic.json")
 KERNEL_SOURCES = ["q4_q8_int8_amd/csrc/mmq_gemm.hip", "q4_q8_int8_amd/csrc/mmq_device.h",
@@ -65,6 +67,19 @@ def measured_traffic():
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def epilogue_ceiling(M: int, N: int, K: int, gemm_us: float) -> dict:
+    """The rescale's floor: RESCALE_FMA_PER_EB FP32 FMAs per element-block (M*N*K/32 of
+    them) at the FP32 vector peak, the GEMM rate that floor allows as a fraction of the int8
+    matrix peak, and the measured GEMM's fraction of that floor."""
+    fmas = RESCALE_FMA_PER_EB * M * N * (K // 32)
+    floor_us = fmas * 2 / (FP32_VECTOR_TFLOPS * 1e12) * 1e6
+    ceiling_tops = 2 * M * N * K / (floor_us * 1e-6) / 1e12
+    return {"fma_per_element_block": RESCALE_FMA_PER_EB, "valu_peak_tflops": FP32_VECTOR_TFLOPS,
+            "floor_us": round(floor_us, 2),
+            "ceiling_frac_of_int8_peak": round(ceiling_tops / INT8_PEAK_TOPS, 4),
+            "gemm_frac_of_ceiling": round(floor_us / gemm_us, 4)}
 
 
 def quant_bytes(M: int, K: int) -> int:
@@ -515,6 +530,9 @@ def main() -> int:
                      "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                      "frac": round(achieved_tops / INT8_PEAK_TOPS, 4),
                      "traffic": measured_traffic()},
+        # The GEMM's vector-ALU rescale alone, at the FP32 vector peak, bounds the GEMM
+        # below the int8 matrix peak: the ceiling it implies and how close the GEMM gets.
+        "epilogue_ceiling": epilogue_ceiling(M, N, K, gemm_s * 1e6),
         "us_per_gmac": round(ms_per_step * 1e3 / (macs / 1e9), 4),
         "step_gpu_us": round(t["step_gpu_us"], 2),
         "graph_step_us": round(t["graph_step_us"], 2),
