@@ -165,8 +165,13 @@ __global__ __launch_bounds__(64 * kTileWaves) void quantize_q8_1_tiled_kernel(
   const bool ok = row < M;
   const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
   const uint32_t seg = 64 * s + lane;  // 16-byte word of chunk l within a row
-  const float4 uA = rowA < M ? x[rowA * (K / 4) + seg] : zero;
-  const float4 uB = rowB < M ? x[rowB * (K / 4) + seg] : zero;
+  // Rows past M load row M-1 (in bounds) and are zeroed after: a load under a condition
+  // would be split into four 4-byte loads, each behind its own branch.
+  const uint32_t rA = rowA < M ? rowA : M - 1, rB = rowB < M ? rowB : M - 1;
+  float4 uA = x[rA * (K / 4) + seg];
+  float4 uB = x[rB * (K / 4) + seg];
+  if (rowA >= M) uA = zero;
+  if (rowB >= M) uB = zero;
   const float4 snd = lo ? uB : uA;
   const float4 u = lo ? uA : uB;
   float4 v;
