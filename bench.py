@@ -404,6 +404,8 @@ def sweep(args) -> int:
         tiles = [mmq.MMQ_TILE_LARGE, mmq.MMQ_TILE_SMALL]
         if W["M"] <= 512:
             tiles.append(mmq.MMQ_TILE_SKINNY)
+        if W["M"] <= mmq.GEMV_MAX_M:
+            tiles.append(mmq.MMQ_TILE_GEMV)
         for tile in tiles:
             t = measure(W, args.rotate, args.steps, args.warmup, tile)
             times[(name, tile)] = t

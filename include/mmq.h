@@ -50,14 +50,19 @@ enum mmq_status {
 #define MMQ_REP_TILE_ROWS 32     /* weight rows per repacked tile */
 #define MMQ_REP_TILE_BYTES 6656  /* bytes per (repacked tile, super-block) */
 
-/* Tile variants of the GEMM: one template in two instantiations (large, small), and a
- * skinny kernel for few tokens that splits K over the wavefronts of a workgroup. */
+/* Tile variants of the GEMM: one template in two instantiations (large, small), a skinny
+ * kernel for few tokens that splits K over the wavefronts of a workgroup, and a vector-ALU
+ * kernel for a handful of tokens (decode). */
 enum mmq_tile {
   MMQ_TILE_AUTO = 0,   /* let the guard choose */
   MMQ_TILE_LARGE = 1,  /* 128 tokens x 256 output features per workgroup, 8 wavefronts */
   MMQ_TILE_SMALL = 2,  /* 32 tokens x 64 output features per workgroup, 2 wavefronts */
-  MMQ_TILE_SKINNY = 3  /* 32 tokens x 32 output features per workgroup, K split over 8
+  MMQ_TILE_SKINNY = 3, /* 32 tokens x 32 output features per workgroup, K split over 8
                           wavefronts and summed in wavefront order (no block-dot output) */
+  MMQ_TILE_GEMV = 4    /* M <= 16 only: up to 4 tokens x 16 output features per workgroup of
+                          4 wavefronts, integer dot products on the vector ALU (v_dot4_i32_i8),
+                          K split over 16 slices and summed in slice order (no block-dot
+                          output) */
 };
 
 /* Why the guard chose what it chose. */
@@ -68,14 +73,17 @@ enum mmq_reason {
   MMQ_REASON_LDS_FALLBACK = 3,  /* the large tile does not fit the LDS budget: small tile */
   MMQ_REASON_FORCED = 4,        /* the caller's options asked for this tile */
   MMQ_REASON_NO_FIT = 5,        /* nothing fits the budget: refused with MMQ_E_LDS */
-  MMQ_REASON_FEW_TOKENS = 6,    /* M <= 128 and the large grid would leave compute units idle:
+  MMQ_REASON_FEW_TOKENS = 6,    /* 8 < M <= 128 and the large grid would leave compute units idle:
                                    the skinny kernel, which splits K over wavefronts */
-  MMQ_REASON_FUSED = 7          /* mmq_q4K_f32: the skinny kernel quantizing its own activations */
+  MMQ_REASON_FUSED = 7,         /* mmq_q4K_f32: the skinny kernel quantizing its own activations */
+  MMQ_REASON_DECODE = 8         /* M <= 8: the vector-ALU kernel, which streams the weights once
+                                   without the MFMA tiles' 32-token padding */
 };
 
 /* Optional knobs for the _ex entry points (NULL = defaults). */
 typedef struct mmq_options {
-  int32_t force_tile;   /* enum mmq_tile. A forced tile that does not fit is refused (MMQ_E_LDS) */
+  int32_t force_tile;   /* enum mmq_tile. A forced tile that does not fit is refused (MMQ_E_LDS);
+                           MMQ_TILE_GEMV with M > 16 is refused with MMQ_E_SHAPE */
   int32_t min_workgroups; /* > 0: choose the large tile only when its grid has at least this many
                              workgroups; 0: the device's compute-unit count (256 in mmq_plan) */
   int64_t lds_budget;   /* > 0: check tiles against this many bytes of LDS instead of the
@@ -216,7 +224,8 @@ int mmq_q4K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, cons
 /*
  * mmq_plan: the LDS-budget guard as a pure host function (no device access). Chooses the
  * tile for an M x N x K product given `lds_budget` bytes per workgroup (opt->lds_budget,
- * when set, takes precedence): the large tile when it fits and its grid has at least
+ * when set, takes precedence): for M <= 8 the vector-ALU kernel (MMQ_TILE_GEMV, reason
+ * MMQ_REASON_DECODE); else the large tile when it fits and its grid has at least
  * opt->min_workgroups workgroups (default 256, the MI355X compute-unit count; a GEMM call
  * uses the device's count); else, for M <= 128, the skinny kernel; else the small tile (more,
  * smaller workgroups: at M = 512, N = 4096 the large tile has 64 workgroups for 256 compute

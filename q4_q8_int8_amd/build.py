@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmmq.so")
 
-SOURCES = ["quantize.hip", "repack.hip", "mmq_gemm.hip", "mmq_skinny.hip", "f16_path.hip",
+SOURCES = ["quantize.hip", "repack.hip", "mmq_gemm.hip", "mmq_skinny.hip", "mmq_gemv.hip",
+           "f16_path.hip",
            "f16_gemm.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -113,7 +113,7 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 
 int check_options(const mmq_options* opt) {
   if (!opt) return MMQ_OK;
-  if (opt->force_tile < MMQ_TILE_AUTO || opt->force_tile > MMQ_TILE_SKINNY)
+  if (opt->force_tile < MMQ_TILE_AUTO || opt->force_tile > MMQ_TILE_GEMV)
     return fail(MMQ_E_ARG, "force_tile %d is not an mmq_tile", opt->force_tile);
   if (opt->lds_budget < 0) return fail(MMQ_E_ARG, "negative lds_budget");
   if (opt->min_workgroups < 0) return fail(MMQ_E_ARG, "negative min_workgroups");
@@ -143,6 +143,13 @@ int plan(int64_t M, int64_t N, const mmq_options* opt, int64_t budget, int64_t c
     if (need_small <= budget) { tile = MMQ_TILE_SMALL; reason = MMQ_REASON_FORCED; }
   } else if (forced == MMQ_TILE_SKINNY) {
     if (mmq::skinny_lds_bytes() <= budget) { tile = MMQ_TILE_SKINNY; reason = MMQ_REASON_FORCED; }
+  } else if (forced == MMQ_TILE_GEMV) {
+    if (M > mmq::kGemvMaxM)
+      return fail(MMQ_E_SHAPE, "the vector-ALU tile takes M <= %d (M = %lld)", mmq::kGemvMaxM,
+                  (long long)M);
+    if (mmq::gemv_lds_bytes(M) <= budget) { tile = MMQ_TILE_GEMV; reason = MMQ_REASON_FORCED; }
+  } else if (M <= mmq::kGemvAutoMaxM && mmq::gemv_lds_bytes(M) <= budget) {
+    tile = MMQ_TILE_GEMV; reason = MMQ_REASON_DECODE;
   } else if (need_large <= budget) {
     if (grid_of(mmq::kLarge) >= min_wg) {
       tile = MMQ_TILE_LARGE; reason = MMQ_REASON_LARGE;
@@ -162,6 +169,14 @@ int plan(int64_t M, int64_t N, const mmq_options* opt, int64_t budget, int64_t c
   info->tile = tile;
   info->reason = reason;
   info->fallback = fallback;
+  if (tile == MMQ_TILE_GEMV) {
+    info->block_m = (int32_t)mmq::gemv_group(M);
+    info->block_n = mmq::kGemvRows;
+    info->threads = 64 * mmq::kGemvWaves;
+    info->lds_bytes = mmq::gemv_lds_bytes(M);
+    info->grid = mmq::gemv_grid(M, N);
+    return MMQ_OK;
+  }
   if (tile == MMQ_TILE_SKINNY) {
     info->block_m = 32;
     info->block_n = 32;
@@ -278,7 +293,9 @@ int mmq_q4K_q8_1_ex(int64_t M, int64_t N, int64_t K, const void* q8, const void*
   g_last = info;
   if (st) return st;
   hipError_t e;
-  if (info.tile == MMQ_TILE_SKINNY) {
+  if (info.tile == MMQ_TILE_GEMV) {
+    e = mmq::launch_mmq_gemv(q8, w_rep, C, M, N, K, static_cast<hipStream_t>(stream));
+  } else if (info.tile == MMQ_TILE_SKINNY) {
     e = mmq::launch_mmq_skinny(q8, w_rep, C, M, N, K, static_cast<hipStream_t>(stream));
   } else {
     const mmq::TileShape ts = info.tile == MMQ_TILE_LARGE ? mmq::kLarge : mmq::kSmall;
@@ -343,13 +360,15 @@ int mmq_q4K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, cons
     return fail(MMQ_E_SHAPE, "window [%lld,%lld) x [%lld,%lld) is empty or outside %lld x %lld",
                 (long long)i0, (long long)i1, (long long)j0, (long long)j1, (long long)M,
                 (long long)N);
-  if (opt && opt->force_tile == MMQ_TILE_SKINNY)
-    return fail(MMQ_E_ARG, "the skinny tile has no block-dot output; force large or small");
+  if (opt && (opt->force_tile == MMQ_TILE_SKINNY || opt->force_tile == MMQ_TILE_GEMV))
+    return fail(MMQ_E_ARG, "the skinny and vector-ALU tiles have no block-dot output; force "
+                           "large or small");
   DeviceInfo* di;
   if ((st = current_device(&di))) return st;
   mmq_kernel_info info;
   st = plan(M, N, opt, di->lds_budget, di->compute_units, &info);
-  if (!st && info.tile == MMQ_TILE_SKINNY) {  // the block dots come from the small tile
+  if (!st && (info.tile == MMQ_TILE_SKINNY || info.tile == MMQ_TILE_GEMV)) {
+    // the block dots come from the small tile
     mmq_options o = opt ? *opt : mmq_options{};
     o.force_tile = MMQ_TILE_SMALL;
     st = plan(M, N, &o, di->lds_budget, di->compute_units, &info);

@@ -1,0 +1,241 @@
+// q4_K x q8_1 product for a handful of tokens (decode), on the vector ALU.
+//
+// The arithmetic is the GEMM's: for token m, weight row n and 32-block b,
+//   S = sum over the block of nibble * q  (exact integer),
+//   C[m][n] += da * (dsv * S + dmv * sa)
+// which is term1 (da * dsv * S) plus term2 (dmv times the row factor da * sa) of the r15 page
+// ("f32-accumulate mma probe + rank-1 term2 rescale", section 2.1), with dsv = d*sc and
+// dmv = -dmin*m expanded by the repack.
+//
+// With one to sixteen tokens the product streams the weights once and does little else, so
+// matrix instructions buy nothing: the MFMA tiles of the other kernels are 32 tokens wide and
+// would be mostly padding. Here a workgroup of four wavefronts owns 16 weight rows (half of a
+// repacked 32-row tile), all of K and a group of at most MT tokens. Its 256 lanes are 16 rows
+// x 16 K-slices (lane l of wavefront w: row l % 16, slice 4w + l / 16), and slice ks takes
+// the super-blocks ks, ks + 16, ks + 32, ...; so at K = 4096 every lane owns one super-block
+// and the grid has N/16 workgroups (256 at N = 4096) per token group. Token groups are
+// separate workgroups, so that more tokens bring more workgroups rather than longer
+// wavefronts; the groups of one row block read the same weights, mostly from L2.
+//
+// Per super-block a lane loads its row's 128 nibble bytes, its 8 scales dsv and the three
+// bf16 pieces of its 8 mins dmv (16- and 4-byte buffer loads; the 16 lanes of a slice read
+// 256 contiguous bytes); in the same burst the lanes of a wavefront load the token bytes of
+// its four slices' super-blocks and their (da, sa) words and put them in the wavefront's own
+// LDS region, which each slice's lanes then read at one address (broadcast). All loads of a
+// step are in flight together: read instead one token at a time with scalar loads, each
+// waited for before its dot products, they cost an L2 round trip per token and pair of
+// blocks. Per block, S is eight v_dot4_i32_i8 over 4 bytes each (both operands signed;
+// nibbles are 0..15), then
+//   u = fma(dmv, float(sa), float(S) * dsv),  acc = fma(u, da, acc).
+//
+// Summation order per output: blocks in order within a super-block, super-blocks in order
+// within a slice, then the 16 slices' partial sums in slice order through LDS. Deterministic;
+// not the GEMM's association (the two agree within the f32 tolerance).
+#include "mmq_device.h"
+
+namespace mmq {
+namespace {
+
+constexpr int kGemvSlices = 64 / kGemvRows;        // K-slices per wavefront
+constexpr int kGemvKS = kGemvSlices * kGemvWaves;  // K-slices per workgroup
+
+template <int MT>
+__global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
+    const int8_t* __restrict__ qs, const uint32_t* __restrict__ words,
+    const float* __restrict__ da_plane, const uint8_t* __restrict__ wrep, float* __restrict__ C,
+    int M, int N, int K, int groups) {
+  // per wavefront and slice: token bytes [MT][256], then (da, float(sa)) [MT][8]; 16 bytes of
+  // padding per slice put the four slices' broadcast reads in different banks. After the
+  // loop the same memory holds the partial sums [kGemvKS][MT][kGemvRows].
+  constexpr int kTokBytes = MT * 256;
+  constexpr int kSlice = kTokBytes + MT * 64 + 16;
+  constexpr int kRegion = kGemvSlices * kSlice;
+  static_assert(kGemvWaves * kRegion >= kGemvKS * MT * kGemvRows * 4, "partial sums fit");
+  __shared__ __align__(16) uint8_t smem[kGemvWaves * kRegion];
+  const int rb = (int)(blockIdx.x / (unsigned)groups);        // row block: rows 16rb..16rb+15
+  const int m0 = (int)(blockIdx.x % (unsigned)groups) * MT;  // first token of the group
+  const int mc = M - m0 < MT ? M - m0 : MT;                    // tokens in the group
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int jj = lane % kGemvRows;
+  const int q = lane / kGemvRows;                              // slice within the wavefront
+  const int ks = wave * kGemvSlices + q;
+  const int j = (rb & 1) * kGemvRows + jj;                     // row within the 32-row tile
+  const int nsb = K >> 8, kb = K >> 5;
+  // steps of this wavefront: its first slice has the most super-blocks
+  const int steps = (nsb - wave * kGemvSlices + kGemvKS - 1) / kGemvKS;
+  uint8_t* region = smem + wave * kRegion;
+
+  const uint8_t* wtile = wrep + (size_t)(rb >> 1) * (size_t)nsb * kRepTileBytes;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wtile, (uint32_t)nsb * (uint32_t)kRepTileBytes);
+
+  float acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+
+  for (int i = 0; i < steps; ++i) {
+    const int s = ks + i * kGemvKS;            // this lane's super-block
+    const bool act = s < nsb;                  // the last step may leave slices idle
+    // weights; an idle slice's offsets are past the tile and read zero
+    const uint32_t rec = (uint32_t)s * kRepTileBytes;
+    v4i nib[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      nib[t] = buf_load16(rw, rec + (t >> 1) * 1024 + (t & 1) * 512 + j * 16);
+    float dsv[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) dsv[b] = buf_load_f32(rw, rec + kRepNibBytes + b * 128 + j * 4);
+    v4i pc[3];
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      pc[p] = buf_load16(rw, rec + kRepNibBytes + kRepDsvBytes + p * 512 + j * 16);
+    // token data of the wavefront's four slices: chunk c = (slice * MT + m) * 16 + part, MT
+    // chunks per lane; (da, sa) of block b of token m of a slice: c = (slice * MT + m) * 8 + b
+    v4i tok[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int c = lane + 64 * t;
+      const int cq = c / (16 * MT), cm = (c / 16) % MT, part = c % 16;
+      const int cs = wave * kGemvSlices + cq + i * kGemvKS;
+      tok[t] = v4i{0, 0, 0, 0};
+      if (cm < mc && cs < nsb)
+        tok[t] = *reinterpret_cast<const v4i*>(qs + (size_t)(m0 + cm) * K + (size_t)cs * 256 +
+                                               part * 16);
+    }
+    constexpr int kSc = kGemvSlices * MT * 8;
+    constexpr int kScPerLane = (kSc + 63) / 64;
+    float2 scv[kScPerLane];
+#pragma unroll
+    for (int t = 0; t < kScPerLane; ++t) {
+      const int c = lane + 64 * t;
+      const int cq = c / (8 * MT), cm = (c / 8) % MT, b = c % 8;
+      const int cs = wave * kGemvSlices + cq + i * kGemvKS;
+      scv[t] = make_float2(0.0f, 0.0f);
+      if (c < kSc && cm < mc && cs < nsb) {
+        const uint32_t w = words[(size_t)(m0 + cm) * kb + (size_t)cs * 8 + b];
+        scv[t] = make_float2(da_plane[((size_t)(cs * 8 + b) * M + m0 + cm) * 2],
+                             (float)((int)w >> 16));
+      }
+    }
+    // the region's reads of the previous step are done before it is overwritten
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int c = lane + 64 * t;
+      *reinterpret_cast<v4i*>(region + (c / (16 * MT)) * kSlice + (c % (16 * MT)) * 16) = tok[t];
+    }
+#pragma unroll
+    for (int t = 0; t < kScPerLane; ++t) {
+      const int c = lane + 64 * t;
+      if (c < kSc)
+        *reinterpret_cast<float2*>(region + (c / (8 * MT)) * kSlice + kTokBytes +
+                                   (c % (8 * MT)) * 8) = scv[t];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (act) {
+      const uint8_t* sl = region + q * kSlice;
+      // dmv = p0 + p1 + p2, exact in f32
+      float dmv[8];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        float p[3];
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+          const uint32_t w = (uint32_t)pc[t][b >> 1];
+          p[t] = __builtin_bit_cast(float, (b & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        }
+        dmv[b] = (p[0] + p[1]) + p[2];
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        int lo[8], hi[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const uint32_t w = (uint32_t)nib[2 * g + (d >> 2)][d & 3];
+          lo[d] = (int)(w & 0x0F0F0F0Fu);
+          hi[d] = (int)((w >> 4) & 0x0F0F0F0Fu);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m < mc) {
+            // blocks 2g and 2g+1 of token m0 + m (64 bytes) and their (da, float(sa)) pairs
+            const v4i* tq = reinterpret_cast<const v4i*>(sl + m * 256 + g * 64);
+            const float4 sc =
+                *reinterpret_cast<const float4*>(sl + kTokBytes + (m * 8 + 2 * g) * 8);
+            int S0 = 0, S1 = 0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const v4i a = tq[h], c = tq[2 + h];
+#pragma unroll
+              for (int d = 0; d < 4; ++d) {
+                S0 = __builtin_amdgcn_sdot4(lo[4 * h + d], a[d], S0, false);
+                S1 = __builtin_amdgcn_sdot4(hi[4 * h + d], c[d], S1, false);
+              }
+            }
+            const float u0 = __builtin_fmaf(dmv[2 * g], sc.y, (float)S0 * dsv[2 * g]);
+            acc[m] = __builtin_fmaf(u0, sc.x, acc[m]);
+            const float u1 = __builtin_fmaf(dmv[2 * g + 1], sc.w, (float)S1 * dsv[2 * g + 1]);
+            acc[m] = __builtin_fmaf(u1, sc.z, acc[m]);
+          }
+        }
+      }
+    }
+  }
+
+  __syncthreads();  // every wavefront is done with its region
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) red[(ks * MT + m) * kGemvRows + jj] = acc[m];
+  __syncthreads();
+  for (int e = threadIdx.x; e < MT * kGemvRows; e += kGemvWaves * 64) {
+    const int m = e / kGemvRows, r = e % kGemvRows;
+    const int n = rb * kGemvRows + r;
+    if (m < mc && n < N) {
+      float v = 0.0f;
+#pragma unroll
+      for (int k2 = 0; k2 < kGemvKS; ++k2) v += red[(k2 * MT + m) * kGemvRows + r];
+      C[(size_t)(m0 + m) * N + n] = v;
+    }
+  }
+}
+
+template <int MT>
+hipError_t launch_mt(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N, int64_t K,
+                     hipStream_t s) {
+  const uint8_t* base = static_cast<const uint8_t*>(q8);
+  const int64_t groups = (M + MT - 1) / MT;
+  hipLaunchKernelGGL((mmq_gemv_kernel<MT>), dim3((unsigned)gemv_grid(M, N)),
+                     dim3(kGemvWaves * 64), 0, s, reinterpret_cast<const int8_t*>(base),
+                     reinterpret_cast<const uint32_t*>(base + M * K),
+                     reinterpret_cast<const float*>(base + q8_planes_offset(M, K)),
+                     static_cast<const uint8_t*>(w_rep), C, (int)M, (int)N, (int)K, (int)groups);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// tokens per workgroup for M tokens: M itself up to 4, else groups of 4
+int64_t gemv_group(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : 4); }
+
+int64_t gemv_lds_bytes(int64_t M) {
+  const int64_t mt = gemv_group(M);
+  return (int64_t)kGemvWaves * kGemvSlices * (mt * 320 + 16);
+}
+
+int64_t gemv_grid(int64_t M, int64_t N) {
+  return (N + kGemvRows - 1) / kGemvRows * ((M + gemv_group(M) - 1) / gemv_group(M));
+}
+
+hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
+                           int64_t K, hipStream_t s) {
+  if (M < 1 || M > kGemvMaxM) return hipErrorInvalidValue;
+  switch (gemv_group(M)) {
+    case 1: return launch_mt<1>(q8, w_rep, C, M, N, K, s);
+    case 2: return launch_mt<2>(q8, w_rep, C, M, N, K, s);
+    default: return launch_mt<4>(q8, w_rep, C, M, N, K, s);
+  }
+}
+
+}  // namespace mmq

@@ -90,6 +90,20 @@ int64_t fused_lds_bytes();
 hipError_t launch_mmq_fused(const float* x, const void* w_rep, float* C, int64_t M, int64_t N,
                             int64_t K, hipStream_t s);
 
+// Vector-ALU product for a handful of tokens (decode): 16 weight rows and up to 4 tokens per
+// workgroup of kGemvWaves wavefronts, K split over 16 slices, M <= kGemvMaxM.
+constexpr int kGemvWaves = 4;
+constexpr int kGemvRows = 16;  // weight rows per workgroup
+constexpr int kGemvMaxM = 16;
+// The guard's choice up to here: from 16 tokens (four token groups, each re-reading the
+// weights) the skinny MFMA kernel is faster.
+constexpr int kGemvAutoMaxM = 8;
+int64_t gemv_group(int64_t M);  // tokens per workgroup
+int64_t gemv_lds_bytes(int64_t M);
+int64_t gemv_grid(int64_t M, int64_t N);
+hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
+                           int64_t K, hipStream_t s);
+
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, hipStream_t s);
 hipError_t launch_repack_q4_K(const void* w, int64_t N, int64_t K, void* w_rep, hipStream_t s);
 

@@ -84,12 +84,16 @@ def test_plan_lds_fallback_and_refusal():
 
 
 SKINNY = mmq.MMQ_TILE_SKINNY
+GEMV = mmq.MMQ_TILE_GEMV
 REASON = {LARGE: mmq.MMQ_REASON_LARGE, SMALL: mmq.MMQ_REASON_SMALL_GRID,
-          SKINNY: mmq.MMQ_REASON_FEW_TOKENS}
+          SKINNY: mmq.MMQ_REASON_FEW_TOKENS, GEMV: mmq.MMQ_REASON_DECODE}
 
 
 @pytest.mark.parametrize("M,N,tile", [
-    (1, 4096, SKINNY),      # large grid 1 x 16, few tokens
+    (1, 4096, GEMV),        # decode: the vector-ALU kernel
+    (8, 4096, GEMV),
+    (1, 65536, GEMV),       # whatever the large grid would be
+    (9, 4096, SKINNY),      # large grid 1 x 16, few tokens
     (16, 4096, SKINNY),
     (128, 4096, SKINNY),
     (129, 4096, SMALL),     # 2 x 16
@@ -132,6 +136,44 @@ def test_blockdots_refuse_the_skinny_tile():
                         ctypes.byref(opt)) == mmq.MMQ_E_ARG
 
 
+def test_blockdots_refuse_the_gemv_tile():
+    opt = mmq.mmq_options(mmq.MMQ_TILE_GEMV, 0, 0)
+    assert mmq.raw_call("mmq_q4K_q8_1_blockdots", 4, 8, 256, A, B, 0, 4, 0, 8, Cp, None,
+                        ctypes.byref(opt)) == mmq.MMQ_E_ARG
+
+
+@pytest.mark.parametrize("M,group,grid", [(1, 1, 256), (2, 2, 256), (3, 4, 256), (4, 4, 256),
+                                          (5, 4, 512), (16, 4, 1024)])
+def test_plan_gemv_tile(M, group, grid):
+    auto = mmq.mmq_plan(M, 4096, 4096, 160 * 1024)
+    assert (auto["tile"], auto["reason"]) == ((GEMV, mmq.MMQ_REASON_DECODE) if M <= 8 else
+                                              (SKINNY, mmq.MMQ_REASON_FEW_TOKENS))
+    p = mmq.mmq_plan(M, 4096, 4096, 160 * 1024, force_tile=GEMV)
+    assert p["tile"] == GEMV
+    assert p["block_m"] == group and p["block_n"] == 16 and p["threads"] == 256
+    # per wavefront and K-slice: 256 token bytes and 8 (da, sa) pairs per token, 16 padding
+    assert p["lds_bytes"] == 4 * 4 * (320 * group + 16) and p["grid"] == grid
+    # ragged N: 4097 rows make 257 blocks of 16
+    assert mmq.mmq_plan(M, 4097, 256, 160 * 1024, force_tile=GEMV)["grid"] == 257 * (grid // 256)
+
+
+def test_plan_gemv_forced_limits():
+    p = mmq.mmq_plan(16, 4096, 4096, 160 * 1024, force_tile=GEMV)
+    assert p["tile"] == GEMV and p["reason"] == mmq.MMQ_REASON_FORCED
+    with pytest.raises(mmq.MMQError) as e:
+        mmq.mmq_plan(17, 4096, 4096, 160 * 1024, force_tile=GEMV)
+    assert e.value.status == mmq.MMQ_E_SHAPE
+    with pytest.raises(mmq.MMQError) as e:
+        mmq.mmq_plan(16, 4096, 4096, 160 * 1024, force_tile=GEMV, opt_lds_budget=20735)
+    assert e.value.status == mmq.MMQ_E_LDS
+    # the vector-ALU tile needs the least LDS: under 6 KiB it is the only one that fits
+    p = mmq.mmq_plan(1, 4096, 4096, 160 * 1024, opt_lds_budget=5376)
+    assert p["tile"] == GEMV and p["lds_bytes"] == 5376
+    with pytest.raises(mmq.MMQError) as e:
+        mmq.mmq_plan(1, 4096, 4096, 160 * 1024, opt_lds_budget=5375)
+    assert e.value.status == mmq.MMQ_E_LDS
+
+
 def test_plan_forced_tiles():
     p = mmq.mmq_plan(16, 4096, 4096, 160 * 1024, force_tile=mmq.MMQ_TILE_LARGE)
     assert p["tile"] == mmq.MMQ_TILE_LARGE and p["reason"] == mmq.MMQ_REASON_FORCED
@@ -150,7 +192,9 @@ def test_plan_ragged_grid():
     p = mmq.mmq_plan(2047, 11008, 4096, 160 * 1024)
     assert p["grid"] == 16 * 43
     p = mmq.mmq_plan(1, 33, 256, 160 * 1024)
-    assert p["grid"] == 2 and p["tile"] == mmq.MMQ_TILE_SKINNY
+    assert p["grid"] == 3 and p["tile"] == GEMV       # 33 rows: three blocks of 16
+    p = mmq.mmq_plan(1, 33, 256, 160 * 1024, force_tile=mmq.MMQ_TILE_SKINNY)
+    assert p["grid"] == 2
     p = mmq.mmq_plan(1, 33, 256, 160 * 1024, force_tile=mmq.MMQ_TILE_SMALL)
     assert p["grid"] == 1
 

@@ -1,0 +1,123 @@
+"""The vector-ALU tile for a handful of tokens (MMQ_TILE_GEMV) against the CPU oracle.
+
+Bar: f32 outputs within 1e-5 * T per element (T from the oracle, float64), every element;
+results deterministic. The tile is the guard's choice for M <= 8 (so the token sweep's M = 1
+shape runs through it by default) and can be forced up to M = 16.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import (assert_within_tolerance, gpu_mmq, gpu_quantize, gpu_repack,
+                            oracle_q8, oracle_w, say, workload)
+
+pytestmark = pytest.mark.gpu
+
+mmq = pytest.importorskip("q4_q8_int8_amd")
+torch = pytest.importorskip("torch")
+
+GEMV = mmq.MMQ_TILE_GEMV
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "the gpu tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+def _check(M, N, K, seed, kind="normal_outliers", wkind="random_fields", force=GEMV):
+    x = synth.activations(kind, M, K, seed)
+    w, _ = synth.q4k_weights(wkind, N, K, seed + 1)
+    q8 = gpu_quantize(x)
+    rep = gpu_repack(w, N, K)
+    say("gemv", (M, N, K), "seed", seed)
+    C = gpu_mmq(M, N, K, q8, rep, force_tile=force)
+    info = mmq.mmq_last_kernel()
+    assert info["tile"] == GEMV
+    q = oracle.quantize_q8_1(x)
+    wo = oracle.decode_q4_K(w)
+    _, T = oracle.mmq_terms(q, wo)
+    r = assert_within_tolerance(C, oracle.mmq(q, wo), T)
+    say("max |err|/T", r)
+    return C, info
+
+
+@pytest.mark.parametrize("name", ["sweep_m1", "sweep_m16"])
+def test_gemv_decode_shapes_every_element(name):
+    """The token sweep's decode shapes: M = 1 by the guard's own choice, M = 16 forced."""
+    W = workload(name)
+    M, N, K = W["M"], W["N"], W["K"]
+    q8 = gpu_quantize(W["x"])
+    rep = gpu_repack(W["w"], N, K)
+    say("gemv", name, (M, N, K))
+    C = gpu_mmq(M, N, K, q8, rep, force_tile=0 if M <= 8 else GEMV)
+    info = mmq.mmq_last_kernel()
+    assert info["tile"] == GEMV
+    assert info["reason"] == (mmq.MMQ_REASON_DECODE if M <= 8 else mmq.MMQ_REASON_FORCED)
+    _, T = oracle.mmq_terms(oracle_q8(name), oracle_w(name))
+    r = assert_within_tolerance(C, oracle.mmq(oracle_q8(name), oracle_w(name)), T)
+    say("max |err|/T", r)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 7, 8, 9, 12, 13, 16])
+def test_gemv_every_token_count(M):
+    """Groups of 1, 2 and 4 tokens, and a ragged last group (M = 5, 7, 9, 13)."""
+    C, info = _check(M, 160, 1024, 100 + M)
+    assert info["block_m"] == (1 if M == 1 else (2 if M == 2 else 4))
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 1, 256),        # one row, one super-block (15 of 16 slices idle)
+    (3, 33, 256),       # three row blocks, the last with one real row
+    (2, 96, 512),       # the second half of a tile
+    (4, 4097, 256),     # 257 row blocks
+    (1, 64, 9472),      # 37 super-blocks: 2 or 3 per slice, the last step partly idle
+    (5, 70, 11008),     # 43 super-blocks over 16 slices, a ragged token group
+    (16, 200, 2816),    # 11 super-blocks: 5 slices idle, wavefront 3 without a step
+])
+def test_gemv_edge_shapes(M, N, K):
+    _check(M, N, K, M * 1000 + N + K)
+
+
+def test_gemv_extreme_values():
+    """Weights with the largest nibbles and scales, activations with outliers per block."""
+    _check(4, 96, 1024, 7, kind="normal_outliers", wkind="fit")
+    _check(3, 64, 768, 8, kind="normal_outliers", wkind="random_fields")
+
+
+def test_gemv_integer_case_exact():
+    """d = 1, sc = 1, dmin = 0, integer activations with a +-127 per block: C = x @ v^T."""
+    rng = np.random.default_rng(11)
+    M, N, K = 13, 96, 1024
+    x = rng.integers(-127, 128, (M, K)).astype(np.float32)
+    x.reshape(M, K // 32, 32)[:, :, 5] = rng.choice([-127.0, 127.0], (M, K // 32))
+    f = {"d_bits": np.full((N, K // 256), 0x3C00, np.uint16),
+         "dmin_bits": np.zeros((N, K // 256), np.uint16),
+         "sc": np.ones((N, K // 32), np.uint8),
+         "m": rng.integers(0, 64, (N, K // 32), dtype=np.uint8),
+         "v": rng.integers(0, 16, (N, K), dtype=np.uint8)}
+    w = synth.q4k_pack(f)
+    q8 = gpu_quantize(x)
+    rep = gpu_repack(w, N, K)
+    say("gemv integer case")
+    C = gpu_mmq(M, N, K, q8, rep, force_tile=GEMV)
+    want = x.astype(np.int64) @ f["v"].astype(np.int64).T
+    assert np.array_equal(C.astype(np.int64), want)
+
+
+def test_gemv_deterministic_and_agrees_with_skinny():
+    x = synth.activations("normal_outliers", 9, 2816, 21)
+    w, _ = synth.q4k_weights("fit", 70, 2816, 22)
+    q8 = gpu_quantize(x)
+    rep = gpu_repack(w, 70, 2816)
+    say("gemv deterministic")
+    a = gpu_mmq(9, 70, 2816, q8, rep, force_tile=GEMV)
+    b = gpu_mmq(9, 70, 2816, q8, rep, force_tile=GEMV)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    s = gpu_mmq(9, 70, 2816, q8, rep, force_tile=mmq.MMQ_TILE_SKINNY)
+    q = oracle.quantize_q8_1(x)
+    wo = oracle.decode_q4_K(w)
+    _, T = oracle.mmq_terms(q, wo)
+    assert_within_tolerance(a, s.astype(np.float64), 2 * T)
