@@ -75,7 +75,8 @@ enum mmq_reason {
   MMQ_REASON_NO_FIT = 5,        /* nothing fits the budget: refused with MMQ_E_LDS */
   MMQ_REASON_FEW_TOKENS = 6,    /* 8 < M <= 128 and the large grid would leave compute units idle:
                                    the skinny kernel, which splits K over wavefronts */
-  MMQ_REASON_FUSED = 7,         /* mmq_q4K_f32: the skinny kernel quantizing its own activations */
+  MMQ_REASON_FUSED = 7,         /* mmq_q4K_f32: the vector-ALU (M <= 8) or skinny kernel quantizing
+                                   its own activations */
   MMQ_REASON_DECODE = 8         /* M <= 8: the vector-ALU kernel, which streams the weights once
                                    without the MFMA tiles' 32-token padding */
 };
@@ -191,17 +192,18 @@ int mmq_q4K_q8_1_ex(int64_t M, int64_t N, int64_t K, const void* q8, const void*
 /*
  * mmq_q4K_f32: the product for few tokens straight from float32 activations x[M][K]
  * (row-major, leading dimension K), quantizing them inside the GEMM. C is bit for bit what
- * quantize_q8_1 followed by mmq_q4K_q8_1_ex with MMQ_TILE_SKINNY writes, but no q8 buffer
- * goes through memory and there is one launch instead of two. Each workgroup quantizes the
- * real token rows of its 32-token tile, one super-block at a time, into LDS (the
- * quantization of quantize_q8_1: the r15 page, section 2.1), then runs the skinny kernel's
- * arithmetic on it. All ceil(N/32) workgroups of a token tile repeat that quantization, so
- * the call is limited to few tokens: 1 <= M <= 128. It pays only for the fewest: at
- * K = N = 4096 it takes 7.8 us at M = 1 against 13.7 us for the two launched kernels, and
- * 8.5 against 10.2 us when both are replayed from a graph; the two kernels are faster from
- * M = 4 in a graph and from M = 8 when launched one by one.
+ * quantize_q8_1 followed by mmq_q4K_q8_1_ex writes with MMQ_TILE_GEMV (M <= 8) or
+ * MMQ_TILE_SKINNY (8 < M <= 128), but no q8 buffer goes through memory and there is one
+ * launch instead of two. Each workgroup quantizes, into LDS, the activations of the
+ * super-blocks it works on (the quantization of quantize_q8_1: the r15 page, section 2.1),
+ * then runs the unfused kernel's arithmetic on them. Every workgroup that needs a token's
+ * super-block repeats that quantization, so the call is limited to few tokens:
+ * 1 <= M <= 128. It pays for the fewest: at K = N = 4096, replayed from a graph over weights
+ * that do not stay in cache, one call takes 6.5 us at M = 1 and 7.9 us at M = 2, against
+ * 8.2 and 8.6 us for quantize_q8_1 followed by the vector-ALU tile; from M = 4 the two kernels
+ * are faster in a graph (9.7 against 10.8 us), and from M = 8 also when launched one by one.
  * w_rep from repack_q4_K (N x K); C overwritten as for mmq_q4K_q8_1; mmq_last_kernel reports
- * MMQ_TILE_SKINNY with reason MMQ_REASON_FUSED.
+ * the tile (MMQ_TILE_GEMV or MMQ_TILE_SKINNY) with reason MMQ_REASON_FUSED.
  * Errors: MMQ_E_ARG, MMQ_E_SHAPE (as mmq_q4K_q8_1, or M > 128), MMQ_E_LDS (the kernel's LDS
  * does not fit the device's per-workgroup limit), MMQ_E_DEVICE, MMQ_E_HIP.
  */

@@ -325,15 +325,27 @@ int mmq_q4K_f32(int64_t M, int64_t N, int64_t K, const float* x, const void* w_r
     return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
   DeviceInfo* di;
   if ((st = current_device(&di))) return st;
+  // up to kGemvAutoMaxM tokens the vector-ALU kernel, else the skinny one, each quantizing
+  // the activations itself
+  const bool gemv = M <= mmq::kGemvAutoMaxM;
   mmq_kernel_info info = {};
-  info.tile = MMQ_TILE_SKINNY;
   info.reason = MMQ_REASON_FUSED;
-  info.block_m = 32;
-  info.block_n = 32;
-  info.threads = 64 * mmq::kSkinnyWaves;
-  info.lds_bytes = mmq::fused_lds_bytes();
   info.lds_budget = di->lds_budget;
-  info.grid = ((M + 31) / 32) * ((N + 31) / 32);
+  if (gemv) {
+    info.tile = MMQ_TILE_GEMV;
+    info.block_m = (int32_t)mmq::gemv_group(M);
+    info.block_n = mmq::kGemvRows;
+    info.threads = 64 * mmq::kGemvWaves;
+    info.lds_bytes = mmq::gemv_lds_bytes(M);
+    info.grid = mmq::gemv_grid(M, N);
+  } else {
+    info.tile = MMQ_TILE_SKINNY;
+    info.block_m = 32;
+    info.block_n = 32;
+    info.threads = 64 * mmq::kSkinnyWaves;
+    info.lds_bytes = mmq::fused_lds_bytes();
+    info.grid = ((M + 31) / 32) * ((N + 31) / 32);
+  }
   if (info.lds_bytes > di->lds_budget) {
     info.tile = MMQ_TILE_AUTO;
     info.reason = MMQ_REASON_NO_FIT;
@@ -342,7 +354,9 @@ int mmq_q4K_f32(int64_t M, int64_t N, int64_t K, const float* x, const void* w_r
                 (long long)info.lds_bytes, (long long)di->lds_budget);
   }
   g_last = info;
-  hipError_t e = mmq::launch_mmq_fused(x, w_rep, C, M, N, K, static_cast<hipStream_t>(stream));
+  hipError_t e = gemv ? mmq::launch_mmq_gemv_fused(x, w_rep, C, M, N, K,
+                                                   static_cast<hipStream_t>(stream))
+                      : mmq::launch_mmq_fused(x, w_rep, C, M, N, K, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("mmq_q4K_f32 launch", e);
   return ok();
 }

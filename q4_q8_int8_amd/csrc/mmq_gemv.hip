@@ -31,7 +31,18 @@
 // Summation order per output: blocks in order within a super-block, super-blocks in order
 // within a slice, then the 16 slices' partial sums in slice order through LDS. Deterministic;
 // not the GEMM's association (the two agree within the f32 tolerance).
+//
+// The FUSED instantiation takes the f32 activations instead of the q8 buffer: each wavefront
+// loads the f32 values of its four slices' super-blocks (in the same burst as the weights)
+// and quantizes them into its LDS region, one pass per token for all four slices: lane l takes
+// 16 values of block (l % 16) / 2 of slice l / 16, and the two lanes of a block combine their
+// max and integer sum with one lane swap. The arithmetic per value and per block is the
+// prepass's (quant1, IEEE divisions, f16 rounding), and max and integer sum do not depend on
+// the order of their terms, so the region holds exactly the bytes and (da, sa) the unfused
+// kernel stages: C is bit for bit that of quantize_q8_1 followed by the unfused kernel, from
+// one launch.
 #include "mmq_device.h"
+#include "quant_device.h"
 
 namespace mmq {
 namespace {
@@ -39,11 +50,11 @@ namespace {
 constexpr int kGemvSlices = 64 / kGemvRows;        // K-slices per wavefront
 constexpr int kGemvKS = kGemvSlices * kGemvWaves;  // K-slices per workgroup
 
-template <int MT>
+template <int MT, bool FUSED>
 __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
     const int8_t* __restrict__ qs, const uint32_t* __restrict__ words,
-    const float* __restrict__ da_plane, const uint8_t* __restrict__ wrep, float* __restrict__ C,
-    int M, int N, int K, int groups) {
+    const float* __restrict__ da_plane, const float4* __restrict__ x,
+    const uint8_t* __restrict__ wrep, float* __restrict__ C, int M, int N, int K, int groups) {
   // per wavefront and slice: token bytes [MT][256], then (da, float(sa)) [MT][8]; 16 bytes of
   // padding per slice put the four slices' broadcast reads in different banks. After the
   // loop the same memory holds the partial sums [kGemvKS][MT][kGemvRows].
@@ -89,11 +100,30 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
 #pragma unroll
     for (int p = 0; p < 3; ++p)
       pc[p] = buf_load16(rw, rec + kRepNibBytes + kRepDsvBytes + p * 512 + j * 16);
-    // token data of the wavefront's four slices: chunk c = (slice * MT + m) * 16 + part, MT
-    // chunks per lane; (da, sa) of block b of token m of a slice: c = (slice * MT + m) * 8 + b
+    // fused: lane l's 16 values of token m0 + m: values 32 fb + 16 fh .. + 15 of the
+    // super-block of slice fq (fq = l / 16, fb = (l % 16) / 2, fh = l % 2); zero for an idle
+    // slice
+    const int fq = lane >> 4, fb = (lane & 15) >> 1, fh = lane & 1;
+    float4 xv[FUSED ? MT : 1][4];
+    if constexpr (FUSED) {
+      const int cs = wave * kGemvSlices + fq + i * kGemvKS;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const size_t base = ((size_t)(m0 + m) * K + (size_t)cs * 256 + fb * 32 + fh * 16) / 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[m][e] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          if (m < mc && cs < nsb) xv[m][e] = x[base + e];
+        }
+      }
+    }
+    // unfused: token data of the wavefront's four slices: chunk c = (slice * MT + m) * 16 +
+    // part, MT chunks per lane; (da, sa) of block b of token m of a slice: c = (slice * MT +
+    // m) * 8 + b
     v4i tok[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
+      if constexpr (FUSED) break;
       const int c = lane + 64 * t;
       const int cq = c / (16 * MT), cm = (c / 16) % MT, part = c % 16;
       const int cs = wave * kGemvSlices + cq + i * kGemvKS;
@@ -107,6 +137,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
     float2 scv[kScPerLane];
 #pragma unroll
     for (int t = 0; t < kScPerLane; ++t) {
+      if constexpr (FUSED) break;
       const int c = lane + 64 * t;
       const int cq = c / (8 * MT), cm = (c / 8) % MT, b = c % 8;
       const int cs = wave * kGemvSlices + cq + i * kGemvKS;
@@ -120,17 +151,53 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
     // the region's reads of the previous step are done before it is overwritten
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    if constexpr (FUSED) {
+      uint8_t* sl = region + fq * kSlice;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int c = lane + 64 * t;
-      *reinterpret_cast<v4i*>(region + (c / (16 * MT)) * kSlice + (c % (16 * MT)) * 16) = tok[t];
-    }
+      for (int m = 0; m < MT; ++m) {
+        if (m < mc) {
+          float a = 0.0f;
 #pragma unroll
-    for (int t = 0; t < kScPerLane; ++t) {
-      const int c = lane + 64 * t;
-      if (c < kSc)
-        *reinterpret_cast<float2*>(region + (c / (8 * MT)) * kSlice + kTokBytes +
-                                   (c % (8 * MT)) * 8) = scv[t];
+          for (int e = 0; e < 4; ++e) {
+            const float4 v = xv[m][e];
+            a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+          }
+          const float amax = fmaxf(a, __int_as_float(dpp<kSwap1>(__float_as_int(a))));
+          const float d = amax / 127.0f;                // IEEE division
+          const float id = d > 0.0f ? 1.0f / d : 0.0f;  // IEEE reciprocal (division)
+          v4i packed;
+          int sum = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float4 v = xv[m][e];
+            const int q0 = quant1(v.x, id), q1 = quant1(v.y, id);
+            const int q2 = quant1(v.z, id), q3 = quant1(v.w, id);
+            sum += q0 + q1 + q2 + q3;
+            packed[e] = (int)((uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) |
+                              ((uint32_t)(q2 & 0xFF) << 16) | ((uint32_t)(q3 & 0xFF) << 24));
+          }
+          sum += dpp<kSwap1>(sum);
+          const _Float16 dh = (_Float16)d;  // RNE
+          *reinterpret_cast<v4i*>(sl + m * 256 + fb * 32 + fh * 16) = packed;
+          if (fh == 0)
+            *reinterpret_cast<float2*>(sl + kTokBytes + (m * 8 + fb) * 8) =
+                make_float2((float)dh, (float)sum);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int c = lane + 64 * t;
+        *reinterpret_cast<v4i*>(region + (c / (16 * MT)) * kSlice + (c % (16 * MT)) * 16) =
+            tok[t];
+      }
+#pragma unroll
+      for (int t = 0; t < kScPerLane; ++t) {
+        const int c = lane + 64 * t;
+        if (c < kSc)
+          *reinterpret_cast<float2*>(region + (c / (8 * MT)) * kSlice + kTokBytes +
+                                     (c % (8 * MT)) * 8) = scv[t];
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -206,11 +273,22 @@ hipError_t launch_mt(const void* q8, const void* w_rep, float* C, int64_t M, int
                      hipStream_t s) {
   const uint8_t* base = static_cast<const uint8_t*>(q8);
   const int64_t groups = (M + MT - 1) / MT;
-  hipLaunchKernelGGL((mmq_gemv_kernel<MT>), dim3((unsigned)gemv_grid(M, N)),
+  hipLaunchKernelGGL((mmq_gemv_kernel<MT, false>), dim3((unsigned)gemv_grid(M, N)),
                      dim3(kGemvWaves * 64), 0, s, reinterpret_cast<const int8_t*>(base),
                      reinterpret_cast<const uint32_t*>(base + M * K),
-                     reinterpret_cast<const float*>(base + q8_planes_offset(M, K)),
+                     reinterpret_cast<const float*>(base + q8_planes_offset(M, K)), nullptr,
                      static_cast<const uint8_t*>(w_rep), C, (int)M, (int)N, (int)K, (int)groups);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_fused_mt(const float* x, const void* w_rep, float* C, int64_t M, int64_t N,
+                           int64_t K, hipStream_t s) {
+  const int64_t groups = (M + MT - 1) / MT;
+  hipLaunchKernelGGL((mmq_gemv_kernel<MT, true>), dim3((unsigned)gemv_grid(M, N)),
+                     dim3(kGemvWaves * 64), 0, s, nullptr, nullptr, nullptr,
+                     reinterpret_cast<const float4*>(x), static_cast<const uint8_t*>(w_rep), C,
+                     (int)M, (int)N, (int)K, (int)groups);
   return hipGetLastError();
 }
 
@@ -235,6 +313,16 @@ hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t 
     case 1: return launch_mt<1>(q8, w_rep, C, M, N, K, s);
     case 2: return launch_mt<2>(q8, w_rep, C, M, N, K, s);
     default: return launch_mt<4>(q8, w_rep, C, M, N, K, s);
+  }
+}
+
+hipError_t launch_mmq_gemv_fused(const float* x, const void* w_rep, float* C, int64_t M,
+                                 int64_t N, int64_t K, hipStream_t s) {
+  if (M < 1 || M > kGemvMaxM) return hipErrorInvalidValue;
+  switch (gemv_group(M)) {
+    case 1: return launch_fused_mt<1>(x, w_rep, C, M, N, K, s);
+    case 2: return launch_fused_mt<2>(x, w_rep, C, M, N, K, s);
+    default: return launch_fused_mt<4>(x, w_rep, C, M, N, K, s);
   }
 }
 

@@ -103,6 +103,9 @@ int64_t gemv_lds_bytes(int64_t M);
 int64_t gemv_grid(int64_t M, int64_t N);
 hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
                            int64_t K, hipStream_t s);
+// The same kernel quantizing its own f32 activations (same LDS, grid and threads).
+hipError_t launch_mmq_gemv_fused(const float* x, const void* w_rep, float* C, int64_t M,
+                                 int64_t N, int64_t K, hipStream_t s);
 
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, hipStream_t s);
 hipError_t launch_repack_q4_K(const void* w, int64_t N, int64_t K, void* w_rep, hipStream_t s);

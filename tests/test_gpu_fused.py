@@ -1,9 +1,10 @@
 """The quantize-fused product for few tokens, mmq_q4K_f32, through the C ABI (needs a GPU).
 
 Bars:
-- C bit for bit equal to quantize_q8_1 followed by mmq_q4K_q8_1_ex with the skinny tile
-  (the fused kernel quantizes with the prepass's arithmetic and then does the skinny
-  kernel's arithmetic in the same order);
+- C bit for bit equal to quantize_q8_1 followed by mmq_q4K_q8_1_ex with the tile the fused
+  call uses: the vector-ALU tile for M <= 8, the skinny tile above (each fused kernel
+  quantizes with the prepass's arithmetic and then does its unfused twin's arithmetic in the
+  same order);
 - within 1e-5 * T of the oracle, as for the unfused product.
 Shapes cover one and several token tiles, ragged M and N, K of one super-block (most
 wavefronts of a workgroup get no super-block) and K with super-blocks that do not divide
@@ -32,11 +33,15 @@ def _gpu():
     torch.cuda.synchronize()
 
 
+def fused_tile(M):
+    return mmq.MMQ_TILE_GEMV if M <= 8 else mmq.MMQ_TILE_SKINNY
+
+
 def two_step(x_dev, M, N, K, rep):
     q8 = torch.zeros(mmq.mmq_q8_1_bytes(M, K), dtype=torch.uint8, device="cuda")
     mmq.quantize_q8_1(x_dev, M, K, q8)
     C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
-    mmq.mmq_q4K_q8_1_ex(M, N, K, q8, rep, C, force_tile=mmq.MMQ_TILE_SKINNY)
+    mmq.mmq_q4K_q8_1_ex(M, N, K, q8, rep, C, force_tile=fused_tile(M))
     torch.cuda.synchronize()
     return C.cpu().numpy()
 
@@ -49,11 +54,12 @@ def fused(x_dev, M, N, K, rep):
 
 
 SHAPES = [(1, 4096, 4096), (2, 256, 512), (7, 33, 768), (16, 4096, 4096), (32, 512, 1024),
-          (33, 96, 2048), (100, 65, 2304), (128, 4096, 4096), (5, 40, 256), (3, 64, 11008)]
+          (33, 96, 2048), (100, 65, 2304), (128, 4096, 4096), (5, 40, 256), (3, 64, 11008),
+          (8, 4097, 4096), (9, 70, 1024), (4, 16, 9472), (1, 1, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
-def test_fused_equals_prepass_then_skinny(M, N, K):
+def test_fused_equals_prepass_then_unfused(M, N, K):
     x = synth.activations("normal_outliers", M, K, 9000 + M + K)
     w, _ = synth.q4k_weights("fit", N, K, 9001 + N)
     rep = gpu_repack(w, N, K)
@@ -64,7 +70,7 @@ def test_fused_equals_prepass_then_skinny(M, N, K):
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), \
         f"{np.count_nonzero(got.view(np.uint32) != want.view(np.uint32))} elements differ"
     info = mmq.mmq_last_kernel()
-    assert info["tile"] == mmq.MMQ_TILE_SKINNY and info["reason"] == mmq.MMQ_REASON_FUSED
+    assert info["tile"] == fused_tile(M) and info["reason"] == mmq.MMQ_REASON_FUSED
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 256, 512), (9, 70, 1024), (40, 33, 768)])
