@@ -1,7 +1,7 @@
 """Benchmark of the q4_K x q8_1 MMQ hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--rotate R] [--no-cpu-baseline]
-                    [--no-f16] [--sweep]
+                    [--no-f16] [--sweep] [--decode [--shape M,N,K]]
 
 Defaults: W = 500 warmup steps (the device's clocks settle after ~50 ms of this load; the
 first q-proj steps take up to 1.5x the steady-state time), then K = 200 timed steps.
@@ -25,6 +25,9 @@ same kernel source (null once the kernel has changed since the counters were tak
 The line also carries `comparator_f16`: the same workload through the f16 comparator path
 (convert_f32_f16, dequantize_q4_K_f16, gemm_f16), each kernel timed the same way, and the
 two whole paths: per call, and with the weights resident in f16. `--no-f16` skips it.
+
+`--sweep` prints one line per configuration and tile instead, and `--decode` one line per
+few-token shape (vector-ALU tile, skinny tile, fused call); neither is the benchmark line.
 """
 from __future__ import annotations
 
@@ -226,11 +229,32 @@ def measure(W: dict, R: int, steps: int, warmup: int, tile: int = 0) -> dict:
     torch.cuda.synchronize()
     graph_step_us = e0.elapsed_time(e1) * 1e3 / (reps_g * R)
     del g
+    # The GEMM alone, replayed the same way: its GPU time without the host's launch cost,
+    # which sets the back-to-back figure of the smallest kernels.
+    g = torch.cuda.CUDAGraph()
+    cs.wait_stream(stream)
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            for r in range(R):
+                gemm(r)
+    stream.wait_stream(cs)
+    for _ in range(2):
+        g.replay()
+    e0, e1 = events()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps_g):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph_gemm_us = e0.elapsed_time(e1) * 1e3 / (reps_g * R)
+    del g
     del xs, reps, q8s, Cs
     torch.cuda.empty_cache()
     return {"ms_per_step": wall * 1e3 / steps, "step_gpu_us": region_gpu_ms * 1e3 / steps,
             "gemm_us": g_ms * 1e3, "quant_us": q_ms * 1e3, "repack_us": repack_us, "plan": plan,
-            "graph_step_us": graph_step_us}
+            "graph_step_us": graph_step_us,
+            "graph_gemm_us": graph_gemm_us}
 
 
 def measure_fused(W: dict, R: int, steps: int, warmup: int) -> dict:
@@ -372,6 +396,47 @@ def gemm_bytes(M: int, N: int, K: int) -> int:
     return mmq.mmq_q8_1_bytes(M, K) + mmq.mmq_q4K_repacked_bytes(N, K) + 4 * M * N
 
 
+def rotation(M: int, N: int, K: int, r_min: int) -> int:
+    """Input/output sets to rotate over so that one pass over them (at least 512 MiB, at most
+    64 sets) exceeds the 256 MB last-level cache: with few tokens a set is little more than
+    the weights, and 8 of them would stay cache-resident."""
+    per_set = 5.6 * M * K + (N + 31) // 32 * (K // 256) * 6656 + 4 * M * N
+    return int(min(64, max(r_min, -(-(512 << 20) // per_set))))
+
+
+DECODE_SHAPES = [(1, 4096, 4096), (2, 4096, 4096), (4, 4096, 4096), (8, 4096, 4096),
+                 (1, 11008, 4096), (1, 4096, 11008)]
+
+
+def decode(args) -> int:
+    """Few-token products (decode shapes of a 7B layer): each shape under the vector-ALU tile
+    and the skinny tile, and through the fused call, with inputs rotated beyond the
+    last-level cache. One JSON line per shape; --shape M,N,K runs one shape only."""
+    import synth
+    import q4_q8_int8_amd as mmq
+    shapes = DECODE_SHAPES
+    if args.shape:
+        shapes = [tuple(int(v) for v in args.shape.split(","))]
+    for M, N, K in shapes:
+        x = synth.activations("normal_outliers", M, K, 1500 + M)
+        w, _ = synth.q4k_weights("fit", N, K, 2004)
+        W = {"M": M, "N": N, "K": K, "x": x, "w": w}
+        R = rotation(M, N, K, args.rotate)
+        wbytes = mmq.mmq_q4K_repacked_bytes(N, K)
+        line = {"config": "decode", "M": M, "N": N, "K": K, "rotate": R}
+        for tile, name in ((mmq.MMQ_TILE_GEMV, "gemv"), (mmq.MMQ_TILE_SKINNY, "skinny")):
+            t = measure(W, R, args.steps, args.warmup, tile)
+            line[name] = {"gemm_graph_us": round(t["graph_gemm_us"], 2),
+                          "gemm_us": round(t["gemm_us"], 2),
+                          "weights_tbps": round(wbytes / (t["graph_gemm_us"] * 1e-6) / 1e12, 2),
+                          "step_graph_us": round(t["graph_step_us"], 2),
+                          "step_us": round(t["step_gpu_us"], 2)}
+        fu = measure_fused(W, R, args.steps, args.warmup)
+        line["fused"] = {"graph_us": round(fu["graph_us"], 2), "us": round(fu["us"], 2)}
+        print(json.dumps(line), flush=True)
+    return 0
+
+
 def config_line(name: str, W: dict, t: dict) -> dict:
     """One JSON line of the per-config table: throughput, peak and HBM fractions."""
     M, N, K = W["M"], W["N"], W["K"]
@@ -389,7 +454,9 @@ def config_line(name: str, W: dict, t: dict) -> dict:
             "step_us": round(t["step_gpu_us"], 2),
             "path_tmacs": round(macs / (t["step_gpu_us"] * 1e-6) / 1e12, 2),
             "graph_step_us": round(t["graph_step_us"], 2),
-            "graph_path_tmacs": round(macs / (t["graph_step_us"] * 1e-6) / 1e12, 2)}
+            "graph_path_tmacs": round(macs / (t["graph_step_us"] * 1e-6) / 1e12, 2),
+            "graph_gemm_us": round(t["graph_gemm_us"], 2),
+            "rotate": t["rotate"]}
 
 
 def sweep(args) -> int:
@@ -401,17 +468,19 @@ def sweep(args) -> int:
     times = {}
     for name in names:
         W = synth.workload(name)
+        R = rotation(W["M"], W["N"], W["K"], args.rotate)
         tiles = [mmq.MMQ_TILE_LARGE, mmq.MMQ_TILE_SMALL]
         if W["M"] <= 512:
             tiles.append(mmq.MMQ_TILE_SKINNY)
         if W["M"] <= mmq.GEMV_MAX_M:
             tiles.append(mmq.MMQ_TILE_GEMV)
         for tile in tiles:
-            t = measure(W, args.rotate, args.steps, args.warmup, tile)
+            t = measure(W, R, args.steps, args.warmup, tile)
+            t["rotate"] = R
             times[(name, tile)] = t
             print(json.dumps(config_line(name, W, t)), flush=True)
         if W["M"] <= 128:
-            fu = measure_fused(W, args.rotate, args.steps, args.warmup)
+            fu = measure_fused(W, R, args.steps, args.warmup)
             macs = W["M"] * W["N"] * W["K"]
             print(json.dumps({"config": name, "M": W["M"], "N": W["N"], "K": W["K"],
                               "fused": {"us": round(fu["us"], 2),
@@ -419,7 +488,7 @@ def sweep(args) -> int:
                                         "tmacs": round(macs / (fu["us"] * 1e-6) / 1e12, 2)}}),
                   flush=True)
         if not args.no_f16:
-            f = measure_f16(W, args.rotate, args.steps, args.warmup)
+            f = measure_f16(W, R, args.steps, args.warmup)
             times[(name, "f16")] = f
             print(json.dumps({"config": name, "M": W["M"], "N": W["N"], "K": W["K"],
                               "comparator_f16": f16_summary(W["M"], W["N"], W["K"], f)}),
@@ -480,6 +549,11 @@ def main() -> int:
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     ap.add_argument("--no-f16", action="store_true",
                     help="skip the f16 comparator path's timing")
+    ap.add_argument("--decode", action="store_true",
+                    help="few-token shapes: vector-ALU vs skinny tile vs fused call, one JSON "
+                         "line per shape")
+    ap.add_argument("--shape", default="", metavar="M,N,K",
+                    help="with --decode: one shape only")
     ap.add_argument("--sweep", action="store_true",
                     help="per-config table (one JSON line per config and tile) instead of the "
                          "benchmark line")
@@ -499,6 +573,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.sweep:
         return sweep(args)
+    if args.decode:
+        return decode(args)
 
     W = synth.workload("qproj")
     M, N, K = W["M"], W["N"], W["K"]
