@@ -464,7 +464,8 @@ def sweep(args) -> int:
     one JSON line each. Not the driver's benchmark line; see the profiles."""
     import synth
     import q4_q8_int8_amd as mmq
-    names = ["tiny", "qproj", "gateup", "down"] + [f"sweep_m{m}" for m in synth.SWEEP_M]
+    names = ["tiny", "qproj", "gateup", "down"] + [f"sweep_m{m}" for m in synth.SWEEP_M] \
+        + list(synth.SHARE8)
     times = {}
     for name in names:
         W = synth.workload(name)

@@ -60,9 +60,9 @@ enum mmq_tile {
   MMQ_TILE_SKINNY = 3, /* 32 tokens x 32 output features per workgroup, K split over 8
                           wavefronts and summed in wavefront order (no block-dot output) */
   MMQ_TILE_GEMV = 4    /* M <= 16 only: up to 4 tokens x 16 output features per workgroup of
-                          4 wavefronts, integer dot products on the vector ALU (v_dot4_i32_i8),
-                          K split over 16 slices and summed in slice order (no block-dot
-                          output) */
+                          8 wavefronts, integer dot products on the vector ALU (v_dot4_i32_i8),
+                          K split over 16 slices x 2 halves of each super-block and summed in
+                          a fixed order (no block-dot output) */
 };
 
 /* Why the guard chose what it chose. */

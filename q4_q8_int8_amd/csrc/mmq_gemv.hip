@@ -9,34 +9,36 @@
 //
 // With one to sixteen tokens the product streams the weights once and does little else, so
 // matrix instructions buy nothing: the MFMA tiles of the other kernels are 32 tokens wide and
-// would be mostly padding. Here a workgroup of four wavefronts owns 16 weight rows (half of a
-// repacked 32-row tile), all of K and a group of at most MT tokens. Its 256 lanes are 16 rows
-// x 16 K-slices (lane l of wavefront w: row l % 16, slice 4w + l / 16), and slice ks takes
-// the super-blocks ks, ks + 16, ks + 32, ...; so at K = 4096 every lane owns one super-block
-// and the grid has N/16 workgroups (256 at N = 4096) per token group. Token groups are
-// separate workgroups, so that more tokens bring more workgroups rather than longer
-// wavefronts; the groups of one row block read the same weights, mostly from L2.
+// would be mostly padding. Here a workgroup of eight wavefronts owns 16 weight rows (half of a
+// repacked 32-row tile), all of K and a group of at most MT tokens. Lane l of wavefront w has
+// row l % 16 and K-slice 4 (w % 4) + l / 16; slice ks takes the super-blocks ks, ks + 16,
+// ks + 32, ..., of which wavefronts 0-3 take blocks 0-3 and wavefronts 4-7 blocks 4-7. So at
+// K = 4096 every lane owns half a super-block, the grid has N/16 workgroups (256 at N = 4096)
+// per token group, and two wavefronts per SIMD overlap one's loads with the other's dot
+// products. Token groups are separate workgroups, so that more tokens bring more workgroups
+// rather than longer wavefronts; the groups of one row block read the same weights, mostly
+// from L2.
 //
-// Per super-block a lane loads its row's 128 nibble bytes, its 8 scales dsv and the three
-// bf16 pieces of its 8 mins dmv (16- and 4-byte buffer loads; the 16 lanes of a slice read
-// 256 contiguous bytes); in the same burst the lanes of a wavefront load the token bytes of
-// its four slices' super-blocks and their (da, sa) words and put them in the wavefront's own
-// LDS region, which each slice's lanes then read at one address (broadcast). All loads of a
-// step are in flight together: read instead one token at a time with scalar loads, each
-// waited for before its dot products, they cost an L2 round trip per token and pair of
-// blocks. Per block, S is eight v_dot4_i32_i8 over 4 bytes each (both operands signed;
-// nibbles are 0..15), then
+// Per step a lane loads its row's 64 nibble bytes of its half, its 4 scales dsv and the three
+// bf16 pieces of its 4 mins dmv (buffer loads; the 16 lanes of a slice read 256 contiguous
+// bytes); in the same burst the lanes of a wavefront load its four slices' token bytes of that
+// half and their (da, sa) words, and put them in the wavefront's own LDS region, which each
+// slice's lanes then read at one address (broadcast). When a slice has another super-block,
+// its loads are issued before this one is computed. Read instead one token at a time with
+// scalar loads, each waited for before its dot products, the token data cost an L2 round trip
+// per token and pair of blocks. Per block, S is eight v_dot4_i32_i8 over 4 bytes each (both
+// operands signed; nibbles are 0..15), then
 //   u = fma(dmv, float(sa), float(S) * dsv),  acc = fma(u, da, acc).
 //
-// Summation order per output: blocks in order within a super-block, super-blocks in order
-// within a slice, then the 16 slices' partial sums in slice order through LDS. Deterministic;
+// Summation order per output: blocks in order within a half, super-blocks in order within a
+// (slice, half), then the 32 (slice, half) partial sums in order through LDS. Deterministic;
 // not the GEMM's association (the two agree within the f32 tolerance).
 //
 // The FUSED instantiation takes the f32 activations instead of the q8 buffer: each wavefront
-// loads the f32 values of its four slices' super-blocks (in the same burst as the weights)
-// and quantizes them into its LDS region, one pass per token for all four slices: lane l takes
-// 16 values of block (l % 16) / 2 of slice l / 16, and the two lanes of a block combine their
-// max and integer sum with one lane swap. The arithmetic per value and per block is the
+// loads the f32 values of its half of its four slices' super-blocks (with the weights) and
+// quantizes them into its LDS region, one pass per token: lane l takes 8 values of block
+// (l % 16) / 4 of the half of slice l / 16, and the four lanes of a block combine their max
+// and integer sum with two lane swaps. The arithmetic per value and per block is the
 // prepass's (quant1, IEEE divisions, f16 rounding), and max and integer sum do not depend on
 // the order of their terms, so the region holds exactly the bytes and (da, sa) the unfused
 // kernel stages: C is bit for bit that of quantize_q8_1 followed by the unfused kernel, from
@@ -47,107 +49,117 @@
 namespace mmq {
 namespace {
 
-constexpr int kGemvSlices = 64 / kGemvRows;        // K-slices per wavefront
-constexpr int kGemvKS = kGemvSlices * kGemvWaves;  // K-slices per workgroup
+constexpr int kGemvSlices = 64 / kGemvRows;              // K-slices per wavefront
+constexpr int kGemvKS = kGemvSlices * (kGemvWaves / 2);  // K-slices per workgroup (16)
 
 template <int MT, bool FUSED>
 __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
     const int8_t* __restrict__ qs, const uint32_t* __restrict__ words,
     const float* __restrict__ da_plane, const float4* __restrict__ x,
     const uint8_t* __restrict__ wrep, float* __restrict__ C, int M, int N, int K, int groups) {
-  // per wavefront and slice: token bytes [MT][256], then (da, float(sa)) [MT][8]; 16 bytes of
-  // padding per slice put the four slices' broadcast reads in different banks. After the
-  // loop the same memory holds the partial sums [kGemvKS][MT][kGemvRows].
-  constexpr int kTokBytes = MT * 256;
-  constexpr int kSlice = kTokBytes + MT * 64 + 16;
+  // Wavefronts 0-3 take blocks 0-3 of their slices' super-blocks, wavefronts 4-7 blocks 4-7.
+  // Per wavefront and slice: its half of the token bytes [MT][128], then (da, float(sa))
+  // [MT][4]; 16 bytes of padding per slice. After the loop the same memory holds the partial
+  // sums [kGemvKS][2][MT][kGemvRows].
+  constexpr int kTokBytes = MT * 128;
+  constexpr int kSlice = kTokBytes + MT * 32 + 16;
   constexpr int kRegion = kGemvSlices * kSlice;
-  static_assert(kGemvWaves * kRegion >= kGemvKS * MT * kGemvRows * 4, "partial sums fit");
+  static_assert(kGemvWaves * kRegion >= kGemvKS * 2 * MT * kGemvRows * 4, "partial sums fit");
   __shared__ __align__(16) uint8_t smem[kGemvWaves * kRegion];
   const int rb = (int)(blockIdx.x / (unsigned)groups);        // row block: rows 16rb..16rb+15
   const int m0 = (int)(blockIdx.x % (unsigned)groups) * MT;  // first token of the group
   const int mc = M - m0 < MT ? M - m0 : MT;                    // tokens in the group
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int hf = wave >> 2;                                    // half of the super-block
+  const int wq = wave & 3;                                     // slice group
   const int jj = lane % kGemvRows;
   const int q = lane / kGemvRows;                              // slice within the wavefront
-  const int ks = wave * kGemvSlices + q;
+  const int ks = wq * kGemvSlices + q;
   const int j = (rb & 1) * kGemvRows + jj;                     // row within the 32-row tile
   const int nsb = K >> 8, kb = K >> 5;
   // steps of this wavefront: its first slice has the most super-blocks
-  const int steps = (nsb - wave * kGemvSlices + kGemvKS - 1) / kGemvKS;
+  const int steps = (nsb - wq * kGemvSlices + kGemvKS - 1) / kGemvKS;
   uint8_t* region = smem + wave * kRegion;
 
   const uint8_t* wtile = wrep + (size_t)(rb >> 1) * (size_t)nsb * kRepTileBytes;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wtile, (uint32_t)nsb * (uint32_t)kRepTileBytes);
 
+  // token staging of this lane (unfused): chunk c = (slice * MT + m) * 8 + part of the
+  // wavefront's half, and (da, sa) c = (slice * MT + m) * 4 + block
+  constexpr int kTokChunks = kGemvSlices * MT * 8;
+  constexpr int kTokPerLane = (kTokChunks + 63) / 64;
+  constexpr int kSc = kGemvSlices * MT * 4;
+  // fused: lane l quantizes 8 values of block (l % 16) / 4 of the half, quarter l % 4, of
+  // slice l / 16
+  const int fq = lane >> 4, fb = (lane & 15) >> 2, fc = lane & 3;
+
+  struct Stage {
+    v4i nib[4];      // chunk (g, h) of the half at 2 (g - 2 hf) + h
+    float dsv[4];
+    uint2 pc[3];     // dmv pieces of blocks 4 hf .. 4 hf + 3
+    v4i tok[FUSED ? 1 : kTokPerLane];
+    float2 sc;       // (da, float(sa)) of entry lane (lane < kSc)
+    float4 xv[FUSED ? MT : 1][2];
+  };
+  auto load = [&](int i, Stage& st) {
+    const int s = ks + i * kGemvKS;
+    const uint32_t rec = (uint32_t)s * kRepTileBytes;  // an idle slice reads past the tile: 0
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      st.nib[t] = buf_load16(rw, rec + (2 * hf + (t >> 1)) * 1024 + (t & 1) * 512 + j * 16);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      st.dsv[b] = buf_load_f32(rw, rec + kRepNibBytes + (4 * hf + b) * 128 + j * 4);
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      st.pc[p] = __builtin_bit_cast(
+          uint2, buf_load_f32x2(rw, rec + kRepNibBytes + kRepDsvBytes + p * 512 + j * 16 + hf * 8));
+    if constexpr (FUSED) {
+      const int cs = wq * kGemvSlices + fq + i * kGemvKS;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const size_t base =
+            ((size_t)(m0 + m) * K + (size_t)cs * 256 + hf * 128 + fb * 32 + fc * 8) / 4;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          st.xv[m][e] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          if (m < mc && cs < nsb) st.xv[m][e] = x[base + e];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < kTokPerLane; ++t) {
+        const int c = lane + 64 * t;
+        const int cq = c / (8 * MT), cm = (c / 8) % MT, part = c % 8;
+        const int cs = wq * kGemvSlices + cq + i * kGemvKS;
+        st.tok[t] = v4i{0, 0, 0, 0};
+        if (c < kTokChunks && cm < mc && cs < nsb)
+          st.tok[t] = *reinterpret_cast<const v4i*>(qs + (size_t)(m0 + cm) * K +
+                                                    (size_t)cs * 256 + hf * 128 + part * 16);
+      }
+      const int cq = lane / (4 * MT), cm = (lane / 4) % MT, b = 4 * hf + lane % 4;
+      const int cs = wq * kGemvSlices + cq + i * kGemvKS;
+      st.sc = make_float2(0.0f, 0.0f);
+      if (lane < kSc && cm < mc && cs < nsb) {
+        const uint32_t w = words[(size_t)(m0 + cm) * kb + (size_t)cs * 8 + b];
+        st.sc = make_float2(da_plane[((size_t)(cs * 8 + b) * M + m0 + cm) * 2],
+                            (float)((int)w >> 16));
+      }
+    }
+  };
+
   float acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
 
+  Stage cur, nxt;
+  if (steps > 0) load(0, cur);
   for (int i = 0; i < steps; ++i) {
-    const int s = ks + i * kGemvKS;            // this lane's super-block
-    const bool act = s < nsb;                  // the last step may leave slices idle
-    // weights; an idle slice's offsets are past the tile and read zero
-    const uint32_t rec = (uint32_t)s * kRepTileBytes;
-    v4i nib[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-      nib[t] = buf_load16(rw, rec + (t >> 1) * 1024 + (t & 1) * 512 + j * 16);
-    float dsv[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) dsv[b] = buf_load_f32(rw, rec + kRepNibBytes + b * 128 + j * 4);
-    v4i pc[3];
-#pragma unroll
-    for (int p = 0; p < 3; ++p)
-      pc[p] = buf_load16(rw, rec + kRepNibBytes + kRepDsvBytes + p * 512 + j * 16);
-    // fused: lane l's 16 values of token m0 + m: values 32 fb + 16 fh .. + 15 of the
-    // super-block of slice fq (fq = l / 16, fb = (l % 16) / 2, fh = l % 2); zero for an idle
-    // slice
-    const int fq = lane >> 4, fb = (lane & 15) >> 1, fh = lane & 1;
-    float4 xv[FUSED ? MT : 1][4];
-    if constexpr (FUSED) {
-      const int cs = wave * kGemvSlices + fq + i * kGemvKS;
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const size_t base = ((size_t)(m0 + m) * K + (size_t)cs * 256 + fb * 32 + fh * 16) / 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          xv[m][e] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-          if (m < mc && cs < nsb) xv[m][e] = x[base + e];
-        }
-      }
-    }
-    // unfused: token data of the wavefront's four slices: chunk c = (slice * MT + m) * 16 +
-    // part, MT chunks per lane; (da, sa) of block b of token m of a slice: c = (slice * MT +
-    // m) * 8 + b
-    v4i tok[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      if constexpr (FUSED) break;
-      const int c = lane + 64 * t;
-      const int cq = c / (16 * MT), cm = (c / 16) % MT, part = c % 16;
-      const int cs = wave * kGemvSlices + cq + i * kGemvKS;
-      tok[t] = v4i{0, 0, 0, 0};
-      if (cm < mc && cs < nsb)
-        tok[t] = *reinterpret_cast<const v4i*>(qs + (size_t)(m0 + cm) * K + (size_t)cs * 256 +
-                                               part * 16);
-    }
-    constexpr int kSc = kGemvSlices * MT * 8;
-    constexpr int kScPerLane = (kSc + 63) / 64;
-    float2 scv[kScPerLane];
-#pragma unroll
-    for (int t = 0; t < kScPerLane; ++t) {
-      if constexpr (FUSED) break;
-      const int c = lane + 64 * t;
-      const int cq = c / (8 * MT), cm = (c / 8) % MT, b = c % 8;
-      const int cs = wave * kGemvSlices + cq + i * kGemvKS;
-      scv[t] = make_float2(0.0f, 0.0f);
-      if (c < kSc && cm < mc && cs < nsb) {
-        const uint32_t w = words[(size_t)(m0 + cm) * kb + (size_t)cs * 8 + b];
-        scv[t] = make_float2(da_plane[((size_t)(cs * 8 + b) * M + m0 + cm) * 2],
-                             (float)((int)w >> 16));
-      }
-    }
+    // the next step's loads go out before this step's compute
+    if (i + 1 < steps) load(i + 1, nxt);
+    const int s = ks + i * kGemvKS;
+    const bool act = s < nsb;
     // the region's reads of the previous step are done before it is overwritten
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -158,79 +170,79 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
         if (m < mc) {
           float a = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float4 v = xv[m][e];
+          for (int e = 0; e < 2; ++e) {
+            const float4 v = cur.xv[m][e];
             a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
           }
-          const float amax = fmaxf(a, __int_as_float(dpp<kSwap1>(__float_as_int(a))));
+          a = fmaxf(a, __int_as_float(dpp<kSwap1>(__float_as_int(a))));
+          const float amax = fmaxf(a, __int_as_float(dpp<kSwap2>(__float_as_int(a))));
           const float d = amax / 127.0f;                // IEEE division
           const float id = d > 0.0f ? 1.0f / d : 0.0f;  // IEEE reciprocal (division)
-          v4i packed;
+          uint2 packed;
           int sum = 0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float4 v = xv[m][e];
+          for (int e = 0; e < 2; ++e) {
+            const float4 v = cur.xv[m][e];
             const int q0 = quant1(v.x, id), q1 = quant1(v.y, id);
             const int q2 = quant1(v.z, id), q3 = quant1(v.w, id);
             sum += q0 + q1 + q2 + q3;
-            packed[e] = (int)((uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) |
-                              ((uint32_t)(q2 & 0xFF) << 16) | ((uint32_t)(q3 & 0xFF) << 24));
+            const uint32_t pw = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) |
+                                ((uint32_t)(q2 & 0xFF) << 16) | ((uint32_t)(q3 & 0xFF) << 24);
+            if (e == 0) packed.x = pw; else packed.y = pw;
           }
           sum += dpp<kSwap1>(sum);
+          sum += dpp<kSwap2>(sum);
           const _Float16 dh = (_Float16)d;  // RNE
-          *reinterpret_cast<v4i*>(sl + m * 256 + fb * 32 + fh * 16) = packed;
-          if (fh == 0)
-            *reinterpret_cast<float2*>(sl + kTokBytes + (m * 8 + fb) * 8) =
+          *reinterpret_cast<uint2*>(sl + m * 128 + fb * 32 + fc * 8) = packed;
+          if (fc == 0)
+            *reinterpret_cast<float2*>(sl + kTokBytes + (m * 4 + fb) * 8) =
                 make_float2((float)dh, (float)sum);
         }
       }
     } else {
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
+      for (int t = 0; t < kTokPerLane; ++t) {
         const int c = lane + 64 * t;
-        *reinterpret_cast<v4i*>(region + (c / (16 * MT)) * kSlice + (c % (16 * MT)) * 16) =
-            tok[t];
+        if (c < kTokChunks)
+          *reinterpret_cast<v4i*>(region + (c / (8 * MT)) * kSlice + (c % (8 * MT)) * 16) =
+              cur.tok[t];
       }
-#pragma unroll
-      for (int t = 0; t < kScPerLane; ++t) {
-        const int c = lane + 64 * t;
-        if (c < kSc)
-          *reinterpret_cast<float2*>(region + (c / (8 * MT)) * kSlice + kTokBytes +
-                                     (c % (8 * MT)) * 8) = scv[t];
-      }
+      if (lane < kSc)
+        *reinterpret_cast<float2*>(region + (lane / (4 * MT)) * kSlice + kTokBytes +
+                                   (lane % (4 * MT)) * 8) = cur.sc;
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
     if (act) {
       const uint8_t* sl = region + q * kSlice;
       // dmv = p0 + p1 + p2, exact in f32
-      float dmv[8];
+      float dmv[4];
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
+      for (int b = 0; b < 4; ++b) {
         float p[3];
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
-          const uint32_t w = (uint32_t)pc[t][b >> 1];
+          const uint32_t w = (b >> 1) ? cur.pc[t].y : cur.pc[t].x;
           p[t] = __builtin_bit_cast(float, (b & 1) ? (w & 0xFFFF0000u) : (w << 16));
         }
         dmv[b] = (p[0] + p[1]) + p[2];
       }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int gg = 0; gg < 2; ++gg) {
         int lo[8], hi[8];
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
-          const uint32_t w = (uint32_t)nib[2 * g + (d >> 2)][d & 3];
+          const uint32_t w = (uint32_t)cur.nib[2 * gg + (d >> 2)][d & 3];
           lo[d] = (int)(w & 0x0F0F0F0Fu);
           hi[d] = (int)((w >> 4) & 0x0F0F0F0Fu);
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m < mc) {
-            // blocks 2g and 2g+1 of token m0 + m (64 bytes) and their (da, float(sa)) pairs
-            const v4i* tq = reinterpret_cast<const v4i*>(sl + m * 256 + g * 64);
+            // blocks 2gg and 2gg+1 of the half for token m0 + m, and their (da, sa) pairs
+            const v4i* tq = reinterpret_cast<const v4i*>(sl + m * 128 + gg * 64);
             const float4 sc =
-                *reinterpret_cast<const float4*>(sl + kTokBytes + (m * 8 + 2 * g) * 8);
+                *reinterpret_cast<const float4*>(sl + kTokBytes + (m * 4 + 2 * gg) * 8);
             int S0 = 0, S1 = 0;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -241,20 +253,22 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
                 S1 = __builtin_amdgcn_sdot4(hi[4 * h + d], c[d], S1, false);
               }
             }
-            const float u0 = __builtin_fmaf(dmv[2 * g], sc.y, (float)S0 * dsv[2 * g]);
+            const float u0 = __builtin_fmaf(dmv[2 * gg], sc.y, (float)S0 * cur.dsv[2 * gg]);
             acc[m] = __builtin_fmaf(u0, sc.x, acc[m]);
-            const float u1 = __builtin_fmaf(dmv[2 * g + 1], sc.w, (float)S1 * dsv[2 * g + 1]);
+            const float u1 =
+                __builtin_fmaf(dmv[2 * gg + 1], sc.w, (float)S1 * cur.dsv[2 * gg + 1]);
             acc[m] = __builtin_fmaf(u1, sc.z, acc[m]);
           }
         }
       }
     }
+    cur = nxt;
   }
 
   __syncthreads();  // every wavefront is done with its region
   float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int m = 0; m < MT; ++m) red[(ks * MT + m) * kGemvRows + jj] = acc[m];
+  for (int m = 0; m < MT; ++m) red[((ks * 2 + hf) * MT + m) * kGemvRows + jj] = acc[m];
   __syncthreads();
   for (int e = threadIdx.x; e < MT * kGemvRows; e += kGemvWaves * 64) {
     const int m = e / kGemvRows, r = e % kGemvRows;
@@ -262,7 +276,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
     if (m < mc && n < N) {
       float v = 0.0f;
 #pragma unroll
-      for (int k2 = 0; k2 < kGemvKS; ++k2) v += red[(k2 * MT + m) * kGemvRows + r];
+      for (int k2 = 0; k2 < 2 * kGemvKS; ++k2) v += red[(k2 * MT + m) * kGemvRows + r];
       C[(size_t)(m0 + m) * N + n] = v;
     }
   }
@@ -299,7 +313,7 @@ int64_t gemv_group(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : 4); }
 
 int64_t gemv_lds_bytes(int64_t M) {
   const int64_t mt = gemv_group(M);
-  return (int64_t)kGemvWaves * kGemvSlices * (mt * 320 + 16);
+  return (int64_t)kGemvWaves * kGemvSlices * (mt * 160 + 16);
 }
 
 int64_t gemv_grid(int64_t M, int64_t N) {

@@ -91,8 +91,9 @@ hipError_t launch_mmq_fused(const float* x, const void* w_rep, float* C, int64_t
                             int64_t K, hipStream_t s);
 
 // Vector-ALU product for a handful of tokens (decode): 16 weight rows and up to 4 tokens per
-// workgroup of kGemvWaves wavefronts, K split over 16 slices, M <= kGemvMaxM.
-constexpr int kGemvWaves = 4;
+// workgroup of kGemvWaves wavefronts, K split over 16 slices and each super-block over two
+// wavefronts, M <= kGemvMaxM.
+constexpr int kGemvWaves = 8;
 constexpr int kGemvRows = 16;  // weight rows per workgroup
 constexpr int kGemvMaxM = 16;
 // The guard's choice up to here: from 16 tokens (four token groups, each re-reading the

@@ -11,6 +11,8 @@ Workloads (LLaMA-7B-shaped prefill, synthetic stand-ins for trained weights):
   gateup    M=2048, K=4096,  N=11008  same distributions as qproj
   down      M=2048, K=11008, N=4096   x = SiLU(g)*u with g,u ~ N(0,1); q4_K fit of N(0,0.02)
   sweep     M in {1,16,128,512,8192}, K=N=4096, distributions of qproj
+  *_share8  one GPU's share of an 8-way split of the output features (column parallel):
+            qproj and down with N=512, gateup with N=1376; distributions of their full shapes
 """
 from __future__ import annotations
 
@@ -30,6 +32,10 @@ WORKLOADS = {
 }
 for _i, _m in enumerate(SWEEP_M):
     WORKLOADS[f"sweep_m{_m}"] = (_m, 4096, 4096, "normal_outliers", 1400 + _i, "fit", 2004)
+SHARE8 = ("qproj_share8", "gateup_share8", "down_share8")
+WORKLOADS["qproj_share8"] = (2048, 4096, 512, "normal_outliers", 1001, "fit", 2011)
+WORKLOADS["gateup_share8"] = (2048, 4096, 1376, "normal_outliers", 1002, "fit", 2012)
+WORKLOADS["down_share8"] = (2048, 11008, 512, "swiglu", 1003, "fit", 2013)
 
 # the seven projection shapes of one LLaMA-7B layer at 2K tokens: (name, N, K)
 PREFILL_SHAPES = (("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),

@@ -150,9 +150,10 @@ def test_plan_gemv_tile(M, group, grid):
                                               (SKINNY, mmq.MMQ_REASON_FEW_TOKENS))
     p = mmq.mmq_plan(M, 4096, 4096, 160 * 1024, force_tile=GEMV)
     assert p["tile"] == GEMV
-    assert p["block_m"] == group and p["block_n"] == 16 and p["threads"] == 256
-    # per wavefront and K-slice: 256 token bytes and 8 (da, sa) pairs per token, 16 padding
-    assert p["lds_bytes"] == 4 * 4 * (320 * group + 16) and p["grid"] == grid
+    assert p["block_m"] == group and p["block_n"] == 16 and p["threads"] == 512
+    # per wavefront and K-slice: its half's 128 token bytes and 4 (da, sa) pairs per token,
+    # 16 padding
+    assert p["lds_bytes"] == 8 * 4 * (160 * group + 16) and p["grid"] == grid
     # ragged N: 4097 rows make 257 blocks of 16
     assert mmq.mmq_plan(M, 4097, 256, 160 * 1024, force_tile=GEMV)["grid"] == 257 * (grid // 256)
 
@@ -164,13 +165,13 @@ def test_plan_gemv_forced_limits():
         mmq.mmq_plan(17, 4096, 4096, 160 * 1024, force_tile=GEMV)
     assert e.value.status == mmq.MMQ_E_SHAPE
     with pytest.raises(mmq.MMQError) as e:
-        mmq.mmq_plan(16, 4096, 4096, 160 * 1024, force_tile=GEMV, opt_lds_budget=20735)
+        mmq.mmq_plan(16, 4096, 4096, 160 * 1024, force_tile=GEMV, opt_lds_budget=20991)
     assert e.value.status == mmq.MMQ_E_LDS
     # the vector-ALU tile needs the least LDS: under 6 KiB it is the only one that fits
-    p = mmq.mmq_plan(1, 4096, 4096, 160 * 1024, opt_lds_budget=5376)
-    assert p["tile"] == GEMV and p["lds_bytes"] == 5376
+    p = mmq.mmq_plan(1, 4096, 4096, 160 * 1024, opt_lds_budget=5632)
+    assert p["tile"] == GEMV and p["lds_bytes"] == 5632
     with pytest.raises(mmq.MMQError) as e:
-        mmq.mmq_plan(1, 4096, 4096, 160 * 1024, opt_lds_budget=5375)
+        mmq.mmq_plan(1, 4096, 4096, 160 * 1024, opt_lds_budget=5631)
     assert e.value.status == mmq.MMQ_E_LDS
 
 

@@ -164,6 +164,24 @@ def test_mmq_sampled_rows(name):
     say("max |err|/T", r, "rows", len(rows))
 
 
+@pytest.mark.parametrize("name", synth.SHARE8)
+def test_mmq_per_gpu_share_shapes(name):
+    """One GPU's share of an 8-way column split (N = 512 or 1376), under the guard's tile and
+    the large tile, on sampled rows."""
+    W = workload(name)
+    M, N, K = W["M"], W["N"], W["K"]
+    q8 = gpu_quantize(W["x"])
+    rep = gpu_repack(W["w"], N, K)
+    rows = sample_rows(M)
+    C_ref = oracle.mmq(oracle_q8(name), oracle_w(name), rows=rows)
+    _, T = oracle.mmq_terms(oracle_q8(name), oracle_w(name), rows=rows)
+    for tile in (0, LARGE):
+        say("mmq share", name, (M, N, K), "tile", tile)
+        C = gpu_mmq(M, N, K, q8, rep, force_tile=tile)
+        r = assert_within_tolerance(C[rows], C_ref, T)
+        say("max |err|/T", r)
+
+
 @pytest.mark.parametrize("name", ["tiny", "sweep_m1", "sweep_m16", "sweep_m128"])
 def test_mmq_skinny_every_element(name):
     """The skinny kernel (K split over the wavefronts of a workgroup) on every element."""
