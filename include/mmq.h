@@ -73,7 +73,8 @@ enum mmq_reason {
   MMQ_REASON_LDS_FALLBACK = 3,  /* the large tile does not fit the LDS budget: small tile */
   MMQ_REASON_FORCED = 4,        /* the caller's options asked for this tile */
   MMQ_REASON_NO_FIT = 5,        /* nothing fits the budget: refused with MMQ_E_LDS */
-  MMQ_REASON_FEW_TOKENS = 6,    /* 8 < M <= 128 and the large grid would leave compute units idle:
+  MMQ_REASON_FEW_TOKENS = 6,    /* 8 < M <= 128, K >= 2048, and the large grid would leave compute
+                                   units idle:
                                    the skinny kernel, which splits K over wavefronts */
   MMQ_REASON_FUSED = 7,         /* mmq_q4K_f32: the vector-ALU (M <= 8) or skinny kernel quantizing
                                    its own activations */
@@ -229,7 +230,8 @@ int mmq_q4K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, cons
  * when set, takes precedence): for M <= 8 the vector-ALU kernel (MMQ_TILE_GEMV, reason
  * MMQ_REASON_DECODE); else the large tile when it fits and its grid has at least
  * opt->min_workgroups workgroups (default 256, the MI355X compute-unit count; a GEMM call
- * uses the device's count); else, for M <= 128, the skinny kernel; else the small tile (more,
+ * uses the device's count); else, for M <= 128 and K >= 2048 (at least one super-block for
+ * each of its wavefronts), the skinny kernel; else the small tile (more,
  * smaller workgroups: at M = 512, N = 4096 the large tile has 64 workgroups for 256 compute
  * units); when the large tile does not fit the budget, the small tile; else MMQ_E_LDS. A
  * kernel that does not fit the budget is never launched: on the r16 page

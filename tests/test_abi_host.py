@@ -110,6 +110,16 @@ def test_plan_prefers_a_grid_that_fills_the_gpu(M, N, tile):
     assert p["fallback"] == 0
 
 
+@pytest.mark.parametrize("M,N,K,tile", [
+    (128, 256, 512, SMALL),     # 2 super-blocks for the skinny kernel's 8 wavefronts
+    (16, 4096, 1792, SMALL),    # 7
+    (16, 4096, 2048, SKINNY),   # 8: one each
+    (128, 256, 2048, SKINNY),
+])
+def test_plan_skinny_needs_a_super_block_per_wavefront(M, N, K, tile):
+    assert mmq.mmq_plan(M, N, K, 160 * 1024)["tile"] == tile
+
+
 def test_plan_min_workgroups_option():
     assert mmq.mmq_plan(512, 4096, 4096, 160 * 1024, min_workgroups=64)["tile"] == LARGE
     assert mmq.mmq_plan(512, 4096, 4096, 160 * 1024, min_workgroups=65)["tile"] == SMALL
