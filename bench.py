@@ -562,8 +562,10 @@ def main() -> int:
     if args.copy_probe:
         return copy_probe(args.copy_probe)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this path has no multi-GPU mode "
-              "(how it would shard is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode. It would "
+              "shard by splitting the output features or the tokens over the GPUs, each "
+              "running the same kernels on its share (--sweep measures the 8-way shares)",
+              file=sys.stderr)
         return 2
 
     import torch
