@@ -59,7 +59,7 @@ enum mmq_tile {
   MMQ_TILE_SMALL = 2,  /* 32 tokens x 64 output features per workgroup, 2 wavefronts */
   MMQ_TILE_SKINNY = 3, /* 32 tokens x 32 output features per workgroup, K split over 8
                           wavefronts and summed in wavefront order (no block-dot output) */
-  MMQ_TILE_GEMV = 4    /* M <= 16 only: up to 4 tokens x 16 output features per workgroup of
+  MMQ_TILE_GEMV = 4    /* M <= 16 only: up to 8 tokens x 16 output features per workgroup of
                           8 wavefronts, integer dot products on the vector ALU (v_dot4_i32_i8),
                           K split over 16 slices x 2 halves of each super-block and summed in
                           a fixed order (no block-dot output) */

@@ -10,7 +10,7 @@
 // With one to sixteen tokens the product streams the weights once and does little else, so
 // matrix instructions buy nothing: the MFMA tiles of the other kernels are 32 tokens wide and
 // would be mostly padding. Here a workgroup of eight wavefronts owns 16 weight rows (half of a
-// repacked 32-row tile), all of K and a group of at most MT tokens. Lane l of wavefront w has
+// repacked 32-row tile), all of K and a group of at most MT (1, 2, 4 or 8) tokens. Lane l of wavefront w has
 // row l % 16 and K-slice 4 (w % 4) + l / 16; slice ks takes the super-blocks ks, ks + 16,
 // ks + 32, ..., of which wavefronts 0-3 take blocks 0-3 and wavefronts 4-7 blocks 4-7. So at
 // K = 4096 every lane owns half a super-block, the grid has N/16 workgroups (256 at N = 4096)
@@ -90,6 +90,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
   constexpr int kTokChunks = kGemvSlices * MT * 8;
   constexpr int kTokPerLane = (kTokChunks + 63) / 64;
   constexpr int kSc = kGemvSlices * MT * 4;
+  constexpr int kScPerLane = (kSc + 63) / 64;
   // fused: lane l quantizes 8 values of block (l % 16) / 4 of the half, quarter l % 4, of
   // slice l / 16
   const int fq = lane >> 4, fb = (lane & 15) >> 2, fc = lane & 3;
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
     float dsv[4];
     uint2 pc[3];     // dmv pieces of blocks 4 hf .. 4 hf + 3
     v4i tok[FUSED ? 1 : kTokPerLane];
-    float2 sc;       // (da, float(sa)) of entry lane (lane < kSc)
+    float2 sc[kScPerLane];  // (da, float(sa)) of entries lane + 64 t (below kSc)
     float4 xv[FUSED ? MT : 1][2];
   };
   auto load = [&](int i, Stage& st) {
@@ -138,13 +139,17 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
           st.tok[t] = *reinterpret_cast<const v4i*>(qs + (size_t)(m0 + cm) * K +
                                                     (size_t)cs * 256 + hf * 128 + part * 16);
       }
-      const int cq = lane / (4 * MT), cm = (lane / 4) % MT, b = 4 * hf + lane % 4;
-      const int cs = wq * kGemvSlices + cq + i * kGemvKS;
-      st.sc = make_float2(0.0f, 0.0f);
-      if (lane < kSc && cm < mc && cs < nsb) {
-        const uint32_t w = words[(size_t)(m0 + cm) * kb + (size_t)cs * 8 + b];
-        st.sc = make_float2(da_plane[((size_t)(cs * 8 + b) * M + m0 + cm) * 2],
-                            (float)((int)w >> 16));
+#pragma unroll
+      for (int t = 0; t < kScPerLane; ++t) {
+        const int c = lane + 64 * t;
+        const int cq = c / (4 * MT), cm = (c / 4) % MT, b = 4 * hf + c % 4;
+        const int cs = wq * kGemvSlices + cq + i * kGemvKS;
+        st.sc[t] = make_float2(0.0f, 0.0f);
+        if (c < kSc && cm < mc && cs < nsb) {
+          const uint32_t w = words[(size_t)(m0 + cm) * kb + (size_t)cs * 8 + b];
+          st.sc[t] = make_float2(da_plane[((size_t)(cs * 8 + b) * M + m0 + cm) * 2],
+                                 (float)((int)w >> 16));
+        }
       }
     }
   };
@@ -207,9 +212,13 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
           *reinterpret_cast<v4i*>(region + (c / (8 * MT)) * kSlice + (c % (8 * MT)) * 16) =
               cur.tok[t];
       }
-      if (lane < kSc)
-        *reinterpret_cast<float2*>(region + (lane / (4 * MT)) * kSlice + kTokBytes +
-                                   (lane % (4 * MT)) * 8) = cur.sc;
+#pragma unroll
+      for (int t = 0; t < kScPerLane; ++t) {
+        const int c = lane + 64 * t;
+        if (c < kSc)
+          *reinterpret_cast<float2*>(region + (c / (4 * MT)) * kSlice + kTokBytes +
+                                     (c % (4 * MT)) * 8) = cur.sc[t];
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -308,8 +317,8 @@ hipError_t launch_fused_mt(const float* x, const void* w_rep, float* C, int64_t 
 
 }  // namespace
 
-// tokens per workgroup for M tokens: M itself up to 4, else groups of 4
-int64_t gemv_group(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : 4); }
+// tokens per workgroup for M tokens: 1, 2, 4, then groups of 8
+int64_t gemv_group(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8)); }
 
 int64_t gemv_lds_bytes(int64_t M) {
   const int64_t mt = gemv_group(M);
@@ -326,7 +335,8 @@ hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t 
   switch (gemv_group(M)) {
     case 1: return launch_mt<1>(q8, w_rep, C, M, N, K, s);
     case 2: return launch_mt<2>(q8, w_rep, C, M, N, K, s);
-    default: return launch_mt<4>(q8, w_rep, C, M, N, K, s);
+    case 4: return launch_mt<4>(q8, w_rep, C, M, N, K, s);
+    default: return launch_mt<8>(q8, w_rep, C, M, N, K, s);
   }
 }
 
@@ -336,7 +346,8 @@ hipError_t launch_mmq_gemv_fused(const float* x, const void* w_rep, float* C, in
   switch (gemv_group(M)) {
     case 1: return launch_fused_mt<1>(x, w_rep, C, M, N, K, s);
     case 2: return launch_fused_mt<2>(x, w_rep, C, M, N, K, s);
-    default: return launch_fused_mt<4>(x, w_rep, C, M, N, K, s);
+    case 4: return launch_fused_mt<4>(x, w_rep, C, M, N, K, s);
+    default: return launch_fused_mt<8>(x, w_rep, C, M, N, K, s);
   }
 }
 

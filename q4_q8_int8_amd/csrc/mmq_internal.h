@@ -90,14 +90,13 @@ int64_t fused_lds_bytes();
 hipError_t launch_mmq_fused(const float* x, const void* w_rep, float* C, int64_t M, int64_t N,
                             int64_t K, hipStream_t s);
 
-// Vector-ALU product for a handful of tokens (decode): 16 weight rows and up to 4 tokens per
+// Vector-ALU product for a handful of tokens (decode): 16 weight rows and up to 8 tokens per
 // workgroup of kGemvWaves wavefronts, K split over 16 slices and each super-block over two
 // wavefronts, M <= kGemvMaxM.
 constexpr int kGemvWaves = 8;
 constexpr int kGemvRows = 16;  // weight rows per workgroup
 constexpr int kGemvMaxM = 16;
-// The guard's choice up to here: from 16 tokens (four token groups, each re-reading the
-// weights) the skinny MFMA kernel is faster.
+// The guard's choice up to here: at 16 tokens the skinny MFMA kernel is faster.
 constexpr int kGemvAutoMaxM = 8;
 int64_t gemv_group(int64_t M);  // tokens per workgroup
 int64_t gemv_lds_bytes(int64_t M);

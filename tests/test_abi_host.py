@@ -153,7 +153,7 @@ def test_blockdots_refuse_the_gemv_tile():
 
 
 @pytest.mark.parametrize("M,group,grid", [(1, 1, 256), (2, 2, 256), (3, 4, 256), (4, 4, 256),
-                                          (5, 4, 512), (16, 4, 1024)])
+                                          (5, 8, 256), (8, 8, 256), (9, 8, 512), (16, 8, 512)])
 def test_plan_gemv_tile(M, group, grid):
     auto = mmq.mmq_plan(M, 4096, 4096, 160 * 1024)
     assert (auto["tile"], auto["reason"]) == ((GEMV, mmq.MMQ_REASON_DECODE) if M <= 8 else
@@ -175,7 +175,7 @@ def test_plan_gemv_forced_limits():
         mmq.mmq_plan(17, 4096, 4096, 160 * 1024, force_tile=GEMV)
     assert e.value.status == mmq.MMQ_E_SHAPE
     with pytest.raises(mmq.MMQError) as e:
-        mmq.mmq_plan(16, 4096, 4096, 160 * 1024, force_tile=GEMV, opt_lds_budget=20991)
+        mmq.mmq_plan(16, 4096, 4096, 160 * 1024, force_tile=GEMV, opt_lds_budget=41471)
     assert e.value.status == mmq.MMQ_E_LDS
     # the vector-ALU tile needs the least LDS: under 6 KiB it is the only one that fits
     p = mmq.mmq_plan(1, 4096, 4096, 160 * 1024, opt_lds_budget=5632)
