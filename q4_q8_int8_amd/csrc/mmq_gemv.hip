@@ -27,8 +27,9 @@
 // its loads are issued before this one is computed. Read instead one token at a time with
 // scalar loads, each waited for before its dot products, the token data cost an L2 round trip
 // per token and pair of blocks. Per block, S is eight v_dot4_i32_i8 over 4 bytes each (both
-// operands signed; nibbles are 0..15), then
-//   u = fma(dmv, float(sa), float(S) * dsv),  acc = fma(u, da, acc).
+// operands signed; nibbles are 0..15) started at the bias word 0x4B400000, then
+//   u = fma(dmv, float(sa), fma(float(D), dsv, -1.5 * 2^23 * dsv)),  acc = fma(u, da, acc),
+// the inner fma being RN(S * dsv) (the biased sum is 1.5 * 2^23 + S exactly).
 //
 // Summation order per output: blocks in order within a half, super-blocks in order within a
 // (slice, half), then the 32 (slice, half) partial sums in order through LDS. Deterministic;
@@ -224,6 +225,12 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
     __builtin_amdgcn_wave_barrier();
     if (act) {
       const uint8_t* sl = region + q * kSlice;
+      // nds = -1.5 * 2^23 * dsv (exact): with the dot products started at the bias word
+      // 0x4B400000, whose float value is 1.5 * 2^23, fma(D, dsv, nds) = RN(S * dsv) in one
+      // instruction, as float(S) * dsv would be in two (|S| < 2^22 keeps D in one binade)
+      float nds[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) nds[b] = -kBiasF * cur.dsv[b];
       // dmv = p0 + p1 + p2, exact in f32
       float dmv[4];
 #pragma unroll
@@ -252,7 +259,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
             const v4i* tq = reinterpret_cast<const v4i*>(sl + m * 128 + gg * 64);
             const float4 sc =
                 *reinterpret_cast<const float4*>(sl + kTokBytes + (m * 4 + 2 * gg) * 8);
-            int S0 = 0, S1 = 0;
+            int S0 = kBiasBits, S1 = kBiasBits;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               const v4i a = tq[h], c = tq[2 + h];
@@ -262,11 +269,11 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
                 S1 = __builtin_amdgcn_sdot4(hi[4 * h + d], c[d], S1, false);
               }
             }
-            const float u0 = __builtin_fmaf(dmv[2 * gg], sc.y, (float)S0 * cur.dsv[2 * gg]);
-            acc[m] = __builtin_fmaf(u0, sc.x, acc[m]);
-            const float u1 =
-                __builtin_fmaf(dmv[2 * gg + 1], sc.w, (float)S1 * cur.dsv[2 * gg + 1]);
-            acc[m] = __builtin_fmaf(u1, sc.z, acc[m]);
+            const float t0 = __builtin_fmaf(__int_as_float(S0), cur.dsv[2 * gg], nds[2 * gg]);
+            acc[m] = __builtin_fmaf(__builtin_fmaf(dmv[2 * gg], sc.y, t0), sc.x, acc[m]);
+            const float t1 =
+                __builtin_fmaf(__int_as_float(S1), cur.dsv[2 * gg + 1], nds[2 * gg + 1]);
+            acc[m] = __builtin_fmaf(__builtin_fmaf(dmv[2 * gg + 1], sc.w, t1), sc.z, acc[m]);
           }
         }
       }
