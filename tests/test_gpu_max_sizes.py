@@ -83,13 +83,22 @@ def test_mmq_largest_k():
     say("mmq largest K: quantize, repack", M, N, K)
     mmq.quantize_q8_1(to_dev(x), M, K, q8)
     mmq.repack_q4_K(to_dev(w), N, K, rep)
-    for tile in (mmq.MMQ_TILE_SKINNY, mmq.MMQ_TILE_SMALL, mmq.MMQ_TILE_LARGE):
+    out = {}
+    for tile in (mmq.MMQ_TILE_SKINNY, mmq.MMQ_TILE_SMALL, mmq.MMQ_TILE_LARGE, mmq.MMQ_TILE_GEMV):
         say("mmq largest K", tile)
         C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
         mmq.mmq_q4K_q8_1_ex(M, N, K, q8, rep, C, force_tile=tile)
         torch.cuda.synchronize()
-        r = assert_within_tolerance(C.cpu().numpy(), C_ref, T)
+        out[tile] = C.cpu().numpy()
+        r = assert_within_tolerance(out[tile], C_ref, T)
         say("max |err|/T", r)
+    # the decode kernel quantizing its own activations: bit for bit the two-step result
+    say("mmq_q4K_f32 largest K")
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    mmq.mmq_q4K_f32(M, N, K, to_dev(x), rep, C)
+    torch.cuda.synchronize()
+    assert mmq.mmq_last_kernel()["tile"] == mmq.MMQ_TILE_GEMV
+    assert np.array_equal(C.cpu().numpy().view(np.uint32), out[mmq.MMQ_TILE_GEMV].view(np.uint32))
 
 
 def test_gemm_f16_largest():
