@@ -10,14 +10,14 @@
 // With one to sixteen tokens the product streams the weights once and does little else, so
 // matrix instructions buy nothing: the MFMA tiles of the other kernels are 32 tokens wide and
 // would be mostly padding. Here a workgroup of eight wavefronts owns 16 weight rows (half of a
-// repacked 32-row tile), all of K and a group of at most MT (1, 2, 4 or 8) tokens. Lane l of wavefront w has
-// row l % 16 and K-slice 4 (w % 4) + l / 16; slice ks takes the super-blocks ks, ks + 16,
-// ks + 32, ..., of which wavefronts 0-3 take blocks 0-3 and wavefronts 4-7 blocks 4-7. So at
-// K = 4096 every lane owns half a super-block, the grid has N/16 workgroups (256 at N = 4096)
-// per token group, and two wavefronts per SIMD overlap one's loads with the other's dot
-// products. Token groups are separate workgroups, so that more tokens bring more workgroups
-// rather than longer wavefronts; the groups of one row block read the same weights, mostly
-// from L2.
+// repacked 32-row tile), all of K and a group of at most MT (1, 2, 4 or 8) tokens. Lane l of
+// wavefront w has row l % 16 and K-slice 4 (w % 4) + l / 16; slice ks takes the super-blocks
+// ks, ks + 16, ks + 32, ..., of which wavefronts 0-3 take blocks 0-3 and wavefronts 4-7 blocks
+// 4-7. So at K = 4096 every lane owns half a super-block, the grid has N/16 workgroups (256 at
+// N = 4096) per token group, and two wavefronts per SIMD overlap one's loads with the other's
+// dot products. Token groups are separate workgroups, so that more tokens bring more
+// workgroups rather than longer wavefronts; the groups of one row block read the same weights,
+// mostly from L2.
 //
 // Per step a lane loads its row's 64 nibble bytes of its half, its 4 scales dsv and the three
 // bf16 pieces of its 4 mins dmv (buffer loads; the 16 lanes of a slice read 256 contiguous
@@ -116,7 +116,8 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
 #pragma unroll
     for (int p = 0; p < 3; ++p)
       st.pc[p] = __builtin_bit_cast(
-          uint2, buf_load_f32x2(rw, rec + kRepNibBytes + kRepDsvBytes + p * 512 + j * 16 + hf * 8));
+          uint2,
+          buf_load_f32x2(rw, rec + kRepNibBytes + kRepDsvBytes + p * 512 + j * 16 + hf * 8));
     if constexpr (FUSED) {
       const int cs = wq * kGemvSlices + fq + i * kGemvKS;
 #pragma unroll
