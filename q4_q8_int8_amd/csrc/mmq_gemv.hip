@@ -67,7 +67,14 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
   constexpr int kRegion = kGemvSlices * kSlice;
   static_assert(kGemvWaves * kRegion >= kGemvKS * 2 * MT * kGemvRows * 4, "partial sums fit");
   __shared__ __align__(16) uint8_t smem[kGemvWaves * kRegion];
-  const int rb = (int)(blockIdx.x / (unsigned)groups);        // row block: rows 16rb..16rb+15
+  // Row block rb (rows 16rb..16rb+15). Workgroups go to the 8 XCDs in turn, so slot u runs on
+  // XCD (u * groups + group) % 8; pairing slots u and u + 8 with the two halves of one 32-row
+  // tile puts both on one XCD, whose L2 then serves the cache lines the halves share (their
+  // dsv rows) once. A last partial run of 16 slots keeps the plain order.
+  const int u = (int)(blockIdx.x / (unsigned)groups);
+  const int nrb = (N + kGemvRows - 1) / kGemvRows;
+  int rb = u;
+  if (u < nrb / 16 * 16) rb = (u & ~15) + 2 * (u & 7) + ((u >> 3) & 1);
   const int m0 = (int)(blockIdx.x % (unsigned)groups) * MT;  // first token of the group
   const int mc = M - m0 < MT ? M - m0 : MT;                    // tokens in the group
   const int lane = threadIdx.x & 63;
