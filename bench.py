@@ -25,6 +25,8 @@ same kernel source (null once the kernel has changed since the counters were tak
 The line also carries `comparator_f16`: the same workload through the f16 comparator path
 (convert_f32_f16, dequantize_q4_K_f16, gemm_f16), each kernel timed the same way, and the
 two whole paths: per call, and with the weights resident in f16. `--no-f16` skips it.
+`decode_m1` adds the one-token product against the same weights' shape (1 x 4096 x 4096) as
+`--decode` times it; `--no-decode` skips it.
 
 `--sweep` prints one line per configuration and tile instead, and `--decode` one line per
 few-token shape (vector-ALU tile, skinny tile, fused call); neither is the benchmark line.
@@ -408,6 +410,25 @@ DECODE_SHAPES = [(1, 4096, 4096), (2, 4096, 4096), (4, 4096, 4096), (8, 4096, 40
                  (1, 11008, 4096), (1, 4096, 11008)]
 
 
+def decode_m1(args) -> dict:
+    """One token against the q-proj weights (1 x 4096 x 4096), as --decode times it: not the
+    benchmark's workload, a second line of sight on the few-token kernels."""
+    import synth
+    import q4_q8_int8_amd as mmq
+    M, N, K = 1, 4096, 4096
+    W = {"M": M, "N": N, "K": K, "x": synth.activations("normal_outliers", M, K, 1500 + M),
+         "w": synth.q4k_weights("fit", N, K, 2004)[0]}
+    R = rotation(M, N, K, args.rotate)
+    t = measure(W, R, args.steps, args.warmup, mmq.MMQ_TILE_GEMV)
+    fu = measure_fused(W, R, args.steps, args.warmup)
+    wbytes = mmq.mmq_q4K_repacked_bytes(N, K)
+    return {"shape": "1 x 4096 x 4096", "rotate": R,
+            "fused_call_graph_us": round(fu["graph_us"], 2),
+            "gemv_graph_us": round(t["graph_gemm_us"], 2),
+            "gemv_weights_tbps": round(wbytes / (t["graph_gemm_us"] * 1e-6) / 1e12, 2),
+            "quantize_then_gemv_graph_us": round(t["graph_step_us"], 2)}
+
+
 def decode(args) -> int:
     """Few-token products (decode shapes of a 7B layer): each shape under the vector-ALU tile
     and the skinny tile, and through the fused call, with inputs rotated beyond the
@@ -550,6 +571,8 @@ def main() -> int:
                     help="only run a plain device copy of MIB MiB (calibrates HBM byte counters)")
     ap.add_argument("--no-f16", action="store_true",
                     help="skip the f16 comparator path's timing")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the one-token (decode) entry of the benchmark line")
     ap.add_argument("--decode", action="store_true",
                     help="few-token shapes: vector-ALU vs skinny tile vs fused call, one JSON "
                          "line per shape")
@@ -627,6 +650,8 @@ def main() -> int:
     }
     if not args.no_f16:
         out["comparator_f16"] = f16_summary(M, N, K, measure_f16(W, R, args.steps, args.warmup))
+    if not args.no_decode:
+        out["decode_m1"] = decode_m1(args)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(W)
     print(json.dumps(out), flush=True)
