@@ -407,7 +407,7 @@ def rotation(M: int, N: int, K: int, r_min: int) -> int:
 
 
 DECODE_SHAPES = [(1, 4096, 4096), (2, 4096, 4096), (4, 4096, 4096), (8, 4096, 4096),
-                 (1, 11008, 4096), (1, 4096, 11008)]
+                 (16, 4096, 4096), (1, 11008, 4096), (1, 4096, 11008)]
 
 
 def decode_m1(args) -> dict:
@@ -430,7 +430,7 @@ def decode_m1(args) -> dict:
 
 
 def decode(args) -> int:
-    """Few-token products (decode shapes of a 7B layer): each shape under the vector-ALU tile
+    """Few-token products (decode shapes of a 7B layer): each shape under the decode tile
     and the skinny tile, and through the fused call, with inputs rotated beyond the
     last-level cache. One JSON line per shape; --shape M,N,K runs one shape only."""
     import synth

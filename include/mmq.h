@@ -59,10 +59,13 @@ enum mmq_tile {
   MMQ_TILE_SMALL = 2,  /* 32 tokens x 64 output features per workgroup, 2 wavefronts */
   MMQ_TILE_SKINNY = 3, /* 32 tokens x 32 output features per workgroup, K split over 8
                           wavefronts and summed in wavefront order (no block-dot output) */
-  MMQ_TILE_GEMV = 4    /* M <= 16 only: up to 8 tokens x 16 output features per workgroup of
-                          8 wavefronts, integer dot products on the vector ALU (v_dot4_i32_i8),
-                          K split over 16 slices x 2 halves of each super-block and summed in
-                          a fixed order (no block-dot output) */
+  MMQ_TILE_GEMV = 4    /* M <= 16 only (decode), 16 output features per workgroup of 8
+                          wavefronts, partial sums added in a fixed order, no block-dot output.
+                          M <= 8: up to 8 tokens per workgroup, integer dot products on the
+                          vector ALU (v_dot4_i32_i8), K split over 16 slices x 2 halves of each
+                          super-block. 9 <= M <= 16: all tokens in one workgroup, one
+                          v_mfma_i32_16x16x32_i8 per block, K split over the wavefronts by
+                          super-block */
 };
 
 /* Why the guard chose what it chose. */
@@ -73,13 +76,13 @@ enum mmq_reason {
   MMQ_REASON_LDS_FALLBACK = 3,  /* the large tile does not fit the LDS budget: small tile */
   MMQ_REASON_FORCED = 4,        /* the caller's options asked for this tile */
   MMQ_REASON_NO_FIT = 5,        /* nothing fits the budget: refused with MMQ_E_LDS */
-  MMQ_REASON_FEW_TOKENS = 6,    /* 8 < M <= 128, K >= 2048, and the large grid would leave compute
+  MMQ_REASON_FEW_TOKENS = 6,    /* 16 < M <= 128, K >= 2048, and the large grid would leave compute
                                    units idle:
                                    the skinny kernel, which splits K over wavefronts */
   MMQ_REASON_FUSED = 7,         /* mmq_q4K_f32: the vector-ALU (M <= 8) or skinny kernel quantizing
                                    its own activations */
-  MMQ_REASON_DECODE = 8         /* M <= 8: the vector-ALU kernel, which streams the weights once
-                                   without the MFMA tiles' 32-token padding */
+  MMQ_REASON_DECODE = 8         /* M <= 16: the decode tile, which streams the weights once
+                                   without the large MFMA tiles' 32-token padding */
 };
 
 /* Optional knobs for the _ex entry points (NULL = defaults). */
@@ -227,7 +230,7 @@ int mmq_q4K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, cons
 /*
  * mmq_plan: the LDS-budget guard as a pure host function (no device access). Chooses the
  * tile for an M x N x K product given `lds_budget` bytes per workgroup (opt->lds_budget,
- * when set, takes precedence): for M <= 8 the vector-ALU kernel (MMQ_TILE_GEMV, reason
+ * when set, takes precedence): for M <= 16 the decode tile (MMQ_TILE_GEMV, reason
  * MMQ_REASON_DECODE); else the large tile when it fits and its grid has at least
  * opt->min_workgroups workgroups (default 256, the MI355X compute-unit count; a GEMM call
  * uses the device's count); else, for M <= 128 and K >= 2048 (at least one super-block for

@@ -36,7 +36,7 @@ MMQ_TILE_AUTO, MMQ_TILE_LARGE, MMQ_TILE_SMALL, MMQ_TILE_SKINNY, MMQ_TILE_GEMV = 
 (MMQ_REASON_NONE, MMQ_REASON_LARGE, MMQ_REASON_SMALL_GRID, MMQ_REASON_LDS_FALLBACK,
  MMQ_REASON_FORCED, MMQ_REASON_NO_FIT, MMQ_REASON_FEW_TOKENS, MMQ_REASON_FUSED,
  MMQ_REASON_DECODE) = range(9)
-GEMV_MAX_M = 16  # largest M of the vector-ALU tile (the guard chooses it up to M = 8)
+GEMV_MAX_M = 16  # largest M of the decode tile, which the guard chooses up to there
 QK8, QK_K, Q4K_BLOCK_BYTES, REP_TILE_ROWS, REP_TILE_BYTES = 32, 256, 144, 32, 6656
 
 

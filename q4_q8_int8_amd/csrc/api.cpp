@@ -146,7 +146,7 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
     if (mmq::skinny_lds_bytes() <= budget) { tile = MMQ_TILE_SKINNY; reason = MMQ_REASON_FORCED; }
   } else if (forced == MMQ_TILE_GEMV) {
     if (M > mmq::kGemvMaxM)
-      return fail(MMQ_E_SHAPE, "the vector-ALU tile takes M <= %d (M = %lld)", mmq::kGemvMaxM,
+      return fail(MMQ_E_SHAPE, "the decode tile takes M <= %d (M = %lld)", mmq::kGemvMaxM,
                   (long long)M);
     if (mmq::gemv_lds_bytes(M) <= budget) { tile = MMQ_TILE_GEMV; reason = MMQ_REASON_FORCED; }
   } else if (M <= mmq::kGemvAutoMaxM && mmq::gemv_lds_bytes(M) <= budget) {
@@ -329,9 +329,9 @@ int mmq_q4K_f32(int64_t M, int64_t N, int64_t K, const float* x, const void* w_r
     return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
   DeviceInfo* di;
   if ((st = current_device(&di))) return st;
-  // up to kGemvAutoMaxM tokens the vector-ALU kernel, else the skinny one, each quantizing
+  // up to kGemvFusedMaxM tokens the vector-ALU kernel, else the skinny one, each quantizing
   // the activations itself
-  const bool gemv = M <= mmq::kGemvAutoMaxM;
+  const bool gemv = M <= mmq::kGemvFusedMaxM;
   mmq_kernel_info info = {};
   info.reason = MMQ_REASON_FUSED;
   info.lds_budget = di->lds_budget;

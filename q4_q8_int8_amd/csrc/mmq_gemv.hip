@@ -306,6 +306,126 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
   }
 }
 
+// 9 to 16 tokens: the vector ALU's dot products set the time there, so one 32-block of 16
+// weight rows x 16 tokens becomes one v_mfma_i32_16x16x32_i8 (no padding at 16 tokens; token
+// columns past M read zero). A workgroup of 8 wavefronts owns 16 weight rows (paired on one
+// XCD as above) and all of K; wavefront w takes the super-blocks w, w + 8, w + 16, ..., each
+// one's loads issued before the previous one is computed. Per block a lane holds, for its token
+// l % 16, the four outputs of rows 4 (l / 16) .. + 3, and rescales them as the GEMM does:
+// y = fma(D, da, nda) with D biased by 0x4B400000, acc = fma(y, dsv, acc). term2 of a
+// super-block is a K = 8 product of dmv and da*sa; as in the GEMM it runs on the bf16 matrix
+// unit from the exact three-piece splits stored in the record and in the q8 buffer: two
+// v_mfma_f32_16x16x32_bf16 whose 4 k-groups of 8 blocks carry the piece pairs (0,0) (0,1)
+// (1,0) (0,2) | (1,1) (2,0) (and two zero groups), added into the same accumulator. The 8
+// wavefronts' partial sums are added in wavefront order through LDS.
+// Operand layout of both instructions: A row l % 16 and B column l % 16 take the 8 k values
+// 8 (l / 16) .. + 7; the result of row 4 (l / 16) + r, column l % 16 is register r of lane l.
+__global__ __launch_bounds__(512) void mmq_gemv_mfma_kernel(
+    const int8_t* __restrict__ qs, const float* __restrict__ da_plane,
+    const uint16_t* __restrict__ tpieces, const uint8_t* __restrict__ wrep,
+    float* __restrict__ C, int M, int N, int K) {
+  __shared__ float red[8][16][16];  // [wavefront][token][row]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int u = (int)blockIdx.x;
+  const int nrb = (N + kGemvRows - 1) / kGemvRows;
+  int rb = u;
+  if (u < nrb / 16 * 16) rb = (u & ~15) + 2 * (u & 7) + ((u >> 3) & 1);
+  const int nsb = K >> 8;
+  const int c16 = lane & 15, kg = lane >> 4;   // operand row / token column, k-group
+  const int j_op = (rb & 1) * 16 + c16;        // A operand row within the 32-row tile
+  const int j_out = (rb & 1) * 16 + 4 * kg;    // first of this lane's 4 output rows in the tile
+  // term2 piece pairs of this lane's k-group: (ia1, jb1) in the first instruction, (ia2, jb2)
+  // in the second (k-groups 2 and 3 of the second are zero)
+  const int ia1 = kg == 2 ? 1 : 0, jb1 = kg == 1 ? 1 : (kg == 3 ? 2 : 0);
+  const int ia2 = kg == 1 ? 2 : 1, jb2 = kg == 0 ? 1 : 0;
+  const bool t2 = kg < 2;
+  const uint8_t* wtile = wrep + (size_t)(rb >> 1) * (size_t)nsb * kRepTileBytes;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wtile, (uint32_t)nsb * (uint32_t)kRepTileBytes);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qs, (uint32_t)M * (uint32_t)K);
+  const __amdgpu_buffer_rsrc_t rda = make_rsrc(da_plane, (uint32_t)M * (uint32_t)(K >> 5) * 8u);
+  const __amdgpu_buffer_rsrc_t rtp = make_rsrc(tpieces, (uint32_t)M * (uint32_t)nsb * 48u);
+  v4i bias = {kBiasBits, kBiasBits, kBiasBits, kBiasBits};
+  asm volatile("" : "+v"(bias));
+
+  struct Stage {
+    uint2 nb[4];     // nibble bytes of A row j_op, k-group kg, of block pairs 0..3
+    float4 dsv[8];   // rows j_out .. j_out + 3 of each block
+    uint2 tb[8];     // token c16, k-group kg, of each block (zero past M)
+    float2 dap[8];   // (da, nda) of token c16 and each block
+    v4i pa[2], pb[2];  // term2 operands: dmv piece of row j_op, da*sa piece of token c16
+  };
+  auto load = [&](int s, Stage& st) {
+    const uint32_t rec = (uint32_t)s * kRepTileBytes;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      st.nb[g] = __builtin_bit_cast(
+          uint2, buf_load_f32x2(rw, rec + g * 1024 + (kg >> 1) * 512 + j_op * 16 + (kg & 1) * 8));
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+      st.dsv[b] =
+          __builtin_bit_cast(float4, buf_load16(rw, rec + kRepNibBytes + b * 128 + j_out * 4));
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+      st.tb[b] = __builtin_bit_cast(
+          uint2, buf_load_f32x2(rq, (uint32_t)c16 * (uint32_t)K + (uint32_t)s * 256 + b * 32 +
+                                        kg * 8));
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+      st.dap[b] = buf_load_f32x2(rda, (((uint32_t)s * 8 + b) * (uint32_t)M + c16) * 8u);
+    const uint32_t wp = rec + kRepNibBytes + kRepDsvBytes + j_op * 16;
+    st.pa[0] = buf_load16(rw, wp + ia1 * 512);
+    st.pa[1] = buf_load16(rw, wp + ia2 * 512);
+    st.pb[0] = buf_load16(rtp, (((uint32_t)s * 3 + jb1) * (uint32_t)M + c16) * 16u);
+    st.pb[1] = buf_load16(rtp, (((uint32_t)s * 3 + jb2) * (uint32_t)M + c16) * 16u);
+    if (!t2) st.pa[1] = v4i{0, 0, 0, 0};
+  };
+
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  Stage cur, nxt;
+  if (wave < nsb) load(wave, cur);
+  for (int s = wave; s < nsb; s += 8) {
+    if (s + 8 < nsb) load(s + 8, nxt);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const uint2 w = cur.nb[b >> 1];
+      const uint2 a = (b & 1) ? make_uint2((w.x >> 4) & 0x0F0F0F0Fu, (w.y >> 4) & 0x0F0F0F0Fu)
+                              : make_uint2(w.x & 0x0F0F0F0Fu, w.y & 0x0F0F0F0Fu);
+      const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, a),
+                                                          __builtin_bit_cast(long, cur.tb[b]),
+                                                          bias, 0, 0, 0);
+      const float dsvb[4] = {cur.dsv[b].x, cur.dsv[b].y, cur.dsv[b].z, cur.dsv[b].w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float y = __builtin_fmaf(__int_as_float(D[r]), cur.dap[b].x, cur.dap[b].y);
+        acc[r] = __builtin_fmaf(y, dsvb[r], acc[r]);
+      }
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, cur.pa[0]),
+                                                  __builtin_bit_cast(v8bf, cur.pb[0]), acc, 0,
+                                                  0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, cur.pa[1]),
+                                                  __builtin_bit_cast(v8bf, cur.pb[1]), acc, 0,
+                                                  0, 0);
+    cur = nxt;
+  }
+
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][c16][4 * kg + r] = acc[r];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int t = threadIdx.x >> 4, rr = threadIdx.x & 15;
+    const int n = rb * kGemvRows + rr;
+    if (t < M && n < N) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) v += red[w][t][rr];
+      C[(size_t)t * N + n] = v;
+    }
+  }
+}
+
 template <int MT>
 hipError_t launch_mt(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N, int64_t K,
                      hipStream_t s) {
@@ -333,9 +453,10 @@ hipError_t launch_fused_mt(const float* x, const void* w_rep, float* C, int64_t 
 }  // namespace
 
 // tokens per workgroup for M tokens: 1, 2, 4, then groups of 8
-int64_t gemv_group(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8)); }
+int64_t gemv_group(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 8 : 16))); }
 
 int64_t gemv_lds_bytes(int64_t M) {
+  if (M > 8) return 8 * 16 * 16 * 4;  // the matrix-unit kernel: partial sums only
   const int64_t mt = gemv_group(M);
   return (int64_t)kGemvWaves * kGemvSlices * (mt * 160 + 16);
 }
@@ -347,6 +468,15 @@ int64_t gemv_grid(int64_t M, int64_t N) {
 hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
                            int64_t K, hipStream_t s) {
   if (M < 1 || M > kGemvMaxM) return hipErrorInvalidValue;
+  if (M > 8) {
+    const uint8_t* base = static_cast<const uint8_t*>(q8);
+    hipLaunchKernelGGL(mmq_gemv_mfma_kernel, dim3((unsigned)gemv_grid(M, N)), dim3(512), 0, s,
+                       reinterpret_cast<const int8_t*>(base),
+                       reinterpret_cast<const float*>(base + q8_planes_offset(M, K)),
+                       reinterpret_cast<const uint16_t*>(base + q8_pieces_offset(M, K)),
+                       static_cast<const uint8_t*>(w_rep), C, (int)M, (int)N, (int)K);
+    return hipGetLastError();
+  }
   switch (gemv_group(M)) {
     case 1: return launch_mt<1>(q8, w_rep, C, M, N, K, s);
     case 2: return launch_mt<2>(q8, w_rep, C, M, N, K, s);
@@ -357,7 +487,7 @@ hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t 
 
 hipError_t launch_mmq_gemv_fused(const float* x, const void* w_rep, float* C, int64_t M,
                                  int64_t N, int64_t K, hipStream_t s) {
-  if (M < 1 || M > kGemvMaxM) return hipErrorInvalidValue;
+  if (M < 1 || M > 8) return hipErrorInvalidValue;  // the fused form exists up to 8 tokens
   switch (gemv_group(M)) {
     case 1: return launch_fused_mt<1>(x, w_rep, C, M, N, K, s);
     case 2: return launch_fused_mt<2>(x, w_rep, C, M, N, K, s);

@@ -90,14 +90,19 @@ int64_t fused_lds_bytes();
 hipError_t launch_mmq_fused(const float* x, const void* w_rep, float* C, int64_t M, int64_t N,
                             int64_t K, hipStream_t s);
 
-// Vector-ALU product for a handful of tokens (decode): 16 weight rows and up to 8 tokens per
-// workgroup of kGemvWaves wavefronts, K split over 16 slices and each super-block over two
-// wavefronts, M <= kGemvMaxM.
+// Product for a handful of tokens (decode), M <= kGemvMaxM, 16 weight rows per workgroup of
+// kGemvWaves wavefronts. Up to 8 tokens: integer dot products on the vector ALU, up to 8
+// tokens per workgroup, K split over 16 slices and each super-block over two wavefronts.
+// 9 to 16 tokens: one 16 x 16 x 32 int8 MFMA per block, all tokens in one workgroup, K split
+// over the wavefronts by super-block.
 constexpr int kGemvWaves = 8;
 constexpr int kGemvRows = 16;  // weight rows per workgroup
 constexpr int kGemvMaxM = 16;
-// The guard's choice up to here: at 16 tokens the skinny MFMA kernel is faster.
-constexpr int kGemvAutoMaxM = 8;
+// The guard's choice up to here (at 16 tokens, K = N = 4096: 10.4 against the skinny
+// kernel's 11.6 us).
+constexpr int kGemvAutoMaxM = 16;
+// The variant that quantizes its activations itself: vector-ALU form only.
+constexpr int kGemvFusedMaxM = 8;
 int64_t gemv_group(int64_t M);  // tokens per workgroup
 int64_t gemv_lds_bytes(int64_t M);
 int64_t gemv_grid(int64_t M, int64_t N);

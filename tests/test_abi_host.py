@@ -90,11 +90,12 @@ REASON = {LARGE: mmq.MMQ_REASON_LARGE, SMALL: mmq.MMQ_REASON_SMALL_GRID,
 
 
 @pytest.mark.parametrize("M,N,tile", [
-    (1, 4096, GEMV),        # decode: the vector-ALU kernel
+    (1, 4096, GEMV),        # decode: the vector-ALU form of the decode tile
     (8, 4096, GEMV),
     (1, 65536, GEMV),       # whatever the large grid would be
-    (9, 4096, SKINNY),      # large grid 1 x 16, few tokens
-    (16, 4096, SKINNY),
+    (9, 4096, GEMV),        # the matrix-unit form
+    (16, 4096, GEMV),
+    (17, 4096, SKINNY),     # large grid 1 x 16, few tokens
     (128, 4096, SKINNY),
     (129, 4096, SMALL),     # 2 x 16
     (512, 4096, SMALL),     # 4 x 16 = 64 < 256 compute units
@@ -112,8 +113,8 @@ def test_plan_prefers_a_grid_that_fills_the_gpu(M, N, tile):
 
 @pytest.mark.parametrize("M,N,K,tile", [
     (128, 256, 512, SMALL),     # 2 super-blocks for the skinny kernel's 8 wavefronts
-    (16, 4096, 1792, SMALL),    # 7
-    (16, 4096, 2048, SKINNY),   # 8: one each
+    (32, 4096, 1792, SMALL),    # 7
+    (32, 4096, 2048, SKINNY),   # 8: one each
     (128, 256, 2048, SKINNY),
 ])
 def test_plan_skinny_needs_a_super_block_per_wavefront(M, N, K, tile):
@@ -153,19 +154,26 @@ def test_blockdots_refuse_the_gemv_tile():
 
 
 @pytest.mark.parametrize("M,group,grid", [(1, 1, 256), (2, 2, 256), (3, 4, 256), (4, 4, 256),
-                                          (5, 8, 256), (8, 8, 256), (9, 8, 512), (16, 8, 512)])
+                                          (5, 8, 256), (8, 8, 256), (9, 16, 256), (16, 16, 256)])
 def test_plan_gemv_tile(M, group, grid):
     auto = mmq.mmq_plan(M, 4096, 4096, 160 * 1024)
-    assert (auto["tile"], auto["reason"]) == ((GEMV, mmq.MMQ_REASON_DECODE) if M <= 8 else
+    assert (auto["tile"], auto["reason"]) == ((GEMV, mmq.MMQ_REASON_DECODE) if M <= 16 else
                                               (SKINNY, mmq.MMQ_REASON_FEW_TOKENS))
     p = mmq.mmq_plan(M, 4096, 4096, 160 * 1024, force_tile=GEMV)
     assert p["tile"] == GEMV
     assert p["block_m"] == group and p["block_n"] == 16 and p["threads"] == 512
-    # per wavefront and K-slice: its half's 128 token bytes and 4 (da, sa) pairs per token,
-    # 16 padding
-    assert p["lds_bytes"] == 8 * 4 * (160 * group + 16) and p["grid"] == grid
+    # up to 8 tokens, per wavefront and K-slice: its half's 128 token bytes and 4 (da, sa)
+    # pairs per token, 16 padding; from 9 tokens (the matrix-unit form) the partial sums only
+    lds = 8 * 4 * (160 * group + 16) if group <= 8 else 8 * 16 * 16 * 4
+    assert p["lds_bytes"] == lds and p["grid"] == grid
     # ragged N: 4097 rows make 257 blocks of 16
     assert mmq.mmq_plan(M, 4097, 256, 160 * 1024, force_tile=GEMV)["grid"] == 257 * (grid // 256)
+
+
+def test_plan_above_decode_tile_is_skinny():
+    """From 17 tokens the guard leaves the decode tile for the skinny one (K >= 2048)."""
+    p = mmq.mmq_plan(17, 4096, 4096, 160 * 1024)
+    assert (p["tile"], p["reason"]) == (SKINNY, mmq.MMQ_REASON_FEW_TOKENS)
 
 
 def test_plan_gemv_forced_limits():
@@ -175,7 +183,7 @@ def test_plan_gemv_forced_limits():
         mmq.mmq_plan(17, 4096, 4096, 160 * 1024, force_tile=GEMV)
     assert e.value.status == mmq.MMQ_E_SHAPE
     with pytest.raises(mmq.MMQError) as e:
-        mmq.mmq_plan(16, 4096, 4096, 160 * 1024, force_tile=GEMV, opt_lds_budget=41471)
+        mmq.mmq_plan(8, 4096, 4096, 160 * 1024, force_tile=GEMV, opt_lds_budget=41471)
     assert e.value.status == mmq.MMQ_E_LDS
     # the vector-ALU tile needs the least LDS: under 6 KiB it is the only one that fits
     p = mmq.mmq_plan(1, 4096, 4096, 160 * 1024, opt_lds_budget=5632)

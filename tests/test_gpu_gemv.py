@@ -1,8 +1,9 @@
 """The vector-ALU tile for a handful of tokens (MMQ_TILE_GEMV) against the CPU oracle.
 
 Bar: f32 outputs within 1e-5 * T per element (T from the oracle, float64), every element;
-results deterministic. The tile is the guard's choice for M <= 8 (so the token sweep's M = 1
-shape runs through it by default) and can be forced up to M = 16.
+results deterministic. The tile is the guard's choice for M <= 16 (vector-ALU dot products up
+to M = 8, a 16 x 16 int8 MFMA per block from M = 9), so the token sweep's M = 1 and M = 16
+shapes run through it by default.
 """
 import numpy as np
 import pytest
@@ -46,16 +47,16 @@ def _check(M, N, K, seed, kind="normal_outliers", wkind="random_fields", force=G
 
 @pytest.mark.parametrize("name", ["sweep_m1", "sweep_m16"])
 def test_gemv_decode_shapes_every_element(name):
-    """The token sweep's decode shapes: M = 1 by the guard's own choice, M = 16 forced."""
+    """The token sweep's decode shapes, M = 1 and M = 16, by the guard's own choice."""
     W = workload(name)
     M, N, K = W["M"], W["N"], W["K"]
     q8 = gpu_quantize(W["x"])
     rep = gpu_repack(W["w"], N, K)
     say("gemv", name, (M, N, K))
-    C = gpu_mmq(M, N, K, q8, rep, force_tile=0 if M <= 8 else GEMV)
+    C = gpu_mmq(M, N, K, q8, rep, force_tile=0)
     info = mmq.mmq_last_kernel()
     assert info["tile"] == GEMV
-    assert info["reason"] == (mmq.MMQ_REASON_DECODE if M <= 8 else mmq.MMQ_REASON_FORCED)
+    assert info["reason"] == mmq.MMQ_REASON_DECODE
     _, T = oracle.mmq_terms(oracle_q8(name), oracle_w(name))
     r = assert_within_tolerance(C, oracle.mmq(oracle_q8(name), oracle_w(name)), T)
     say("max |err|/T", r)
