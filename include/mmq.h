@@ -59,11 +59,11 @@ enum mmq_tile {
   MMQ_TILE_SMALL = 2,  /* 32 tokens x 64 output features per workgroup, 2 wavefronts */
   MMQ_TILE_SKINNY = 3, /* 32 tokens x 32 output features per workgroup, K split over 8
                           wavefronts and summed in wavefront order (no block-dot output) */
-  MMQ_TILE_GEMV = 4    /* M <= 16 only (decode), 16 output features per workgroup of 8
-                          wavefronts, partial sums added in a fixed order, no block-dot output.
-                          M <= 8: up to 8 tokens per workgroup, integer dot products on the
+  MMQ_TILE_GEMV = 4    /* M <= 16 only (decode), 16 output features per workgroup, partial
+                          sums added in a fixed order, no block-dot output. M <= 8: 8
+                          wavefronts, up to 8 tokens per workgroup, integer dot products on the
                           vector ALU (v_dot4_i32_i8), K split over 16 slices x 2 halves of each
-                          super-block. 9 <= M <= 16: all tokens in one workgroup, one
+                          super-block. 9 <= M <= 16: 16 wavefronts, all tokens in one workgroup, one
                           v_mfma_i32_16x16x32_i8 per block, K split over the wavefronts by
                           super-block */
 };
@@ -203,9 +203,9 @@ int mmq_q4K_q8_1_ex(int64_t M, int64_t N, int64_t K, const void* q8, const void*
  * then runs the unfused kernel's arithmetic on them. Every workgroup that needs a token's
  * super-block repeats that quantization, so the call is limited to few tokens:
  * 1 <= M <= 128. It pays for the fewest: at K = N = 4096, replayed from a graph over weights
- * that do not stay in cache, one call takes 5.9, 6.9 and 9.0 us at M = 1, 2 and 4, against
- * 8.4, 8.7 and 9.3 us for quantize_q8_1 followed by the vector-ALU tile; from M = 8
- * the two kernels are faster (11.1 against 13.2 us).
+ * that do not stay in cache, one call takes 6.0, 7.0 and 9.1 us at M = 1, 2 and 4, against
+ * 8.4, 8.7 and 9.4 us for quantize_q8_1 followed by the vector-ALU tile; from M = 8
+ * the two kernels are faster (11.1 against 13.4 us).
  * w_rep from repack_q4_K (N x K); C overwritten as for mmq_q4K_q8_1; mmq_last_kernel reports
  * the tile (MMQ_TILE_GEMV or MMQ_TILE_SKINNY) with reason MMQ_REASON_FUSED.
  * Errors: MMQ_E_ARG, MMQ_E_SHAPE (as mmq_q4K_q8_1, or M > 128), MMQ_E_LDS (the kernel's LDS

@@ -176,7 +176,7 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
   if (tile == MMQ_TILE_GEMV) {
     info->block_m = (int32_t)mmq::gemv_group(M);
     info->block_n = mmq::kGemvRows;
-    info->threads = 64 * mmq::kGemvWaves;
+    info->threads = 64 * (M > mmq::kGemvDotMaxM ? mmq::kGemvMfmaWaves : mmq::kGemvWaves);
     info->lds_bytes = mmq::gemv_lds_bytes(M);
     info->grid = mmq::gemv_grid(M, N);
     return MMQ_OK;

@@ -307,24 +307,28 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
 }
 
 // 9 to 16 tokens: the vector ALU's dot products set the time there, so one 32-block of 16
-// weight rows x 16 tokens becomes one v_mfma_i32_16x16x32_i8 (no padding at 16 tokens; token
-// columns past M read zero). A workgroup of 8 wavefronts owns 16 weight rows (paired on one
-// XCD as above) and all of K; wavefront w takes the super-blocks w, w + 8, w + 16, ..., each
-// one's loads issued before the previous one is computed. Per block a lane holds, for its token
+// weight rows x 16 tokens becomes one v_mfma_i32_16x16x32_i8 (no padding at 16 tokens; the
+// columns of tokens past M are computed from in-bounds or zero reads and never stored). A
+// workgroup of NW wavefronts owns 16 weight rows (paired on one XCD as above) and all of K;
+// wavefront w takes the super-blocks w, w + NW, w + 2 NW, ... With 8 wavefronts each
+// super-block's loads are issued before the previous one is computed; the launch uses 16
+// (66 registers, no second stage), 1-3 % faster at K = 4096 and 11008, where a wavefront has
+// one or three super-blocks. Per block a lane holds, for its token
 // l % 16, the four outputs of rows 4 (l / 16) .. + 3, and rescales them as the GEMM does:
 // y = fma(D, da, nda) with D biased by 0x4B400000, acc = fma(y, dsv, acc). term2 of a
 // super-block is a K = 8 product of dmv and da*sa; as in the GEMM it runs on the bf16 matrix
 // unit from the exact three-piece splits stored in the record and in the q8 buffer: two
 // v_mfma_f32_16x16x32_bf16 whose 4 k-groups of 8 blocks carry the piece pairs (0,0) (0,1)
-// (1,0) (0,2) | (1,1) (2,0) (and two zero groups), added into the same accumulator. The 8
+// (1,0) (0,2) | (1,1) (2,0) (and two zero groups), added into the same accumulator. The NW
 // wavefronts' partial sums are added in wavefront order through LDS.
 // Operand layout of both instructions: A row l % 16 and B column l % 16 take the 8 k values
 // 8 (l / 16) .. + 7; the result of row 4 (l / 16) + r, column l % 16 is register r of lane l.
-__global__ __launch_bounds__(512) void mmq_gemv_mfma_kernel(
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
     const int8_t* __restrict__ qs, const float* __restrict__ da_plane,
     const uint16_t* __restrict__ tpieces, const uint8_t* __restrict__ wrep,
     float* __restrict__ C, int M, int N, int K) {
-  __shared__ float red[8][16][16];  // [wavefront][token][row]
+  __shared__ float red[NW][16][16];  // [wavefront][token][row]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int u = (int)blockIdx.x;
@@ -383,10 +387,17 @@ __global__ __launch_bounds__(512) void mmq_gemv_mfma_kernel(
 
   typedef float v4f __attribute__((ext_vector_type(4)));
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  // with 8 wavefronts the next super-block's loads are issued before the current one is
+  // computed; with 16 there is no room for a second stage in 128 registers
+  constexpr bool kPrefetch = NW <= 8;
   Stage cur, nxt;
-  if (wave < nsb) load(wave, cur);
-  for (int s = wave; s < nsb; s += 8) {
-    if (s + 8 < nsb) load(s + 8, nxt);
+  if (kPrefetch && wave < nsb) load(wave, cur);
+  for (int s = wave; s < nsb; s += NW) {
+    if constexpr (kPrefetch) {
+      if (s + NW < nsb) load(s + NW, nxt);
+    } else {
+      load(s, cur);
+    }
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const uint2 w = cur.nb[b >> 1];
@@ -408,7 +419,7 @@ __global__ __launch_bounds__(512) void mmq_gemv_mfma_kernel(
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, cur.pa[1]),
                                                   __builtin_bit_cast(v8bf, cur.pb[1]), acc, 0,
                                                   0, 0);
-    cur = nxt;
+    if constexpr (kPrefetch) cur = nxt;
   }
 
 #pragma unroll
@@ -420,7 +431,7 @@ __global__ __launch_bounds__(512) void mmq_gemv_mfma_kernel(
     if (t < M && n < N) {
       float v = 0.0f;
 #pragma unroll
-      for (int w = 0; w < 8; ++w) v += red[w][t][rr];
+      for (int w = 0; w < NW; ++w) v += red[w][t][rr];
       C[(size_t)t * N + n] = v;
     }
   }
@@ -456,7 +467,7 @@ hipError_t launch_fused_mt(const float* x, const void* w_rep, float* C, int64_t 
 int64_t gemv_group(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 8 : 16))); }
 
 int64_t gemv_lds_bytes(int64_t M) {
-  if (M > 8) return 8 * 16 * 16 * 4;  // the matrix-unit kernel: partial sums only
+  if (M > kGemvDotMaxM) return kGemvMfmaWaves * 16 * 16 * 4;  // the matrix-unit form: partial sums only
   const int64_t mt = gemv_group(M);
   return (int64_t)kGemvWaves * kGemvSlices * (mt * 160 + 16);
 }
@@ -468,9 +479,10 @@ int64_t gemv_grid(int64_t M, int64_t N) {
 hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
                            int64_t K, hipStream_t s) {
   if (M < 1 || M > kGemvMaxM) return hipErrorInvalidValue;
-  if (M > 8) {
+  if (M > kGemvDotMaxM) {
     const uint8_t* base = static_cast<const uint8_t*>(q8);
-    hipLaunchKernelGGL(mmq_gemv_mfma_kernel, dim3((unsigned)gemv_grid(M, N)), dim3(512), 0, s,
+    hipLaunchKernelGGL(mmq_gemv_mfma_kernel<kGemvMfmaWaves>, dim3((unsigned)gemv_grid(M, N)),
+                       dim3(64 * kGemvMfmaWaves), 0, s,
                        reinterpret_cast<const int8_t*>(base),
                        reinterpret_cast<const float*>(base + q8_planes_offset(M, K)),
                        reinterpret_cast<const uint16_t*>(base + q8_pieces_offset(M, K)),
@@ -487,7 +499,7 @@ hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t 
 
 hipError_t launch_mmq_gemv_fused(const float* x, const void* w_rep, float* C, int64_t M,
                                  int64_t N, int64_t K, hipStream_t s) {
-  if (M < 1 || M > 8) return hipErrorInvalidValue;  // the fused form exists up to 8 tokens
+  if (M < 1 || M > kGemvFusedMaxM) return hipErrorInvalidValue;
   switch (gemv_group(M)) {
     case 1: return launch_fused_mt<1>(x, w_rep, C, M, N, K, s);
     case 2: return launch_fused_mt<2>(x, w_rep, C, M, N, K, s);

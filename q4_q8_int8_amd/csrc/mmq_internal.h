@@ -98,11 +98,14 @@ hipError_t launch_mmq_fused(const float* x, const void* w_rep, float* C, int64_t
 constexpr int kGemvWaves = 8;
 constexpr int kGemvRows = 16;  // weight rows per workgroup
 constexpr int kGemvMaxM = 16;
+constexpr int kGemvMfmaWaves = 16;  // wavefronts per workgroup of the 9-16 token form
 // The guard's choice up to here (at 16 tokens, K = N = 4096: 10.4 against the skinny
 // kernel's 11.6 us).
 constexpr int kGemvAutoMaxM = 16;
+// The vector-ALU form up to here, the matrix-unit form above.
+constexpr int kGemvDotMaxM = 8;
 // The variant that quantizes its activations itself: vector-ALU form only.
-constexpr int kGemvFusedMaxM = 8;
+constexpr int kGemvFusedMaxM = kGemvDotMaxM;
 int64_t gemv_group(int64_t M);  // tokens per workgroup
 int64_t gemv_lds_bytes(int64_t M);
 int64_t gemv_grid(int64_t M, int64_t N);

@@ -161,10 +161,11 @@ def test_plan_gemv_tile(M, group, grid):
                                               (SKINNY, mmq.MMQ_REASON_FEW_TOKENS))
     p = mmq.mmq_plan(M, 4096, 4096, 160 * 1024, force_tile=GEMV)
     assert p["tile"] == GEMV
-    assert p["block_m"] == group and p["block_n"] == 16 and p["threads"] == 512
+    assert p["block_m"] == group and p["block_n"] == 16
+    assert p["threads"] == (512 if group <= 8 else 1024)
     # up to 8 tokens, per wavefront and K-slice: its half's 128 token bytes and 4 (da, sa)
     # pairs per token, 16 padding; from 9 tokens (the matrix-unit form) the partial sums only
-    lds = 8 * 4 * (160 * group + 16) if group <= 8 else 8 * 16 * 16 * 4
+    lds = 8 * 4 * (160 * group + 16) if group <= 8 else 16 * 16 * 16 * 4
     assert p["lds_bytes"] == lds and p["grid"] == grid
     # ragged N: 4097 rows make 257 blocks of 16
     assert mmq.mmq_plan(M, 4097, 256, 160 * 1024, force_tile=GEMV)["grid"] == 257 * (grid // 256)
