@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--rotate R] [--no-cpu-baseline]
                     [--no-f16] [--sweep] [--decode [--shape M,N,K]]
 
-Defaults: W = 500 warmup steps (the device's clocks settle after ~50 ms of this load; the
-first q-proj steps take up to 1.5x the steady-state time), then K = 200 timed steps.
+Defaults: W = 500 warmup steps, and at least 300 ms of warmup whatever W is (the device's
+clocks settle after ~50 ms of this load; the first q-proj steps take up to 1.5x the
+steady-state time), then K = 200 timed steps.
 
 Workload: the LLaMA-7B q-proj prefill product, M=2048 tokens, K=4096, N=4096, with
 synthetic seeded inputs (synth.py: activations N(0,1) with 0.1% outliers x20, q4_K fit of
@@ -97,11 +98,22 @@ def cpu_baseline(W: dict, window_s: float = 10.0) -> dict:
     """The CPU oracle (as it stands) on the same workload: quantize, decode, f64 product."""
     import numpy as np
     import oracle
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        pool = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        pool = affinity
+    threads = min(pool, affinity)   # the BLAS pool cannot run more threads than it may use
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     M, N, K = W["M"], W["N"], W["K"]
     # The whole workload (quantize + q4_K decode + float64 product) takes well under the
     # ~10 s timing window on a many-core host, so it is repeated until the window is filled.
@@ -116,7 +128,8 @@ def cpu_baseline(W: dict, window_s: float = 10.0) -> dict:
             break
     assert np.isfinite(C).all()
     return {"value": reps * M * N * K / dt / 1e12, "unit": "TMAC/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpus_in_affinity": affinity, "blas_threads": pool,
+            "cpu_model": model,
             "sample": f"the full {M}x{N}x{K} workload (quantize + q4_K decode + float64 "
                       f"product) repeated {reps} times in {dt:.1f} s"}
 
@@ -134,7 +147,24 @@ def copy_probe(mib: int) -> int:
     return 0
 
 
-def measure(W: dict, R: int, steps: int, warmup: int, tile: int = 0) -> dict:
+def warm(step, warmup: int, warmup_ms: float) -> int:
+    """Run step(i) at least `warmup` times and for at least `warmup_ms` of wall time, then
+    synchronize. Under this load the device's clocks take tens of milliseconds to settle,
+    so a step count alone (the driver passes a handful) would leave the timed steps inside
+    the ramp. Returns the number of warmup steps run."""
+    import torch
+    i, t0 = 0, time.perf_counter()
+    while i < warmup or (time.perf_counter() - t0) * 1e3 < warmup_ms:
+        step(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()   # the wall clock must see the GPU's progress
+    torch.cuda.synchronize()
+    return i
+
+
+def measure(W: dict, R: int, steps: int, warmup: int, tile: int = 0,
+            warmup_ms: float = 0.0) -> dict:
     """Time the whole path (quantize + GEMM) on one workload; see the module docstring."""
     import torch
 
@@ -174,9 +204,7 @@ def measure(W: dict, R: int, steps: int, warmup: int, tile: int = 0) -> dict:
         quant(i % R)
         gemm(i % R)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warmup_run = warm(step, warmup, warmup_ms)
     plan = mmq.mmq_last_kernel()
 
     # The timed region: exactly `steps` steps of the whole path between synchronizations,
@@ -256,7 +284,7 @@ def measure(W: dict, R: int, steps: int, warmup: int, tile: int = 0) -> dict:
     return {"ms_per_step": wall * 1e3 / steps, "step_gpu_us": region_gpu_ms * 1e3 / steps,
             "gemm_us": g_ms * 1e3, "quant_us": q_ms * 1e3, "repack_us": repack_us, "plan": plan,
             "graph_step_us": graph_step_us,
-            "graph_gemm_us": graph_gemm_us}
+            "graph_gemm_us": graph_gemm_us, "warmup_run": warmup_run}
 
 
 def measure_fused(W: dict, R: int, steps: int, warmup: int) -> dict:
@@ -565,6 +593,8 @@ def main() -> int:
     # covers that; the timed steps then measure the steady state.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--warmup-ms", type=float, default=300.0,
+                    help="also warm up for at least this much wall time (the clocks' ramp)")
     ap.add_argument("--rotate", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -605,7 +635,7 @@ def main() -> int:
     W = synth.workload("qproj")
     M, N, K = W["M"], W["N"], W["K"]
     R = max(1, args.rotate)
-    t = measure(W, R, args.steps, args.warmup)
+    t = measure(W, R, args.steps, args.warmup, warmup_ms=args.warmup_ms)
     plan = t["plan"]
     macs = M * N * K
     ms_per_step = t["ms_per_step"]
@@ -640,6 +670,11 @@ def main() -> int:
         "us_per_gmac": round(ms_per_step * 1e3 / (macs / 1e9), 4),
         "step_gpu_us": round(t["step_gpu_us"], 2),
         "graph_step_us": round(t["graph_step_us"], 2),
+        # the timed step against its two kernels' own averages, measured right after it: a
+        # ratio well below 1 would mean the timed steps ran at another clock than the
+        # kernels (e.g. still inside the warmup ramp)
+        "step_over_kernel_sum": round(t["step_gpu_us"] / (t["quant_us"] + t["gemm_us"]), 4),
+        "warmup_steps_run": t["warmup_run"],
         "gemm": {"us": round(gemm_s * 1e6, 2),
                  "tmacs": round(macs / gemm_s / 1e12, 2),
                  "us_per_gmac": round(gemm_s * 1e6 / (macs / 1e9), 4)},

@@ -57,7 +57,7 @@ int dequantize_q4_K_f16(const void* w_q4K, int64_t N, int64_t K, void* w_f16, vo
  * exact in float32; the order of the float32 additions is fixed by the kernel (deterministic).
  * Preconditions: K % 8 == 0 (rows of whole 16-byte words); M*K and N*K below 2^30.
  * Errors: MMQ_E_ARG (null or misaligned pointer, M, N or K <= 0), MMQ_E_SHAPE, MMQ_E_LDS (the
- *         device allows less than the kernel's 96 KiB of LDS), MMQ_E_DEVICE, MMQ_E_HIP.
+ *         device allows less than the kernel's 144 KiB of LDS), MMQ_E_DEVICE, MMQ_E_HIP.
  */
 int gemm_f16(int64_t M, int64_t N, int64_t K, const void* x_f16, const void* w_f16, float* C,
              void* stream);

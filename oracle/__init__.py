@@ -14,7 +14,7 @@ from .mmq_oracle import (  # noqa: F401
     QK8, QK_K, Q4K_BLOCK_BYTES,
     Q8, Q4K,
     f16_encode, f16_decode, round_half_away,
-    quantize_q8_1, bf16_pieces, q8_1_image,
+    quantize_q8_1,
     decode_q4_K, q4_K_scales, dequantize_q4_K,
     mmq, block_dots, mmq_terms,
 )

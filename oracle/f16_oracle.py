@@ -15,11 +15,12 @@ against exact rationals). No function is "parity unpinned".
 from __future__ import annotations
 
 import numpy as np
+from numpy.typing import NDArray
 
 from .mmq_oracle import Q4K, QK8, f16_decode, f16_encode, q4_K_scales
 
 
-def convert_f32_f16(x) -> np.ndarray:
+def convert_f32_f16(x) -> NDArray:
     """f32 activations [M, K] -> f16 bit patterns [M, K], nearest value, ties to even.
 
     Reading: the pages name the f16 path without its conversion; the plainest one is IEEE
@@ -29,7 +30,7 @@ def convert_f32_f16(x) -> np.ndarray:
         return f16_encode(np.asarray(x, dtype=np.float32))
 
 
-def dequantize_q4_K_f16(w: Q4K) -> np.ndarray:
+def dequantize_q4_K_f16(w: Q4K) -> NDArray:
     """q4_K weights -> f16 bit patterns [N, K]: w = dsv*v + dmv per sub-block [r15 §2.1].
 
     Reading: the value is evaluated in float32 and then rounded to f16 (nearest, ties to
@@ -47,7 +48,7 @@ def dequantize_q4_K_f16(w: Q4K) -> np.ndarray:
     return f16_encode(val.reshape(N, K))
 
 
-def gemm_f16(a_bits, w_bits) -> tuple[np.ndarray, np.ndarray]:
+def gemm_f16(a_bits, w_bits) -> tuple[NDArray, NDArray]:
     """C[i, j] = sum_k a_ik * w_jk for f16 operands, and T[i, j] = sum_k |a_ik * w_jk|.
 
     a_bits [M, K] and w_bits [N, K] are f16 bit patterns. Each product of two f16 values is

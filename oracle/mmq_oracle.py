@@ -17,6 +17,7 @@ from __future__ import annotations
 from typing import NamedTuple, Sequence
 
 import numpy as np
+from numpy.typing import NDArray
 
 QK8 = 32              # q8_1 block length: activations are quantized in blocks of 32 [r15 §2.1]
 QK_K = 256            # q4_K super-block length (8 sub-blocks of 32) [r12 §2, "KDR=4 restage-skip"]
@@ -25,32 +26,32 @@ Q4K_BLOCK_BYTES = 144  # 2+2 bytes f16 d/dmin, 12 bytes 6-bit sc/m, 128 bytes of
 
 class Q8(NamedTuple):
     """q8_1 activations: per 32-block an f16 scale da and the integer block sum sa."""
-    qs: np.ndarray       # int8  [M, K]
-    da_bits: np.ndarray  # uint16 [M, K/32], f16 bit pattern of the block scale
-    sa: np.ndarray       # int32 [M, K/32], integer sum of the block's 32 quantized values
+    qs: NDArray       # int8  [M, K]
+    da_bits: NDArray  # uint16 [M, K/32], f16 bit pattern of the block scale
+    sa: NDArray       # int32 [M, K/32], integer sum of the block's 32 quantized values
 
 
 class Q4K(NamedTuple):
     """Decoded q4_K fields."""
-    d: np.ndarray     # float64 [N, K/256]  super-block scale (an f16 value)
-    dmin: np.ndarray  # float64 [N, K/256]  super-block min scale (an f16 value)
-    sc: np.ndarray    # int64 [N, K/32]     6-bit sub-block scale
-    m: np.ndarray     # int64 [N, K/32]     6-bit sub-block min
-    v: np.ndarray     # int64 [N, K]        4-bit unsigned values 0..15
+    d: NDArray     # float64 [N, K/256]  super-block scale (an f16 value)
+    dmin: NDArray  # float64 [N, K/256]  super-block min scale (an f16 value)
+    sc: NDArray    # int64 [N, K/32]     6-bit sub-block scale
+    m: NDArray     # int64 [N, K/32]     6-bit sub-block min
+    v: NDArray     # int64 [N, K]        4-bit unsigned values 0..15
 
 
 # ----------------------------------------------------------------------------- float16
-def f16_encode(x) -> np.ndarray:
+def f16_encode(x) -> NDArray:
     """f32 -> f16 bit pattern, IEEE round-to-nearest-even with subnormals (numpy's cast)."""
     return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
-def f16_decode(bits) -> np.ndarray:
+def f16_decode(bits) -> NDArray:
     """f16 bit pattern -> exact float64 value."""
     return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
 
 
-def round_half_away(v) -> np.ndarray:
+def round_half_away(v) -> NDArray:
     """Round to the nearest integer, ties away from zero (C's roundf), as float64.
 
     Evaluated in float64, where |v| + 0.5 is exact for every float32 |v| < 2^29.
@@ -93,76 +94,6 @@ def quantize_q8_1(x) -> Q8:
     return Q8(qs=q.reshape(M, K), da_bits=f16_encode(d), sa=sa)
 
 
-def bf16_pieces(v) -> np.ndarray:
-    """Three bfloat16 values summing exactly to each float32 v, as uint16 bits [..., 3].
-
-    A storage form (not part of the method): the library keeps the two rank-1 factors of
-    term2 in this form so that a bf16 matrix instruction can multiply them. For finite v:
-        p0 = bf16_rne(v), p1 = bf16_rne(v - p0), p2 = v - p0 - p1,
-    where bf16_rne rounds a float32 to its top 16 bits, to nearest with ties to even.
-    Both differences are exact (each operand pair is within a factor of two), and p2 has
-    few enough significant bits to be a bfloat16 whenever v has at most 23, which covers
-    every da*sa and every dmin*m. A non-finite v is stored as {top 16 bits of v, 0, 0}.
-    """
-    v = np.ascontiguousarray(v, dtype=np.float32)
-
-    def rne_bits(x):
-        b = x.view(np.uint32).astype(np.uint64)
-        return ((b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
-
-    with np.errstate(invalid="ignore", over="ignore"):   # non-finite v: replaced below
-        a = rne_bits(v)
-        r = (v - a.view(np.float32)).astype(np.float32)
-        b = rne_bits(r)
-        c = (r - b.view(np.float32)).astype(np.float32)
-    out = np.stack([a >> 16, b >> 16, c.view(np.uint32) >> 16], axis=-1).astype(np.uint16)
-    bad = ~np.isfinite(v)
-    out[bad] = 0
-    out[bad, 0] = (v[bad].view(np.uint32) >> 16).astype(np.uint16)
-    return out
-
-
-def q8_1_image(q: Q8) -> np.ndarray:
-    """Byte image of quantized activations as the library stores them.
-
-    1. qs int8 [M][K] row-major;
-    2. one 32-bit word per (row, 32-block), [M][K/32]: low 16 bits = f16 bits of da, high
-       16 bits = sa as a signed 16-bit integer (the token-pair staging word of the r15 page,
-       §3.2, the wide kernel's uint2-packed da/sa);
-    3. zero padding up to a multiple of 256 bytes;
-    4. per (block, row), block-major [K/32][M], the float32 pair (da, -1.5 * 2^23 * da): the
-       token factor of term1, and with it the constant the GEMM adds when it rescales an
-       integer result offset by 1.5 * 2^23 (both exact: da has 11 significant bits);
-    5. zero padding up to a multiple of 256 bytes;
-    6. the folded row factor of term2, da*sa (r16 page §2.1, exact in float32), as the three
-       bf16 pieces of bf16_pieces, [ceil(K/256)][3][M][8]: piece i of row r, block 8s+e at
-       [s][i][r][e]; slots of blocks past K/32 are zero.
-    """
-    M, K = q.qs.shape
-    nb = K // QK8
-    nsb = -(-nb // 8)
-    words = (q.da_bits.astype(np.uint32)
-             | ((q.sa.astype(np.int32) & 0xFFFF).astype(np.uint32) << np.uint32(16)))
-    head = np.concatenate([q.qs.reshape(-1).view(np.uint8),
-                           words.astype("<u4").reshape(-1).view(np.uint8)])
-    da = f16_decode(q.da_bits)                                  # exact f64
-    dma = da * q.sa.astype(np.float64)                          # exact: <= 23 significant bits
-    assert np.array_equal(dma.astype(np.float32).astype(np.float64), dma)
-    nda = -1.5 * 2.0 ** 23 * da                                  # exact in f64
-    assert np.array_equal(nda.astype(np.float32).astype(np.float64), nda)
-    plane = np.ascontiguousarray(np.stack([da.T, nda.T], axis=-1)).astype("<f4")
-    plane = plane.reshape(-1).view(np.uint8)                    # [K/32][M][2]
-    pieces = np.zeros((nsb, 3, M, 8), "<u2")
-    pc = bf16_pieces(dma.astype(np.float32))                    # [M][K/32][3]
-    for b in range(nb):
-        pieces[b // 8, :, :, b % 8] = pc[:, b, :].T
-
-    def pad256(a):
-        return np.concatenate([a, np.zeros((-a.size) % 256, np.uint8)])
-
-    return np.concatenate([pad256(head), pad256(plane), pieces.reshape(-1).view(np.uint8)])
-
-
 def decode_q4_K(blocks) -> Q4K:
     """Decode q4_K super-blocks u8 [N, K/256, 144] into their fields [r15 §2.1].
 
@@ -201,7 +132,7 @@ def decode_q4_K(blocks) -> Q4K:
                v=v.reshape(N, nsb * QK_K))
 
 
-def q4_K_scales(w: Q4K) -> tuple[np.ndarray, np.ndarray]:
+def q4_K_scales(w: Q4K) -> tuple[NDArray, NDArray]:
     """Per sub-block effective scale dsv = d*sc and negative bias dmv = -(dmin*m) [r15 §2.1].
 
     Both products are exact in float64 (f16 value times a 6-bit integer).
@@ -211,7 +142,7 @@ def q4_K_scales(w: Q4K) -> tuple[np.ndarray, np.ndarray]:
     return d * w.sc, -(dmin * w.m)
 
 
-def dequantize_q4_K(w: Q4K, rows: Sequence[int] | None = None) -> np.ndarray:
+def dequantize_q4_K(w: Q4K, rows: Sequence[int] | None = None) -> NDArray:
     """Weights as float64 [N, K]: b = dsv*v + dmv = d*sc*v - dmin*m [r15 §2.1]. Exact in f64."""
     dsv, dmv = q4_K_scales(w)
     v = w.v if rows is None else w.v[rows]
@@ -223,7 +154,7 @@ def dequantize_q4_K(w: Q4K, rows: Sequence[int] | None = None) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------- the product
-def _a_f64(q: Q8, rows) -> np.ndarray:
+def _a_f64(q: Q8, rows) -> NDArray:
     """Dequantized activations da*q as float64 (exact: an f16 value times an 8-bit integer)."""
     qs = q.qs[rows].astype(np.float64)
     da = f16_decode(q.da_bits[rows])
@@ -231,7 +162,7 @@ def _a_f64(q: Q8, rows) -> np.ndarray:
     return (qs.reshape(R, K // QK8, QK8) * da[..., None]).reshape(R, K)
 
 
-def mmq(q: Q8, w: Q4K, rows: Sequence[int] | None = None) -> np.ndarray:
+def mmq(q: Q8, w: Q4K, rows: Sequence[int] | None = None) -> NDArray:
     """C[i, j] = sum_k (da_i,b(k) * q_ik) * w_jk in float64 -- the direct dot product.
 
     Dequantize both operands to float and take their product with one f64 matrix
@@ -245,7 +176,7 @@ def mmq(q: Q8, w: Q4K, rows: Sequence[int] | None = None) -> np.ndarray:
     return a @ wt.T
 
 
-def block_dots(q: Q8, w: Q4K, rows: Sequence[int], cols: Sequence[int]) -> np.ndarray:
+def block_dots(q: Q8, w: Q4K, rows: Sequence[int], cols: Sequence[int]) -> NDArray:
     """Per-block integer dot products S[b, i, j] = sum_{k in block b} q_ik * v_jk [r15 §2.1].
 
     Exact int64 by brute force (np.einsum on integers); shape [K/32, len(rows), len(cols)].

@@ -1,10 +1,11 @@
 """q4_K x q8_1 quantized matrix multiply (MMQ) on MI355X (gfx950).
 
 A thin ctypes binding over libmmq.so, whose C ABI is declared in include/mmq.h (the integer
-product) and include/mmq_f16.h (the f16 comparator path). The
-functions here have the same names and arguments as the C entry points and only marshal
-arguments: tensors are passed as device pointers, the stream defaults to torch's current
-stream, and a nonzero status raises MMQError. Every step of the computation runs in the
+product) and include/mmq_f16.h (the f16 comparator path). The functions here have the same
+names and arguments as the C entry points and only marshal arguments: each tensor is checked
+(a contiguous CUDA tensor on the current device, of the expected dtype and at least the size
+the call reads or writes; MMQArgumentError otherwise) and passed as a device pointer, the
+stream defaults to torch's current stream, and a nonzero status raises MMQError. Every step of the computation runs in the
 library's HIP kernels; there is no fallback path. Importing this package fails loudly when
 libmmq.so has not been built (python q4_q8_int8_amd/build.py).
 """
@@ -15,8 +16,7 @@ import os
 import re
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# MMQ_LIBRARY may name another build of the same library (e.g. a tile-shape variant)
-LIB_PATH = os.environ.get("MMQ_LIBRARY") or os.path.join(_PKG, "libmmq.so")
+LIB_PATH = os.path.join(_PKG, "libmmq.so")
 INCLUDE_DIR = os.path.join(os.path.dirname(_PKG), "include")
 HEADER_PATH = os.path.join(INCLUDE_DIR, "mmq.h")
 HEADER_PATHS = (HEADER_PATH, os.path.join(INCLUDE_DIR, "mmq_f16.h"))
@@ -108,11 +108,41 @@ def _check(fn: str, status: int) -> None:
         raise MMQError(fn, status)
 
 
-def _ptr(t) -> int | None:
-    """Device pointer of a tensor (or an int address, or None)."""
-    if t is None or isinstance(t, int):
-        return t
+class MMQArgumentError(ValueError):
+    """A tensor handed to a wrapper does not fit the call (raised before any launch)."""
+
+
+def _dev(t, name: str, nbytes: int, dtype=None) -> int:
+    """Device pointer of tensor t after checking that the call may use it: a contiguous CUDA
+    tensor on the current device, of `dtype` when given, holding at least `nbytes` bytes.
+    The C ABI takes bare pointers and cannot check buffer sizes itself, so an undersized or
+    mistyped buffer is refused here rather than read or written out of bounds."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise MMQArgumentError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if dtype is not None and t.dtype != dtype:
+        raise MMQArgumentError(f"{name}: dtype must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise MMQArgumentError(f"{name}: must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise MMQArgumentError(f"{name}: holds {have} bytes, the call needs {nbytes}")
+    if not t.is_cuda:
+        raise MMQArgumentError(f"{name}: must be a CUDA tensor (got device {t.device})")
+    if t.device.index != torch.cuda.current_device():
+        raise MMQArgumentError(f"{name}: on {t.device}, but the current device is "
+                               f"cuda:{torch.cuda.current_device()}")
     return t.data_ptr()
+
+
+def _f32():
+    import torch
+    return torch.float32
+
+
+def _i32():
+    import torch
+    return torch.int32
 
 
 def _stream(stream) -> int | None:
@@ -150,42 +180,58 @@ def mmq_q4K_repacked_bytes(N: int, K: int) -> int:
 
 
 # ---------------------------------------------------------------- the hot path
+def _gemm_ptrs(M: int, N: int, K: int, q8, w_rep, C):
+    return (_dev(q8, "q8", mmq_q8_1_bytes(M, K)),
+            _dev(w_rep, "w_rep", mmq_q4K_repacked_bytes(N, K)),
+            _dev(C, "C", 4 * M * N, _f32()))
+
+
 def quantize_q8_1(x, M: int, K: int, q8, stream=None) -> None:
     """x: f32 [M, K] device tensor; q8: device buffer of mmq_q8_1_bytes(M, K) bytes."""
-    _check("quantize_q8_1", _lib.quantize_q8_1(_ptr(x), M, K, _ptr(q8), _stream(stream)))
+    xp = _dev(x, "x", 4 * M * K, _f32())
+    qp = _dev(q8, "q8", mmq_q8_1_bytes(M, K))
+    _check("quantize_q8_1", _lib.quantize_q8_1(xp, M, K, qp, _stream(stream)))
 
 
 def repack_q4_K(w_q4K, N: int, K: int, w_rep, stream=None) -> None:
     """w_q4K: q4_K blocks (mmq_q4K_bytes); w_rep: mmq_q4K_repacked_bytes(N, K) bytes."""
-    _check("repack_q4_K", _lib.repack_q4_K(_ptr(w_q4K), N, K, _ptr(w_rep), _stream(stream)))
+    wp = _dev(w_q4K, "w_q4K", mmq_q4K_bytes(N, K))
+    rp = _dev(w_rep, "w_rep", mmq_q4K_repacked_bytes(N, K))
+    _check("repack_q4_K", _lib.repack_q4_K(wp, N, K, rp, _stream(stream)))
 
 
 def mmq_q4K_q8_1(M: int, N: int, K: int, q8, w_rep, C, stream=None) -> None:
     """C[M, N] (f32 device tensor) = q8 (M x K) times repacked q4_K weights (N x K)^T."""
-    _check("mmq_q4K_q8_1",
-           _lib.mmq_q4K_q8_1(M, N, K, _ptr(q8), _ptr(w_rep), _ptr(C), _stream(stream)))
+    qp, rp, cp = _gemm_ptrs(M, N, K, q8, w_rep, C)
+    _check("mmq_q4K_q8_1", _lib.mmq_q4K_q8_1(M, N, K, qp, rp, cp, _stream(stream)))
 
 
 def mmq_q4K_q8_1_ex(M: int, N: int, K: int, q8, w_rep, C, stream=None,
                     force_tile: int = MMQ_TILE_AUTO, lds_budget: int = 0,
                     min_workgroups: int = 0) -> None:
+    qp, rp, cp = _gemm_ptrs(M, N, K, q8, w_rep, C)
     _check("mmq_q4K_q8_1_ex",
-           _lib.mmq_q4K_q8_1_ex(M, N, K, _ptr(q8), _ptr(w_rep), _ptr(C), _stream(stream),
+           _lib.mmq_q4K_q8_1_ex(M, N, K, qp, rp, cp, _stream(stream),
                                 _opts(force_tile, lds_budget, min_workgroups)))
 
 
 def mmq_q4K_f32(M: int, N: int, K: int, x, w_rep, C, stream=None) -> None:
     """Few tokens (M <= 128): C[M, N] from f32 activations x [M, K], quantized in the GEMM."""
-    _check("mmq_q4K_f32",
-           _lib.mmq_q4K_f32(M, N, K, _ptr(x), _ptr(w_rep), _ptr(C), _stream(stream)))
+    xp = _dev(x, "x", 4 * M * K, _f32())
+    rp = _dev(w_rep, "w_rep", mmq_q4K_repacked_bytes(N, K))
+    cp = _dev(C, "C", 4 * M * N, _f32())
+    _check("mmq_q4K_f32", _lib.mmq_q4K_f32(M, N, K, xp, rp, cp, _stream(stream)))
 
 
 def mmq_q4K_q8_1_blockdots(M: int, N: int, K: int, q8, w_rep, i0: int, i1: int, j0: int,
                            j1: int, S, stream=None, force_tile: int = MMQ_TILE_AUTO,
                            lds_budget: int = 0) -> None:
     """S: int32 device tensor [K/32, i1-i0, j1-j0] of per-block integer dot products."""
+    qp = _dev(q8, "q8", mmq_q8_1_bytes(M, K))
+    rp = _dev(w_rep, "w_rep", mmq_q4K_repacked_bytes(N, K))
+    sp = _dev(S, "S", 4 * (K // QK8) * max(i1 - i0, 0) * max(j1 - j0, 0), _i32())
     _check("mmq_q4K_q8_1_blockdots",
-           _lib.mmq_q4K_q8_1_blockdots(M, N, K, _ptr(q8), _ptr(w_rep), i0, i1, j0, j1, _ptr(S),
+           _lib.mmq_q4K_q8_1_blockdots(M, N, K, qp, rp, i0, i1, j0, j1, sp,
                                        _stream(stream), _opts(force_tile, lds_budget)))
 
 
@@ -207,18 +253,24 @@ def mmq_f16_bytes(rows: int, K: int) -> int:
 
 def convert_f32_f16(x, M: int, K: int, x_f16, stream=None) -> None:
     """x: f32 [M, K] device tensor; x_f16: device buffer of mmq_f16_bytes(M, K) bytes."""
-    _check("convert_f32_f16", _lib.convert_f32_f16(_ptr(x), M, K, _ptr(x_f16), _stream(stream)))
+    xp = _dev(x, "x", 4 * M * K, _f32())
+    hp = _dev(x_f16, "x_f16", mmq_f16_bytes(M, K))
+    _check("convert_f32_f16", _lib.convert_f32_f16(xp, M, K, hp, _stream(stream)))
 
 
 def dequantize_q4_K_f16(w_q4K, N: int, K: int, w_f16, stream=None) -> None:
     """w_q4K: q4_K blocks (mmq_q4K_bytes); w_f16: mmq_f16_bytes(N, K) bytes."""
-    _check("dequantize_q4_K_f16",
-           _lib.dequantize_q4_K_f16(_ptr(w_q4K), N, K, _ptr(w_f16), _stream(stream)))
+    wp = _dev(w_q4K, "w_q4K", mmq_q4K_bytes(N, K))
+    hp = _dev(w_f16, "w_f16", mmq_f16_bytes(N, K))
+    _check("dequantize_q4_K_f16", _lib.dequantize_q4_K_f16(wp, N, K, hp, _stream(stream)))
 
 
 def gemm_f16(M: int, N: int, K: int, x_f16, w_f16, C, stream=None) -> None:
     """C[M, N] (f32 device tensor) = x_f16 [M, K] times w_f16 [N, K]^T, f32 accumulation."""
-    _check("gemm_f16", _lib.gemm_f16(M, N, K, _ptr(x_f16), _ptr(w_f16), _ptr(C), _stream(stream)))
+    xp = _dev(x_f16, "x_f16", mmq_f16_bytes(M, K))
+    wp = _dev(w_f16, "w_f16", mmq_f16_bytes(N, K))
+    cp = _dev(C, "C", 4 * M * N, _f32())
+    _check("gemm_f16", _lib.gemm_f16(M, N, K, xp, wp, cp, _stream(stream)))
 
 
 def mmq_last_kernel() -> dict:

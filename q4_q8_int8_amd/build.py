@@ -47,11 +47,9 @@ def _run(cmd: list[str]) -> None:
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
-    """Compile every HIP/C++ source and link libmmq.so (or `out`); returns its path.
-
-    `defines` are extra -D options (e.g. tile-shape variants built for comparison).
-    """
+def build(verbose: bool = False) -> str:
+    """Compile every HIP/C++ source and link libmmq.so in the package directory; returns its
+    path."""
     if not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     tmp = tempfile.mkdtemp(prefix="mmq_build_")
@@ -62,18 +60,18 @@ def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
             obj = os.path.join(tmp, src + ".o")
             objs.append(obj)
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmds.append([HIPCC, *FLAGS, *[f"-D{d}" for d in defines], *lang, "-c",
+            cmds.append([HIPCC, *FLAGS, *lang, "-c",
                          os.path.join(CSRC, src), "-o", obj])
         with ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
             for cmd, _ in zip(cmds, ex.map(_run, cmds)):
                 if verbose:
                     print(" ".join(cmd))
-        out_tmp = out + ".tmp"
+        out_tmp = LIB + ".tmp"
         _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out_tmp])
-        os.replace(out_tmp, out)
+        os.replace(out_tmp, LIB)
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
-    return out
+    return LIB
 
 
 if __name__ == "__main__":

@@ -15,17 +15,20 @@
 //
 // y equals float(S) * da bit for bit, without an int->float conversion instruction.
 // term2 is rank-1 per block: the row factor dma = da * sa (exact in f32, written by the
-// quantize prepass) times the column factor dmv. Summed over a pair of blocks it is a K=2
-// outer product, which v_mfma_f32_32x32x2_f32 adds into the same accumulator. Per element
-// the terms are added in a fixed order (term1 of each block, term2 of each pair of blocks),
-// so results are deterministic and identical across tile variants.
+// quantize prepass) times the column factor dmv (exact in f32). Both are stored as three
+// bf16 pieces that sum to them exactly, so over the 8 blocks of a super-block term2 is a
+// K = 8 product of pieces; three v_mfma_f32_32x32x16_bf16 per token tile and super-block
+// (each lane half supplying one piece pair) add the six largest of the nine piece products
+// into the same accumulator, every product exact in f32. Per element the terms are added
+// in a fixed order (term1 of each block, a third of term2 after blocks 1, 3 and 5), so
+// results are deterministic and identical across tile variants.
 //
 // Operand orientation: MFMA rows (src0) are weight rows, columns (src1, one per lane) are
 // tokens. Lane l holds token l%32 of a tile and, in its 16 accumulator registers r, the
 // weight rows 8*(r/4) + 4*(l/32) + r%4. Per block, the token scale da and its nb are one
 // float pair per lane and the weight scales dsv 16 floats per lane (lane-half broadcast),
-// all read from LDS;
-// dma and dmv for term2 are one float per lane per pair of blocks.
+// all read from LDS; the term2 operands are one 16-byte bf16 read each (8 blocks' pieces)
+// per token tile and third of a super-block.
 //
 // Workgroup: NW wavefronts; wavefront w owns weight tile (32 rows) tn*NW + w for all
 // BM = 32*TT tokens of the workgroup. Everything a super-block (256 k) needs from memory is

@@ -1,8 +1,13 @@
-"""Reference byte images of the library's own layouts, written from include/mmq.h.
+"""Reference byte images of the library's own storage layouts, written from include/mmq.h.
 
-These are test-side restatements of the documented layouts (they are not the method's
-arithmetic, which lives in oracle/): the repacked weight records that repack_q4_K must
-produce, and a reader of such records used to check the layout spec round-trips.
+These are test-side restatements of the documented layouts, not the method's arithmetic
+(that lives in oracle/, which knows only the q8_1 fields q, da, sa and the q4_K fields).
+Each image is built from the oracle's fields:
+  - q8_image: the whole q8 buffer quantize_q8_1 writes: q and the packed (da, sa) words,
+    then the GEMM's planes derived from da and sa;
+  - repack_reference: the repacked weight records repack_q4_K writes;
+  - read_repacked: a reader of such records, used to check that the layout round-trips;
+  - bf16_pieces: the three-piece bfloat16 split both planes use.
 """
 import numpy as np
 
@@ -10,6 +15,83 @@ import oracle
 
 TILE_ROWS = 32
 TILE_BYTES = 6656
+BIAS = 1.5 * 2.0 ** 23  # the GEMM's integer results come offset by this value
+
+
+def _rne_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> the float32 bits of its nearest bfloat16 (ties to even), low half zero."""
+    b = x.view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+
+
+def bf16_pieces(v) -> np.ndarray:
+    """Three bfloat16 values summing exactly to each float32 v, as uint16 bits [..., 3].
+
+    As the header defines them: p0 = bf16_rne(v), p1 = bf16_rne(v - p0), p2 = v - p0 - p1
+    (both differences are exact in float32); a non-finite v is stored as {top 16 bits, 0, 0}.
+    """
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):   # non-finite v: replaced below
+        a = _rne_bf16_bits(v)
+        r = (v - a.view(np.float32)).astype(np.float32)
+        b = _rne_bf16_bits(r)
+        c = (r - b.view(np.float32)).astype(np.float32)
+    out = np.stack([a >> 16, b >> 16, c.view(np.uint32) >> 16], axis=-1).astype(np.uint16)
+    bad = ~np.isfinite(v)
+    out[bad] = 0
+    out[bad, 0] = (v[bad].view(np.uint32) >> 16).astype(np.uint16)
+    return out
+
+
+def bf16_value(bits) -> np.ndarray:
+    """Exact float64 value of bfloat16 bit patterns."""
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _pad256(a: np.ndarray) -> np.ndarray:
+    return np.concatenate([a, np.zeros((-a.size) % 256, np.uint8)])
+
+
+def q8_words(q: oracle.Q8) -> np.ndarray:
+    """The packed scale words [M][K/32]: f16 bits of da in bits 0..15, sa (s16) in 16..31."""
+    return (q.da_bits.astype(np.uint32)
+            | ((q.sa.astype(np.int32) & 0xFFFF).astype(np.uint32) << np.uint32(16)))
+
+
+def q8_image(q: oracle.Q8) -> np.ndarray:
+    """Byte image of a q8 buffer (unwritten padding as zero) from the oracle's q, da, sa.
+
+    Regions: q int8 [M][K]; the scale words [M][K/32]; at the next 256-byte boundary the
+    float32 pairs (da, -1.5*2^23*da) [K/32][M]; at the next one the bf16 pieces of da*sa,
+    [ceil(K/256)][3][M][8] (piece i of row r, block 8s+e at [s][i][r][e]).
+    """
+    M, K = q.qs.shape
+    nb = K // 32
+    nsb = -(-nb // 8)
+    head = np.concatenate([q.qs.reshape(-1).view(np.uint8),
+                           q8_words(q).astype("<u4").reshape(-1).view(np.uint8)])
+    da = oracle.f16_decode(q.da_bits)                           # exact
+    dma = da * q.sa.astype(np.float64)                          # exact in float32
+    assert np.array_equal(dma.astype(np.float32).astype(np.float64), dma)
+    pairs = np.stack([da.T, -BIAS * da.T], axis=-1).astype("<f4")   # [K/32][M][2], exact
+    assert np.array_equal(pairs[..., 1].astype(np.float64), -BIAS * da.T)
+    pieces = np.zeros((nsb, 3, M, 8), "<u2")
+    pc = bf16_pieces(dma.astype(np.float32))                    # [M][K/32][3]
+    for b in range(nb):
+        pieces[b // 8, :, :, b % 8] = pc[:, b, :].T
+    return np.concatenate([_pad256(head), _pad256(pairs.reshape(-1).view(np.uint8)),
+                           pieces.reshape(-1).view(np.uint8)])
+
+
+def q8_regions(img: np.ndarray, M: int, K: int) -> dict:
+    """Split a q8 buffer image into its regions: qs, words, pairs (f32), pieces (u16)."""
+    nb = K // 32
+    P = -(-(M * K + 4 * M * nb) // 256) * 256
+    Q = -(-(P + 8 * M * nb) // 256) * 256
+    return {"qs": img[:M * K].view(np.int8).reshape(M, K),
+            "words": img[M * K:M * K + 4 * M * nb].view("<u4").reshape(M, nb),
+            "pairs": img[P:P + 8 * M * nb].view("<f4").reshape(nb, M, 2),
+            "pieces": img[Q:].view("<u2").reshape(-1, 3, M, 8)}
 
 
 def repack_reference(w_blocks: np.ndarray, fields: dict) -> np.ndarray:
@@ -31,7 +113,7 @@ def repack_reference(w_blocks: np.ndarray, fields: dict) -> np.ndarray:
     dmv[:N] = -(dmin[..., None] * m)
     a = dsv.reshape(nt, TILE_ROWS, nsb, 8).transpose(0, 2, 3, 1)        # [t, s, b, j]
     out[..., 4096:5120] = np.ascontiguousarray(a).view(np.uint8).reshape(nt, nsb, 1024)
-    pc = oracle.bf16_pieces(dmv).reshape(nt, TILE_ROWS, nsb, 8, 3)      # [t, j, s, b, i]
+    pc = bf16_pieces(dmv).reshape(nt, TILE_ROWS, nsb, 8, 3)             # [t, j, s, b, i]
     pc = np.ascontiguousarray(pc.transpose(0, 2, 4, 1, 3)).astype("<u2")  # [t, s, i, j, b]
     out[..., 5120:6656] = pc.view(np.uint8).reshape(nt, nsb, 1536)
     return out.reshape(-1)
@@ -50,6 +132,6 @@ def read_repacked(rep: np.ndarray, N: int, K: int) -> dict:
     dsv = r[..., 4096:5120].copy().view(np.float32).reshape(nt, nsb, 8, TILE_ROWS)
     dsv = dsv.transpose(0, 3, 1, 2).reshape(nt * TILE_ROWS, K // 32)
     pc = r[..., 5120:6656].copy().view("<u2").reshape(nt, nsb, 3, TILE_ROWS, 8)
-    vals = (pc.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    vals = bf16_value(pc)
     dmv = vals.sum(axis=2).transpose(0, 2, 1, 3).reshape(nt * TILE_ROWS, K // 32)
     return {"v": v[:N], "dsv": dsv[:N], "dmv": dmv[:N]}

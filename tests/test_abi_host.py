@@ -337,3 +337,45 @@ def test_fused_path_reaches_the_device_check():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: the call would run")
     assert mmq.raw_call("mmq_q4K_f32", 128, 8, 256, A, B, Cp, None) == mmq.MMQ_E_DEVICE
+
+
+# ---------------------------------------------------------------- the binding's tensor checks
+def _t(n, dtype=None):
+    import torch
+    return torch.zeros(n, dtype=dtype or torch.uint8)
+
+
+def test_binding_refuses_unfit_tensors():
+    """Each wrapper checks type, dtype, contiguity and byte size (and, on a GPU machine, that the
+    tensor is on the current CUDA device) before calling the library, which cannot check
+    buffer sizes itself."""
+    import torch
+    M, N, K = 4, 40, 256
+    q8 = _t(mmq.mmq_q8_1_bytes(M, K))
+    rep = _t(mmq.mmq_q4K_repacked_bytes(N, K))
+    C = _t(M * N, torch.float32)
+    x = _t(M * K, torch.float32)
+    bad = [
+        lambda: mmq.mmq_q4K_q8_1(M, N, K, q8[:-1], rep, C),                  # q8 one byte short
+        lambda: mmq.mmq_q4K_q8_1(M, N, K, q8, rep[:-16], C),                 # w_rep short
+        lambda: mmq.mmq_q4K_q8_1(M, N, K, q8, rep, C[:-1]),                  # C short
+        lambda: mmq.mmq_q4K_q8_1(M, N, K, q8, rep, C.to(torch.float16)),     # C not f32
+        lambda: mmq.mmq_q4K_q8_1(M, N, K, q8, rep, C.view(M, N).t()),        # C not contiguous
+        lambda: mmq.mmq_q4K_q8_1(M, N, K, 12345, rep, C),                    # not a tensor
+        lambda: mmq.quantize_q8_1(x.to(torch.float64), M, K, q8),            # x not f32
+        lambda: mmq.quantize_q8_1(x[:-1], M, K, q8),
+        lambda: mmq.repack_q4_K(_t(mmq.mmq_q4K_bytes(N, K) - 1), N, K, rep),
+        lambda: mmq.mmq_q4K_f32(M, N, K, x.view(M, K)[:, ::2], rep, C),
+        lambda: mmq.mmq_q4K_q8_1_blockdots(M, N, K, q8, rep, 0, M, 0, N,
+                                           _t(K // 32 * M * N, torch.int32)[:-1]),
+        lambda: mmq.mmq_q4K_q8_1_blockdots(M, N, K, q8, rep, 0, M, 0, N,
+                                           _t(K // 32 * M * N, torch.float32)),
+        lambda: mmq.convert_f32_f16(x, M, K, _t(2 * M * K - 1)),
+        lambda: mmq.gemm_f16(M, N, K, _t(2 * M * K), _t(2 * N * K), C[:-1]),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(mmq.MMQArgumentError):
+            call()
+    # well-sized host tensors pass every check but the device one
+    with pytest.raises(mmq.MMQArgumentError, match="CUDA tensor"):
+        mmq.mmq_q4K_q8_1(M, N, K, q8, rep, C)

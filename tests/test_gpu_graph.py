@@ -36,7 +36,8 @@ def _replay_and_check(g, out, want, disturb):
         assert np.array_equal(got, want), f"replay {i} differs from the eager result"
 
 
-@pytest.mark.parametrize("M,N,K", [(2048, 4096, 4096), (1, 4096, 4096), (100, 512, 1024)])
+@pytest.mark.parametrize("M,N,K", [(2048, 4096, 4096), (1, 4096, 4096), (12, 4096, 4096),
+                                   (16, 1024, 2048), (100, 512, 1024)])
 def test_integer_step_in_a_graph(M, N, K):
     x = to_dev(synth.activations("normal_outliers", M, K, 7000 + M))
     w, _ = synth.q4k_weights("fit", N, K, 7001)

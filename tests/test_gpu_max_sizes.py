@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 
 import oracle
+from tests.layout_ref import q8_image
 import synth
 from tests.gpu_util import assert_within_tolerance, say, to_dev
 
@@ -70,8 +71,11 @@ def test_mmq_largest_activations(tile):
     say("max |err|/T", r, "plan", mmq.mmq_last_kernel()["tile"])
 
 
-def test_mmq_largest_k():
-    M, N, K = 2, 33, 1 << 24                  # K at its limit, 65536 super-blocks
+@pytest.mark.parametrize("M", [2, 16])
+def test_mmq_largest_k(M):
+    """K at its limit (65536 super-blocks) on every tile; M = 16 takes the decode tile's
+    matrix-unit form and the fused call's skinny kernel, M = 2 the vector-ALU form for both."""
+    N, K = 33, 1 << 24
     x = synth.activations("normal_outliers", M, K, 5003)
     w, _ = synth.q4k_weights("random_fields", N, K, 5004)
     q = oracle.quantize_q8_1(x)
@@ -97,8 +101,9 @@ def test_mmq_largest_k():
     C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
     mmq.mmq_q4K_f32(M, N, K, to_dev(x), rep, C)
     torch.cuda.synchronize()
-    assert mmq.mmq_last_kernel()["tile"] == mmq.MMQ_TILE_GEMV
-    assert np.array_equal(C.cpu().numpy().view(np.uint32), out[mmq.MMQ_TILE_GEMV].view(np.uint32))
+    fused = mmq.MMQ_TILE_GEMV if M <= 8 else mmq.MMQ_TILE_SKINNY
+    assert mmq.mmq_last_kernel()["tile"] == fused
+    assert np.array_equal(C.cpu().numpy().view(np.uint32), out[fused].view(np.uint32))
 
 
 def test_gemm_f16_largest():
@@ -190,7 +195,7 @@ def test_quantize_largest(K):
     edge = (1 << 31) // (K // 4)
     rows = sorted({0, 1, 31, 32, edge - 1, edge, M // 2, M - 33, M - 32, M - 2, M - 1})
     got = q8_rows(q8, M, K, rows)
-    want_image = oracle.q8_1_image(oracle.quantize_q8_1(block[[r % R for r in rows]]))
+    want_image = q8_image(oracle.quantize_q8_1(block[[r % R for r in rows]]))
     want = q8_rows(want_image, len(rows), K, range(len(rows)))
     for name, g, w in zip(("qs", "words", "(da, nda) plane", "pieces"), got, want):
         assert np.array_equal(g, w), f"{name}: {np.count_nonzero(g != w)} bytes differ"

@@ -15,7 +15,7 @@ import oracle
 import synth
 from tests.gpu_util import (assert_within_tolerance, gpu_blockdots, gpu_mmq, gpu_quantize,
                             gpu_repack, oracle_q8, oracle_w, sample_rows, say, workload)
-from tests.layout_ref import repack_reference
+from tests.layout_ref import q8_image, q8_regions, repack_reference
 
 pytestmark = pytest.mark.gpu
 
@@ -35,14 +35,28 @@ def _gpu():
 
 
 # ----------------------------------------------------------------------------- quantize
+def check_q8(got: np.ndarray, x: np.ndarray) -> None:
+    """The q8 buffer of x, in two checks: (i) q, the f16 bits of da and sa bit-exact against
+    the oracle's quantization; (ii) the GEMM's derived planes against the layout reference
+    built from those same oracle fields."""
+    M, K = x.shape
+    q = oracle.quantize_q8_1(x)
+    reg = q8_regions(got, M, K)
+    assert np.array_equal(reg["qs"], q.qs), f"{np.count_nonzero(reg['qs'] != q.qs)} q differ"
+    da_bits = (reg["words"] & 0xFFFF).astype(np.uint16)
+    sa = (reg["words"] >> 16).astype(np.uint16).view(np.int16).astype(np.int32)
+    assert np.array_equal(da_bits, q.da_bits), "da differs"
+    assert np.array_equal(sa, q.sa), "sa differs"
+    want = q8_image(q)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want), f"{np.count_nonzero(got != want)} plane bytes differ"
+
+
 @pytest.mark.parametrize("name", CONFIGS + SWEEP)
 def test_quantize_bitexact(name):
     W = workload(name)
     say("quantize", name, W["x"].shape)
-    got = gpu_quantize(W["x"]).cpu().numpy()
-    want = oracle.q8_1_image(oracle_q8(name))
-    assert got.shape == want.shape
-    assert np.array_equal(got, want), f"{np.count_nonzero(got != want)} bytes differ"
+    check_q8(gpu_quantize(W["x"]).cpu().numpy(), W["x"])
 
 
 def test_quantize_edge_blocks(golden_dir):
@@ -53,16 +67,14 @@ def test_quantize_edge_blocks(golden_dir):
     for shape in [(len(blocks), 32), (1, 32 * len(blocks))]:
         xs = x.reshape(shape)
         say("quantize edge blocks", shape)
-        got = gpu_quantize(xs).cpu().numpy()
-        assert np.array_equal(got, oracle.q8_1_image(oracle.quantize_q8_1(xs)))
+        check_q8(gpu_quantize(xs).cpu().numpy(), xs)
 
 
 @pytest.mark.parametrize("M,K", [(1, 32), (3, 96), (37, 256), (129, 4128)])
 def test_quantize_ragged(M, K):
     x = synth.activations("normal_outliers", M, K, M * 31 + K)
     say("quantize ragged", M, K)
-    got = gpu_quantize(x).cpu().numpy()
-    assert np.array_equal(got, oracle.q8_1_image(oracle.quantize_q8_1(x)))
+    check_q8(gpu_quantize(x).cpu().numpy(), x)
 
 
 # ----------------------------------------------------------------------------- repack

@@ -140,70 +140,6 @@ def test_q8_1_invariants_random():
         assert oracle.f16_decode(q.da_bits[i, b]) == want
 
 
-def _bf16_value(bits) -> np.ndarray:
-    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
-
-
-# (value, expected pieces) derived by hand from round-to-nearest-even at 8 significant bits
-_BF16_PIECE_CASES = [
-    (1.0, (0x3F80, 0, 0)),
-    (1 + 2.0 ** -8, (0x3F80, 0x3B80, 0)),              # tie, even side is 1.0; rest 2^-8
-    (1 + 3 * 2.0 ** -8, (0x3F82, 0xBB80, 0)),          # tie, even side is 1 + 2^-6
-    (1 + 2.0 ** -9 + 2.0 ** -17, (0x3F80, 0x3B00, 0x3700)),  # below the tie; the rest is
-    (-(1 + 2.0 ** -9 + 2.0 ** -17), (0xBF80, 0xBB00, 0xB700)),  # a tie at 2^-9 (even)
-    (0.0, (0, 0, 0)),
-    (-0.0, (0x8000, 0, 0)),
-    (float("inf"), (0x7F80, 0, 0)),
-]
-
-
-@pytest.mark.parametrize("v,want", _BF16_PIECE_CASES)
-def test_bf16_pieces_hand_examples(v, want):
-    got = oracle.bf16_pieces(np.array([v], np.float32))[0]
-    assert tuple(int(g) for g in got) == want
-
-
-def test_bf16_pieces_exact_for_every_block_factor():
-    """p0 + p1 + p2 == v exactly, with shrinking pieces, for da*sa over every sa and f16
-    scales spread over the whole f16 range (subnormals included), and for every dmin*m."""
-    sa = np.arange(-4064, 4065, dtype=np.float64)
-    da = np.arange(1, 0x7C00, 53, dtype=np.uint16).view(np.float16).astype(np.float64)
-    v = (da[:, None] * sa[None, :]).ravel()
-    dmin = np.arange(0, 0x7C00, 7, dtype=np.uint16).view(np.float16).astype(np.float64)
-    v = np.concatenate([v, -(dmin[:, None] * np.arange(64.0)[None, :]).ravel()])
-    v32 = v.astype(np.float32)
-    assert np.array_equal(v32.astype(np.float64), v)        # all exact in float32
-    p = _bf16_value(oracle.bf16_pieces(v32))
-    assert np.array_equal(p.sum(axis=-1), v)
-    assert np.all(np.abs(p[:, 1]) <= 2.0 ** -8 * np.abs(v) * (1 + 2.0 ** -7))
-    assert np.all(np.abs(p[:, 2]) <= 2.0 ** -16 * np.abs(v))
-
-
-def test_q8_1_image_layout():
-    x = synth.activations("normal", 3, 64, 5)
-    q = oracle.quantize_q8_1(x)
-    img = oracle.q8_1_image(q)
-    assert img.dtype == np.uint8 and img.size == 256 + 256 + 48 * 3
-    assert np.array_equal(img[:192].view(np.int8).reshape(3, 64), q.qs)
-    words = img[192:216].view("<u4").reshape(3, 2)
-    assert np.all(img[216:256] == 0)
-    pairs = img[256:304].view("<f4").reshape(2, 3, 2)          # [block][row][da, -1.5*2^23*da]
-    assert np.all(img[304:512] == 0)
-    pieces = _bf16_value(img[512:].view("<u2")).reshape(1, 3, 3, 8)   # [sb][piece][row][e]
-    assert np.all(pieces[..., 2:] == 0)                        # blocks past K/32
-    for i in range(3):
-        for b in range(2):
-            w = int(words[i, b])
-            assert w & 0xFFFF == int(q.da_bits[i, b])
-            hi = w >> 16
-            sa = hi - 65536 if hi >= 32768 else hi
-            assert sa == int(q.sa[i, b])
-            da = Fraction(float(np.uint16(w & 0xFFFF).view(np.float16)))
-            assert Fraction(float(pairs[b, i, 0])) == da
-            assert Fraction(float(pairs[b, i, 1])) == -Fraction(3 * 2 ** 22) * da
-            assert sum(Fraction(float(pieces[0, k, i, b])) for k in range(3)) == da * sa
-
-
 # ----------------------------------------------------------------------------- q4_K
 def _golden_q4k(golden_dir):
     with open(os.path.join(golden_dir, "q4_K_worked_block.json")) as f:
