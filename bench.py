@@ -47,7 +47,13 @@ sys.path.insert(0, ROOT)
 INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, tera-ops/s (1 MAC = 2 ops)
 F16_PEAK_TFLOPS = 2500.0         # MI355X dense f16 MFMA
 HBM_PEAK_GBS = 8000.0
-FP32_VECTOR_TFLOPS = 157.3       # MI355X FP32 vector rate (no packed FP32: one FMA per lane)
+# MI355X FP32 vector rate without packed-FP32 instructions, which this library never uses:
+# 16 FMA lanes per SIMD per cycle, 256 CUs x 4 SIMDs at 2.4 GHz (the published 157.3 TFLOP/s
+# counts two FMAs per lane per packed instruction).
+FP32_VECTOR_TFLOPS = 78.6
+# The same FMA, measured with chains of independent v_fma_f32 on an MI355X at two wavefronts
+# per SIMD (the GEMM's occupancy): 33.9 T FMA/s.
+FP32_FMA_TFLOPS_AT_GEMM_OCCUPANCY = 67.8
 RESCALE_FMA_PER_EB = 2           # the rescale's FMAs per element-block (32-block of one C value)
 PAGES_QPROJ_TMACS = 15.19        # the pages' best q-proj MMQ kernel: 34.36 GMAC in 2.262 ms
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmq_qproj_traffic.json")
@@ -77,15 +83,20 @@ def measured_traffic():
 
 def epilogue_ceiling(M: int, N: int, K: int, gemm_us: float) -> dict:
     """The rescale's floor: RESCALE_FMA_PER_EB FP32 FMAs per element-block (M*N*K/32 of
-    them) at the FP32 vector peak, the GEMM rate that floor allows as a fraction of the int8
-    matrix peak, and the measured GEMM's fraction of that floor."""
+    them) at the FP32 vector rate (non-packed, as built), the GEMM rate that floor allows as
+    a fraction of the int8 matrix peak, and the measured GEMM's fraction of that floor; the
+    same at the FMA rate measured at the GEMM's occupancy."""
     fmas = RESCALE_FMA_PER_EB * M * N * (K // 32)
     floor_us = fmas * 2 / (FP32_VECTOR_TFLOPS * 1e12) * 1e6
+    occ_us = fmas * 2 / (FP32_FMA_TFLOPS_AT_GEMM_OCCUPANCY * 1e12) * 1e6
     ceiling_tops = 2 * M * N * K / (floor_us * 1e-6) / 1e12
     return {"fma_per_element_block": RESCALE_FMA_PER_EB, "valu_peak_tflops": FP32_VECTOR_TFLOPS,
             "floor_us": round(floor_us, 2),
             "ceiling_frac_of_int8_peak": round(ceiling_tops / INT8_PEAK_TOPS, 4),
-            "gemm_frac_of_ceiling": round(floor_us / gemm_us, 4)}
+            "gemm_frac_of_ceiling": round(floor_us / gemm_us, 4),
+            "valu_tflops_at_occupancy": FP32_FMA_TFLOPS_AT_GEMM_OCCUPANCY,
+            "floor_at_occupancy_us": round(occ_us, 2),
+            "gemm_frac_of_floor_at_occupancy": round(occ_us / gemm_us, 4)}
 
 
 def quant_bytes(M: int, K: int) -> int:
@@ -664,8 +675,8 @@ def main() -> int:
                      "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                      "frac": round(achieved_tops / INT8_PEAK_TOPS, 4),
                      "traffic": measured_traffic()},
-        # The GEMM's vector-ALU rescale alone, at the FP32 vector peak, bounds the GEMM
-        # below the int8 matrix peak: the ceiling it implies and how close the GEMM gets.
+        # The GEMM's vector-ALU rescale alone, at the non-packed FP32 vector rate, bounds the
+        # GEMM below the int8 matrix peak: the ceiling it implies and how close the GEMM gets.
         "epilogue_ceiling": epilogue_ceiling(M, N, K, gemm_s * 1e6),
         "us_per_gmac": round(ms_per_step * 1e3 / (macs / 1e9), 4),
         "step_gpu_us": round(t["step_gpu_us"], 2),

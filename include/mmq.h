@@ -59,13 +59,16 @@ enum mmq_tile {
   MMQ_TILE_SMALL = 2,  /* 32 tokens x 64 output features per workgroup, 2 wavefronts */
   MMQ_TILE_SKINNY = 3, /* 32 tokens x 32 output features per workgroup, K split over 8
                           wavefronts and summed in wavefront order (no block-dot output) */
-  MMQ_TILE_GEMV = 4    /* M <= 16 only (decode), 16 output features per workgroup, partial
+  MMQ_TILE_GEMV = 4,   /* M <= 16 only (decode), 16 output features per workgroup, partial
                           sums added in a fixed order, no block-dot output. M <= 8: 8
                           wavefronts, up to 8 tokens per workgroup, integer dot products on the
                           vector ALU (v_dot4_i32_i8), K split over 16 slices x 2 halves of each
                           super-block. 9 <= M <= 16: 16 wavefronts, all tokens in one workgroup, one
                           v_mfma_i32_16x16x32_i8 per block, K split over the wavefronts by
                           super-block */
+  MMQ_TILE_MEDIUM = 5  /* 32 tokens x 256 output features per workgroup, 8 wavefronts (the
+                          template of the large and small tiles); with a workspace, K may be
+                          split over workgroups (split-K, see mmq_options) */
 };
 
 /* Why the guard chose what it chose. */
@@ -81,8 +84,10 @@ enum mmq_reason {
                                    the skinny kernel, which splits K over wavefronts */
   MMQ_REASON_FUSED = 7,         /* mmq_q4K_f32: the vector-ALU (M <= 8) or skinny kernel quantizing
                                    its own activations */
-  MMQ_REASON_DECODE = 8         /* M <= 16: the decode tile, which streams the weights once
+  MMQ_REASON_DECODE = 8,        /* M <= 16: the decode tile, which streams the weights once
                                    without the large MFMA tiles' 32-token padding */
+  MMQ_REASON_SPLIT_K = 9        /* the large grid would leave compute units idle and a workspace
+                                   was given: the medium tile, K split over workgroups */
 };
 
 /* Optional knobs for the _ex entry points (NULL = defaults). */
@@ -93,6 +98,16 @@ typedef struct mmq_options {
                              workgroups; 0: the device's compute-unit count (256 in mmq_plan) */
   int64_t lds_budget;   /* > 0: check tiles against this many bytes of LDS instead of the
                            device's per-workgroup limit (lets a caller force the fallback) */
+  void* workspace;      /* device scratch for split-K partial sums, caller-owned, 16-byte
+                           aligned, or NULL: with workspace_bytes > 0 the guard may split K over
+                           workgroups (the medium tile) when the large tile's grid would leave
+                           compute units idle. Its contents on entry do not matter; on return
+                           they are undefined. The library allocates nothing */
+  int64_t workspace_bytes; /* usable bytes at workspace (0: no split-K) */
+  int32_t splits;       /* > 0: split K into exactly this many super-block ranges (1 <= splits
+                           <= K/256; more than 1 needs force_tile MEDIUM, LARGE or SMALL and a
+                           workspace of splits*M*N*4 bytes); 0: the guard decides */
+  int32_t reserved;     /* must be 0 */
 } mmq_options;
 
 /* What the guard decided for a product (filled by mmq_plan and by every GEMM call). */
@@ -105,7 +120,11 @@ typedef struct mmq_kernel_info {
   int32_t fallback;     /* 1 when the large tile was rejected by the LDS budget */
   int64_t lds_bytes;    /* LDS the chosen kernel uses (0 when none) */
   int64_t lds_budget;   /* budget the guard checked against */
-  int64_t grid;         /* workgroups launched (1-D grid) */
+  int64_t grid;         /* workgroups launched by the GEMM kernel (1-D grid) */
+  int32_t splits;       /* K ranges the GEMM is split into (1: no split-K) */
+  int32_t reserved;
+  int64_t workspace_bytes; /* workspace the split-K partial sums use: splits*M*N*4 when
+                              splits > 1, else 0 */
 } mmq_kernel_info;
 
 /* ---------------------------------------------------------------- sizes (host only) */
@@ -189,9 +208,26 @@ int repack_q4_K(const void* w_q4K, int64_t N, int64_t K, void* w_rep, void* stre
 int mmq_q4K_q8_1(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
                  float* C, void* stream);
 
-/* As mmq_q4K_q8_1, with options (tile choice, LDS budget); opt may be NULL. */
+/*
+ * As mmq_q4K_q8_1, with options (tile choice, LDS budget, split-K workspace); opt may be NULL.
+ * With a workspace (opt->workspace, opt->workspace_bytes) and a product whose large-tile grid
+ * would leave compute units idle (few tokens or few output features: M = 128..1024 at
+ * N = 4096, one GPU's share of a column-split layer), the guard may choose the medium tile
+ * with K split into `splits` ranges of super-blocks: each workgroup writes the partial sums
+ * of its range to plane [split] of the workspace ([splits][M][N] float32), and a second kernel
+ * adds the planes into C in increasing split order. The result is deterministic (the same
+ * bits on every call) and within the same bound as the unsplit product, but it associates
+ * the sum differently. Both kernels run on `stream`; the workspace must not be used by other
+ * work until the call's kernels have finished.
+ * Errors: as mmq_q4K_q8_1; MMQ_E_ARG for a bad option (a null or misaligned workspace with
+ * workspace_bytes > 0, a forced split the workspace cannot hold, reserved != 0).
+ */
 int mmq_q4K_q8_1_ex(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
                     float* C, void* stream, const mmq_options* opt);
+
+/* Bytes of split-K workspace the guard would use for an M x N x K product given an unlimited
+ * workspace (0 when it would not split K). Host only. */
+int mmq_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
 
 /*
  * mmq_q4K_f32: the product for few tokens straight from float32 activations x[M][K]
@@ -233,7 +269,9 @@ int mmq_q4K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, cons
  * when set, takes precedence): for M <= 16 the decode tile (MMQ_TILE_GEMV, reason
  * MMQ_REASON_DECODE); else the large tile when it fits and its grid has at least
  * opt->min_workgroups workgroups (default 256, the MI355X compute-unit count; a GEMM call
- * uses the device's count); else, for M <= 128 and K >= 2048 (at least one super-block for
+ * uses the device's count); else, when the options carry a workspace, the medium tile with
+ * K split so that the grid fills the compute units (MMQ_REASON_SPLIT_K; see
+ * mmq_q4K_q8_1_ex); else, for M <= 128 and K >= 2048 (at least one super-block for
  * each of its wavefronts), the skinny kernel; else the small tile (more,
  * smaller workgroups: at M = 512, N = 4096 the large tile has 64 workgroups for 256 compute
  * units); when the large tile does not fit the budget, the small tile; else MMQ_E_LDS. A

@@ -32,17 +32,20 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 
 MMQ_OK, MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_LDS, MMQ_E_DEVICE, MMQ_E_HIP = range(6)
-MMQ_TILE_AUTO, MMQ_TILE_LARGE, MMQ_TILE_SMALL, MMQ_TILE_SKINNY, MMQ_TILE_GEMV = 0, 1, 2, 3, 4
+(MMQ_TILE_AUTO, MMQ_TILE_LARGE, MMQ_TILE_SMALL, MMQ_TILE_SKINNY, MMQ_TILE_GEMV,
+ MMQ_TILE_MEDIUM) = range(6)
 (MMQ_REASON_NONE, MMQ_REASON_LARGE, MMQ_REASON_SMALL_GRID, MMQ_REASON_LDS_FALLBACK,
  MMQ_REASON_FORCED, MMQ_REASON_NO_FIT, MMQ_REASON_FEW_TOKENS, MMQ_REASON_FUSED,
- MMQ_REASON_DECODE) = range(9)
+ MMQ_REASON_DECODE, MMQ_REASON_SPLIT_K) = range(10)
 GEMV_MAX_M = 16  # largest M of the decode tile, which the guard chooses up to there
 QK8, QK_K, Q4K_BLOCK_BYTES, REP_TILE_ROWS, REP_TILE_BYTES = 32, 256, 144, 32, 6656
 
 
 class mmq_options(ctypes.Structure):
     _fields_ = [("force_tile", ctypes.c_int32), ("min_workgroups", ctypes.c_int32),
-                ("lds_budget", ctypes.c_int64)]
+                ("lds_budget", ctypes.c_int64), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_int64), ("splits", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class mmq_kernel_info(ctypes.Structure):
@@ -50,7 +53,8 @@ class mmq_kernel_info(ctypes.Structure):
                 ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
                 ("threads", ctypes.c_int32), ("fallback", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int64), ("lds_budget", ctypes.c_int64),
-                ("grid", ctypes.c_int64)]
+                ("grid", ctypes.c_int64), ("splits", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -74,6 +78,7 @@ _SIGS = {
     "mmq_q4K_q8_1": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "mmq_q4K_q8_1_ex": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.POINTER(mmq_options)],
     "mmq_q4K_f32": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
+    "mmq_workspace_bytes": [_i64, _i64, _i64, ctypes.POINTER(_sz)],
     "mmq_q4K_q8_1_blockdots": [_i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp,
                                ctypes.POINTER(mmq_options)],
     "mmq_plan": [_i64, _i64, _i64, ctypes.POINTER(mmq_options), _i64,
@@ -154,10 +159,21 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream
 
 
-def _opts(force_tile: int = MMQ_TILE_AUTO, lds_budget: int = 0, min_workgroups: int = 0):
-    if force_tile == MMQ_TILE_AUTO and lds_budget == 0 and min_workgroups == 0:
+def _opts(force_tile: int = MMQ_TILE_AUTO, lds_budget: int = 0, min_workgroups: int = 0,
+          workspace: int | None = None, workspace_bytes: int = 0, splits: int = 0):
+    if (force_tile == MMQ_TILE_AUTO and lds_budget == 0 and min_workgroups == 0
+            and workspace_bytes == 0 and splits == 0):
         return None
-    return ctypes.byref(mmq_options(force_tile, min_workgroups, lds_budget))
+    return ctypes.byref(mmq_options(force_tile, min_workgroups, lds_budget, workspace,
+                                    workspace_bytes, splits, 0))
+
+
+def _workspace(workspace):
+    """(pointer, bytes) of an optional split-K workspace tensor (a contiguous CUDA tensor)."""
+    if workspace is None:
+        return None, 0
+    nbytes = workspace.numel() * workspace.element_size()
+    return _dev(workspace, "workspace", 0), nbytes
 
 
 # ---------------------------------------------------------------- sizes
@@ -208,11 +224,21 @@ def mmq_q4K_q8_1(M: int, N: int, K: int, q8, w_rep, C, stream=None) -> None:
 
 def mmq_q4K_q8_1_ex(M: int, N: int, K: int, q8, w_rep, C, stream=None,
                     force_tile: int = MMQ_TILE_AUTO, lds_budget: int = 0,
-                    min_workgroups: int = 0) -> None:
+                    min_workgroups: int = 0, workspace=None, splits: int = 0) -> None:
+    """As mmq_q4K_q8_1 with options; `workspace` (any contiguous CUDA tensor, its whole byte
+    size usable) lets the guard split K over workgroups, `splits` forces a split count."""
     qp, rp, cp = _gemm_ptrs(M, N, K, q8, w_rep, C)
+    wp, wb = _workspace(workspace)
     _check("mmq_q4K_q8_1_ex",
            _lib.mmq_q4K_q8_1_ex(M, N, K, qp, rp, cp, _stream(stream),
-                                _opts(force_tile, lds_budget, min_workgroups)))
+                                _opts(force_tile, lds_budget, min_workgroups, wp, wb, splits)))
+
+
+def mmq_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Split-K workspace the guard would use for M x N x K given an unlimited one (0: none)."""
+    n = _sz()
+    _check("mmq_workspace_bytes", _lib.mmq_workspace_bytes(M, N, K, ctypes.byref(n)))
+    return n.value
 
 
 def mmq_q4K_f32(M: int, N: int, K: int, x, w_rep, C, stream=None) -> None:
@@ -237,9 +263,11 @@ def mmq_q4K_q8_1_blockdots(M: int, N: int, K: int, q8, w_rep, i0: int, i1: int, 
 
 # ---------------------------------------------------------------- the guard
 def mmq_plan(M: int, N: int, K: int, lds_budget: int, force_tile: int = MMQ_TILE_AUTO,
-             opt_lds_budget: int = 0, min_workgroups: int = 0) -> dict:
+             opt_lds_budget: int = 0, min_workgroups: int = 0, workspace_bytes: int = 0,
+             splits: int = 0) -> dict:
     info = mmq_kernel_info()
-    _check("mmq_plan", _lib.mmq_plan(M, N, K, _opts(force_tile, opt_lds_budget, min_workgroups),
+    _check("mmq_plan", _lib.mmq_plan(M, N, K, _opts(force_tile, opt_lds_budget, min_workgroups,
+                                                    None, workspace_bytes, splits),
                                      lds_budget, ctypes.byref(info)))
     return info.as_dict()
 

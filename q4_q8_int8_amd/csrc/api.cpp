@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
 #include <mutex>
 
@@ -38,6 +39,7 @@ constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every in-kernel 32-bit i
 constexpr int64_t kMaxK = (int64_t)1 << 24;
 
 constexpr int64_t kDefaultComputeUnits = 256;  // MI355X; mmq_plan assumes it
+constexpr int64_t kDefaultLdsBudget = 160 * 1024;  // MI355X per-workgroup LDS
 // Up to this many tokens the skinny kernel (K split over the wavefronts of a workgroup) beats
 // the small tile: at K = N = 4096 it takes 7.7 / 9.8 / 24.6 us for M = 1 / 16 / 128 against
 // 28.8 / 28.8 / 30.6 us, and loses at M = 512 (85 against 42 us).
@@ -113,11 +115,41 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 
 int check_options(const mmq_options* opt) {
   if (!opt) return MMQ_OK;
-  if (opt->force_tile < MMQ_TILE_AUTO || opt->force_tile > MMQ_TILE_GEMV)
+  if (opt->force_tile < MMQ_TILE_AUTO || opt->force_tile > MMQ_TILE_MEDIUM)
     return fail(MMQ_E_ARG, "force_tile %d is not an mmq_tile", opt->force_tile);
   if (opt->lds_budget < 0) return fail(MMQ_E_ARG, "negative lds_budget");
   if (opt->min_workgroups < 0) return fail(MMQ_E_ARG, "negative min_workgroups");
+  if (opt->workspace_bytes < 0) return fail(MMQ_E_ARG, "negative workspace_bytes");
+  if (opt->splits < 0) return fail(MMQ_E_ARG, "negative splits");
+  if (opt->reserved != 0) return fail(MMQ_E_ARG, "mmq_options.reserved must be 0");
   return MMQ_OK;
+}
+
+// Split-K: at most this many super-block ranges (the partial planes cost 8*M*N bytes of
+// memory traffic each, written and read back).
+constexpr int64_t kMaxSplits = 16;
+
+// The guard's cost model of the template's tiles, fitted to graph-replayed timings of 11
+// few-token and few-feature shapes (M = 32..1024 at N = 4096, K = 4096 and 11008; one GPU's
+// share of an 8-way column split of the 7B projections) under every tile and split count
+// 1..16: a workgroup spends c microseconds per super-block, `occ` workgroups share a compute
+// unit, and each split adds its partial plane's traffic. The model's pick is within 3 % of
+// the fastest measured choice on average (20 % at worst).
+struct TileCost {
+  int tile;
+  double us_per_sb;  // per super-block and round of workgroups
+  double occ;        // workgroups per compute unit (registers and LDS)
+};
+constexpr TileCost kTileCosts[] = {{MMQ_TILE_LARGE, 3.83, 1.0},
+                                   {MMQ_TILE_MEDIUM, 1.85, 1.0},
+                                   {MMQ_TILE_SMALL, 1.35, 3.0}};
+constexpr double kUsPerPartialMB = 0.234;
+// The skinny kernel in the same model: one workgroup per 32 x 32 output tile and compute
+// unit at a time, its 8 wavefronts each walking K/8 super-blocks.
+constexpr double kSkinnyUsPerSb = 4.8;
+
+mmq::TileShape tile_shape(int tile) {
+  return tile == MMQ_TILE_LARGE ? mmq::kLarge : tile == MMQ_TILE_MEDIUM ? mmq::kMedium : mmq::kSmall;
 }
 
 // The guard: which tile, given the LDS budget and the compute units the grid should fill.
@@ -135,13 +167,33 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
   info->lds_budget = budget;
   const int64_t need_large = mmq::kLarge.lds_bytes();
   const int64_t need_small = mmq::kSmall.lds_bytes();
+  const int64_t need_medium = mmq::kMedium.lds_bytes();
   const int forced = opt ? opt->force_tile : MMQ_TILE_AUTO;
+  const int64_t nsb = K / 256;
+  const int64_t ws_bytes = opt ? opt->workspace_bytes : 0;
+  const int64_t forced_splits = opt ? opt->splits : 0;
+  auto plane_bytes = [&](int64_t sp) { return sp > 1 ? sp * M * N * 4 : 0; };
+  if (forced_splits > 0) {
+    if (forced_splits > nsb)
+      return fail(MMQ_E_ARG, "splits = %lld is more than the %lld super-blocks of K",
+                  (long long)forced_splits, (long long)nsb);
+    if (forced_splits > 1 && forced != MMQ_TILE_MEDIUM && forced != MMQ_TILE_LARGE &&
+        forced != MMQ_TILE_SMALL)
+      return fail(MMQ_E_ARG, "split-K needs force_tile MEDIUM, LARGE or SMALL");
+    if (plane_bytes(forced_splits) > ws_bytes)
+      return fail(MMQ_E_ARG, "%lld splits need %lld bytes of workspace, %lld given",
+                  (long long)forced_splits, (long long)plane_bytes(forced_splits),
+                  (long long)ws_bytes);
+  }
+  int64_t splits = forced_splits > 0 ? forced_splits : 1;
 
   int tile = 0, reason = MMQ_REASON_NONE, fallback = 0;
   if (forced == MMQ_TILE_LARGE) {
     if (need_large <= budget) { tile = MMQ_TILE_LARGE; reason = MMQ_REASON_FORCED; }
   } else if (forced == MMQ_TILE_SMALL) {
     if (need_small <= budget) { tile = MMQ_TILE_SMALL; reason = MMQ_REASON_FORCED; }
+  } else if (forced == MMQ_TILE_MEDIUM) {
+    if (need_medium <= budget) { tile = MMQ_TILE_MEDIUM; reason = MMQ_REASON_FORCED; }
   } else if (forced == MMQ_TILE_SKINNY) {
     if (mmq::skinny_lds_bytes() <= budget) { tile = MMQ_TILE_SKINNY; reason = MMQ_REASON_FORCED; }
   } else if (forced == MMQ_TILE_GEMV) {
@@ -152,15 +204,44 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
   } else if (M <= mmq::kGemvAutoMaxM && mmq::gemv_lds_bytes(M) <= budget) {
     tile = MMQ_TILE_GEMV; reason = MMQ_REASON_DECODE;
   } else if (need_large <= budget) {
-    if (grid_of(mmq::kLarge) >= min_wg) {
-      tile = MMQ_TILE_LARGE; reason = MMQ_REASON_LARGE;
-    } else if (M <= kSkinnyMaxM && K / 256 >= mmq::kSkinnyWaves &&
-               mmq::skinny_lds_bytes() <= budget) {
-      // (the skinny kernel splits K over its wavefronts: below 8 super-blocks some of them
-      // get none, and the small tile is faster: 5.5 against 7.6 us at 128 x 256 x 512)
+    // the cheapest (tile, splits) under the cost model: splits only with a workspace that
+    // holds their planes, each split at least one super-block
+    const double cus = (double)compute_units;
+    double best = 1e300;
+    int best_tile = 0;
+    int64_t best_sp = 1;
+    if (M <= kSkinnyMaxM && nsb >= mmq::kSkinnyWaves && mmq::skinny_lds_bytes() <= budget) {
+      // (below 8 super-blocks some of the skinny kernel's wavefronts get none, and the small
+      // tile is faster: 5.5 against 7.6 us at 128 x 256 x 512)
+      const double grid = (double)(((M + 31) / 32) * ((N + 31) / 32));
+      const double rounds = grid / cus > 1.0 ? grid / cus : 1.0;
+      best = kSkinnyUsPerSb * rounds * (double)((nsb + mmq::kSkinnyWaves - 1) / mmq::kSkinnyWaves);
+      best_tile = MMQ_TILE_SKINNY;
+    }
+    for (const TileCost& c : kTileCosts) {
+      if (tile_shape(c.tile).lds_bytes() > budget) continue;
+      for (int64_t sp = 1; sp <= kMaxSplits && sp <= nsb; sp *= 2) {
+        if (sp > 1 && plane_bytes(sp) > ws_bytes) break;
+        // the large tile only with a grid of at least min_wg workgroups
+        if (c.tile == MMQ_TILE_LARGE && grid_of(mmq::kLarge) * sp < min_wg) continue;
+        const double grid = (double)grid_of(tile_shape(c.tile)) * (double)sp;
+        const double rounds = grid / (cus * c.occ) > 1.0 ? grid / (cus * c.occ) : 1.0;
+        const double per_wg = (double)((nsb + sp - 1) / sp);
+        double cost = c.us_per_sb * rounds * per_wg;
+        if (sp > 1) cost += kUsPerPartialMB * (double)(8 * sp + 4) * (double)M * (double)N * 1e-6;
+        if (cost < best) { best = cost; best_tile = c.tile; best_sp = sp; }
+      }
+    }
+    if ((grid_of(mmq::kLarge) >= min_wg && ws_bytes == 0) || best_tile == MMQ_TILE_LARGE) {
+      tile = MMQ_TILE_LARGE;
+      reason = best_sp > 1 ? MMQ_REASON_SPLIT_K : MMQ_REASON_LARGE;
+      splits = grid_of(mmq::kLarge) >= min_wg && ws_bytes == 0 ? 1 : best_sp;
+    } else if (best_sp > 1) {
+      tile = best_tile; reason = MMQ_REASON_SPLIT_K; splits = best_sp;
+    } else if (best_tile == MMQ_TILE_SKINNY) {
       tile = MMQ_TILE_SKINNY; reason = MMQ_REASON_FEW_TOKENS;
     } else {
-      tile = MMQ_TILE_SMALL; reason = MMQ_REASON_SMALL_GRID;
+      tile = best_tile ? best_tile : MMQ_TILE_SMALL; reason = MMQ_REASON_SMALL_GRID;
     }
   } else if (need_small <= budget) {
     tile = MMQ_TILE_SMALL; reason = MMQ_REASON_LDS_FALLBACK; fallback = 1;
@@ -173,6 +254,9 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
   info->tile = tile;
   info->reason = reason;
   info->fallback = fallback;
+  info->splits = 1;
+  if (splits > 1 && tile != MMQ_TILE_MEDIUM && tile != MMQ_TILE_LARGE && tile != MMQ_TILE_SMALL)
+    splits = 1;  // (an LDS fallback to another kind of kernel drops a forced split)
   if (tile == MMQ_TILE_GEMV) {
     info->block_m = (int32_t)mmq::gemv_group(M);
     info->block_n = mmq::kGemvRows;
@@ -189,7 +273,7 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
     info->grid = ((M + 31) / 32) * ((N + 31) / 32);
     return MMQ_OK;
   }
-  const mmq::TileShape ts = tile == MMQ_TILE_LARGE ? mmq::kLarge : mmq::kSmall;
+  const mmq::TileShape ts = tile_shape(tile);
   const int64_t gm = (M + ts.block_m() - 1) / ts.block_m();
   const int64_t ntiles = (N + 31) / 32;
   const int64_t gn = (ntiles + ts.nw - 1) / ts.nw;
@@ -197,12 +281,37 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
   info->block_n = ts.block_n();
   info->threads = ts.threads();
   info->lds_bytes = ts.lds_bytes();
-  info->grid = gm * gn;
+  info->grid = gm * gn * splits;
+  info->splits = (int32_t)splits;
+  info->workspace_bytes = plane_bytes(splits);
   return MMQ_OK;
 }
 
 int hip_fail(const char* what, hipError_t e) {
   return fail(MMQ_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Launch what the guard planned; with split-K the GEMM writes the partial planes into ws and
+// a second kernel adds them into C, both on the stream.
+int launch_planned(const mmq_kernel_info& info, int64_t M, int64_t N, int64_t K, const void* q8,
+                   const void* w_rep, float* C, void* ws, hipStream_t stream) {
+  hipError_t e;
+  if (info.tile == MMQ_TILE_GEMV) {
+    e = mmq::launch_mmq_gemv(q8, w_rep, C, M, N, K, stream);
+  } else if (info.tile == MMQ_TILE_SKINNY) {
+    e = mmq::launch_mmq_skinny(q8, w_rep, C, M, N, K, stream);
+  } else {
+    const mmq::TileShape ts = tile_shape(info.tile);
+    const int64_t gm = (M + ts.block_m() - 1) / ts.block_m();
+    const int64_t gn = ((N + 31) / 32 + ts.nw - 1) / ts.nw;
+    const int64_t sp = info.splits;
+    e = mmq::launch_mmq(info.tile, q8, w_rep, sp > 1 ? ws : C, M, N, K, gm, gn, sp, 0, 0, false,
+                        0, 0, 0, 0, stream);
+    if (e == hipSuccess && sp > 1)
+      e = mmq::launch_reduce_splits(static_cast<const float*>(ws), C, M, N, sp, stream);
+  }
+  if (e != hipSuccess) return hip_fail("mmq_q4K_q8_1 launch", e);
+  return ok();
 }
 
 }  // namespace
@@ -290,25 +399,27 @@ int mmq_q4K_q8_1_ex(int64_t M, int64_t N, int64_t K, const void* q8, const void*
   if (!q8 || !w_rep || !C) return fail(MMQ_E_ARG, "null device pointer");
   if (!aligned16(q8) || !aligned16(w_rep) || !aligned16(C))
     return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
+  if (opt && opt->workspace_bytes > 0 && (!opt->workspace || !aligned16(opt->workspace)))
+    return fail(MMQ_E_ARG, "workspace_bytes > 0 needs a 16-byte aligned workspace");
   DeviceInfo* di;
   if ((st = current_device(&di))) return st;
   mmq_kernel_info info;
   st = plan(M, N, K, opt, di->lds_budget, di->compute_units, &info);
   g_last = info;
   if (st) return st;
-  hipError_t e;
-  if (info.tile == MMQ_TILE_GEMV) {
-    e = mmq::launch_mmq_gemv(q8, w_rep, C, M, N, K, static_cast<hipStream_t>(stream));
-  } else if (info.tile == MMQ_TILE_SKINNY) {
-    e = mmq::launch_mmq_skinny(q8, w_rep, C, M, N, K, static_cast<hipStream_t>(stream));
-  } else {
-    const mmq::TileShape ts = info.tile == MMQ_TILE_LARGE ? mmq::kLarge : mmq::kSmall;
-    const int64_t gm = (M + ts.block_m() - 1) / ts.block_m();
-    const int64_t gn = info.grid / gm;
-    e = mmq::launch_mmq(info.tile, q8, w_rep, C, M, N, K, gm, gn, 0, 0, false, 0, 0, 0, 0,
+  return launch_planned(info, M, N, K, q8, w_rep, C, opt ? opt->workspace : nullptr,
                         static_cast<hipStream_t>(stream));
-  }
-  if (e != hipSuccess) return hip_fail("mmq_q4K_q8_1 launch", e);
+}
+
+int mmq_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(MMQ_E_ARG, "bytes is NULL");
+  int st = check_gemm_shape(M, N, K);
+  if (st) return st;
+  mmq_options o = {};
+  o.workspace_bytes = INT64_MAX;
+  mmq_kernel_info info;
+  if ((st = plan(M, N, K, &o, kDefaultLdsBudget, kDefaultComputeUnits, &info))) return st;
+  *bytes = (size_t)info.workspace_bytes;
   return ok();
 }
 
@@ -380,28 +491,34 @@ int mmq_q4K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, cons
                 (long long)N);
   if (opt && (opt->force_tile == MMQ_TILE_SKINNY || opt->force_tile == MMQ_TILE_GEMV))
     return fail(MMQ_E_ARG, "the skinny and vector-ALU tiles have no block-dot output; force "
-                           "large or small");
+                           "large, medium or small");
+  if (opt && opt->splits > 1)
+    return fail(MMQ_E_ARG, "the block dots are written without split-K");
   DeviceInfo* di;
   if ((st = current_device(&di))) return st;
   mmq_kernel_info info;
   st = plan(M, N, K, opt, di->lds_budget, di->compute_units, &info);
-  if (!st && (info.tile == MMQ_TILE_SKINNY || info.tile == MMQ_TILE_GEMV)) {
-    // the block dots come from the small tile
+  if (!st && (info.tile == MMQ_TILE_SKINNY || info.tile == MMQ_TILE_GEMV || info.splits > 1)) {
+    // the block dots come from the small tile, unsplit
     mmq_options o = opt ? *opt : mmq_options{};
     o.force_tile = MMQ_TILE_SMALL;
+    o.workspace_bytes = 0;
+    o.splits = 0;
     st = plan(M, N, K, &o, di->lds_budget, di->compute_units, &info);
   }
   g_last = info;
   if (st) return st;
-  const mmq::TileShape ts = info.tile == MMQ_TILE_LARGE ? mmq::kLarge : mmq::kSmall;
+  const mmq::TileShape ts = tile_shape(info.tile);
   const int64_t tm0 = i0 / ts.block_m();
   const int64_t tm1 = (i1 + ts.block_m() - 1) / ts.block_m();
   const int64_t tn0 = j0 / ts.block_n();
   const int64_t tn1 = (j1 + ts.block_n() - 1) / ts.block_n();
   const int64_t gm = tm1 - tm0, gn = tn1 - tn0;
   g_last.grid = gm * gn;
-  hipError_t e = mmq::launch_mmq(info.tile, q8, w_rep, S, M, N, K, gm, gn, tm0, tn0, true, i0,
-                                 i1, j0, j1, static_cast<hipStream_t>(stream));
+  g_last.splits = 1;
+  g_last.workspace_bytes = 0;
+  hipError_t e = mmq::launch_mmq(info.tile, q8, w_rep, S, M, N, K, gm, gn, 1, tm0, tn0, true,
+                                 i0, i1, j0, j1, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail("mmq_q4K_q8_1_blockdots launch", e);
   return ok();
 }

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
     const int8_t* __restrict__ qs, const float* __restrict__ da_plane,
     const uint16_t* __restrict__ tpieces,
     const uint8_t* __restrict__ wrep, void* __restrict__ out, int M, int N, int K, int gm,
-    int tm0, int tn0, int i0, int i1, int j0, int j1) {
+    int gmn, int splits, int tm0, int tn0, int i0, int i1, int j0, int j1) {
   constexpr int BM = 32 * TT;
   constexpr int NS = 8 * TT;                      // (block, token tile) steps per super-block
   constexpr int A_BYTES = BM * kRowStride;        // token tile
@@ -89,8 +89,12 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  const int tm = tm0 + (int)(blockIdx.x % (unsigned)gm);
-  const int tn = tn0 + (int)(blockIdx.x / (unsigned)gm);
+  // Workgroup (tile, split): split sp walks super-blocks [sb0, sb1) of K and writes its partial
+  // sums to plane sp of out ([splits][M][N]); with one split the plane is C itself.
+  const int sp = (int)(blockIdx.x / (unsigned)gmn);
+  const int tile_id = (int)(blockIdx.x - (unsigned)sp * (unsigned)gmn);
+  const int tm = tm0 + tile_id % gm;
+  const int tn = tn0 + tile_id / gm;
   const int m0 = tm * BM;
   const int ntiles = (N + 31) >> 5;
   const int wt_raw = tn * NW + wave;
@@ -98,6 +102,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   const int wt = wt_ok ? wt_raw : ntiles - 1;  // idle wavefronts still stage and sync
   const int nsb = K >> 8;
   const int kb = K >> 5;
+  const int sb0 = sp * nsb / splits, sb1 = (sp + 1) * nsb / splits;
   const v4i rq = make_rsrc_sgpr(qs, (uint32_t)M * (uint32_t)K);
   const v4i rda = make_rsrc_sgpr(da_plane, (uint32_t)M * (uint32_t)kb * 8u);
   const v4i rtp = make_rsrc_sgpr(tpieces, (uint32_t)M * (uint32_t)nsb * 48u);
@@ -195,16 +200,16 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   // issued; group 3 is still in use at the end of the stage, so it goes through nib3.
   v4i raw[4], nib3;
 #pragma unroll
-  for (int v = 0; v < NOPS; ++v) issue_op(v, 0, 0, nib3);
+  for (int v = 0; v < NOPS; ++v) issue_op(v, sb0, 0, nib3);
 #pragma unroll
-  for (int g = 0; g < 3; ++g) raw[g] = load_nib(0, g);
+  for (int g = 0; g < 3; ++g) raw[g] = load_nib(sb0, g);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int s = 0; s < nsb; ++s) {
-    const int p = s & 1;
+  for (int s = sb0; s < sb1; ++s) {
+    const int p = (s - sb0) & 1;
     raw[3] = nib3;
-    const bool more = s + 1 < nsb;
+    const bool more = s + 1 < sb1;
 
     const uint8_t* st = smem + p * STAGE;
     const uint8_t* sArow = st + l32 * kRowStride + h * 16;
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
     // rows; after the transpose 8 consecutive lanes write one token row's 128 contiguous
     // bytes. Each wavefront uses its own 32 x 36 float region, double-buffered over t.
     constexpr int TS = 36;  // row stride in floats: rows 36 dwords apart hit distinct banks
-    float* C = static_cast<float*>(out);
+    float* C = static_cast<float*>(out) + (size_t)sp * (size_t)M * (size_t)N;
     const int j0c = wt * 32;
     const int rr = lane >> 3, c4 = lane & 7;  // read-back: rows rr + 8k, columns 4*c4..+3
 #pragma unroll
@@ -356,8 +361,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
 
 template <int TT, int NW, bool STORE_S>
 hipError_t launch_t(const void* q8, const void* w_rep, void* out, int64_t M, int64_t N,
-                    int64_t K, int64_t gm, int64_t gn, int64_t tm0, int64_t tn0, int64_t i0,
-                    int64_t i1, int64_t j0, int64_t j1, hipStream_t s) {
+                    int64_t K, int64_t gm, int64_t gn, int64_t splits, int64_t tm0, int64_t tn0,
+                    int64_t i0, int64_t i1, int64_t j0, int64_t j1, hipStream_t s) {
   constexpr TileShape ts{TT, NW};
   const uint8_t* base = static_cast<const uint8_t*>(q8);
   const int8_t* qs = reinterpret_cast<const int8_t*>(base);
@@ -370,28 +375,77 @@ hipError_t launch_t(const void* q8, const void* w_rep, void* out, int64_t M, int
                                        (int)ts.lds_bytes());
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)(gm * gn)), dim3(ts.threads()), (size_t)ts.lds_bytes(),
-                     s, qs, da_plane, tpieces, static_cast<const uint8_t*>(w_rep), out, (int)M, (int)N,
-                     (int)K, (int)gm, (int)tm0, (int)tn0, (int)i0, (int)i1, (int)j0, (int)j1);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(gm * gn * splits)), dim3(ts.threads()),
+                     (size_t)ts.lds_bytes(), s, qs, da_plane, tpieces,
+                     static_cast<const uint8_t*>(w_rep), out, (int)M, (int)N, (int)K, (int)gm,
+                     (int)(gm * gn), (int)splits, (int)tm0, (int)tn0, (int)i0, (int)i1, (int)j0,
+                     (int)j1);
   return hipGetLastError();
+}
+
+// C = the sum of the partial planes ws[0..splits), added in increasing split order (so the
+// result is deterministic), four consecutive elements per thread when N % 4 == 0.
+template <bool VEC4>
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ ws,
+                                                            float* __restrict__ C, int64_t n,
+                                                            int splits) {
+  const int64_t plane = n;
+  if constexpr (VEC4) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    float4 a = *reinterpret_cast<const float4*>(ws + i);
+    for (int sp = 1; sp < splits; ++sp) {
+      const float4 b = *reinterpret_cast<const float4*>(ws + sp * plane + i);
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    *reinterpret_cast<float4*>(C + i) = a;
+  } else {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float a = ws[i];
+    for (int sp = 1; sp < splits; ++sp) a += ws[sp * plane + i];
+    C[i] = a;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_mmq(int tile, const void* q8, const void* w_rep, void* out, int64_t M,
-                      int64_t N, int64_t K, int64_t gm, int64_t gn, int64_t tm0, int64_t tn0,
-                      bool store_s, int64_t i0, int64_t i1, int64_t j0, int64_t j1,
+                      int64_t N, int64_t K, int64_t gm, int64_t gn, int64_t splits, int64_t tm0,
+                      int64_t tn0, bool store_s, int64_t i0, int64_t i1, int64_t j0, int64_t j1,
                       hipStream_t s) {
+  constexpr TileShape L = kLarge, S = kSmall, D = kMedium;
   if (tile == 1) {
-    return store_s ? launch_t<kLarge.tt, kLarge.nw, true>(q8, w_rep, out, M, N, K, gm, gn, tm0,
-                                                          tn0, i0, i1, j0, j1, s)
-                   : launch_t<kLarge.tt, kLarge.nw, false>(q8, w_rep, out, M, N, K, gm, gn,
-                                                           tm0, tn0, i0, i1, j0, j1, s);
+    return store_s ? launch_t<L.tt, L.nw, true>(q8, w_rep, out, M, N, K, gm, gn, 1, tm0, tn0,
+                                                i0, i1, j0, j1, s)
+                   : launch_t<L.tt, L.nw, false>(q8, w_rep, out, M, N, K, gm, gn, splits, tm0,
+                                                 tn0, i0, i1, j0, j1, s);
   }
-  return store_s ? launch_t<kSmall.tt, kSmall.nw, true>(q8, w_rep, out, M, N, K, gm, gn, tm0,
-                                                        tn0, i0, i1, j0, j1, s)
-                 : launch_t<kSmall.tt, kSmall.nw, false>(q8, w_rep, out, M, N, K, gm, gn, tm0,
-                                                         tn0, i0, i1, j0, j1, s);
+  if (tile == 5) {
+    return store_s ? launch_t<D.tt, D.nw, true>(q8, w_rep, out, M, N, K, gm, gn, 1, tm0, tn0,
+                                                i0, i1, j0, j1, s)
+                   : launch_t<D.tt, D.nw, false>(q8, w_rep, out, M, N, K, gm, gn, splits, tm0,
+                                                 tn0, i0, i1, j0, j1, s);
+  }
+  return store_s ? launch_t<S.tt, S.nw, true>(q8, w_rep, out, M, N, K, gm, gn, 1, tm0, tn0, i0,
+                                              i1, j0, j1, s)
+                 : launch_t<S.tt, S.nw, false>(q8, w_rep, out, M, N, K, gm, gn, splits, tm0, tn0,
+                                               i0, i1, j0, j1, s);
+}
+
+hipError_t launch_reduce_splits(const float* ws, float* C, int64_t M, int64_t N, int64_t splits,
+                                hipStream_t s) {
+  const int64_t n = M * N;
+  if (N % 4 == 0) {
+    const int64_t blocks = (n / 4 + 255) / 256;
+    hipLaunchKernelGGL(reduce_splits_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, ws, C,
+                       n, (int)splits);
+  } else {
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(reduce_splits_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, ws,
+                       C, n, (int)splits);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace mmq

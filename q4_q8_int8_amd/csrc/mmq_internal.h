@@ -38,6 +38,8 @@ struct TileShape {
 };
 constexpr TileShape kLarge{4, 8};
 constexpr TileShape kSmall{1, 2};
+// 32 tokens x 256 weight rows, 8 wavefronts: the tile that splits K over workgroups
+constexpr TileShape kMedium{1, 8};
 
 // q8 buffer: int8 q [M][K], u32 scale words [M][K/32], then (each at a 256-byte boundary)
 // the GEMM's planes: f32 pairs (da, nda = -kBiasF * da) [K/32][M][2], and dma = da*sa as
@@ -118,13 +120,17 @@ hipError_t launch_mmq_gemv_fused(const float* x, const void* w_rep, float* C, in
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, hipStream_t s);
 hipError_t launch_repack_q4_K(const void* w, int64_t N, int64_t K, void* w_rep, hipStream_t s);
 
-// GEMM launch: a 1-D grid of gm*gn workgroups covering token tiles [tm0, tm0+gm) and
-// weight-tile groups [tn0, tn0+gn). store_s selects the store-S epilogue (S written to
-// out as int32 [K/32][i1-i0][j1-j0]); otherwise out is C.
+// GEMM launch: a 1-D grid of gm*gn*splits workgroups covering token tiles [tm0, tm0+gm),
+// weight-tile groups [tn0, tn0+gn) and `splits` contiguous ranges of super-blocks. store_s
+// selects the store-S epilogue (S written to out as int32 [K/32][i1-i0][j1-j0], one split);
+// otherwise out is C when splits == 1, else the partial planes [splits][M][N] f32 that
+// launch_reduce_splits adds into C. tile: 1 large, 2 small, 5 medium (kMedium).
 hipError_t launch_mmq(int tile, const void* q8, const void* w_rep, void* out, int64_t M,
-                      int64_t N, int64_t K, int64_t gm, int64_t gn, int64_t tm0, int64_t tn0,
-                      bool store_s, int64_t i0, int64_t i1, int64_t j0, int64_t j1,
+                      int64_t N, int64_t K, int64_t gm, int64_t gn, int64_t splits, int64_t tm0,
+                      int64_t tn0, bool store_s, int64_t i0, int64_t i1, int64_t j0, int64_t j1,
                       hipStream_t s);
+hipError_t launch_reduce_splits(const float* ws, float* C, int64_t M, int64_t N, int64_t splits,
+                                hipStream_t s);
 
 // The f16 comparator path: f32 -> f16 conversion of n values, q4_K -> f16 dequantization,
 // and the f16 GEMM (K % 8 == 0, 2*M*K and 2*N*K below 2^31).

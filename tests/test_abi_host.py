@@ -379,3 +379,79 @@ def test_binding_refuses_unfit_tensors():
     # well-sized host tensors pass every check but the device one
     with pytest.raises(mmq.MMQArgumentError, match="CUDA tensor"):
         mmq.mmq_q4K_q8_1(M, N, K, q8, rep, C)
+
+
+# ---------------------------------------------------------------- split-K planning
+MEDIUM = mmq.MMQ_TILE_MEDIUM
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (2048, 512, 4096), (2048, 512, 11008),
+                                   (1024, 4096, 4096), (32, 4096, 4096)])
+def test_plan_splits_with_a_workspace(M, N, K):
+    p = mmq.mmq_plan(M, N, K, 160 * 1024, workspace_bytes=1 << 40)
+    assert p["reason"] == mmq.MMQ_REASON_SPLIT_K and p["splits"] > 1
+    assert p["splits"] <= K // 256 and p["splits"] & (p["splits"] - 1) == 0
+    assert p["workspace_bytes"] == p["splits"] * M * N * 4
+    assert mmq.mmq_workspace_bytes(M, N, K) == p["workspace_bytes"]
+    gm = -(-M // p["block_m"])
+    gn = -(-N // p["block_n"])
+    assert p["grid"] == gm * gn * p["splits"]
+    # without a workspace the same product is not split
+    q = mmq.mmq_plan(M, N, K, 160 * 1024)
+    assert q["splits"] == 1 and q["workspace_bytes"] == 0
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 4096, 4096), (2048, 11008, 4096), (8192, 4096, 4096),
+                                   (1, 4096, 4096), (16, 4096, 4096)])
+def test_plan_does_not_split_what_fills_the_gpu(M, N, K):
+    p = mmq.mmq_plan(M, N, K, 160 * 1024, workspace_bytes=1 << 40)
+    assert p["splits"] == 1 and p["workspace_bytes"] == 0
+    assert mmq.mmq_workspace_bytes(M, N, K) == 0
+
+
+def test_plan_splits_within_the_workspace():
+    M, N, K = 128, 4096, 4096
+    full = mmq.mmq_plan(M, N, K, 160 * 1024, workspace_bytes=1 << 40)
+    half = mmq.mmq_plan(M, N, K, 160 * 1024, workspace_bytes=full["workspace_bytes"] // 2)
+    assert 1 < half["splits"] < full["splits"]
+    assert half["workspace_bytes"] <= full["workspace_bytes"] // 2
+    one = mmq.mmq_plan(M, N, K, 160 * 1024, workspace_bytes=2 * M * N * 4 - 1)
+    assert one["splits"] == 1
+
+
+def test_forced_splits():
+    p = mmq.mmq_plan(150, 300, 2816, 160 * 1024, force_tile=MEDIUM, splits=11,
+                     workspace_bytes=11 * 150 * 300 * 4)
+    assert p["tile"] == MEDIUM and p["splits"] == 11 and p["grid"] == 5 * 2 * 11
+    p = mmq.mmq_plan(150, 300, 2816, 160 * 1024, force_tile=MEDIUM, splits=1)
+    assert p["splits"] == 1 and p["workspace_bytes"] == 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(force_tile=MEDIUM, splits=12, workspace_bytes=1 << 30),   # 11 super-blocks only
+    dict(splits=2, workspace_bytes=1 << 30),                        # split-K needs a tile
+    dict(force_tile=mmq.MMQ_TILE_SKINNY, splits=2, workspace_bytes=1 << 30),
+    dict(force_tile=MEDIUM, splits=2, workspace_bytes=2 * 150 * 300 * 4 - 1),  # no room
+    dict(splits=-1),
+    dict(workspace_bytes=-1),
+])
+def test_split_option_errors(kw):
+    with pytest.raises(mmq.MMQError) as e:
+        mmq.mmq_plan(150, 300, 2816, 160 * 1024, **kw)
+    assert e.value.status == mmq.MMQ_E_ARG
+
+
+def test_reserved_option_must_be_zero():
+    bad = mmq.mmq_options(0, 0, 0, None, 0, 0, 1)
+    info = mmq.mmq_kernel_info()
+    assert mmq.raw_call("mmq_plan", 128, 256, 512, ctypes.byref(bad), 65536,
+                        ctypes.byref(info)) == mmq.MMQ_E_ARG
+
+
+def test_ex_refuses_a_workspace_size_without_a_pointer():
+    opt = mmq.mmq_options(0, 0, 0, None, 1 << 20, 0, 0)
+    assert mmq.raw_call("mmq_q4K_q8_1_ex", 128, 256, 512, A, B, Cp, None,
+                        ctypes.byref(opt)) == mmq.MMQ_E_ARG
+    opt = mmq.mmq_options(0, 0, 0, B + 8, 1 << 20, 0, 0)
+    assert mmq.raw_call("mmq_q4K_q8_1_ex", 128, 256, 512, A, B, Cp, None,
+                        ctypes.byref(opt)) == mmq.MMQ_E_ARG
