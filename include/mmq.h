@@ -230,6 +230,23 @@ int mmq_q4K_q8_1_ex(int64_t M, int64_t N, int64_t K, const void* q8, const void*
 int mmq_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
 
 /*
+ * mmq_q4K_q8_1_static: for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). The same product, kernels
+ * and guard as mmq_q4K_q8_1_ex, with the split-K workspace taken from a 32 MiB array of device
+ * memory that the library's code object holds (one per GPU, for the life of the process)
+ * instead of the caller's buffer; the guard plans its splits within those 32 MiB. The call
+ * allocates nothing. opt may be NULL and must carry no workspace. Every call on a GPU uses
+ * that GPU's one array, so calls that overlap on one GPU (on different streams, or from
+ * several threads) race and must be serialized by the caller; the array's contents between
+ * calls do not matter (each split-K call writes every partial sum it reads).
+ * Errors: as mmq_q4K_q8_1_ex; MMQ_E_ARG for a workspace in opt, or forced splits whose
+ * partial planes (splits*M*N*4 bytes) exceed 32 MiB; MMQ_E_HIP if the array's device address
+ * cannot be found.
+ */
+int mmq_q4K_q8_1_static(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+                        float* C, void* stream, const mmq_options* opt);
+
+/*
  * mmq_q4K_f32: the product for few tokens straight from float32 activations x[M][K]
  * (row-major, leading dimension K), quantizing them inside the GEMM. C is bit for bit what
  * quantize_q8_1 followed by mmq_q4K_q8_1_ex writes with MMQ_TILE_GEMV (M <= 8) or

@@ -79,6 +79,7 @@ _SIGS = {
     "mmq_q4K_q8_1_ex": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.POINTER(mmq_options)],
     "mmq_q4K_f32": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "mmq_workspace_bytes": [_i64, _i64, _i64, ctypes.POINTER(_sz)],
+    "mmq_q4K_q8_1_static": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.POINTER(mmq_options)],
     "mmq_q4K_q8_1_blockdots": [_i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp,
                                ctypes.POINTER(mmq_options)],
     "mmq_plan": [_i64, _i64, _i64, ctypes.POINTER(mmq_options), _i64,
@@ -232,6 +233,18 @@ def mmq_q4K_q8_1_ex(M: int, N: int, K: int, q8, w_rep, C, stream=None,
     _check("mmq_q4K_q8_1_ex",
            _lib.mmq_q4K_q8_1_ex(M, N, K, qp, rp, cp, _stream(stream),
                                 _opts(force_tile, lds_budget, min_workgroups, wp, wb, splits)))
+
+
+def mmq_q4K_q8_1_static(M: int, N: int, K: int, q8, w_rep, C, stream=None,
+                        force_tile: int = MMQ_TILE_AUTO, lds_budget: int = 0,
+                        min_workgroups: int = 0, splits: int = 0) -> None:
+    """As mmq_q4K_q8_1_ex, the split-K workspace being the library's own 32 MiB device array
+    (for callers that cannot allocate); calls that overlap on one GPU race."""
+    qp, rp, cp = _gemm_ptrs(M, N, K, q8, w_rep, C)
+    _check("mmq_q4K_q8_1_static",
+           _lib.mmq_q4K_q8_1_static(M, N, K, qp, rp, cp, _stream(stream),
+                                    _opts(force_tile, lds_budget, min_workgroups, None, 0,
+                                          splits)))
 
 
 def mmq_workspace_bytes(M: int, N: int, K: int) -> int:

@@ -19,8 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmmq.so")
 
 SOURCES = ["quantize.hip", "repack.hip", "mmq_gemm.hip", "mmq_skinny.hip", "mmq_gemv.hip",
-           "f16_path.hip",
-           "f16_gemm.hip", "api.cpp"]
+           "f16_path.hip", "f16_gemm.hip", "static_scratch.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

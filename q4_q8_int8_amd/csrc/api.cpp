@@ -291,6 +291,18 @@ int hip_fail(const char* what, hipError_t e) {
   return fail(MMQ_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Argument checks of the GEMM entry points, before any device access.
+int check_gemm_call(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+                    const float* C, const mmq_options* opt) {
+  int st = check_gemm_shape(M, N, K);
+  if (st) return st;
+  if ((st = check_options(opt))) return st;
+  if (!q8 || !w_rep || !C) return fail(MMQ_E_ARG, "null device pointer");
+  if (!aligned16(q8) || !aligned16(w_rep) || !aligned16(C))
+    return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
+  return MMQ_OK;
+}
+
 // Launch what the guard planned; with split-K the GEMM writes the partial planes into ws and
 // a second kernel adds them into C, both on the stream.
 int launch_planned(const mmq_kernel_info& info, int64_t M, int64_t N, int64_t K, const void* q8,
@@ -315,6 +327,18 @@ int launch_planned(const mmq_kernel_info& info, int64_t M, int64_t N, int64_t K,
 }
 
 }  // namespace
+
+namespace mmq {
+int api_fail(int status, const char* msg) { return fail(status, "%s", msg); }
+int api_check_gemm_call(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+                        const float* C, const mmq_options* opt) {
+  return check_gemm_call(M, N, K, q8, w_rep, C, opt);
+}
+int api_current_device() {
+  DeviceInfo* di;
+  return current_device(&di);
+}
+}  // namespace mmq
 
 extern "C" {
 
@@ -393,12 +417,8 @@ int mmq_plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t ld
 
 int mmq_q4K_q8_1_ex(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
                     float* C, void* stream, const mmq_options* opt) {
-  int st = check_gemm_shape(M, N, K);
+  int st = check_gemm_call(M, N, K, q8, w_rep, C, opt);
   if (st) return st;
-  if ((st = check_options(opt))) return st;
-  if (!q8 || !w_rep || !C) return fail(MMQ_E_ARG, "null device pointer");
-  if (!aligned16(q8) || !aligned16(w_rep) || !aligned16(C))
-    return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
   if (opt && opt->workspace_bytes > 0 && (!opt->workspace || !aligned16(opt->workspace)))
     return fail(MMQ_E_ARG, "workspace_bytes > 0 needs a 16-byte aligned workspace");
   DeviceInfo* di;

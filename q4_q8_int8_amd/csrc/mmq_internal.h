@@ -132,6 +132,14 @@ hipError_t launch_mmq(int tile, const void* q8, const void* w_rep, void* out, in
 hipError_t launch_reduce_splits(const float* ws, float* C, int64_t M, int64_t N, int64_t splits,
                                 hipStream_t s);
 
+// Host-side helpers of the C ABI (api.cpp) for the other entry-point source: record an error
+// for mmq_last_error, the GEMM entry points' argument checks, and the device check (0 when the
+// current device is a gfx950).
+int api_fail(int status, const char* msg);
+int api_check_gemm_call(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+                        const float* C, const struct mmq_options* opt);
+int api_current_device();
+
 // The f16 comparator path: f32 -> f16 conversion of n values, q4_K -> f16 dequantization,
 // and the f16 GEMM (K % 8 == 0, 2*M*K and 2*N*K below 2^31).
 hipError_t launch_convert_f32_f16(const float* x, int64_t n, void* y, hipStream_t s);

@@ -455,3 +455,34 @@ def test_ex_refuses_a_workspace_size_without_a_pointer():
     opt = mmq.mmq_options(0, 0, 0, B + 8, 1 << 20, 0, 0)
     assert mmq.raw_call("mmq_q4K_q8_1_ex", 128, 256, 512, A, B, Cp, None,
                         ctypes.byref(opt)) == mmq.MMQ_E_ARG
+
+
+# ---------------------------------------------------------------- the static-scratch entry point
+@pytest.mark.parametrize("call,status", [
+    (("mmq_q4K_q8_1_static", 4, 8, 100, A, B, Cp, None, None), mmq.MMQ_E_SHAPE),
+    (("mmq_q4K_q8_1_static", 4, 8, 256, None, B, Cp, None, None), mmq.MMQ_E_ARG),
+    (("mmq_q4K_q8_1_static", 4, 8, 256, A, B, Cp + 4, None, None), mmq.MMQ_E_ARG),
+    (("mmq_q4K_q8_1_static", 0, 8, 256, A, B, Cp, None, None), mmq.MMQ_E_ARG),
+])
+def test_static_entry_validation(call, status):
+    assert mmq.raw_call(*call) == status
+    assert mmq.mmq_last_error() != ""
+
+
+def test_static_entry_refuses_a_workspace_and_oversized_splits():
+    opt = mmq.mmq_options(0, 0, 0, B, 1 << 20, 0, 0)
+    assert mmq.raw_call("mmq_q4K_q8_1_static", 128, 256, 512, A, B, Cp, None,
+                        ctypes.byref(opt)) == mmq.MMQ_E_ARG
+    # 4 splits of 256 x 16384 floats are 64 MiB
+    opt = mmq.mmq_options(mmq.MMQ_TILE_MEDIUM, 0, 0, None, 0, 4, 0)
+    assert mmq.raw_call("mmq_q4K_q8_1_static", 256, 16384, 1024, A, B, Cp, None,
+                        ctypes.byref(opt)) == mmq.MMQ_E_ARG
+    assert "32 MiB" in mmq.mmq_last_error()
+
+
+def test_static_entry_reaches_the_device_check():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: the call would run")
+    assert mmq.raw_call("mmq_q4K_q8_1_static", 128, 256, 512, A, B, Cp, None,
+                        None) == mmq.MMQ_E_DEVICE
