@@ -1,4 +1,5 @@
-"""CPU oracle for the q4_K x q8_1 quantized matrix multiply (MMQ) and its f16 comparator.
+"""CPU oracle for the q4_K x q8_1 quantized matrix multiply (MMQ), its q6_K variant and its
+f16 comparator.
 
 TEST INFRASTRUCTURE ONLY. Only the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or call anything here. The HIP
@@ -19,3 +20,7 @@ from .mmq_oracle import (  # noqa: F401
     mmq, block_dots, mmq_terms,
 )
 from .f16_oracle import convert_f32_f16, dequantize_q4_K_f16, gemm_f16  # noqa: F401
+from .q6k_oracle import (  # noqa: F401
+    Q6K, Q6K_BLOCK_BYTES, decode_q6_K, q6_K_scales, dequantize_q6_K,
+    mmq_q6K, block_dots_q6K, mmq_q6K_terms, mmq_q6K_fold_terms,
+)

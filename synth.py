@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the q4_K x q8_1 MMQ path.
 
 This module only *generates inputs*: f32 activations of the prefill workloads and
-q4_K weight blocks in the GGUF byte layout. It holds none of the arithmetic of the
+q4_K and q6_K weight blocks in the GGUF byte layouts. It holds none of the arithmetic of the
 quantized multiply itself (no q8_1 quantization, no block dot product, no rescale);
 both the HIP path and the CPU oracle consume what it produces.
 
@@ -157,6 +157,89 @@ def q4k_weights(kind: str, N: int, K: int, seed: int) -> tuple[np.ndarray, dict]
     else:
         raise ValueError(f"unknown weight kind {kind!r}")
     return q4k_pack(f), f
+
+
+# ----------------------------------------------------------------------------- q6_K fields
+Q6K_BLOCK_BYTES = 210  # 128 bytes low nibbles + 64 bytes high 2-bit pairs + 16 int8 scales + f16 d
+
+
+def q6k_random_fields(N: int, K: int, seed: int) -> dict:
+    """Independent uniform q6_K fields: d = f16(U[1e-4, 2e-3]); 16-element group scales
+    sc ~ U{-127..127} (int8); 6-bit values u ~ U{0..63}."""
+    assert K % QK_K == 0
+    rng = np.random.default_rng(seed)
+    return {
+        "d_bits": _f16_bits(rng.uniform(1e-4, 2e-3, (N, K // QK_K))),
+        "sc": rng.integers(-127, 128, (N, K // 16), dtype=np.int8),
+        "u": rng.integers(0, 64, (N, K), dtype=np.uint8),
+    }
+
+
+def q6k_fit(w: np.ndarray) -> dict:
+    """Fit q6_K fields to f32 weights [N, K]: per 16-element group the scale sc_f = max|x|/31;
+    per super-block d = f16(max |sc_f| / 127); sc = clamp(rint(sc_f/d), -127, 127) (int8),
+    u = clamp(rint(x/(d*sc)) + 32, 0, 63); a zero denominator gives sc = 0 or u = 32. Only
+    the distribution of the resulting fields matters."""
+    w = np.asarray(w, dtype=np.float64)
+    N, K = w.shape
+    assert K % QK_K == 0
+    xs = w.reshape(N, K // QK_K, 16, 16)
+    sc_f = np.abs(xs).max(axis=3) / 31.0                          # [N, nsb, 16]
+    d_bits = _f16_bits(sc_f.max(axis=2) / 127.0)
+    d = _f16_val(d_bits)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        sc = np.where(d > 0, np.rint(sc_f / d), 0.0)
+        sc = np.clip(sc, -127, 127)
+        scale = (d * sc)[..., None]
+        u = np.where(scale != 0, np.rint(xs / scale) + 32, 32.0)
+    u = np.clip(u, 0, 63)
+    return {"d_bits": d_bits, "sc": sc.astype(np.int8).reshape(N, K // 16),
+            "u": u.astype(np.uint8).reshape(N, K)}
+
+
+def q6k_pack(f: dict) -> np.ndarray:
+    """Pack q6_K fields into GGUF-layout blocks, u8 [N, K/256, 210].
+
+    Byte layout of one 210-byte super-block of 256 values (6-bit u, stored value u - 32):
+      0..127    ql: the low 4 bits. The block is two halves of 128 values; half h owns bytes
+                64h..64h+63. Value 128h + 32q + l (q = 0..3, l = 0..31) keeps its low 4 bits in
+                byte 64h + l + 32*(q & 1), in the low nibble for q < 2 and the high nibble for
+                q >= 2.
+      128..191  qh: the high 2 bits. Half h owns bytes 128 + 32h .. +31; value 128h + 32q + l
+                keeps them in bits 2q..2q+1 of byte 128 + 32h + l.
+      192..207  the 16 int8 scales, one per 16 consecutive values (value v uses scale v // 16).
+      208..209  d (f16, little endian).
+    """
+    N, K = f["u"].shape
+    nsb = K // QK_K
+    u = f["u"].reshape(N, nsb, 2, 4, 32).astype(np.uint8)        # [n, s, half, q, l]
+    assert u.max(initial=0) < 64
+    out = np.zeros((N, nsb, Q6K_BLOCK_BYTES), dtype=np.uint8)
+    lo = u & 15
+    hi = u >> 4
+    ql = np.zeros((N, nsb, 2, 64), dtype=np.uint8)
+    ql[..., 0:32] = lo[:, :, :, 0, :] | (lo[:, :, :, 2, :] << 4)
+    ql[..., 32:64] = lo[:, :, :, 1, :] | (lo[:, :, :, 3, :] << 4)
+    qh = hi[:, :, :, 0, :] | (hi[:, :, :, 1, :] << 2) | (hi[:, :, :, 2, :] << 4) \
+        | (hi[:, :, :, 3, :] << 6)
+    out[..., 0:128] = ql.reshape(N, nsb, 128)
+    out[..., 128:192] = qh.reshape(N, nsb, 64)
+    out[..., 192:208] = np.asarray(f["sc"], np.int8).reshape(N, nsb, 16).view(np.uint8)
+    out[..., 208:210] = np.asarray(f["d_bits"], np.uint16).reshape(N, nsb, 1).view(np.uint8)
+    return out
+
+
+def q6k_weights(kind: str, N: int, K: int, seed: int) -> tuple[np.ndarray, dict]:
+    """(packed q6_K blocks u8 [N, K/256, 210], the fields they encode)."""
+    if kind == "random_fields":
+        f = q6k_random_fields(N, K, seed)
+    elif kind == "fit":
+        rng = np.random.default_rng(seed)
+        w = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
+        f = q6k_fit(w)
+    else:
+        raise ValueError(f"unknown weight kind {kind!r}")
+    return q6k_pack(f), f
 
 
 def workload(name: str, need_fields: bool = False) -> dict:
