@@ -49,6 +49,8 @@ enum mmq_status {
 #define MMQ_Q4K_BLOCK_BYTES 144  /* bytes of one q4_K super-block */
 #define MMQ_REP_TILE_ROWS 32     /* weight rows per repacked tile */
 #define MMQ_REP_TILE_BYTES 6656  /* bytes per (repacked tile, super-block) */
+#define MMQ_Q6K_BLOCK_BYTES 210  /* bytes of one q6_K super-block */
+#define MMQ_REP6_TILE_BYTES 10240 /* bytes per (repacked q6_K tile, super-block) */
 
 /* Tile variants of the GEMM: one template in two instantiations (large, small), a skinny
  * kernel for few tokens that splits K over the wavefronts of a workgroup, and a vector-ALU
@@ -275,6 +277,58 @@ int mmq_q4K_f32(int64_t M, int64_t N, int64_t K, const float* x, const void* w_r
  * Errors: as mmq_q4K_q8_1; MMQ_E_SHAPE for an empty or out-of-range window.
  */
 int mmq_q4K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+                           int64_t i0, int64_t i1, int64_t j0, int64_t j1, int32_t* S,
+                           void* stream, const mmq_options* opt);
+
+/* ---------------------------------------------------------------- the q6_K variant */
+
+/*
+ * The q6_K weight format (the r16 page, sections 2.3 and 5, names the q6_K kernel family that
+ * the rank-1 fold was carried over to; the pages give no layout, and the GGUF q6_K layout is
+ * the reading taken): 256 values per 210-byte super-block, each a 6-bit u whose weight value
+ * is the signed integer u - 32, one int8 scale sc per 16 consecutive values and one f16 d:
+ *   bytes 0..127   low 4 bits: value 128h + 32q + l (h = 0..1, q = 0..3, l = 0..31) in byte
+ *                  64h + 32(q mod 2) + l, the low nibble for q < 2, the high one for q >= 2
+ *   bytes 128..191 high 2 bits: bits 2q..2q+1 of byte 128 + 32h + l
+ *   bytes 192..207 the 16 scales (int8), scale g for values 16g..16g+15
+ *   bytes 208..209 d (f16, little endian)
+ * so w = d * sc * (u - 32). The product with q8_1 activations is one term per group of 16:
+ *   C_ij = sum_g da_i,b(g) * dsv_jg * S_ijg,  S_ijg = sum_{k in g} q_ik (u_jk - 32), dsv = d*sc.
+ * The int8 MFMA is signed, so it takes the values u - 32 directly and the offset needs no
+ * rank-1 correction (the fold form on the pages computes the same S from u and the group
+ * sums of q).
+ */
+int mmq_q6K_bytes(int64_t N, int64_t K, size_t* bytes);          /* N*(K/256)*210 */
+int mmq_q6K_repacked_bytes(int64_t N, int64_t K, size_t* bytes); /* ceil(N/32)*(K/256)*10240 */
+
+/*
+ * repack_q6_K: q6_K blocks [N][K/256] of 210 bytes -> one 10240-byte record per (tile t of 32
+ * weight rows, super-block s), records ordered [t][s]; rows N..32*ceil(N/32)-1 are zero:
+ *   bytes [0, 8192):     int8 u - 32, [b 0..7][h 0..1][j 0..31][16 bytes] = values
+ *                        32b + 16h .. +15 of the super-block of row 32t+j
+ *   bytes [8192, 10240): float dsv[g 0..15][j 0..31] = d*sc_g of row 32t+j (exact in f32)
+ * Errors: MMQ_E_ARG (null pointer, w_rep not 16-byte aligned, N or K <= 0), MMQ_E_SHAPE (K %
+ * 256; ceil(N/32)*(K/256) >= 2^31), MMQ_E_DEVICE, MMQ_E_HIP.
+ */
+int repack_q6_K(const void* w_q6K, int64_t N, int64_t K, void* w_rep, void* stream);
+
+/*
+ * mmq_q6K_q8_1: C[M][N] (float32, row-major, overwritten) = the product above, from q8 of
+ * quantize_q8_1 (M x K) and w_rep of repack_q6_K (N x K). The GEMM template of the q4_K
+ * product (large, medium and small tiles, the same guard, split-K with a workspace through
+ * the _ex options): per 32-block two int8 MFMAs, each keeping one 16-value group (the lane half
+ * that holds it), S_ijg exact; per group y = RN(S * da), acc += dsv * y, groups in increasing
+ * order (deterministic). There is no skinny or decode kernel for q6_K.
+ * Same preconditions and errors as mmq_q4K_q8_1 (forcing MMQ_TILE_SKINNY or MMQ_TILE_GEMV is
+ * MMQ_E_ARG).
+ */
+int mmq_q6K_q8_1(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+                 float* C, void* stream);
+int mmq_q6K_q8_1_ex(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+                    float* C, void* stream, const mmq_options* opt);
+
+/* The q6_K group dot products S_ijg for a window, S int32 [K/16][i1-i0][j1-j0] (test path). */
+int mmq_q6K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
                            int64_t i0, int64_t i1, int64_t j0, int64_t j1, int32_t* S,
                            void* stream, const mmq_options* opt);
 

@@ -39,6 +39,7 @@ MMQ_OK, MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_LDS, MMQ_E_DEVICE, MMQ_E_HIP = range(6)
  MMQ_REASON_DECODE, MMQ_REASON_SPLIT_K) = range(10)
 GEMV_MAX_M = 16  # largest M of the decode tile, which the guard chooses up to there
 QK8, QK_K, Q4K_BLOCK_BYTES, REP_TILE_ROWS, REP_TILE_BYTES = 32, 256, 144, 32, 6656
+Q6K_BLOCK_BYTES, REP6_TILE_BYTES = 210, 10240
 
 
 class mmq_options(ctypes.Structure):
@@ -79,6 +80,13 @@ _SIGS = {
     "mmq_q4K_q8_1_ex": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.POINTER(mmq_options)],
     "mmq_q4K_f32": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "mmq_workspace_bytes": [_i64, _i64, _i64, ctypes.POINTER(_sz)],
+    "mmq_q6K_bytes": [_i64, _i64, ctypes.POINTER(_sz)],
+    "mmq_q6K_repacked_bytes": [_i64, _i64, ctypes.POINTER(_sz)],
+    "repack_q6_K": [_vp, _i64, _i64, _vp, _vp],
+    "mmq_q6K_q8_1": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
+    "mmq_q6K_q8_1_ex": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.POINTER(mmq_options)],
+    "mmq_q6K_q8_1_blockdots": [_i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp,
+                               ctypes.POINTER(mmq_options)],
     "mmq_q4K_q8_1_static": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, ctypes.POINTER(mmq_options)],
     "mmq_q4K_q8_1_blockdots": [_i64, _i64, _i64, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp,
                                ctypes.POINTER(mmq_options)],
@@ -272,6 +280,59 @@ def mmq_q4K_q8_1_blockdots(M: int, N: int, K: int, q8, w_rep, i0: int, i1: int, 
     _check("mmq_q4K_q8_1_blockdots",
            _lib.mmq_q4K_q8_1_blockdots(M, N, K, qp, rp, i0, i1, j0, j1, sp,
                                        _stream(stream), _opts(force_tile, lds_budget)))
+
+
+# ---------------------------------------------------------------- the q6_K variant
+def mmq_q6K_bytes(N: int, K: int) -> int:
+    n = _sz()
+    _check("mmq_q6K_bytes", _lib.mmq_q6K_bytes(N, K, ctypes.byref(n)))
+    return n.value
+
+
+def mmq_q6K_repacked_bytes(N: int, K: int) -> int:
+    n = _sz()
+    _check("mmq_q6K_repacked_bytes", _lib.mmq_q6K_repacked_bytes(N, K, ctypes.byref(n)))
+    return n.value
+
+
+def repack_q6_K(w_q6K, N: int, K: int, w_rep, stream=None) -> None:
+    """w_q6K: q6_K blocks (mmq_q6K_bytes); w_rep: mmq_q6K_repacked_bytes(N, K) bytes."""
+    wp = _dev(w_q6K, "w_q6K", mmq_q6K_bytes(N, K))
+    rp = _dev(w_rep, "w_rep", mmq_q6K_repacked_bytes(N, K))
+    _check("repack_q6_K", _lib.repack_q6_K(wp, N, K, rp, _stream(stream)))
+
+
+def _gemm6_ptrs(M: int, N: int, K: int, q8, w_rep, C):
+    return (_dev(q8, "q8", mmq_q8_1_bytes(M, K)),
+            _dev(w_rep, "w_rep", mmq_q6K_repacked_bytes(N, K)),
+            _dev(C, "C", 4 * M * N, _f32()))
+
+
+def mmq_q6K_q8_1(M: int, N: int, K: int, q8, w_rep, C, stream=None) -> None:
+    """C[M, N] (f32) = q8 (M x K) times repacked q6_K weights (N x K)^T."""
+    qp, rp, cp = _gemm6_ptrs(M, N, K, q8, w_rep, C)
+    _check("mmq_q6K_q8_1", _lib.mmq_q6K_q8_1(M, N, K, qp, rp, cp, _stream(stream)))
+
+
+def mmq_q6K_q8_1_ex(M: int, N: int, K: int, q8, w_rep, C, stream=None,
+                    force_tile: int = MMQ_TILE_AUTO, lds_budget: int = 0,
+                    min_workgroups: int = 0, workspace=None, splits: int = 0) -> None:
+    qp, rp, cp = _gemm6_ptrs(M, N, K, q8, w_rep, C)
+    wp, wb = _workspace(workspace)
+    _check("mmq_q6K_q8_1_ex",
+           _lib.mmq_q6K_q8_1_ex(M, N, K, qp, rp, cp, _stream(stream),
+                                _opts(force_tile, lds_budget, min_workgroups, wp, wb, splits)))
+
+
+def mmq_q6K_q8_1_blockdots(M: int, N: int, K: int, q8, w_rep, i0: int, i1: int, j0: int,
+                           j1: int, S, stream=None, force_tile: int = MMQ_TILE_AUTO) -> None:
+    """S: int32 device tensor [K/16, i1-i0, j1-j0] of per-group integer dot products."""
+    qp = _dev(q8, "q8", mmq_q8_1_bytes(M, K))
+    rp = _dev(w_rep, "w_rep", mmq_q6K_repacked_bytes(N, K))
+    sp = _dev(S, "S", 4 * (K // 16) * max(i1 - i0, 0) * max(j1 - j0, 0), _i32())
+    _check("mmq_q6K_q8_1_blockdots",
+           _lib.mmq_q6K_q8_1_blockdots(M, N, K, qp, rp, i0, i1, j0, j1, sp, _stream(stream),
+                                       _opts(force_tile)))
 
 
 # ---------------------------------------------------------------- the guard

@@ -154,8 +154,8 @@ mmq::TileShape tile_shape(int tile) {
 
 // The guard: which tile, given the LDS budget and the compute units the grid should fill.
 int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget,
-         int64_t compute_units,
-         mmq_kernel_info* info) {
+         int64_t compute_units, mmq_kernel_info* info, int fmt = mmq::kFmtQ4K) {
+  const bool q6 = fmt == mmq::kFmtQ6K;
   memset(info, 0, sizeof(*info));
   if (opt && opt->lds_budget > 0) budget = opt->lds_budget;
   const int64_t min_wg = opt && opt->min_workgroups > 0 ? opt->min_workgroups : compute_units;
@@ -165,10 +165,13 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
     return gm * gn;
   };
   info->lds_budget = budget;
-  const int64_t need_large = mmq::kLarge.lds_bytes();
-  const int64_t need_small = mmq::kSmall.lds_bytes();
-  const int64_t need_medium = mmq::kMedium.lds_bytes();
+  const int64_t need_large = mmq::kLarge.lds_bytes(fmt);
+  const int64_t need_small = mmq::kSmall.lds_bytes(fmt);
+  const int64_t need_medium = mmq::kMedium.lds_bytes(fmt);
   const int forced = opt ? opt->force_tile : MMQ_TILE_AUTO;
+  if (q6 && (forced == MMQ_TILE_SKINNY || forced == MMQ_TILE_GEMV))
+    return fail(MMQ_E_ARG, "the q6_K product has no skinny or decode kernel: force large, medium "
+                           "or small");
   const int64_t nsb = K / 256;
   const int64_t ws_bytes = opt ? opt->workspace_bytes : 0;
   const int64_t forced_splits = opt ? opt->splits : 0;
@@ -201,7 +204,7 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
       return fail(MMQ_E_SHAPE, "the decode tile takes M <= %d (M = %lld)", mmq::kGemvMaxM,
                   (long long)M);
     if (mmq::gemv_lds_bytes(M) <= budget) { tile = MMQ_TILE_GEMV; reason = MMQ_REASON_FORCED; }
-  } else if (M <= mmq::kGemvAutoMaxM && mmq::gemv_lds_bytes(M) <= budget) {
+  } else if (!q6 && M <= mmq::kGemvAutoMaxM && mmq::gemv_lds_bytes(M) <= budget) {
     tile = MMQ_TILE_GEMV; reason = MMQ_REASON_DECODE;
   } else if (need_large <= budget) {
     // the cheapest (tile, splits) under the cost model: splits only with a workspace that
@@ -210,7 +213,8 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
     double best = 1e300;
     int best_tile = 0;
     int64_t best_sp = 1;
-    if (M <= kSkinnyMaxM && nsb >= mmq::kSkinnyWaves && mmq::skinny_lds_bytes() <= budget) {
+    if (!q6 && M <= kSkinnyMaxM && nsb >= mmq::kSkinnyWaves &&
+        mmq::skinny_lds_bytes() <= budget) {
       // (below 8 super-blocks some of the skinny kernel's wavefronts get none, and the small
       // tile is faster: 5.5 against 7.6 us at 128 x 256 x 512)
       const double grid = (double)(((M + 31) / 32) * ((N + 31) / 32));
@@ -219,7 +223,7 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
       best_tile = MMQ_TILE_SKINNY;
     }
     for (const TileCost& c : kTileCosts) {
-      if (tile_shape(c.tile).lds_bytes() > budget) continue;
+      if (tile_shape(c.tile).lds_bytes(fmt) > budget) continue;
       for (int64_t sp = 1; sp <= kMaxSplits && sp <= nsb; sp *= 2) {
         if (sp > 1 && plane_bytes(sp) > ws_bytes) break;
         // the large tile only with a grid of at least min_wg workgroups
@@ -280,7 +284,7 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
   info->block_m = ts.block_m();
   info->block_n = ts.block_n();
   info->threads = ts.threads();
-  info->lds_bytes = ts.lds_bytes();
+  info->lds_bytes = ts.lds_bytes(fmt);
   info->grid = gm * gn * splits;
   info->splits = (int32_t)splits;
   info->workspace_bytes = plane_bytes(splits);
@@ -306,7 +310,8 @@ int check_gemm_call(int64_t M, int64_t N, int64_t K, const void* q8, const void*
 // Launch what the guard planned; with split-K the GEMM writes the partial planes into ws and
 // a second kernel adds them into C, both on the stream.
 int launch_planned(const mmq_kernel_info& info, int64_t M, int64_t N, int64_t K, const void* q8,
-                   const void* w_rep, float* C, void* ws, hipStream_t stream) {
+                   const void* w_rep, float* C, void* ws, hipStream_t stream,
+                   int fmt = mmq::kFmtQ4K) {
   hipError_t e;
   if (info.tile == MMQ_TILE_GEMV) {
     e = mmq::launch_mmq_gemv(q8, w_rep, C, M, N, K, stream);
@@ -318,11 +323,75 @@ int launch_planned(const mmq_kernel_info& info, int64_t M, int64_t N, int64_t K,
     const int64_t gn = ((N + 31) / 32 + ts.nw - 1) / ts.nw;
     const int64_t sp = info.splits;
     e = mmq::launch_mmq(info.tile, q8, w_rep, sp > 1 ? ws : C, M, N, K, gm, gn, sp, 0, 0, false,
-                        0, 0, 0, 0, stream);
+                        0, 0, 0, 0, stream, fmt);
     if (e == hipSuccess && sp > 1)
       e = mmq::launch_reduce_splits(static_cast<const float*>(ws), C, M, N, sp, stream);
   }
   if (e != hipSuccess) return hip_fail("mmq_q4K_q8_1 launch", e);
+  return ok();
+}
+
+// The GEMM entry points of both weight formats: validate, plan, launch.
+int gemm_ex(int fmt, int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+            float* C, void* stream, const mmq_options* opt) {
+  int st = check_gemm_call(M, N, K, q8, w_rep, C, opt);
+  if (st) return st;
+  if (opt && opt->workspace_bytes > 0 && (!opt->workspace || !aligned16(opt->workspace)))
+    return fail(MMQ_E_ARG, "workspace_bytes > 0 needs a 16-byte aligned workspace");
+  DeviceInfo* di;
+  if ((st = current_device(&di))) return st;
+  mmq_kernel_info info;
+  st = plan(M, N, K, opt, di->lds_budget, di->compute_units, &info, fmt);
+  g_last = info;
+  if (st) return st;
+  return launch_planned(info, M, N, K, q8, w_rep, C, opt ? opt->workspace : nullptr,
+                        static_cast<hipStream_t>(stream), fmt);
+}
+
+int blockdots(int fmt, int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+              int64_t i0, int64_t i1, int64_t j0, int64_t j1, int32_t* S, void* stream,
+              const mmq_options* opt) {
+  int st = check_gemm_shape(M, N, K);
+  if (st) return st;
+  if ((st = check_options(opt))) return st;
+  if (!q8 || !w_rep || !S) return fail(MMQ_E_ARG, "null device pointer");
+  if (!aligned16(q8) || !aligned16(w_rep) || !aligned16(S))
+    return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
+  if (!(0 <= i0 && i0 < i1 && i1 <= M && 0 <= j0 && j0 < j1 && j1 <= N))
+    return fail(MMQ_E_SHAPE, "window [%lld,%lld) x [%lld,%lld) is empty or outside %lld x %lld",
+                (long long)i0, (long long)i1, (long long)j0, (long long)j1, (long long)M,
+                (long long)N);
+  if (opt && (opt->force_tile == MMQ_TILE_SKINNY || opt->force_tile == MMQ_TILE_GEMV))
+    return fail(MMQ_E_ARG, "the skinny and vector-ALU tiles have no block-dot output; force "
+                           "large, medium or small");
+  if (opt && opt->splits > 1)
+    return fail(MMQ_E_ARG, "the block dots are written without split-K");
+  DeviceInfo* di;
+  if ((st = current_device(&di))) return st;
+  mmq_kernel_info info;
+  st = plan(M, N, K, opt, di->lds_budget, di->compute_units, &info, fmt);
+  if (!st && (info.tile == MMQ_TILE_SKINNY || info.tile == MMQ_TILE_GEMV || info.splits > 1)) {
+    // the block dots come from the small tile, unsplit
+    mmq_options o = opt ? *opt : mmq_options{};
+    o.force_tile = MMQ_TILE_SMALL;
+    o.workspace_bytes = 0;
+    o.splits = 0;
+    st = plan(M, N, K, &o, di->lds_budget, di->compute_units, &info, fmt);
+  }
+  g_last = info;
+  if (st) return st;
+  const mmq::TileShape ts = tile_shape(info.tile);
+  const int64_t tm0 = i0 / ts.block_m();
+  const int64_t tm1 = (i1 + ts.block_m() - 1) / ts.block_m();
+  const int64_t tn0 = j0 / ts.block_n();
+  const int64_t tn1 = (j1 + ts.block_n() - 1) / ts.block_n();
+  const int64_t gm = tm1 - tm0, gn = tn1 - tn0;
+  g_last.grid = gm * gn;
+  g_last.splits = 1;
+  g_last.workspace_bytes = 0;
+  hipError_t e = mmq::launch_mmq(info.tile, q8, w_rep, S, M, N, K, gm, gn, 1, tm0, tn0, true,
+                                 i0, i1, j0, j1, static_cast<hipStream_t>(stream), fmt);
+  if (e != hipSuccess) return hip_fail("blockdots launch", e);
   return ok();
 }
 
@@ -417,18 +486,7 @@ int mmq_plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t ld
 
 int mmq_q4K_q8_1_ex(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
                     float* C, void* stream, const mmq_options* opt) {
-  int st = check_gemm_call(M, N, K, q8, w_rep, C, opt);
-  if (st) return st;
-  if (opt && opt->workspace_bytes > 0 && (!opt->workspace || !aligned16(opt->workspace)))
-    return fail(MMQ_E_ARG, "workspace_bytes > 0 needs a 16-byte aligned workspace");
-  DeviceInfo* di;
-  if ((st = current_device(&di))) return st;
-  mmq_kernel_info info;
-  st = plan(M, N, K, opt, di->lds_budget, di->compute_units, &info);
-  g_last = info;
-  if (st) return st;
-  return launch_planned(info, M, N, K, q8, w_rep, C, opt ? opt->workspace : nullptr,
-                        static_cast<hipStream_t>(stream));
+  return gemm_ex(mmq::kFmtQ4K, M, N, K, q8, w_rep, C, stream, opt);
 }
 
 int mmq_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
@@ -499,48 +557,60 @@ int mmq_q4K_f32(int64_t M, int64_t N, int64_t K, const float* x, const void* w_r
 int mmq_q4K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
                            int64_t i0, int64_t i1, int64_t j0, int64_t j1, int32_t* S,
                            void* stream, const mmq_options* opt) {
-  int st = check_gemm_shape(M, N, K);
+  return blockdots(mmq::kFmtQ4K, M, N, K, q8, w_rep, i0, i1, j0, j1, S, stream, opt);
+}
+
+// ---------------------------------------------------------------- q6_K
+
+int mmq_q6K_bytes(int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(MMQ_E_ARG, "bytes is NULL");
+  if (N <= 0 || K <= 0) return fail(MMQ_E_ARG, "N and K must be positive");
+  if (K % MMQ_QK_K) return fail(MMQ_E_SHAPE, "K = %lld is not a multiple of 256", (long long)K);
+  if (N > kMaxDim || K > kMaxDim) return fail(MMQ_E_SHAPE, "weight matrix too large");
+  *bytes = (size_t)N * (size_t)(K / MMQ_QK_K) * MMQ_Q6K_BLOCK_BYTES;
+  return ok();
+}
+
+int mmq_q6K_repacked_bytes(int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(MMQ_E_ARG, "bytes is NULL");
+  if (N <= 0 || K <= 0) return fail(MMQ_E_ARG, "N and K must be positive");
+  if (K % MMQ_QK_K) return fail(MMQ_E_SHAPE, "K = %lld is not a multiple of 256", (long long)K);
+  if (N > kMaxDim || K > kMaxDim) return fail(MMQ_E_SHAPE, "weight matrix too large");
+  static_assert(MMQ_REP6_TILE_BYTES == mmq::kRep6TileBytes, "repacked q6_K record size");
+  static_assert(MMQ_Q6K_BLOCK_BYTES == mmq::kQ6KBlockBytes, "q6_K block size");
+  *bytes = (size_t)((N + 31) / 32) * (size_t)(K / MMQ_QK_K) * MMQ_REP6_TILE_BYTES;
+  return ok();
+}
+
+int repack_q6_K(const void* w_q6K, int64_t N, int64_t K, void* w_rep, void* stream) {
+  size_t nb;
+  int st = mmq_q6K_repacked_bytes(N, K, &nb);
   if (st) return st;
-  if ((st = check_options(opt))) return st;
-  if (!q8 || !w_rep || !S) return fail(MMQ_E_ARG, "null device pointer");
-  if (!aligned16(q8) || !aligned16(w_rep) || !aligned16(S))
-    return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");
-  if (!(0 <= i0 && i0 < i1 && i1 <= M && 0 <= j0 && j0 < j1 && j1 <= N))
-    return fail(MMQ_E_SHAPE, "window [%lld,%lld) x [%lld,%lld) is empty or outside %lld x %lld",
-                (long long)i0, (long long)i1, (long long)j0, (long long)j1, (long long)M,
-                (long long)N);
-  if (opt && (opt->force_tile == MMQ_TILE_SKINNY || opt->force_tile == MMQ_TILE_GEMV))
-    return fail(MMQ_E_ARG, "the skinny and vector-ALU tiles have no block-dot output; force "
-                           "large, medium or small");
-  if (opt && opt->splits > 1)
-    return fail(MMQ_E_ARG, "the block dots are written without split-K");
+  if ((__int128)((N + 31) / 32) * (K / MMQ_QK_K) >= ((__int128)1 << 31))
+    return fail(MMQ_E_SHAPE, "repack_q6_K takes ceil(N/32)*(K/256) below 2^31");
+  if (!w_q6K || !w_rep) return fail(MMQ_E_ARG, "null device pointer");
+  if (!aligned16(w_rep)) return fail(MMQ_E_ARG, "w_rep must be 16-byte aligned");
   DeviceInfo* di;
   if ((st = current_device(&di))) return st;
-  mmq_kernel_info info;
-  st = plan(M, N, K, opt, di->lds_budget, di->compute_units, &info);
-  if (!st && (info.tile == MMQ_TILE_SKINNY || info.tile == MMQ_TILE_GEMV || info.splits > 1)) {
-    // the block dots come from the small tile, unsplit
-    mmq_options o = opt ? *opt : mmq_options{};
-    o.force_tile = MMQ_TILE_SMALL;
-    o.workspace_bytes = 0;
-    o.splits = 0;
-    st = plan(M, N, K, &o, di->lds_budget, di->compute_units, &info);
-  }
-  g_last = info;
-  if (st) return st;
-  const mmq::TileShape ts = tile_shape(info.tile);
-  const int64_t tm0 = i0 / ts.block_m();
-  const int64_t tm1 = (i1 + ts.block_m() - 1) / ts.block_m();
-  const int64_t tn0 = j0 / ts.block_n();
-  const int64_t tn1 = (j1 + ts.block_n() - 1) / ts.block_n();
-  const int64_t gm = tm1 - tm0, gn = tn1 - tn0;
-  g_last.grid = gm * gn;
-  g_last.splits = 1;
-  g_last.workspace_bytes = 0;
-  hipError_t e = mmq::launch_mmq(info.tile, q8, w_rep, S, M, N, K, gm, gn, 1, tm0, tn0, true,
-                                 i0, i1, j0, j1, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail("mmq_q4K_q8_1_blockdots launch", e);
+  hipError_t e = mmq::launch_repack_q6_K(w_q6K, N, K, w_rep, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail("repack_q6_K launch", e);
   return ok();
+}
+
+int mmq_q6K_q8_1_ex(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+                    float* C, void* stream, const mmq_options* opt) {
+  return gemm_ex(mmq::kFmtQ6K, M, N, K, q8, w_rep, C, stream, opt);
+}
+
+int mmq_q6K_q8_1(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep, float* C,
+                 void* stream) {
+  return mmq_q6K_q8_1_ex(M, N, K, q8, w_rep, C, stream, nullptr);
+}
+
+int mmq_q6K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,
+                           int64_t i0, int64_t i1, int64_t j0, int64_t j1, int32_t* S,
+                           void* stream, const mmq_options* opt) {
+  return blockdots(mmq::kFmtQ6K, M, N, K, q8, w_rep, i0, i1, j0, j1, S, stream, opt);
 }
 
 // ---------------------------------------------------------------- f16 comparator path

@@ -60,7 +60,7 @@ __device__ __forceinline__ void set_priority(int p) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
-template <int TT, int NW, bool STORE_S>
+template <int TT, int NW, bool STORE_S, int FMT>
 __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
     const int8_t* __restrict__ qs, const float* __restrict__ da_plane,
     const uint16_t* __restrict__ tpieces,
@@ -70,14 +70,21 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   constexpr int NS = 8 * TT;                      // (block, token tile) steps per super-block
   constexpr int A_BYTES = BM * kRowStride;        // token tile
   constexpr int DA_BYTES = BM * 64;               // (da, nb) pairs [8][BM][2]
-  constexpr int TP_BYTES = BM * 48;               // token pieces of da*sa [3][BM][8]
-  constexpr int W_BYTES = kRepDsvBytes + kRepPieceBytes;  // per wavefront: dsv, dmv pieces
+  constexpr bool Q6 = FMT == kFmtQ6K;
+  // q4_K: token pieces of da*sa [3][BM][8] for term2; q6_K has no term2
+  constexpr int TP_BYTES = Q6 ? 0 : BM * 48;
+  // per wavefront: q4_K dsv and the dmv pieces, q6_K dsv of its 16 groups
+  constexpr int W_BYTES = Q6 ? kRep6DsvBytes : kRepDsvBytes + kRepPieceBytes;
+  constexpr int W_OPS = Q6 ? 2 : 3;               // 1 KiB loads of W_BYTES (q4_K: 2.5)
+  constexpr int REC = Q6 ? kRep6TileBytes : kRepTileBytes;   // record per (tile, super-block)
+  constexpr int REC_W = Q6 ? kRep6ValBytes : kRepNibBytes;   // where its scales start
+  constexpr int NG = Q6 ? 8 : 4;   // 16-byte operand loads per lane and super-block
   constexpr int STAGE = A_BYTES + DA_BYTES + TP_BYTES + NW * W_BYTES;
-  static_assert(STAGE == TileShape{TT, NW}.stage_bytes(), "LDS stage layout");
+  static_assert(STAGE == TileShape{TT, NW}.stage_bytes(FMT), "LDS stage layout");
   constexpr int A_SLOTS = BM * (kRowStride / 16);  // 16-byte slots of the token tile
   constexpr int A_DMA = (A_SLOTS + 63) / 64;       // wavefront-wide DMA instructions
   constexpr int A_PER_WAVE = (A_DMA + NW - 1) / NW;
-  constexpr int TP_SLOTS = 3 * BM;                 // 16-byte slots of the token pieces
+  constexpr int TP_SLOTS = Q6 ? 0 : 3 * BM;        // 16-byte slots of the token pieces
   constexpr int TP_DMA = (TP_SLOTS + 63) / 64;
   constexpr int TP_PER_WAVE = (TP_DMA + NW - 1) / NW;
 
@@ -106,9 +113,9 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   const v4i rq = make_rsrc_sgpr(qs, (uint32_t)M * (uint32_t)K);
   const v4i rda = make_rsrc_sgpr(da_plane, (uint32_t)M * (uint32_t)kb * 8u);
   const v4i rtp = make_rsrc_sgpr(tpieces, (uint32_t)M * (uint32_t)nsb * 48u);
-  const uint8_t* wtile = wrep + (size_t)wt * nsb * kRepTileBytes;
-  const v4i rwd = make_rsrc_sgpr(wtile, (uint32_t)nsb * kRepTileBytes);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wtile, (uint32_t)nsb * kRepTileBytes);
+  const uint8_t* wtile = wrep + (size_t)wt * nsb * REC;
+  const v4i rwd = make_rsrc_sgpr(wtile, (uint32_t)nsb * REC);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wtile, (uint32_t)nsb * REC);
 
   // Token-tile DMA slots of this lane: slot q = 64*k + lane holds chunk q % 17 of row q / 17;
   // chunk 16 is the row's padding and reads past the end (zero), as do rows past M.
@@ -124,8 +131,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   }
   // Token-piece DMA slots: slot q = 64*k + lane holds piece q / BM of token m0 + q % BM; the
   // pieces of super-block s sit at [s][piece][M][8] in memory and [piece][BM][8] in LDS.
-  uint32_t tp_off[TP_PER_WAVE];
-  bool tp_act[TP_PER_WAVE];
+  uint32_t tp_off[TP_PER_WAVE > 0 ? TP_PER_WAVE : 1];
+  bool tp_act[TP_PER_WAVE > 0 ? TP_PER_WAVE : 1];
 #pragma unroll
   for (int j = 0; j < TP_PER_WAVE; ++j) {
     const int k = wave + j * NW;
@@ -135,19 +142,20 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
     tp_off[j] = ((uint32_t)pc * (uint32_t)M + (uint32_t)(m0 + r)) * 16u;
   }
   // What stage s of the pipeline loads into LDS, as NOPS single DMA instructions of this
-  // wavefront (its token-tile DMAs, its da DMAs, its token-piece DMA, its 2560 bytes of dsv
-  // and dmv pieces), followed by op NOPS: nibble group 3 into registers. Op v is a
-  // compile-time constant wherever it is issued, so each call folds to one instruction.
-  // Nibble groups 0..2 are loaded separately, in place (load_nib).
+  // wavefront (its token-tile DMAs, its da DMAs, its token-piece DMA (q4_K), its W_BYTES of
+  // weight scales), followed by op NOPS: the last weight-operand load (q4_K nibble group 3,
+  // q6_K block 7) into registers. Op v is a compile-time constant wherever it is issued, so
+  // each call folds to one instruction. The other operand loads are issued separately, in
+  // place (load_nib).
   constexpr int DA_PER_WAVE = (8 + NW - 1) / NW;
   // The next stage's ops are issued three at a time at the first step of every other
   // sub-block (the last ones at the last step at the latest), so that the wavefronts of a
   // workgroup do not queue all their memory instructions at once. Finer spreading costs
   // registers: each issue point constrains how far ahead the compiler schedules LDS reads.
   auto op_step = [](int v) { return ((v / 3) * 2 * TT < NS - 1) ? (v / 3) * 2 * TT : NS - 1; };
-  constexpr int NOPS = A_PER_WAVE + DA_PER_WAVE + TP_PER_WAVE + 3 + 1;
+  constexpr int NOPS = A_PER_WAVE + DA_PER_WAVE + TP_PER_WAVE + W_OPS + 1;
   auto load_nib = [&](int s, int g) -> v4i {
-    return buf_load16(rw, (uint32_t)s * kRepTileBytes + g * 1024 + lane * 16);
+    return buf_load16(rw, (uint32_t)s * REC + g * 1024 + lane * 16);
   };
   const uint32_t lds0 = lds_addr(smem);
   auto issue_op = [&](int v, int s, int p, v4i& nib3) {
@@ -174,13 +182,13 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
       return;
     }
     v -= TP_PER_WAVE;
-    if (v < 3) {  // dsv [8][32] and dmv pieces [3][32][8]: 2560 contiguous bytes
+    if (v < W_OPS) {  // q4_K: dsv [8][32] and dmv pieces [3][32][8]; q6_K: dsv [16][32]
       const uint32_t sw = st + A_BYTES + DA_BYTES + TP_BYTES + wave * W_BYTES;
-      const uint32_t wo = (uint32_t)s * kRepTileBytes + kRepNibBytes + lane * 16;
-      if (v < 2 || lane < 32) dma16(rwd, sw + v * 1024, wo + v * 1024);
+      const uint32_t wo = (uint32_t)s * REC + REC_W + lane * 16;
+      if (Q6 || v < 2 || lane < 32) dma16(rwd, sw + v * 1024, wo + v * 1024);
       return;
     }
-    nib3 = load_nib(s, 3);
+    nib3 = load_nib(s, NG - 1);
   };
 
   v16i bias;
@@ -195,20 +203,21 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 
-  // raw[g]: the nibbles of sub-blocks 2g and 2g+1 of the current stage. Groups 0..2 of the
-  // next stage are loaded into raw[g] as soon as the last MFMA that reads them has been
-  // issued; group 3 is still in use at the end of the stage, so it goes through nib3.
-  v4i raw[4], nib3;
+  // raw[g]: q4_K: the nibbles of sub-blocks 2g and 2g+1 of the current stage; q6_K: the
+  // values of block g. Loads 0..NG-2 of the next stage go into raw[g] as soon as the last
+  // MFMA that reads them has been issued; the last one is still in use at the end of the
+  // stage, so it goes through nib3.
+  v4i raw[NG], nib3;
 #pragma unroll
   for (int v = 0; v < NOPS; ++v) issue_op(v, sb0, 0, nib3);
 #pragma unroll
-  for (int g = 0; g < 3; ++g) raw[g] = load_nib(sb0, g);
+  for (int g = 0; g < NG - 1; ++g) raw[g] = load_nib(sb0, g);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int s = sb0; s < sb1; ++s) {
     const int p = (s - sb0) & 1;
-    raw[3] = nib3;
+    raw[NG - 1] = nib3;
     const bool more = s + 1 < sb1;
 
     const uint8_t* st = smem + p * STAGE;
@@ -221,6 +230,9 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
       const v4i rr = raw[b >> 1];
       return (b & 1) ? ((rr >> 4) & 0x0F0F0F0F) : (rr & 0x0F0F0F0F);
     };
+    // q6_K: the weight operand of group gi (0, 1) of block b: lane half h carries the values
+    // 16h..16h+15 of the block, so keeping only half gi's lanes makes the MFMA sum one group
+    auto wop6_of = [&](int b, int gi) -> v4i { return h == gi ? raw[b] : v4i{0, 0, 0, 0}; };
     auto top_of = [&](int n) -> v4i {  // token operand of step n: 16 int8 of row t*32+l32
       const int b = n / TT, t = n % TT;
       return *reinterpret_cast<const v4i*>(sArow + t * 32 * kRowStride + b * 32);
@@ -235,23 +247,22 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
     };
 
     if constexpr (STORE_S) {
-      // test path: every S of the window, straight from the MFMA
-      v4i nxt[3] = {raw[0], raw[1], raw[2]};
+      // test path: every S of the window, straight from the MFMA (q4_K: one per 32-block,
+      // plane index s*8 + b; q6_K: one per 16-value group, plane index s*16 + 2b + gi)
+      v4i nxt[NG - 1];
+#pragma unroll
+      for (int g = 0; g < NG - 1; ++g) nxt[g] = raw[g];
       if (more) {
 #pragma unroll
         for (int v = 0; v < NOPS; ++v) issue_op(v, s + 1, p ^ 1, nib3);
 #pragma unroll
-        for (int g = 0; g < 3; ++g) nxt[g] = load_nib(s + 1, g);
+        for (int g = 0; g < NG - 1; ++g) nxt[g] = load_nib(s + 1, g);
       }
-#pragma unroll
-      for (int n = 0; n < NS; ++n) {
-        const int b = n / TT, t = n % TT;
-        const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(wop_of(b), top_of(n), bias, 0, 0, 0);
+      auto store = [&](const v16i& D, int bg, int t) {
         const int i = m0 + t * 32 + l32;
         if (wt_ok && i >= i0 && i < i1) {
           int32_t* S = static_cast<int32_t*>(out);
           const size_t plane = (size_t)(i1 - i0) * (size_t)(j1 - j0);
-          const int bg = s * 8 + b;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int j = wt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -259,9 +270,68 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
               S[(size_t)bg * plane + (size_t)(i - i0) * (j1 - j0) + (j - j0)] = D[r] - kBiasBits;
           }
         }
+      };
+#pragma unroll
+      for (int n = 0; n < NS; ++n) {
+        const int b = n / TT, t = n % TT;
+        if constexpr (Q6) {
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi)
+            store(__builtin_amdgcn_mfma_i32_32x32x32_i8(wop6_of(b, gi), top_of(n), bias, 0, 0, 0),
+                  s * 16 + 2 * b + gi, t);
+        } else {
+          store(__builtin_amdgcn_mfma_i32_32x32x32_i8(wop_of(b), top_of(n), bias, 0, 0, 0),
+                s * 8 + b, t);
+        }
       }
 #pragma unroll
-      for (int g = 0; g < 3; ++g) raw[g] = nxt[g];
+      for (int g = 0; g < NG - 1; ++g) raw[g] = nxt[g];
+    } else if constexpr (Q6) {
+      // q6_K, step n = b*TT + t: per 16-value group gi of block b, one MFMA on the lane half
+      // that holds it, then y = RN(S * da) and acc += dsv_g * y, groups in increasing order.
+      // The two groups' dsv (32 floats per lane) are read from LDS once per block.
+      float dsv[2][16];
+      v4i w6[2];
+#pragma unroll
+      for (int n = 0; n < NS; ++n) {
+        const int b = n / TT, t = n % TT;
+        if (n % 2 == 0) set_priority(3 - (n % 8) / 2);
+        if (more) {
+#pragma unroll
+          for (int v = 0; v < NOPS; ++v)
+            if (op_step(v) == n) issue_op(v, s + 1, p ^ 1, nib3);
+          // block g's MFMAs were issued by step (g+1)*TT - 1
+#pragma unroll
+          for (int g = 0; g < NG - 1; ++g)
+            if (n == (g + 1) * TT) raw[g] = load_nib(s + 1, g);
+        }
+        if (t == 0) {
+          w6[0] = wop6_of(b, 0);
+          w6[1] = wop6_of(b, 1);
+          dsv_of(2 * b, dsv[0]);
+          dsv_of(2 * b + 1, dsv[1]);
+        }
+        // The empty asm statements keep the steps in order (they are ordered among
+        // themselves): the step's MFMAs cannot be issued before its token operand passes one,
+        // nor its FMAs sink past the next. Left free, the compiler issued all the
+        // super-block's MFMAs first and spilled their results.
+        v4i top = top_of(n);
+        asm volatile("" : "+v"(top));
+        const v16i D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(w6[0], top, bias, 0, 0, 0);
+        const v16i D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(w6[1], top, bias, 0, 0, 0);
+        const float2 dac = da_of(n);  // (da, nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float y = __builtin_fmaf(__int_as_float(D0[r]), dac.x, dac.y);
+          acc[t][r] = __builtin_fmaf(y, dsv[0][r], acc[t][r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float y = __builtin_fmaf(__int_as_float(D1[r]), dac.x, dac.y);
+          acc[t][r] = __builtin_fmaf(y, dsv[1][r], acc[t][r]);
+        }
+        asm volatile("" : "+v"(acc[t]));
+      }
     } else {
       // Step n = b*TT + t. Entering step n: D(n) has been issued, the token operand of step
       // n+1 and da of step n are in registers; dsv[b & 1] holds block b's weight scales.
@@ -359,24 +429,24 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   }
 }
 
-template <int TT, int NW, bool STORE_S>
+template <int TT, int NW, bool STORE_S, int FMT>
 hipError_t launch_t(const void* q8, const void* w_rep, void* out, int64_t M, int64_t N,
                     int64_t K, int64_t gm, int64_t gn, int64_t splits, int64_t tm0, int64_t tn0,
                     int64_t i0, int64_t i1, int64_t j0, int64_t j1, hipStream_t s) {
   constexpr TileShape ts{TT, NW};
+  constexpr int64_t lds = ts.lds_bytes(FMT);
   const uint8_t* base = static_cast<const uint8_t*>(q8);
   const int8_t* qs = reinterpret_cast<const int8_t*>(base);
   const float* da_plane = reinterpret_cast<const float*>(base + q8_planes_offset(M, K));
   const uint16_t* tpieces = reinterpret_cast<const uint16_t*>(base + q8_pieces_offset(M, K));
-  auto kern = mmq_kernel<TT, NW, STORE_S>;
-  if (ts.lds_bytes() > 65536) {
+  auto kern = mmq_kernel<TT, NW, STORE_S, FMT>;
+  if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)ts.lds_bytes());
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)(gm * gn * splits)), dim3(ts.threads()),
-                     (size_t)ts.lds_bytes(), s, qs, da_plane, tpieces,
+                     (size_t)lds, s, qs, da_plane, tpieces,
                      static_cast<const uint8_t*>(w_rep), out, (int)M, (int)N, (int)K, (int)gm,
                      (int)(gm * gn), (int)splits, (int)tm0, (int)tn0, (int)i0, (int)i1, (int)j0,
                      (int)j1);
@@ -408,29 +478,41 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
   }
 }
 
-}  // namespace
-
-hipError_t launch_mmq(int tile, const void* q8, const void* w_rep, void* out, int64_t M,
+template <int FMT>
+hipError_t launch_fmt(int tile, const void* q8, const void* w_rep, void* out, int64_t M,
                       int64_t N, int64_t K, int64_t gm, int64_t gn, int64_t splits, int64_t tm0,
                       int64_t tn0, bool store_s, int64_t i0, int64_t i1, int64_t j0, int64_t j1,
                       hipStream_t s) {
   constexpr TileShape L = kLarge, S = kSmall, D = kMedium;
   if (tile == 1) {
-    return store_s ? launch_t<L.tt, L.nw, true>(q8, w_rep, out, M, N, K, gm, gn, 1, tm0, tn0,
-                                                i0, i1, j0, j1, s)
-                   : launch_t<L.tt, L.nw, false>(q8, w_rep, out, M, N, K, gm, gn, splits, tm0,
-                                                 tn0, i0, i1, j0, j1, s);
+    return store_s ? launch_t<L.tt, L.nw, true, FMT>(q8, w_rep, out, M, N, K, gm, gn, 1, tm0,
+                                                     tn0, i0, i1, j0, j1, s)
+                   : launch_t<L.tt, L.nw, false, FMT>(q8, w_rep, out, M, N, K, gm, gn, splits,
+                                                      tm0, tn0, i0, i1, j0, j1, s);
   }
   if (tile == 5) {
-    return store_s ? launch_t<D.tt, D.nw, true>(q8, w_rep, out, M, N, K, gm, gn, 1, tm0, tn0,
-                                                i0, i1, j0, j1, s)
-                   : launch_t<D.tt, D.nw, false>(q8, w_rep, out, M, N, K, gm, gn, splits, tm0,
-                                                 tn0, i0, i1, j0, j1, s);
+    return store_s ? launch_t<D.tt, D.nw, true, FMT>(q8, w_rep, out, M, N, K, gm, gn, 1, tm0,
+                                                     tn0, i0, i1, j0, j1, s)
+                   : launch_t<D.tt, D.nw, false, FMT>(q8, w_rep, out, M, N, K, gm, gn, splits,
+                                                      tm0, tn0, i0, i1, j0, j1, s);
   }
-  return store_s ? launch_t<S.tt, S.nw, true>(q8, w_rep, out, M, N, K, gm, gn, 1, tm0, tn0, i0,
-                                              i1, j0, j1, s)
-                 : launch_t<S.tt, S.nw, false>(q8, w_rep, out, M, N, K, gm, gn, splits, tm0, tn0,
-                                               i0, i1, j0, j1, s);
+  return store_s ? launch_t<S.tt, S.nw, true, FMT>(q8, w_rep, out, M, N, K, gm, gn, 1, tm0, tn0,
+                                                   i0, i1, j0, j1, s)
+                 : launch_t<S.tt, S.nw, false, FMT>(q8, w_rep, out, M, N, K, gm, gn, splits, tm0,
+                                                    tn0, i0, i1, j0, j1, s);
+}
+
+}  // namespace
+
+hipError_t launch_mmq(int tile, const void* q8, const void* w_rep, void* out, int64_t M,
+                      int64_t N, int64_t K, int64_t gm, int64_t gn, int64_t splits, int64_t tm0,
+                      int64_t tn0, bool store_s, int64_t i0, int64_t i1, int64_t j0, int64_t j1,
+                      hipStream_t s, int fmt) {
+  return fmt == kFmtQ6K
+             ? launch_fmt<kFmtQ6K>(tile, q8, w_rep, out, M, N, K, gm, gn, splits, tm0, tn0,
+                                   store_s, i0, i1, j0, j1, s)
+             : launch_fmt<kFmtQ4K>(tile, q8, w_rep, out, M, N, K, gm, gn, splits, tm0, tn0,
+                                   store_s, i0, i1, j0, j1, s);
 }
 
 hipError_t launch_reduce_splits(const float* ws, float* C, int64_t M, int64_t N, int64_t splits,

@@ -22,6 +22,18 @@ constexpr int kRepTileBytes = kRepNibBytes + kRepDsvBytes + kRepPieceBytes;  // 
 
 constexpr int kRowStride = 272;  // LDS bytes per staged token row (256 + 16 padding)
 
+// q6_K: the GGUF block (210 bytes) and the repacked record per (32-row tile, super-block):
+// int8 values u - 32 [b 0..7][h 0..1][j 0..31][16] (8192 B), then dsv = d*sc f32 [16][32]
+// (2048 B).
+constexpr int kQ6KBlockBytes = 210;
+constexpr int kRep6ValBytes = 8192;
+constexpr int kRep6DsvBytes = 2048;
+constexpr int kRep6TileBytes = kRep6ValBytes + kRep6DsvBytes;  // 10240
+
+// Weight formats of the GEMM template.
+constexpr int kFmtQ4K = 0;
+constexpr int kFmtQ6K = 1;
+
 // GEMM tile shapes: TT token tiles of 32 per wavefront, NW wavefronts (one 32-row weight
 // tile each) per workgroup.
 struct TileShape {
@@ -30,11 +42,15 @@ struct TileShape {
   constexpr int block_n() const { return 32 * nw; }
   constexpr int threads() const { return 64 * nw; }
   // LDS: two stages, each: the int8 token tile [BM][272], the (da, nda) pairs f32 [8][BM][2],
-  // the token pieces bf16 [3][BM][8], and per wavefront its dsv and dmv pieces (2560 bytes)
-  constexpr int64_t stage_bytes() const {
-    return (int64_t)block_m() * (kRowStride + 64 + 48) + (int64_t)nw * (kRepDsvBytes + kRepPieceBytes);
+  // and per wavefront its weight scales. q4_K also stages the token pieces bf16 [3][BM][8],
+  // and its weight scales are dsv and the dmv pieces (2560 bytes); q6_K's are dsv [16][32]
+  // (2048 bytes).
+  constexpr int64_t stage_bytes(int fmt = kFmtQ4K) const {
+    return fmt == kFmtQ4K
+               ? (int64_t)block_m() * (kRowStride + 64 + 48) + (int64_t)nw * (kRepDsvBytes + kRepPieceBytes)
+               : (int64_t)block_m() * (kRowStride + 64) + (int64_t)nw * kRep6DsvBytes;
   }
-  constexpr int64_t lds_bytes() const { return 2 * stage_bytes(); }
+  constexpr int64_t lds_bytes(int fmt = kFmtQ4K) const { return 2 * stage_bytes(fmt); }
 };
 constexpr TileShape kLarge{4, 8};
 constexpr TileShape kSmall{1, 2};
@@ -119,6 +135,7 @@ hipError_t launch_mmq_gemv_fused(const float* x, const void* w_rep, float* C, in
 
 hipError_t launch_quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, hipStream_t s);
 hipError_t launch_repack_q4_K(const void* w, int64_t N, int64_t K, void* w_rep, hipStream_t s);
+hipError_t launch_repack_q6_K(const void* w, int64_t N, int64_t K, void* w_rep, hipStream_t s);
 
 // GEMM launch: a 1-D grid of gm*gn*splits workgroups covering token tiles [tm0, tm0+gm),
 // weight-tile groups [tn0, tn0+gn) and `splits` contiguous ranges of super-blocks. store_s
@@ -128,7 +145,7 @@ hipError_t launch_repack_q4_K(const void* w, int64_t N, int64_t K, void* w_rep, 
 hipError_t launch_mmq(int tile, const void* q8, const void* w_rep, void* out, int64_t M,
                       int64_t N, int64_t K, int64_t gm, int64_t gn, int64_t splits, int64_t tm0,
                       int64_t tn0, bool store_s, int64_t i0, int64_t i1, int64_t j0, int64_t j1,
-                      hipStream_t s);
+                      hipStream_t s, int fmt = kFmtQ4K);
 hipError_t launch_reduce_splits(const float* ws, float* C, int64_t M, int64_t N, int64_t splits,
                                 hipStream_t s);
 

@@ -1,12 +1,14 @@
 """Reference byte images of the library's own storage layouts, written from include/mmq.h.
 
 These are test-side restatements of the documented layouts, not the method's arithmetic
-(that lives in oracle/, which knows only the q8_1 fields q, da, sa and the q4_K fields).
+(that lives in oracle/, which knows only the q8_1 fields q, da, sa and the q4_K and q6_K
+fields).
 Each image is built from the oracle's fields:
   - q8_image: the whole q8 buffer quantize_q8_1 writes: q and the packed (da, sa) words,
     then the GEMM's planes derived from da and sa;
   - repack_reference: the repacked weight records repack_q4_K writes;
   - read_repacked: a reader of such records, used to check that the layout round-trips;
+  - repack_q6k_reference, read_repacked_q6k: the same for repack_q6_K;
   - bf16_pieces: the three-piece bfloat16 split both planes use.
 """
 import numpy as np
@@ -135,3 +137,38 @@ def read_repacked(rep: np.ndarray, N: int, K: int) -> dict:
     vals = bf16_value(pc)
     dmv = vals.sum(axis=2).transpose(0, 2, 1, 3).reshape(nt * TILE_ROWS, K // 32)
     return {"v": v[:N], "dsv": dsv[:N], "dmv": dmv[:N]}
+
+
+TILE6_BYTES = 10240
+
+
+def repack_q6k_reference(fields: dict) -> np.ndarray:
+    """Expected repack_q6_K output for the q6_K fields (u [N, K], sc [N, K/16], d_bits)."""
+    u = np.asarray(fields["u"], np.int64)
+    N, K = u.shape
+    nsb = K // 256
+    nt = -(-N // TILE_ROWS)
+    vals = np.zeros((nt * TILE_ROWS, K), np.int64)
+    vals[:N] = u - 32
+    v = vals.reshape(nt, TILE_ROWS, nsb, 8, 2, 16)                    # [t, j, s, b, h, e]
+    v = v.transpose(0, 2, 3, 4, 1, 5).astype(np.int8)                 # [t, s, b, h, j, e]
+    d = np.asarray(fields["d_bits"], np.uint16).view(np.float16).astype(np.float32)
+    dsv = np.zeros((nt * TILE_ROWS, nsb, 16), np.float32)
+    dsv[:N] = d[..., None] * np.asarray(fields["sc"], np.float32).reshape(N, nsb, 16)
+    dsv = dsv.reshape(nt, TILE_ROWS, nsb, 16).transpose(0, 2, 3, 1)   # [t, s, g, j]
+    out = np.zeros((nt, nsb, TILE6_BYTES), np.uint8)
+    out[..., :8192] = np.ascontiguousarray(v).view(np.uint8).reshape(nt, nsb, 8192)
+    out[..., 8192:] = np.ascontiguousarray(dsv).view(np.uint8).reshape(nt, nsb, 2048)
+    return out.reshape(-1)
+
+
+def read_repacked_q6k(rep: np.ndarray, N: int, K: int) -> dict:
+    """Decode repacked q6_K records back into the values u - 32 [N, K] and dsv [N, K/16]."""
+    nsb = K // 256
+    nt = -(-N // TILE_ROWS)
+    r = rep.reshape(nt, nsb, TILE6_BYTES)
+    v = r[..., :8192].copy().view(np.int8).reshape(nt, nsb, 8, 2, TILE_ROWS, 16)
+    v = v.transpose(0, 4, 1, 2, 3, 5).reshape(nt * TILE_ROWS, K)      # [t, j, s, b, h, e]
+    dsv = r[..., 8192:].copy().view(np.float32).reshape(nt, nsb, 16, TILE_ROWS)
+    dsv = dsv.transpose(0, 3, 1, 2).reshape(nt * TILE_ROWS, K // 16)
+    return {"v": v[:N].astype(np.int64), "dsv": dsv[:N]}

@@ -106,3 +106,21 @@ def test_q8_image_layout():
     assert np.array_equal(reg["qs"], q.qs)
     assert np.array_equal(reg["words"], words)
     assert np.array_equal(reg["pairs"], pairs)
+
+
+@pytest.mark.parametrize("N,K", [(32, 256), (33, 512), (70, 768), (5, 256)])
+def test_repack_q6k_reference_roundtrip(N, K):
+    """The q6_K record reference, read back, gives the oracle's decode of the same blocks."""
+    from tests.layout_ref import read_repacked_q6k, repack_q6k_reference
+    f = synth.q6k_random_fields(N, K, N * 5 + K)
+    rep = repack_q6k_reference(f)
+    assert rep.size == -(-N // 32) * (K // 256) * 10240
+    got = read_repacked_q6k(rep, N, K)
+    w = oracle.decode_q6_K(synth.q6k_pack(f))
+    assert np.array_equal(got["v"], w.u - 32)
+    assert np.array_equal(got["dsv"].astype(np.float64), oracle.q6_K_scales(w))
+    nt = -(-N // 32)
+    last = rep.reshape(nt, K // 256, 10240)[-1]
+    rows_used = N - (nt - 1) * 32
+    vals = last[:, :8192].reshape(K // 256, 8, 2, 32, 16)
+    assert np.all(vals[:, :, :, rows_used:, :] == 0)
