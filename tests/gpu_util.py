@@ -1,5 +1,7 @@
 """Helpers for the GPU tests: device buffers, calls through the C ABI, oracle caching."""
 import functools
+import json
+import os
 import sys
 
 import numpy as np
@@ -86,4 +88,11 @@ def assert_within_tolerance(C_gpu: np.ndarray, C_ref: np.ndarray, T: np.ndarray,
         raise AssertionError(f"{bad.sum()} elements outside {tol}*T, first {idx}: "
                              f"gpu={C_gpu[bad][:5]}, ref={C_ref[bad][:5]}, T={T[bad][:5]}")
     pos = T > 0
-    return float((err[pos] / T[pos]).max()) if np.any(pos) else 0.0
+    r = float((err[pos] / T[pos]).max()) if np.any(pos) else 0.0
+    log = os.environ.get("PARITY_LOG")
+    if log:   # the measured ratio of each case, for the record of the run
+        with open(log, "a") as f:
+            f.write(json.dumps({"case": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0],
+                                "shape": list(C_gpu.shape), "max_err_over_T": r,
+                                "tol": tol}) + "\n")
+    return r

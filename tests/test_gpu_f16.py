@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import oracle_w, sample_rows, say, to_dev, workload
+from tests.gpu_util import oracle_w, sample_rows, say, to_dev, workload  # noqa: F401
 from tests.test_oracle_f16_pins import _F16_CASES
 
 pytestmark = pytest.mark.gpu
@@ -72,6 +72,12 @@ def check_gemm(C_gpu, a_bits, w_bits, K):
     pos = T > 0
     ratio = float((err[pos] / T[pos]).max()) if pos.any() else 0.0
     print(f"[f16 gemm] max |err|/T = {ratio:.3e} (bound {tol:.3e})")
+    log = os.environ.get("PARITY_LOG")
+    if log:   # the measured ratio beside its bound, for the record of the run
+        with open(log, "a") as f:
+            f.write(json.dumps({"case": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0],
+                                "shape": list(C_gpu.shape), "max_err_over_T": ratio,
+                                "tol": tol}) + "\n")
     return ratio
 
 
@@ -161,14 +167,12 @@ def test_gemm_ragged_and_degenerate(M, N, K):
 
 
 @pytest.mark.parametrize("name", ["qproj", "gateup", "down"])
-def test_gemm_full_size_sampled_rows(name):
+def test_gemm_full_size_every_element(name):
     W = workload(name)
     a = oracle.convert_f32_f16(W["x"])
     w = oracle.dequantize_q4_K_f16(oracle_w(name))
     say("gemm_f16 full size", name, a.shape, w.shape)
-    C = gpu_gemm(a, w)
-    rows = sample_rows(W["M"])
-    check_gemm(C[rows], a[rows], w, W["K"])
+    check_gemm(gpu_gemm(a, w), a, w, W["K"])
 
 
 def test_gemm_deterministic():

@@ -73,7 +73,8 @@ def test_fused_equals_prepass_then_unfused(M, N, K):
     assert info["tile"] == fused_tile(M) and info["reason"] == mmq.MMQ_REASON_FUSED
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 256, 512), (9, 70, 1024), (40, 33, 768)])
+@pytest.mark.parametrize("M,N,K", [(1, 256, 512), (9, 70, 1024), (40, 33, 768),
+                                   (1, 4096, 4096), (8, 4096, 4096), (128, 4096, 4096)])
 def test_fused_against_the_oracle(M, N, K):
     x = synth.activations("normal_outliers", M, K, 9100 + M)
     w, _ = synth.q4k_weights("random_fields", N, K, 9101 + N)
