@@ -441,7 +441,7 @@ def rotation(M: int, N: int, K: int, r_min: int) -> int:
     """Input/output sets to rotate over so that one pass over them (at least 512 MiB, at most
     64 sets) exceeds the 256 MB last-level cache: with few tokens a set is little more than
     the weights, and 8 of them would stay cache-resident."""
-    per_set = 5.6 * M * K + (N + 31) // 32 * (K // 256) * 6656 + 4 * M * N
+    per_set = 5.6 * M * K + (N + 31) // 32 * (K // 256) * 4608 + 4 * M * N
     return int(min(64, max(r_min, -(-(512 << 20) // per_set))))
 
 

@@ -48,7 +48,7 @@ enum mmq_status {
 #define MMQ_QK_K 256             /* q4_K super-block length */
 #define MMQ_Q4K_BLOCK_BYTES 144  /* bytes of one q4_K super-block */
 #define MMQ_REP_TILE_ROWS 32     /* weight rows per repacked tile */
-#define MMQ_REP_TILE_BYTES 6656  /* bytes per (repacked tile, super-block) */
+#define MMQ_REP_TILE_BYTES 4608  /* bytes per (repacked tile, super-block) */
 #define MMQ_Q6K_BLOCK_BYTES 210  /* bytes of one q6_K super-block */
 #define MMQ_REP6_TILE_BYTES 10240 /* bytes per (repacked q6_K tile, super-block) */
 
@@ -139,7 +139,8 @@ int mmq_q8_1_bytes(int64_t M, int64_t K, size_t* bytes);
 /* Bytes of q4_K weights N x K in the GGUF layout: N*(K/256)*144. K % 256 == 0. */
 int mmq_q4K_bytes(int64_t N, int64_t K, size_t* bytes);
 
-/* Bytes of repacked q4_K weights: ceil(N/32)*(K/256)*6656. K % 256 == 0. */
+/* Bytes of repacked q4_K weights: ceil(N/32)*(K/256)*4608 (4.5 bits per weight, the size
+ * of the GGUF blocks). K % 256 == 0. */
 int mmq_q4K_repacked_bytes(int64_t N, int64_t K, size_t* bytes);
 
 /* ---------------------------------------------------------------- the hot path */
@@ -178,16 +179,19 @@ int quantize_q8_1(const float* x, int64_t M, int64_t K, void* q8, void* stream);
 
 /*
  * repack_q4_K: q4_K weights (GGUF layout, [N][K/256] super-blocks of 144 bytes, the fields of
- * the r15 page, section 2.1) -> the GEMM's layout. Run once per weight matrix.
- * Output (mmq_q4K_repacked_bytes(N, K) bytes): one 6656-byte record per (tile t of 32 weight
+ * the r15 page, section 2.1) -> the kernels' layout. Run once per weight matrix.
+ * Output (mmq_q4K_repacked_bytes(N, K) bytes): one 4608-byte record per (tile t of 32 weight
  * rows, super-block s), records ordered [t][s]; rows N..32*ceil(N/32)-1 are zero. Record:
  *   bytes [0, 4096):   nibbles, [g 0..3][h 0..1][j 0..31][16 bytes] = bytes 32g+16h .. +15 of
  *                      the 128 nibble bytes of row 32t+j (low nibble: sub-block 2g, element
  *                      16h+e; high nibble: sub-block 2g+1, element 16h+e)
- *   bytes [4096, 5120): float dsv[b 0..7][j 0..31] = d*sc of sub-block b of row 32t+j
- *   bytes [5120, 6656): uint16 bf16 pieces [i 0..2][j 0..31][b 0..7] of dmv = -(dmin*m),
- *                       split as the pieces of da*sa at quantize_q8_1 (they sum to dmv)
- * Both scale products are exact in float32.
+ *   bytes [4096, 4608): [j 0..31][16 bytes] = bytes 0..15 of row 32t+j's block, unchanged:
+ *                       f16 d, f16 dmin, the 12 bytes of packed 6-bit sc and m
+ * The kernels expand the scales of sub-block b from the header as they stage it:
+ * dsv = d*sc and dmv = -(dmin*m), both exact in float32 (and dmv for the matrix unit as the
+ * three bf16 pieces that sum to it exactly: the top 16 bits of dmv, the top 16 bits of what
+ * is left, and the rest). Precondition of the products: finite d and dmin in every block
+ * (a non-finite one leaves its row's outputs unspecified).
  * Errors: MMQ_E_ARG, MMQ_E_SHAPE (K % 256; ceil(N/32)*(K/256) >= 2^31), MMQ_E_DEVICE,
  *         MMQ_E_HIP.
  */

@@ -38,7 +38,7 @@ MMQ_OK, MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_LDS, MMQ_E_DEVICE, MMQ_E_HIP = range(6)
  MMQ_REASON_FORCED, MMQ_REASON_NO_FIT, MMQ_REASON_FEW_TOKENS, MMQ_REASON_FUSED,
  MMQ_REASON_DECODE, MMQ_REASON_SPLIT_K) = range(10)
 GEMV_MAX_M = 16  # largest M of the decode tile, which the guard chooses up to there
-QK8, QK_K, Q4K_BLOCK_BYTES, REP_TILE_ROWS, REP_TILE_BYTES = 32, 256, 144, 32, 6656
+QK8, QK_K, Q4K_BLOCK_BYTES, REP_TILE_ROWS, REP_TILE_BYTES = 32, 256, 144, 32, 4608
 Q6K_BLOCK_BYTES, REP6_TILE_BYTES = 210, 10240
 
 

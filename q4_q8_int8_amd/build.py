@@ -30,6 +30,10 @@ FLAGS = [
     # MFMA results in VGPRs: the epilogue reads every S on the vector ALU, and an MFMA that
     # writes accumulation registers would cost one v_accvgpr_read per element
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # every loop marked "#pragma unroll" in the kernels is meant to unroll completely (the
+    # GEMM's super-block loop holds register tuples indexed by the step number); the default
+    # size limit for such loops is below that loop's size
+    "-mllvm", "-pragma-unroll-threshold=262144",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

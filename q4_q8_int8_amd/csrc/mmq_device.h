@@ -68,4 +68,69 @@ static __device__ __forceinline__ void dma16(v4i r, uint32_t lds, uint32_t off) 
 }
 #pragma clang diagnostic pop
 
+// Weight scales of one row's q4_K super-block, from the 16-byte header the repacked record
+// keeps per row (word 0: f16 d in bits 0..15, f16 dmin in bits 16..31; words 1..3: the 12
+// packed scale bytes s0..s11), for the four sub-blocks 4*half .. 4*half + 3. GGUF packing:
+// sub-block b < 4 has sc = s[b] & 63 and m = s[b+4] & 63; b >= 4 has the low four bits of sc
+// and m in the low and high nibble of s[b+4] and their top two bits in bits 6..7 of s[b-4]
+// and s[b]. Four bytes at a time: dsv[k] = d * sc and dmv[k] = -(dmin * m), each exact in f32
+// (an f16 times a 6-bit integer).
+static __device__ __forceinline__ void q4k_scales(v4i hdr, bool half, float (&dsv)[4],
+                                                  float (&dmv)[4]) {
+  const uint32_t w0 = (uint32_t)hdr[0], s0 = (uint32_t)hdr[1], s1 = (uint32_t)hdr[2],
+                 s2 = (uint32_t)hdr[3];
+  const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(w0 & 0xFFFFu));
+  const float dmin = (float)__builtin_bit_cast(_Float16, (uint16_t)(w0 >> 16));
+  // both halves' bytes, then a blend (a select of lane-varying operands would branch)
+  const uint32_t hm = 0u - (uint32_t)half;
+  const uint32_t sc = (((s2 & 0x0F0F0F0Fu) | ((s0 >> 2) & 0x30303030u)) & hm) |
+                      ((s0 & 0x3F3F3F3Fu) & ~hm);
+  const uint32_t mm = ((((s2 >> 4) & 0x0F0F0F0Fu) | ((s1 >> 2) & 0x30303030u)) & hm) |
+                      ((s1 & 0x3F3F3F3Fu) & ~hm);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    dsv[k] = d * (float)((sc >> (8 * k)) & 0xFFu);
+    dmv[k] = -(dmin * (float)((mm >> (8 * k)) & 0xFFu));
+  }
+}
+
+// Three bfloat16 pieces that sum exactly to a finite float v, by truncation: p0 = the top 16
+// bits of v, p1 = the top 16 bits of r = v - p0, p2 = r - p1. Both differences are exact (each
+// drops leading bits of the significand), and p2 keeps at most the last 8 of v's 24
+// significant bits, so it is a bfloat16 value too. Returned as the float bit patterns whose
+// high halves are the pieces (their low halves are not part of the pieces).
+static __device__ __forceinline__ void bf16_trunc3(float v, uint32_t& p0, uint32_t& p1,
+                                                   uint32_t& p2) {
+  p0 = __builtin_bit_cast(uint32_t, v);
+  const float r = v - __builtin_bit_cast(float, p0 & 0xFFFF0000u);
+  p1 = __builtin_bit_cast(uint32_t, r);
+  p2 = __builtin_bit_cast(uint32_t, r - __builtin_bit_cast(float, p1 & 0xFFFF0000u));
+}
+
+// The high halves of two float bit patterns as one word: lo's in bits 0..15, hi's above.
+static __device__ __forceinline__ uint32_t pack_hi16(uint32_t lo, uint32_t hi) {
+  return (lo >> 16) | (hi & 0xFFFF0000u);
+}
+
+// The weight scales of sub-blocks 4*half .. 4*half + 3 of row `row` (0..31) of a tile, as the
+// MFMA kernels stage them in LDS at sw: dsv f32 [8][32], then the three bf16 pieces of dmv
+// [3][32][8] (bf16_trunc3). The header must hold finite d and dmin.
+static __device__ __forceinline__ void q4k_stage_scales(v4i hdr, int row, bool half,
+                                                        uint8_t* sw) {
+  float dsv[4], dmv[4];
+  q4k_scales(hdr, half, dsv, dmv);
+  const int b0 = 4 * (int)half;
+  float* sd = reinterpret_cast<float*>(sw);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) sd[(b0 + k) * 32 + row] = dsv[k];
+  uint32_t p[4][3];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) bf16_trunc3(dmv[k], p[k][0], p[k][1], p[k][2]);
+  uint16_t* pc = reinterpret_cast<uint16_t*>(sw + kWDsvBytes);
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+    *reinterpret_cast<uint2*>(pc + (i * 32 + row) * 8 + b0) =
+        make_uint2(pack_hi16(p[0][i], p[1][i]), pack_hi16(p[2][i], p[3][i]));
+}
+
 }  // namespace mmq

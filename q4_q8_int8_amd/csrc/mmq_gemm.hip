@@ -15,9 +15,9 @@
 //
 // y equals float(S) * da bit for bit, without an int->float conversion instruction.
 // term2 is rank-1 per block: the row factor dma = da * sa (exact in f32, written by the
-// quantize prepass) times the column factor dmv (exact in f32). Both are stored as three
-// bf16 pieces that sum to them exactly, so over the 8 blocks of a super-block term2 is a
-// K = 8 product of pieces; three v_mfma_f32_32x32x16_bf16 per token tile and super-block
+// quantize prepass) times the column factor dmv (exact in f32). Both come as three bf16
+// pieces that sum to them exactly (those of dma from the prepass, those of dmv expanded in
+// the kernel), so over the 8 blocks of a super-block term2 is a K = 8 product of pieces; three v_mfma_f32_32x32x16_bf16 per token tile and super-block
 // (each lane half supplying one piece pair) add the six largest of the nine piece products
 // into the same accumulator, every product exact in f32. Per element the terms are added
 // in a fixed order (term1 of each block, a third of term2 after blocks 1, 3 and 5), so
@@ -36,8 +36,10 @@
 //   - into LDS by direct-to-LDS buffer loads (no registers, no conversion): the int8 token
 //     tile in 272-byte rows (16 bytes of padding, so the 16-byte operand reads of 16
 //     consecutive rows hit distinct banks and every LDS address is a per-lane base plus a
-//     constant), the (da, nb) pairs and the dma pieces of the token tile, and each
-//     wavefront's dsv/dmv;
+//     constant), the (da, nb) pairs and the dma pieces of the token tile, and the 16-byte
+//     q4_K headers of each wavefront's 32 weight rows (d, dmin, the packed sc and m), from
+//     which the wavefront expands dsv = d*sc and the dmv = -(dmin*m) pieces into its LDS
+//     region when the stage begins, while its first MFMA runs (q4k_stage_scales);
 //   - into registers: the wavefront's nibbles, where the 64 lanes of one load read 1 KiB of
 //     contiguous memory.
 // Buffer loads take 32-bit offsets off wave-uniform descriptors; reads past the end of an
@@ -73,9 +75,10 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   constexpr bool Q6 = FMT == kFmtQ6K;
   // q4_K: token pieces of da*sa [3][BM][8] for term2; q6_K has no term2
   constexpr int TP_BYTES = Q6 ? 0 : BM * 48;
-  // per wavefront: q4_K dsv and the dmv pieces, q6_K dsv of its 16 groups
-  constexpr int W_BYTES = Q6 ? kRep6DsvBytes : kRepDsvBytes + kRepPieceBytes;
-  constexpr int W_OPS = Q6 ? 2 : 3;               // 1 KiB loads of W_BYTES (q4_K: 2.5)
+  // per wavefront in LDS: q4_K dsv and the dmv pieces, expanded at the start of the stage
+  // from the tile's 32 row headers loaded behind them; q6_K dsv of its 16 groups
+  constexpr int W_BYTES = Q6 ? kRep6DsvBytes : kWDsvBytes + kWPieceBytes + kRepHdrBytes;
+  constexpr int W_OPS = Q6 ? 2 : 1;  // direct-to-LDS loads of the record's scales or headers
   constexpr int REC = Q6 ? kRep6TileBytes : kRepTileBytes;   // record per (tile, super-block)
   constexpr int REC_W = Q6 ? kRep6ValBytes : kRepNibBytes;   // where its scales start
   constexpr int NG = Q6 ? 8 : 4;   // 16-byte operand loads per lane and super-block
@@ -142,18 +145,18 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
     tp_off[j] = ((uint32_t)pc * (uint32_t)M + (uint32_t)(m0 + r)) * 16u;
   }
   // What stage s of the pipeline loads into LDS, as NOPS single DMA instructions of this
-  // wavefront (its token-tile DMAs, its da DMAs, its token-piece DMA (q4_K), its W_BYTES of
-  // weight scales), followed by op NOPS: the last weight-operand load (q4_K nibble group 3,
-  // q6_K block 7) into registers. Op v is a compile-time constant wherever it is issued, so
-  // each call folds to one instruction. The other operand loads are issued separately, in
-  // place (load_nib).
+  // wavefront (its token-tile DMAs, its da DMAs, its token-piece DMA (q4_K), its weight
+  // scales: q4_K the 32 row headers, q6_K 2 KiB of dsv), followed by op NOPS: the last
+  // weight-operand load (q4_K nibble group 3, q6_K block 7) into registers. Op v is a
+  // compile-time constant wherever it is issued, so each call folds to one instruction. The
+  // other operand loads are issued separately, in place (load_nib).
   constexpr int DA_PER_WAVE = (8 + NW - 1) / NW;
   // The next stage's ops are issued three at a time at the first step of every other
   // sub-block (the last ones at the last step at the latest), so that the wavefronts of a
   // workgroup do not queue all their memory instructions at once. Finer spreading costs
   // registers: each issue point constrains how far ahead the compiler schedules LDS reads.
-  auto op_step = [](int v) { return ((v / 3) * 2 * TT < NS - 1) ? (v / 3) * 2 * TT : NS - 1; };
   constexpr int NOPS = A_PER_WAVE + DA_PER_WAVE + TP_PER_WAVE + W_OPS + 1;
+  auto op_step = [](int v) { return ((v / 3) * 2 * TT < NS - 1) ? (v / 3) * 2 * TT : NS - 1; };
   auto load_nib = [&](int s, int g) -> v4i {
     return buf_load16(rw, (uint32_t)s * REC + g * 1024 + lane * 16);
   };
@@ -182,10 +185,11 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
       return;
     }
     v -= TP_PER_WAVE;
-    if (v < W_OPS) {  // q4_K: dsv [8][32] and dmv pieces [3][32][8]; q6_K: dsv [16][32]
+    if (v < W_OPS) {  // q4_K: the row headers [32][16] (lanes 0..31); q6_K: dsv [16][32]
       const uint32_t sw = st + A_BYTES + DA_BYTES + TP_BYTES + wave * W_BYTES;
       const uint32_t wo = (uint32_t)s * REC + REC_W + lane * 16;
-      if (Q6 || v < 2 || lane < 32) dma16(rwd, sw + v * 1024, wo + v * 1024);
+      if (Q6) dma16(rwd, sw + v * 1024, wo + v * 1024);
+      else if (lane < 32) dma16(rwd, sw + kWDsvBytes + kWPieceBytes, wo);
       return;
     }
     nib3 = load_nib(s, NG - 1);
@@ -226,6 +230,18 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
     const uint8_t* sTp = st + A_BYTES + DA_BYTES;
     const uint8_t* sW = st + A_BYTES + DA_BYTES + TP_BYTES + wave * W_BYTES;
     const float* sWw = reinterpret_cast<const float*>(sW);
+    // q4_K, before the stage's first read of dsv or the dmv pieces: lane (l32, h) expands
+    // sub-blocks 4h .. 4h+3 of row l32 from its header, loaded behind the region. Only this
+    // wavefront reads the region, so a wavefront-scope fence orders the other lanes' writes
+    // before those reads.
+    auto expand_scales = [&]() {
+      uint8_t* sWm = smem + p * STAGE + A_BYTES + DA_BYTES + TP_BYTES + wave * W_BYTES;
+      const v4i hdr =
+          *reinterpret_cast<const v4i*>(sWm + kWDsvBytes + kWPieceBytes + l32 * 16);
+      q4k_stage_scales(hdr, l32, h != 0, sWm);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    };
     auto wop_of = [&](int b) -> v4i {
       const v4i rr = raw[b >> 1];
       return (b & 1) ? ((rr >> 4) & 0x0F0F0F0F) : (rr & 0x0F0F0F0F);
@@ -335,11 +351,14 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
     } else {
       // Step n = b*TT + t. Entering step n: D(n) has been issued, the token operand of step
       // n+1 and da of step n are in registers; dsv[b & 1] holds block b's weight scales.
-      float dsv[2][16];
-      dsv_of(0, dsv[0]);
+      // the first MFMA needs no weight scales: issued first, it runs while they are expanded
+      v16i Dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(wop_of(0), top_of(0), bias, 0, 0, 0);
+      asm volatile("" : "+v"(Dn));  // issued here, not sunk below the expansion
       v4i tnext = top_of(1 % NS);
       float2 da = da_of(0);
-      v16i Dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(wop_of(0), top_of(0), bias, 0, 0, 0);
+      expand_scales();
+      float dsv[2][16];
+      dsv_of(0, dsv[0]);
 #pragma unroll
       for (int n = 0; n < NS; ++n) {
         const int b = n / TT, t = n % TT;
@@ -365,6 +384,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
         }
         if (n + 2 < NS) tnext = top_of(n + 2);
         if (t == 0 && b + 1 < 8) dsv_of(b + 1, dsv[(b + 1) & 1]);
+        // the next stage's weight scales, from the header issued at its step 0, into the
+        // other stage buffer (read by no one before the barrier that ends this stage)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float y = __builtin_fmaf(__int_as_float(D[r]), dac.x, dac.y);
@@ -377,7 +398,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
           const int u = b >> 1;
           const int ia = u == 0 ? 0 : (u == 1 ? 1 - h : 1 + h);
           const int jb = u == 0 ? h : (u == 1 ? 2 * h : 1 - h);
-          const v8bf wa = *reinterpret_cast<const v8bf*>(sW + kRepDsvBytes + (ia * 32 + l32) * 16);
+          const v8bf wa = *reinterpret_cast<const v8bf*>(sW + kWDsvBytes + (ia * 32 + l32) * 16);
           const v8bf tb = *reinterpret_cast<const v8bf*>(sTp + (jb * BM + t * 32 + l32) * 16);
           acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, tb, acc[t], 0, 0, 0);
         }

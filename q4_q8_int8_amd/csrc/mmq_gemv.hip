@@ -5,7 +5,7 @@
 //   C[m][n] += da * (dsv * S + dmv * sa)
 // which is term1 (da * dsv * S) plus term2 (dmv times the row factor da * sa) of the r15 page
 // ("f32-accumulate mma probe + rank-1 term2 rescale", section 2.1), with dsv = d*sc and
-// dmv = -dmin*m expanded by the repack.
+// dmv = -dmin*m expanded from the row's header in the repacked record.
 //
 // With one to sixteen tokens the product streams the weights once and does little else, so
 // matrix instructions buy nothing: the MFMA tiles of the other kernels are 32 tokens wide and
@@ -19,9 +19,9 @@
 // workgroups rather than longer wavefronts; the groups of one row block read the same weights,
 // mostly from L2.
 //
-// Per step a lane loads its row's 64 nibble bytes of its half, its 4 scales dsv and the three
-// bf16 pieces of its 4 mins dmv (buffer loads; the 16 lanes of a slice read 256 contiguous
-// bytes); in the same burst the lanes of a wavefront load its four slices' token bytes of that
+// Per step a lane loads its row's 64 nibble bytes of its half and its row's 16-byte header,
+// from which it expands the 4 scales dsv and 4 mins dmv of its half (buffer loads; the 16
+// lanes of a slice read 256 contiguous bytes); in the same burst the lanes of a wavefront load its four slices' token bytes of that
 // half and their (da, sa) words, and put them in the wavefront's own LDS region, which each
 // slice's lanes then read at one address (broadcast). When a slice has another super-block,
 // its loads are issued before this one is computed. Read instead one token at a time with
@@ -51,6 +51,7 @@ namespace mmq {
 namespace {
 
 constexpr int kGemvSlices = 64 / kGemvRows;              // K-slices per wavefront
+constexpr int kGemvMfmaScaleBytes = 1280;                // 9-16 tokens: scales per wavefront
 constexpr int kGemvKS = kGemvSlices * (kGemvWaves / 2);  // K-slices per workgroup (16)
 
 template <int MT, bool FUSED>
@@ -105,8 +106,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
 
   struct Stage {
     v4i nib[4];      // chunk (g, h) of the half at 2 (g - 2 hf) + h
-    float dsv[4];
-    uint2 pc[3];     // dmv pieces of blocks 4 hf .. 4 hf + 3
+    v4i hdr;         // the row's super-block header (d, dmin, packed sc and m)
     v4i tok[FUSED ? 1 : kTokPerLane];
     float2 sc[kScPerLane];  // (da, float(sa)) of entries lane + 64 t (below kSc)
     float4 xv[FUSED ? MT : 1][2];
@@ -117,14 +117,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       st.nib[t] = buf_load16(rw, rec + (2 * hf + (t >> 1)) * 1024 + (t & 1) * 512 + j * 16);
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      st.dsv[b] = buf_load_f32(rw, rec + kRepNibBytes + (4 * hf + b) * 128 + j * 4);
-#pragma unroll
-    for (int p = 0; p < 3; ++p)
-      st.pc[p] = __builtin_bit_cast(
-          uint2,
-          buf_load_f32x2(rw, rec + kRepNibBytes + kRepDsvBytes + p * 512 + j * 16 + hf * 8));
+    st.hdr = buf_load16(rw, rec + kRepNibBytes + j * 16);
     if constexpr (FUSED) {
       const int cs = wq * kGemvSlices + fq + i * kGemvKS;
 #pragma unroll
@@ -233,24 +226,14 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
     __builtin_amdgcn_wave_barrier();
     if (act) {
       const uint8_t* sl = region + q * kSlice;
+      float dsv[4], dmv[4];
+      q4k_scales(cur.hdr, hf != 0, dsv, dmv);
       // nds = -1.5 * 2^23 * dsv (exact): with the dot products started at the bias word
       // 0x4B400000, whose float value is 1.5 * 2^23, fma(D, dsv, nds) = RN(S * dsv) in one
       // instruction, as float(S) * dsv would be in two (|S| < 2^22 keeps D in one binade)
       float nds[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) nds[b] = -kBiasF * cur.dsv[b];
-      // dmv = p0 + p1 + p2, exact in f32
-      float dmv[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        float p[3];
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {
-          const uint32_t w = (b >> 1) ? cur.pc[t].y : cur.pc[t].x;
-          p[t] = __builtin_bit_cast(float, (b & 1) ? (w & 0xFFFF0000u) : (w << 16));
-        }
-        dmv[b] = (p[0] + p[1]) + p[2];
-      }
+      for (int b = 0; b < 4; ++b) nds[b] = -kBiasF * dsv[b];
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
         int lo[8], hi[8];
@@ -277,10 +260,10 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
                 S1 = __builtin_amdgcn_sdot4(hi[4 * h + d], c[d], S1, false);
               }
             }
-            const float t0 = __builtin_fmaf(__int_as_float(S0), cur.dsv[2 * gg], nds[2 * gg]);
+            const float t0 = __builtin_fmaf(__int_as_float(S0), dsv[2 * gg], nds[2 * gg]);
             acc[m] = __builtin_fmaf(__builtin_fmaf(dmv[2 * gg], sc.y, t0), sc.x, acc[m]);
             const float t1 =
-                __builtin_fmaf(__int_as_float(S1), cur.dsv[2 * gg + 1], nds[2 * gg + 1]);
+                __builtin_fmaf(__int_as_float(S1), dsv[2 * gg + 1], nds[2 * gg + 1]);
             acc[m] = __builtin_fmaf(__builtin_fmaf(dmv[2 * gg + 1], sc.w, t1), sc.z, acc[m]);
           }
         }
@@ -317,7 +300,9 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
 // l % 16, the four outputs of rows 4 (l / 16) .. + 3, and rescales them as the GEMM does:
 // y = fma(D, da, nda) with D biased by 0x4B400000, acc = fma(y, dsv, acc). term2 of a
 // super-block is a K = 8 product of dmv and da*sa; as in the GEMM it runs on the bf16 matrix
-// unit from the exact three-piece splits stored in the record and in the q8 buffer: two
+// unit from exact three-piece splits, those of da*sa stored in the q8 buffer, those of dmv
+// (bf16_trunc3) expanded from the row headers into the wavefront's LDS region (with dsv) per
+// super-block, lane (c, g) taking sub-blocks 2g and 2g + 1 of row c: two
 // v_mfma_f32_16x16x32_bf16 whose 4 k-groups of 8 blocks carry the piece pairs (0,0) (0,1)
 // (1,0) (0,2) | (1,1) (2,0) (and two zero groups), added into the same accumulator. The NW
 // wavefronts' partial sums are added in wavefront order through LDS.
@@ -329,6 +314,10 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
     const uint16_t* __restrict__ tpieces, const uint8_t* __restrict__ wrep,
     float* __restrict__ C, int M, int N, int K) {
   __shared__ float red[NW][16][16];  // [wavefront][token][row]
+  // per wavefront: dsv f32 [8 blocks][16 rows], then the dmv pieces bf16 [3][16 rows][8]
+  constexpr int kWsDsv = 8 * 16 * 4;
+  static_assert(kWsDsv + 3 * 16 * 8 * 2 == kGemvMfmaScaleBytes, "scale region");
+  __shared__ __align__(16) uint8_t wsc[NW][kGemvMfmaScaleBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int u = (int)blockIdx.x;
@@ -338,7 +327,6 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
   const int nsb = K >> 8;
   const int c16 = lane & 15, kg = lane >> 4;   // operand row / token column, k-group
   const int j_op = (rb & 1) * 16 + c16;        // A operand row within the 32-row tile
-  const int j_out = (rb & 1) * 16 + 4 * kg;    // first of this lane's 4 output rows in the tile
   // term2 piece pairs of this lane's k-group: (ia1, jb1) in the first instruction, (ia2, jb2)
   // in the second (k-groups 2 and 3 of the second are zero)
   const int ia1 = kg == 2 ? 1 : 0, jb1 = kg == 1 ? 1 : (kg == 3 ? 2 : 0);
@@ -354,10 +342,10 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
 
   struct Stage {
     uint2 nb[4];     // nibble bytes of A row j_op, k-group kg, of block pairs 0..3
-    float4 dsv[8];   // rows j_out .. j_out + 3 of each block
+    v4i hdr;         // super-block header of row j_op
     uint2 tb[8];     // token c16, k-group kg, of each block (zero past M)
     float2 dap[8];   // (da, nda) of token c16 and each block
-    v4i pa[2], pb[2];  // term2 operands: dmv piece of row j_op, da*sa piece of token c16
+    v4i pb[2];       // term2 operands: the da*sa pieces of token c16
   };
   auto load = [&](int s, Stage& st) {
     const uint32_t rec = (uint32_t)s * kRepTileBytes;
@@ -365,10 +353,7 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
     for (int g = 0; g < 4; ++g)
       st.nb[g] = __builtin_bit_cast(
           uint2, buf_load_f32x2(rw, rec + g * 1024 + (kg >> 1) * 512 + j_op * 16 + (kg & 1) * 8));
-#pragma unroll
-    for (int b = 0; b < 8; ++b)
-      st.dsv[b] =
-          __builtin_bit_cast(float4, buf_load16(rw, rec + kRepNibBytes + b * 128 + j_out * 4));
+    st.hdr = buf_load16(rw, rec + kRepNibBytes + j_op * 16);
 #pragma unroll
     for (int b = 0; b < 8; ++b)
       st.tb[b] = __builtin_bit_cast(
@@ -377,13 +362,11 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
 #pragma unroll
     for (int b = 0; b < 8; ++b)
       st.dap[b] = buf_load_f32x2(rda, (((uint32_t)s * 8 + b) * (uint32_t)M + c16) * 8u);
-    const uint32_t wp = rec + kRepNibBytes + kRepDsvBytes + j_op * 16;
-    st.pa[0] = buf_load16(rw, wp + ia1 * 512);
-    st.pa[1] = buf_load16(rw, wp + ia2 * 512);
     st.pb[0] = buf_load16(rtp, (((uint32_t)s * 3 + jb1) * (uint32_t)M + c16) * 16u);
     st.pb[1] = buf_load16(rtp, (((uint32_t)s * 3 + jb2) * (uint32_t)M + c16) * 16u);
-    if (!t2) st.pa[1] = v4i{0, 0, 0, 0};
   };
+  float* sdsv = reinterpret_cast<float*>(wsc[wave]);
+  uint32_t* spc = reinterpret_cast<uint32_t*>(wsc[wave] + kWsDsv);
 
   typedef float v4f __attribute__((ext_vector_type(4)));
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -398,6 +381,29 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
     } else {
       load(s, cur);
     }
+    // weight scales of the super-block: lane (c16, kg) expands sub-blocks 2kg, 2kg + 1 of
+    // row c16 of the half tile into the region, after the previous super-block's reads
+    {
+      float dsv4[4], dmv4[4];
+      q4k_scales(cur.hdr, kg >= 2, dsv4, dmv4);
+      const bool odd = (kg & 1) != 0;
+      const float dsv_a = odd ? dsv4[2] : dsv4[0], dsv_b = odd ? dsv4[3] : dsv4[1];
+      const float dmv_a = odd ? dmv4[2] : dmv4[0], dmv_b = odd ? dmv4[3] : dmv4[1];
+      uint32_t pa_[3], pb_[3];
+      bf16_trunc3(dmv_a, pa_[0], pa_[1], pa_[2]);
+      bf16_trunc3(dmv_b, pb_[0], pb_[1], pb_[2]);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      sdsv[(2 * kg) * 16 + c16] = dsv_a;
+      sdsv[(2 * kg + 1) * 16 + c16] = dsv_b;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) spc[(i * 16 + c16) * 4 + kg] = pack_hi16(pa_[i], pb_[i]);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+    const v4i pa0 = *reinterpret_cast<const v4i*>(spc + (ia1 * 16 + c16) * 4);
+    const v4i pa1 = t2 ? *reinterpret_cast<const v4i*>(spc + (ia2 * 16 + c16) * 4)
+                       : v4i{0, 0, 0, 0};
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       const uint2 w = cur.nb[b >> 1];
@@ -406,17 +412,18 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
       const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, a),
                                                           __builtin_bit_cast(long, cur.tb[b]),
                                                           bias, 0, 0, 0);
-      const float dsvb[4] = {cur.dsv[b].x, cur.dsv[b].y, cur.dsv[b].z, cur.dsv[b].w};
+      const float4 dq = *reinterpret_cast<const float4*>(sdsv + b * 16 + 4 * kg);
+      const float dsvb[4] = {dq.x, dq.y, dq.z, dq.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float y = __builtin_fmaf(__int_as_float(D[r]), cur.dap[b].x, cur.dap[b].y);
         acc[r] = __builtin_fmaf(y, dsvb[r], acc[r]);
       }
     }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, cur.pa[0]),
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, pa0),
                                                   __builtin_bit_cast(v8bf, cur.pb[0]), acc, 0,
                                                   0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, cur.pa[1]),
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, pa1),
                                                   __builtin_bit_cast(v8bf, cur.pb[1]), acc, 0,
                                                   0, 0);
     if constexpr (kPrefetch) cur = nxt;
@@ -467,7 +474,8 @@ hipError_t launch_fused_mt(const float* x, const void* w_rep, float* C, int64_t 
 int64_t gemv_group(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 8 : 16))); }
 
 int64_t gemv_lds_bytes(int64_t M) {
-  if (M > kGemvDotMaxM) return kGemvMfmaWaves * 16 * 16 * 4;  // the matrix-unit form: partial sums only
+  // the matrix-unit form: the partial sums, and per wavefront its expanded weight scales
+  if (M > kGemvDotMaxM) return kGemvMfmaWaves * (16 * 16 * 4 + kGemvMfmaScaleBytes);
   const int64_t mt = gemv_group(M);
   return (int64_t)kGemvWaves * kGemvSlices * (mt * 160 + 16);
 }

@@ -14,11 +14,15 @@ constexpr float kBiasF = 12582912.0f;
 
 constexpr int kRepTileRows = 32;
 // Repacked weight record per (32-row tile, super-block): nibbles [4][2][32][16] (4096 B),
-// dsv f32 [8][32] (1024 B), then dmv as three bf16 pieces [3][32][8] (1536 B).
+// then each row's 16-byte q4_K header [32][16] (f16 d, f16 dmin, the 12 packed 6-bit scale
+// and min bytes; 512 B): 4608 B per 8192 weights, 4.5 bits per weight.
 constexpr int kRepNibBytes = 4096;
-constexpr int kRepDsvBytes = 1024;
-constexpr int kRepPieceBytes = 1536;
-constexpr int kRepTileBytes = kRepNibBytes + kRepDsvBytes + kRepPieceBytes;  // 6656
+constexpr int kRepHdrBytes = 512;
+constexpr int kRepTileBytes = kRepNibBytes + kRepHdrBytes;  // 4608
+// The weight scales as the kernels stage them in LDS, expanded from the headers: dsv = d*sc
+// f32 [8][32] (1024 B), then dmv = -(dmin*m) as three bf16 pieces [3][32][8] (1536 B).
+constexpr int kWDsvBytes = 1024;
+constexpr int kWPieceBytes = 1536;
 
 constexpr int kRowStride = 272;  // LDS bytes per staged token row (256 + 16 padding)
 
@@ -43,11 +47,11 @@ struct TileShape {
   constexpr int threads() const { return 64 * nw; }
   // LDS: two stages, each: the int8 token tile [BM][272], the (da, nda) pairs f32 [8][BM][2],
   // and per wavefront its weight scales. q4_K also stages the token pieces bf16 [3][BM][8],
-  // and its weight scales are dsv and the dmv pieces (2560 bytes); q6_K's are dsv [16][32]
-  // (2048 bytes).
+  // and its weight scales are dsv and the dmv pieces (2560 bytes) with the 32 row headers
+  // they are expanded from (512 bytes); q6_K's are dsv [16][32] (2048 bytes).
   constexpr int64_t stage_bytes(int fmt = kFmtQ4K) const {
     return fmt == kFmtQ4K
-               ? (int64_t)block_m() * (kRowStride + 64 + 48) + (int64_t)nw * (kRepDsvBytes + kRepPieceBytes)
+               ? (int64_t)block_m() * (kRowStride + 64 + 48) + (int64_t)nw * (kWDsvBytes + kWPieceBytes + kRepHdrBytes)
                : (int64_t)block_m() * (kRowStride + 64) + (int64_t)nw * kRep6DsvBytes;
   }
   constexpr int64_t lds_bytes(int fmt = kFmtQ4K) const { return 2 * stage_bytes(fmt); }

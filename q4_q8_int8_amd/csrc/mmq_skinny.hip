@@ -13,9 +13,10 @@
 // Per super-block a wavefront loads everything it needs with single instructions: the
 // token operand of each block straight into registers (16 bytes per lane; token rows past
 // M read past the end of the buffer, which returns zero), (da, nb) of each block, the three bf16
-// pieces of da*sa, its four 16-byte nibble words, and, into its own 2560-byte LDS region,
-// the weight scales dsv and the dmv pieces (which every lane half needs in a different
-// pattern). Per block: D = MFMA_i8(w, q, bias), y = fma(D, da, nb) with nb = -12582912*da,
+// pieces of da*sa, its four 16-byte nibble words and the 16-byte header of row l % 32. From
+// the header lane l expands the weight scales dsv and the dmv pieces of its row's sub-blocks
+// 4 (l / 32) .. + 3 into the wavefront's own 2560-byte LDS region (every lane half needs
+// them in a different pattern). Per block: D = MFMA_i8(w, q, bias), y = fma(D, da, nb) with nb = -12582912*da,
 // acc = fma(y, dsv, acc) exactly as in the main kernel; one third of the super-block's
 // term2 is added by a bf16 MFMA after blocks 1, 3 and 5.
 //
@@ -43,7 +44,7 @@ constexpr int kFQRow = 272;                        // int8 row: 256 values + 16 
 constexpr int kFQBytes = 32 * kFQRow;              // [32 rows][272]
 constexpr int kFDaBytes = 8 * 32 * 8;              // (da, nb) [8 blocks][32 rows]
 constexpr int kFPcBytes = 3 * 32 * 16;             // pieces [3][32 rows][8 bf16]
-constexpr int kFRegion = kRepDsvBytes + kRepPieceBytes + kFQBytes + kFDaBytes + kFPcBytes;
+constexpr int kFRegion = kWDsvBytes + kWPieceBytes + kFQBytes + kFDaBytes + kFPcBytes;
 
 template <int KW, bool FUSED>
 __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
     const uint16_t* __restrict__ tpieces, const float4* __restrict__ x,
     const uint8_t* __restrict__ wrep, float* __restrict__ C, int M, int N, int K, int gm) {
   extern __shared__ __align__(16) uint8_t smem[];
-  constexpr int W_BYTES = kRepDsvBytes + kRepPieceBytes;
+  constexpr int W_BYTES = kWDsvBytes + kWPieceBytes;
   constexpr int REGION = FUSED ? kFRegion : W_BYTES;
 
   const int tid = threadIdx.x;
@@ -71,10 +72,8 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
   const __amdgpu_buffer_rsrc_t rda = make_rsrc(da_plane, (uint32_t)M * (uint32_t)kb * 8u);
   const __amdgpu_buffer_rsrc_t rtp = make_rsrc(tpieces, (uint32_t)M * (uint32_t)nsb * 48u);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wtile, (uint32_t)nsb * kRepTileBytes);
-  const v4i rwd = make_rsrc_sgpr(wtile, (uint32_t)nsb * kRepTileBytes);
 
   uint8_t* sW = smem + wave * REGION;
-  const uint32_t sWa = lds_addr(smem) + (uint32_t)(wave * REGION);  // its LDS address
   const float* sWw = reinterpret_cast<const float*>(sW);
   uint8_t* sQ = sW + W_BYTES;                                      // fused: token tile
   float2* sDa = reinterpret_cast<float2*>(sQ + kFQBytes);
@@ -97,17 +96,12 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
   for (int s = s0; s < s1; ++s) {
-    // this wavefront's earlier LDS reads of its region are done before the loads (and, fused,
-    // the quantized tile of this super-block) overwrite it
+    // this wavefront's earlier LDS reads of its region are done before the weight scales
+    // (and, fused, the quantized tile of this super-block) overwrite it
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), the other counters unconstrained
-    if constexpr (FUSED) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-    }
-    const uint32_t wo = (uint32_t)s * kRepTileBytes + kRepNibBytes + lane * 16;
-    dma16(rwd, sWa, wo);
-    dma16(rwd, sWa + 1024, wo + 1024);
-    if (lane < 32) dma16(rwd, sWa + 2048, wo + 2048);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const v4i hdr = buf_load16(rw, (uint32_t)s * kRepTileBytes + kRepNibBytes + l32 * 16);
     v4i raw[4], tok[8], tp[3];
     float2 da[8];  // (da, nb) per block
 #pragma unroll
@@ -175,10 +169,12 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
       for (int j = 0; j < 3; ++j)
         tp[j] = buf_load16(rtp, (((uint32_t)s * 3 + j) * (uint32_t)M + m0 + l32) * 16u);
     }
-    // everything, the LDS region included, has landed; the fence keeps the compiler from
-    // moving the region's reads above the wait
+    q4k_stage_scales(hdr, l32, h != 0, sW);
+    // everything has landed and the region is written; the fence and the barrier keep the
+    // compiler from moving the region's reads above the writes of the other lanes
     __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 
     auto wop_of = [&](int b) -> v4i {
       const v4i rr = raw[b >> 1];
@@ -205,7 +201,7 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
         const int u = b >> 1;
         const int ia = u == 0 ? 0 : (u == 1 ? 1 - h : 1 + h);
         const int jb = u == 0 ? h : (u == 1 ? 2 * h : 1 - h);
-        const v8bf wa = *reinterpret_cast<const v8bf*>(sW + kRepDsvBytes + (ia * 32 + l32) * 16);
+        const v8bf wa = *reinterpret_cast<const v8bf*>(sW + kWDsvBytes + (ia * 32 + l32) * 16);
         const v4i t0 = tp[0], t1 = tp[1], t2 = tp[2];
         const v4i tsel = jb == 0 ? t0 : (jb == 1 ? t1 : t2);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, __builtin_bit_cast(v8bf, tsel), acc,
@@ -236,7 +232,7 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
 }  // namespace
 
 int64_t skinny_lds_bytes() {
-  const int64_t regions = (int64_t)kSkinnyWaves * (kRepDsvBytes + kRepPieceBytes);
+  const int64_t regions = (int64_t)kSkinnyWaves * (kWDsvBytes + kWPieceBytes);
   const int64_t reduce = (int64_t)kSkinnyWaves * 16 * 64 * 4;
   return regions > reduce ? regions : reduce;
 }

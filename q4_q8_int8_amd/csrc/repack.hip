@@ -1,10 +1,12 @@
 // Offline weight repacks: GGUF-layout q4_K (and q6_K, below) super-blocks -> one record per
-// (32-row weight tile, super-block) laid out for the GEMM's operand loads (layouts in
+// (32-row weight tile, super-block) laid out for the kernels' operand loads (layouts in
 // include/mmq.h).
-// The q4_K fields are those of the r15 page ("f32-accumulate mma probe + rank-1 term2
-// rescale", section 2.1); the scale expansion dsv = d*sc, dmv = -(dmin*m) is the B-staging
-// step quoted there, moved to load time. dmv is stored as three bf16 pieces that sum to it
-// exactly, the operand form of the GEMM's bf16 matrix instruction for term2.
+// The q4_K record keeps the fields of the r15 page ("f32-accumulate mma probe + rank-1 term2
+// rescale", section 2.1) as the GGUF block holds them: the nibbles, regrouped so that one
+// 16-byte load per lane feeds a matrix instruction, and each row's 16-byte header (d, dmin
+// and the packed 6-bit sc, m), unchanged. The kernels expand dsv = d*sc and dmv = -(dmin*m)
+// from the header when they stage a super-block, the B-staging step quoted there, so the
+// record is 4.5 bits per weight, the size of the GGUF blocks themselves.
 #include "mmq_internal.h"
 
 namespace mmq {
@@ -12,17 +14,6 @@ namespace {
 
 __device__ __forceinline__ float f16_to_f32(uint32_t lo, uint32_t hi) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(lo | (hi << 8)));
-}
-
-// 6-bit scale and min of sub-block b from the 12 packed scale bytes (GGUF q4_K packing).
-__device__ __forceinline__ void scale_min(const uint8_t* s, int b, int& sc, int& m) {
-  if (b < 4) {
-    sc = s[b] & 63;
-    m = s[b + 4] & 63;
-  } else {
-    sc = (s[b + 4] & 15) | ((s[b - 4] >> 6) << 4);
-    m = (s[b + 4] >> 4) | ((s[b] >> 6) << 4);
-  }
 }
 
 // One workgroup per (tile, super-block); 256 threads.
@@ -43,25 +34,11 @@ __global__ __launch_bounds__(256) void repack_q4_K_kernel(const uint8_t* __restr
                                           16 * h);
     reinterpret_cast<uint4*>(rec)[tid] = v;
   }
-  {  // scales: thread = (b, j)
-    const int b = tid >> 5, j = tid & 31;
-    const int row = tile * kRepTileRows + j;
-    float dsv = 0.0f, dmv = 0.0f;
-    if (row < N) {
-      const uint8_t* blk = w + ((size_t)row * nsb + sb) * 144;
-      const float d = f16_to_f32(blk[0], blk[1]);
-      const float dmin = f16_to_f32(blk[2], blk[3]);
-      int sc, m;
-      scale_min(blk + 4, b, sc, m);
-      dsv = d * (float)sc;
-      dmv = -(dmin * (float)m);
-    }
-    reinterpret_cast<float*>(rec + kRepNibBytes)[b * 32 + j] = dsv;
-    uint16_t p[3];
-    bf16_split3(dmv, p[0], p[1], p[2]);
-    uint16_t* pc = reinterpret_cast<uint16_t*>(rec + kRepNibBytes + kRepDsvBytes);
-#pragma unroll
-    for (int i = 0; i < 3; ++i) pc[(i * 32 + j) * 8 + b] = p[i];
+  if (tid < kRepTileRows) {  // headers: thread = row j, the block's first 16 bytes
+    const int row = tile * kRepTileRows + tid;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (row < N) v = *reinterpret_cast<const uint4*>(w + ((size_t)row * nsb + sb) * 144);
+    reinterpret_cast<uint4*>(rec + kRepNibBytes)[tid] = v;
   }
 }
 

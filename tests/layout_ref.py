@@ -6,17 +6,18 @@ fields).
 Each image is built from the oracle's fields:
   - q8_image: the whole q8 buffer quantize_q8_1 writes: q and the packed (da, sa) words,
     then the GEMM's planes derived from da and sa;
-  - repack_reference: the repacked weight records repack_q4_K writes;
+  - repack_reference: the repacked weight records repack_q4_K writes (the GGUF blocks'
+    bytes regrouped);
   - read_repacked: a reader of such records, used to check that the layout round-trips;
   - repack_q6k_reference, read_repacked_q6k: the same for repack_q6_K;
-  - bf16_pieces: the three-piece bfloat16 split both planes use.
+  - bf16_pieces: the three-piece bfloat16 split of the q8 buffer's piece plane.
 """
 import numpy as np
 
 import oracle
 
 TILE_ROWS = 32
-TILE_BYTES = 6656
+TILE_BYTES = 4608
 BIAS = 1.5 * 2.0 ** 23  # the GEMM's integer results come offset by this value
 
 
@@ -96,8 +97,9 @@ def q8_regions(img: np.ndarray, M: int, K: int) -> dict:
             "pieces": img[Q:].view("<u2").reshape(-1, 3, M, 8)}
 
 
-def repack_reference(w_blocks: np.ndarray, fields: dict) -> np.ndarray:
-    """Expected repack_q4_K output for GGUF blocks u8 [N, K/256, 144] encoding `fields`."""
+def repack_reference(w_blocks: np.ndarray) -> np.ndarray:
+    """Expected repack_q4_K output for GGUF blocks u8 [N, K/256, 144]: per (32-row tile,
+    super-block) the nibble bytes regrouped [g][h][j][16], then each row's 16-byte header."""
     N, nsb, _ = w_blocks.shape
     nt = -(-N // TILE_ROWS)
     pad = nt * TILE_ROWS - N
@@ -105,24 +107,14 @@ def repack_reference(w_blocks: np.ndarray, fields: dict) -> np.ndarray:
     out = np.zeros((nt, nsb, TILE_BYTES), np.uint8)
     nib = wp[..., 16:144].reshape(nt, TILE_ROWS, nsb, 4, 2, 16)        # [t, j, s, g, h, 16]
     out[..., :4096] = nib.transpose(0, 2, 3, 4, 1, 5).reshape(nt, nsb, 4096)
-    d = fields["d_bits"].view(np.float16).astype(np.float32)           # [N, nsb]
-    dmin = fields["dmin_bits"].view(np.float16).astype(np.float32)
-    sc = fields["sc"].astype(np.float32).reshape(N, nsb, 8)
-    m = fields["m"].astype(np.float32).reshape(N, nsb, 8)
-    dsv = np.zeros((nt * TILE_ROWS, nsb, 8), np.float32)
-    dmv = np.zeros((nt * TILE_ROWS, nsb, 8), np.float32)
-    dsv[:N] = d[..., None] * sc
-    dmv[:N] = -(dmin[..., None] * m)
-    a = dsv.reshape(nt, TILE_ROWS, nsb, 8).transpose(0, 2, 3, 1)        # [t, s, b, j]
-    out[..., 4096:5120] = np.ascontiguousarray(a).view(np.uint8).reshape(nt, nsb, 1024)
-    pc = bf16_pieces(dmv).reshape(nt, TILE_ROWS, nsb, 8, 3)             # [t, j, s, b, i]
-    pc = np.ascontiguousarray(pc.transpose(0, 2, 4, 1, 3)).astype("<u2")  # [t, s, i, j, b]
-    out[..., 5120:6656] = pc.view(np.uint8).reshape(nt, nsb, 1536)
+    hdr = wp[..., :16].reshape(nt, TILE_ROWS, nsb, 16)                  # [t, j, s, 16]
+    out[..., 4096:] = hdr.transpose(0, 2, 1, 3).reshape(nt, nsb, 512)
     return out.reshape(-1)
 
 
 def read_repacked(rep: np.ndarray, N: int, K: int) -> dict:
-    """Decode repacked records back into v [N, K], dsv and dmv [N, K/32] (float32)."""
+    """Decode repacked records back into the nibble values v [N, K] and the GGUF blocks'
+    16-byte headers [N, K/256, 16]."""
     nsb = K // 256
     nt = -(-N // TILE_ROWS)
     r = rep.reshape(nt, nsb, TILE_BYTES)
@@ -131,12 +123,8 @@ def read_repacked(rep: np.ndarray, N: int, K: int) -> dict:
     hi = nib >> 4
     v = np.stack([lo, hi], axis=3)                                     # [t, s, g, lohi, h, j, 16]
     v = v.transpose(0, 5, 1, 2, 3, 4, 6).reshape(nt * TILE_ROWS, K)    # [t, j, s, g, lohi, h, e]
-    dsv = r[..., 4096:5120].copy().view(np.float32).reshape(nt, nsb, 8, TILE_ROWS)
-    dsv = dsv.transpose(0, 3, 1, 2).reshape(nt * TILE_ROWS, K // 32)
-    pc = r[..., 5120:6656].copy().view("<u2").reshape(nt, nsb, 3, TILE_ROWS, 8)
-    vals = bf16_value(pc)
-    dmv = vals.sum(axis=2).transpose(0, 2, 1, 3).reshape(nt * TILE_ROWS, K // 32)
-    return {"v": v[:N], "dsv": dsv[:N], "dmv": dmv[:N]}
+    hdr = r[..., 4096:].reshape(nt, nsb, TILE_ROWS, 16).transpose(0, 2, 1, 3)
+    return {"v": v[:N], "hdr": hdr.reshape(nt * TILE_ROWS, nsb, 16)[:N]}
 
 
 TILE6_BYTES = 10240

@@ -33,9 +33,9 @@ def test_sizes():
     assert mmq.mmq_q8_1_bytes(3, 96) == 512 + 256 + 48 * 3
     assert mmq.mmq_q8_1_bytes(2, 288) == 768 + 256 + 48 * 2 * 2
     assert mmq.mmq_q4K_bytes(4096, 4096) == 4096 * 16 * 144
-    assert mmq.mmq_q4K_repacked_bytes(4096, 4096) == 128 * 16 * 6656
-    assert mmq.mmq_q4K_repacked_bytes(33, 256) == 2 * 6656
-    assert mmq.mmq_q4K_repacked_bytes(11008, 4096) == 344 * 16 * 6656
+    assert mmq.mmq_q4K_repacked_bytes(4096, 4096) == 128 * 16 * 4608 == 4096 * 4096 * 9 // 16
+    assert mmq.mmq_q4K_repacked_bytes(33, 256) == 2 * 4608
+    assert mmq.mmq_q4K_repacked_bytes(11008, 4096) == 344 * 16 * 4608
 
 
 @pytest.mark.parametrize("fn,args,status", [
@@ -57,10 +57,11 @@ def test_size_null_out():
 
 
 # two stages of: token tile [BM][272], (da, nda) [8][BM][2] f32, token pieces [3][BM][8]
-# bf16, and per wavefront dsv [8][32] f32 + dmv pieces [3][32][8] bf16
+# bf16, and per wavefront dsv [8][32] f32 + dmv pieces [3][32][8] bf16 + the 32 row headers
+# [32][16] they are expanded from
 LARGE, SMALL = mmq.MMQ_TILE_LARGE, mmq.MMQ_TILE_SMALL
-LARGE_LDS = 2 * (128 * 272 + 128 * 64 + 128 * 48 + 8 * 2560)
-SMALL_LDS = 2 * (32 * 272 + 32 * 64 + 32 * 48 + 2 * 2560)
+LARGE_LDS = 2 * (128 * 272 + 128 * 64 + 128 * 48 + 8 * 3072)
+SMALL_LDS = 2 * (32 * 272 + 32 * 64 + 32 * 48 + 2 * 3072)
 
 
 def test_plan_large_when_it_fits():
@@ -164,8 +165,9 @@ def test_plan_gemv_tile(M, group, grid):
     assert p["block_m"] == group and p["block_n"] == 16
     assert p["threads"] == (512 if group <= 8 else 1024)
     # up to 8 tokens, per wavefront and K-slice: its half's 128 token bytes and 4 (da, sa)
-    # pairs per token, 16 padding; from 9 tokens (the matrix-unit form) the partial sums only
-    lds = 8 * 4 * (160 * group + 16) if group <= 8 else 16 * 16 * 16 * 4
+    # pairs per token, 16 padding; from 9 tokens (the matrix-unit form) per wavefront its
+    # partial sums and its expanded weight scales (dsv [8][16] f32, dmv pieces [3][16][8])
+    lds = 8 * 4 * (160 * group + 16) if group <= 8 else 16 * (16 * 16 * 4 + 512 + 768)
     assert p["lds_bytes"] == lds and p["grid"] == grid
     # ragged N: 4097 rows make 257 blocks of 16
     assert mmq.mmq_plan(M, 4097, 256, 160 * 1024, force_tile=GEMV)["grid"] == 257 * (grid // 256)

@@ -1,7 +1,7 @@
 """The test-side layout references agree with the layouts include/mmq.h specifies (CPU only).
 
 These pin the storage forms the GPU parity tests compare bytes against: the repacked weight
-records, the q8 buffer's derived planes and the three-piece bfloat16 split. None of this is
+records, the q8 buffer's derived planes and its three-piece bfloat16 split. None of this is
 the method's arithmetic, which the oracle holds and tests/test_oracle_pins.py pins.
 """
 from fractions import Fraction
@@ -18,29 +18,38 @@ from tests.layout_ref import (bf16_pieces, bf16_value, q8_image, q8_regions, rea
 @pytest.mark.parametrize("N,K", [(32, 256), (33, 512), (70, 768), (5, 256)])
 def test_repack_reference_roundtrip(N, K):
     f = synth.q4k_random_fields(N, K, N * 7 + K)
-    rep = repack_reference(synth.q4k_pack(f), f)
-    assert rep.size == -(-N // 32) * (K // 256) * 6656
+    w = synth.q4k_pack(f)
+    rep = repack_reference(w)
+    assert rep.size == -(-N // 32) * (K // 256) * 4608       # 4.5 bits per weight
+    assert rep.size * 8 == 4.5 * (-(-N // 32) * 32) * K
     got = read_repacked(rep, N, K)
     assert np.array_equal(got["v"], f["v"])
-    d = np.repeat(f["d_bits"].view(np.float16).astype(np.float64), 8, axis=1)
-    dmin = np.repeat(f["dmin_bits"].view(np.float16).astype(np.float64), 8, axis=1)
-    assert np.array_equal(got["dsv"].astype(np.float64), d * f["sc"])
-    assert np.array_equal(got["dmv"].astype(np.float64), -(dmin * f["m"]))
-    # padding rows of the last tile are zero
+    # the headers are the blocks' own 16 bytes, so they decode to the generator's scales
+    blocks = np.concatenate([got["hdr"], np.zeros((N, K // 256, 128), np.uint8)], axis=2)
+    dec = oracle.decode_q4_K(blocks)
+    assert np.array_equal(dec.d, f["d_bits"].view(np.float16).astype(np.float64))
+    assert np.array_equal(dec.dmin, f["dmin_bits"].view(np.float16).astype(np.float64))
+    assert np.array_equal(dec.sc, f["sc"].astype(np.int64))
+    assert np.array_equal(dec.m, f["m"].astype(np.int64))
+    # padding rows of the last tile are zero, nibbles and headers
     nt = -(-N // 32)
-    last = rep.reshape(nt, K // 256, 6656)[-1]
+    last = rep.reshape(nt, K // 256, 4608)[-1]
     rows_used = N - (nt - 1) * 32
     nib = last[:, :4096].reshape(K // 256, 4, 2, 32, 16)
     assert np.all(nib[:, :, :, rows_used:, :] == 0)
+    assert np.all(last[:, 4096:].reshape(K // 256, 32, 16)[:, rows_used:, :] == 0)
 
 
-def test_repack_reference_nibble_order():
-    """Record byte (g, h, j, e) is q4_K nibble byte 32g + 16h + e of row j."""
-    f = synth.q4k_random_fields(32, 256, 1)
+def test_repack_reference_nibble_and_header_order():
+    """Record byte (g, h, j, e) is q4_K nibble byte 32g + 16h + e of row j; record byte
+    4096 + 16j + e is byte e of row j's block."""
+    f = synth.q4k_random_fields(32, 512, 1)
     w = synth.q4k_pack(f)
-    rep = repack_reference(w, f)
+    rep = repack_reference(w)
     for g, h, j, e in [(0, 0, 0, 0), (3, 1, 31, 15), (2, 0, 17, 9), (1, 1, 5, 3)]:
         assert rep[((g * 2 + h) * 32 + j) * 16 + e] == w[j, 0, 16 + 32 * g + 16 * h + e]
+    for s, j, e in [(0, 0, 0), (1, 31, 15), (1, 7, 4), (0, 12, 2)]:
+        assert rep[s * 4608 + 4096 + 16 * j + e] == w[j, s, e]
 
 
 # (value, expected pieces) derived by hand from round-to-nearest-even at 8 significant bits
