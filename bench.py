@@ -175,8 +175,9 @@ def warm(step, warmup: int, warmup_ms: float) -> int:
 
 
 def measure(W: dict, R: int, steps: int, warmup: int, tile: int = 0,
-            warmup_ms: float = 0.0) -> dict:
-    """Time the whole path (quantize + GEMM) on one workload; see the module docstring."""
+            warmup_ms: float = 0.0, workspace_bytes: int = 0) -> dict:
+    """Time the whole path (quantize + GEMM) on one workload; see the module docstring.
+    workspace_bytes > 0 hands the GEMM a split-K workspace of that size."""
     import torch
 
     import q4_q8_int8_amd as mmq
@@ -191,6 +192,8 @@ def measure(W: dict, R: int, steps: int, warmup: int, tile: int = 0,
             for _ in range(R)]
     q8s = [torch.empty(mmq.mmq_q8_1_bytes(M, K), dtype=torch.uint8, device=dev) for _ in range(R)]
     Cs = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(R)]
+    ws = (torch.empty(workspace_bytes, dtype=torch.uint8, device=dev) if workspace_bytes > 0
+          else None)
 
     def events():
         return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -209,7 +212,7 @@ def measure(W: dict, R: int, steps: int, warmup: int, tile: int = 0,
         mmq.quantize_q8_1(xs[r], M, K, q8s[r])
 
     def gemm(r):
-        mmq.mmq_q4K_q8_1_ex(M, N, K, q8s[r], reps[r], Cs[r], force_tile=tile)
+        mmq.mmq_q4K_q8_1_ex(M, N, K, q8s[r], reps[r], Cs[r], force_tile=tile, workspace=ws)
 
     def step(i):
         quant(i % R)
@@ -519,6 +522,50 @@ def config_line(name: str, W: dict, t: dict) -> dict:
             "rotate": t["rotate"]}
 
 
+def q6k_line(name: str, W: dict, R: int, steps: int, warmup: int) -> dict:
+    """The q6_K x q8_1 product on a workload's shape (q6_K weights fitted to the same kind
+    of synthetic matrix): `steps` back-to-back launches of its GEMM (the guard's tile) between
+    one pair of HIP events, the inputs rotating over R sets."""
+    import torch
+
+    import synth
+    import q4_q8_int8_amd as mmq
+
+    dev = torch.device("cuda:0")
+    M, N, K = W["M"], W["N"], W["K"]
+    stream = torch.cuda.current_stream()
+    w6, _ = synth.q6k_weights("fit", N, K, 2006)
+    w_dev = torch.from_numpy(w6).to(dev)
+    x = torch.from_numpy(W["x"]).to(dev)
+    reps = [torch.empty(mmq.mmq_q6K_repacked_bytes(N, K), dtype=torch.uint8, device=dev)
+            for _ in range(R)]
+    q8s = [torch.empty(mmq.mmq_q8_1_bytes(M, K), dtype=torch.uint8, device=dev) for _ in range(R)]
+    Cs = [torch.empty((M, N), dtype=torch.float32, device=dev) for _ in range(R)]
+    for r in range(R):
+        mmq.repack_q6_K(w_dev, N, K, reps[r])
+        mmq.quantize_q8_1(x, M, K, q8s[r])
+
+    def gemm(i):
+        mmq.mmq_q6K_q8_1(M, N, K, q8s[i % R], reps[i % R], Cs[i % R])
+
+    warm(gemm, warmup, 100.0)
+    plan = mmq.mmq_last_kernel()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        gemm(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    macs = M * N * K
+    return {"config": name, "M": M, "N": N, "K": K,
+            "q6_K": {"tile": plan["tile"], "grid": plan["grid"], "gemm_us": round(us, 2),
+                     "gemm_tmacs": round(macs / (us * 1e-6) / 1e12, 2),
+                     "int8_peak_frac": round(2 * macs / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4),
+                     "repacked_bytes": mmq.mmq_q6K_repacked_bytes(N, K)}}
+
+
 def sweep(args) -> int:
     """Every configuration (and each tile the guard allows), then the 7-projection prefill:
     one JSON line each. Not the driver's benchmark line; see the profiles."""
@@ -526,6 +573,8 @@ def sweep(args) -> int:
     import q4_q8_int8_amd as mmq
     names = ["tiny", "qproj", "gateup", "down"] + [f"sweep_m{m}" for m in synth.SWEEP_M] \
         + list(synth.SHARE8)
+    if args.config:
+        names = [n for n in args.config.split(",") if n]
     times = {}
     for name in names:
         W = synth.workload(name)
@@ -540,6 +589,17 @@ def sweep(args) -> int:
             t["rotate"] = R
             times[(name, tile)] = t
             print(json.dumps(config_line(name, W, t)), flush=True)
+        # the guard's choice when it may split K over workgroups (a caller's workspace)
+        wsb = mmq.mmq_workspace_bytes(W["M"], W["N"], W["K"])
+        if wsb > 0:
+            t = measure(W, R, args.steps, args.warmup, mmq.MMQ_TILE_AUTO, workspace_bytes=wsb)
+            t["rotate"] = R
+            times[(name, "split")] = t
+            line = config_line(name, W, t)
+            line.update({"workspace_bytes": wsb, "splits": t["plan"].get("splits")})
+            print(json.dumps(line), flush=True)
+        if name in ("tiny", "qproj"):
+            print(json.dumps(q6k_line(name, W, R, args.steps, args.warmup)), flush=True)
         if W["M"] <= 128:
             fu = measure_fused(W, R, args.steps, args.warmup)
             macs = W["M"] * W["N"] * W["K"]
@@ -555,11 +615,13 @@ def sweep(args) -> int:
                               "comparator_f16": f16_summary(W["M"], W["N"], W["K"], f)}),
                   flush=True)
         del W
+    if args.config:
+        return 0
     # 7-projection prefill of a 32-layer 7B at 2048 tokens, GEMM-only: per layer q, k, v, o
     # are q-proj shaped, gate and up gate/up shaped, down down shaped; three K=4096
     # activations (attention input, attention output, FFN input) and one K=11008 one are
     # quantized. Each product takes its faster tile.
-    best = {n: min((t for (c, k), t in times.items() if c == n and k != "f16"),
+    best = {n: min((t for (c, k), t in times.items() if c == n and k not in ("f16", "split")),
                    key=lambda t: t["gemm_us"])
             for n in ("qproj", "gateup", "down")}
     layer_gemm = 4 * best["qproj"]["gemm_us"] + 2 * best["gateup"]["gemm_us"] \
@@ -622,6 +684,8 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="per-config table (one JSON line per config and tile) instead of the "
                          "benchmark line")
+    ap.add_argument("--config", default="", metavar="NAMES",
+                    help="with --sweep: only these configurations (comma-separated names)")
     args = ap.parse_args()
     if args.copy_probe:
         return copy_probe(args.copy_probe)

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
     const int8_t* __restrict__ qs, const float* __restrict__ da_plane,
     const uint16_t* __restrict__ tpieces,
     const uint8_t* __restrict__ wrep, void* __restrict__ out, int M, int N, int K, int gm,
-    int gmn, int splits, int tm0, int tn0, int i0, int i1, int j0, int j1) {
+    int gmn, int splits, int tm0, int tn0, int i0, int i1, int j0, int j1, int xbm, int xgm) {
   constexpr int BM = 32 * TT;
   constexpr int NS = 8 * TT;                      // (block, token tile) steps per super-block
   constexpr int A_BYTES = BM * kRowStride;        // token tile
@@ -103,8 +103,21 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   // sums to plane sp of out ([splits][M][N]); with one split the plane is C itself.
   const int sp = (int)(blockIdx.x / (unsigned)gmn);
   const int tile_id = (int)(blockIdx.x - (unsigned)sp * (unsigned)gmn);
-  const int tm = tm0 + tile_id % gm;
-  const int tn = tn0 + tile_id / gm;
+  // Workgroups go to the 8 XCDs in turn (workgroup i to XCD i % 8), each XCD with its own
+  // L2. With xbm > 0, XCD x works through its own block of xbm token tiles by
+  // gmn / 8 / xbm weight-tile groups (xgm such blocks along the tokens), which its L2 fetches
+  // once; in the plain order every XCD would fetch every weight tile.
+  int ti, tj;
+  if (xbm > 0) {
+    const int x = tile_id & 7, k = tile_id >> 3;
+    ti = (x % xgm) * xbm + k % xbm;
+    tj = (x / xgm) * ((gmn >> 3) / xbm) + k / xbm;
+  } else {
+    ti = tile_id % gm;
+    tj = tile_id / gm;
+  }
+  const int tm = tm0 + ti;
+  const int tn = tn0 + tj;
   const int m0 = tm * BM;
   const int ntiles = (N + 31) >> 5;
   const int wt_raw = tn * NW + wave;
@@ -450,6 +463,29 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   }
 }
 
+// The XCD blocks of a gm x gn tile grid: bm token tiles by gm*gn/8/bm weight-tile groups per
+// XCD, xgm = gm/bm blocks along the tokens and 8/xgm along the weights, of the shapes that
+// split the grid into 8 equal blocks the one whose tiles are the fewest bytes (a token tile
+// being tok_bytes, a weight-tile group w_bytes); {0, 0} (the plain order) when none does.
+struct XcdBlock {
+  int bm, xgm;
+};
+XcdBlock xcd_block(int64_t gm, int64_t gn, double tok_bytes, double w_bytes) {
+  XcdBlock best{0, 0};
+  if (gm * gn < 16 || (gm * gn) % 8) return best;
+  double cost = 0.0;
+  for (int64_t xgm = 1; xgm <= 8; xgm *= 2) {
+    const int64_t xgn = 8 / xgm;
+    if (gm % xgm || gn % xgn) continue;
+    const double c = (double)(gm / xgm) * tok_bytes + (double)(gn / xgn) * w_bytes;
+    if (best.bm == 0 || c < cost) {
+      cost = c;
+      best = {(int)(gm / xgm), (int)xgm};
+    }
+  }
+  return best;
+}
+
 template <int TT, int NW, bool STORE_S, int FMT>
 hipError_t launch_t(const void* q8, const void* w_rep, void* out, int64_t M, int64_t N,
                     int64_t K, int64_t gm, int64_t gn, int64_t splits, int64_t tm0, int64_t tn0,
@@ -461,6 +497,11 @@ hipError_t launch_t(const void* q8, const void* w_rep, void* out, int64_t M, int
   const float* da_plane = reinterpret_cast<const float*>(base + q8_planes_offset(M, K));
   const uint16_t* tpieces = reinterpret_cast<const uint16_t*>(base + q8_pieces_offset(M, K));
   auto kern = mmq_kernel<TT, NW, STORE_S, FMT>;
+  // bytes of one token tile (its rows of the q8 buffer) and of one weight-tile group (its
+  // records) per super-block column, for the XCD blocks
+  const double tok_tile = (double)ts.block_m() * (K / 256) * 400.0;
+  const double w_tile = (double)NW * (K / 256) * (FMT == kFmtQ6K ? kRep6TileBytes : kRepTileBytes);
+  const XcdBlock xb = xcd_block(gm, gn, tok_tile, w_tile);
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -470,7 +511,7 @@ hipError_t launch_t(const void* q8, const void* w_rep, void* out, int64_t M, int
                      (size_t)lds, s, qs, da_plane, tpieces,
                      static_cast<const uint8_t*>(w_rep), out, (int)M, (int)N, (int)K, (int)gm,
                      (int)(gm * gn), (int)splits, (int)tm0, (int)tn0, (int)i0, (int)i1, (int)j0,
-                     (int)j1);
+                     (int)j1, xb.bm, xb.xgm);
   return hipGetLastError();
 }
 
