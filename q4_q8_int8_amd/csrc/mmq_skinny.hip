@@ -45,6 +45,7 @@ constexpr int kFQBytes = 32 * kFQRow;              // [32 rows][272]
 constexpr int kFDaBytes = 8 * 32 * 8;              // (da, nb) [8 blocks][32 rows]
 constexpr int kFPcBytes = 3 * 32 * 16;             // pieces [3][32 rows][8 bf16]
 constexpr int kFRegion = kWDsvBytes + kWPieceBytes + kFQBytes + kFDaBytes + kFPcBytes;
+constexpr int kRedStride = 65;                     // floats per row of the partial sums
 
 template <int KW, bool FUSED>
 __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
@@ -210,11 +211,13 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
     }
   }
 
-  // partial sums: [wave][register][lane], then summed in wavefront order
+  // partial sums: [wave][register][lane], rows of kRedStride floats, then summed in
+  // wavefront order. The read below takes, per wavefront, 16 registers x 2 lanes of each of
+  // 2 tokens; with 64-float rows all of them fell on 4 of the LDS banks, with 65 they spread.
   __syncthreads();  // every wavefront is done with its LDS region
   float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[r];
+  for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * kRedStride + lane] = acc[r];
   __syncthreads();
   // element e = 32 * token + row of the 32 x 32 tile, so consecutive threads store
   // consecutive output features
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
     const int r = 4 * (jl >> 3) + (jl & 3), ln = 32 * ((jl >> 2) & 1) + il;
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < KW; ++w) v += red[(w * 16 + r) * 64 + ln];
+    for (int w = 0; w < KW; ++w) v += red[(w * 16 + r) * kRedStride + ln];
     const int i = m0 + il, j = tn * 32 + jl;
     if (i < M && j < N) C[(size_t)i * N + j] = v;
   }
@@ -233,13 +236,13 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
 
 int64_t skinny_lds_bytes() {
   const int64_t regions = (int64_t)kSkinnyWaves * (kWDsvBytes + kWPieceBytes);
-  const int64_t reduce = (int64_t)kSkinnyWaves * 16 * 64 * 4;
+  const int64_t reduce = (int64_t)kSkinnyWaves * 16 * kRedStride * 4;
   return regions > reduce ? regions : reduce;
 }
 
 int64_t fused_lds_bytes() {
   const int64_t regions = (int64_t)kSkinnyWaves * kFRegion;
-  const int64_t reduce = (int64_t)kSkinnyWaves * 16 * 64 * 4;
+  const int64_t reduce = (int64_t)kSkinnyWaves * 16 * kRedStride * 4;
   return regions > reduce ? regions : reduce;
 }
 

@@ -133,12 +133,12 @@ def test_plan_skinny_tile():
     p = mmq.mmq_plan(16, 4096, 4096, 160 * 1024, force_tile=mmq.MMQ_TILE_SKINNY)
     assert p["tile"] == mmq.MMQ_TILE_SKINNY and p["reason"] == mmq.MMQ_REASON_FORCED
     assert p["block_m"] == 32 and p["block_n"] == 32 and p["threads"] == 512
-    assert p["lds_bytes"] == 8 * 16 * 64 * 4 and p["grid"] == 1 * 128
+    assert p["lds_bytes"] == 8 * 16 * 65 * 4 and p["grid"] == 1 * 128
     p = mmq.mmq_plan(70, 100, 512, 160 * 1024, force_tile=mmq.MMQ_TILE_SKINNY)
     assert p["grid"] == 3 * 4
     with pytest.raises(mmq.MMQError) as e:
         mmq.mmq_plan(16, 4096, 4096, 160 * 1024, force_tile=mmq.MMQ_TILE_SKINNY,
-                     opt_lds_budget=8 * 16 * 64 * 4 - 1)
+                     opt_lds_budget=8 * 16 * 65 * 4 - 1)
     assert e.value.status == mmq.MMQ_E_LDS
 
 
