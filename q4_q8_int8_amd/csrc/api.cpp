@@ -310,13 +310,13 @@ int check_gemm_call(int64_t M, int64_t N, int64_t K, const void* q8, const void*
 // Launch what the guard planned; with split-K the GEMM writes the partial planes into ws and
 // a second kernel adds them into C, both on the stream.
 int launch_planned(const mmq_kernel_info& info, int64_t M, int64_t N, int64_t K, const void* q8,
-                   const void* w_rep, float* C, void* ws, hipStream_t stream,
-                   int fmt = mmq::kFmtQ4K) {
+                   const void* w_rep, float* C, void* ws, int64_t compute_units,
+                   hipStream_t stream, int fmt = mmq::kFmtQ4K) {
   hipError_t e;
   if (info.tile == MMQ_TILE_GEMV) {
     e = mmq::launch_mmq_gemv(q8, w_rep, C, M, N, K, stream);
   } else if (info.tile == MMQ_TILE_SKINNY) {
-    e = mmq::launch_mmq_skinny(q8, w_rep, C, M, N, K, stream);
+    e = mmq::launch_mmq_skinny(q8, w_rep, C, M, N, K, compute_units, stream);
   } else {
     const mmq::TileShape ts = tile_shape(info.tile);
     const int64_t gm = (M + ts.block_m() - 1) / ts.block_m();
@@ -345,7 +345,7 @@ int gemm_ex(int fmt, int64_t M, int64_t N, int64_t K, const void* q8, const void
   g_last = info;
   if (st) return st;
   return launch_planned(info, M, N, K, q8, w_rep, C, opt ? opt->workspace : nullptr,
-                        static_cast<hipStream_t>(stream), fmt);
+                        di->compute_units, static_cast<hipStream_t>(stream), fmt);
 }
 
 int blockdots(int fmt, int64_t M, int64_t N, int64_t K, const void* q8, const void* w_rep,

@@ -68,6 +68,23 @@ static __device__ __forceinline__ void dma16(v4i r, uint32_t lds, uint32_t off) 
 }
 #pragma clang diagnostic pop
 
+// Output tile (ti, tj) of workgroup `tile` in a grid of gm token tiles x gmn / gm weight
+// tiles. With xbm > 0 (xcd_block), XCD x = tile % 8 works through its own block of xbm token
+// tiles by gmn / 8 / xbm weight tiles, xgm such blocks along the tokens, so that its L2
+// fetches each weight tile of its block once; in the plain order (xbm = 0, token tiles
+// fastest) the workgroups sharing a weight tile go to different XCDs.
+static __device__ __forceinline__ void xcd_tile(int tile, int gm, int gmn, int xbm, int xgm,
+                                                int& ti, int& tj) {
+  if (xbm > 0) {
+    const int x = tile & 7, k = tile >> 3;
+    ti = (x % xgm) * xbm + k % xbm;
+    tj = (x / xgm) * ((gmn >> 3) / xbm) + k / xbm;
+  } else {
+    ti = tile % gm;
+    tj = tile / gm;
+  }
+}
+
 // Weight scales of one row's q4_K super-block, from the 16-byte header the repacked record
 // keeps per row (word 0: f16 d in bits 0..15, f16 dmin in bits 16..31; words 1..3: the 12
 // packed scale bytes s0..s11), for the four sub-blocks 4*half .. 4*half + 3. GGUF packing:

@@ -103,19 +103,8 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   // sums to plane sp of out ([splits][M][N]); with one split the plane is C itself.
   const int sp = (int)(blockIdx.x / (unsigned)gmn);
   const int tile_id = (int)(blockIdx.x - (unsigned)sp * (unsigned)gmn);
-  // Workgroups go to the 8 XCDs in turn (workgroup i to XCD i % 8), each XCD with its own
-  // L2. With xbm > 0, XCD x works through its own block of xbm token tiles by
-  // gmn / 8 / xbm weight-tile groups (xgm such blocks along the tokens), which its L2 fetches
-  // once; in the plain order every XCD would fetch every weight tile.
   int ti, tj;
-  if (xbm > 0) {
-    const int x = tile_id & 7, k = tile_id >> 3;
-    ti = (x % xgm) * xbm + k % xbm;
-    tj = (x / xgm) * ((gmn >> 3) / xbm) + k / xbm;
-  } else {
-    ti = tile_id % gm;
-    tj = tile_id / gm;
-  }
+  xcd_tile(tile_id, gm, gmn, xbm, xgm, ti, tj);
   const int tm = tm0 + ti;
   const int tn = tn0 + tj;
   const int m0 = tm * BM;
@@ -461,29 +450,6 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
       }
     }
   }
-}
-
-// The XCD blocks of a gm x gn tile grid: bm token tiles by gm*gn/8/bm weight-tile groups per
-// XCD, xgm = gm/bm blocks along the tokens and 8/xgm along the weights, of the shapes that
-// split the grid into 8 equal blocks the one whose tiles are the fewest bytes (a token tile
-// being tok_bytes, a weight-tile group w_bytes); {0, 0} (the plain order) when none does.
-struct XcdBlock {
-  int bm, xgm;
-};
-XcdBlock xcd_block(int64_t gm, int64_t gn, double tok_bytes, double w_bytes) {
-  XcdBlock best{0, 0};
-  if (gm * gn < 16 || (gm * gn) % 8) return best;
-  double cost = 0.0;
-  for (int64_t xgm = 1; xgm <= 8; xgm *= 2) {
-    const int64_t xgn = 8 / xgm;
-    if (gm % xgm || gn % xgn) continue;
-    const double c = (double)(gm / xgm) * tok_bytes + (double)(gn / xgn) * w_bytes;
-    if (best.bm == 0 || c < cost) {
-      cost = c;
-      best = {(int)(gm / xgm), (int)xgm};
-    }
-  }
-  return best;
 }
 
 template <int TT, int NW, bool STORE_S, int FMT>

@@ -56,6 +56,30 @@ struct TileShape {
   }
   constexpr int64_t lds_bytes(int fmt = kFmtQ4K) const { return 2 * stage_bytes(fmt); }
 };
+// The XCD blocks of a gm x gn grid of output tiles. Workgroups go to the 8 XCDs in turn
+// (workgroup i to XCD i % 8), each XCD with its own L2. Of the shapes that split the grid into
+// 8 equal blocks (bm token tiles by gm*gn/8/bm weight tiles; xgm = gm/bm blocks along the
+// tokens, 8/xgm along the weights), the one whose tiles are the fewest bytes, a token tile
+// being tok_bytes and a weight tile w_bytes; {0, 0} (the plain order) when none does.
+struct XcdBlock {
+  int bm, xgm;
+};
+inline XcdBlock xcd_block(int64_t gm, int64_t gn, double tok_bytes, double w_bytes) {
+  XcdBlock best{0, 0};
+  if (gm * gn < 16 || (gm * gn) % 8) return best;
+  double cost = 0.0;
+  for (int64_t xgm = 1; xgm <= 8; xgm *= 2) {
+    const int64_t xgn = 8 / xgm;
+    if (gm % xgm || gn % xgn) continue;
+    const double c = (double)(gm / xgm) * tok_bytes + (double)(gn / xgn) * w_bytes;
+    if (best.bm == 0 || c < cost) {
+      cost = c;
+      best = {(int)(gm / xgm), (int)xgm};
+    }
+  }
+  return best;
+}
+
 constexpr TileShape kLarge{4, 8};
 constexpr TileShape kSmall{1, 2};
 // 32 tokens x 256 weight rows, 8 wavefronts: the tile that splits K over workgroups
@@ -105,8 +129,10 @@ __host__ __device__ inline void bf16_split3(float v, uint16_t& p1, uint16_t& p2,
 // kSkinnyWaves wavefronts and summed through LDS in wavefront order.
 constexpr int kSkinnyWaves = 8;
 int64_t skinny_lds_bytes();
+// compute_units: the device's, which picks the kernel's form (more workgroups than compute
+// units: the form that fits two workgroups per compute unit)
 hipError_t launch_mmq_skinny(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
-                             int64_t K, hipStream_t s);
+                             int64_t K, int64_t compute_units, hipStream_t s);
 // The same kernel quantizing its own f32 activations (few tokens; per-wavefront LDS tile).
 int64_t fused_lds_bytes();
 hipError_t launch_mmq_fused(const float* x, const void* w_rep, float* C, int64_t M, int64_t N,

@@ -47,11 +47,18 @@ constexpr int kFPcBytes = 3 * 32 * 16;             // pieces [3][32 rows][8 bf16
 constexpr int kFRegion = kWDsvBytes + kWPieceBytes + kFQBytes + kFDaBytes + kFPcBytes;
 constexpr int kRedStride = 65;                     // floats per row of the partial sums
 
-template <int KW, bool FUSED>
-__global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
+// LAZY (unfused only): the token operands and (da, nb) of each block are loaded where they are
+// used, with no MFMA pipelining, so that the kernel fits 128 registers and two workgroups share
+// a compute unit (four wavefronts per SIMD cover each other's loads); chosen when the grid has
+// more workgroups than the device has compute units. Otherwise all eight blocks' operands are
+// loaded with the super-block and the MFMA of block b+1 is issued before block b's rescale
+// (158 registers, one workgroup per compute unit, the shorter path per wavefront).
+template <int KW, bool FUSED, bool LAZY>
+__global__ __launch_bounds__(KW * 64, LAZY ? 4 : 1) void mmq_skinny_kernel(
     const int8_t* __restrict__ qs, const float* __restrict__ da_plane,
     const uint16_t* __restrict__ tpieces, const float4* __restrict__ x,
-    const uint8_t* __restrict__ wrep, float* __restrict__ C, int M, int N, int K, int gm) {
+    const uint8_t* __restrict__ wrep, float* __restrict__ C, int M, int N, int K, int gm,
+    int gmn, int xbm, int xgm) {
   extern __shared__ __align__(16) uint8_t smem[];
   constexpr int W_BYTES = kWDsvBytes + kWPieceBytes;
   constexpr int REGION = FUSED ? kFRegion : W_BYTES;
@@ -61,8 +68,8 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const int tm = (int)(blockIdx.x % (unsigned)gm);
-  const int tn = (int)(blockIdx.x / (unsigned)gm);
+  int tm, tn;  // the workgroups of one weight tile on one XCD (xcd_tile)
+  xcd_tile((int)blockIdx.x, gm, gmn, xbm, xgm, tm, tn);
   const int m0 = tm * 32;
   const int nsb = K >> 8;
   const int kb = K >> 5;
@@ -103,8 +110,8 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
     const v4i hdr = buf_load16(rw, (uint32_t)s * kRepTileBytes + kRepNibBytes + l32 * 16);
-    v4i raw[4], tok[8], tp[3];
-    float2 da[8];  // (da, nb) per block
+    v4i raw[4], tok[LAZY ? 1 : 8], tp[3];
+    float2 da[LAZY ? 1 : 8];  // (da, nb) per block
 #pragma unroll
     for (int g = 0; g < 4; ++g)
       raw[g] = buf_load16(rw, (uint32_t)s * kRepTileBytes + g * 1024 + lane * 16);
@@ -161,19 +168,25 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
 #pragma unroll
       for (int j = 0; j < 3; ++j) tp[j] = *reinterpret_cast<const v4i*>(sPc + (j * 32 + l32) * 16);
     } else {
+      if constexpr (!LAZY) {
 #pragma unroll
-      for (int b = 0; b < 8; ++b) tok[b] = buf_load16(rq, tok_row + (uint32_t)s * 256 + b * 32);
+        for (int b = 0; b < 8; ++b) tok[b] = buf_load16(rq, tok_row + (uint32_t)s * 256 + b * 32);
 #pragma unroll
-      for (int b = 0; b < 8; ++b)
-        da[b] = buf_load_f32x2(rda, (((uint32_t)s * 8 + b) * (uint32_t)M + m0 + l32) * 8u);
+        for (int b = 0; b < 8; ++b)
+          da[b] = buf_load_f32x2(rda, (((uint32_t)s * 8 + b) * (uint32_t)M + m0 + l32) * 8u);
+      }
 #pragma unroll
       for (int j = 0; j < 3; ++j)
         tp[j] = buf_load16(rtp, (((uint32_t)s * 3 + j) * (uint32_t)M + m0 + l32) * 16u);
     }
     q4k_stage_scales(hdr, l32, h != 0, sW);
-    // everything has landed and the region is written; the fence and the barrier keep the
-    // compiler from moving the region's reads above the writes of the other lanes
-    __builtin_amdgcn_s_waitcnt(0);
+    // the region is written (and, unless LAZY, every load of the super-block has landed);
+    // the fence and the barrier keep the compiler from moving the region's reads above the
+    // writes of the other lanes
+    if constexpr (LAZY)
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
 
@@ -181,11 +194,22 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
       const v4i rr = raw[b >> 1];
       return (b & 1) ? ((rr >> 4) & 0x0F0F0F0F) : (rr & 0x0F0F0F0F);
     };
-    v16i Dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(wop_of(0), tok[0], bias, 0, 0, 0);
+    v16i Dn;
+    if constexpr (!LAZY) Dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(wop_of(0), tok[0], bias, 0, 0, 0);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const v16i D = Dn;
-      if (b + 1 < 8) Dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(wop_of(b + 1), tok[b + 1], bias, 0, 0, 0);
+      v16i D;
+      float2 dab;
+      if constexpr (LAZY) {
+        const v4i tb = buf_load16(rq, tok_row + (uint32_t)s * 256 + b * 32);
+        dab = buf_load_f32x2(rda, (((uint32_t)s * 8 + b) * (uint32_t)M + m0 + l32) * 8u);
+        D = __builtin_amdgcn_mfma_i32_32x32x32_i8(wop_of(b), tb, bias, 0, 0, 0);
+      } else {
+        D = Dn;
+        dab = da[b];
+        if (b + 1 < 8)
+          Dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(wop_of(b + 1), tok[b + 1], bias, 0, 0, 0);
+      }
       float dsv[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -194,7 +218,7 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float y = __builtin_fmaf(__int_as_float(D[r]), da[b].x, da[b].y);
+        const float y = __builtin_fmaf(__int_as_float(D[r]), dab.x, dab.y);
         acc[r] = __builtin_fmaf(y, dsv[r], acc[r]);
       }
       if (b == 1 || b == 3 || b == 5) {
@@ -234,6 +258,12 @@ __global__ __launch_bounds__(KW * 64, 1) void mmq_skinny_kernel(
 
 }  // namespace
 
+// XCD blocks of the skinny grid (one 32 x 32 output tile per workgroup): a token tile is its
+// rows of the q8 buffer, a weight tile its records, per super-block column
+static XcdBlock skinny_xcd_block(int64_t gm, int64_t gn, int64_t K) {
+  return xcd_block(gm, gn, 32.0 * (double)(K / 256) * 400.0, (double)(K / 256) * kRepTileBytes);
+}
+
 int64_t skinny_lds_bytes() {
   const int64_t regions = (int64_t)kSkinnyWaves * (kWDsvBytes + kWPieceBytes);
   const int64_t reduce = (int64_t)kSkinnyWaves * 16 * kRedStride * 4;
@@ -247,31 +277,35 @@ int64_t fused_lds_bytes() {
 }
 
 hipError_t launch_mmq_skinny(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
-                             int64_t K, hipStream_t s) {
+                             int64_t K, int64_t compute_units, hipStream_t s) {
   const uint8_t* base = static_cast<const uint8_t*>(q8);
   const int8_t* qs = reinterpret_cast<const int8_t*>(base);
   const float* da_plane = reinterpret_cast<const float*>(base + q8_planes_offset(M, K));
   const uint16_t* tpieces = reinterpret_cast<const uint16_t*>(base + q8_pieces_offset(M, K));
   const int64_t gm = (M + 31) / 32, gn = (N + 31) / 32;
-  hipLaunchKernelGGL((mmq_skinny_kernel<kSkinnyWaves, false>), dim3((unsigned)(gm * gn)),
-                     dim3(kSkinnyWaves * 64), (size_t)skinny_lds_bytes(), s, qs, da_plane,
-                     tpieces, nullptr, static_cast<const uint8_t*>(w_rep), C, (int)M, (int)N,
-                     (int)K, (int)gm);
+  const XcdBlock xb = skinny_xcd_block(gm, gn, K);
+  auto kern = gm * gn > compute_units ? mmq_skinny_kernel<kSkinnyWaves, false, true>
+                                      : mmq_skinny_kernel<kSkinnyWaves, false, false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(gm * gn)), dim3(kSkinnyWaves * 64),
+                     (size_t)skinny_lds_bytes(), s, qs, da_plane, tpieces, nullptr,
+                     static_cast<const uint8_t*>(w_rep), C, (int)M, (int)N, (int)K, (int)gm,
+                     (int)(gm * gn), xb.bm, xb.xgm);
   return hipGetLastError();
 }
 
 hipError_t launch_mmq_fused(const float* x, const void* w_rep, float* C, int64_t M, int64_t N,
                             int64_t K, hipStream_t s) {
-  auto kern = mmq_skinny_kernel<kSkinnyWaves, true>;
+  auto kern = mmq_skinny_kernel<kSkinnyWaves, true, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)fused_lds_bytes());
   if (e != hipSuccess) return e;
   const int64_t gm = (M + 31) / 32, gn = (N + 31) / 32;
+  const XcdBlock xb = skinny_xcd_block(gm, gn, K);
   hipLaunchKernelGGL(kern, dim3((unsigned)(gm * gn)), dim3(kSkinnyWaves * 64),
                      (size_t)fused_lds_bytes(), s, nullptr, nullptr, nullptr,
                      reinterpret_cast<const float4*>(x), static_cast<const uint8_t*>(w_rep), C,
-                     (int)M, (int)N, (int)K, (int)gm);
+                     (int)M, (int)N, (int)K, (int)gm, (int)(gm * gn), xb.bm, xb.xgm);
   return hipGetLastError();
 }
 
