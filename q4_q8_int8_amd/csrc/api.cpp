@@ -129,24 +129,29 @@ int check_options(const mmq_options* opt) {
 // memory traffic each, written and read back).
 constexpr int64_t kMaxSplits = 16;
 
-// The guard's cost model of the template's tiles, fitted to graph-replayed timings of 11
-// few-token and few-feature shapes (M = 32..1024 at N = 4096, K = 4096 and 11008; one GPU's
-// share of an 8-way column split of the 7B projections) under every tile and split count
-// 1..16: a workgroup spends c microseconds per super-block, `occ` workgroups share a compute
-// unit, and each split adds its partial plane's traffic. The model's pick is within 3 % of
-// the fastest measured choice on average (20 % at worst).
+// The guard's cost model of the template's tiles, fitted to graph-replayed timings of 13
+// few-token and few-feature shapes (M = 32..1024 at N = 4096 and 11008, K = 4096 and 11008;
+// one GPU's share of an 8-way column split of the 7B projections) under every tile and split
+// count 1..16, with and without a workspace: a workgroup spends c microseconds per
+// super-block, `occ` workgroups share a compute unit, and each split adds its partial
+// plane's traffic. The model's pick is within 2 % of the fastest measured choice on average
+// (25 % at worst: 2048 x 1376 x 4096 with a workspace, 4 splits of the large tile where 2
+// were fastest).
 struct TileCost {
   int tile;
   double us_per_sb;  // per super-block and round of workgroups
   double occ;        // workgroups per compute unit (registers and LDS)
 };
-constexpr TileCost kTileCosts[] = {{MMQ_TILE_LARGE, 3.83, 1.0},
-                                   {MMQ_TILE_MEDIUM, 1.85, 1.0},
-                                   {MMQ_TILE_SMALL, 1.35, 3.0}};
+constexpr TileCost kTileCosts[] = {{MMQ_TILE_LARGE, 4.0, 1.0},
+                                   {MMQ_TILE_MEDIUM, 2.1, 1.0},
+                                   {MMQ_TILE_SMALL, 1.5, 2.5}};
 constexpr double kUsPerPartialMB = 0.234;
-// The skinny kernel in the same model: one workgroup per 32 x 32 output tile and compute
-// unit at a time, its 8 wavefronts each walking K/8 super-blocks.
-constexpr double kSkinnyUsPerSb = 4.8;
+// The skinny kernel in the same model: one workgroup per 32 x 32 output tile, its 8
+// wavefronts each walking K/8 super-blocks; one workgroup per compute unit at a time when
+// the grid fits the device in one round, else the form that shares a compute unit between
+// two (an effective 1.2 per compute unit).
+constexpr double kSkinnyUsPerSb = 3.6;
+constexpr double kSkinnyOccLargeGrid = 1.2;
 
 mmq::TileShape tile_shape(int tile) {
   return tile == MMQ_TILE_LARGE ? mmq::kLarge : tile == MMQ_TILE_MEDIUM ? mmq::kMedium : mmq::kSmall;
@@ -218,7 +223,8 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
       // (below 8 super-blocks some of the skinny kernel's wavefronts get none, and the small
       // tile is faster: 5.5 against 7.6 us at 128 x 256 x 512)
       const double grid = (double)(((M + 31) / 32) * ((N + 31) / 32));
-      const double rounds = grid / cus > 1.0 ? grid / cus : 1.0;
+      const double occ = grid > cus ? kSkinnyOccLargeGrid : 1.0;
+      const double rounds = grid / (cus * occ) > 1.0 ? grid / (cus * occ) : 1.0;
       best = kSkinnyUsPerSb * rounds * (double)((nsb + mmq::kSkinnyWaves - 1) / mmq::kSkinnyWaves);
       best_tile = MMQ_TILE_SKINNY;
     }

@@ -86,8 +86,10 @@ def test_plan_lds_fallback_and_refusal():
 
 SKINNY = mmq.MMQ_TILE_SKINNY
 GEMV = mmq.MMQ_TILE_GEMV
+MEDIUM = mmq.MMQ_TILE_MEDIUM
 REASON = {LARGE: mmq.MMQ_REASON_LARGE, SMALL: mmq.MMQ_REASON_SMALL_GRID,
-          SKINNY: mmq.MMQ_REASON_FEW_TOKENS, GEMV: mmq.MMQ_REASON_DECODE}
+          MEDIUM: mmq.MMQ_REASON_SMALL_GRID, SKINNY: mmq.MMQ_REASON_FEW_TOKENS,
+          GEMV: mmq.MMQ_REASON_DECODE}
 
 
 @pytest.mark.parametrize("M,N,tile", [
@@ -99,8 +101,8 @@ REASON = {LARGE: mmq.MMQ_REASON_LARGE, SMALL: mmq.MMQ_REASON_SMALL_GRID,
     (17, 4096, SKINNY),     # large grid 1 x 16, few tokens
     (128, 4096, SKINNY),
     (129, 4096, SMALL),     # 2 x 16
-    (512, 4096, SMALL),     # 4 x 16 = 64 < 256 compute units
-    (1024, 4096, SMALL),    # 8 x 16 = 128
+    (512, 4096, MEDIUM),    # 4 x 16 = 64 < 256 compute units; 32 x 256 tiles: 16 x 16
+    (1024, 4096, MEDIUM),   # 8 x 16 = 128
     (2048, 4096, LARGE),    # 16 x 16 = 256
     (1024, 11008, LARGE),   # 8 x 43 = 344
     (128, 65536, LARGE),    # 1 x 256
@@ -124,9 +126,11 @@ def test_plan_skinny_needs_a_super_block_per_wavefront(M, N, K, tile):
 
 def test_plan_min_workgroups_option():
     assert mmq.mmq_plan(512, 4096, 4096, 160 * 1024, min_workgroups=64)["tile"] == LARGE
-    assert mmq.mmq_plan(512, 4096, 4096, 160 * 1024, min_workgroups=65)["tile"] == SMALL
+    p = mmq.mmq_plan(512, 4096, 4096, 160 * 1024, min_workgroups=65)
+    assert p["tile"] in (SMALL, MEDIUM) and p["grid"] >= 65
     assert mmq.mmq_plan(64, 4096, 4096, 160 * 1024, min_workgroups=16)["tile"] == LARGE
-    assert mmq.mmq_plan(2048, 4096, 4096, 160 * 1024, min_workgroups=257)["tile"] == SMALL
+    p = mmq.mmq_plan(2048, 4096, 4096, 160 * 1024, min_workgroups=257)
+    assert p["tile"] in (SMALL, MEDIUM) and p["grid"] >= 257
 
 
 def test_plan_skinny_tile():
@@ -387,7 +391,7 @@ def test_binding_refuses_unfit_tensors():
 MEDIUM = mmq.MMQ_TILE_MEDIUM
 
 
-@pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (2048, 512, 4096), (2048, 512, 11008),
+@pytest.mark.parametrize("M,N,K", [(128, 4096, 11008), (2048, 512, 4096), (2048, 512, 11008),
                                    (1024, 4096, 4096), (32, 4096, 4096)])
 def test_plan_splits_with_a_workspace(M, N, K):
     p = mmq.mmq_plan(M, N, K, 160 * 1024, workspace_bytes=1 << 40)
@@ -412,7 +416,7 @@ def test_plan_does_not_split_what_fills_the_gpu(M, N, K):
 
 
 def test_plan_splits_within_the_workspace():
-    M, N, K = 128, 4096, 4096
+    M, N, K = 128, 4096, 11008
     full = mmq.mmq_plan(M, N, K, 160 * 1024, workspace_bytes=1 << 40)
     half = mmq.mmq_plan(M, N, K, 160 * 1024, workspace_bytes=full["workspace_bytes"] // 2)
     assert 1 < half["splits"] < full["splits"]

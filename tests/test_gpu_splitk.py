@@ -47,7 +47,7 @@ def run(M, N, K, q8, rep, ws_bytes, **kw):
     return C.cpu().numpy(), mmq.mmq_last_kernel()
 
 
-@pytest.mark.parametrize("M,N,K", [(128, 4096, 4096), (2048, 512, 4096), (32, 1376, 2048),
+@pytest.mark.parametrize("M,N,K", [(128, 4096, 11008), (2048, 512, 4096), (32, 1376, 2048),
                                    (100, 700, 2816), (256, 1024, 1024)])
 def test_guard_splits_every_element(M, N, K):
     q8, rep, C_ref, T = case(M, N, K, M + N + K)
@@ -73,7 +73,7 @@ def test_forced_splits_every_element(tile, splits):
 
 
 def test_split_results_repeat_bit_for_bit():
-    M, N, K = 128, 4096, 4096
+    M, N, K = 128, 4096, 11008
     q8, rep, _, _ = case(M, N, K, 77)
     need = mmq.mmq_workspace_bytes(M, N, K)
     say("split-K repeat")
@@ -83,7 +83,7 @@ def test_split_results_repeat_bit_for_bit():
 
 
 def test_small_workspace_means_fewer_splits():
-    M, N, K = 128, 4096, 4096
+    M, N, K = 128, 4096, 11008
     q8, rep, C_ref, T = case(M, N, K, 78)
     full = mmq.mmq_workspace_bytes(M, N, K)
     say("split-K half workspace")
