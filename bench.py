@@ -580,6 +580,8 @@ def sweep(args) -> int:
         W = synth.workload(name)
         R = rotation(W["M"], W["N"], W["K"], args.rotate)
         tiles = [mmq.MMQ_TILE_LARGE, mmq.MMQ_TILE_SMALL]
+        if W["M"] <= 2048:
+            tiles.insert(1, mmq.MMQ_TILE_MEDIUM)
         if W["M"] <= 512:
             tiles.append(mmq.MMQ_TILE_SKINNY)
         if W["M"] <= mmq.GEMV_MAX_M:
