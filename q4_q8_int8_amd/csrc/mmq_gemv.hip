@@ -54,8 +54,12 @@ constexpr int kGemvSlices = 64 / kGemvRows;              // K-slices per wavefro
 constexpr int kGemvMfmaScaleBytes = 1280;                // 9-16 tokens: scales per wavefront
 constexpr int kGemvKS = kGemvSlices * (kGemvWaves / 2);  // K-slices per workgroup (16)
 
-template <int MT, bool FUSED>
-__global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
+// ONE: K fits one step per slice (at most kGemvKS super-blocks), so no next step is ever
+// loaded; without the second stage's registers (79-80 VGPRs for 1-2 tokens, fused 1) three
+// workgroups share a compute unit, which matters most when the grid has more than two per
+// unit (N > 8192 rows).
+template <int MT, bool FUSED, bool ONE>
+__global__ __launch_bounds__(kGemvWaves * 64, ONE ? 6 : 1) void mmq_gemv_kernel(
     const int8_t* __restrict__ qs, const uint32_t* __restrict__ words,
     const float* __restrict__ da_plane, const float4* __restrict__ x,
     const uint8_t* __restrict__ wrep, float* __restrict__ C, int M, int N, int K, int groups) {
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
   if (steps > 0) load(0, cur);
   for (int i = 0; i < steps; ++i) {
     // the next step's loads go out before this step's compute
-    if (i + 1 < steps) load(i + 1, nxt);
+    if (!ONE && i + 1 < steps) load(i + 1, nxt);
     const int s = ks + i * kGemvKS;
     const bool act = s < nsb;
     // the region's reads of the previous step are done before it is overwritten
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void mmq_gemv_kernel(
         }
       }
     }
-    cur = nxt;
+    if constexpr (!ONE) cur = nxt;
   }
 
   __syncthreads();  // every wavefront is done with its region
@@ -444,12 +448,12 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
   }
 }
 
-template <int MT>
+template <int MT, bool ONE>
 hipError_t launch_mt(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N, int64_t K,
                      hipStream_t s) {
   const uint8_t* base = static_cast<const uint8_t*>(q8);
   const int64_t groups = (M + MT - 1) / MT;
-  hipLaunchKernelGGL((mmq_gemv_kernel<MT, false>), dim3((unsigned)gemv_grid(M, N)),
+  hipLaunchKernelGGL((mmq_gemv_kernel<MT, false, ONE>), dim3((unsigned)gemv_grid(M, N)),
                      dim3(kGemvWaves * 64), 0, s, reinterpret_cast<const int8_t*>(base),
                      reinterpret_cast<const uint32_t*>(base + M * K),
                      reinterpret_cast<const float*>(base + q8_planes_offset(M, K)), nullptr,
@@ -457,11 +461,11 @@ hipError_t launch_mt(const void* q8, const void* w_rep, float* C, int64_t M, int
   return hipGetLastError();
 }
 
-template <int MT>
+template <int MT, bool ONE>
 hipError_t launch_fused_mt(const float* x, const void* w_rep, float* C, int64_t M, int64_t N,
                            int64_t K, hipStream_t s) {
   const int64_t groups = (M + MT - 1) / MT;
-  hipLaunchKernelGGL((mmq_gemv_kernel<MT, true>), dim3((unsigned)gemv_grid(M, N)),
+  hipLaunchKernelGGL((mmq_gemv_kernel<MT, true, ONE>), dim3((unsigned)gemv_grid(M, N)),
                      dim3(kGemvWaves * 64), 0, s, nullptr, nullptr, nullptr,
                      reinterpret_cast<const float4*>(x), static_cast<const uint8_t*>(w_rep), C,
                      (int)M, (int)N, (int)K, (int)groups);
@@ -497,22 +501,29 @@ hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t 
                        static_cast<const uint8_t*>(w_rep), C, (int)M, (int)N, (int)K);
     return hipGetLastError();
   }
+  // one step per slice: the single-stage form for 1 and 2 tokens (at 4 and 8 tokens it would
+  // spill)
+  const bool one = K / 256 <= kGemvKS;
   switch (gemv_group(M)) {
-    case 1: return launch_mt<1>(q8, w_rep, C, M, N, K, s);
-    case 2: return launch_mt<2>(q8, w_rep, C, M, N, K, s);
-    case 4: return launch_mt<4>(q8, w_rep, C, M, N, K, s);
-    default: return launch_mt<8>(q8, w_rep, C, M, N, K, s);
+    case 1: return one ? launch_mt<1, true>(q8, w_rep, C, M, N, K, s)
+                       : launch_mt<1, false>(q8, w_rep, C, M, N, K, s);
+    case 2: return one ? launch_mt<2, true>(q8, w_rep, C, M, N, K, s)
+                       : launch_mt<2, false>(q8, w_rep, C, M, N, K, s);
+    case 4: return launch_mt<4, false>(q8, w_rep, C, M, N, K, s);
+    default: return launch_mt<8, false>(q8, w_rep, C, M, N, K, s);
   }
 }
 
 hipError_t launch_mmq_gemv_fused(const float* x, const void* w_rep, float* C, int64_t M,
                                  int64_t N, int64_t K, hipStream_t s) {
   if (M < 1 || M > kGemvFusedMaxM) return hipErrorInvalidValue;
+  // the single-stage form for one token (80 VGPRs; at two tokens it would spill)
   switch (gemv_group(M)) {
-    case 1: return launch_fused_mt<1>(x, w_rep, C, M, N, K, s);
-    case 2: return launch_fused_mt<2>(x, w_rep, C, M, N, K, s);
-    case 4: return launch_fused_mt<4>(x, w_rep, C, M, N, K, s);
-    default: return launch_fused_mt<8>(x, w_rep, C, M, N, K, s);
+    case 1: return K / 256 <= kGemvKS ? launch_fused_mt<1, true>(x, w_rep, C, M, N, K, s)
+                                      : launch_fused_mt<1, false>(x, w_rep, C, M, N, K, s);
+    case 2: return launch_fused_mt<2, false>(x, w_rep, C, M, N, K, s);
+    case 4: return launch_fused_mt<4, false>(x, w_rep, C, M, N, K, s);
+    default: return launch_fused_mt<8, false>(x, w_rep, C, M, N, K, s);
   }
 }
 

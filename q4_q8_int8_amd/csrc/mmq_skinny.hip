@@ -47,10 +47,11 @@ constexpr int kFPcBytes = 3 * 32 * 16;             // pieces [3][32 rows][8 bf16
 constexpr int kFRegion = kWDsvBytes + kWPieceBytes + kFQBytes + kFDaBytes + kFPcBytes;
 constexpr int kRedStride = 65;                     // floats per row of the partial sums
 
-// LAZY (unfused only): the token operands and (da, nb) of each block are loaded where they are
-// used, with no MFMA pipelining, so that the kernel fits 128 registers and two workgroups share
-// a compute unit (four wavefronts per SIMD cover each other's loads); chosen when the grid has
-// more workgroups than the device has compute units. Otherwise all eight blocks' operands are
+// LAZY (unfused only): the token operands and (da, nb) of each block are loaded two blocks
+// ahead of their MFMA instead of with the super-block, with no MFMA pipelining, so that the
+// kernel fits 128 registers and two workgroups share a compute unit (four wavefronts per SIMD
+// cover each other's loads); chosen when the grid has more workgroups than the device has
+// compute units. Otherwise all eight blocks' operands are
 // loaded with the super-block and the MFMA of block b+1 is issued before block b's rescale
 // (158 registers, one workgroup per compute unit, the shorter path per wavefront).
 template <int KW, bool FUSED, bool LAZY>
@@ -196,13 +197,26 @@ __global__ __launch_bounds__(KW * 64, LAZY ? 4 : 1) void mmq_skinny_kernel(
     };
     v16i Dn;
     if constexpr (!LAZY) Dn = __builtin_amdgcn_mfma_i32_32x32x32_i8(wop_of(0), tok[0], bias, 0, 0, 0);
+    // LAZY: the token operand and (da, nb) of block b are loaded PF blocks ahead
+    constexpr int PF = 2;
+    v4i tq[PF + 1];
+    float2 dq[PF + 1];
+    auto lazy_load = [&](int b) {
+      tq[b % (PF + 1)] = buf_load16(rq, tok_row + (uint32_t)s * 256 + b * 32);
+      dq[b % (PF + 1)] = buf_load_f32x2(rda, (((uint32_t)s * 8 + b) * (uint32_t)M + m0 + l32) * 8u);
+    };
+    if constexpr (LAZY) {
+#pragma unroll
+      for (int b = 0; b < PF; ++b) lazy_load(b);
+    }
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       v16i D;
       float2 dab;
       if constexpr (LAZY) {
-        const v4i tb = buf_load16(rq, tok_row + (uint32_t)s * 256 + b * 32);
-        dab = buf_load_f32x2(rda, (((uint32_t)s * 8 + b) * (uint32_t)M + m0 + l32) * 8u);
+        if (b + PF < 8) lazy_load(b + PF);
+        const v4i tb = tq[b % (PF + 1)];
+        dab = dq[b % (PF + 1)];
         D = __builtin_amdgcn_mfma_i32_32x32x32_i8(wop_of(b), tb, bias, 0, 0, 0);
       } else {
         D = Dn;
