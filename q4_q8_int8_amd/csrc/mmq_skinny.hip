@@ -51,9 +51,9 @@ constexpr int kRedStride = 65;                     // floats per row of the part
 // ahead of their MFMA instead of with the super-block, with no MFMA pipelining, so that the
 // kernel fits 128 registers and two workgroups share a compute unit (four wavefronts per SIMD
 // cover each other's loads); chosen when the grid has more workgroups than the device has
-// compute units. Otherwise all eight blocks' operands are
-// loaded with the super-block and the MFMA of block b+1 is issued before block b's rescale
-// (158 registers, one workgroup per compute unit, the shorter path per wavefront).
+// compute units. Otherwise (PIPE below) everything a super-block needs is loaded into
+// registers while the previous one is computed, and the MFMA of block b+1 is issued before
+// block b's rescale (238 registers, one workgroup per compute unit).
 template <int KW, bool FUSED, bool LAZY>
 __global__ __launch_bounds__(KW * 64, LAZY ? 4 : 1) void mmq_skinny_kernel(
     const int8_t* __restrict__ qs, const float* __restrict__ da_plane,
@@ -104,18 +104,56 @@ __global__ __launch_bounds__(KW * 64, LAZY ? 4 : 1) void mmq_skinny_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
+  // PIPE (unfused, one workgroup per compute unit): everything super-block s needs is loaded
+  // into registers while super-block s-1 is computed (two register sets)
+  constexpr bool PIPE = !FUSED && !LAZY;
+  struct SbRegs {
+    v4i hdr, raw[4], tok[8], tp[3];
+    float2 da[8];
+  };
+  auto load_sb = [&](int s, SbRegs& r) {
+    r.hdr = buf_load16(rw, (uint32_t)s * kRepTileBytes + kRepNibBytes + l32 * 16);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      r.raw[g] = buf_load16(rw, (uint32_t)s * kRepTileBytes + g * 1024 + lane * 16);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) r.tok[b] = buf_load16(rq, tok_row + (uint32_t)s * 256 + b * 32);
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+      r.da[b] = buf_load_f32x2(rda, (((uint32_t)s * 8 + b) * (uint32_t)M + m0 + l32) * 8u);
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      r.tp[j] = buf_load16(rtp, (((uint32_t)s * 3 + j) * (uint32_t)M + m0 + l32) * 16u);
+  };
+  SbRegs nxt;
+  if constexpr (PIPE) {
+    if (s0 < s1) load_sb(s0, nxt);
+  }
+
   for (int s = s0; s < s1; ++s) {
     // this wavefront's earlier LDS reads of its region are done before the weight scales
     // (and, fused, the quantized tile of this super-block) overwrite it
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), the other counters unconstrained
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    const v4i hdr = buf_load16(rw, (uint32_t)s * kRepTileBytes + kRepNibBytes + l32 * 16);
-    v4i raw[4], tok[LAZY ? 1 : 8], tp[3];
+    v4i hdr, raw[4], tok[LAZY ? 1 : 8], tp[3];
     float2 da[LAZY ? 1 : 8];  // (da, nb) per block
+    if constexpr (PIPE) {
+      const SbRegs cur = nxt;
+      if (s + 1 < s1) load_sb(s + 1, nxt);
+      hdr = cur.hdr;
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      raw[g] = buf_load16(rw, (uint32_t)s * kRepTileBytes + g * 1024 + lane * 16);
+      for (int g = 0; g < 4; ++g) raw[g] = cur.raw[g];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) { tok[b] = cur.tok[b]; da[b] = cur.da[b]; }
+#pragma unroll
+      for (int j = 0; j < 3; ++j) tp[j] = cur.tp[j];
+    } else {
+      hdr = buf_load16(rw, (uint32_t)s * kRepTileBytes + kRepNibBytes + l32 * 16);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        raw[g] = buf_load16(rw, (uint32_t)s * kRepTileBytes + g * 1024 + lane * 16);
+    }
     if constexpr (FUSED) {
       // quantize rows 0..mt-1 of super-block s: lane = 8 * block + chunk, one float4 each.
       // Rows go in unrolled chunks of 8, 4, 2 or 1 (no early exit inside a chunk), so the
@@ -168,14 +206,7 @@ __global__ __launch_bounds__(KW * 64, LAZY ? 4 : 1) void mmq_skinny_kernel(
       for (int b2 = 0; b2 < 8; ++b2) da[b2] = sDa[b2 * 32 + l32];
 #pragma unroll
       for (int j = 0; j < 3; ++j) tp[j] = *reinterpret_cast<const v4i*>(sPc + (j * 32 + l32) * 16);
-    } else {
-      if constexpr (!LAZY) {
-#pragma unroll
-        for (int b = 0; b < 8; ++b) tok[b] = buf_load16(rq, tok_row + (uint32_t)s * 256 + b * 32);
-#pragma unroll
-        for (int b = 0; b < 8; ++b)
-          da[b] = buf_load_f32x2(rda, (((uint32_t)s * 8 + b) * (uint32_t)M + m0 + l32) * 8u);
-      }
+    } else if constexpr (LAZY) {
 #pragma unroll
       for (int j = 0; j < 3; ++j)
         tp[j] = buf_load16(rtp, (((uint32_t)s * 3 + j) * (uint32_t)M + m0 + l32) * 16u);
@@ -184,10 +215,10 @@ __global__ __launch_bounds__(KW * 64, LAZY ? 4 : 1) void mmq_skinny_kernel(
     // the region is written (and, unless LAZY, every load of the super-block has landed);
     // the fence and the barrier keep the compiler from moving the region's reads above the
     // writes of the other lanes
-    if constexpr (LAZY)
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    else
+    if constexpr (FUSED)
       __builtin_amdgcn_s_waitcnt(0);
+    else
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); register operands wait on their own
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
 
