@@ -81,7 +81,7 @@ enum mmq_reason {
   MMQ_REASON_LDS_FALLBACK = 3,  /* the large tile does not fit the LDS budget: small tile */
   MMQ_REASON_FORCED = 4,        /* the caller's options asked for this tile */
   MMQ_REASON_NO_FIT = 5,        /* nothing fits the budget: refused with MMQ_E_LDS */
-  MMQ_REASON_FEW_TOKENS = 6,    /* 16 < M <= 128, K >= 2048, and the large grid would leave compute
+  MMQ_REASON_FEW_TOKENS = 6,    /* 16 < M <= 256, K >= 2048, and the large grid would leave compute
                                    units idle:
                                    the skinny kernel, which splits K over wavefronts */
   MMQ_REASON_FUSED = 7,         /* mmq_q4K_f32: the vector-ALU (M <= 8) or skinny kernel quantizing
@@ -218,7 +218,7 @@ int mmq_q4K_q8_1(int64_t M, int64_t N, int64_t K, const void* q8, const void* w_
  * As mmq_q4K_q8_1, with options (tile choice, LDS budget, split-K workspace); opt may be NULL.
  * With a workspace (opt->workspace, opt->workspace_bytes) and a product whose large-tile grid
  * would leave compute units idle (few tokens or few output features: M = 128..1024 at
- * N = 4096, one GPU's share of a column-split layer), the guard may choose the medium tile
+ * N = 4096, one GPU's share of a column-split layer), the guard may choose a tile
  * with K split into `splits` ranges of super-blocks: each workgroup writes the partial sums
  * of its range to plane [split] of the workspace ([splits][M][N] float32), and a second kernel
  * adds the planes into C in increasing split order. The result is deterministic (the same
@@ -342,14 +342,16 @@ int mmq_q6K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, cons
  * mmq_plan: the LDS-budget guard as a pure host function (no device access). Chooses the
  * tile for an M x N x K product given `lds_budget` bytes per workgroup (opt->lds_budget,
  * when set, takes precedence): for M <= 16 the decode tile (MMQ_TILE_GEMV, reason
- * MMQ_REASON_DECODE); else the large tile when it fits and its grid has at least
- * opt->min_workgroups workgroups (default 256, the MI355X compute-unit count; a GEMM call
- * uses the device's count); else, when the options carry a workspace, the medium tile with
- * K split so that the grid fills the compute units (MMQ_REASON_SPLIT_K; see
- * mmq_q4K_q8_1_ex); else, for M <= 128 and K >= 2048 (at least one super-block for
- * each of its wavefronts), the skinny kernel; else the small tile (more,
- * smaller workgroups: at M = 512, N = 4096 the large tile has 64 workgroups for 256 compute
- * units); when the large tile does not fit the budget, the small tile; else MMQ_E_LDS. A
+ * MMQ_REASON_DECODE); else, with no workspace, the large tile when it fits and its grid has
+ * at least opt->min_workgroups workgroups (default 256, the MI355X compute-unit count; a GEMM
+ * call uses the device's count); else the cheapest choice under a cost model (rounds of the
+ * grid over the compute units times a per-tile cost per super-block, plus the partial
+ * planes' traffic of a split) among the large, medium and small tiles that fit (with a
+ * workspace, each with K split into 1, 2, 4, 8 or 16 ranges: MMQ_REASON_SPLIT_K; see
+ * mmq_q4K_q8_1_ex) and, for M <= 256 and K >= 2048 (at least one super-block for each of its
+ * wavefronts), the skinny kernel (MMQ_REASON_FEW_TOKENS); an unsplit medium or small tile is
+ * reported as MMQ_REASON_SMALL_GRID. When the large tile does not fit the budget, the small
+ * tile (fallback = 1, MMQ_REASON_LDS_FALLBACK); when nothing fits, MMQ_E_LDS. A
  * kernel that does not fit the budget is never launched: on the r16 page
  * (section 1) an over-budget launch failed silently and produced wrong numbers, so here
  * the fallback is explicit and reported (fallback, reason), and a refusal is an error.

@@ -40,10 +40,14 @@ constexpr int64_t kMaxK = (int64_t)1 << 24;
 
 constexpr int64_t kDefaultComputeUnits = 256;  // MI355X; mmq_plan assumes it
 constexpr int64_t kDefaultLdsBudget = 160 * 1024;  // MI355X per-workgroup LDS
-// Up to this many tokens the skinny kernel (K split over the wavefronts of a workgroup) beats
-// the small tile: at K = N = 4096 it takes 7.7 / 9.8 / 24.6 us for M = 1 / 16 / 128 against
-// 28.8 / 28.8 / 30.6 us, and loses at M = 512 (85 against 42 us).
-constexpr int64_t kSkinnyMaxM = 128;
+// The guard considers the skinny kernel (K split over the wavefronts of a workgroup) up to
+// this many tokens: at K = N = 4096 it takes 10.5 / 16.3 / 22.1 / 27.7 us for M = 32 / 128 /
+// 192 / 256 against 31.0 / 31.1 / 32.3 / 32.9 us for the small tile, ties it at 320 and
+// loses from 384 (38.9 against 33.7 us for the medium tile).
+constexpr int64_t kSkinnyGuardMaxM = 256;
+// mmq_q4K_f32 (the skinny kernel quantizing its own token tile in every workgroup) takes up
+// to this many tokens.
+constexpr int64_t kFusedMaxM = 128;
 struct DeviceInfo {
   std::once_flag once;
   int status = MMQ_OK;
@@ -129,22 +133,22 @@ int check_options(const mmq_options* opt) {
 // memory traffic each, written and read back).
 constexpr int64_t kMaxSplits = 16;
 
-// The guard's cost model of the template's tiles, fitted to graph-replayed timings of 13
+// The guard's cost model of the template's tiles, fitted to graph-replayed timings of 20
 // few-token and few-feature shapes (M = 32..1024 at N = 4096 and 11008, K = 4096 and 11008;
 // one GPU's share of an 8-way column split of the 7B projections) under every tile and split
 // count 1..16, with and without a workspace: a workgroup spends c microseconds per
 // super-block, `occ` workgroups share a compute unit, and each split adds its partial
-// plane's traffic. The model's pick is within 2 % of the fastest measured choice on average
-// (25 % at worst: 2048 x 1376 x 4096 with a workspace, 4 splits of the large tile where 2
-// were fastest).
+// plane's traffic. The model's pick is 2.8 % above the fastest measured choice on average
+// over the 40 cases (24 % at worst: 32 x 4096 x 4096 with a workspace, 8 splits of the small
+// tile where the skinny kernel was fastest).
 struct TileCost {
   int tile;
   double us_per_sb;  // per super-block and round of workgroups
   double occ;        // workgroups per compute unit (registers and LDS)
 };
-constexpr TileCost kTileCosts[] = {{MMQ_TILE_LARGE, 4.0, 1.0},
-                                   {MMQ_TILE_MEDIUM, 2.1, 1.0},
-                                   {MMQ_TILE_SMALL, 1.5, 2.5}};
+constexpr TileCost kTileCosts[] = {{MMQ_TILE_LARGE, 3.6, 1.0},
+                                   {MMQ_TILE_MEDIUM, 2.3, 1.0},
+                                   {MMQ_TILE_SMALL, 1.7, 2.5}};
 constexpr double kUsPerPartialMB = 0.234;
 // The skinny kernel in the same model: one workgroup per 32 x 32 output tile, its 8
 // wavefronts each walking K/8 super-blocks; one workgroup per compute unit at a time when
@@ -218,7 +222,7 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
     double best = 1e300;
     int best_tile = 0;
     int64_t best_sp = 1;
-    if (!q6 && M <= kSkinnyMaxM && nsb >= mmq::kSkinnyWaves &&
+    if (!q6 && M <= kSkinnyGuardMaxM && nsb >= mmq::kSkinnyWaves &&
         mmq::skinny_lds_bytes() <= budget) {
       // (below 8 super-blocks some of the skinny kernel's wavefronts get none, and the small
       // tile is faster: 5.5 against 7.6 us at 128 x 256 x 512)
@@ -516,9 +520,9 @@ int mmq_q4K_f32(int64_t M, int64_t N, int64_t K, const float* x, const void* w_r
                 void* stream) {
   int st = check_gemm_shape(M, N, K);
   if (st) return st;
-  if (M > kSkinnyMaxM)
+  if (M > kFusedMaxM)
     return fail(MMQ_E_SHAPE, "mmq_q4K_f32 is for few tokens: M = %lld is above %lld",
-                (long long)M, (long long)kSkinnyMaxM);
+                (long long)M, (long long)kFusedMaxM);
   if (!x || !w_rep || !C) return fail(MMQ_E_ARG, "null device pointer");
   if (!aligned16(x) || !aligned16(w_rep) || !aligned16(C))
     return fail(MMQ_E_ARG, "device pointers must be 16-byte aligned");

@@ -100,7 +100,8 @@ REASON = {LARGE: mmq.MMQ_REASON_LARGE, SMALL: mmq.MMQ_REASON_SMALL_GRID,
     (16, 4096, GEMV),
     (17, 4096, SKINNY),     # large grid 1 x 16, few tokens
     (128, 4096, SKINNY),
-    (129, 4096, SMALL),     # 2 x 16
+    (256, 4096, SKINNY),
+    (257, 4096, SMALL),     # 3 x 16
     (512, 4096, MEDIUM),    # 4 x 16 = 64 < 256 compute units; 32 x 256 tiles: 16 x 16
     (1024, 4096, MEDIUM),   # 8 x 16 = 128
     (2048, 4096, LARGE),    # 16 x 16 = 256
