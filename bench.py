@@ -54,6 +54,10 @@ FP32_VECTOR_TFLOPS = 78.6
 # The same FMA, measured with chains of independent v_fma_f32 on an MI355X at two wavefronts
 # per SIMD (the GEMM's occupancy): 33.9 T FMA/s.
 FP32_FMA_TFLOPS_AT_GEMM_OCCUPANCY = 67.8
+# The shader clock while the q-proj GEMM runs, from s_memtime against s_memrealtime (100 MHz)
+# read per workgroup in an instrumented copy of the kernel: 1.92-2.02 GHz, 1.99 on average.
+# 16 FMA lanes per SIMD per cycle at that clock: 65.2 TFLOP/s.
+GEMM_CLOCK_GHZ = 1.99
 RESCALE_FMA_PER_EB = 2           # the rescale's FMAs per element-block (32-block of one C value)
 PAGES_QPROJ_TMACS = 15.19        # the pages' best q-proj MMQ kernel: 34.36 GMAC in 2.262 ms
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mmq_qproj_traffic.json")
@@ -85,10 +89,13 @@ def epilogue_ceiling(M: int, N: int, K: int, gemm_us: float) -> dict:
     """The rescale's floor: RESCALE_FMA_PER_EB FP32 FMAs per element-block (M*N*K/32 of
     them) at the FP32 vector rate (non-packed, as built), the GEMM rate that floor allows as
     a fraction of the int8 matrix peak, and the measured GEMM's fraction of that floor; the
-    same at the FMA rate measured at the GEMM's occupancy."""
+    same at the FMA rate measured at the GEMM's occupancy, and at the clock measured while
+    the GEMM runs."""
     fmas = RESCALE_FMA_PER_EB * M * N * (K // 32)
     floor_us = fmas * 2 / (FP32_VECTOR_TFLOPS * 1e12) * 1e6
     occ_us = fmas * 2 / (FP32_FMA_TFLOPS_AT_GEMM_OCCUPANCY * 1e12) * 1e6
+    clk_tflops = FP32_VECTOR_TFLOPS * GEMM_CLOCK_GHZ / 2.4
+    clk_us = fmas * 2 / (clk_tflops * 1e12) * 1e6
     ceiling_tops = 2 * M * N * K / (floor_us * 1e-6) / 1e12
     return {"fma_per_element_block": RESCALE_FMA_PER_EB, "valu_peak_tflops": FP32_VECTOR_TFLOPS,
             "floor_us": round(floor_us, 2),
@@ -96,7 +103,11 @@ def epilogue_ceiling(M: int, N: int, K: int, gemm_us: float) -> dict:
             "gemm_frac_of_ceiling": round(floor_us / gemm_us, 4),
             "valu_tflops_at_occupancy": FP32_FMA_TFLOPS_AT_GEMM_OCCUPANCY,
             "floor_at_occupancy_us": round(occ_us, 2),
-            "gemm_frac_of_floor_at_occupancy": round(occ_us / gemm_us, 4)}
+            "gemm_frac_of_floor_at_occupancy": round(occ_us / gemm_us, 4),
+            "clock_ghz_under_load": GEMM_CLOCK_GHZ,
+            "valu_tflops_at_that_clock": round(clk_tflops, 1),
+            "floor_at_that_clock_us": round(clk_us, 2),
+            "gemm_frac_of_floor_at_that_clock": round(clk_us / gemm_us, 4)}
 
 
 def quant_bytes(M: int, K: int) -> int:
