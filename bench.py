@@ -592,7 +592,7 @@ def sweep(args) -> int:
         R = rotation(W["M"], W["N"], W["K"], args.rotate)
         tiles = [mmq.MMQ_TILE_LARGE, mmq.MMQ_TILE_SMALL]
         if W["M"] <= 2048:
-            tiles.insert(1, mmq.MMQ_TILE_MEDIUM)
+            tiles[1:1] = [mmq.MMQ_TILE_HALF, mmq.MMQ_TILE_MEDIUM]
         if W["M"] <= 512:
             tiles.append(mmq.MMQ_TILE_SKINNY)
         if W["M"] <= mmq.GEMV_MAX_M:

@@ -52,9 +52,9 @@ enum mmq_status {
 #define MMQ_Q6K_BLOCK_BYTES 210  /* bytes of one q6_K super-block */
 #define MMQ_REP6_TILE_BYTES 10240 /* bytes per (repacked q6_K tile, super-block) */
 
-/* Tile variants of the GEMM: one template in two instantiations (large, small), a skinny
- * kernel for few tokens that splits K over the wavefronts of a workgroup, and a vector-ALU
- * kernel for a handful of tokens (decode). */
+/* Tile variants of the GEMM: one template in four instantiations (large, half, medium,
+ * small), a skinny kernel for few tokens that splits K over the wavefronts of a workgroup,
+ * and a vector-ALU kernel for a handful of tokens (decode). */
 enum mmq_tile {
   MMQ_TILE_AUTO = 0,   /* let the guard choose */
   MMQ_TILE_LARGE = 1,  /* 128 tokens x 256 output features per workgroup, 8 wavefronts */
@@ -68,9 +68,12 @@ enum mmq_tile {
                           super-block. 9 <= M <= 16: 16 wavefronts, all tokens in one workgroup, one
                           v_mfma_i32_16x16x32_i8 per block, K split over the wavefronts by
                           super-block */
-  MMQ_TILE_MEDIUM = 5  /* 32 tokens x 256 output features per workgroup, 8 wavefronts (the
+  MMQ_TILE_MEDIUM = 5, /* 32 tokens x 256 output features per workgroup, 8 wavefronts (the
                           template of the large and small tiles); with a workspace, K may be
                           split over workgroups (split-K, see mmq_options) */
+  MMQ_TILE_HALF = 6    /* 64 tokens x 256 output features per workgroup, 8 wavefronts (the
+                          same template): half the large tile's token rows, for grids the
+                          large tile would leave short of compute units; split-K as medium */
 };
 
 /* Why the guard chose what it chose. */
@@ -107,7 +110,7 @@ typedef struct mmq_options {
                            they are undefined. The library allocates nothing */
   int64_t workspace_bytes; /* usable bytes at workspace (0: no split-K) */
   int32_t splits;       /* > 0: split K into exactly this many super-block ranges (1 <= splits
-                           <= K/256; more than 1 needs force_tile MEDIUM, LARGE or SMALL and a
+                           <= K/256; more than 1 needs force_tile LARGE, HALF, MEDIUM or SMALL and a
                            workspace of splits*M*N*4 bytes); 0: the guard decides */
   int32_t reserved;     /* must be 0 */
 } mmq_options;

@@ -33,7 +33,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MMQ_OK, MMQ_E_ARG, MMQ_E_SHAPE, MMQ_E_LDS, MMQ_E_DEVICE, MMQ_E_HIP = range(6)
 (MMQ_TILE_AUTO, MMQ_TILE_LARGE, MMQ_TILE_SMALL, MMQ_TILE_SKINNY, MMQ_TILE_GEMV,
- MMQ_TILE_MEDIUM) = range(6)
+ MMQ_TILE_MEDIUM, MMQ_TILE_HALF) = range(7)
 (MMQ_REASON_NONE, MMQ_REASON_LARGE, MMQ_REASON_SMALL_GRID, MMQ_REASON_LDS_FALLBACK,
  MMQ_REASON_FORCED, MMQ_REASON_NO_FIT, MMQ_REASON_FEW_TOKENS, MMQ_REASON_FUSED,
  MMQ_REASON_DECODE, MMQ_REASON_SPLIT_K) = range(10)

@@ -119,7 +119,7 @@ int check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 
 int check_options(const mmq_options* opt) {
   if (!opt) return MMQ_OK;
-  if (opt->force_tile < MMQ_TILE_AUTO || opt->force_tile > MMQ_TILE_MEDIUM)
+  if (opt->force_tile < MMQ_TILE_AUTO || opt->force_tile > MMQ_TILE_HALF)
     return fail(MMQ_E_ARG, "force_tile %d is not an mmq_tile", opt->force_tile);
   if (opt->lds_budget < 0) return fail(MMQ_E_ARG, "negative lds_budget");
   if (opt->min_workgroups < 0) return fail(MMQ_E_ARG, "negative min_workgroups");
@@ -133,23 +133,24 @@ int check_options(const mmq_options* opt) {
 // memory traffic each, written and read back).
 constexpr int64_t kMaxSplits = 16;
 
-// The guard's cost model of the template's tiles, fitted to graph-replayed timings of 20
-// few-token and few-feature shapes (M = 32..1024 at N = 4096 and 11008, K = 4096 and 11008;
+// The guard's cost model of the template's tiles, fitted to graph-replayed timings of 22
+// few-token and few-feature shapes (M = 32..2048 at N = 4096 and 11008, K = 4096 and 11008;
 // one GPU's share of an 8-way column split of the 7B projections) under every tile and split
 // count 1..16, with and without a workspace: a workgroup spends c microseconds per
 // super-block, `occ` workgroups share a compute unit, and each split adds its partial
-// plane's traffic. The model's pick is 2.8 % above the fastest measured choice on average
-// over the 40 cases (24 % at worst: 32 x 4096 x 4096 with a workspace, 8 splits of the small
-// tile where the skinny kernel was fastest).
+// plane's traffic. The model's pick is 0.8 % above the fastest measured choice on average
+// over the 44 cases (10 % at worst: 128 x 11008 x 4096 with a workspace, the small tile
+// unsplit where the large tile with 4 splits was fastest).
 struct TileCost {
   int tile;
   double us_per_sb;  // per super-block and round of workgroups
   double occ;        // workgroups per compute unit (registers and LDS)
 };
-constexpr TileCost kTileCosts[] = {{MMQ_TILE_LARGE, 3.6, 1.0},
-                                   {MMQ_TILE_MEDIUM, 2.3, 1.0},
+constexpr TileCost kTileCosts[] = {{MMQ_TILE_LARGE, 3.4, 1.0},
+                                   {MMQ_TILE_HALF, 2.6, 1.0},
+                                   {MMQ_TILE_MEDIUM, 2.1, 1.0},
                                    {MMQ_TILE_SMALL, 1.7, 2.5}};
-constexpr double kUsPerPartialMB = 0.234;
+constexpr double kUsPerPartialMB = 0.45;
 // The skinny kernel in the same model: one workgroup per 32 x 32 output tile, its 8
 // wavefronts each walking K/8 super-blocks; one workgroup per compute unit at a time when
 // the grid fits the device in one round, else the form that shares a compute unit between
@@ -157,8 +158,17 @@ constexpr double kUsPerPartialMB = 0.234;
 constexpr double kSkinnyUsPerSb = 3.6;
 constexpr double kSkinnyOccLargeGrid = 1.2;
 
+// the tiles of the GEMM template, which can split K
+bool template_tile(int tile) {
+  return tile == MMQ_TILE_LARGE || tile == MMQ_TILE_HALF || tile == MMQ_TILE_MEDIUM ||
+         tile == MMQ_TILE_SMALL;
+}
+
 mmq::TileShape tile_shape(int tile) {
-  return tile == MMQ_TILE_LARGE ? mmq::kLarge : tile == MMQ_TILE_MEDIUM ? mmq::kMedium : mmq::kSmall;
+  return tile == MMQ_TILE_LARGE    ? mmq::kLarge
+         : tile == MMQ_TILE_HALF   ? mmq::kHalf
+         : tile == MMQ_TILE_MEDIUM ? mmq::kMedium
+                                   : mmq::kSmall;
 }
 
 // The guard: which tile, given the LDS budget and the compute units the grid should fill.
@@ -177,6 +187,7 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
   const int64_t need_large = mmq::kLarge.lds_bytes(fmt);
   const int64_t need_small = mmq::kSmall.lds_bytes(fmt);
   const int64_t need_medium = mmq::kMedium.lds_bytes(fmt);
+  const int64_t need_half = mmq::kHalf.lds_bytes(fmt);
   const int forced = opt ? opt->force_tile : MMQ_TILE_AUTO;
   if (q6 && (forced == MMQ_TILE_SKINNY || forced == MMQ_TILE_GEMV))
     return fail(MMQ_E_ARG, "the q6_K product has no skinny or decode kernel: force large, medium "
@@ -189,9 +200,8 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
     if (forced_splits > nsb)
       return fail(MMQ_E_ARG, "splits = %lld is more than the %lld super-blocks of K",
                   (long long)forced_splits, (long long)nsb);
-    if (forced_splits > 1 && forced != MMQ_TILE_MEDIUM && forced != MMQ_TILE_LARGE &&
-        forced != MMQ_TILE_SMALL)
-      return fail(MMQ_E_ARG, "split-K needs force_tile MEDIUM, LARGE or SMALL");
+    if (forced_splits > 1 && !template_tile(forced))
+      return fail(MMQ_E_ARG, "split-K needs force_tile LARGE, HALF, MEDIUM or SMALL");
     if (plane_bytes(forced_splits) > ws_bytes)
       return fail(MMQ_E_ARG, "%lld splits need %lld bytes of workspace, %lld given",
                   (long long)forced_splits, (long long)plane_bytes(forced_splits),
@@ -206,6 +216,8 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
     if (need_small <= budget) { tile = MMQ_TILE_SMALL; reason = MMQ_REASON_FORCED; }
   } else if (forced == MMQ_TILE_MEDIUM) {
     if (need_medium <= budget) { tile = MMQ_TILE_MEDIUM; reason = MMQ_REASON_FORCED; }
+  } else if (forced == MMQ_TILE_HALF) {
+    if (need_half <= budget) { tile = MMQ_TILE_HALF; reason = MMQ_REASON_FORCED; }
   } else if (forced == MMQ_TILE_SKINNY) {
     if (mmq::skinny_lds_bytes() <= budget) { tile = MMQ_TILE_SKINNY; reason = MMQ_REASON_FORCED; }
   } else if (forced == MMQ_TILE_GEMV) {
@@ -269,7 +281,7 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
   info->reason = reason;
   info->fallback = fallback;
   info->splits = 1;
-  if (splits > 1 && tile != MMQ_TILE_MEDIUM && tile != MMQ_TILE_LARGE && tile != MMQ_TILE_SMALL)
+  if (splits > 1 && !template_tile(tile))
     splits = 1;  // (an LDS fallback to another kind of kernel drops a forced split)
   if (tile == MMQ_TILE_GEMV) {
     info->block_m = (int32_t)mmq::gemv_group(M);
@@ -373,7 +385,7 @@ int blockdots(int fmt, int64_t M, int64_t N, int64_t K, const void* q8, const vo
                 (long long)N);
   if (opt && (opt->force_tile == MMQ_TILE_SKINNY || opt->force_tile == MMQ_TILE_GEMV))
     return fail(MMQ_E_ARG, "the skinny and vector-ALU tiles have no block-dot output; force "
-                           "large, medium or small");
+                           "large, half, medium or small");
   if (opt && opt->splits > 1)
     return fail(MMQ_E_ARG, "the block dots are written without split-K");
   DeviceInfo* di;

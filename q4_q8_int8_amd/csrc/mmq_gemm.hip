@@ -511,11 +511,17 @@ hipError_t launch_fmt(int tile, const void* q8, const void* w_rep, void* out, in
                       int64_t N, int64_t K, int64_t gm, int64_t gn, int64_t splits, int64_t tm0,
                       int64_t tn0, bool store_s, int64_t i0, int64_t i1, int64_t j0, int64_t j1,
                       hipStream_t s) {
-  constexpr TileShape L = kLarge, S = kSmall, D = kMedium;
+  constexpr TileShape L = kLarge, S = kSmall, D = kMedium, H = kHalf;
   if (tile == 1) {
     return store_s ? launch_t<L.tt, L.nw, true, FMT>(q8, w_rep, out, M, N, K, gm, gn, 1, tm0,
                                                      tn0, i0, i1, j0, j1, s)
                    : launch_t<L.tt, L.nw, false, FMT>(q8, w_rep, out, M, N, K, gm, gn, splits,
+                                                      tm0, tn0, i0, i1, j0, j1, s);
+  }
+  if (tile == 6) {
+    return store_s ? launch_t<H.tt, H.nw, true, FMT>(q8, w_rep, out, M, N, K, gm, gn, 1, tm0,
+                                                     tn0, i0, i1, j0, j1, s)
+                   : launch_t<H.tt, H.nw, false, FMT>(q8, w_rep, out, M, N, K, gm, gn, splits,
                                                       tm0, tn0, i0, i1, j0, j1, s);
   }
   if (tile == 5) {

@@ -84,6 +84,8 @@ constexpr TileShape kLarge{4, 8};
 constexpr TileShape kSmall{1, 2};
 // 32 tokens x 256 weight rows, 8 wavefronts: the tile that splits K over workgroups
 constexpr TileShape kMedium{1, 8};
+// 64 tokens x 256 weight rows, 8 wavefronts: half the large tile's token rows
+constexpr TileShape kHalf{2, 8};
 
 // q8 buffer: int8 q [M][K], u32 scale words [M][K/32], then (each at a 256-byte boundary)
 // the GEMM's planes: f32 pairs (da, nda = -kBiasF * da) [K/32][M][2], and dma = da*sa as
@@ -171,7 +173,8 @@ hipError_t launch_repack_q6_K(const void* w, int64_t N, int64_t K, void* w_rep, 
 // weight-tile groups [tn0, tn0+gn) and `splits` contiguous ranges of super-blocks. store_s
 // selects the store-S epilogue (S written to out as int32 [K/32][i1-i0][j1-j0], one split);
 // otherwise out is C when splits == 1, else the partial planes [splits][M][N] f32 that
-// launch_reduce_splits adds into C. tile: 1 large, 2 small, 5 medium (kMedium).
+// launch_reduce_splits adds into C. tile: 1 large, 2 small, 5 medium (kMedium), 6 half
+// (kHalf).
 hipError_t launch_mmq(int tile, const void* q8, const void* w_rep, void* out, int64_t M,
                       int64_t N, int64_t K, int64_t gm, int64_t gn, int64_t splits, int64_t tm0,
                       int64_t tn0, bool store_s, int64_t i0, int64_t i1, int64_t j0, int64_t j1,

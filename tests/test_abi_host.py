@@ -72,6 +72,24 @@ def test_plan_large_when_it_fits():
     assert p["grid"] == 16 * 16
 
 
+HALF_LDS = 2 * (64 * 272 + 64 * 64 + 64 * 48 + 8 * 3072)
+
+
+def test_plan_half_tile_forced():
+    p = mmq.mmq_plan(1000, 3000, 4096, 160 * 1024, force_tile=mmq.MMQ_TILE_HALF)
+    assert p["tile"] == mmq.MMQ_TILE_HALF and p["reason"] == mmq.MMQ_REASON_FORCED
+    assert p["block_m"] == 64 and p["block_n"] == 256 and p["threads"] == 512
+    assert p["lds_bytes"] == HALF_LDS
+    assert p["grid"] == 16 * 12                 # ceil(1000/64) x ceil(ceil(3000/32)/8)
+    # a budget below its stages refuses it (MMQ_E_LDS), as for every forced tile
+    with pytest.raises(mmq.MMQError) as e:
+        mmq.mmq_plan(1000, 3000, 4096, HALF_LDS - 1, force_tile=mmq.MMQ_TILE_HALF)
+    assert e.value.status == mmq.MMQ_E_LDS
+    p = mmq.mmq_plan(1000, 3000, 4096, 160 * 1024, force_tile=mmq.MMQ_TILE_HALF, splits=4,
+                     workspace_bytes=4 * 1000 * 3000 * 4)
+    assert p["tile"] == mmq.MMQ_TILE_HALF and p["splits"] == 4 and p["grid"] == 16 * 12 * 4
+
+
 def test_plan_lds_fallback_and_refusal():
     p = mmq.mmq_plan(2048, 4096, 4096, LARGE_LDS - 1)
     assert p["tile"] == mmq.MMQ_TILE_SMALL and p["fallback"] == 1
@@ -87,9 +105,10 @@ def test_plan_lds_fallback_and_refusal():
 SKINNY = mmq.MMQ_TILE_SKINNY
 GEMV = mmq.MMQ_TILE_GEMV
 MEDIUM = mmq.MMQ_TILE_MEDIUM
+HALF = mmq.MMQ_TILE_HALF
 REASON = {LARGE: mmq.MMQ_REASON_LARGE, SMALL: mmq.MMQ_REASON_SMALL_GRID,
-          MEDIUM: mmq.MMQ_REASON_SMALL_GRID, SKINNY: mmq.MMQ_REASON_FEW_TOKENS,
-          GEMV: mmq.MMQ_REASON_DECODE}
+          MEDIUM: mmq.MMQ_REASON_SMALL_GRID, HALF: mmq.MMQ_REASON_SMALL_GRID,
+          SKINNY: mmq.MMQ_REASON_FEW_TOKENS, GEMV: mmq.MMQ_REASON_DECODE}
 
 
 @pytest.mark.parametrize("M,N,tile", [
@@ -103,7 +122,9 @@ REASON = {LARGE: mmq.MMQ_REASON_LARGE, SMALL: mmq.MMQ_REASON_SMALL_GRID,
     (256, 4096, SKINNY),
     (257, 4096, SMALL),     # 3 x 16
     (512, 4096, MEDIUM),    # 4 x 16 = 64 < 256 compute units; 32 x 256 tiles: 16 x 16
-    (1024, 4096, MEDIUM),   # 8 x 16 = 128
+    (768, 4096, HALF),      # 6 x 16 = 96; 64 x 256 tiles: 12 x 16
+    (1024, 4096, HALF),     # 8 x 16 = 128; 16 x 16
+    (256, 11008, HALF),     # 2 x 43 = 86; 4 x 43
     (2048, 4096, LARGE),    # 16 x 16 = 256
     (1024, 11008, LARGE),   # 8 x 43 = 344
     (128, 65536, LARGE),    # 1 x 256
@@ -128,10 +149,10 @@ def test_plan_skinny_needs_a_super_block_per_wavefront(M, N, K, tile):
 def test_plan_min_workgroups_option():
     assert mmq.mmq_plan(512, 4096, 4096, 160 * 1024, min_workgroups=64)["tile"] == LARGE
     p = mmq.mmq_plan(512, 4096, 4096, 160 * 1024, min_workgroups=65)
-    assert p["tile"] in (SMALL, MEDIUM) and p["grid"] >= 65
+    assert p["tile"] in (SMALL, MEDIUM, HALF) and p["grid"] >= 65
     assert mmq.mmq_plan(64, 4096, 4096, 160 * 1024, min_workgroups=16)["tile"] == LARGE
     p = mmq.mmq_plan(2048, 4096, 4096, 160 * 1024, min_workgroups=257)
-    assert p["tile"] in (SMALL, MEDIUM) and p["grid"] >= 257
+    assert p["tile"] in (SMALL, MEDIUM, HALF) and p["grid"] >= 257
 
 
 def test_plan_skinny_tile():
@@ -393,7 +414,7 @@ MEDIUM = mmq.MMQ_TILE_MEDIUM
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 4096, 11008), (2048, 512, 4096), (2048, 512, 11008),
-                                   (1024, 4096, 4096), (32, 4096, 4096)])
+                                   (256, 4096, 11008), (64, 4096, 11008)])
 def test_plan_splits_with_a_workspace(M, N, K):
     p = mmq.mmq_plan(M, N, K, 160 * 1024, workspace_bytes=1 << 40)
     assert p["reason"] == mmq.MMQ_REASON_SPLIT_K and p["splits"] > 1
@@ -417,7 +438,7 @@ def test_plan_does_not_split_what_fills_the_gpu(M, N, K):
 
 
 def test_plan_splits_within_the_workspace():
-    M, N, K = 128, 4096, 11008
+    M, N, K = 2048, 512, 11008
     full = mmq.mmq_plan(M, N, K, 160 * 1024, workspace_bytes=1 << 40)
     half = mmq.mmq_plan(M, N, K, 160 * 1024, workspace_bytes=full["workspace_bytes"] // 2)
     assert 1 < half["splits"] < full["splits"]

@@ -23,6 +23,7 @@ mmq = pytest.importorskip("q4_q8_int8_amd")
 torch = pytest.importorskip("torch")
 
 LARGE, SMALL, SKINNY = mmq.MMQ_TILE_LARGE, mmq.MMQ_TILE_SMALL, mmq.MMQ_TILE_SKINNY
+MEDIUM, HALF = mmq.MMQ_TILE_MEDIUM, mmq.MMQ_TILE_HALF
 CONFIGS = ["tiny", "qproj", "gateup", "down"]
 SWEEP = [f"sweep_m{m}" for m in synth.SWEEP_M]
 
@@ -96,7 +97,7 @@ def test_repack_ragged_rows(N, K):
 
 
 # ----------------------------------------------------------------------------- block dots
-@pytest.mark.parametrize("tile", [LARGE, SMALL])
+@pytest.mark.parametrize("tile", [LARGE, HALF, MEDIUM, SMALL])
 def test_blockdots_tiny_every_element(tile):
     W = workload("tiny")
     M, N, K = W["M"], W["N"], W["K"]
@@ -116,7 +117,7 @@ WINDOWS = {  # (i0, i1, j0, j1) -- corners, tile edges and ragged tails
 
 
 @pytest.mark.parametrize("name", sorted(WINDOWS))
-@pytest.mark.parametrize("tile", [LARGE, SMALL])
+@pytest.mark.parametrize("tile", [LARGE, HALF, SMALL])
 def test_blockdots_windows(name, tile):
     W = workload(name)
     M, N, K = W["M"], W["N"], W["K"]
@@ -130,7 +131,7 @@ def test_blockdots_windows(name, tile):
 
 
 # ----------------------------------------------------------------------------- the product
-@pytest.mark.parametrize("tile", [LARGE, SMALL])
+@pytest.mark.parametrize("tile", [LARGE, HALF, MEDIUM, SMALL])
 def test_mmq_tiny_every_element(tile):
     W = workload("tiny")
     M, N, K = W["M"], W["N"], W["K"]
@@ -225,6 +226,28 @@ def test_mmq_skinny_every_element(name):
     say("max |err|/T", r)
 
 
+@pytest.mark.parametrize("M,N,K,lazy", [(200, 4096, 4096, True), (256, 1376, 4096, True),
+                                        (33, 4096, 11008, False)])
+def test_mmq_guard_skinny_range_every_element(M, N, K, lazy):
+    """Shapes the guard gives to the skinny kernel, every element: ragged token tiles in the
+    two-workgroups-per-CU form (grid above the compute units; token operands loaded two
+    blocks ahead), and 5 to 6 super-blocks per wavefront in the one-round form (the next
+    super-block's loads in flight)."""
+    x = synth.activations("normal_outliers", M, K, 7000 + M)
+    w, _ = synth.q4k_weights("fit", N, K, 7001 + M)
+    q8 = gpu_quantize(x)
+    rep = gpu_repack(w, N, K)
+    say("mmq guard skinny", (M, N, K))
+    C = gpu_mmq(M, N, K, q8, rep)
+    info = mmq.mmq_last_kernel()
+    assert info["tile"] == SKINNY and (info["grid"] > 256) == lazy
+    q = oracle.quantize_q8_1(x)
+    wo = oracle.decode_q4_K(w)
+    _, T = oracle.mmq_terms(q, wo)
+    r = assert_within_tolerance(C, oracle.mmq(q, wo), T)
+    say("max |err|/T", r)
+
+
 def test_mmq_skinny_deterministic():
     x = synth.activations("normal_outliers", 40, 2816, 15)
     w, f = synth.q4k_weights("fit", 70, 2816, 16)
@@ -241,17 +264,17 @@ def test_mmq_skinny_deterministic():
 
 
 def test_mmq_tiles_agree_bitwise_and_deterministic():
-    """Both tile instantiations add the same terms in the same order: identical bits."""
+    """The template's four instantiations add the same terms in the same order: identical
+    bits, on ragged M and N."""
     x = synth.activations("normal_outliers", 300, 1024, 5)
     w, f = synth.q4k_weights("fit", 200, 1024, 6)
     q8 = gpu_quantize(x)
     rep = gpu_repack(w, 200, 1024)
     say("mmq tiles agree")
     a = gpu_mmq(300, 200, 1024, q8, rep, force_tile=LARGE)
-    b = gpu_mmq(300, 200, 1024, q8, rep, force_tile=SMALL)
-    c = gpu_mmq(300, 200, 1024, q8, rep, force_tile=LARGE)
-    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
-    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+    for tile in (SMALL, MEDIUM, HALF, LARGE):
+        b = gpu_mmq(300, 200, 1024, q8, rep, force_tile=tile)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), tile
 
 
 def test_mmq_lds_fallback_reported():
@@ -285,7 +308,7 @@ def test_mmq_edge_shapes(M, N, K):
     wo = oracle.decode_q4_K(w)
     _, T = oracle.mmq_terms(q, wo)
     C_ref = oracle.mmq(q, wo)
-    for tile in (LARGE, SMALL, SKINNY):
+    for tile in (LARGE, HALF, SMALL, SKINNY):
         say("mmq edge", (M, N, K), tile)
         C = gpu_mmq(M, N, K, q8, rep, force_tile=tile)
         assert_within_tolerance(C, C_ref, T)
@@ -306,7 +329,7 @@ def test_mmq_integer_case_exact():
     q8 = gpu_quantize(x)
     rep = gpu_repack(w, N, K)
     want = (x.astype(np.int64) @ f["v"].astype(np.int64).T).astype(np.float64)
-    for tile in (LARGE, SMALL):
+    for tile in (LARGE, HALF, SMALL):
         say("mmq integer case", tile)
         C = gpu_mmq(M, N, K, q8, rep, force_tile=tile)
         assert np.array_equal(C.astype(np.float64), want)

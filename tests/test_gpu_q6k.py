@@ -21,6 +21,7 @@ mmq = pytest.importorskip("q4_q8_int8_amd")
 torch = pytest.importorskip("torch")
 
 LARGE, SMALL, MEDIUM = mmq.MMQ_TILE_LARGE, mmq.MMQ_TILE_SMALL, mmq.MMQ_TILE_MEDIUM
+HALF = mmq.MMQ_TILE_HALF
 # (M, K, N, activation kind, x seed, weight kind, w seed)
 SHAPES = {
     "tiny": (128, 512, 256, "normal", 1000, "random_fields", 2100),
@@ -72,7 +73,7 @@ def test_repack_q6k_bytes(N, K):
     assert np.array_equal(got, repack_q6k_reference(f))
 
 
-@pytest.mark.parametrize("tile", [LARGE, SMALL, MEDIUM])
+@pytest.mark.parametrize("tile", [LARGE, SMALL, MEDIUM, HALF])
 def test_q6k_group_dots_tiny_every_element(tile):
     x, w, f, q, wo = case("tiny")
     M, K, N = SHAPES["tiny"][:3]
@@ -94,7 +95,7 @@ def test_q6k_group_dots_qproj_windows(tile):
         assert np.array_equal(S.astype(np.int64), want)
 
 
-@pytest.mark.parametrize("tile", [0, LARGE, SMALL, MEDIUM])
+@pytest.mark.parametrize("tile", [0, LARGE, SMALL, MEDIUM, HALF])
 def test_q6k_tiny_every_element(tile):
     x, w, f, q, wo = case("tiny")
     M, K, N = SHAPES["tiny"][:3]

@@ -20,6 +20,7 @@ mmq = pytest.importorskip("q4_q8_int8_amd")
 torch = pytest.importorskip("torch")
 
 MEDIUM, LARGE, SMALL = mmq.MMQ_TILE_MEDIUM, mmq.MMQ_TILE_LARGE, mmq.MMQ_TILE_SMALL
+HALF = mmq.MMQ_TILE_HALF
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -54,7 +55,7 @@ def test_guard_splits_every_element(M, N, K):
     need = mmq.mmq_workspace_bytes(M, N, K)
     say("split-K guard", (M, N, K), "workspace", need)
     C, info = run(M, N, K, q8, rep, need)
-    assert info["tile"] in (MEDIUM, LARGE, SMALL) and info["reason"] == mmq.MMQ_REASON_SPLIT_K
+    assert info["tile"] in (MEDIUM, LARGE, SMALL, HALF) and info["reason"] == mmq.MMQ_REASON_SPLIT_K
     assert info["splits"] > 1 and info["workspace_bytes"] == need
     assert info["workspace_bytes"] == info["splits"] * M * N * 4
     r = assert_within_tolerance(C, C_ref, T)
@@ -62,7 +63,7 @@ def test_guard_splits_every_element(M, N, K):
 
 
 @pytest.mark.parametrize("tile,splits", [(MEDIUM, 2), (MEDIUM, 3), (MEDIUM, 11), (LARGE, 4),
-                                         (SMALL, 5), (MEDIUM, 1)])
+                                         (SMALL, 5), (MEDIUM, 1), (HALF, 3)])
 def test_forced_splits_every_element(tile, splits):
     M, N, K = 150, 300, 2816            # 11 super-blocks, ragged M and N
     q8, rep, C_ref, T = case(M, N, K, 31)
@@ -83,7 +84,7 @@ def test_split_results_repeat_bit_for_bit():
 
 
 def test_small_workspace_means_fewer_splits():
-    M, N, K = 128, 4096, 11008
+    M, N, K = 2048, 512, 11008
     q8, rep, C_ref, T = case(M, N, K, 78)
     full = mmq.mmq_workspace_bytes(M, N, K)
     say("split-K half workspace")

@@ -48,8 +48,8 @@ def both(M, N, K, q8, rep):
 
 
 def test_static_scratch_matches_the_caller_workspace_twice():
-    first = (128, 4096, 11008)    # split 16 ways: 32 MiB of partial planes, all of it
-    second = (64, 1376, 2048)     # smaller, split again, over what the first call left
+    first = (128, 4096, 11008)    # split 4 ways: 8 MiB of partial planes
+    second = (32, 1376, 2048)     # smaller, split 8 ways, over what the first call left
     for (M, N, K), seed in ((first, 9100), (second, 9200)):
         x, w, q8, rep = inputs(M, N, K, seed)
         say("static scratch", (M, N, K))
