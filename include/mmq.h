@@ -92,7 +92,8 @@ enum mmq_reason {
   MMQ_REASON_DECODE = 8,        /* M <= 16: the decode tile, which streams the weights once
                                    without the large MFMA tiles' 32-token padding */
   MMQ_REASON_SPLIT_K = 9        /* the large grid would leave compute units idle and a workspace
-                                   was given: the medium tile, K split over workgroups */
+                                   was given: a tile of the template, K split over
+                                   workgroups */
 };
 
 /* Optional knobs for the _ex entry points (NULL = defaults). */
@@ -105,7 +106,7 @@ typedef struct mmq_options {
                            device's per-workgroup limit (lets a caller force the fallback) */
   void* workspace;      /* device scratch for split-K partial sums, caller-owned, 16-byte
                            aligned, or NULL: with workspace_bytes > 0 the guard may split K over
-                           workgroups (the medium tile) when the large tile's grid would leave
+                           workgroups (a tile of the template) when the large tile's grid would leave
                            compute units idle. Its contents on entry do not matter; on return
                            they are undefined. The library allocates nothing */
   int64_t workspace_bytes; /* usable bytes at workspace (0: no split-K) */
@@ -322,7 +323,7 @@ int repack_q6_K(const void* w_q6K, int64_t N, int64_t K, void* w_rep, void* stre
 /*
  * mmq_q6K_q8_1: C[M][N] (float32, row-major, overwritten) = the product above, from q8 of
  * quantize_q8_1 (M x K) and w_rep of repack_q6_K (N x K). The GEMM template of the q4_K
- * product (large, medium and small tiles, the same guard, split-K with a workspace through
+ * product (large, half, medium and small tiles, the same guard, split-K with a workspace through
  * the _ex options): per 32-block two int8 MFMAs, each keeping one 16-value group (the lane half
  * that holds it), S_ijg exact; per group y = RN(S * da), acc += dsv * y, groups in increasing
  * order (deterministic). There is no skinny or decode kernel for q6_K.
@@ -349,10 +350,10 @@ int mmq_q6K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, cons
  * at least opt->min_workgroups workgroups (default 256, the MI355X compute-unit count; a GEMM
  * call uses the device's count); else the cheapest choice under a cost model (rounds of the
  * grid over the compute units times a per-tile cost per super-block, plus the partial
- * planes' traffic of a split) among the large, medium and small tiles that fit (with a
+ * planes' traffic of a split) among the large, half, medium and small tiles that fit (with a
  * workspace, each with K split into 1, 2, 4, 8 or 16 ranges: MMQ_REASON_SPLIT_K; see
  * mmq_q4K_q8_1_ex) and, for M <= 256 and K >= 2048 (at least one super-block for each of its
- * wavefronts), the skinny kernel (MMQ_REASON_FEW_TOKENS); an unsplit medium or small tile is
+ * wavefronts), the skinny kernel (MMQ_REASON_FEW_TOKENS); an unsplit half, medium or small tile is
  * reported as MMQ_REASON_SMALL_GRID. When the large tile does not fit the budget, the small
  * tile (fallback = 1, MMQ_REASON_LDS_FALLBACK); when nothing fits, MMQ_E_LDS. A
  * kernel that does not fit the budget is never launched: on the r16 page
