@@ -68,6 +68,55 @@ def test_integer_step_in_a_graph(M, N, K):
     _replay_and_check(g, C, want, disturb)
 
 
+@pytest.mark.parametrize("M,N,K,tile,split", [(768, 1376, 2048, "half", False),
+                                               (200, 4096, 4096, "auto", False),
+                                               (2048, 512, 4096, "auto", True)])
+def test_ex_options_in_a_graph(M, N, K, tile, split):
+    """The half tile, the skinny kernel's two-workgroups-per-CU form, and split-K (the GEMM
+    writing its partial planes into the caller's workspace, then the second pass) captured
+    with the quantize step."""
+    x = to_dev(synth.activations("normal_outliers", M, K, 7100 + M))
+    w, _ = synth.q4k_weights("fit", N, K, 7101)
+    rep = torch.empty(mmq.mmq_q4K_repacked_bytes(N, K), dtype=torch.uint8, device="cuda")
+    mmq.repack_q4_K(to_dev(w), N, K, rep)
+    q8 = torch.zeros(mmq.mmq_q8_1_bytes(M, K), dtype=torch.uint8, device="cuda")
+    C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    ws = None
+    if split:
+        ws = torch.empty(mmq.mmq_workspace_bytes(M, N, K) // 4, dtype=torch.float32,
+                         device="cuda")
+    force = mmq.MMQ_TILE_HALF if tile == "half" else mmq.MMQ_TILE_AUTO
+
+    def step():
+        mmq.quantize_q8_1(x, M, K, q8)
+        mmq.mmq_q4K_q8_1_ex(M, N, K, q8, rep, C, force_tile=force, workspace=ws)
+
+    say("graph: ex options eager", M, N, K, tile, split)
+    step()
+    torch.cuda.synchronize()
+    want = C.cpu().numpy()
+    info = mmq.mmq_last_kernel()
+    if tile == "half":
+        assert info["tile"] == mmq.MMQ_TILE_HALF
+    if split:
+        assert info["splits"] > 1
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+
+    def disturb():  # scribble over the q8 buffer and the workspace eagerly
+        q8.fill_(0x55)
+        if ws is not None:
+            ws.fill_(float("nan"))
+    say("graph: ex options replays", M, N, K)
+    _replay_and_check(g, C, want, disturb)
+
+
 def test_f16_path_in_a_graph():
     M, N, K = 512, 1024, 2048
     x = to_dev(synth.activations("normal_outliers", M, K, 7002))
