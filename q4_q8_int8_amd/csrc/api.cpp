@@ -138,9 +138,9 @@ constexpr int64_t kMaxSplits = 16;
 // one GPU's share of an 8-way column split of the 7B projections) under every tile and split
 // count 1..16, with and without a workspace: a workgroup spends c microseconds per
 // super-block, `occ` workgroups share a compute unit, and each split adds its partial
-// plane's traffic. The model's pick is 0.8 % above the fastest measured choice on average
-// over the 44 cases (10 % at worst: 128 x 11008 x 4096 with a workspace, the small tile
-// unsplit where the large tile with 4 splits was fastest).
+// plane's traffic. The model's pick is 0.6 % above the fastest measured choice on average
+// over the 44 cases (14 % at worst: 32 x 11008 x 4096 with a workspace, the skinny kernel
+// where the small tile with 4 splits was fastest).
 struct TileCost {
   int tile;
   double us_per_sb;  // per super-block and round of workgroups
