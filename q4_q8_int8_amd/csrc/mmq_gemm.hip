@@ -216,11 +216,15 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
   // EARLY (the q4_K small tile, one token tile and two wavefronts): a super-block is too
   // short to cover the next stage's load latency with loads spread over its steps, so every
   // load of stage s+1 is issued at the first step of super-block s, the nibbles into a second
-  // register set (rawB) that becomes raw when the stage ends. (Measured: 8-10 % faster for the
-  // small tile at 128..2048 tokens; no gain for the medium tile, a loss for the half tile.)
+  // register set (rawB) that becomes raw when the stage ends. ENIB (the medium tile, eight
+  // wavefronts): only the nibbles go early (all of a stage's loads at once from eight
+  // wavefronts stall on issue); the other loads stay spread over the steps. (Measured: the
+  // small tile 8-10 % faster at 128..2048 tokens, the medium tile 1-8 %; the half tile is
+  // slower with either, so it keeps the in-place reloads.)
   constexpr bool EARLY = !STORE_S && !Q6 && TT == 1 && NW == 2;
-  v4i raw[NG], nib3, rawB[EARLY ? NG : 1];
-  if constexpr (EARLY) {
+  constexpr bool ENIB = !STORE_S && !Q6 && TT == 1 && NW == 8;
+  v4i raw[NG], nib3, rawB[(EARLY || ENIB) ? NG : 1];
+  if constexpr (EARLY || ENIB) {
 #pragma unroll
     for (int v = 0; v < NOPS - 1; ++v) issue_op(v, sb0, 0, nib3);
 #pragma unroll
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
 
   for (int s = sb0; s < sb1; ++s) {
     const int p = (s - sb0) & 1;
-    if constexpr (!EARLY) raw[NG - 1] = nib3;
+    if constexpr (!EARLY && !ENIB) raw[NG - 1] = nib3;
     const bool more = s + 1 < sb1;
 
     const uint8_t* st = smem + p * STAGE;
@@ -390,6 +394,14 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
 #pragma unroll
               for (int g = 0; g < NG; ++g) rawB[g] = load_nib(s + 1, g);
             }
+          } else if constexpr (ENIB) {
+            if (n == 0) {
+#pragma unroll
+              for (int g = 0; g < NG; ++g) rawB[g] = load_nib(s + 1, g);
+            }
+#pragma unroll
+            for (int v = 0; v < NOPS - 1; ++v)
+              if (op_step(v) == n) issue_op(v, s + 1, p ^ 1, nib3);
           } else {
 #pragma unroll
             for (int v = 0; v < NOPS; ++v)
@@ -432,7 +444,7 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void mmq_kernel(
     if constexpr (!STORE_S) __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0);  // this wavefront's stage s+1 loads have landed
     __syncthreads();                // ... and everyone's; stage s is no longer read
-    if constexpr (EARLY) {
+    if constexpr (EARLY || ENIB) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) raw[g] = rawB[g];
     }
