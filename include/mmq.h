@@ -54,7 +54,7 @@ enum mmq_status {
 
 /* Tile variants of the GEMM: one template in four instantiations (large, half, medium,
  * small), a skinny kernel for few tokens that splits K over the wavefronts of a workgroup,
- * and a vector-ALU kernel for a handful of tokens (decode). */
+ * and a decode kernel for a handful of tokens in a vector-ALU and a matrix-unit form. */
 enum mmq_tile {
   MMQ_TILE_AUTO = 0,   /* let the guard choose */
   MMQ_TILE_LARGE = 1,  /* 128 tokens x 256 output features per workgroup, 8 wavefronts */
@@ -62,12 +62,15 @@ enum mmq_tile {
   MMQ_TILE_SKINNY = 3, /* 32 tokens x 32 output features per workgroup, K split over 8
                           wavefronts and summed in wavefront order (no block-dot output) */
   MMQ_TILE_GEMV = 4,   /* M <= 16 only (decode), 16 output features per workgroup, partial
-                          sums added in a fixed order, no block-dot output. M <= 8: 8
-                          wavefronts, up to 8 tokens per workgroup, integer dot products on the
-                          vector ALU (v_dot4_i32_i8), K split over 16 slices x 2 halves of each
-                          super-block. 9 <= M <= 16: 16 wavefronts, all tokens in one workgroup, one
+                          sums added in a fixed order, no block-dot output, in two forms.
+                          Vector-ALU form (threads = 512): 8 wavefronts, up to 8 tokens per
+                          workgroup, integer dot products on the vector ALU (v_dot4_i32_i8), K
+                          split over 16 slices x 2 halves of each super-block; taken for M <= 4,
+                          and for 5 <= M <= 8 when ceil(N/16) exceeds the compute units or the
+                          LDS budget is below the other form's. Matrix-unit form (threads =
+                          1024, 128 KiB of LDS): 16 wavefronts, all tokens in one workgroup, one
                           v_mfma_i32_16x16x32_i8 per block, K split over the wavefronts by
-                          super-block */
+                          super-block; taken for 9 <= M <= 16, and for 5 <= M <= 8 otherwise */
   MMQ_TILE_MEDIUM = 5, /* 32 tokens x 256 output features per workgroup, 8 wavefronts (the
                           template of the large and small tiles); with a workspace, K may be
                           split over workgroups (split-K, see mmq_options) */
@@ -259,9 +262,10 @@ int mmq_q4K_q8_1_static(int64_t M, int64_t N, int64_t K, const void* q8, const v
 /*
  * mmq_q4K_f32: the product for few tokens straight from float32 activations x[M][K]
  * (row-major, leading dimension K), quantizing them inside the GEMM. C is bit for bit what
- * quantize_q8_1 followed by mmq_q4K_q8_1_ex writes with MMQ_TILE_GEMV (M <= 8) or
- * MMQ_TILE_SKINNY (8 < M <= 128), but no q8 buffer goes through memory and there is one
- * launch instead of two. Each workgroup quantizes, into LDS, the activations of the
+ * quantize_q8_1 followed by mmq_q4K_q8_1_ex writes with MMQ_TILE_GEMV in its vector-ALU form
+ * (M <= 8; the form mmq_q4K_q8_1_ex takes under an LDS budget below the matrix-unit form's)
+ * or with MMQ_TILE_SKINNY (8 < M <= 128), but no q8 buffer goes through memory and there is
+ * one launch instead of two. Each workgroup quantizes, into LDS, the activations of the
  * super-blocks it works on (the quantization of quantize_q8_1: the r15 page, section 2.1),
  * then runs the unfused kernel's arithmetic on them. Every workgroup that needs a token's
  * super-block repeats that quantization, so the call is limited to few tokens:
@@ -346,7 +350,8 @@ int mmq_q6K_q8_1_blockdots(int64_t M, int64_t N, int64_t K, const void* q8, cons
  * mmq_plan: the LDS-budget guard as a pure host function (no device access). Chooses the
  * tile for an M x N x K product given `lds_budget` bytes per workgroup (opt->lds_budget,
  * when set, takes precedence): for M <= 16 the decode tile (MMQ_TILE_GEMV, reason
- * MMQ_REASON_DECODE); else, with no workspace, the large tile when it fits and its grid has
+ * MMQ_REASON_DECODE, in the form that enum entry describes, with the compute-unit count as
+ * below); else, with no workspace, the large tile when it fits and its grid has
  * at least opt->min_workgroups workgroups (default 256, the MI355X compute-unit count; a GEMM
  * call uses the device's count); else the cheapest choice under a cost model (rounds of the
  * grid over the compute units times a per-tile cost per super-block, plus the partial

@@ -52,6 +52,10 @@ namespace {
 
 constexpr int kGemvSlices = 64 / kGemvRows;              // K-slices per wavefront
 constexpr int kGemvMfmaScaleBytes = 1280;                // 9-16 tokens: scales per wavefront
+// 9-16 tokens, per wavefront: its super-block's token bytes [16][256], (da, nda) [8][16] and
+// da*sa pieces [3][16][16 bytes]
+constexpr int kGemvTq = 16 * 256, kGemvTda = 8 * 16 * 8, kGemvTpc = 3 * 16 * 16;
+constexpr int kGemvMfmaTokBytes = kGemvTq + kGemvTda + kGemvTpc;
 constexpr int kGemvKS = kGemvSlices * (kGemvWaves / 2);  // K-slices per workgroup (16)
 
 // ONE: K fits one step per slice (at most kGemvKS super-blocks), so no next step is ever
@@ -317,11 +321,15 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
     const int8_t* __restrict__ qs, const float* __restrict__ da_plane,
     const uint16_t* __restrict__ tpieces, const uint8_t* __restrict__ wrep,
     float* __restrict__ C, int M, int N, int K) {
-  __shared__ float red[NW][16][16];  // [wavefront][token][row]
-  // per wavefront: dsv f32 [8 blocks][16 rows], then the dmv pieces bf16 [3][16 rows][8]
+  // LDS: per wavefront its expanded weight scales (dsv f32 [8 blocks][16 rows], then the dmv
+  // pieces bf16 [3][16 rows][8]); the partial sums [wavefront][token][row]; per wavefront its
+  // super-block's token-side operands (gemv_mfma_tok_bytes)
   constexpr int kWsDsv = 8 * 16 * 4;
   static_assert(kWsDsv + 3 * 16 * 8 * 2 == kGemvMfmaScaleBytes, "scale region");
-  __shared__ __align__(16) uint8_t wsc[NW][kGemvMfmaScaleBytes];
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int kRedOff = NW * kGemvMfmaScaleBytes;
+  constexpr int kTokOff = kRedOff + NW * 16 * 16 * 4;
+  float(*red)[16][16] = reinterpret_cast<float(*)[16][16]>(smem + kRedOff);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int u = (int)blockIdx.x;
@@ -338,58 +346,53 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
   const bool t2 = kg < 2;
   const uint8_t* wtile = wrep + (size_t)(rb >> 1) * (size_t)nsb * kRepTileBytes;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wtile, (uint32_t)nsb * (uint32_t)kRepTileBytes);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qs, (uint32_t)M * (uint32_t)K);
-  const __amdgpu_buffer_rsrc_t rda = make_rsrc(da_plane, (uint32_t)M * (uint32_t)(K >> 5) * 8u);
-  const __amdgpu_buffer_rsrc_t rtp = make_rsrc(tpieces, (uint32_t)M * (uint32_t)nsb * 48u);
+  const v4i rq = make_rsrc_sgpr(qs, (uint32_t)M * (uint32_t)K);
+  const v4i rda = make_rsrc_sgpr(da_plane, (uint32_t)M * (uint32_t)(K >> 5) * 8u);
+  const v4i rtp = make_rsrc_sgpr(tpieces, (uint32_t)M * (uint32_t)nsb * 48u);
   v4i bias = {kBiasBits, kBiasBits, kBiasBits, kBiasBits};
   asm volatile("" : "+v"(bias));
 
-  struct Stage {
-    uint2 nb[4];     // nibble bytes of A row j_op, k-group kg, of block pairs 0..3
-    v4i hdr;         // super-block header of row j_op
-    uint2 tb[8];     // token c16, k-group kg, of each block (zero past M)
-    float2 dap[8];   // (da, nda) of token c16 and each block
-    v4i pb[2];       // term2 operands: the da*sa pieces of token c16
+  // The wavefront's token-side operands of super-block s go to its LDS region by
+  // direct-to-LDS loads, 7 instructions instead of one 8-byte load per block and lane:
+  //   tokens [16][256]: 16-byte chunk c of token t at chunk position c ^ t (token t's row
+  //     starts at bank 0 like every other, so the XOR spreads the operand reads of the 16
+  //     tokens over all banks); tokens past M read past the end of q and are zero;
+  //   (da, nda) [8 blocks][16 tokens]; the da*sa pieces [3][16 tokens][8 blocks].
+  // Tokens past M get other rows' scales or zeros: finite, and their columns are not stored.
+  const uint32_t tok = lds_addr(smem) + (uint32_t)(kTokOff + wave * kGemvMfmaTokBytes);
+  const uint8_t* stok = smem + kTokOff + wave * kGemvMfmaTokBytes;
+  auto stage_tokens = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = 64 * i + lane, t = q >> 4, c = (q & 15) ^ t;
+      dma16(rq, tok + i * 1024,
+            (uint32_t)t * (uint32_t)K + (uint32_t)s * 256u + (uint32_t)c * 16u);
+    }
+    dma16(rda, tok + kGemvTq, (((uint32_t)s * 8 + (lane >> 3)) * (uint32_t)M + 2 * (lane & 7)) * 8u);
+    if (lane < 48)
+      dma16(rtp, tok + kGemvTq + kGemvTda,
+            (((uint32_t)s * 3 + (lane >> 4)) * (uint32_t)M + (lane & 15)) * 16u);
   };
-  auto load = [&](int s, Stage& st) {
-    const uint32_t rec = (uint32_t)s * kRepTileBytes;
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      st.nb[g] = __builtin_bit_cast(
-          uint2, buf_load_f32x2(rw, rec + g * 1024 + (kg >> 1) * 512 + j_op * 16 + (kg & 1) * 8));
-    st.hdr = buf_load16(rw, rec + kRepNibBytes + j_op * 16);
-#pragma unroll
-    for (int b = 0; b < 8; ++b)
-      st.tb[b] = __builtin_bit_cast(
-          uint2, buf_load_f32x2(rq, (uint32_t)c16 * (uint32_t)K + (uint32_t)s * 256 + b * 32 +
-                                        kg * 8));
-#pragma unroll
-    for (int b = 0; b < 8; ++b)
-      st.dap[b] = buf_load_f32x2(rda, (((uint32_t)s * 8 + b) * (uint32_t)M + c16) * 8u);
-    st.pb[0] = buf_load16(rtp, (((uint32_t)s * 3 + jb1) * (uint32_t)M + c16) * 16u);
-    st.pb[1] = buf_load16(rtp, (((uint32_t)s * 3 + jb2) * (uint32_t)M + c16) * 16u);
-  };
-  float* sdsv = reinterpret_cast<float*>(wsc[wave]);
-  uint32_t* spc = reinterpret_cast<uint32_t*>(wsc[wave] + kWsDsv);
+  float* sdsv = reinterpret_cast<float*>(smem + wave * kGemvMfmaScaleBytes);
+  uint32_t* spc = reinterpret_cast<uint32_t*>(smem + wave * kGemvMfmaScaleBytes + kWsDsv);
 
   typedef float v4f __attribute__((ext_vector_type(4)));
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  // with 8 wavefronts the next super-block's loads are issued before the current one is
-  // computed; with 16 there is no room for a second stage in 128 registers
-  constexpr bool kPrefetch = NW <= 8;
-  Stage cur, nxt;
-  if (kPrefetch && wave < nsb) load(wave, cur);
   for (int s = wave; s < nsb; s += NW) {
-    if constexpr (kPrefetch) {
-      if (s + NW < nsb) load(s + NW, nxt);
-    } else {
-      load(s, cur);
-    }
+    // weights: nibble bytes of A row j_op, k-group kg, of block pairs 0..3, and its header
+    const uint32_t rec = (uint32_t)s * kRepTileBytes;
+    uint2 nb[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      nb[g] = __builtin_bit_cast(
+          uint2, buf_load_f32x2(rw, rec + g * 1024 + (kg >> 1) * 512 + j_op * 16 + (kg & 1) * 8));
+    const v4i hdr = buf_load16(rw, rec + kRepNibBytes + j_op * 16);
+    stage_tokens(s);
     // weight scales of the super-block: lane (c16, kg) expands sub-blocks 2kg, 2kg + 1 of
     // row c16 of the half tile into the region, after the previous super-block's reads
     {
       float dsv4[4], dmv4[4];
-      q4k_scales(cur.hdr, kg >= 2, dsv4, dmv4);
+      q4k_scales(hdr, kg >= 2, dsv4, dmv4);
       const bool odd = (kg & 1) != 0;
       const float dsv_a = odd ? dsv4[2] : dsv4[0], dsv_b = odd ? dsv4[3] : dsv4[1];
       const float dmv_a = odd ? dmv4[2] : dmv4[0], dmv_b = odd ? dmv4[3] : dmv4[1];
@@ -402,35 +405,44 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
       sdsv[(2 * kg + 1) * 16 + c16] = dsv_b;
 #pragma unroll
       for (int i = 0; i < 3; ++i) spc[(i * 16 + c16) * 4 + kg] = pack_hi16(pa_[i], pb_[i]);
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
     }
+    // this wavefront's direct-to-LDS loads (and every other load) have landed, and the
+    // scale writes are ordered before the reads below
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     const v4i pa0 = *reinterpret_cast<const v4i*>(spc + (ia1 * 16 + c16) * 4);
     const v4i pa1 = t2 ? *reinterpret_cast<const v4i*>(spc + (ia2 * 16 + c16) * 4)
                        : v4i{0, 0, 0, 0};
+    const float2* sdap = reinterpret_cast<const float2*>(stok + kGemvTq);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const uint2 w = cur.nb[b >> 1];
+      const uint2 w = nb[b >> 1];
       const uint2 a = (b & 1) ? make_uint2((w.x >> 4) & 0x0F0F0F0Fu, (w.y >> 4) & 0x0F0F0F0Fu)
                               : make_uint2(w.x & 0x0F0F0F0Fu, w.y & 0x0F0F0F0Fu);
+      const uint2 tb = *reinterpret_cast<const uint2*>(
+          stok + c16 * 256 + (((2 * b + (kg >> 1)) ^ c16) << 4) + (kg & 1) * 8);
       const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, a),
-                                                          __builtin_bit_cast(long, cur.tb[b]),
-                                                          bias, 0, 0, 0);
+                                                          __builtin_bit_cast(long, tb), bias, 0,
+                                                          0, 0);
       const float4 dq = *reinterpret_cast<const float4*>(sdsv + b * 16 + 4 * kg);
       const float dsvb[4] = {dq.x, dq.y, dq.z, dq.w};
+      const float2 dap = sdap[b * 16 + c16];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float y = __builtin_fmaf(__int_as_float(D[r]), cur.dap[b].x, cur.dap[b].y);
+        const float y = __builtin_fmaf(__int_as_float(D[r]), dap.x, dap.y);
         acc[r] = __builtin_fmaf(y, dsvb[r], acc[r]);
       }
     }
+    const v4i pb0 = *reinterpret_cast<const v4i*>(stok + kGemvTq + kGemvTda + (jb1 * 16 + c16) * 16);
+    const v4i pb1 = *reinterpret_cast<const v4i*>(stok + kGemvTq + kGemvTda + (jb2 * 16 + c16) * 16);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, pa0),
-                                                  __builtin_bit_cast(v8bf, cur.pb[0]), acc, 0,
-                                                  0, 0);
+                                                  __builtin_bit_cast(v8bf, pb0), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, pa1),
-                                                  __builtin_bit_cast(v8bf, cur.pb[1]), acc, 0,
-                                                  0, 0);
-    if constexpr (kPrefetch) cur = nxt;
+                                                  __builtin_bit_cast(v8bf, pb1), acc, 0, 0, 0);
+    // every read of this super-block's regions is done before the next one's loads overwrite
+    // them (the scales are rewritten after the fence at the top of the next expansion)
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
 #pragma unroll
@@ -453,7 +465,8 @@ hipError_t launch_mt(const void* q8, const void* w_rep, float* C, int64_t M, int
                      hipStream_t s) {
   const uint8_t* base = static_cast<const uint8_t*>(q8);
   const int64_t groups = (M + MT - 1) / MT;
-  hipLaunchKernelGGL((mmq_gemv_kernel<MT, false, ONE>), dim3((unsigned)gemv_grid(M, N)),
+  hipLaunchKernelGGL((mmq_gemv_kernel<MT, false, ONE>),
+                     dim3((unsigned)((N + kGemvRows - 1) / kGemvRows * groups)),
                      dim3(kGemvWaves * 64), 0, s, reinterpret_cast<const int8_t*>(base),
                      reinterpret_cast<const uint32_t*>(base + M * K),
                      reinterpret_cast<const float*>(base + q8_planes_offset(M, K)), nullptr,
@@ -465,7 +478,8 @@ template <int MT, bool ONE>
 hipError_t launch_fused_mt(const float* x, const void* w_rep, float* C, int64_t M, int64_t N,
                            int64_t K, hipStream_t s) {
   const int64_t groups = (M + MT - 1) / MT;
-  hipLaunchKernelGGL((mmq_gemv_kernel<MT, true, ONE>), dim3((unsigned)gemv_grid(M, N)),
+  hipLaunchKernelGGL((mmq_gemv_kernel<MT, true, ONE>),
+                     dim3((unsigned)((N + kGemvRows - 1) / kGemvRows * groups)),
                      dim3(kGemvWaves * 64), 0, s, nullptr, nullptr, nullptr,
                      reinterpret_cast<const float4*>(x), static_cast<const uint8_t*>(w_rep), C,
                      (int)M, (int)N, (int)K, (int)groups);
@@ -475,26 +489,41 @@ hipError_t launch_fused_mt(const float* x, const void* w_rep, float* C, int64_t 
 }  // namespace
 
 // tokens per workgroup for M tokens: 1, 2, 4, then groups of 8
-int64_t gemv_group(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 8 : 16))); }
+bool gemv_mfma_form(int64_t M, int64_t N, int64_t compute_units) {
+  return M > kGemvDotMaxM ||
+         (M >= kGemvMfmaMinM && (N + kGemvRows - 1) / kGemvRows <= compute_units);
+}
 
-int64_t gemv_lds_bytes(int64_t M) {
-  // the matrix-unit form: the partial sums, and per wavefront its expanded weight scales
-  if (M > kGemvDotMaxM) return kGemvMfmaWaves * (16 * 16 * 4 + kGemvMfmaScaleBytes);
-  const int64_t mt = gemv_group(M);
+// tokens per workgroup of the vector-ALU form
+static int64_t gemv_dot_group(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8)); }
+
+int64_t gemv_group(int64_t M, bool mfma) { return mfma ? kGemvMaxM : gemv_dot_group(M); }
+
+int64_t gemv_lds_bytes(int64_t M, bool mfma) {
+  // the matrix-unit form: per wavefront its expanded weight scales, its partial sums and its
+  // super-block's token-side operands
+  if (mfma) return kGemvMfmaWaves * (16 * 16 * 4 + kGemvMfmaScaleBytes + kGemvMfmaTokBytes);
+  const int64_t mt = gemv_dot_group(M);
   return (int64_t)kGemvWaves * kGemvSlices * (mt * 160 + 16);
 }
 
-int64_t gemv_grid(int64_t M, int64_t N) {
-  return (N + kGemvRows - 1) / kGemvRows * ((M + gemv_group(M) - 1) / gemv_group(M));
+int64_t gemv_grid(int64_t M, int64_t N, bool mfma) {
+  const int64_t g = gemv_group(M, mfma);
+  return (N + kGemvRows - 1) / kGemvRows * ((M + g - 1) / g);
 }
 
 hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
-                           int64_t K, hipStream_t s) {
-  if (M < 1 || M > kGemvMaxM) return hipErrorInvalidValue;
-  if (M > kGemvDotMaxM) {
+                           int64_t K, bool mfma, hipStream_t s) {
+  if (M < 1 || M > kGemvMaxM || (!mfma && M > kGemvDotMaxM)) return hipErrorInvalidValue;
+  if (mfma) {
     const uint8_t* base = static_cast<const uint8_t*>(q8);
-    hipLaunchKernelGGL(mmq_gemv_mfma_kernel<kGemvMfmaWaves>, dim3((unsigned)gemv_grid(M, N)),
-                       dim3(64 * kGemvMfmaWaves), 0, s,
+    const int64_t lds = gemv_lds_bytes(M, true);
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(mmq_gemv_mfma_kernel<kGemvMfmaWaves>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mmq_gemv_mfma_kernel<kGemvMfmaWaves>, dim3((unsigned)gemv_grid(M, N, true)),
+                       dim3(64 * kGemvMfmaWaves), (size_t)lds, s,
                        reinterpret_cast<const int8_t*>(base),
                        reinterpret_cast<const float*>(base + q8_planes_offset(M, K)),
                        reinterpret_cast<const uint16_t*>(base + q8_pieces_offset(M, K)),
@@ -504,7 +533,7 @@ hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t 
   // one step per slice: the single-stage form for 1 and 2 tokens (at 4 and 8 tokens it would
   // spill)
   const bool one = K / 256 <= kGemvKS;
-  switch (gemv_group(M)) {
+  switch (gemv_dot_group(M)) {
     case 1: return one ? launch_mt<1, true>(q8, w_rep, C, M, N, K, s)
                        : launch_mt<1, false>(q8, w_rep, C, M, N, K, s);
     case 2: return one ? launch_mt<2, true>(q8, w_rep, C, M, N, K, s)
@@ -518,7 +547,7 @@ hipError_t launch_mmq_gemv_fused(const float* x, const void* w_rep, float* C, in
                                  int64_t N, int64_t K, hipStream_t s) {
   if (M < 1 || M > kGemvFusedMaxM) return hipErrorInvalidValue;
   // the single-stage form for one token (80 VGPRs; at two tokens it would spill)
-  switch (gemv_group(M)) {
+  switch (gemv_dot_group(M)) {
     case 1: return K / 256 <= kGemvKS ? launch_fused_mt<1, true>(x, w_rep, C, M, N, K, s)
                                       : launch_fused_mt<1, false>(x, w_rep, C, M, N, K, s);
     case 2: return launch_fused_mt<2, false>(x, w_rep, C, M, N, K, s);

@@ -140,27 +140,35 @@ int64_t fused_lds_bytes();
 hipError_t launch_mmq_fused(const float* x, const void* w_rep, float* C, int64_t M, int64_t N,
                             int64_t K, hipStream_t s);
 
-// Product for a handful of tokens (decode), M <= kGemvMaxM, 16 weight rows per workgroup of
-// kGemvWaves wavefronts. Up to 8 tokens: integer dot products on the vector ALU, up to 8
-// tokens per workgroup, K split over 16 slices and each super-block over two wavefronts.
-// 9 to 16 tokens: one 16 x 16 x 32 int8 MFMA per block, all tokens in one workgroup, K split
-// over the wavefronts by super-block.
+// Product for a handful of tokens (decode), M <= kGemvMaxM, 16 weight rows per workgroup, in
+// two forms. The vector-ALU form (kGemvWaves wavefronts, up to 8 tokens): integer dot
+// products on the vector ALU, up to 8 tokens per workgroup, K split over 16 slices and each
+// super-block over two wavefronts. The matrix-unit form (kGemvMfmaWaves wavefronts, up to 16
+// tokens): one 16 x 16 x 32 int8 MFMA per block, all tokens in one workgroup, K split over
+// the wavefronts by super-block.
 constexpr int kGemvWaves = 8;
 constexpr int kGemvRows = 16;  // weight rows per workgroup
 constexpr int kGemvMaxM = 16;
-constexpr int kGemvMfmaWaves = 16;  // wavefronts per workgroup of the 9-16 token form
-// The guard's choice up to here (at 16 tokens, K = N = 4096: 10.4 against the skinny
-// kernel's 11.6 us).
+constexpr int kGemvMfmaWaves = 16;  // wavefronts per workgroup of the matrix-unit form
+// The guard's choice up to here (at 16 tokens, K = N = 4096: 5.9 against the skinny
+// kernel's 9.6 us).
 constexpr int kGemvAutoMaxM = 16;
-// The vector-ALU form up to here, the matrix-unit form above.
+// The vector-ALU form serves at most this many tokens.
 constexpr int kGemvDotMaxM = 8;
+// From this many tokens the matrix-unit form is taken when its grid (one workgroup of 16
+// wavefronts and 128 KiB of LDS per compute unit) runs in one round: graph-replayed at
+// K = N = 4096 it takes 5.5-5.6 us for 4 to 8 tokens against the vector-ALU form's 5.6 (4),
+// 6.5 (5) and 7.2 us (8); at N = 11008 (three rounds) 13.5 us against 7.7-13.9.
+constexpr int kGemvMfmaMinM = 5;
 // The variant that quantizes its activations itself: vector-ALU form only.
 constexpr int kGemvFusedMaxM = kGemvDotMaxM;
-int64_t gemv_group(int64_t M);  // tokens per workgroup
-int64_t gemv_lds_bytes(int64_t M);
-int64_t gemv_grid(int64_t M, int64_t N);
+// The form the guard takes for M tokens and N rows on a device of compute_units.
+bool gemv_mfma_form(int64_t M, int64_t N, int64_t compute_units);
+int64_t gemv_group(int64_t M, bool mfma);  // tokens per workgroup
+int64_t gemv_lds_bytes(int64_t M, bool mfma);
+int64_t gemv_grid(int64_t M, int64_t N, bool mfma);
 hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
-                           int64_t K, hipStream_t s);
+                           int64_t K, bool mfma, hipStream_t s);
 // The same kernel quantizing its own f32 activations (same LDS, grid and threads).
 hipError_t launch_mmq_gemv_fused(const float* x, const void* w_rep, float* C, int64_t M,
                                  int64_t N, int64_t K, hipStream_t s);

@@ -180,23 +180,38 @@ def test_blockdots_refuse_the_gemv_tile():
                         ctypes.byref(opt)) == mmq.MMQ_E_ARG
 
 
-@pytest.mark.parametrize("M,group,grid", [(1, 1, 256), (2, 2, 256), (3, 4, 256), (4, 4, 256),
-                                          (5, 8, 256), (8, 8, 256), (9, 16, 256), (16, 16, 256)])
-def test_plan_gemv_tile(M, group, grid):
-    auto = mmq.mmq_plan(M, 4096, 4096, 160 * 1024)
-    assert (auto["tile"], auto["reason"]) == ((GEMV, mmq.MMQ_REASON_DECODE) if M <= 16 else
-                                              (SKINNY, mmq.MMQ_REASON_FEW_TOKENS))
-    p = mmq.mmq_plan(M, 4096, 4096, 160 * 1024, force_tile=GEMV)
+MFMA_GEMV_LDS = 16 * (16 * 16 * 4 + 512 + 768 + 16 * 256 + 8 * 16 * 8 + 3 * 16 * 16)
+
+
+@pytest.mark.parametrize("M,N,group,grid", [
+    (1, 4096, 1, 256), (2, 4096, 2, 256), (3, 4096, 4, 256), (4, 4096, 4, 256),
+    (5, 4096, 16, 256), (8, 4096, 16, 256),     # 5-8 tokens, one round: the matrix-unit form
+    (5, 4097, 8, 257), (8, 11008, 8, 688),      # more row blocks than compute units: vector ALU
+    (9, 4096, 16, 256), (16, 4096, 16, 256), (9, 4097, 16, 257), (16, 11008, 16, 688)])
+def test_plan_gemv_tile(M, N, group, grid):
+    auto = mmq.mmq_plan(M, N, 4096, 160 * 1024)
+    assert (auto["tile"], auto["reason"]) == (GEMV, mmq.MMQ_REASON_DECODE)
+    p = mmq.mmq_plan(M, N, 4096, 160 * 1024, force_tile=GEMV)
     assert p["tile"] == GEMV
     assert p["block_m"] == group and p["block_n"] == 16
     assert p["threads"] == (512 if group <= 8 else 1024)
-    # up to 8 tokens, per wavefront and K-slice: its half's 128 token bytes and 4 (da, sa)
-    # pairs per token, 16 padding; from 9 tokens (the matrix-unit form) per wavefront its
-    # partial sums and its expanded weight scales (dsv [8][16] f32, dmv pieces [3][16][8])
-    lds = 8 * 4 * (160 * group + 16) if group <= 8 else 16 * (16 * 16 * 4 + 512 + 768)
+    # the vector-ALU form, per wavefront and K-slice: its half's 128 token bytes and 4
+    # (da, sa) pairs per token, 16 padding; the matrix-unit form, per wavefront: its partial
+    # sums, its expanded weight scales (dsv [8][16] f32, dmv pieces [3][16][8]) and its
+    # super-block's token bytes [16][256], (da, nda) pairs [8][16] and pieces [3][16][8]
+    lds = 8 * 4 * (160 * group + 16) if group <= 8 else MFMA_GEMV_LDS
     assert p["lds_bytes"] == lds and p["grid"] == grid
-    # ragged N: 4097 rows make 257 blocks of 16
-    assert mmq.mmq_plan(M, 4097, 256, 160 * 1024, force_tile=GEMV)["grid"] == 257 * (grid // 256)
+
+
+def test_plan_gemv_form_falls_back_within_the_budget():
+    """5-8 tokens take the vector-ALU form where the matrix-unit form's LDS does not fit."""
+    p = mmq.mmq_plan(8, 4096, 4096, 160 * 1024, opt_lds_budget=MFMA_GEMV_LDS - 1)
+    assert p["tile"] == GEMV and p["threads"] == 512 and p["lds_bytes"] == 8 * 4 * (160 * 8 + 16)
+    p = mmq.mmq_plan(8, 4096, 4096, 160 * 1024, opt_lds_budget=MFMA_GEMV_LDS)
+    assert p["tile"] == GEMV and p["threads"] == 1024
+    # from 9 tokens only the matrix-unit form serves: below its LDS another tile is taken
+    p = mmq.mmq_plan(9, 4096, 4096, 160 * 1024, opt_lds_budget=MFMA_GEMV_LDS - 1)
+    assert p["tile"] != GEMV
 
 
 def test_plan_above_decode_tile_is_skinny():
@@ -212,7 +227,7 @@ def test_plan_gemv_forced_limits():
         mmq.mmq_plan(17, 4096, 4096, 160 * 1024, force_tile=GEMV)
     assert e.value.status == mmq.MMQ_E_SHAPE
     with pytest.raises(mmq.MMQError) as e:
-        mmq.mmq_plan(8, 4096, 4096, 160 * 1024, force_tile=GEMV, opt_lds_budget=41471)
+        mmq.mmq_plan(8, 8192, 4096, 160 * 1024, force_tile=GEMV, opt_lds_budget=41471)
     assert e.value.status == mmq.MMQ_E_LDS
     # the vector-ALU tile needs the least LDS: under 6 KiB it is the only one that fits
     p = mmq.mmq_plan(1, 4096, 4096, 160 * 1024, opt_lds_budget=5632)

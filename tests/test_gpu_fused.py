@@ -1,10 +1,10 @@
 """The quantize-fused product for few tokens, mmq_q4K_f32, through the C ABI (needs a GPU).
 
 Bars:
-- C bit for bit equal to quantize_q8_1 followed by mmq_q4K_q8_1_ex with the tile the fused
-  call uses: the vector-ALU tile for M <= 8, the skinny tile above (each fused kernel
-  quantizes with the prepass's arithmetic and then does its unfused twin's arithmetic in the
-  same order);
+- C bit for bit equal to quantize_q8_1 followed by mmq_q4K_q8_1_ex with the kernel the fused
+  call uses: the decode tile's vector-ALU form for M <= 8 (taken under an LDS budget below
+  the matrix-unit form's), the skinny tile above (each fused kernel quantizes with the
+  prepass's arithmetic and then does its unfused twin's arithmetic in the same order);
 - within 1e-5 * T of the oracle, as for the unfused product.
 Shapes cover one and several token tiles, ragged M and N, K of one super-block (most
 wavefronts of a workgroup get no super-block) and K with super-blocks that do not divide
@@ -37,11 +37,18 @@ def fused_tile(M):
     return mmq.MMQ_TILE_GEMV if M <= 8 else mmq.MMQ_TILE_SKINNY
 
 
+# an LDS budget one byte below the decode tile's matrix-unit form leaves up to 8 tokens to its
+# vector-ALU form, the unfused twin of the fused kernel
+VALU_FORM_BUDGET = mmq.mmq_plan(9, 160, 1024, 160 * 1024, force_tile=mmq.MMQ_TILE_GEMV)[
+    "lds_bytes"] - 1
+
+
 def two_step(x_dev, M, N, K, rep):
     q8 = torch.zeros(mmq.mmq_q8_1_bytes(M, K), dtype=torch.uint8, device="cuda")
     mmq.quantize_q8_1(x_dev, M, K, q8)
     C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
-    mmq.mmq_q4K_q8_1_ex(M, N, K, q8, rep, C, force_tile=fused_tile(M))
+    mmq.mmq_q4K_q8_1_ex(M, N, K, q8, rep, C, force_tile=fused_tile(M),
+                        lds_budget=VALU_FORM_BUDGET if M <= 8 else 0)
     torch.cuda.synchronize()
     return C.cpu().numpy()
 

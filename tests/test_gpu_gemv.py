@@ -1,9 +1,10 @@
-"""The vector-ALU tile for a handful of tokens (MMQ_TILE_GEMV) against the CPU oracle.
+"""The decode tile for a handful of tokens (MMQ_TILE_GEMV) against the CPU oracle.
 
 Bar: f32 outputs within 1e-5 * T per element (T from the oracle, float64), every element;
-results deterministic. The tile is the guard's choice for M <= 16 (vector-ALU dot products up
-to M = 8, a 16 x 16 int8 MFMA per block from M = 9), so the token sweep's M = 1 and M = 16
-shapes run through it by default.
+results deterministic. The tile is the guard's choice for M <= 16, in two forms: vector-ALU
+dot products (up to M = 4, and up to M = 8 when the rows need more than one round of
+workgroups) and a 16 x 16 int8 MFMA per block (from M = 9, and from M = 5 within one round),
+so the token sweep's M = 1 and M = 16 shapes run through it by default.
 """
 import numpy as np
 import pytest
@@ -28,13 +29,14 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _check(M, N, K, seed, kind="normal_outliers", wkind="random_fields", force=GEMV):
+def _check(M, N, K, seed, kind="normal_outliers", wkind="random_fields", force=GEMV,
+           lds_budget=0):
     x = synth.activations(kind, M, K, seed)
     w, _ = synth.q4k_weights(wkind, N, K, seed + 1)
     q8 = gpu_quantize(x)
     rep = gpu_repack(w, N, K)
-    say("gemv", (M, N, K), "seed", seed)
-    C = gpu_mmq(M, N, K, q8, rep, force_tile=force)
+    say("gemv", (M, N, K), "seed", seed, "lds budget", lds_budget)
+    C = gpu_mmq(M, N, K, q8, rep, force_tile=force, lds_budget=lds_budget)
     info = mmq.mmq_last_kernel()
     assert info["tile"] == GEMV
     q = oracle.quantize_q8_1(x)
@@ -68,6 +70,21 @@ def test_gemv_every_token_count(M):
     C, info = _check(M, 160, 1024, 100 + M)
     assert info["block_m"] == mmq.mmq_plan(M, 160, 1024, 160 * 1024, force_tile=GEMV)["block_m"]
     assert info["block_m"] >= min(M, 4)
+
+
+# LDS of the matrix-unit form; one byte less leaves 5-8 tokens to the vector-ALU form
+MFMA_FORM_LDS = mmq.mmq_plan(8, 160, 1024, 160 * 1024, force_tile=GEMV)["lds_bytes"]
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 160, 1024), (6, 96, 2816), (7, 4097, 256),
+                                   (8, 70, 11008)])
+def test_gemv_both_forms_from_5_to_8_tokens(M, N, K):
+    """5 to 8 tokens run in either form, by the guard's choice of form: the matrix-unit form
+    when its grid runs in one round and fits the LDS, else the vector-ALU form."""
+    a, ia = _check(M, N, K, 300 + M)
+    b, ib = _check(M, N, K, 300 + M, lds_budget=MFMA_FORM_LDS - 1)
+    assert ib["threads"] == 512 and ib["block_m"] == 8
+    assert ia["threads"] == (1024 if (N + 15) // 16 <= 256 else 512)
 
 
 @pytest.mark.parametrize("M,N,K", [

@@ -22,7 +22,7 @@ _spec = importlib.util.spec_from_file_location(
 build = importlib.util.module_from_spec(_spec)
 _spec.loader.exec_module(build)
 
-USERS = ["mmq_gemm.hip"]   # the sources that call dma16
+USERS = ["mmq_gemm.hip", "mmq_gemv.hip"]   # the sources that call dma16
 M0 = re.compile(r"\bm0\b")
 
 
