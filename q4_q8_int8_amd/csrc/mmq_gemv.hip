@@ -297,23 +297,22 @@ __global__ __launch_bounds__(kGemvWaves * 64, ONE ? 6 : 1) void mmq_gemv_kernel(
   }
 }
 
-// 9 to 16 tokens: the vector ALU's dot products set the time there, so one 32-block of 16
-// weight rows x 16 tokens becomes one v_mfma_i32_16x16x32_i8 (no padding at 16 tokens; the
-// columns of tokens past M are computed from in-bounds or zero reads and never stored). A
-// workgroup of NW wavefronts owns 16 weight rows (paired on one XCD as above) and all of K;
-// wavefront w takes the super-blocks w, w + NW, w + 2 NW, ... With 8 wavefronts each
-// super-block's loads are issued before the previous one is computed; the launch uses 16
-// (66 registers, no second stage), 1-3 % faster at K = 4096 and 11008, where a wavefront has
-// one or three super-blocks. Per block a lane holds, for its token
-// l % 16, the four outputs of rows 4 (l / 16) .. + 3, and rescales them as the GEMM does:
-// y = fma(D, da, nda) with D biased by 0x4B400000, acc = fma(y, dsv, acc). term2 of a
-// super-block is a K = 8 product of dmv and da*sa; as in the GEMM it runs on the bf16 matrix
-// unit from exact three-piece splits, those of da*sa stored in the q8 buffer, those of dmv
-// (bf16_trunc3) expanded from the row headers into the wavefront's LDS region (with dsv) per
-// super-block, lane (c, g) taking sub-blocks 2g and 2g + 1 of row c: two
-// v_mfma_f32_16x16x32_bf16 whose 4 k-groups of 8 blocks carry the piece pairs (0,0) (0,1)
-// (1,0) (0,2) | (1,1) (2,0) (and two zero groups), added into the same accumulator. The NW
-// wavefronts' partial sums are added in wavefront order through LDS.
+// The matrix-unit form (9 to 16 tokens, and from 5 where its grid runs in one round): the
+// vector ALU's dot products set the time there, so one 32-block of 16 weight rows x 16
+// tokens becomes one v_mfma_i32_16x16x32_i8 (no padding at 16 tokens; the columns of tokens
+// past M are computed from in-bounds or zero reads and never stored). A workgroup of NW
+// wavefronts owns 16 weight rows (paired on one XCD as above) and all of K; wavefront w takes
+// the super-blocks w, w + NW, w + 2 NW, ..., loading each one's weights into registers and
+// its token-side operands into its own LDS region (seven direct-to-LDS loads), then computing
+// it. Per block a lane holds, for its token l % 16, the four outputs of rows 4 (l / 16) .. + 3,
+// and rescales them as the GEMM does: y = fma(D, da, nda) with D biased by 0x4B400000,
+// acc = fma(y, dsv, acc). term2 of a super-block is a K = 8 product of dmv and da*sa; as in
+// the GEMM it runs on the bf16 matrix unit from exact three-piece splits, those of da*sa
+// stored in the q8 buffer, those of dmv (bf16_trunc3) expanded from the row headers into the
+// wavefront's LDS region (with dsv) per super-block, lane (c, g) taking sub-blocks 2g and
+// 2g + 1 of row c: two v_mfma_f32_16x16x32_bf16 whose 4 k-groups of 8 blocks carry the piece
+// pairs (0,0) (0,1) (1,0) (0,2) | (1,1) (2,0) (and two zero groups), added into the same
+// accumulator. The NW wavefronts' partial sums are added in wavefront order through LDS.
 // Operand layout of both instructions: A row l % 16 and B column l % 16 take the 8 k values
 // 8 (l / 16) .. + 7; the result of row 4 (l / 16) + r, column l % 16 is register r of lane l.
 template <int NW>
