@@ -32,6 +32,9 @@ extern "C" int mmq_q4K_q8_1_static(int64_t M, int64_t N, int64_t K, const void* 
   if (st) return st;
   if (opt && (opt->workspace || opt->workspace_bytes))
     return mmq::api_fail(MMQ_E_ARG, "mmq_q4K_q8_1_static uses its own scratch: pass no workspace");
+  if (opt && opt->splits > K / 256)
+    return mmq::api_fail(MMQ_E_ARG, "splits is more than the super-blocks of K");
+  // at most K/256 <= 2^16 splits of an output below 2^40 elements: the product fits 64 bits
   if (opt && opt->splits > 1 && opt->splits * M * N * 4 > kScratchBytes)
     return mmq::api_fail(MMQ_E_ARG, "the forced splits' partial planes exceed the 32 MiB scratch "
                                     "of mmq_q4K_q8_1_static");

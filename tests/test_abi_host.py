@@ -521,6 +521,12 @@ def test_static_entry_refuses_a_workspace_and_oversized_splits():
     assert mmq.raw_call("mmq_q4K_q8_1_static", 256, 16384, 1024, A, B, Cp, None,
                         ctypes.byref(opt)) == mmq.MMQ_E_ARG
     assert "32 MiB" in mmq.mmq_last_error()
+    # more splits than super-blocks, on the largest output: refused before any device access
+    # (and before the size of their planes is formed)
+    opt = mmq.mmq_options(mmq.MMQ_TILE_MEDIUM, 0, 0, None, 0, (1 << 31) - 1, 0)
+    assert mmq.raw_call("mmq_q4K_q8_1_static", 1 << 20, 1 << 20, 1024, A, B, Cp, None,
+                        ctypes.byref(opt)) == mmq.MMQ_E_ARG
+    assert "super-blocks" in mmq.mmq_last_error()
 
 
 def test_static_entry_reaches_the_device_check():
