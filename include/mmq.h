@@ -63,14 +63,17 @@ enum mmq_tile {
                           wavefronts and summed in wavefront order (no block-dot output) */
   MMQ_TILE_GEMV = 4,   /* M <= 16 only (decode), 16 output features per workgroup, partial
                           sums added in a fixed order, no block-dot output, in two forms.
-                          Vector-ALU form (threads = 512): 8 wavefronts, up to 8 tokens per
-                          workgroup, integer dot products on the vector ALU (v_dot4_i32_i8), K
-                          split over 16 slices x 2 halves of each super-block; taken for M <= 4,
-                          and for 5 <= M <= 8 when ceil(N/16) exceeds the compute units or the
-                          LDS budget is below the other form's. Matrix-unit form (threads =
-                          1024, 128 KiB of LDS): 16 wavefronts, all tokens in one workgroup, one
-                          v_mfma_i32_16x16x32_i8 per block, K split over the wavefronts by
-                          super-block; taken for 9 <= M <= 16, and for 5 <= M <= 8 otherwise */
+                          Vector-ALU form (threads = 512, block_m <= 8): 8 wavefronts, up to 8
+                          tokens per workgroup, integer dot products on the vector ALU
+                          (v_dot4_i32_i8), K split over 16 slices x 2 halves of each
+                          super-block; taken for M <= 4, and for 5 <= M <= 8 when the LDS budget
+                          is below the other form's. Matrix-unit form (block_m = 16): all tokens
+                          in one workgroup, one v_mfma_i32_16x16x32_i8 per block, K split over
+                          the wavefronts by super-block, each loading its next super-block's
+                          weights while it computes one; 16 wavefronts (threads = 1024, 128 KiB
+                          of LDS) when ceil(N/16) workgroups fit the compute units once, 8
+                          (512 threads, 64 KiB) when they fit twice, else 4 (256, 32 KiB);
+                          taken for 5 <= M <= 16 */
   MMQ_TILE_MEDIUM = 5, /* 32 tokens x 256 output features per workgroup, 8 wavefronts (the
                           template of the large and small tiles); with a workspace, K may be
                           split over workgroups (split-K, see mmq_options) */

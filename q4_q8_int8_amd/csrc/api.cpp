@@ -210,10 +210,15 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
   int64_t splits = forced_splits > 0 ? forced_splits : 1;
 
   int tile = 0, reason = MMQ_REASON_NONE, fallback = 0;
-  // the decode tile's form: up to kGemvDotMaxM tokens the matrix-unit form only where it
-  // fits the budget (the vector-ALU form needs far less LDS)
-  const bool gemv_mfma = mmq::gemv_mfma_form(M, N, compute_units) &&
-                         (M > mmq::kGemvDotMaxM || mmq::gemv_lds_bytes(M, true) <= budget);
+  // the decode tile's form (0: vector ALU, else the matrix-unit form's wavefronts): up to
+  // kGemvDotMaxM tokens the matrix-unit form only where it fits the budget (the vector-ALU
+  // form needs far less LDS)
+  const int mfma_waves = mmq::gemv_mfma_waves(N, compute_units);
+  const int gemv_form =
+      mmq::gemv_mfma_form(M) &&
+              (M > mmq::kGemvDotMaxM || mmq::gemv_lds_bytes(M, mfma_waves) <= budget)
+          ? mfma_waves
+          : 0;
   if (forced == MMQ_TILE_LARGE) {
     if (need_large <= budget) { tile = MMQ_TILE_LARGE; reason = MMQ_REASON_FORCED; }
   } else if (forced == MMQ_TILE_SMALL) {
@@ -228,10 +233,10 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
     if (M > mmq::kGemvMaxM)
       return fail(MMQ_E_SHAPE, "the decode tile takes M <= %d (M = %lld)", mmq::kGemvMaxM,
                   (long long)M);
-    if (mmq::gemv_lds_bytes(M, gemv_mfma) <= budget) {
+    if (mmq::gemv_lds_bytes(M, gemv_form) <= budget) {
       tile = MMQ_TILE_GEMV; reason = MMQ_REASON_FORCED;
     }
-  } else if (!q6 && M <= mmq::kGemvAutoMaxM && mmq::gemv_lds_bytes(M, gemv_mfma) <= budget) {
+  } else if (!q6 && M <= mmq::kGemvAutoMaxM && mmq::gemv_lds_bytes(M, gemv_form) <= budget) {
     tile = MMQ_TILE_GEMV; reason = MMQ_REASON_DECODE;
   } else if (need_large <= budget) {
     // the cheapest (tile, splits) under the cost model: splits only with a workspace that
@@ -290,11 +295,11 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
   if (splits > 1 && !template_tile(tile))
     splits = 1;  // (an LDS fallback to another kind of kernel drops a forced split)
   if (tile == MMQ_TILE_GEMV) {
-    info->block_m = (int32_t)mmq::gemv_group(M, gemv_mfma);
+    info->block_m = (int32_t)mmq::gemv_group(M, gemv_form);
     info->block_n = mmq::kGemvRows;
-    info->threads = 64 * (gemv_mfma ? mmq::kGemvMfmaWaves : mmq::kGemvWaves);
-    info->lds_bytes = mmq::gemv_lds_bytes(M, gemv_mfma);
-    info->grid = mmq::gemv_grid(M, N, gemv_mfma);
+    info->threads = 64 * (gemv_form ? gemv_form : mmq::kGemvWaves);
+    info->lds_bytes = mmq::gemv_lds_bytes(M, gemv_form);
+    info->grid = mmq::gemv_grid(M, N, gemv_form);
     return MMQ_OK;
   }
   if (tile == MMQ_TILE_SKINNY) {
@@ -342,9 +347,10 @@ int launch_planned(const mmq_kernel_info& info, int64_t M, int64_t N, int64_t K,
                    hipStream_t stream, int fmt = mmq::kFmtQ4K) {
   hipError_t e;
   if (info.tile == MMQ_TILE_GEMV) {
-    // the form the guard chose (the matrix-unit form runs kGemvMfmaWaves wavefronts)
-    e = mmq::launch_mmq_gemv(q8, w_rep, C, M, N, K, info.threads == 64 * mmq::kGemvMfmaWaves,
-                             stream);
+    // the form the guard chose: the matrix-unit form takes all tokens in one workgroup, with
+    // threads / 64 wavefronts
+    e = mmq::launch_mmq_gemv(q8, w_rep, C, M, N, K,
+                             info.block_m == mmq::kGemvMaxM ? info.threads / 64 : 0, stream);
   } else if (info.tile == MMQ_TILE_SKINNY) {
     e = mmq::launch_mmq_skinny(q8, w_rep, C, M, N, K, compute_units, stream);
   } else {
@@ -556,11 +562,11 @@ int mmq_q4K_f32(int64_t M, int64_t N, int64_t K, const float* x, const void* w_r
   info.lds_budget = di->lds_budget;
   if (gemv) {
     info.tile = MMQ_TILE_GEMV;
-    info.block_m = (int32_t)mmq::gemv_group(M, false);
+    info.block_m = (int32_t)mmq::gemv_group(M, 0);
     info.block_n = mmq::kGemvRows;
     info.threads = 64 * mmq::kGemvWaves;
-    info.lds_bytes = mmq::gemv_lds_bytes(M, false);
-    info.grid = mmq::gemv_grid(M, N, false);
+    info.lds_bytes = mmq::gemv_lds_bytes(M, 0);
+    info.grid = mmq::gemv_grid(M, N, 0);
   } else {
     info.tile = MMQ_TILE_SKINNY;
     info.block_m = 32;

@@ -297,14 +297,19 @@ __global__ __launch_bounds__(kGemvWaves * 64, ONE ? 6 : 1) void mmq_gemv_kernel(
   }
 }
 
-// The matrix-unit form (9 to 16 tokens, and from 5 where its grid runs in one round): the
-// vector ALU's dot products set the time there, so one 32-block of 16 weight rows x 16
-// tokens becomes one v_mfma_i32_16x16x32_i8 (no padding at 16 tokens; the columns of tokens
-// past M are computed from in-bounds or zero reads and never stored). A workgroup of NW
-// wavefronts owns 16 weight rows (paired on one XCD as above) and all of K; wavefront w takes
-// the super-blocks w, w + NW, w + 2 NW, ..., loading each one's weights into registers and
-// its token-side operands into its own LDS region (seven direct-to-LDS loads), then computing
-// it. Per block a lane holds, for its token l % 16, the four outputs of rows 4 (l / 16) .. + 3,
+// The matrix-unit form (from 5 tokens to 16): the vector ALU's dot products set the time
+// there, so one 32-block of 16 weight rows x 16 tokens becomes one v_mfma_i32_16x16x32_i8 (no
+// padding at 16 tokens; the columns of tokens past M are computed from in-bounds or zero reads
+// and never stored). A workgroup of NW wavefronts owns 16 weight rows (paired on one XCD as
+// above) and all of K; wavefront w takes the super-blocks w, w + NW, w + 2 NW, ..., each
+// one's weights in registers and its token-side operands in the wavefront's own LDS region
+// (six direct-to-LDS loads), then computes it. The weights of the wavefront's next
+// super-block are loaded while it computes this one. NW is 16 where the N / 16 workgroups fit
+// the compute units once (a workgroup takes 128 KiB of LDS, so one per unit), 8 where they fit
+// twice and 4 beyond: with 16 wavefronts at N = 11008 the grid took three rounds, and every
+// workgroup stages all of K's token operands (5.9 KB per super-block, 2.5x the bytes of its
+// weights), so more workgroups at once beat more wavefronts per workgroup there.
+// Per block a lane holds, for its token l % 16, the four outputs of rows 4 (l / 16) .. + 3,
 // and rescales them as the GEMM does: y = fma(D, da, nda) with D biased by 0x4B400000,
 // acc = fma(y, dsv, acc). term2 of a super-block is a K = 8 product of dmv and da*sa; as in
 // the GEMM it runs on the bf16 matrix unit from exact three-piece splits, those of da*sa
@@ -320,9 +325,10 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
     const int8_t* __restrict__ qs, const float* __restrict__ da_plane,
     const uint16_t* __restrict__ tpieces, const uint8_t* __restrict__ wrep,
     float* __restrict__ C, int M, int N, int K) {
+  static_assert(NW >= 4, "the final sum takes 256 work-items");
   // LDS: per wavefront its expanded weight scales (dsv f32 [8 blocks][16 rows], then the dmv
   // pieces bf16 [3][16 rows][8]); the partial sums [wavefront][token][row]; per wavefront its
-  // super-block's token-side operands (gemv_mfma_tok_bytes)
+  // super-block's token-side operands (kGemvMfmaTokBytes)
   constexpr int kWsDsv = 8 * 16 * 4;
   static_assert(kWsDsv + 3 * 16 * 8 * 2 == kGemvMfmaScaleBytes, "scale region");
   extern __shared__ __align__(16) uint8_t smem[];
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
   asm volatile("" : "+v"(bias));
 
   // The wavefront's token-side operands of super-block s go to its LDS region by
-  // direct-to-LDS loads, 7 instructions instead of one 8-byte load per block and lane:
+  // direct-to-LDS loads, 6 instructions instead of one 8-byte load per block and lane:
   //   tokens [16][256]: 16-byte chunk c of token t at chunk position c ^ t (token t's row
   //     starts at bank 0 like every other, so the XOR spreads the operand reads of the 16
   //     tokens over all banks); tokens past M read past the end of q and are zero;
@@ -372,42 +378,53 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
       dma16(rtp, tok + kGemvTq + kGemvTda,
             (((uint32_t)s * 3 + (lane >> 4)) * (uint32_t)M + (lane & 15)) * 16u);
   };
-  float* sdsv = reinterpret_cast<float*>(smem + wave * kGemvMfmaScaleBytes);
-  uint32_t* spc = reinterpret_cast<uint32_t*>(smem + wave * kGemvMfmaScaleBytes + kWsDsv);
-
-  typedef float v4f __attribute__((ext_vector_type(4)));
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int s = wave; s < nsb; s += NW) {
-    // weights: nibble bytes of A row j_op, k-group kg, of block pairs 0..3, and its header
+  // weights of super-block s: the nibble bytes of A row j_op, k-group kg, of block pairs
+  // 0..3 (kWLoads loads with the header)
+  constexpr int kWLoads = 5;
+  auto load_weights = [&](int s, uint2* nb, v4i& hdr) {
     const uint32_t rec = (uint32_t)s * kRepTileBytes;
-    uint2 nb[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g)
       nb[g] = __builtin_bit_cast(
           uint2, buf_load_f32x2(rw, rec + g * 1024 + (kg >> 1) * 512 + j_op * 16 + (kg & 1) * 8));
-    const v4i hdr = buf_load16(rw, rec + kRepNibBytes + j_op * 16);
-    stage_tokens(s);
-    // weight scales of the super-block: lane (c16, kg) expands sub-blocks 2kg, 2kg + 1 of
-    // row c16 of the half tile into the region, after the previous super-block's reads
-    {
-      float dsv4[4], dmv4[4];
-      q4k_scales(hdr, kg >= 2, dsv4, dmv4);
-      const bool odd = (kg & 1) != 0;
-      const float dsv_a = odd ? dsv4[2] : dsv4[0], dsv_b = odd ? dsv4[3] : dsv4[1];
-      const float dmv_a = odd ? dmv4[2] : dmv4[0], dmv_b = odd ? dmv4[3] : dmv4[1];
-      uint32_t pa_[3], pb_[3];
-      bf16_trunc3(dmv_a, pa_[0], pa_[1], pa_[2]);
-      bf16_trunc3(dmv_b, pb_[0], pb_[1], pb_[2]);
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      sdsv[(2 * kg) * 16 + c16] = dsv_a;
-      sdsv[(2 * kg + 1) * 16 + c16] = dsv_b;
+    hdr = buf_load16(rw, rec + kRepNibBytes + j_op * 16);
+  };
+  float* sdsv = reinterpret_cast<float*>(smem + wave * kGemvMfmaScaleBytes);
+  uint32_t* spc = reinterpret_cast<uint32_t*>(smem + wave * kGemvMfmaScaleBytes + kWsDsv);
+  // weight scales of a super-block: lane (c16, kg) expands sub-blocks 2kg, 2kg + 1 of row c16
+  // of the half tile into the region, after the previous super-block's reads
+  auto expand_scales = [&](const v4i& hdr) {
+    float dsv4[4], dmv4[4];
+    q4k_scales(hdr, kg >= 2, dsv4, dmv4);
+    const bool odd = (kg & 1) != 0;
+    const float dsv_a = odd ? dsv4[2] : dsv4[0], dsv_b = odd ? dsv4[3] : dsv4[1];
+    const float dmv_a = odd ? dmv4[2] : dmv4[0], dmv_b = odd ? dmv4[3] : dmv4[1];
+    uint32_t pa_[3], pb_[3];
+    bf16_trunc3(dmv_a, pa_[0], pa_[1], pa_[2]);
+    bf16_trunc3(dmv_b, pb_[0], pb_[1], pb_[2]);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    sdsv[(2 * kg) * 16 + c16] = dsv_a;
+    sdsv[(2 * kg + 1) * 16 + c16] = dsv_b;
 #pragma unroll
-      for (int i = 0; i < 3; ++i) spc[(i * 16 + c16) * 4 + kg] = pack_hi16(pa_[i], pb_[i]);
-    }
-    // this wavefront's direct-to-LDS loads (and every other load) have landed, and the
-    // scale writes are ordered before the reads below
-    __builtin_amdgcn_s_waitcnt(0);
+    for (int i = 0; i < 3; ++i) spc[(i * 16 + c16) * 4 + kg] = pack_hi16(pa_[i], pb_[i]);
+  };
+
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  // One super-block s whose weights are in nb / hdr; the next one's go to nbn / hdrn.
+  auto step = [&](int s, const uint2* nb, const v4i& hdr, uint2* nbn, v4i& hdrn) {
+    expand_scales(hdr);
+    stage_tokens(s);
+    const bool next = s + NW < nsb;
+    // the next weights are issued after the token loads (the asm keeps them there), so that
+    // waiting for all but the last kWLoads vector loads waits for exactly the token loads
+    asm volatile("" ::: "memory");
+    if (next) load_weights(s + NW, nbn, hdrn);
+    // this wavefront's direct-to-LDS loads have landed, and the scale writes are ordered
+    // before the reads below: s_waitcnt vmcnt(kWLoads) lgkmcnt(0), or vmcnt(0) lgkmcnt(0)
+    if (next) __builtin_amdgcn_s_waitcnt(0x0070 | kWLoads);
+    else __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
     const v4i pa0 = *reinterpret_cast<const v4i*>(spc + (ia1 * 16 + c16) * 4);
@@ -439,10 +456,21 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
                                                   __builtin_bit_cast(v8bf, pb0), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, pa1),
                                                   __builtin_bit_cast(v8bf, pb1), acc, 0, 0, 0);
-    // every read of this super-block's regions is done before the next one's loads overwrite
-    // them (the scales are rewritten after the fence at the top of the next expansion)
-    __builtin_amdgcn_s_waitcnt(0);
+    // every LDS read of this super-block is done before the next one's loads overwrite the
+    // region (the scales are rewritten after the fence in the next expansion): lgkmcnt(0),
+    // the next weights may still be in flight
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+  };
+  // two register sets for the weights, used in turn (a copy from one to the other would wait
+  // for the loads at the end of every step)
+  uint2 nbA[4], nbB[4];
+  v4i hdrA, hdrB;
+  if (wave < nsb) load_weights(wave, nbA, hdrA);
+  for (int s = wave; s < nsb; s += 2 * NW) {
+    step(s, nbA, hdrA, nbB, hdrB);
+    if (s + NW < nsb) step(s + NW, nbB, hdrB, nbA, hdrA);
   }
+  // (a wavefront without a super-block issued no load)
 
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][c16][4 * kg + r] = acc[r];
@@ -487,47 +515,58 @@ hipError_t launch_fused_mt(const float* x, const void* w_rep, float* C, int64_t 
 
 }  // namespace
 
-// tokens per workgroup for M tokens: 1, 2, 4, then groups of 8
-bool gemv_mfma_form(int64_t M, int64_t N, int64_t compute_units) {
-  return M > kGemvDotMaxM ||
-         (M >= kGemvMfmaMinM && (N + kGemvRows - 1) / kGemvRows <= compute_units);
+bool gemv_mfma_form(int64_t M) { return M >= kGemvMfmaMinM; }
+
+int gemv_mfma_waves(int64_t N, int64_t compute_units) {
+  const int64_t nrb = (N + kGemvRows - 1) / kGemvRows;
+  return nrb <= compute_units ? 16 : (nrb <= 2 * compute_units ? 8 : 4);
 }
 
-// tokens per workgroup of the vector-ALU form
+// tokens per workgroup of the vector-ALU form: 1, 2, 4, then groups of 8
 static int64_t gemv_dot_group(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : 8)); }
 
-int64_t gemv_group(int64_t M, bool mfma) { return mfma ? kGemvMaxM : gemv_dot_group(M); }
+int64_t gemv_group(int64_t M, int mfma_waves) { return mfma_waves ? kGemvMaxM : gemv_dot_group(M); }
 
-int64_t gemv_lds_bytes(int64_t M, bool mfma) {
+int64_t gemv_lds_bytes(int64_t M, int mfma_waves) {
   // the matrix-unit form: per wavefront its expanded weight scales, its partial sums and its
   // super-block's token-side operands
-  if (mfma) return kGemvMfmaWaves * (16 * 16 * 4 + kGemvMfmaScaleBytes + kGemvMfmaTokBytes);
+  if (mfma_waves) return mfma_waves * (16 * 16 * 4 + kGemvMfmaScaleBytes + kGemvMfmaTokBytes);
   const int64_t mt = gemv_dot_group(M);
   return (int64_t)kGemvWaves * kGemvSlices * (mt * 160 + 16);
 }
 
-int64_t gemv_grid(int64_t M, int64_t N, bool mfma) {
-  const int64_t g = gemv_group(M, mfma);
+int64_t gemv_grid(int64_t M, int64_t N, int mfma_waves) {
+  const int64_t g = gemv_group(M, mfma_waves);
   return (N + kGemvRows - 1) / kGemvRows * ((M + g - 1) / g);
 }
 
+namespace {
+template <int NW>
+hipError_t launch_mfma(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
+                       int64_t K, hipStream_t s) {
+  const uint8_t* base = static_cast<const uint8_t*>(q8);
+  const int64_t lds = gemv_lds_bytes(M, NW);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mmq_gemv_mfma_kernel<NW>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mmq_gemv_mfma_kernel<NW>, dim3((unsigned)gemv_grid(M, N, NW)),
+                     dim3(64 * NW), (size_t)lds, s, reinterpret_cast<const int8_t*>(base),
+                     reinterpret_cast<const float*>(base + q8_planes_offset(M, K)),
+                     reinterpret_cast<const uint16_t*>(base + q8_pieces_offset(M, K)),
+                     static_cast<const uint8_t*>(w_rep), C, (int)M, (int)N, (int)K);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
-                           int64_t K, bool mfma, hipStream_t s) {
-  if (M < 1 || M > kGemvMaxM || (!mfma && M > kGemvDotMaxM)) return hipErrorInvalidValue;
-  if (mfma) {
-    const uint8_t* base = static_cast<const uint8_t*>(q8);
-    const int64_t lds = gemv_lds_bytes(M, true);
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(mmq_gemv_mfma_kernel<kGemvMfmaWaves>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mmq_gemv_mfma_kernel<kGemvMfmaWaves>, dim3((unsigned)gemv_grid(M, N, true)),
-                       dim3(64 * kGemvMfmaWaves), (size_t)lds, s,
-                       reinterpret_cast<const int8_t*>(base),
-                       reinterpret_cast<const float*>(base + q8_planes_offset(M, K)),
-                       reinterpret_cast<const uint16_t*>(base + q8_pieces_offset(M, K)),
-                       static_cast<const uint8_t*>(w_rep), C, (int)M, (int)N, (int)K);
-    return hipGetLastError();
+                           int64_t K, int mfma_waves, hipStream_t s) {
+  if (M < 1 || M > kGemvMaxM || (!mfma_waves && M > kGemvDotMaxM)) return hipErrorInvalidValue;
+  switch (mfma_waves) {
+    case 0: break;
+    case 4: return launch_mfma<4>(q8, w_rep, C, M, N, K, s);
+    case 8: return launch_mfma<8>(q8, w_rep, C, M, N, K, s);
+    case 16: return launch_mfma<16>(q8, w_rep, C, M, N, K, s);
+    default: return hipErrorInvalidValue;
   }
   // one step per slice: the single-stage form for 1 and 2 tokens (at 4 and 8 tokens it would
   // spill)

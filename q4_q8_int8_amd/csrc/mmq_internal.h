@@ -143,32 +143,37 @@ hipError_t launch_mmq_fused(const float* x, const void* w_rep, float* C, int64_t
 // Product for a handful of tokens (decode), M <= kGemvMaxM, 16 weight rows per workgroup, in
 // two forms. The vector-ALU form (kGemvWaves wavefronts, up to 8 tokens): integer dot
 // products on the vector ALU, up to 8 tokens per workgroup, K split over 16 slices and each
-// super-block over two wavefronts. The matrix-unit form (kGemvMfmaWaves wavefronts, up to 16
+// super-block over two wavefronts. The matrix-unit form (16, 8 or 4 wavefronts, up to 16
 // tokens): one 16 x 16 x 32 int8 MFMA per block, all tokens in one workgroup, K split over
 // the wavefronts by super-block.
 constexpr int kGemvWaves = 8;
 constexpr int kGemvRows = 16;  // weight rows per workgroup
 constexpr int kGemvMaxM = 16;
-constexpr int kGemvMfmaWaves = 16;  // wavefronts per workgroup of the matrix-unit form
-// The guard's choice up to here (at 16 tokens, K = N = 4096: 5.9 against the skinny
-// kernel's 9.6 us).
+// The guard's choice up to here (at 16 tokens, K = N = 4096: 5.6 against the skinny
+// kernel's 9.4 us).
 constexpr int kGemvAutoMaxM = 16;
 // The vector-ALU form serves at most this many tokens.
 constexpr int kGemvDotMaxM = 8;
-// From this many tokens the matrix-unit form is taken when its grid (one workgroup of 16
-// wavefronts and 128 KiB of LDS per compute unit) runs in one round: graph-replayed at
-// K = N = 4096 it takes 5.5-5.6 us for 4 to 8 tokens against the vector-ALU form's 5.6 (4),
-// 6.5 (5) and 7.2 us (8); at N = 11008 (three rounds) 13.5 us against 7.7-13.9.
+// From this many tokens the guard takes the matrix-unit form, at any N. Graph-replayed over
+// weights that do not stay in cache, at 5 to 8 tokens it takes 5.5-5.6 us at K = N = 4096
+// (16 wavefronts), 7.6-8.1 us at N = 5120-8192 (8) and 10.0 us at N = 11008 (4), against the
+// vector-ALU form's 6.7-7.5, 9.9-10.7 (8 tokens) and 12.6-14.2 us. At 3 and 4 tokens the two
+// are within 11 % of each other either way (the vector-ALU form ahead at 5120-8192 rows, behind
+// at 4096 and 11008), and the vector-ALU form is kept.
 constexpr int kGemvMfmaMinM = 5;
 // The variant that quantizes its activations itself: vector-ALU form only.
 constexpr int kGemvFusedMaxM = kGemvDotMaxM;
-// The form the guard takes for M tokens and N rows on a device of compute_units.
-bool gemv_mfma_form(int64_t M, int64_t N, int64_t compute_units);
-int64_t gemv_group(int64_t M, bool mfma);  // tokens per workgroup
-int64_t gemv_lds_bytes(int64_t M, bool mfma);
-int64_t gemv_grid(int64_t M, int64_t N, bool mfma);
+// Whether the guard takes the matrix-unit form for M tokens, and that form's wavefronts per
+// workgroup for N rows on a device of compute_units (16, 8 or 4, so that the N / 16
+// workgroups run in one round where they can). The helpers below take mfma_waves = 0 for the
+// vector-ALU form.
+bool gemv_mfma_form(int64_t M);
+int gemv_mfma_waves(int64_t N, int64_t compute_units);
+int64_t gemv_group(int64_t M, int mfma_waves);  // tokens per workgroup
+int64_t gemv_lds_bytes(int64_t M, int mfma_waves);
+int64_t gemv_grid(int64_t M, int64_t N, int mfma_waves);
 hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
-                           int64_t K, bool mfma, hipStream_t s);
+                           int64_t K, int mfma_waves, hipStream_t s);
 // The same kernel quantizing its own f32 activations (same LDS, grid and threads).
 hipError_t launch_mmq_gemv_fused(const float* x, const void* w_rep, float* C, int64_t M,
                                  int64_t N, int64_t K, hipStream_t s);

@@ -180,38 +180,60 @@ def test_blockdots_refuse_the_gemv_tile():
                         ctypes.byref(opt)) == mmq.MMQ_E_ARG
 
 
-MFMA_GEMV_LDS = 16 * (16 * 16 * 4 + 512 + 768 + 16 * 256 + 8 * 16 * 8 + 3 * 16 * 16)
+# the matrix-unit form's LDS per wavefront: its partial sums, its expanded weight scales
+# (dsv [8][16] f32, dmv pieces [3][16][8]) and its super-block's token bytes [16][256],
+# (da, nda) pairs [8][16] and pieces [3][16][8]
+MFMA_WAVE_LDS = 16 * 16 * 4 + 512 + 768 + 16 * 256 + 8 * 16 * 8 + 3 * 16 * 16
+MFMA_GEMV_LDS = 16 * MFMA_WAVE_LDS
 
 
-@pytest.mark.parametrize("M,N,group,grid", [
-    (1, 4096, 1, 256), (2, 4096, 2, 256), (3, 4096, 4, 256), (4, 4096, 4, 256),
-    (5, 4096, 16, 256), (8, 4096, 16, 256),     # 5-8 tokens, one round: the matrix-unit form
-    (5, 4097, 8, 257), (8, 11008, 8, 688),      # more row blocks than compute units: vector ALU
-    (9, 4096, 16, 256), (16, 4096, 16, 256), (9, 4097, 16, 257), (16, 11008, 16, 688)])
-def test_plan_gemv_tile(M, N, group, grid):
+def dot_lds(group):
+    """The vector-ALU form, per wavefront and K-slice: its half's 128 token bytes and 4
+    (da, sa) pairs per token, 16 padding."""
+    return 8 * 4 * (160 * group + 16)
+
+
+@pytest.mark.parametrize("M,N,group,grid,waves", [
+    (1, 4096, 1, 256, 0), (2, 4096, 2, 256, 0), (3, 4096, 4, 256, 0), (4, 4096, 4, 256, 0),
+    (2, 11008, 2, 688, 0), (4, 11008, 4, 688, 0),  # up to 4 tokens the vector ALU
+    (5, 4096, 16, 256, 16), (8, 4096, 16, 256, 16),
+    (16, 4096, 16, 256, 16),                    # the row blocks fit 256 compute units once
+    (5, 4097, 16, 257, 8), (9, 8192, 16, 512, 8),  # twice: 8 wavefronts
+    (8, 11008, 16, 688, 4), (16, 11008, 16, 688, 4), (5, 16400, 16, 1025, 4)])
+def test_plan_gemv_tile(M, N, group, grid, waves):
     auto = mmq.mmq_plan(M, N, 4096, 160 * 1024)
     assert (auto["tile"], auto["reason"]) == (GEMV, mmq.MMQ_REASON_DECODE)
     p = mmq.mmq_plan(M, N, 4096, 160 * 1024, force_tile=GEMV)
     assert p["tile"] == GEMV
     assert p["block_m"] == group and p["block_n"] == 16
-    assert p["threads"] == (512 if group <= 8 else 1024)
-    # the vector-ALU form, per wavefront and K-slice: its half's 128 token bytes and 4
-    # (da, sa) pairs per token, 16 padding; the matrix-unit form, per wavefront: its partial
-    # sums, its expanded weight scales (dsv [8][16] f32, dmv pieces [3][16][8]) and its
-    # super-block's token bytes [16][256], (da, nda) pairs [8][16] and pieces [3][16][8]
-    lds = 8 * 4 * (160 * group + 16) if group <= 8 else MFMA_GEMV_LDS
+    assert p["threads"] == (512 if waves == 0 else 64 * waves)
+    lds = dot_lds(group) if waves == 0 else waves * MFMA_WAVE_LDS
     assert p["lds_bytes"] == lds and p["grid"] == grid
 
 
-def test_plan_gemv_form_falls_back_within_the_budget():
-    """5-8 tokens take the vector-ALU form where the matrix-unit form's LDS does not fit."""
-    p = mmq.mmq_plan(8, 4096, 4096, 160 * 1024, opt_lds_budget=MFMA_GEMV_LDS - 1)
-    assert p["tile"] == GEMV and p["threads"] == 512 and p["lds_bytes"] == 8 * 4 * (160 * 8 + 16)
-    p = mmq.mmq_plan(8, 4096, 4096, 160 * 1024, opt_lds_budget=MFMA_GEMV_LDS)
-    assert p["tile"] == GEMV and p["threads"] == 1024
+@pytest.mark.parametrize("M,N,waves", [(8, 4096, 16), (5, 4096, 16), (5, 4097, 8),
+                                       (7, 8192, 8)])
+def test_plan_gemv_form_falls_back_within_the_budget(M, N, waves):
+    """5-8 tokens take the vector-ALU form where the matrix-unit form's LDS (at the wavefront
+    count the row blocks call for) does not fit."""
+    need = waves * MFMA_WAVE_LDS
+    group = 8
+    p = mmq.mmq_plan(M, N, 4096, 160 * 1024, opt_lds_budget=need - 1)
+    assert p["tile"] == GEMV and p["threads"] == 512 and p["block_m"] == group
+    assert p["lds_bytes"] == dot_lds(group)
+    p = mmq.mmq_plan(M, N, 4096, 160 * 1024, opt_lds_budget=need)
+    assert p["tile"] == GEMV and p["threads"] == 64 * waves and p["block_m"] == 16
+
+
+def test_plan_gemv_matrix_form_only_from_9_tokens():
     # from 9 tokens only the matrix-unit form serves: below its LDS another tile is taken
     p = mmq.mmq_plan(9, 4096, 4096, 160 * 1024, opt_lds_budget=MFMA_GEMV_LDS - 1)
     assert p["tile"] != GEMV
+    # at 5-8 tokens with 4 wavefronts (32 KiB) the vector-ALU form (40.5 KiB) needs more, and
+    # so does every other tile
+    with pytest.raises(mmq.MMQError) as e:
+        mmq.mmq_plan(8, 11008, 4096, 160 * 1024, opt_lds_budget=4 * MFMA_WAVE_LDS - 1)
+    assert e.value.status == mmq.MMQ_E_LDS
 
 
 def test_plan_above_decode_tile_is_skinny():

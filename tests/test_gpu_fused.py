@@ -37,10 +37,12 @@ def fused_tile(M):
     return mmq.MMQ_TILE_GEMV if M <= 8 else mmq.MMQ_TILE_SKINNY
 
 
-# an LDS budget one byte below the decode tile's matrix-unit form leaves up to 8 tokens to its
-# vector-ALU form, the unfused twin of the fused kernel
-VALU_FORM_BUDGET = mmq.mmq_plan(9, 160, 1024, 160 * 1024, force_tile=mmq.MMQ_TILE_GEMV)[
-    "lds_bytes"] - 1
+def valu_form_budget(M, N, K):
+    """An LDS budget that leaves M <= 8 tokens to the decode tile's vector-ALU form, the
+    unfused twin of the fused kernel: one byte below the matrix-unit form's LDS where the guard
+    takes that form (its LDS depends on the wavefront count N calls for), else no budget."""
+    p = mmq.mmq_plan(M, N, K, 160 * 1024, force_tile=mmq.MMQ_TILE_GEMV)
+    return p["lds_bytes"] - 1 if p["block_m"] == 16 else 0
 
 
 def two_step(x_dev, M, N, K, rep):
@@ -48,8 +50,10 @@ def two_step(x_dev, M, N, K, rep):
     mmq.quantize_q8_1(x_dev, M, K, q8)
     C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
     mmq.mmq_q4K_q8_1_ex(M, N, K, q8, rep, C, force_tile=fused_tile(M),
-                        lds_budget=VALU_FORM_BUDGET if M <= 8 else 0)
+                        lds_budget=valu_form_budget(M, N, K) if M <= 8 else 0)
     torch.cuda.synchronize()
+    if M <= 8:
+        assert mmq.mmq_last_kernel()["block_m"] <= 8, "the two-step path must take the vector-ALU form"
     return C.cpu().numpy()
 
 

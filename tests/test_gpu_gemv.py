@@ -2,9 +2,10 @@
 
 Bar: f32 outputs within 1e-5 * T per element (T from the oracle, float64), every element;
 results deterministic. The tile is the guard's choice for M <= 16, in two forms: vector-ALU
-dot products (up to M = 4, and up to M = 8 when the rows need more than one round of
-workgroups) and a 16 x 16 int8 MFMA per block (from M = 9, and from M = 5 within one round),
-so the token sweep's M = 1 and M = 16 shapes run through it by default.
+dot products (up to M = 4) and a 16 x 16 int8 MFMA per block (from M = 5) with 16, 8 or 4
+wavefronts per workgroup by the number of 16-row blocks, so the token sweep's M = 1 and
+M = 16 shapes run through it by default. The vector-ALU form still serves 5 to 8 tokens under
+an LDS budget below the matrix-unit form's, and is tested that way too.
 """
 import numpy as np
 import pytest
@@ -72,19 +73,41 @@ def test_gemv_every_token_count(M):
     assert info["block_m"] >= min(M, 4)
 
 
-# LDS of the matrix-unit form; one byte less leaves 5-8 tokens to the vector-ALU form
-MFMA_FORM_LDS = mmq.mmq_plan(8, 160, 1024, 160 * 1024, force_tile=GEMV)["lds_bytes"]
+def mfma_waves(N):
+    """The matrix-unit form's wavefronts per workgroup: its N / 16 workgroups fit the 256
+    compute units that mmq_plan assumes once (16), twice (8) or not (4)."""
+    nrb = (N + 15) // 16
+    return 16 if nrb <= 256 else (8 if nrb <= 512 else 4)
+
+
+def valu_budget(M, N, K):
+    """One byte below the matrix-unit form's LDS: leaves 5-8 tokens to the vector-ALU form."""
+    return mmq.mmq_plan(M, N, K, 160 * 1024, force_tile=GEMV)["lds_bytes"] - 1
 
 
 @pytest.mark.parametrize("M,N,K", [(5, 160, 1024), (6, 96, 2816), (7, 4097, 256),
-                                   (8, 70, 11008)])
+                                   (8, 70, 11008), (6, 8192, 512)])
 def test_gemv_both_forms_from_5_to_8_tokens(M, N, K):
-    """5 to 8 tokens run in either form, by the guard's choice of form: the matrix-unit form
-    when its grid runs in one round and fits the LDS, else the vector-ALU form."""
+    """5 to 8 tokens run in either form: the matrix-unit form by the guard's choice, the
+    vector-ALU form under an LDS budget one byte below it."""
     a, ia = _check(M, N, K, 300 + M)
-    b, ib = _check(M, N, K, 300 + M, lds_budget=MFMA_FORM_LDS - 1)
+    assert ia["block_m"] == 16 and ia["threads"] == 64 * mfma_waves(N)
+    b, ib = _check(M, N, K, 300 + M, lds_budget=valu_budget(M, N, K))
     assert ib["threads"] == 512 and ib["block_m"] == 8
-    assert ia["threads"] == (1024 if (N + 15) // 16 <= 256 else 512)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (16, 4112, 1024),   # 257 row blocks: 8 wavefronts, one super-block each
+    (5, 4100, 2816),    # 8 wavefronts over 11 super-blocks: three take a second one
+    (6, 8192, 4096),    # 512 row blocks: 8 wavefronts, two super-blocks each
+    (9, 8208, 9472),    # 513 row blocks: 4 wavefronts over 37 super-blocks (10, 9, 9, 9)
+    (16, 11008, 4096),  # the gate/up rows: 4 wavefronts, four super-blocks each
+])
+def test_gemv_matrix_form_wave_counts(M, N, K):
+    """The matrix-unit form with 8 and 4 wavefronts per workgroup, each wavefront taking one or
+    several super-blocks (the next one's weights loaded during this one), every element."""
+    C, info = _check(M, N, K, 700 + M)
+    assert info["block_m"] == 16 and info["threads"] == 64 * mfma_waves(N)
 
 
 @pytest.mark.parametrize("M,N,K", [
@@ -95,15 +118,23 @@ def test_gemv_both_forms_from_5_to_8_tokens(M, N, K):
     (1, 64, 9472),      # 37 super-blocks: 2 or 3 per slice, the last step partly idle
     (5, 70, 11008),     # 43 super-blocks over 16 slices, a ragged token group
     (16, 200, 2816),    # 11 super-blocks: 5 slices idle, wavefront 3 without a step
+    (6, 1, 256),        # matrix-unit form: one row, one super-block, 15 wavefronts idle
+    (12, 33, 512),      # three row blocks, the last with one real row, 4 tokens past M
 ])
-def test_gemv_edge_shapes(M, N, K):
-    _check(M, N, K, M * 1000 + N + K)
+@pytest.mark.parametrize("form", ["guard", "vector_alu"])
+def test_gemv_edge_shapes(M, N, K, form):
+    """By the guard's choice of form, and from 5 to 8 tokens also in the vector-ALU form."""
+    if form == "vector_alu" and not 5 <= M <= 8:
+        pytest.skip("the guard's form is the vector-ALU one below 5 tokens, the only one above 8")
+    _check(M, N, K, M * 1000 + N + K, lds_budget=valu_budget(M, N, K) if form != "guard" else 0)
 
 
-def test_gemv_extreme_values():
-    """Weights with the largest nibbles and scales, activations with outliers per block."""
-    _check(4, 96, 1024, 7, kind="normal_outliers", wkind="fit")
-    _check(3, 64, 768, 8, kind="normal_outliers", wkind="random_fields")
+@pytest.mark.parametrize("M", [4, 3, 6])
+def test_gemv_extreme_values(M):
+    """Weights with the largest nibbles and scales, activations with outliers per block; 3 and
+    4 tokens in the vector-ALU form, 6 in the matrix-unit form."""
+    for (N, K, seed, wkind) in [(96, 1024, 7, "fit"), (64, 768, 8, "random_fields")]:
+        _check(M, N, K, seed, kind="normal_outliers", wkind=wkind)
 
 
 def test_gemv_integer_case_exact():
