@@ -460,8 +460,9 @@ def rotation(M: int, N: int, K: int, r_min: int) -> int:
 
 
 DECODE_SHAPES = [(1, 4096, 4096), (2, 4096, 4096), (4, 4096, 4096), (5, 4096, 4096),
-                 (8, 4096, 4096), (12, 4096, 4096), (16, 4096, 4096), (1, 11008, 4096),
-                 (8, 11008, 4096), (16, 11008, 4096), (1, 4096, 11008)]
+                 (8, 4096, 4096), (12, 4096, 4096), (16, 4096, 4096), (8, 8192, 4096),
+                 (16, 8192, 4096), (1, 11008, 4096), (4, 11008, 4096), (8, 11008, 4096),
+                 (16, 11008, 4096), (1, 4096, 11008), (16, 4096, 11008)]
 
 
 def decode_m1(args) -> dict:
