@@ -273,9 +273,9 @@ int mmq_q4K_q8_1_static(int64_t M, int64_t N, int64_t K, const void* q8, const v
  * then runs the unfused kernel's arithmetic on them. Every workgroup that needs a token's
  * super-block repeats that quantization, so the call is limited to few tokens:
  * 1 <= M <= 128. It pays for the fewest: at K = N = 4096, replayed from a graph over weights
- * that do not stay in cache, one call takes 5.2, 6.2 and 8.2 us at M = 1, 2 and 4, against
- * 7.5, 7.9 and 8.8 us for quantize_q8_1 followed by the decode tile; from M = 5 the two
- * kernels are faster (8.7 against 9.7 us, at M = 8 8.7 against 12.5).
+ * that do not stay in cache, one call takes 5.3, 6.2 and 8.3 us at M = 1, 2 and 4, against
+ * 7.5, 7.9 and 8.9 us for quantize_q8_1 followed by the decode tile; from M = 5 the two
+ * kernels are faster (8.8 against 9.7 us, at M = 8 8.7 against 12.3).
  * w_rep from repack_q4_K (N x K); C overwritten as for mmq_q4K_q8_1; mmq_last_kernel reports
  * the tile (MMQ_TILE_GEMV or MMQ_TILE_SKINNY) with reason MMQ_REASON_FUSED.
  * Errors: MMQ_E_ARG, MMQ_E_SHAPE (as mmq_q4K_q8_1, or M > 128), MMQ_E_LDS (the kernel's LDS
