@@ -37,8 +37,11 @@ def _replay_and_check(g, out, want, disturb):
 
 
 @pytest.mark.parametrize("M,N,K", [(2048, 4096, 4096), (1, 4096, 4096), (12, 4096, 4096),
-                                   (16, 1024, 2048), (100, 512, 1024)])
+                                   (8, 11008, 1024), (6, 8192, 512), (16, 1024, 2048),
+                                   (100, 512, 1024)])
 def test_integer_step_in_a_graph(M, N, K):
+    """The guard's choice under capture: the large tile, the decode tile's vector-ALU form
+    and its matrix-unit form with 16, 4 and 8 wavefronts, and the small tile."""
     x = to_dev(synth.activations("normal_outliers", M, K, 7000 + M))
     w, _ = synth.q4k_weights("fit", N, K, 7001)
     rep = torch.empty(mmq.mmq_q4K_repacked_bytes(N, K), dtype=torch.uint8, device="cuda")
