@@ -70,10 +70,11 @@ enum mmq_tile {
                           is below the other form's. Matrix-unit form (block_m = 16): all tokens
                           in one workgroup, one v_mfma_i32_16x16x32_i8 per block, K split over
                           the wavefronts by super-block, each loading its next super-block's
-                          weights while it computes one; 16 wavefronts (threads = 1024, 128 KiB
-                          of LDS) when ceil(N/16) workgroups fit the compute units once, 8
-                          (512 threads, 64 KiB) when they fit twice, else 4 (256, 32 KiB);
-                          taken for 5 <= M <= 16 */
+                          weights while it computes one: 16 wavefronts and 16 rows per
+                          workgroup (threads = 1024, block_n = 16, 128 KiB of LDS) when
+                          ceil(N/16) workgroups fit the compute units once, 8 wavefronts and
+                          32 rows (512, 32, 82 KiB) when ceil(N/32) fit, else 4 wavefronts and
+                          16 rows (256, 16, 32 KiB); taken for 5 <= M <= 16 */
   MMQ_TILE_MEDIUM = 5, /* 32 tokens x 256 output features per workgroup, 8 wavefronts (the
                           template of the large and small tiles); with a workspace, K may be
                           split over workgroups (split-K, see mmq_options) */

@@ -214,11 +214,13 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
   // kGemvDotMaxM tokens the matrix-unit form only where it fits the budget (the vector-ALU
   // form needs far less LDS)
   const int mfma_waves = mmq::gemv_mfma_waves(N, compute_units);
+  const int mfma_rows = mmq::gemv_mfma_rows(N, compute_units);
   const int gemv_form =
       mmq::gemv_mfma_form(M) &&
-              (M > mmq::kGemvDotMaxM || mmq::gemv_lds_bytes(M, mfma_waves) <= budget)
+              (M > mmq::kGemvDotMaxM || mmq::gemv_lds_bytes(M, mfma_waves, mfma_rows) <= budget)
           ? mfma_waves
           : 0;
+  const int gemv_rows = gemv_form ? mfma_rows : mmq::kGemvRows;
   if (forced == MMQ_TILE_LARGE) {
     if (need_large <= budget) { tile = MMQ_TILE_LARGE; reason = MMQ_REASON_FORCED; }
   } else if (forced == MMQ_TILE_SMALL) {
@@ -233,10 +235,10 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
     if (M > mmq::kGemvMaxM)
       return fail(MMQ_E_SHAPE, "the decode tile takes M <= %d (M = %lld)", mmq::kGemvMaxM,
                   (long long)M);
-    if (mmq::gemv_lds_bytes(M, gemv_form) <= budget) {
+    if (mmq::gemv_lds_bytes(M, gemv_form, gemv_rows) <= budget) {
       tile = MMQ_TILE_GEMV; reason = MMQ_REASON_FORCED;
     }
-  } else if (!q6 && M <= mmq::kGemvAutoMaxM && mmq::gemv_lds_bytes(M, gemv_form) <= budget) {
+  } else if (!q6 && M <= mmq::kGemvAutoMaxM && mmq::gemv_lds_bytes(M, gemv_form, gemv_rows) <= budget) {
     tile = MMQ_TILE_GEMV; reason = MMQ_REASON_DECODE;
   } else if (need_large <= budget) {
     // the cheapest (tile, splits) under the cost model: splits only with a workspace that
@@ -296,10 +298,10 @@ int plan(int64_t M, int64_t N, int64_t K, const mmq_options* opt, int64_t budget
     splits = 1;  // (an LDS fallback to another kind of kernel drops a forced split)
   if (tile == MMQ_TILE_GEMV) {
     info->block_m = (int32_t)mmq::gemv_group(M, gemv_form);
-    info->block_n = mmq::kGemvRows;
+    info->block_n = gemv_rows;
     info->threads = 64 * (gemv_form ? gemv_form : mmq::kGemvWaves);
-    info->lds_bytes = mmq::gemv_lds_bytes(M, gemv_form);
-    info->grid = mmq::gemv_grid(M, N, gemv_form);
+    info->lds_bytes = mmq::gemv_lds_bytes(M, gemv_form, gemv_rows);
+    info->grid = mmq::gemv_grid(M, N, gemv_form, gemv_rows);
     return MMQ_OK;
   }
   if (tile == MMQ_TILE_SKINNY) {
@@ -348,9 +350,10 @@ int launch_planned(const mmq_kernel_info& info, int64_t M, int64_t N, int64_t K,
   hipError_t e;
   if (info.tile == MMQ_TILE_GEMV) {
     // the form the guard chose: the matrix-unit form takes all tokens in one workgroup, with
-    // threads / 64 wavefronts
+    // threads / 64 wavefronts and block_n weight rows
     e = mmq::launch_mmq_gemv(q8, w_rep, C, M, N, K,
-                             info.block_m == mmq::kGemvMaxM ? info.threads / 64 : 0, stream);
+                             info.block_m == mmq::kGemvMaxM ? info.threads / 64 : 0,
+                             info.block_n, stream);
   } else if (info.tile == MMQ_TILE_SKINNY) {
     e = mmq::launch_mmq_skinny(q8, w_rep, C, M, N, K, compute_units, stream);
   } else {
@@ -565,8 +568,8 @@ int mmq_q4K_f32(int64_t M, int64_t N, int64_t K, const float* x, const void* w_r
     info.block_m = (int32_t)mmq::gemv_group(M, 0);
     info.block_n = mmq::kGemvRows;
     info.threads = 64 * mmq::kGemvWaves;
-    info.lds_bytes = mmq::gemv_lds_bytes(M, 0);
-    info.grid = mmq::gemv_grid(M, N, 0);
+    info.lds_bytes = mmq::gemv_lds_bytes(M, 0, mmq::kGemvRows);
+    info.grid = mmq::gemv_grid(M, N, 0, mmq::kGemvRows);
   } else {
     info.tile = MMQ_TILE_SKINNY;
     info.block_m = 32;

@@ -300,15 +300,19 @@ __global__ __launch_bounds__(kGemvWaves * 64, ONE ? 6 : 1) void mmq_gemv_kernel(
 // The matrix-unit form (from 5 tokens to 16): the vector ALU's dot products set the time
 // there, so one 32-block of 16 weight rows x 16 tokens becomes one v_mfma_i32_16x16x32_i8 (no
 // padding at 16 tokens; the columns of tokens past M are computed from in-bounds or zero reads
-// and never stored). A workgroup of NW wavefronts owns 16 weight rows (paired on one XCD as
-// above) and all of K; wavefront w takes the super-blocks w, w + NW, w + 2 NW, ..., each
-// one's weights in registers and its token-side operands in the wavefront's own LDS region
-// (six direct-to-LDS loads), then computes it. The weights of the wavefront's next
-// super-block are loaded while it computes this one. NW is 16 where the N / 16 workgroups fit
-// the compute units once (a workgroup takes 128 KiB of LDS, so one per unit), 8 where they fit
-// twice and 4 beyond: with 16 wavefronts at N = 11008 the grid took three rounds, and every
-// workgroup stages all of K's token operands (5.9 KB per super-block, 2.5x the bytes of its
-// weights), so more workgroups at once beat more wavefronts per workgroup there.
+// and never stored). A workgroup of NW wavefronts owns RT 16-row halves of a repacked tile
+// (with one half, the two halves of a tile go to workgroups on one XCD as above) and all of
+// K; wavefront w takes the super-blocks w, w + NW, w + 2 NW, ..., each one's weights in
+// registers and its token-side operands in the wavefront's own LDS region (six direct-to-LDS
+// loads), then computes it. The weights of the wavefront's next super-block are loaded while
+// it computes this one. The shape follows the rows N: where the N / 16 workgroups fit the
+// compute units once, 16 wavefronts and one half (128 KiB of LDS, one workgroup per unit);
+// where N / 32 fit, 8 wavefronts and both halves (82 KiB); else 4 wavefronts and one half
+// (32 KiB, up to five per unit). Every workgroup stages all of K's token operands (5.9 KB per
+// super-block, 2.5x the bytes of one half's weights), so two halves halve that traffic per
+// weight byte, while more workgroups in flight hide more latency: with 16 wavefronts at
+// N = 11008 the grid took three rounds, and there two halves with 4 wavefronts (half the
+// workgroups) were slower than one.
 // Per block a lane holds, for its token l % 16, the four outputs of rows 4 (l / 16) .. + 3,
 // and rescales them as the GEMM does: y = fma(D, da, nda) with D biased by 0x4B400000,
 // acc = fma(y, dsv, acc). term2 of a super-block is a K = 8 product of dmv and da*sa; as in
@@ -320,36 +324,42 @@ __global__ __launch_bounds__(kGemvWaves * 64, ONE ? 6 : 1) void mmq_gemv_kernel(
 // accumulator. The NW wavefronts' partial sums are added in wavefront order through LDS.
 // Operand layout of both instructions: A row l % 16 and B column l % 16 take the 8 k values
 // 8 (l / 16) .. + 7; the result of row 4 (l / 16) + r, column l % 16 is register r of lane l.
-template <int NW>
+template <int NW, int RT>
 __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
     const int8_t* __restrict__ qs, const float* __restrict__ da_plane,
     const uint16_t* __restrict__ tpieces, const uint8_t* __restrict__ wrep,
     float* __restrict__ C, int M, int N, int K) {
   static_assert(NW >= 4, "the final sum takes 256 work-items");
-  // LDS: per wavefront its expanded weight scales (dsv f32 [8 blocks][16 rows], then the dmv
-  // pieces bf16 [3][16 rows][8]); the partial sums [wavefront][token][row]; per wavefront its
-  // super-block's token-side operands (kGemvMfmaTokBytes)
+  static_assert(RT == 1 || RT == 2, "one or two 16-row halves of a tile per workgroup");
+  constexpr int kRows = RT * 16;  // weight rows per workgroup
+  // LDS: per wavefront its expanded weight scales, per half (dsv f32 [8 blocks][16 rows],
+  // then the dmv pieces bf16 [3][16 rows][8]); the partial sums [wavefront][token][row]; per
+  // wavefront its super-block's token-side operands (kGemvMfmaTokBytes)
   constexpr int kWsDsv = 8 * 16 * 4;
   static_assert(kWsDsv + 3 * 16 * 8 * 2 == kGemvMfmaScaleBytes, "scale region");
   extern __shared__ __align__(16) uint8_t smem[];
-  constexpr int kRedOff = NW * kGemvMfmaScaleBytes;
-  constexpr int kTokOff = kRedOff + NW * 16 * 16 * 4;
-  float(*red)[16][16] = reinterpret_cast<float(*)[16][16]>(smem + kRedOff);
+  constexpr int kRedOff = NW * RT * kGemvMfmaScaleBytes;
+  constexpr int kTokOff = kRedOff + NW * 16 * kRows * 4;
+  float(*red)[16][kRows] = reinterpret_cast<float(*)[16][kRows]>(smem + kRedOff);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int u = (int)blockIdx.x;
-  const int nrb = (N + kGemvRows - 1) / kGemvRows;
+  // row block rb of kRows rows; with 16 rows, halves of one tile paired on one XCD
   int rb = u;
-  if (u < nrb / 16 * 16) rb = (u & ~15) + 2 * (u & 7) + ((u >> 3) & 1);
+  if (RT == 1) {
+    const int nrb = (N + kGemvRows - 1) / kGemvRows;
+    if (u < nrb / 16 * 16) rb = (u & ~15) + 2 * (u & 7) + ((u >> 3) & 1);
+  }
   const int nsb = K >> 8;
   const int c16 = lane & 15, kg = lane >> 4;   // operand row / token column, k-group
-  const int j_op = (rb & 1) * 16 + c16;        // A operand row within the 32-row tile
+  // A operand row within the 32-row tile, of half h
+  auto j_op = [&](int h) { return (RT == 2 ? h : (rb & 1)) * 16 + c16; };
   // term2 piece pairs of this lane's k-group: (ia1, jb1) in the first instruction, (ia2, jb2)
   // in the second (k-groups 2 and 3 of the second are zero)
   const int ia1 = kg == 2 ? 1 : 0, jb1 = kg == 1 ? 1 : (kg == 3 ? 2 : 0);
   const int ia2 = kg == 1 ? 2 : 1, jb2 = kg == 0 ? 1 : 0;
   const bool t2 = kg < 2;
-  const uint8_t* wtile = wrep + (size_t)(rb >> 1) * (size_t)nsb * kRepTileBytes;
+  const uint8_t* wtile = wrep + (size_t)(RT == 2 ? rb : rb >> 1) * (size_t)nsb * kRepTileBytes;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wtile, (uint32_t)nsb * (uint32_t)kRepTileBytes);
   const v4i rq = make_rsrc_sgpr(qs, (uint32_t)M * (uint32_t)K);
   const v4i rda = make_rsrc_sgpr(da_plane, (uint32_t)M * (uint32_t)(K >> 5) * 8u);
@@ -378,42 +388,59 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
       dma16(rtp, tok + kGemvTq + kGemvTda,
             (((uint32_t)s * 3 + (lane >> 4)) * (uint32_t)M + (lane & 15)) * 16u);
   };
-  // weights of super-block s: the nibble bytes of A row j_op, k-group kg, of block pairs
-  // 0..3 (kWLoads loads with the header)
-  constexpr int kWLoads = 5;
-  auto load_weights = [&](int s, uint2* nb, v4i& hdr) {
+  // weights of super-block s, per half: the nibble bytes of A row j_op(h), k-group kg, of
+  // block pairs 0..3, and the row's header (kWLoads loads in all)
+  constexpr int kWLoads = 5 * RT;
+  auto load_weights = [&](int s, uint2 (*nb)[4], v4i* hdr) {
     const uint32_t rec = (uint32_t)s * kRepTileBytes;
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      nb[g] = __builtin_bit_cast(
-          uint2, buf_load_f32x2(rw, rec + g * 1024 + (kg >> 1) * 512 + j_op * 16 + (kg & 1) * 8));
-    hdr = buf_load16(rw, rec + kRepNibBytes + j_op * 16);
+    for (int h = 0; h < RT; ++h) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        nb[h][g] = __builtin_bit_cast(
+            uint2, buf_load_f32x2(rw, rec + g * 1024 + (kg >> 1) * 512 + j_op(h) * 16 + (kg & 1) * 8));
+      hdr[h] = buf_load16(rw, rec + kRepNibBytes + j_op(h) * 16);
+    }
   };
-  float* sdsv = reinterpret_cast<float*>(smem + wave * kGemvMfmaScaleBytes);
-  uint32_t* spc = reinterpret_cast<uint32_t*>(smem + wave * kGemvMfmaScaleBytes + kWsDsv);
+  auto sdsv = [&](int h) {
+    return reinterpret_cast<float*>(smem + (wave * RT + h) * kGemvMfmaScaleBytes);
+  };
+  auto spc = [&](int h) {
+    return reinterpret_cast<uint32_t*>(smem + (wave * RT + h) * kGemvMfmaScaleBytes + kWsDsv);
+  };
   // weight scales of a super-block: lane (c16, kg) expands sub-blocks 2kg, 2kg + 1 of row c16
-  // of the half tile into the region, after the previous super-block's reads
-  auto expand_scales = [&](const v4i& hdr) {
-    float dsv4[4], dmv4[4];
-    q4k_scales(hdr, kg >= 2, dsv4, dmv4);
-    const bool odd = (kg & 1) != 0;
-    const float dsv_a = odd ? dsv4[2] : dsv4[0], dsv_b = odd ? dsv4[3] : dsv4[1];
-    const float dmv_a = odd ? dmv4[2] : dmv4[0], dmv_b = odd ? dmv4[3] : dmv4[1];
-    uint32_t pa_[3], pb_[3];
-    bf16_trunc3(dmv_a, pa_[0], pa_[1], pa_[2]);
-    bf16_trunc3(dmv_b, pb_[0], pb_[1], pb_[2]);
+  // of each half into the region, after the previous super-block's reads
+  auto expand_scales = [&](const v4i* hdr) {
+    float dsv_a[RT], dsv_b[RT];
+    uint32_t pa_[RT][3], pb_[RT][3];
+#pragma unroll
+    for (int h = 0; h < RT; ++h) {
+      float dsv4[4], dmv4[4];
+      q4k_scales(hdr[h], kg >= 2, dsv4, dmv4);
+      const bool odd = (kg & 1) != 0;
+      dsv_a[h] = odd ? dsv4[2] : dsv4[0];
+      dsv_b[h] = odd ? dsv4[3] : dsv4[1];
+      const float dmv_a = odd ? dmv4[2] : dmv4[0], dmv_b = odd ? dmv4[3] : dmv4[1];
+      bf16_trunc3(dmv_a, pa_[h][0], pa_[h][1], pa_[h][2]);
+      bf16_trunc3(dmv_b, pb_[h][0], pb_[h][1], pb_[h][2]);
+    }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    sdsv[(2 * kg) * 16 + c16] = dsv_a;
-    sdsv[(2 * kg + 1) * 16 + c16] = dsv_b;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) spc[(i * 16 + c16) * 4 + kg] = pack_hi16(pa_[i], pb_[i]);
+    for (int h = 0; h < RT; ++h) {
+      sdsv(h)[(2 * kg) * 16 + c16] = dsv_a[h];
+      sdsv(h)[(2 * kg + 1) * 16 + c16] = dsv_b[h];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) spc(h)[(i * 16 + c16) * 4 + kg] = pack_hi16(pa_[h][i], pb_[h][i]);
+    }
   };
 
   typedef float v4f __attribute__((ext_vector_type(4)));
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  v4f acc[RT];
+#pragma unroll
+  for (int h = 0; h < RT; ++h) acc[h] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   // One super-block s whose weights are in nb / hdr; the next one's go to nbn / hdrn.
-  auto step = [&](int s, const uint2* nb, const v4i& hdr, uint2* nbn, v4i& hdrn) {
+  auto step = [&](int s, uint2 (*nb)[4], const v4i* hdr, uint2 (*nbn)[4], v4i* hdrn) {
     expand_scales(hdr);
     stage_tokens(s);
     const bool next = s + NW < nsb;
@@ -423,39 +450,52 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
     if (next) load_weights(s + NW, nbn, hdrn);
     // this wavefront's direct-to-LDS loads have landed, and the scale writes are ordered
     // before the reads below: s_waitcnt vmcnt(kWLoads) lgkmcnt(0), or vmcnt(0) lgkmcnt(0)
+    static_assert(kWLoads < 16, "vmcnt in the low field");
     if (next) __builtin_amdgcn_s_waitcnt(0x0070 | kWLoads);
     else __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    const v4i pa0 = *reinterpret_cast<const v4i*>(spc + (ia1 * 16 + c16) * 4);
-    const v4i pa1 = t2 ? *reinterpret_cast<const v4i*>(spc + (ia2 * 16 + c16) * 4)
-                       : v4i{0, 0, 0, 0};
+    v4i pa0[RT], pa1[RT];
+#pragma unroll
+    for (int h = 0; h < RT; ++h) {
+      pa0[h] = *reinterpret_cast<const v4i*>(spc(h) + (ia1 * 16 + c16) * 4);
+      pa1[h] = t2 ? *reinterpret_cast<const v4i*>(spc(h) + (ia2 * 16 + c16) * 4)
+                  : v4i{0, 0, 0, 0};
+    }
     const float2* sdap = reinterpret_cast<const float2*>(stok + kGemvTq);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-      const uint2 w = nb[b >> 1];
-      const uint2 a = (b & 1) ? make_uint2((w.x >> 4) & 0x0F0F0F0Fu, (w.y >> 4) & 0x0F0F0F0Fu)
-                              : make_uint2(w.x & 0x0F0F0F0Fu, w.y & 0x0F0F0F0Fu);
       const uint2 tb = *reinterpret_cast<const uint2*>(
           stok + c16 * 256 + (((2 * b + (kg >> 1)) ^ c16) << 4) + (kg & 1) * 8);
-      const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, a),
-                                                          __builtin_bit_cast(long, tb), bias, 0,
-                                                          0, 0);
-      const float4 dq = *reinterpret_cast<const float4*>(sdsv + b * 16 + 4 * kg);
-      const float dsvb[4] = {dq.x, dq.y, dq.z, dq.w};
       const float2 dap = sdap[b * 16 + c16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float y = __builtin_fmaf(__int_as_float(D[r]), dap.x, dap.y);
-        acc[r] = __builtin_fmaf(y, dsvb[r], acc[r]);
+      for (int h = 0; h < RT; ++h) {
+        const uint2 w = nb[h][b >> 1];
+        const uint2 a = (b & 1) ? make_uint2((w.x >> 4) & 0x0F0F0F0Fu, (w.y >> 4) & 0x0F0F0F0Fu)
+                                : make_uint2(w.x & 0x0F0F0F0Fu, w.y & 0x0F0F0F0Fu);
+        const v4i D = __builtin_amdgcn_mfma_i32_16x16x32_i8(__builtin_bit_cast(long, a),
+                                                            __builtin_bit_cast(long, tb), bias,
+                                                            0, 0, 0);
+        const float4 dq = *reinterpret_cast<const float4*>(sdsv(h) + b * 16 + 4 * kg);
+        const float dsvb[4] = {dq.x, dq.y, dq.z, dq.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float y = __builtin_fmaf(__int_as_float(D[r]), dap.x, dap.y);
+          acc[h][r] = __builtin_fmaf(y, dsvb[r], acc[h][r]);
+        }
       }
     }
     const v4i pb0 = *reinterpret_cast<const v4i*>(stok + kGemvTq + kGemvTda + (jb1 * 16 + c16) * 16);
     const v4i pb1 = *reinterpret_cast<const v4i*>(stok + kGemvTq + kGemvTda + (jb2 * 16 + c16) * 16);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, pa0),
-                                                  __builtin_bit_cast(v8bf, pb0), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, pa1),
-                                                  __builtin_bit_cast(v8bf, pb1), acc, 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < RT; ++h) {
+      acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, pa0[h]),
+                                                       __builtin_bit_cast(v8bf, pb0), acc[h], 0,
+                                                       0, 0);
+      acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, pa1[h]),
+                                                       __builtin_bit_cast(v8bf, pb1), acc[h], 0,
+                                                       0, 0);
+    }
     // every LDS read of this super-block is done before the next one's loads overwrite the
     // region (the scales are rewritten after the fence in the next expansion): lgkmcnt(0),
     // the next weights may still be in flight
@@ -463,8 +503,8 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
   };
   // two register sets for the weights, used in turn (a copy from one to the other would wait
   // for the loads at the end of every step)
-  uint2 nbA[4], nbB[4];
-  v4i hdrA, hdrB;
+  uint2 nbA[RT][4], nbB[RT][4];
+  v4i hdrA[RT], hdrB[RT];
   if (wave < nsb) load_weights(wave, nbA, hdrA);
   for (int s = wave; s < nsb; s += 2 * NW) {
     step(s, nbA, hdrA, nbB, hdrB);
@@ -473,11 +513,13 @@ __global__ __launch_bounds__(64 * NW) void mmq_gemv_mfma_kernel(
   // (a wavefront without a super-block issued no load)
 
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[wave][c16][4 * kg + r] = acc[r];
+  for (int h = 0; h < RT; ++h)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][c16][h * 16 + 4 * kg + r] = acc[h][r];
   __syncthreads();
-  if (threadIdx.x < 256) {
-    const int t = threadIdx.x >> 4, rr = threadIdx.x & 15;
-    const int n = rb * kGemvRows + rr;
+  for (int e = threadIdx.x; e < 16 * kRows; e += 64 * NW) {
+    const int t = e / kRows, rr = e % kRows;
+    const int n = rb * kRows + rr;
     if (t < M && n < N) {
       float v = 0.0f;
 #pragma unroll
@@ -518,8 +560,14 @@ hipError_t launch_fused_mt(const float* x, const void* w_rep, float* C, int64_t 
 bool gemv_mfma_form(int64_t M) { return M >= kGemvMfmaMinM; }
 
 int gemv_mfma_waves(int64_t N, int64_t compute_units) {
-  const int64_t nrb = (N + kGemvRows - 1) / kGemvRows;
-  return nrb <= compute_units ? 16 : (nrb <= 2 * compute_units ? 8 : 4);
+  if ((N + kGemvRows - 1) / kGemvRows <= compute_units) return 16;
+  return (N + 31) / 32 <= compute_units ? 8 : 4;
+}
+
+int gemv_mfma_rows(int64_t N, int64_t compute_units) {
+  // 32 rows only with 8 wavefronts: with 4 (N / 32 above the compute units) the halved grid
+  // left too few wavefronts in flight
+  return gemv_mfma_waves(N, compute_units) == 8 ? 2 * kGemvRows : kGemvRows;
 }
 
 // tokens per workgroup of the vector-ALU form: 1, 2, 4, then groups of 8
@@ -527,29 +575,30 @@ static int64_t gemv_dot_group(int64_t M) { return M <= 1 ? 1 : (M <= 2 ? 2 : (M 
 
 int64_t gemv_group(int64_t M, int mfma_waves) { return mfma_waves ? kGemvMaxM : gemv_dot_group(M); }
 
-int64_t gemv_lds_bytes(int64_t M, int mfma_waves) {
-  // the matrix-unit form: per wavefront its expanded weight scales, its partial sums and its
-  // super-block's token-side operands
-  if (mfma_waves) return mfma_waves * (16 * 16 * 4 + kGemvMfmaScaleBytes + kGemvMfmaTokBytes);
+int64_t gemv_lds_bytes(int64_t M, int mfma_waves, int rows) {
+  // the matrix-unit form: per wavefront its expanded weight scales (per 16-row half), its
+  // partial sums and its super-block's token-side operands
+  if (mfma_waves)
+    return mfma_waves * (rows / 16 * kGemvMfmaScaleBytes + 16 * rows * 4 + kGemvMfmaTokBytes);
   const int64_t mt = gemv_dot_group(M);
   return (int64_t)kGemvWaves * kGemvSlices * (mt * 160 + 16);
 }
 
-int64_t gemv_grid(int64_t M, int64_t N, int mfma_waves) {
+int64_t gemv_grid(int64_t M, int64_t N, int mfma_waves, int rows) {
   const int64_t g = gemv_group(M, mfma_waves);
-  return (N + kGemvRows - 1) / kGemvRows * ((M + g - 1) / g);
+  return (N + rows - 1) / rows * ((M + g - 1) / g);
 }
 
 namespace {
-template <int NW>
+template <int NW, int RT>
 hipError_t launch_mfma(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
                        int64_t K, hipStream_t s) {
   const uint8_t* base = static_cast<const uint8_t*>(q8);
-  const int64_t lds = gemv_lds_bytes(M, NW);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mmq_gemv_mfma_kernel<NW>),
+  const int64_t lds = gemv_lds_bytes(M, NW, RT * 16);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(mmq_gemv_mfma_kernel<NW, RT>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mmq_gemv_mfma_kernel<NW>, dim3((unsigned)gemv_grid(M, N, NW)),
+  hipLaunchKernelGGL((mmq_gemv_mfma_kernel<NW, RT>), dim3((unsigned)gemv_grid(M, N, NW, RT * 16)),
                      dim3(64 * NW), (size_t)lds, s, reinterpret_cast<const int8_t*>(base),
                      reinterpret_cast<const float*>(base + q8_planes_offset(M, K)),
                      reinterpret_cast<const uint16_t*>(base + q8_pieces_offset(M, K)),
@@ -559,14 +608,13 @@ hipError_t launch_mfma(const void* q8, const void* w_rep, float* C, int64_t M, i
 }  // namespace
 
 hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
-                           int64_t K, int mfma_waves, hipStream_t s) {
+                           int64_t K, int mfma_waves, int rows, hipStream_t s) {
   if (M < 1 || M > kGemvMaxM || (!mfma_waves && M > kGemvDotMaxM)) return hipErrorInvalidValue;
-  switch (mfma_waves) {
-    case 0: break;
-    case 4: return launch_mfma<4>(q8, w_rep, C, M, N, K, s);
-    case 8: return launch_mfma<8>(q8, w_rep, C, M, N, K, s);
-    case 16: return launch_mfma<16>(q8, w_rep, C, M, N, K, s);
-    default: return hipErrorInvalidValue;
+  if (mfma_waves) {  // the shapes the guard takes (gemv_mfma_waves, gemv_mfma_rows)
+    if (rows == 16 && mfma_waves == 16) return launch_mfma<16, 1>(q8, w_rep, C, M, N, K, s);
+    if (rows == 32 && mfma_waves == 8) return launch_mfma<8, 2>(q8, w_rep, C, M, N, K, s);
+    if (rows == 16 && mfma_waves == 4) return launch_mfma<4, 1>(q8, w_rep, C, M, N, K, s);
+    return hipErrorInvalidValue;
   }
   // one step per slice: the single-stage form for 1 and 2 tokens (at 4 and 8 tokens it would
   // spill)

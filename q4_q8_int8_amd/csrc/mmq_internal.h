@@ -143,11 +143,11 @@ hipError_t launch_mmq_fused(const float* x, const void* w_rep, float* C, int64_t
 // Product for a handful of tokens (decode), M <= kGemvMaxM, 16 weight rows per workgroup, in
 // two forms. The vector-ALU form (kGemvWaves wavefronts, up to 8 tokens): integer dot
 // products on the vector ALU, up to 8 tokens per workgroup, K split over 16 slices and each
-// super-block over two wavefronts. The matrix-unit form (16, 8 or 4 wavefronts, up to 16
-// tokens): one 16 x 16 x 32 int8 MFMA per block, all tokens in one workgroup, K split over
-// the wavefronts by super-block.
+// super-block over two wavefronts. The matrix-unit form (16 wavefronts and 16 rows, 8 and 32,
+// or 4 and 16; up to 16 tokens): one 16 x 16 x 32 int8 MFMA per block and 16 rows, all tokens
+// in one workgroup, K split over the wavefronts by super-block.
 constexpr int kGemvWaves = 8;
-constexpr int kGemvRows = 16;  // weight rows per workgroup
+constexpr int kGemvRows = 16;  // weight rows per workgroup (the matrix-unit form: 16 or 32)
 constexpr int kGemvMaxM = 16;
 // The guard's choice up to here (at 16 tokens, K = N = 4096: 5.6 against the skinny
 // kernel's 9.4 us).
@@ -163,17 +163,18 @@ constexpr int kGemvDotMaxM = 8;
 constexpr int kGemvMfmaMinM = 5;
 // The variant that quantizes its activations itself: vector-ALU form only.
 constexpr int kGemvFusedMaxM = kGemvDotMaxM;
-// Whether the guard takes the matrix-unit form for M tokens, and that form's wavefronts per
-// workgroup for N rows on a device of compute_units (16, 8 or 4, so that the N / 16
-// workgroups run in one round where they can). The helpers below take mfma_waves = 0 for the
-// vector-ALU form.
+// Whether the guard takes the matrix-unit form for M tokens, and that form's wavefronts and
+// weight rows per workgroup for N rows on a device of compute_units (16 and 16 where N / 16
+// workgroups run in one round, 8 and 32 where N / 32 do, else 4 and 16). The helpers below
+// take mfma_waves = 0 (and 16 rows) for the vector-ALU form.
 bool gemv_mfma_form(int64_t M);
 int gemv_mfma_waves(int64_t N, int64_t compute_units);
+int gemv_mfma_rows(int64_t N, int64_t compute_units);  // weight rows per workgroup, 16 or 32
 int64_t gemv_group(int64_t M, int mfma_waves);  // tokens per workgroup
-int64_t gemv_lds_bytes(int64_t M, int mfma_waves);
-int64_t gemv_grid(int64_t M, int64_t N, int mfma_waves);
+int64_t gemv_lds_bytes(int64_t M, int mfma_waves, int rows);
+int64_t gemv_grid(int64_t M, int64_t N, int mfma_waves, int rows);
 hipError_t launch_mmq_gemv(const void* q8, const void* w_rep, float* C, int64_t M, int64_t N,
-                           int64_t K, int mfma_waves, hipStream_t s);
+                           int64_t K, int mfma_waves, int rows, hipStream_t s);
 // The same kernel quantizing its own f32 activations (same LDS, grid and threads).
 hipError_t launch_mmq_gemv_fused(const float* x, const void* w_rep, float* C, int64_t M,
                                  int64_t N, int64_t K, hipStream_t s);

@@ -180,10 +180,14 @@ def test_blockdots_refuse_the_gemv_tile():
                         ctypes.byref(opt)) == mmq.MMQ_E_ARG
 
 
-# the matrix-unit form's LDS per wavefront: its partial sums, its expanded weight scales
-# (dsv [8][16] f32, dmv pieces [3][16][8]) and its super-block's token bytes [16][256],
-# (da, nda) pairs [8][16] and pieces [3][16][8]
-MFMA_WAVE_LDS = 16 * 16 * 4 + 512 + 768 + 16 * 256 + 8 * 16 * 8 + 3 * 16 * 16
+# the matrix-unit form's LDS per wavefront: its expanded weight scales per 16-row half (dsv
+# [8][16] f32, dmv pieces [3][16][8]), its partial sums [16 tokens][rows] and its super-block's
+# token bytes [16][256], (da, nda) pairs [8][16] and pieces [3][16][8]
+def mfma_wave_lds(rows):
+    return rows // 16 * (512 + 768) + 16 * rows * 4 + 16 * 256 + 8 * 16 * 8 + 3 * 16 * 16
+
+
+MFMA_WAVE_LDS = mfma_wave_lds(16)
 MFMA_GEMV_LDS = 16 * MFMA_WAVE_LDS
 
 
@@ -193,36 +197,41 @@ def dot_lds(group):
     return 8 * 4 * (160 * group + 16)
 
 
-@pytest.mark.parametrize("M,N,group,grid,waves", [
-    (1, 4096, 1, 256, 0), (2, 4096, 2, 256, 0), (3, 4096, 4, 256, 0), (4, 4096, 4, 256, 0),
-    (2, 11008, 2, 688, 0), (4, 11008, 4, 688, 0),  # up to 4 tokens the vector ALU
-    (5, 4096, 16, 256, 16), (8, 4096, 16, 256, 16),
-    (16, 4096, 16, 256, 16),                    # the row blocks fit 256 compute units once
-    (5, 4097, 16, 257, 8), (9, 8192, 16, 512, 8),  # twice: 8 wavefronts
-    (8, 11008, 16, 688, 4), (16, 11008, 16, 688, 4), (5, 16400, 16, 1025, 4)])
-def test_plan_gemv_tile(M, N, group, grid, waves):
+@pytest.mark.parametrize("M,N,group,grid,waves,rows", [
+    (1, 4096, 1, 256, 0, 16), (2, 4096, 2, 256, 0, 16), (3, 4096, 4, 256, 0, 16),
+    (4, 4096, 4, 256, 0, 16), (2, 11008, 2, 688, 0, 16), (4, 11008, 4, 688, 0, 16),
+    # up to 4 tokens the vector ALU; from 5 the matrix unit, whose N/16 workgroups fit 256
+    # compute units once: 16 wavefronts
+    (5, 4096, 16, 256, 16, 16), (8, 4096, 16, 256, 16, 16), (16, 4096, 16, 256, 16, 16),
+    # N/32 workgroups fit once: 32 rows, 8 wavefronts
+    (5, 4097, 16, 129, 8, 32), (9, 8192, 16, 256, 8, 32), (16, 5120, 16, 160, 8, 32),
+    # beyond: 16 rows, 4 wavefronts
+    (9, 8208, 16, 513, 4, 16), (8, 11008, 16, 688, 4, 16), (16, 11008, 16, 688, 4, 16),
+    (5, 16400, 16, 1025, 4, 16)])
+def test_plan_gemv_tile(M, N, group, grid, waves, rows):
     auto = mmq.mmq_plan(M, N, 4096, 160 * 1024)
     assert (auto["tile"], auto["reason"]) == (GEMV, mmq.MMQ_REASON_DECODE)
     p = mmq.mmq_plan(M, N, 4096, 160 * 1024, force_tile=GEMV)
     assert p["tile"] == GEMV
-    assert p["block_m"] == group and p["block_n"] == 16
+    assert p["block_m"] == group and p["block_n"] == rows
     assert p["threads"] == (512 if waves == 0 else 64 * waves)
-    lds = dot_lds(group) if waves == 0 else waves * MFMA_WAVE_LDS
+    lds = dot_lds(group) if waves == 0 else waves * mfma_wave_lds(rows)
     assert p["lds_bytes"] == lds and p["grid"] == grid
 
 
-@pytest.mark.parametrize("M,N,waves", [(8, 4096, 16), (5, 4096, 16), (5, 4097, 8),
-                                       (7, 8192, 8)])
-def test_plan_gemv_form_falls_back_within_the_budget(M, N, waves):
-    """5-8 tokens take the vector-ALU form where the matrix-unit form's LDS (at the wavefront
-    count the row blocks call for) does not fit."""
-    need = waves * MFMA_WAVE_LDS
+@pytest.mark.parametrize("M,N,waves,rows", [(8, 4096, 16, 16), (5, 4096, 16, 16),
+                                            (5, 4097, 8, 32), (7, 8192, 8, 32)])
+def test_plan_gemv_form_falls_back_within_the_budget(M, N, waves, rows):
+    """5-8 tokens take the vector-ALU form where the matrix-unit form's LDS (at the shape the
+    row blocks call for) does not fit."""
+    need = waves * mfma_wave_lds(rows)
     group = 8
     p = mmq.mmq_plan(M, N, 4096, 160 * 1024, opt_lds_budget=need - 1)
     assert p["tile"] == GEMV and p["threads"] == 512 and p["block_m"] == group
     assert p["lds_bytes"] == dot_lds(group)
     p = mmq.mmq_plan(M, N, 4096, 160 * 1024, opt_lds_budget=need)
     assert p["tile"] == GEMV and p["threads"] == 64 * waves and p["block_m"] == 16
+    assert p["block_n"] == rows
 
 
 def test_plan_gemv_matrix_form_only_from_9_tokens():

@@ -92,22 +92,26 @@ def test_gemv_both_forms_from_5_to_8_tokens(M, N, K):
     vector-ALU form under an LDS budget one byte below it."""
     a, ia = _check(M, N, K, 300 + M)
     assert ia["block_m"] == 16 and ia["threads"] == 64 * mfma_waves(N)
+    assert ia["block_n"] == (32 if mfma_waves(N) == 8 else 16)
     b, ib = _check(M, N, K, 300 + M, lds_budget=valu_budget(M, N, K))
     assert ib["threads"] == 512 and ib["block_m"] == 8
 
 
 @pytest.mark.parametrize("M,N,K", [
-    (16, 4112, 1024),   # 257 row blocks: 8 wavefronts, one super-block each
+    (16, 4112, 1024),   # 257 16-row blocks: 129 of 32 rows (the last with 16), 8 wavefronts
     (5, 4100, 2816),    # 8 wavefronts over 11 super-blocks: three take a second one
-    (6, 8192, 4096),    # 512 row blocks: 8 wavefronts, two super-blocks each
+    (6, 8192, 4096),    # 256 blocks of 32 rows: 8 wavefronts, two super-blocks each
+    (7, 4104, 512),     # 129 blocks of 32 rows, the last with 8 rows: a half with none
     (9, 8208, 9472),    # 513 row blocks: 4 wavefronts over 37 super-blocks (10, 9, 9, 9)
     (16, 11008, 4096),  # the gate/up rows: 4 wavefronts, four super-blocks each
 ])
 def test_gemv_matrix_form_wave_counts(M, N, K):
-    """The matrix-unit form with 8 and 4 wavefronts per workgroup, each wavefront taking one or
-    several super-blocks (the next one's weights loaded during this one), every element."""
+    """The matrix-unit form with 8 wavefronts and 32 rows and with 4 wavefronts and 16 rows per
+    workgroup, each wavefront taking one or several super-blocks (the next one's weights
+    loaded during this one), every element."""
     C, info = _check(M, N, K, 700 + M)
     assert info["block_m"] == 16 and info["threads"] == 64 * mfma_waves(N)
+    assert info["block_n"] == (32 if mfma_waves(N) == 8 else 16)
 
 
 @pytest.mark.parametrize("M,N,K", [
