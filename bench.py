@@ -172,8 +172,8 @@ def copy_probe(mib: int) -> int:
 def warm(step, warmup: int, warmup_ms: float) -> int:
     """Run step(i) at least `warmup` times and for at least `warmup_ms` of wall time, then
     synchronize. Under this load the device's clocks take tens of milliseconds to settle,
-    so a step count alone (the driver passes a handful) would leave the timed steps inside
-    the ramp. Returns the number of warmup steps run."""
+    so a step count alone (a caller may ask for a handful) would leave the timed steps
+    inside the ramp. Returns the number of warmup steps run."""
     import torch
     i, t0 = 0, time.perf_counter()
     while i < warmup or (time.perf_counter() - t0) * 1e3 < warmup_ms:
@@ -581,7 +581,7 @@ def q6k_line(name: str, W: dict, R: int, steps: int, warmup: int) -> dict:
 
 def sweep(args) -> int:
     """Every configuration (and each tile the guard allows), then the 7-projection prefill:
-    one JSON line each. Not the driver's benchmark line; see the profiles."""
+    one JSON line each. Not the headline benchmark line; see the profiles."""
     import synth
     import q4_q8_int8_amd as mmq
     names = ["tiny", "qproj", "gateup", "down"] + [f"sweep_m{m}" for m in synth.SWEEP_M] \
